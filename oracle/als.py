@@ -1,0 +1,216 @@
+"""Greedy expanded-rank ternary decomposition A ~ B diag(D) C, in fp64.
+
+Test infrastructure: only tests, the smoke check and the benchmark's CPU
+baseline may use this module.  It is a plain, slow transcription of the
+method as the pages describe it; matrix products come from numpy (a library
+primitive), nothing is fused or reordered.
+
+Sources (ExTernD: Expanded-Rank Ternary Decomposition Ternary LLM PTQ with
+Accuracy Approaching Any Quantization Level):
+  §2.1  representation, k = mu * min(m, n), energy E
+  §2.3  greedy sequential ALS: alternating ternary fit, optimal scale, deflation
+  §2.4  batched block ALS with decorrelated targets and a joint scale solve
+  Appendix (monotone residual): the residual norm never increases.
+
+Readings (listed with their reasons in the design doc):
+  * k = round-half-away(mu * min(m, n)) computed in fp64, mu widened from fp32.
+  * One iteration is the V update followed by the U update; there are `iters`
+    of them and no early stop.  The scale uses the final u and v, and u.x with
+    x = R v from the last iteration equals u^T R v.
+  * u0 / U0 come from oracle.init_rule (dense +-1, keyed on the component index).
+  * Block mode: b_eff = min(block, floor(min(m, n) / 8)); a trailing partial
+    block takes the remaining components.  The ridge is
+    eps = 1e-6 * trace(G) / b for each Gram matrix G.  The joint scale system
+    [(U^T U) o (V^T V)] d = diag(U^T R V) is solved by Cholesky; if that fails
+    it is retried with the same kind of ridge and the event is counted.
+  * ||A|| = 0 gives E = 1.
+"""
+import math
+
+import numpy as np
+
+from .init_rule import init_signs, init_block
+from .ternarize import ternarize, ternarize_columns
+
+__all__ = ["rank_for", "block_width", "ridge", "decompose_seq", "decompose_block",
+           "rank1_fit", "SeqResult"]
+
+
+def rank_for(m, n, mu):
+    """k = mu * min(m, n), rounded half away from zero (§2.1)."""
+    mu64 = float(np.float32(mu))
+    v = mu64 * float(min(m, n))
+    whole = math.floor(v)
+    return int(whole) + (1 if v - whole >= 0.5 else 0)
+
+
+def block_width(m, n, block):
+    """Effective block width: requested b capped at floor(min(m,n)/8) (§2.4).
+
+    Returns 1 (sequential) when the request or the cap is below 2.
+    """
+    if block <= 1:
+        return 1
+    b = min(int(block), min(m, n) // 8)
+    return b if b >= 2 else 1
+
+
+def ridge(G):
+    """eps for (G + eps I): 1e-6 times the mean diagonal of G (§2.4 names eps only)."""
+    b = G.shape[0]
+    return 1e-6 * float(np.trace(G)) / b
+
+
+class SeqResult:
+    """Factors and diagnostics of one decomposition.
+
+    B: m x k int8, C: k x n int8, D: k float64, trace: ||R||^2 after each
+    component (sequential) or block (block mode), E: energy preserved,
+    norm_a2: ||A||^2, extra: mode-specific diagnostics.
+    """
+
+    def __init__(self, B, C, D, trace, E, norm_a2, extra=None):
+        self.B, self.C, self.D = B, C, D
+        self.trace, self.E, self.norm_a2 = trace, E, norm_a2
+        self.extra = extra or {}
+
+
+def rank1_fit(R, u0, tau, iters):
+    """Alternating ternary fit of one component against residual R (§2.3 steps 1-2).
+
+    Returns dict with u, v (int8), d, c = u^T R v, the history of the
+    intermediate vectors (y_t = R^T u, v_t, x_t = R v, u_t) and nnz counts.
+    R is not modified.
+    """
+    u = np.asarray(u0, dtype=np.float64)
+    hist = []
+    x = None
+    v = None
+    for _ in range(iters):
+        y = R.T @ u
+        v = ternarize(y, tau).astype(np.float64)
+        x = R @ v
+        u_new = ternarize(x, tau).astype(np.float64)
+        hist.append((y, v.copy(), x, u_new.copy()))
+        u = u_new
+    nu = float(np.count_nonzero(u))
+    nv = float(np.count_nonzero(v))
+    c = float(u @ x)
+    d = c / (nu * nv)
+    return {"u": u.astype(np.int8), "v": v.astype(np.int8), "d": d, "c": c,
+            "nnz_u": int(nu), "nnz_v": int(nv), "hist": hist}
+
+
+def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None):
+    """Greedy sequential ALS (§2.3).  Returns SeqResult.
+
+    record: optional set of component indices whose rank1_fit history and
+    pre-deflation residual are kept in result.extra["records"].
+    """
+    A = np.asarray(A)
+    m, n = A.shape
+    if k is None:
+        k = rank_for(m, n, mu)
+    R = A.astype(np.float64, copy=True)
+    norm_a2 = float(np.sum(R * R))
+    B = np.zeros((m, k), dtype=np.int8)
+    C = np.zeros((k, n), dtype=np.int8)
+    D = np.zeros(k, dtype=np.float64)
+    trace = np.zeros(k, dtype=np.float64)
+    decrease = np.zeros(k, dtype=np.float64)
+    sum_nnz_u = 0
+    records = {}
+    for i in range(k):
+        u0 = init_signs(seed, i, m)
+        if record is not None and i in record:
+            records[i] = {"R": R.copy()}
+        fit = rank1_fit(R, u0, tau, iters)
+        u = fit["u"].astype(np.float64)
+        v = fit["v"].astype(np.float64)
+        d = fit["d"]
+        R -= d * np.outer(u, v)
+        B[:, i] = fit["u"]
+        C[i, :] = fit["v"]
+        D[i] = d
+        trace[i] = float(np.sum(R * R))
+        decrease[i] = fit["c"] ** 2 / (fit["nnz_u"] * fit["nnz_v"])
+        sum_nnz_u += sum(int(np.count_nonzero(h[3])) for h in fit["hist"])
+        if record is not None and i in record:
+            records[i]["fit"] = fit
+    last = trace[k - 1] if k > 0 else norm_a2
+    E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
+    return SeqResult(B, C, D, trace, E, norm_a2,
+                     {"decrease": decrease, "records": records, "sum_nnz_u": sum_nnz_u})
+
+
+def _cholesky_solve(G, rhs, eps):
+    """Solve (G + eps I) X = rhs by Cholesky (rhs may be a matrix)."""
+    Gr = G + eps * np.eye(G.shape[0])
+    Lc = np.linalg.cholesky(Gr)
+    z = np.linalg.solve(Lc, rhs)
+    return np.linalg.solve(Lc.T, z)
+
+
+def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None):
+    """Batched block ALS with decorrelated targets (§2.4).  Returns SeqResult.
+
+    Each iteration:  P = R^T U;  V <- T_col( P (U^T U + eps I)^-1 );
+                     Q = R V;    U <- T_col( Q (V^T V + eps I)^-1 ).
+    Then diag(U^T R V) is read off the last Q, the b scales solve
+    [(U^T U) o (V^T V)] d = diag(U^T R V), and R <- R - U diag(d) V^T.
+
+    force_width: run the block iteration with exactly this width, bypassing
+    the cap and the fall-back to sequential mode (used to pin b = 1 against
+    the sequential algorithm).
+    """
+    A = np.asarray(A)
+    m, n = A.shape
+    if k is None:
+        k = rank_for(m, n, mu)
+    b = block_width(m, n, block) if force_width is None else int(force_width)
+    if b == 1 and force_width is None:
+        res = decompose_seq(A, mu, tau, iters, seed, k)
+        res.extra["b"] = 1
+        return res
+    R = A.astype(np.float64, copy=True)
+    norm_a2 = float(np.sum(R * R))
+    B = np.zeros((m, k), dtype=np.int8)
+    C = np.zeros((k, n), dtype=np.int8)
+    D = np.zeros(k, dtype=np.float64)
+    nblocks = (k + b - 1) // b
+    trace = np.zeros(nblocks, dtype=np.float64)
+    decrease = np.zeros(nblocks, dtype=np.float64)
+    ridge_retries = 0
+    for blk in range(nblocks):
+        c0 = blk * b
+        bb = min(b, k - c0)
+        U = init_block(seed, c0, bb, m)
+        V = None
+        Q = None
+        GU = GV = None
+        for _ in range(iters):
+            P = R.T @ U
+            GU = U.T @ U
+            V = ternarize_columns(_cholesky_solve(GU, P.T, ridge(GU)).T, tau).astype(np.float64)
+            Q = R @ V
+            GV = V.T @ V
+            U = ternarize_columns(_cholesky_solve(GV, Q.T, ridge(GV)).T, tau).astype(np.float64)
+        GU = U.T @ U
+        GV = V.T @ V
+        rhs = np.sum(U * Q, axis=0)
+        Mjs = GU * GV
+        try:
+            d = _cholesky_solve(Mjs, rhs, 0.0)
+        except np.linalg.LinAlgError:
+            ridge_retries += 1
+            d = _cholesky_solve(Mjs, rhs, ridge(Mjs))
+        R -= (U * d) @ V.T
+        B[:, c0:c0 + bb] = U.astype(np.int8)
+        C[c0:c0 + bb, :] = V.T.astype(np.int8)
+        D[c0:c0 + bb] = d
+        trace[blk] = float(np.sum(R * R))
+        decrease[blk] = float(d @ rhs)
+    last = trace[-1] if nblocks > 0 else norm_a2
+    E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
+    return SeqResult(B, C, D, trace, E, norm_a2,
+                     {"decrease": decrease, "b": b, "ridge_retries": ridge_retries})

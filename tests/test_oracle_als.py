@@ -1,0 +1,191 @@
+"""Pins of the oracle's sequential and block ALS (CPU only).
+
+Each check is fixed by the pages or by mathematics rather than by retyping
+the oracle: the exact least-squares decrease of a rank-1 deflation, a
+brute-force optimum on tiny matrices, exact recovery of ternary rank-1
+matrices, symmetries, the prefix property, block b=1 against sequential,
+and the residual-monotone property the pages prove.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+
+def _small(m, n, seed, scale=1.0):
+    return synthetic.gaussian(m, n, seed, std=scale)
+
+
+def test_rank_rule():
+    assert oracle.rank_for(256, 256, 2.0) == 512
+    assert oracle.rank_for(2560, 2560, 2.0) == 5120
+    assert oracle.rank_for(9728, 2560, 3.0) == 7680
+    assert oracle.rank_for(1024, 2560, 2.5) == 2560
+    assert oracle.rank_for(4096, 4096, 3.5) == 14336
+    assert oracle.rank_for(10, 3, 0.5) == 2          # 1.5 rounds up
+    assert oracle.rank_for(7, 7, 0.0) == 0
+
+
+def test_block_width_rule():
+    assert oracle.block_width(2560, 2560, 64) == 64
+    assert oracle.block_width(1024, 2560, 256) == 128   # cap floor(1024/8)
+    assert oracle.block_width(15, 100, 64) == 1         # cap 1 -> sequential
+    assert oracle.block_width(100, 100, 1) == 1
+
+
+def test_sequential_invariants():
+    A = _small(48, 40, 0)
+    r = oracle.decompose_seq(A, 1.5, 0.7, iters=15, seed=3)
+    k = oracle.rank_for(48, 40, 1.5)
+    assert r.B.shape == (48, k) and r.C.shape == (k, 40) and r.D.shape == (k,)
+    assert set(np.unique(r.B)).issubset({-1, 0, 1})
+    assert set(np.unique(r.C)).issubset({-1, 0, 1})
+    # every component has a nonzero u and v (the fallback guarantees it)
+    assert np.all(np.count_nonzero(r.B, axis=0) > 0)
+    assert np.all(np.count_nonzero(r.C, axis=1) > 0)
+    # ||R||^2 never increases (Appendix), and each step removes exactly
+    # (u^T R v)^2 / (||u||^2 ||v||^2), the least-squares optimum for that u, v
+    prev = np.concatenate([[r.norm_a2], r.trace[:-1]])
+    assert np.all(r.trace <= prev * (1 + 1e-12))
+    np.testing.assert_allclose(prev - r.trace, r.extra["decrease"], rtol=1e-9,
+                               atol=1e-12 * r.norm_a2)
+    # the energy of the factors alone matches the trace
+    assert oracle.energy_from_factors(A, r.B, r.C, r.D) == pytest.approx(r.E, abs=1e-12)
+
+
+def test_scale_is_least_squares():
+    # For the fitted u, v, no other scale lowers ||R - d u v^T||.
+    A = _small(30, 20, 1)
+    R = A.astype(np.float64)
+    fit = oracle.rank1_fit(R, oracle.init_signs(0, 0, 30), 0.7, 15)
+    u, v = fit["u"].astype(float), fit["v"].astype(float)
+    f = lambda d: float(np.sum((R - d * np.outer(u, v)) ** 2))
+    d = fit["d"]
+    for eps in (1e-3, -1e-3, 1e-6, -1e-6):
+        assert f(d) <= f(d * (1 + eps))
+
+
+def test_brute_force_rank1_bound():
+    # The ALS decrease can never beat the best ternary rank-1 fit.
+    rng = np.random.default_rng(7)
+    tern = [np.array(t, dtype=float) for t in itertools.product((-1, 0, 1), repeat=4) if any(t)]
+    for trial in range(5):
+        R = rng.standard_normal((4, 4))
+        best = max((u @ R @ v) ** 2 / ((u @ u) * (v @ v)) for u in tern for v in tern)
+        fit = oracle.rank1_fit(R, oracle.init_signs(trial, 0, 4), 0.7, 15)
+        got = fit["c"] ** 2 / (fit["nnz_u"] * fit["nnz_v"])
+        assert got <= best * (1 + 1e-12)
+        assert got > 0
+
+
+def test_exact_recovery_of_ternary_rank1():
+    rng = np.random.default_rng(9)
+    for trial in range(4):
+        m, n = 24, 17
+        us = rng.choice([-1, 0, 1], size=m, p=[0.3, 0.4, 0.3])
+        vs = rng.choice([-1, 0, 1], size=n, p=[0.3, 0.4, 0.3])
+        us[0], vs[0] = 1, -1
+        A = (0.375 * np.outer(us, vs)).astype(np.float32)
+        r = oracle.decompose_seq(A, 0.25, 0.7, seed=trial)
+        assert r.trace[0] == 0.0
+        assert r.E == 1.0
+        assert np.all(r.D[1:] == 0.0)
+        assert abs(r.D[0]) == 0.375
+
+
+def test_single_entry_matrix():
+    A = np.zeros((9, 13), dtype=np.float32)
+    A[4, 7] = -2.5
+    r = oracle.decompose_seq(A, 0.5, 1.0, seed=0)
+    assert r.E == 1.0
+    assert r.B[:, 0].tolist() == [0] * 4 + [int(np.sign(r.B[4, 0]))] + [0] * 4
+    assert np.count_nonzero(r.C[0]) == 1 and r.C[0, 7] != 0
+    assert r.D[0] * r.B[4, 0] * r.C[0, 7] == -2.5
+
+
+def test_zero_matrix():
+    r = oracle.decompose_seq(np.zeros((8, 8), np.float32), 1.0, 0.7)
+    assert r.E == 1.0 and np.all(r.D == 0.0)
+
+
+def test_symmetries():
+    A = _small(40, 32, 2)
+    r = oracle.decompose_seq(A, 1.0, 0.7, seed=1)
+    rn = oracle.decompose_seq(-A, 1.0, 0.7, seed=1)
+    assert np.array_equal(rn.B, r.B) and np.array_equal(rn.C, -r.C)
+    assert np.array_equal(rn.D, r.D)
+    for p in (-7, 9):
+        rs = oracle.decompose_seq(np.ldexp(A, p), 1.0, 0.7, seed=1)
+        assert np.array_equal(rs.B, r.B) and np.array_equal(rs.C, r.C)
+        assert np.array_equal(rs.D, np.ldexp(r.D, p))
+        assert rs.E == r.E
+
+
+def test_prefix_property():
+    A = _small(36, 36, 3)
+    r_small = oracle.decompose_seq(A, 0.5, 1.0, seed=2)
+    r_big = oracle.decompose_seq(A, 1.5, 1.0, seed=2)
+    k1 = r_small.D.size
+    assert np.array_equal(r_big.B[:, :k1], r_small.B)
+    assert np.array_equal(r_big.C[:k1], r_small.C)
+    assert np.array_equal(r_big.D[:k1], r_small.D)
+    assert r_big.E >= r_small.E
+
+
+def test_block_width_one_equals_sequential():
+    # With b = 1 the decorrelated targets are positive multiples of R^T u and
+    # R v, T_tau is scale invariant and the joint solve reduces to the single
+    # scale, so the block iteration reproduces the sequential one (§2.3, §2.4).
+    A = _small(40, 28, 4)
+    rs = oracle.decompose_seq(A, 1.0, 0.7, seed=5)
+    rb = oracle.decompose_block(A, 1.0, 0.7, block=1, seed=5, force_width=1)
+    assert np.array_equal(rb.B, rs.B) and np.array_equal(rb.C, rs.C)
+    np.testing.assert_allclose(rb.D, rs.D, rtol=1e-10)
+    np.testing.assert_allclose(rb.trace, rs.trace, rtol=1e-9)
+
+
+def test_block_invariants():
+    A = _small(96, 80, 6)
+    r = oracle.decompose_block(A, 2.0, 0.7, block=8, seed=0)
+    assert r.extra["b"] == 8
+    prev = np.concatenate([[r.norm_a2], r.trace[:-1]])
+    # per-block decrease is rhs^T M^-1 rhs >= 0 and equals the drop of ||R||^2
+    assert np.all(r.extra["decrease"] >= 0)
+    np.testing.assert_allclose(prev - r.trace, r.extra["decrease"], rtol=1e-8,
+                               atol=1e-12 * r.norm_a2)
+    assert oracle.energy_from_factors(A, r.B, r.C, r.D) == pytest.approx(r.E, abs=1e-12)
+    assert set(np.unique(r.B)).issubset({-1, 0, 1})
+
+
+def test_block_close_to_sequential():
+    # Pages (§3.1 table caption): block within about 0.2 points of sequential.
+    A = synthetic.gaussian(256, 256, 0)
+    rs = oracle.decompose_seq(A, 1.0, 0.7, seed=0)
+    rb = oracle.decompose_block(A, 1.0, 0.7, block=32, seed=0)
+    assert abs(rb.E - rs.E) < 0.005
+
+
+def test_block_trailing_partial_block():
+    A = _small(64, 64, 8)
+    r = oracle.decompose_block(A, 0.7, 0.7, block=8, seed=0)   # k = 45 -> 5 full + 5
+    assert r.D.size == 45 and r.trace.size == 6
+    assert oracle.energy_from_factors(A, r.B, r.C, r.D) == pytest.approx(r.E, abs=1e-12)
+
+
+@pytest.mark.parametrize("tau,lo,hi", [(0.7, 0.36, 0.47), (1.0, 0.52, 0.62), (2.0, 0.82, 0.92)])
+def test_factor_sparsity_tracks_tau(tau, lo, hi):
+    # Pages (§1): tau = 0.7 / 1.0 / 2.0 give about 41 / 57 / 87 % zeros.
+    A = synthetic.gaussian(128, 128, 1)
+    r = oracle.decompose_seq(A, 1.0, tau, seed=0)
+    zf = oracle.zero_fraction(r.B, r.C)
+    assert lo < zf < hi
+
+
+def test_energy_grows_with_mu():
+    A = synthetic.gaussian(64, 64, 2)
+    es = [oracle.decompose_seq(A, mu, 0.7, seed=0).E for mu in (0.5, 1.0, 2.0, 3.0)]
+    assert all(b >= a for a, b in zip(es, es[1:]))
+    assert es[-1] > 0.99

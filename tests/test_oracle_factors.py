@@ -1,0 +1,65 @@
+"""Pins of the oracle's codec, energy, storage formula and starting-vector rule."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def test_pack2_known_words():
+    # hand-packed: +1 -> 01, -1 -> 11, 0 -> 00, element j at bits 2j..2j+1
+    T = np.array([[1, -1, 0, 1]], dtype=np.int8)
+    assert oracle.pack2(T).tolist() == [[1 + (3 << 2) + (1 << 6)]]
+    T = np.zeros((1, 17), dtype=np.int8)
+    T[0, 15] = -1
+    T[0, 16] = 1
+    assert oracle.pack2(T).tolist() == [[3 << 30, 1]]
+
+
+def test_pack2_roundtrip_and_invalid():
+    rng = np.random.default_rng(0)
+    for L in (1, 15, 16, 17, 100):
+        T = rng.integers(-1, 2, size=(5, L)).astype(np.int8)
+        assert np.array_equal(oracle.unpack2(oracle.pack2(T), L), T)
+    with pytest.raises(ValueError):
+        oracle.unpack2(np.array([[2]], dtype=np.uint32), 1)
+    with pytest.raises(ValueError):
+        oracle.unpack2(np.array([[1 << 2]], dtype=np.uint32), 1)
+
+
+def test_energy_of_exact_factors():
+    rng = np.random.default_rng(1)
+    B = rng.integers(-1, 2, size=(20, 7))
+    C = rng.integers(-1, 2, size=(7, 11))
+    D = rng.standard_normal(7)
+    A = (B * D) @ C
+    assert oracle.energy_from_factors(A, B, C, D) == pytest.approx(1.0, abs=1e-14)
+    assert oracle.energy_from_factors(A, B, C, np.zeros(7)) == 0.0
+
+
+def test_bpw_eq1():
+    # Eq. 1 (§2.6) for a square matrix at mu=2 with 43% zeros: 2*2*(2-0.43)
+    assert oracle.bpw_eff(2.0, 100, 100, 0.43) == pytest.approx(6.28)
+    # mask entropy quoted on the pages for 43% zeros, H(0.43) ~ 0.99 bits
+    h = -(0.43 * math.log2(0.43) + 0.57 * math.log2(0.57))
+    assert round(h, 2) == 0.99
+    assert oracle.bpw_packed2(512, 256, 256) == pytest.approx((2 * 512 * 512 + 32 * 512) / 65536)
+
+
+def test_splitmix64_known_answer():
+    # First SplitMix64 output from state 0, as published with the generator.
+    assert oracle.splitmix64_mix(0) == 0xE220A8397B1DCDAF
+
+
+def test_init_signs_matches_scalar_hash_and_is_balanced():
+    u = oracle.init_signs(7, 3, 1000)
+    for r in (0, 1, 500, 999):
+        assert u[r] == (-1.0 if oracle.init_hash(7, 3, r) >> 63 else 1.0)
+    big = oracle.init_signs(0, 0, 200_000)
+    assert abs(big.mean()) < 0.01
+    # different components and seeds give uncorrelated starts
+    a, b, c = oracle.init_signs(0, 0, 50_000), oracle.init_signs(0, 1, 50_000), oracle.init_signs(1, 0, 50_000)
+    assert abs(a @ b) / 50_000 < 0.02 and abs(a @ c) / 50_000 < 0.02
+    Ub = oracle.init_block(0, 4, 3, 64)
+    assert np.array_equal(Ub[:, 1], oracle.init_signs(0, 5, 64))

@@ -1,0 +1,128 @@
+"""Pins of the oracle's T_tau and optimal projection (CPU only).
+
+Each test ties oracle.ternarize / oracle.optimal_projection to something the
+pages or mathematics fix independently of the code: hand-worked vectors,
+a Gaussian closed form, brute force over all ternary vectors, invariances.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import optimize, special, stats
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _cases():
+    with open(os.path.join(HERE, "golden", "ternarize_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: c["why"][:40])
+def test_hand_worked_vectors(case):
+    t = oracle.ternarize(np.array(case["x"], dtype=np.float64), case["tau"])
+    assert t.tolist() == case["t"]
+
+
+def test_threshold_is_mean_times_tau():
+    # S is within N * 2**-s of the exact sum; compare against math.fsum.
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 3, 17, 1000, 4097):
+        x = rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6)
+        thr, big = oracle.mean_abs_threshold(x, 1.0)
+        exact = math.fsum(np.abs(x)) / n
+        assert big == np.abs(x).max()
+        assert abs(thr - exact) <= 1e-12 * exact
+
+
+def test_sign_and_scale_invariance():
+    rng = np.random.default_rng(1)
+    for n in (5, 64, 1001):
+        x = rng.standard_normal(n)
+        for tau in (0.3, 0.7, 1.0, 2.0, 4.0):
+            t = oracle.ternarize(x, tau)
+            assert np.array_equal(oracle.ternarize(-x, tau), -t)
+            for p in (-40, -3, 5, 60):
+                assert np.array_equal(oracle.ternarize(np.ldexp(x, p), tau), t)
+
+
+def test_order_free():
+    # A permutation of the input permutes the output (the mean does not
+    # depend on summation order).
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(3000) * np.exp(rng.standard_normal(3000) * 3)
+    perm = rng.permutation(x.size)
+    for tau in (0.7, 1.0, 2.0):
+        assert np.array_equal(oracle.ternarize(x[perm], tau), oracle.ternarize(x, tau)[perm])
+
+
+def test_output_is_ternary_and_nonzero():
+    rng = np.random.default_rng(3)
+    for n in (1, 2, 7, 100):
+        for tau in (0.7, 2.0, 50.0):
+            t = oracle.ternarize(rng.standard_normal(n), tau)
+            assert set(np.unique(t)).issubset({-1, 0, 1})
+            assert np.count_nonzero(t) >= 1
+
+
+@pytest.mark.parametrize("tau", [0.7, 1.0, 2.0])
+def test_gaussian_zero_fraction_closed_form(tau):
+    # For iid N(0,1), mean|x| -> sqrt(2/pi); the zero fraction tends to
+    # P(|x| <= tau*sqrt(2/pi)) = erf(tau/sqrt(pi)).  The pages report
+    # ~41/57/87% zeros at tau = 0.7/1.0/2.0 on real matrices (§1, §3.2).
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal(1_000_000)
+    zf = float(np.mean(oracle.ternarize(x, tau) == 0))
+    closed = special.erf(tau / math.sqrt(math.pi))
+    assert abs(zf - closed) < 0.003
+    pages = {0.7: 0.41, 1.0: 0.57, 2.0: 0.87}[tau]
+    assert abs(zf - pages) < 0.03
+
+
+def _captured(x, t):
+    """Fraction of ||x||^2 captured by the best multiple of ternary t."""
+    t = t.astype(np.float64)
+    return float((x @ t) ** 2 / (t @ t) / (x @ x))
+
+
+def test_optimal_projection_vs_brute_force():
+    rng = np.random.default_rng(4)
+    for n in range(1, 8):
+        for _ in range(6):
+            x = rng.standard_normal(n)
+            if n > 2:
+                x[rng.integers(n)] = 0.0
+            best = 0.0
+            for tt in itertools.product((-1, 0, 1), repeat=n):
+                tt = np.array(tt, dtype=np.float64)
+                if not tt.any():
+                    continue
+                best = max(best, (x @ tt) ** 2 / (tt @ tt))
+            t, alpha = oracle.optimal_projection(x)
+            got = (x @ t) ** 2 / (t.astype(np.float64) @ t)
+            assert got == pytest.approx(best, rel=1e-12, abs=1e-300)
+            # alpha is the least-squares scale for t
+            assert alpha == pytest.approx((x @ t) / np.count_nonzero(t), rel=1e-12)
+
+
+def test_threshold_ties_optimal_projection_on_gaussians():
+    # Continuum: a threshold at t sigma captures 2 phi(t)^2 / Q(t) of the
+    # energy.  The optimum solves phi(t) = 2 t Q(t).  The pages say T_0.7
+    # empirically ties the optimal projection (§2.2).
+    phi, Q = stats.norm.pdf, stats.norm.sf
+    cap = lambda t: 2 * phi(t) ** 2 / Q(t)
+    t_opt = optimize.brentq(lambda t: phi(t) - 2 * t * Q(t), 0.1, 2.0)
+    t07 = 0.7 * math.sqrt(2 / math.pi)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(1_000_000)
+    c07 = _captured(x, oracle.ternarize(x, 0.7))
+    copt = _captured(x, oracle.optimal_projection(x)[0])
+    assert c07 == pytest.approx(cap(t07), abs=0.003)
+    assert copt == pytest.approx(cap(t_opt), abs=0.003)
+    assert copt >= c07
+    assert c07 / copt > 0.995
