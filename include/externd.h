@@ -1,0 +1,165 @@
+/*
+ * externd.h — C ABI of the MI355X (gfx950) ExTernD library.
+ *
+ * ExTernD ("ExTernD: Expanded-Rank Ternary Decomposition Ternary LLM PTQ with
+ * Accuracy Approaching Any Quantization Level") approximates a real matrix
+ * A (m x n) by B diag(D) C with ternary B (m x k), ternary C (k x n) and real
+ * D (k), k = mu * min(m, n) (§2.1).  Component i is fitted to the residual
+ * R = A - sum_{j<i} d_j b_j c_j^T by a fixed number of alternating ternary fits
+ * v = T_tau(R^T u), u = T_tau(R v) (§2.3 step 1, T_tau of §2.2), given the
+ * least-squares scale d = u^T R v / (|u|^2 |v|^2) (§2.3 step 2) and deflated
+ * out of R (§2.3 step 3).  Block mode extracts b components at a time with
+ * decorrelated targets and a joint scale solve (§2.4).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named A, R, x, y, B2, C2, D, energy, trace, stats, capture_* and
+ *    workspace are DEVICE pointers (hipMalloc'd or equivalent) on the current
+ *    HIP device.  The caller owns every buffer; the library never frees them.
+ *  - Matrices are row-major and densely packed (leading dimension = columns).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    All device work is enqueued on it; entry points return without waiting
+ *    for it, so device outputs are valid once the stream has completed.
+ *  - Argument errors are detected on the host before anything is enqueued
+ *    and return EXTERND_EINVAL; device-side failures return EXTERND_EHIP with
+ *    a message available from externd_last_error().
+ *  - 2-bit ternary codes: a row of length L occupies ceil(L/16) uint32 words;
+ *    element j sits in bits 2*(j%16)..2*(j%16)+1 of word j/16 with
+ *    00 = 0, 01 = +1, 11 = -1 (10 never produced).  Padding bits are 00.
+ *    B2 is component-major: row i (ceil(m/16) words) holds column i of B.
+ *    C2 row i (ceil(n/16) words) holds row i of C.
+ */
+#ifndef EXTERND_H
+#define EXTERND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum externd_status {
+  EXTERND_OK = 0,
+  EXTERND_EINVAL = 1,       /* bad argument (null pointer, size, non-finite knob) */
+  EXTERND_ENOMEM = 2,       /* workspace allocation failed or too small */
+  EXTERND_EHIP = 3,         /* HIP runtime error or a failed kernel launch */
+  EXTERND_EUNSUPPORTED = 4  /* device is not gfx950 / shape outside a mode's limits */
+};
+
+/* Execution modes of the sequential path. */
+enum externd_mode {
+  EXTERND_MODE_AUTO = -1,      /* resident when the shape fits on chip, else streaming */
+  EXTERND_MODE_STREAMING = 0,  /* R in device memory, one kernel per ALS half-step */
+  EXTERND_MODE_RESIDENT = 1    /* one cooperative kernel, R kept in LDS/VGPRs */
+};
+
+/* Indices into the optional int64 statistics array (EXTERND_STATS_LEN entries). */
+enum externd_stat {
+  EXTERND_STAT_SUM_NNZ_U = 0,   /* sum over components and iterations of nnz(u_t) */
+  EXTERND_STAT_SUM_NNZ_V = 1,   /* same for v_t */
+  EXTERND_STAT_NNZ_B = 2,       /* nonzeros in the final B */
+  EXTERND_STAT_NNZ_C = 3,       /* nonzeros in the final C */
+  EXTERND_STAT_FALLBACKS = 4,   /* T_tau calls that fell back to the single largest entry */
+  EXTERND_STAT_NONFINITE = 5,   /* non-finite entries found in A (energy is NaN if > 0) */
+  EXTERND_STAT_MODE = 6,        /* mode actually run (0 streaming, 1 resident, 2 block) */
+  EXTERND_STAT_GRID = 7,        /* workgroups of the resident kernel (0 otherwise) */
+  EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
+  EXTERND_STAT_TIMEOUTS = 9,    /* resident mode: 1 if an exchange wait ran out (energy is NaN) */
+  EXTERND_STATS_LEN = 16
+};
+
+/*
+ * Optional knobs of externd_decompose.  Zero-initialise, set struct_size to
+ * sizeof(externd_opts), then set what you need.  A NULL opts means defaults.
+ */
+typedef struct externd_opts {
+  uint32_t struct_size;   /* sizeof(externd_opts) */
+  uint32_t reserved0;
+  uint64_t seed;          /* starting-vector seed (default 0) */
+  int32_t mode;           /* enum externd_mode; sequential path only (default AUTO) */
+  int32_t reserved1;
+  double* trace;          /* device, optional: ||R||^2 after each component
+                             (sequential: k entries, predicted from the exact
+                             per-step decrease) or after each block (block mode:
+                             ceil(k/b) entries) */
+  int64_t* stats;         /* device, optional: EXTERND_STATS_LEN counters (overwritten) */
+  /* Test capture of one component of the sequential path (capture_component
+   * < 0 disables it).  Each pointer may be NULL. */
+  int64_t capture_component;
+  float* capture_R;       /* m*n: residual before the component (row-resident copy) */
+  float* capture_Rcol;    /* m*n: the same residual from the column-resident copy */
+  float* capture_R_next;  /* m*n: residual after the component's deflation */
+  float* capture_y;       /* iters*n: y_t = R^T u_{t-1} */
+  float* capture_x;       /* iters*m: x_t = R v_t */
+  int8_t* capture_v;      /* iters*n: v_t */
+  int8_t* capture_u;      /* iters*m: u_t (u_0 is the seeded start) */
+  float* capture_d;       /* 1: the component's scale */
+} externd_opts;
+
+/*
+ * Decompose A (m x n, fp32, row-major) into k = externd_rank(m, n, mu)
+ * components.  §2.3 (block <= 1) or §2.4 (block > 1).
+ *   mu     > 0, finite: inner-rank multiplier (§2.1).
+ *   tau    >= 0, finite: threshold scale of T_tau (§2.2), used as fp32.
+ *   iters  >= 1: alternating-fit iterations per component / block (§2.3: 15).
+ *   block  <= 1: sequential greedy ALS; otherwise block ALS with
+ *          b = externd_block_width(m, n, block) (falls back to sequential if < 2).
+ * Outputs (device): B2 [k][ceil(m/16)] u32, C2 [k][ceil(n/16)] u32, D [k] fp32,
+ *   energy [1] fp64 = 1 - ||A - B diag(D) C||^2 / ||A||^2 of the fp32 residual
+ *   (1 when ||A|| = 0; NaN when A has non-finite entries).
+ * A is not modified.  Workspace is allocated stream-ordered and freed before
+ * return is observed by the stream.
+ */
+int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
+                      int32_t iters, int32_t block, void* stream,
+                      uint32_t* B2, uint32_t* C2, float* D, double* energy,
+                      const externd_opts* opts);
+
+/* energy = 1 - ||A - B diag(D) C||^2 / ||A||^2 accumulated in fp64 from the
+ * 2-bit factors (§2.1).  k may be 0 (energy 0, or 1 for A = 0). */
+int externd_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2,
+                   const uint32_t* C2, const float* D, int64_t k, void* stream,
+                   double* energy);
+
+/* A_hat = B diag(D) C (m x n fp32 row-major), accumulated in fp64 per entry (§2.1). */
+int externd_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D,
+                        int64_t m, int64_t n, int64_t k, void* stream, float* A_hat);
+
+/* k = mu * min(m, n) rounded half away from zero in fp64 (§2.1); -1 on bad input. */
+int64_t externd_rank(int64_t m, int64_t n, float mu);
+
+/* Block width actually used for a request: min(block, floor(min(m,n)/8)),
+ * 1 meaning sequential (§2.4). */
+int32_t externd_block_width(int64_t m, int64_t n, int32_t block);
+
+/* 1 if the resident sequential kernel can hold an m x n residual on chip. */
+int32_t externd_resident_fits(int64_t m, int64_t n);
+
+/* ---- single-step entry points (the same device routines as the streaming path) ---- */
+
+/* codes = T_tau(x) for a length-N fp32 vector (§2.2); nnz (device int32, may
+ * be NULL) receives the number of nonzeros. */
+int externd_ternarize(const float* x, int64_t N, float tau, void* stream,
+                      uint32_t* codes, int32_t* nnz);
+
+/* y = R^T u for R (m x n) and u given as 2-bit codes of length m (§2.3 step 1). */
+int externd_gemv_t(const float* R, int64_t m, int64_t n, const uint32_t* u_codes,
+                   void* stream, float* y);
+
+/* x = R v for v given as 2-bit codes of length n (§2.3 step 1). */
+int externd_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes,
+                   void* stream, float* x);
+
+/* R <- R - d u v^T in place, one fp32 rounding per entry (§2.3 step 3). */
+int externd_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
+                    const uint32_t* v_codes, float d, void* stream);
+
+/* Status text and the last error message of the calling thread. */
+const char* externd_status_string(int status);
+const char* externd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXTERND_H */

@@ -1,0 +1,252 @@
+"""Python binding of libexternd.so, the MI355X ExTernD library.
+
+ExTernD ("ExTernD: Expanded-Rank Ternary Decomposition Ternary LLM PTQ with
+Accuracy Approaching Any Quantization Level", §2) factors a weight matrix as
+A ~ B diag(D) C with ternary B, C.  Every step runs in the HIP kernels behind
+the C ABI declared in include/externd.h; this module only marshals torch
+tensors (device memory) and the current HIP stream into those calls.  It
+raises ImportError when the shared library has not been built; there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "decompose", "energy", "reconstruct", "rank", "block_width", "resident_fits",
+    "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
+    "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libexternd.so")
+
+MODE_AUTO, MODE_STREAMING, MODE_RESIDENT = -1, 0, 1
+STATS_LEN = 16
+STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
+        "nonfinite": 5, "mode": 6, "grid": 7, "ridge_retries": 8, "timeouts": 9}
+
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is missing; build it with "
+                      "`python -m ternary_rank_weight_amd.build`")
+_lib = ctypes.CDLL(library_path)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+        ("seed", ctypes.c_uint64), ("mode", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+        ("trace", _p), ("stats", _p),
+        ("capture_component", ctypes.c_int64),
+        ("capture_R", _p), ("capture_Rcol", _p), ("capture_R_next", _p),
+        ("capture_y", _p), ("capture_x", _p), ("capture_v", _p), ("capture_u", _p),
+        ("capture_d", _p),
+    ]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_decompose = _sig("externd_decompose", ctypes.c_int,
+                  [_p, _i64, _i64, _f32, _f32, _i32, _i32, _p, _p, _p, _p, _p, ctypes.POINTER(_Opts)])
+_energy = _sig("externd_energy", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _p, _p])
+_reconstruct = _sig("externd_reconstruct", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p])
+_rank = _sig("externd_rank", ctypes.c_int64, [_i64, _i64, _f32])
+_block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
+_resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
+_ternarize = _sig("externd_ternarize", ctypes.c_int, [_p, _i64, _f32, _p, _p, _p])
+_gemv_t = _sig("externd_gemv_t", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
+_gemv_n = _sig("externd_gemv_n", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
+_deflate = _sig("externd_deflate", ctypes.c_int, [_p, _i64, _i64, _p, _p, _f32, _p])
+_status_string = _sig("externd_status_string", ctypes.c_char_p, [ctypes.c_int])
+_last_error = _sig("externd_last_error", ctypes.c_char_p, [])
+
+# Every exported symbol of the C ABI, for load checks.
+ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_rank",
+               "externd_block_width", "externd_resident_fits", "externd_ternarize",
+               "externd_gemv_t", "externd_gemv_n", "externd_deflate",
+               "externd_status_string", "externd_last_error")
+
+
+class ExterndError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"{_status_string(status).decode()}: {_last_error().decode()}")
+
+
+def _check(status):
+    if status != 0:
+        raise ExterndError(status)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rank(m, n, mu):
+    """k = mu * min(m, n) rounded half away from zero (§2.1)."""
+    return int(_rank(m, n, mu))
+
+
+def block_width(m, n, block):
+    """Block width used for a request (§2.4); 1 means sequential."""
+    return int(_block_width(m, n, block))
+
+
+def resident_fits(m, n):
+    return bool(_resident_fits(m, n))
+
+
+class Decomposition:
+    """Device outputs of one decomposition.
+
+    B2: (k, ceil(m/16)) int32 words of 2-bit codes (component-major B),
+    C2: (k, ceil(n/16)) int32 words (rows of C), D: (k,) float32,
+    energy: (1,) float64, trace / stats: optional device tensors,
+    capture: dict of captured tensors when requested.
+    """
+
+    def __init__(self, m, n, k, B2, C2, D, energy, trace, stats, capture):
+        self.m, self.n, self.k = m, n, k
+        self.B2, self.C2, self.D, self.energy = B2, C2, D, energy
+        self.trace, self.stats, self.capture = trace, stats, capture
+
+    def stat(self, name):
+        return int(self.stats[STAT[name]].item())
+
+
+def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
+              capture=None, out=None):
+    """Run externd_decompose on the current stream.
+
+    A: (m, n) float32 CUDA tensor.  capture: component index whose
+    intermediate vectors and residuals are recorded (sequential path only).
+    out: optional Decomposition whose B2/C2/D/energy buffers are reused.
+    """
+    _need(A, torch.float32, "A")
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D")
+    m, n = A.shape
+    k = rank(m, n, mu)
+    if k < 0:
+        raise ValueError("bad mu")
+    dev = A.device
+    if out is not None and (out.m, out.n, out.k) == (m, n, k):
+        B2, C2, D, E = out.B2, out.C2, out.D, out.energy
+    else:
+        B2 = torch.empty((k, (m + 15) // 16), dtype=torch.int32, device=dev)
+        C2 = torch.empty((k, (n + 15) // 16), dtype=torch.int32, device=dev)
+        D = torch.empty((k,), dtype=torch.float32, device=dev)
+        E = torch.empty((1,), dtype=torch.float64, device=dev)
+    b = block_width(m, n, block)
+    ntrace = ((k + b - 1) // b) if b > 1 else k
+    tr = torch.empty((max(ntrace, 1),), dtype=torch.float64, device=dev) if trace else None
+    st = torch.zeros((STATS_LEN,), dtype=torch.int64, device=dev) if stats else None
+    opts = _Opts()
+    opts.struct_size = ctypes.sizeof(_Opts)
+    opts.seed = seed
+    opts.mode = mode
+    opts.trace = _ptr(tr)
+    opts.stats = _ptr(st)
+    opts.capture_component = -1
+    cap = None
+    if capture is not None:
+        cap = {
+            "R": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "Rcol": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "R_next": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "y": torch.empty((iters, n), dtype=torch.float32, device=dev),
+            "x": torch.empty((iters, m), dtype=torch.float32, device=dev),
+            "v": torch.empty((iters, n), dtype=torch.int8, device=dev),
+            "u": torch.empty((iters, m), dtype=torch.int8, device=dev),
+            "d": torch.empty((1,), dtype=torch.float32, device=dev),
+        }
+        opts.capture_component = int(capture)
+        opts.capture_R = _ptr(cap["R"])
+        opts.capture_Rcol = _ptr(cap["Rcol"])
+        opts.capture_R_next = _ptr(cap["R_next"])
+        opts.capture_y = _ptr(cap["y"])
+        opts.capture_x = _ptr(cap["x"])
+        opts.capture_v = _ptr(cap["v"])
+        opts.capture_u = _ptr(cap["u"])
+        opts.capture_d = _ptr(cap["d"])
+    _check(_decompose(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
+                      _ptr(D), _ptr(E), ctypes.byref(opts)))
+    return Decomposition(m, n, k, B2, C2, D, E, tr, st, cap)
+
+
+def energy(A, B2, C2, D):
+    """E = 1 - ||A - B diag(D) C||^2 / ||A||^2 from 2-bit factors, fp64 (§2.1)."""
+    _need(A, torch.float32, "A")
+    m, n = A.shape
+    k = D.numel()
+    E = torch.empty((1,), dtype=torch.float64, device=A.device)
+    _check(_energy(_ptr(A), m, n, _ptr(B2), _ptr(C2), _ptr(D), k, _stream(), _ptr(E)))
+    return E
+
+
+def reconstruct(B2, C2, D, m, n):
+    """A_hat = B diag(D) C as an (m, n) float32 tensor (§2.1)."""
+    k = D.numel()
+    out = torch.empty((m, n), dtype=torch.float32, device=D.device)
+    _check(_reconstruct(_ptr(B2), _ptr(C2), _ptr(D), m, n, k, _stream(), _ptr(out)))
+    return out
+
+
+def ternarize(x, tau):
+    """T_tau of a float32 vector (§2.2) -> (2-bit code words, nnz)."""
+    _need(x, torch.float32, "x")
+    N = x.numel()
+    codes = torch.empty(((N + 15) // 16,), dtype=torch.int32, device=x.device)
+    nnz = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _check(_ternarize(_ptr(x), N, tau, _stream(), _ptr(codes), _ptr(nnz)))
+    return codes, nnz
+
+
+def gemv_t(R, u_codes):
+    """y = R^T u with u as 2-bit codes (§2.3)."""
+    _need(R, torch.float32, "R")
+    m, n = R.shape
+    y = torch.empty((n,), dtype=torch.float32, device=R.device)
+    _check(_gemv_t(_ptr(R), m, n, _ptr(u_codes), _stream(), _ptr(y)))
+    return y
+
+
+def gemv_n(R, v_codes):
+    """x = R v with v as 2-bit codes (§2.3)."""
+    _need(R, torch.float32, "R")
+    m, n = R.shape
+    x = torch.empty((m,), dtype=torch.float32, device=R.device)
+    _check(_gemv_n(_ptr(R), m, n, _ptr(v_codes), _stream(), _ptr(x)))
+    return x
+
+
+def deflate(R, u_codes, v_codes, d):
+    """R <- R - d u v^T in place (§2.3 step 3)."""
+    _need(R, torch.float32, "R")
+    m, n = R.shape
+    _check(_deflate(_ptr(R), m, n, _ptr(u_codes), _ptr(v_codes), float(d), _stream()))
+    return R

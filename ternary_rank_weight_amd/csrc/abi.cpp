@@ -1,0 +1,306 @@
+// C ABI of the ExTernD library: argument validation, device checks,
+// workspace management and dispatch to the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/externd.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(EXTERND_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+struct DeviceInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+// Current device must be a gfx950; remembers its compute-unit count.
+int check_device(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(EXTERND_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.gfx950) return fail(EXTERND_EUNSUPPORTED, "device %d is not gfx950", dev);
+  if (cus) *cus = d.cus;
+  return EXTERND_OK;
+}
+
+bool bad_size(int64_t m, int64_t n) {
+  return m <= 0 || n <= 0 || m > (int64_t(1) << 31) - 1 || n > (int64_t(1) << 31) - 1 ||
+         m * n > (int64_t(1) << 40);
+}
+
+// Stream-ordered workspace: allocated on the stream, freed on the stream.
+struct Workspace {
+  void* ptr = nullptr;
+  hipStream_t s = nullptr;
+  ~Workspace() {
+    if (ptr) (void)hipFreeAsync(ptr, s);
+  }
+};
+
+int alloc_ws(Workspace& w, size_t bytes, hipStream_t s) {
+  w.s = s;
+  hipError_t e = hipMallocAsync(&w.ptr, bytes, s);
+  if (e != hipSuccess) {
+    w.ptr = nullptr;
+    return fail(EXTERND_ENOMEM, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
+  }
+  return EXTERND_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* externd_status_string(int status) {
+  switch (status) {
+    case EXTERND_OK: return "ok";
+    case EXTERND_EINVAL: return "invalid argument";
+    case EXTERND_ENOMEM: return "out of device memory";
+    case EXTERND_EHIP: return "HIP runtime error";
+    case EXTERND_EUNSUPPORTED: return "unsupported device or shape";
+    default: return "unknown status";
+  }
+}
+
+const char* externd_last_error(void) { return g_last_error.c_str(); }
+
+int64_t externd_rank(int64_t m, int64_t n, float mu) {
+  if (m <= 0 || n <= 0 || !std::isfinite(mu) || mu < 0.f) return -1;
+  const double v = (double)mu * (double)(m < n ? m : n);
+  if (v > 9.0e15) return -1;
+  const double whole = std::floor(v);
+  return (int64_t)whole + ((v - whole) >= 0.5 ? 1 : 0);
+}
+
+int32_t externd_block_width(int64_t m, int64_t n, int32_t block) {
+  if (block <= 1 || m <= 0 || n <= 0) return 1;
+  const int64_t cap = (m < n ? m : n) / 8;
+  const int64_t b = block < cap ? block : cap;
+  return b >= 2 ? (int32_t)b : 1;
+}
+
+int32_t externd_resident_fits(int64_t m, int64_t n) {
+  int cus = 0;
+  if (check_device(&cus) != EXTERND_OK) return 0;
+  return externd::resident_fits(m, n, cus) ? 1 : 0;
+}
+
+int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau, int32_t iters,
+                      int32_t block, void* stream, uint32_t* B2, uint32_t* C2, float* D,
+                      double* energy, const externd_opts* opts) {
+  if (!A || !energy) return fail(EXTERND_EINVAL, "null A or energy pointer");
+  if (bad_size(m, n)) return fail(EXTERND_EINVAL, "bad shape %lld x %lld", (long long)m, (long long)n);
+  if (!std::isfinite(mu) || mu <= 0.f) return fail(EXTERND_EINVAL, "mu must be finite and > 0");
+  if (!std::isfinite(tau) || tau < 0.f) return fail(EXTERND_EINVAL, "tau must be finite and >= 0");
+  if (iters < 1) return fail(EXTERND_EINVAL, "iters must be >= 1");
+  const int64_t k = externd_rank(m, n, mu);
+  if (k < 0 || k > (int64_t(1) << 31)) return fail(EXTERND_EINVAL, "rank out of range");
+  if (k > 0 && (!B2 || !C2 || !D)) return fail(EXTERND_EINVAL, "null factor pointer");
+  externd_opts o{};
+  o.struct_size = sizeof(externd_opts);
+  o.mode = EXTERND_MODE_AUTO;
+  o.capture_component = -1;
+  if (opts) {
+    if (opts->struct_size != sizeof(externd_opts))
+      return fail(EXTERND_EINVAL, "externd_opts.struct_size %u != %zu", opts->struct_size,
+                  sizeof(externd_opts));
+    o = *opts;
+  }
+  if (o.mode < -1 || o.mode > 1) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
+  int cus = 0;
+  int st = check_device(&cus);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int b = externd_block_width(m, n, block);
+
+  if (b > 1) {
+    externd::BlockArgs ba{};
+    ba.A = A;
+    ba.m = m;
+    ba.n = n;
+    ba.k = k;
+    ba.b = b;
+    ba.tau = tau;
+    ba.iters = iters;
+    ba.seed = o.seed;
+    ba.B2 = B2;
+    ba.C2 = C2;
+    ba.D = D;
+    ba.energy = energy;
+    ba.trace = o.trace;
+    ba.stats = reinterpret_cast<long long*>(o.stats);
+    Workspace w;
+    if ((st = alloc_ws(w, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
+    hipError_t e = externd::run_block(ba, w.ptr, s);
+    if (e != hipSuccess) return hip_fail(e, "block decomposition");
+    return EXTERND_OK;
+  }
+
+  externd::SeqArgs sa{};
+  sa.A = A;
+  sa.m = m;
+  sa.n = n;
+  sa.k = k;
+  sa.tau = tau;
+  sa.iters = iters;
+  sa.seed = o.seed;
+  sa.B2 = B2;
+  sa.C2 = C2;
+  sa.D = D;
+  sa.energy = energy;
+  sa.trace = o.trace;
+  sa.stats = reinterpret_cast<long long*>(o.stats);
+  sa.capture_component = o.capture_component;
+  if (o.capture_component >= 0) {
+    if (o.capture_component >= k) return fail(EXTERND_EINVAL, "capture_component >= k");
+    sa.capture_R = o.capture_R;
+    sa.capture_Rcol = o.capture_Rcol;
+    sa.capture_R_next = o.capture_R_next;
+    sa.capture_y = o.capture_y;
+    sa.capture_x = o.capture_x;
+    sa.capture_v = o.capture_v;
+    sa.capture_u = o.capture_u;
+    sa.capture_d = o.capture_d;
+  } else {
+    sa.capture_component = -1;
+  }
+  const bool fits = externd::resident_fits(m, n, cus);
+  int mode = o.mode;
+  if (mode == EXTERND_MODE_AUTO) mode = fits ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
+  if (mode == EXTERND_MODE_RESIDENT && !fits)
+    return fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel", (long long)m,
+                (long long)n);
+  Workspace w;
+  hipError_t e;
+  if (mode == EXTERND_MODE_RESIDENT) {
+    if ((st = alloc_ws(w, externd::resident_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+    int grid = 0;
+    e = externd::run_resident_seq(sa, w.ptr, cus, s, &grid);
+    if (e != hipSuccess) return hip_fail(e, "resident decomposition");
+  } else {
+    if ((st = alloc_ws(w, externd::stream_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+    e = externd::run_stream_seq(sa, w.ptr, s);
+    if (e != hipSuccess) return hip_fail(e, "streaming decomposition");
+  }
+  return EXTERND_OK;
+}
+
+int externd_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2, const uint32_t* C2,
+                   const float* D, int64_t k, void* stream, double* energy) {
+  if (!A || !energy) return fail(EXTERND_EINVAL, "null A or energy pointer");
+  if (bad_size(m, n) || k < 0) return fail(EXTERND_EINVAL, "bad shape");
+  if (k > 0 && (!B2 || !C2 || !D)) return fail(EXTERND_EINVAL, "null factor pointer");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w;
+  if ((st = alloc_ws(w, externd::energy_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+  hipError_t e = externd::run_energy(A, m, n, B2, C2, D, k, energy, w.ptr, s);
+  if (e != hipSuccess) return hip_fail(e, "energy");
+  return EXTERND_OK;
+}
+
+int externd_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m,
+                        int64_t n, int64_t k, void* stream, float* A_hat) {
+  if (!A_hat) return fail(EXTERND_EINVAL, "null output pointer");
+  if (bad_size(m, n) || k < 0) return fail(EXTERND_EINVAL, "bad shape");
+  if (k > 0 && (!B2 || !C2 || !D)) return fail(EXTERND_EINVAL, "null factor pointer");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipError_t e = externd::run_reconstruct(B2, C2, D, m, n, k, A_hat, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reconstruct");
+  return EXTERND_OK;
+}
+
+int externd_ternarize(const float* x, int64_t N, float tau, void* stream, uint32_t* codes,
+                      int32_t* nnz) {
+  if (!x || !codes) return fail(EXTERND_EINVAL, "null pointer");
+  if (N <= 0 || N > (int64_t(1) << 31) - 1) return fail(EXTERND_EINVAL, "bad length");
+  if (!std::isfinite(tau) || tau < 0.f) return fail(EXTERND_EINVAL, "tau must be finite and >= 0");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipError_t e = externd::launch_ternarize(x, N, tau, codes, nnz, nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ternarize");
+  return EXTERND_OK;
+}
+
+int externd_gemv_t(const float* R, int64_t m, int64_t n, const uint32_t* u_codes, void* stream,
+                   float* y) {
+  if (!R || !u_codes || !y) return fail(EXTERND_EINVAL, "null pointer");
+  if (bad_size(m, n)) return fail(EXTERND_EINVAL, "bad shape");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w;
+  if ((st = alloc_ws(w, sizeof(float) * (size_t)(externd::gemv_t_chunks(m) * n) + 256, s)) != EXTERND_OK) return st;
+  hipError_t e = externd::launch_gemv_t(const_cast<float*>(R), m, n, u_codes,
+                                        static_cast<float*>(w.ptr), y, nullptr, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "gemv_t");
+  return EXTERND_OK;
+}
+
+int externd_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, void* stream,
+                   float* x) {
+  if (!R || !v_codes || !x) return fail(EXTERND_EINVAL, "null pointer");
+  if (bad_size(m, n)) return fail(EXTERND_EINVAL, "bad shape");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipError_t e = externd::launch_gemv_n(R, m, n, v_codes, x, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemv_n");
+  return EXTERND_OK;
+}
+
+int externd_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
+                    const uint32_t* v_codes, float d, void* stream) {
+  if (!R || !u_codes || !v_codes) return fail(EXTERND_EINVAL, "null pointer");
+  if (bad_size(m, n)) return fail(EXTERND_EINVAL, "bad shape");
+  if (!std::isfinite(d)) return fail(EXTERND_EINVAL, "d must be finite");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w;
+  if ((st = alloc_ws(w, 256, s)) != EXTERND_OK) return st;
+  float* dptr = static_cast<float*>(w.ptr);
+  hipError_t e = externd::launch_fill_f32(dptr, 1, d, s);
+  if (e == hipSuccess) e = externd::launch_deflate(R, m, n, u_codes, v_codes, dptr, s);
+  if (e != hipSuccess) return hip_fail(e, "deflate");
+  return EXTERND_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal interface between the C ABI and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <algorithm>
+
+#include "../../include/externd.h"
+
+namespace externd {
+
+// Arguments of one sequential decomposition (device pointers).
+struct SeqArgs {
+  const float* A;
+  int64_t m, n, k;
+  float tau;
+  int iters;
+  uint64_t seed;
+  uint32_t* B2;
+  uint32_t* C2;
+  float* D;
+  double* energy;
+  double* trace;
+  long long* stats;
+  int64_t capture_component;
+  float* capture_R;
+  float* capture_Rcol;
+  float* capture_R_next;
+  float* capture_y;
+  float* capture_x;
+  int8_t* capture_v;
+  int8_t* capture_u;
+  float* capture_d;
+};
+
+// Arguments of one block-mode decomposition.
+struct BlockArgs {
+  const float* A;
+  int64_t m, n, k;
+  int b;
+  float tau;
+  int iters;
+  uint64_t seed;
+  uint32_t* B2;
+  uint32_t* C2;
+  float* D;
+  double* energy;
+  double* trace;
+  long long* stats;
+};
+
+// streaming sequential path and single-step kernels (seq_stream.hip)
+size_t stream_workspace_bytes(int64_t m, int64_t n);
+hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s);
+int64_t gemv_t_chunks(int64_t m);
+hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
+                            long long* fallbacks, hipStream_t s);
+hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
+                         float* y, const float* dprev, const uint32_t* uprev,
+                         const uint32_t* vprev, hipStream_t s);
+hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
+                         hipStream_t s);
+hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
+                          const uint32_t* v_codes, const float* dptr, hipStream_t s);
+hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
+                        double* out, long long* nonfinite, hipStream_t s);
+hipError_t launch_energy_finish(const double* a2, const double* r2, const long long* nonfinite,
+                                double* energy, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t v, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t count, float v, hipStream_t s);
+hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t s);
+hipError_t launch_copy_f32(const float* a, float* b, int64_t count, hipStream_t s);
+
+// resident sequential path (seq_resident.hip)
+bool resident_fits(int64_t m, int64_t n, int num_cus);
+size_t resident_workspace_bytes(int64_t m, int64_t n);
+hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s, int* grid_out);
+
+// block path (block.hip)
+size_t block_workspace_bytes(int64_t m, int64_t n, int b);
+hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s);
+
+// energy / reconstruction from 2-bit factors (factors.hip)
+size_t energy_workspace_bytes(int64_t m, int64_t n);
+hipError_t run_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2, const uint32_t* C2,
+                      const float* D, int64_t k, double* energy, void* ws, hipStream_t s);
+hipError_t run_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m,
+                           int64_t n, int64_t k, float* out, hipStream_t s);
+
+}  // namespace externd

@@ -1,0 +1,600 @@
+// Resident sequential path: one cooperative kernel runs every component and
+// every alternating iteration of the greedy ALS (ExTernD §2.3) with the
+// residual R held on chip for the whole decomposition.
+//
+// Layout.  Workgroup g of G owns
+//   * the row block  rows [g*RB, g*RB+RB) x all n columns, kept in LDS, used
+//     for x = R v (each workgroup finishes its rows' dot products locally);
+//   * the column block  all m rows x columns [g*CB, g*CB+CB), kept in VGPRs,
+//     used for y = R^T u (each workgroup finishes its columns locally).
+// Both copies receive the same fp32 deflation R <- fl32(R - d u v^T), so they
+// stay bit-identical.  Thread t holds entries of index t + T*j of every
+// length-m or length-n vector, which is exactly the set of rows (column copy)
+// and columns (row copy) it multiplies, so the vectors never move through LDS.
+//
+// Exchange.  After a half-step every workgroup publishes its finished outputs
+// (RB values of x or CB values of y) as 64-bit words {round:32 | value:32}
+// written with agent-scope atomic stores, then reads all m (or n) words with
+// agent-scope atomic loads until each carries the current round.  Value and
+// round share one atomic word, so no fence or grid barrier is needed; one
+// exchange per half-step, two per ALS iteration.  Every workgroup then holds
+// the whole vector and applies T_tau (§2.2) redundantly and identically.
+//
+// Termination.  Every wait is bounded: a workgroup that waits too long sets a
+// device error flag and the whole grid returns; the host reports EHIP.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace externd {
+
+namespace {
+
+constexpr unsigned kSpinLimit = 1u << 21;
+
+struct ResArgs {
+  const float* A;
+  int m, n, k;
+  float tau;
+  int iters;
+  uint64_t seed;
+  int G, RB, CB;
+  uint32_t* B2;
+  uint32_t* C2;
+  float* D;
+  double* trace;
+  long long* stats;            // EXTERND_STATS_LEN, written by workgroup 0
+  const double* a2;            // ||A||^2
+  const long long* nonfinite;  // count of non-finite entries of A
+  unsigned long long* yslot;   // n words
+  unsigned long long* xslot;   // m words
+  unsigned* err;
+  double* r2_partial;          // G fp64
+  int64_t cap_i;
+  float* cap_R;
+  float* cap_Rcol;
+  float* cap_R_next;
+  float* cap_y;
+  float* cap_x;
+  int8_t* cap_v;
+  int8_t* cap_u;
+  float* cap_d;
+};
+
+__device__ inline unsigned long long ll_pack(unsigned round, float v) {
+  return ((unsigned long long)round << 32) | (unsigned long long)__float_as_uint(v);
+}
+
+// Sum acc[l] over the T threads of the block for l < L.  Result lands in
+// out[l] (LDS).  Fixed order: 16 lanes per output each add 16 strided
+// entries, then an xor butterfly over the 16 lanes.
+template <int T, int L>
+__device__ inline void reduce_outputs(const float (&acc)[L], float* red, float* out) {
+  constexpr int P = 16;           // lanes per output
+  constexpr int S = T + 1;        // padded stride against bank conflicts
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int l = 0; l < L; ++l) red[l * S + t] = acc[l];
+  __syncthreads();
+  for (int base = 0; base < L; base += T / P) {
+    const int l = base + t / P;
+    const int part = t % P;
+    float s = 0.f;
+    if (l < L) {
+#pragma unroll
+      for (int q = 0; q < T / P; ++q) s += red[l * S + part + P * q];
+    }
+#pragma unroll
+    for (int off = P / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    if (l < L && part == 0) out[l] = s;
+  }
+  __syncthreads();
+}
+
+// Read the n (or m) published words of the current round into val[j] for
+// index t + T*j.  Returns false if a wait ran out.
+template <int T, int K>
+__device__ inline bool gather(const unsigned long long* slot, int N, unsigned round, float (&val)[K],
+                              const unsigned* err) {
+  const int t = threadIdx.x;
+  unsigned long long w[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int idx = t + T * j;
+    w[j] = idx < N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : ll_pack(round, 0.f);
+  }
+  unsigned spins = 0;
+  bool ok = true;
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < K; ++j) all = all && (unsigned)(w[j] >> 32) == round;
+    if (all) break;
+    if (++spins > kSpinLimit) { ok = false; break; }
+    if ((spins & 255u) == 0 &&
+        __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+      ok = false;
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int idx = t + T * j;
+      if ((unsigned)(w[j] >> 32) != round)
+        w[j] = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) val[j] = ok ? __uint_as_float((unsigned)w[j]) : 0.f;
+  return ok;
+}
+
+// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond N).
+// Identical in every workgroup.  Writes T_tau(x) to out in the same layout and
+// returns this thread's count of nonzeros.
+template <int T, int K>
+__device__ inline int ternarize_dist(const float (&val)[K], int N, float tau, float (&out)[K],
+                                     double* scratch, int& fallback) {
+  const int t = threadIdx.x;
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(val[j]));
+  const float M = block_max<T>(mx, reinterpret_cast<float*>(scratch));
+  int cnt = 0;
+  if (M == 0.f) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
+    fallback = 1;
+    return t == 0 ? 1 : 0;
+  }
+  const int s = fixed_point_shift(M, N);
+  long long q = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) q += fixed_point_q(val[j], s);
+  const long long Q = block_sum<T>(q, reinterpret_cast<long long*>(scratch));
+  const double thr = fixed_point_threshold(Q, s, tau, N);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const bool keep = (double)fabsf(val[j]) > thr;
+    out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
+    cnt += keep ? 1 : 0;
+  }
+  fallback = 0;
+  if ((double)M > thr) return cnt;
+  int first = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int idx = t + T * j;
+    if (idx < N && fabsf(val[j]) == M) first = min(first, idx);
+  }
+  const int pick = block_min_i<T>(first, reinterpret_cast<int*>(scratch));
+  cnt = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (t + T * j == pick) {
+      out[j] = val[j] > 0.f ? 1.f : -1.f;
+      cnt = 1;
+    }
+  }
+  fallback = 1;
+  return cnt;
+}
+
+// Copy this workgroup's rows of the row-resident residual to dst (m x n).
+template <int T, int KR, int LR>
+__device__ void dump_rows(const float* rrow, const ResArgs& a, int row0, float* dst) {
+  const int t = threadIdx.x;
+  for (int l = 0; l < LR; ++l)
+    for (int j = 0; j < KR; ++j) {
+      const int row = row0 + l, col = t + T * j;
+      if (l < a.RB && row < a.m && col < a.n) dst[(int64_t)row * a.n + col] = rrow[(l * KR + j) * T + t];
+    }
+}
+
+// CAP selects the test-capture instantiation: the same arithmetic plus stores
+// of one component's intermediate vectors and residuals.
+template <int T, int KR, int LR, int KC, int LC, bool CAP>
+__global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
+  constexpr int LMAX = LR > LC ? LR : LC;
+  __shared__ float rrow[LR * KR * T];
+  __shared__ float red[LMAX * (T + 1)];
+  __shared__ float outv[LMAX];
+  __shared__ float u_own[LR];
+  __shared__ float v_own[LC];
+  __shared__ uint8_t ub[KC * T];
+  __shared__ uint8_t vb[KR * T];
+  __shared__ double scratch[T / kWave];
+  __shared__ int s_bad;
+
+  const int t = threadIdx.x;
+  const int g = blockIdx.x;
+  const int m = a.m, n = a.n;
+  const int row0 = g * a.RB, col0 = g * a.CB;
+  const int wm = (m + 15) / 16, wn = (n + 15) / 16;
+  if (t == 0) s_bad = 0;
+
+  if (*a.nonfinite > 0) {
+    // Nothing sensible can be computed: zero this workgroup's share of the outputs.
+    for (int64_t w = (int64_t)g * T + t; w < (int64_t)a.k * wm; w += (int64_t)a.G * T) a.B2[w] = 0u;
+    for (int64_t w = (int64_t)g * T + t; w < (int64_t)a.k * wn; w += (int64_t)a.G * T) a.C2[w] = 0u;
+    for (int64_t w = (int64_t)g * T + t; w < a.k; w += (int64_t)a.G * T) a.D[w] = 0.f;
+    if (t == 0) a.r2_partial[g] = 0.0;
+    return;
+  }
+
+  // R <- A into both copies.
+#pragma unroll
+  for (int l = 0; l < LR; ++l) {
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int row = row0 + l, col = t + T * j;
+      rrow[(l * KR + j) * T + t] =
+          (l < a.RB && row < m && col < n) ? a.A[(int64_t)row * n + col] : 0.f;
+    }
+  }
+  float rc[LC][KC];
+#pragma unroll
+  for (int l = 0; l < LC; ++l) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int col = col0 + l, row = t + T * j;
+      rc[l][j] = (l < a.CB && col < n && row < m) ? a.A[(int64_t)row * n + col] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  float u[KC], v[KR];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) u[j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < KR; ++j) v[j] = 0.f;
+  float d32 = 0.f;
+  unsigned ry = 0, rx = 0;
+  long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
+  double trace_state = *a.a2;
+  const bool capturer = (g == 0);
+
+  for (int i = 0; i <= a.k; ++i) {
+    // ---- deflate component i-1 out of both copies (§2.3 step 3) ----
+    if (i > 0) {
+#pragma unroll
+      for (int l = 0; l < LR; ++l) {
+        const float ul = (l < a.RB && row0 + l < m) ? u_own[l] : 0.f;
+        if (ul != 0.f) {
+          float* rp = rrow + l * KR * T + t;
+#pragma unroll
+          for (int j = 0; j < KR; ++j) rp[j * T] = fmaf(-d32, ul * v[j], rp[j * T]);
+        }
+      }
+#pragma unroll
+      for (int l = 0; l < LC; ++l) {
+        const float vl = (l < a.CB && col0 + l < n) ? v_own[l] : 0.f;
+        if (vl != 0.f) {
+#pragma unroll
+          for (int j = 0; j < KC; ++j) rc[l][j] = fmaf(-d32, u[j] * vl, rc[l][j]);
+        }
+      }
+      if constexpr (CAP) {
+        if (i - 1 == a.cap_i && a.cap_R_next) dump_rows<T, KR, LR>(rrow, a, row0, a.cap_R_next);
+      }
+    }
+    if (i == a.k) break;
+    if (CAP && i == a.cap_i) {
+      if (a.cap_R) dump_rows<T, KR, LR>(rrow, a, row0, a.cap_R);
+      if (a.cap_Rcol) {
+        for (int l = 0; l < LC; ++l)
+#pragma unroll
+          for (int j = 0; j < KC; ++j) {
+            const int col = col0 + l, row = t + T * j;
+            if (l < a.CB && col < n && row < m) a.cap_Rcol[(int64_t)row * n + col] = rc[l][j];
+          }
+      }
+    }
+
+    // ---- starting vector u0 of component i ----
+    {
+      const uint64_t base = start_base(a.seed, (uint64_t)i);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int row = t + T * j;
+        u[j] = row < m ? start_sign(base, (uint64_t)row) : 0.f;
+      }
+    }
+
+    double cpart = 0.0;  // u . x of the last iteration, this thread's share
+    for (int it = 0; it < a.iters; ++it) {
+      const bool cap = CAP && (i == a.cap_i) && capturer;
+      // ---- y = R^T u on the column copy; v = T_tau(y) ----
+      {
+        float acc[LC];
+#pragma unroll
+        for (int l = 0; l < LC; ++l) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < KC; ++j) s = fmaf(u[j], rc[l][j], s);
+          acc[l] = s;
+        }
+        reduce_outputs<T, LC>(acc, red, outv);
+        ++ry;
+        if (t < a.CB && col0 + t < n)
+          __hip_atomic_store(a.yslot + col0 + t, ll_pack(ry, outv[t]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        float y[KR];
+        if (!gather<T, KR>(a.yslot, n, ry, y, a.err)) s_bad = 1;
+        __syncthreads();
+        if (s_bad) {
+          if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+        int fb;
+        st_nnz_v += ternarize_dist<T, KR>(y, n, a.tau, v, scratch, fb);
+        st_fb += fb;
+        if (cap) {
+          for (int j = 0; j < KR; ++j) {
+            const int col = t + T * j;
+            if (col < n) {
+              if (a.cap_y) a.cap_y[(int64_t)it * n + col] = y[j];
+              if (a.cap_v) a.cap_v[(int64_t)it * n + col] = (int8_t)v[j];
+            }
+          }
+        }
+      }
+      // ---- x = R v on the row copy; u = T_tau(x) ----
+      {
+        float acc[LR];
+#pragma unroll
+        for (int l = 0; l < LR; ++l) {
+          const float* rp = rrow + l * KR * T + t;
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < KR; ++j) s = fmaf(v[j], rp[j * T], s);
+          acc[l] = s;
+        }
+        reduce_outputs<T, LR>(acc, red, outv);
+        ++rx;
+        if (t < a.RB && row0 + t < m)
+          __hip_atomic_store(a.xslot + row0 + t, ll_pack(rx, outv[t]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        float x[KC];
+        if (!gather<T, KC>(a.xslot, m, rx, x, a.err)) s_bad = 1;
+        __syncthreads();
+        if (s_bad) {
+          if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+        int fb;
+        st_nnz_u += ternarize_dist<T, KC>(x, m, a.tau, u, scratch, fb);
+        st_fb += fb;
+        if (it == a.iters - 1) {
+#pragma unroll
+          for (int j = 0; j < KC; ++j) cpart += (double)u[j] * (double)x[j];
+        }
+        if (cap) {
+          for (int j = 0; j < KC; ++j) {
+            const int row = t + T * j;
+            if (row < m) {
+              if (a.cap_x) a.cap_x[(int64_t)it * m + row] = x[j];
+              if (a.cap_u) a.cap_u[(int64_t)it * m + row] = (int8_t)u[j];
+            }
+          }
+        }
+      }
+    }
+
+    // ---- scale d = u.x / (nnz_u nnz_v) (§2.3 step 2) ----
+    long long counts = 0;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) counts += (u[j] != 0.f) ? (1ll << 32) : 0ll;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) counts += (v[j] != 0.f) ? 1ll : 0ll;
+    const double c = block_sum<T>(cpart, scratch);
+    const long long cnts = block_sum<T>(counts, reinterpret_cast<long long*>(scratch));
+    const double nu = (double)(cnts >> 32), nv = (double)(cnts & 0xffffffffll);
+    const double den = nu * nv;
+    d32 = (float)(c / den);
+    trace_state -= c * c / den;
+    st_b += (long long)nu;
+    st_c += (long long)nv;
+    if (g == 0 && t == 0) {
+      a.D[i] = d32;
+      if (a.trace) a.trace[i] = trace_state;
+      if (CAP && i == a.cap_i && a.cap_d) *a.cap_d = d32;
+    }
+
+    // ---- own-row u and own-column v for the deflation; codes for B2 / C2 ----
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int row = t + T * j;
+      ub[row] = (uint8_t)code_of(u[j]);
+      if (row >= row0 && row < row0 + a.RB && row < m) u_own[row - row0] = u[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int col = t + T * j;
+      vb[col] = (uint8_t)code_of(v[j]);
+      if (col >= col0 && col < col0 + a.CB && col < n) v_own[col - col0] = v[j];
+    }
+    __syncthreads();
+    for (int w = g + a.G * t; w < wm; w += a.G * T) {
+      uint32_t word = 0;
+      for (int e = 0; e < 16; ++e)
+        if (w * 16 + e < m) word |= (uint32_t)ub[w * 16 + e] << (2 * e);
+      a.B2[(int64_t)i * wm + w] = word;
+    }
+    for (int w = g + a.G * t; w < wn; w += a.G * T) {
+      uint32_t word = 0;
+      for (int e = 0; e < 16; ++e)
+        if (w * 16 + e < n) word |= (uint32_t)vb[w * 16 + e] << (2 * e);
+      a.C2[(int64_t)i * wn + w] = word;
+    }
+    __syncthreads();
+  }
+
+  // ---- ||R||^2 of the final residual over this workgroup's rows ----
+  double r2 = 0.0;
+#pragma unroll
+  for (int l = 0; l < LR; ++l)
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const double r = (double)rrow[(l * KR + j) * T + t];
+      r2 += r * r;
+    }
+  r2 = block_sum<T>(r2, scratch);
+  if (t == 0) a.r2_partial[g] = r2;
+
+  if (g == 0 && a.stats) {
+    const long long s_u = block_sum<T>(st_nnz_u, reinterpret_cast<long long*>(scratch));
+    const long long s_v = block_sum<T>(st_nnz_v, reinterpret_cast<long long*>(scratch));
+    if (t == 0) {
+      a.stats[EXTERND_STAT_SUM_NNZ_U] = s_u;
+      a.stats[EXTERND_STAT_SUM_NNZ_V] = s_v;
+      a.stats[EXTERND_STAT_NNZ_B] = st_b;
+      a.stats[EXTERND_STAT_NNZ_C] = st_c;
+      a.stats[EXTERND_STAT_FALLBACKS] = st_fb;
+      a.stats[EXTERND_STAT_MODE] = EXTERND_MODE_RESIDENT;
+      a.stats[EXTERND_STAT_GRID] = a.G;
+    }
+  }
+}
+
+__global__ void k_fill_u64(unsigned long long* p, int64_t count) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = 0ull;
+}
+__global__ void k_resident_finish(const double* __restrict__ r2_partial, int G,
+                                  const double* __restrict__ a2, const long long* __restrict__ nonfinite,
+                                  const unsigned* __restrict__ err, double* __restrict__ energy,
+                                  long long* __restrict__ stats) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double r2 = 0.0;
+  for (int g = 0; g < G; ++g) r2 += r2_partial[g];
+  double e;
+  if (*nonfinite > 0 || *err != 0u) e = __longlong_as_double(0x7ff8000000000000ll);
+  else if (*a2 == 0.0) e = 1.0;
+  else e = 1.0 - r2 / *a2;
+  *energy = e;
+  if (stats) {
+    stats[EXTERND_STAT_NONFINITE] = *nonfinite;
+    stats[EXTERND_STAT_TIMEOUTS] = *err;
+  }
+}
+
+// Tile instantiations: (threads, columns per thread KR, rows per workgroup LR,
+// rows per thread KC, columns per workgroup LC).
+struct Tile {
+  int KR, LR, KC, LC;
+};
+constexpr int kResT = 512;
+constexpr Tile kTiles[] = {{1, 32, 1, 32}, {2, 16, 2, 16}, {5, 10, 5, 10}};
+
+inline int tile_grid(const Tile& tl, int64_t m, int64_t n) {
+  const int64_t g1 = (m + tl.LR - 1) / tl.LR, g2 = (n + tl.LC - 1) / tl.LC;
+  return (int)std::max<int64_t>(1, std::max(g1, g2));
+}
+inline bool tile_fits(const Tile& tl, int64_t m, int64_t n, int num_cus) {
+  if (m < 1 || n < 1) return false;
+  if ((m + kResT - 1) / kResT > tl.KC || (n + kResT - 1) / kResT > tl.KR) return false;
+  return tile_grid(tl, m, n) <= std::min(256, num_cus);
+}
+inline int pick_tile(int64_t m, int64_t n, int num_cus) {
+  for (int i = 0; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); ++i)
+    if (tile_fits(kTiles[i], m, n, num_cus)) return i;
+  return -1;
+}
+
+template <int KR, int LR, int KC, int LC>
+hipError_t launch_tile(ResArgs& ra, hipStream_t s) {
+  void* args[] = {&ra};
+  void* fn = ra.cap_i >= 0 ? reinterpret_cast<void*>(&k_seq_resident<kResT, KR, LR, KC, LC, true>)
+                           : reinterpret_cast<void*>(&k_seq_resident<kResT, KR, LR, KC, LC, false>);
+  return hipLaunchCooperativeKernel(fn, dim3(ra.G), dim3(kResT), args, 0, s);
+}
+
+}  // namespace
+
+bool resident_fits(int64_t m, int64_t n, int num_cus) {
+  if (m > (1 << 30) || n > (1 << 30)) return false;
+  return pick_tile(m, n, num_cus) >= 0;
+}
+
+size_t resident_workspace_bytes(int64_t m, int64_t n) {
+  return sizeof(unsigned long long) * (size_t)(m + n) + sizeof(double) * (256 + 4096 + 8) +
+         sizeof(long long) * 8 + sizeof(unsigned) * 64 + 256 * 8;
+}
+
+static inline char* align256(char* p) {
+  return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
+}
+
+hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s, int* grid_out) {
+  const int ti = pick_tile(a.m, a.n, num_cus);
+  if (ti < 0) return hipErrorInvalidValue;
+  const Tile tl = kTiles[ti];
+  char* p = align256(static_cast<char*>(ws));
+  unsigned long long* yslot = reinterpret_cast<unsigned long long*>(p);
+  p = align256(p + sizeof(unsigned long long) * a.n);
+  unsigned long long* xslot = reinterpret_cast<unsigned long long*>(p);
+  p = align256(p + sizeof(unsigned long long) * a.m);
+  double* r2p = reinterpret_cast<double*>(p);
+  p = align256(p + sizeof(double) * 256);
+  double* npart = reinterpret_cast<double*>(p);
+  p = align256(p + sizeof(double) * 4096);
+  double* a2 = reinterpret_cast<double*>(p);
+  p = align256(p + sizeof(double) * 8);
+  long long* nonfinite = reinterpret_cast<long long*>(p);
+  p = align256(p + sizeof(long long) * 8);
+  unsigned* err = reinterpret_cast<unsigned*>(p);
+
+  hipError_t e;
+  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)a.n);
+  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)a.m);
+  if ((e = launch_fill_i64(nonfinite, 1, 0, s)) != hipSuccess) return e;
+  if ((e = launch_fill_u32(err, 1, 0u, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, a.m * a.n, npart, 4096, a2, nonfinite, s)) != hipSuccess) return e;
+  if (a.stats && (e = launch_fill_i64(a.stats, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
+
+  ResArgs ra{};
+  ra.A = a.A;
+  ra.m = (int)a.m;
+  ra.n = (int)a.n;
+  ra.k = (int)a.k;
+  ra.tau = a.tau;
+  ra.iters = a.iters;
+  ra.seed = a.seed;
+  ra.G = tile_grid(tl, a.m, a.n);
+  ra.RB = (int)((a.m + ra.G - 1) / ra.G);
+  ra.CB = (int)((a.n + ra.G - 1) / ra.G);
+  ra.B2 = a.B2;
+  ra.C2 = a.C2;
+  ra.D = a.D;
+  ra.trace = a.trace;
+  ra.stats = a.stats;
+  ra.a2 = a2;
+  ra.nonfinite = nonfinite;
+  ra.yslot = yslot;
+  ra.xslot = xslot;
+  ra.err = err;
+  ra.r2_partial = r2p;
+  ra.cap_i = a.capture_component;
+  ra.cap_R = a.capture_R;
+  ra.cap_Rcol = a.capture_Rcol;
+  ra.cap_R_next = a.capture_R_next;
+  ra.cap_y = a.capture_y;
+  ra.cap_x = a.capture_x;
+  ra.cap_v = a.capture_v;
+  ra.cap_u = a.capture_u;
+  ra.cap_d = a.capture_d;
+  if (grid_out) *grid_out = ra.G;
+
+  switch (ti) {
+    case 0: e = launch_tile<1, 32, 1, 32>(ra, s); break;
+    case 1: e = launch_tile<2, 16, 2, 16>(ra, s); break;
+    default: e = launch_tile<5, 10, 5, 10>(ra, s); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_resident_finish, dim3(1), dim3(64), 0, s, r2p, ra.G, a2, nonfinite, err,
+                     a.energy, a.stats);
+  return hipGetLastError();
+}
+
+}  // namespace externd

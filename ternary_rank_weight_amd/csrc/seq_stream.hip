@@ -1,0 +1,477 @@
+// Streaming sequential path: R lives in device memory and every ALS half-step
+// is one or two kernels.  Also provides the single-step entry points.
+//
+// ExTernD §2.3: for each component, alternate v = T_tau(R^T u), u = T_tau(R v)
+// for `iters` iterations, take d = u^T R v / (|u|^2 |v|^2) and deflate
+// R <- R - d u v^T.  T_tau is the mean-threshold ternarizer of §2.2.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace externd {
+
+// ---------------------------------------------------------------------------
+// T_tau on one vector by a single workgroup (§2.2).  Writes 2-bit codes of
+// all ceil(N/16) words, the nonzero count, and bumps *fallbacks when the
+// single-largest-entry rule fires.
+// ---------------------------------------------------------------------------
+constexpr int kTernT = 1024;
+
+__global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ x, int64_t N,
+                                                      float tau, uint32_t* __restrict__ codes,
+                                                      int32_t* __restrict__ nnz_out,
+                                                      long long* __restrict__ fallbacks) {
+  __shared__ double scratch[kTernT / kWave];
+  float* fs = reinterpret_cast<float*>(scratch);
+  int* is = reinterpret_cast<int*>(scratch);
+  long long* ls = reinterpret_cast<long long*>(scratch);
+  const int tid = threadIdx.x;
+  float mx = 0.f;
+  for (int64_t j = tid; j < N; j += kTernT) mx = fmaxf(mx, fabsf(x[j]));
+  const float M = block_max<kTernT>(mx, fs);
+  const int64_t words = (N + 15) / 16;
+  if (M == 0.f) {
+    for (int64_t w = tid; w < words; w += kTernT) codes[w] = (w == 0) ? 1u : 0u;
+    if (tid == 0) {
+      if (nnz_out) *nnz_out = 1;
+      if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
+    }
+    return;
+  }
+  const int s = fixed_point_shift(M, N);
+  long long q = 0;
+  for (int64_t j = tid; j < N; j += kTernT) q += fixed_point_q(x[j], s);
+  const long long Q = block_sum<kTernT>(q, ls);
+  const double thr = fixed_point_threshold(Q, s, tau, N);
+  int cnt = 0;
+  for (int64_t w = tid; w < words; w += kTernT) {
+    uint32_t word = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t j = w * 16 + e;
+      if (j < N) {
+        const float v = x[j];
+        if ((double)fabsf(v) > thr) {
+          word |= code_of(v) << (2 * e);
+          ++cnt;
+        }
+      }
+    }
+    codes[w] = word;
+  }
+  if ((double)M > thr) {
+    const int total = block_sum<kTernT>(cnt, is);
+    if (tid == 0 && nnz_out) *nnz_out = total;
+    return;
+  }
+  // Nothing passed: keep the smallest index holding the largest magnitude.
+  int first = INT32_MAX;
+  for (int64_t j = tid; j < N; j += kTernT)
+    if (fabsf(x[j]) == M) { first = (int)j; break; }
+  const int idx = block_min_i<kTernT>(first, is);
+  __syncthreads();  // codes words written above are visible block-wide below
+  if (tid == 0) {
+    codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
+    if (nnz_out) *nnz_out = 1;
+    if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// y = R^T u, in two deterministic stages: per row-chunk partial sums, then a
+// fixed-order sum over chunks.  Rows with u_r = 0 are skipped (never read).
+// When `dprev` is non-null the previous component is first deflated out of
+// every row the chunk touches (§2.3 step 3 fused into the next step 1):
+// R_rc <- fl32(R_rc - d u'_r v'_c), written back.
+// ---------------------------------------------------------------------------
+constexpr int kGtT = 256;     // columns per workgroup
+constexpr int kGtRows = 64;   // rows per chunk
+
+__global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
+    float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
+    float* __restrict__ partial, const float* __restrict__ dprev,
+    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev) {
+  const int64_t c = (int64_t)blockIdx.x * kGtT + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * kGtRows;
+  const int64_t r1 = min(m, r0 + kGtRows);
+  float acc = 0.f;
+  const bool incol = c < n;
+  if (dprev) {
+    const float d = *dprev;
+    const float vc = incol ? code_at(vprev, c) : 0.f;
+    for (int64_t r = r0; r < r1; ++r) {
+      const float ur = code_at(u_codes, r);
+      const float up = code_at(uprev, r);
+      if (up != 0.f && incol) {
+        float val = R[r * n + c];
+        if (vc != 0.f) {
+          val = fmaf(-d, up * vc, val);
+          R[r * n + c] = val;
+        }
+        acc = fmaf(ur, val, acc);
+      } else if (ur != 0.f && incol) {
+        acc = fmaf(ur, R[r * n + c], acc);
+      }
+    }
+  } else {
+    for (int64_t r = r0; r < r1; ++r) {
+      const float ur = code_at(u_codes, r);
+      if (ur != 0.f && incol) acc = fmaf(ur, R[r * n + c], acc);
+    }
+  }
+  if (incol) partial[(int64_t)blockIdx.y * n + c] = acc;
+}
+
+__global__ void k_sum_chunks(const float* __restrict__ partial, int64_t chunks, int64_t n,
+                             float* __restrict__ y) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  float acc = 0.f;
+  for (int64_t q = 0; q < chunks; ++q) acc += partial[q * n + c];
+  y[c] = acc;
+}
+
+// x = R v: one wave per row, lanes stride the row; masked add/sub as FMA with
+// v in {-1, 0, 1} (exact products).
+constexpr int kGnT = 256;
+
+__global__ __launch_bounds__(kGnT) void k_gemv_n(const float* __restrict__ R, int64_t m,
+                                                 int64_t n, const uint32_t* __restrict__ v_codes,
+                                                 float* __restrict__ x) {
+  const int64_t row = (int64_t)blockIdx.x * (kGnT / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= m) return;
+  const float* rp = R + row * n;
+  float acc = 0.f;
+  for (int64_t c = lane; c < n; c += kWave) acc = fmaf(code_at(v_codes, c), rp[c], acc);
+  acc = wave_sum(acc);
+  if (lane == 0) x[row] = acc;
+}
+
+// R <- R - d u v^T (one rounding per entry), d read from device memory.
+__global__ void k_deflate(float* __restrict__ R, int64_t m, int64_t n,
+                          const uint32_t* __restrict__ u_codes,
+                          const uint32_t* __restrict__ v_codes, const float* __restrict__ dptr) {
+  const int64_t r = blockIdx.y;
+  const float ur = code_at(u_codes, r);
+  if (ur == 0.f) return;
+  const float d = *dptr;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const float vc = code_at(v_codes, c);
+    if (vc != 0.f) R[r * n + c] = fmaf(-d, ur * vc, R[r * n + c]);
+  }
+}
+
+// u0 of component `comp` as 2-bit codes.
+__global__ void k_start_codes(uint64_t seed, int64_t comp, int64_t m, uint32_t* __restrict__ codes) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w * 16 >= m) return;
+  const uint64_t base = start_base(seed, (uint64_t)comp);
+  uint32_t word = 0;
+  for (int e = 0; e < 16; ++e) {
+    const int64_t r = w * 16 + e;
+    if (r < m) word |= code_of(start_sign(base, (uint64_t)r)) << (2 * e);
+  }
+  codes[w] = word;
+}
+
+// d = (u . x) / (nnz_u nnz_v) in fp64, stored as fp32 in D[i]; trace update.
+__global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, int64_t m,
+                                                  const uint32_t* __restrict__ u_codes,
+                                                  const int32_t* __restrict__ nnz_u,
+                                                  const int32_t* __restrict__ nnz_v,
+                                                  float* __restrict__ D, int64_t i,
+                                                  double* __restrict__ trace_state,
+                                                  double* __restrict__ trace,
+                                                  long long* __restrict__ stats) {
+  __shared__ double scratch[kTernT / kWave];
+  double acc = 0.0;
+  for (int64_t r = threadIdx.x; r < m; r += kTernT) acc += (double)code_at(u_codes, r) * (double)x[r];
+  const double c = block_sum<kTernT>(acc, scratch);
+  if (threadIdx.x == 0) {
+    const double den = (double)(*nnz_u) * (double)(*nnz_v);
+    const double d = c / den;
+    D[i] = (float)d;
+    const double t = trace_state[0] - c * c / den;
+    trace_state[0] = t;
+    if (trace) trace[i] = t;
+    if (stats) {
+      stats[EXTERND_STAT_NNZ_B] += *nnz_u;
+      stats[EXTERND_STAT_NNZ_C] += *nnz_v;
+    }
+  }
+}
+
+__global__ void k_add_stat(long long* stats, int idx, const int32_t* val) {
+  if (threadIdx.x == 0 && stats) stats[idx] += *val;
+}
+
+// ---------------------------------------------------------------------------
+// Squared Frobenius norm with a fixed reduction order, plus a count of
+// non-finite entries.  Stage 1 writes one fp64 partial per workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kNormT = 256;
+
+__global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restrict__ A, int64_t total,
+                                                          int64_t per_block,
+                                                          double* __restrict__ partial,
+                                                          long long* __restrict__ nonfinite) {
+  __shared__ double scratch[kNormT / kWave];
+  const int64_t b0 = (int64_t)blockIdx.x * per_block;
+  const int64_t b1 = min(total, b0 + per_block);
+  double acc = 0.0;
+  long long bad = 0;
+  for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
+    const float v = A[j];
+    if (!isfinite(v)) ++bad;
+    acc += (double)v * (double)v;
+  }
+  const double s = block_sum<kNormT>(acc, scratch);
+  if (threadIdx.x == 0) partial[blockIdx.x] = s;
+  if (nonfinite) {
+    const long long b = block_sum<kNormT>(bad, reinterpret_cast<long long*>(scratch));
+    if (threadIdx.x == 0 && b) atomicAdd(reinterpret_cast<unsigned long long*>(nonfinite), (unsigned long long)b);
+  }
+}
+
+__global__ void k_sum_partials(const double* __restrict__ partial, int64_t count,
+                               double* __restrict__ out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double s = 0.0;
+  for (int64_t i = 0; i < count; ++i) s += partial[i];
+  *out = s;
+}
+
+// energy = 1 - r2 / a2 (1 when a2 = 0, NaN when A had non-finite entries).
+__global__ void k_energy_finish(const double* __restrict__ a2, const double* __restrict__ r2,
+                                const long long* __restrict__ nonfinite, double* __restrict__ energy,
+                                double* __restrict__ trace_state) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double e;
+  if (nonfinite && *nonfinite > 0) e = __longlong_as_double(0x7ff8000000000000ll);
+  else if (*a2 == 0.0) e = 1.0;
+  else e = 1.0 - *r2 / *a2;
+  *energy = e;
+  (void)trace_state;
+}
+
+__global__ void k_fill_u32(uint32_t* p, int64_t count, uint32_t v) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = v;
+}
+__global__ void k_fill_f32(float* p, int64_t count, float v) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = v;
+}
+__global__ void k_fill_i64(long long* p, int64_t count, long long v) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = v;
+}
+__global__ void k_copy_f32(const float* __restrict__ a, float* __restrict__ b, int64_t count) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    b[j] = a[j];
+}
+__global__ void k_copy_i64(const long long* __restrict__ a, long long* __restrict__ b, int64_t count) {
+  for (int64_t j = threadIdx.x; j < count; j += blockDim.x) b[j] = a[j];
+}
+__global__ void k_set_f64(double* p, const double* src) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = *src;
+}
+__global__ void k_codes_to_i8(const uint32_t* __restrict__ codes, int64_t N, int8_t* __restrict__ out) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < N) out[j] = (int8_t)code_at(codes, j);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid1(int64_t count, int threads, int64_t cap = 4096) {
+  int64_t g = (count + threads - 1) / threads;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t v, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid1(count, 256)), dim3(256), 0, s, p, count, v);
+  return hipGetLastError();
+}
+hipError_t launch_fill_f32(float* p, int64_t count, float v, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid1(count, 256)), dim3(256), 0, s, p, count, v);
+  return hipGetLastError();
+}
+hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i64, dim3(grid1(count, 256)), dim3(256), 0, s, p, count, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
+                            long long* fallbacks, hipStream_t s) {
+  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks);
+  return hipGetLastError();
+}
+
+int64_t gemv_t_chunks(int64_t m) { return (m + kGtRows - 1) / kGtRows; }
+
+hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
+                         float* y, const float* dprev, const uint32_t* uprev,
+                         const uint32_t* vprev, hipStream_t s) {
+  const int64_t chunks = gemv_t_chunks(m);
+  dim3 grid((unsigned)((n + kGtT - 1) / kGtT), (unsigned)chunks);
+  hipLaunchKernelGGL(k_gemv_t_partial, grid, dim3(kGtT), 0, s, R, m, n, u_codes, partial, dprev,
+                     uprev, vprev);
+  hipLaunchKernelGGL(k_sum_chunks, dim3(grid1(n, 256, 1 << 30)), dim3(256), 0, s, partial, chunks,
+                     n, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
+                         hipStream_t s) {
+  const unsigned rows_per_block = kGnT / kWave;
+  dim3 grid((unsigned)((m + rows_per_block - 1) / rows_per_block));
+  hipLaunchKernelGGL(k_gemv_n, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
+                          const uint32_t* v_codes, const float* dptr, hipStream_t s) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  dim3 grid((unsigned)std::min<int64_t>((n + 255) / 256, 64), (unsigned)m);
+  hipLaunchKernelGGL(k_deflate, grid, dim3(256), 0, s, R, m, n, u_codes, v_codes, dptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
+                        double* out, long long* nonfinite, hipStream_t s) {
+  int64_t blocks = std::min<int64_t>(partial_cap, std::max<int64_t>(1, (total + 65535) / 65536));
+  const int64_t per_block = (total + blocks - 1) / blocks;
+  if (total == 0) blocks = 1;
+  hipLaunchKernelGGL(k_norm2_partial, dim3((unsigned)blocks), dim3(kNormT), 0, s, A, total,
+                     std::max<int64_t>(per_block, 1), partial, nonfinite);
+  hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(64), 0, s, partial, blocks, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_energy_finish(const double* a2, const double* r2, const long long* nonfinite,
+                                double* energy, hipStream_t s) {
+  hipLaunchKernelGGL(k_energy_finish, dim3(1), dim3(64), 0, s, a2, r2, nonfinite, energy, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* a, float* b, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_f32, dim3(grid1(count, 256)), dim3(256), 0, s, a, b, count);
+  return hipGetLastError();
+}
+
+// Whole streaming decomposition (sequential mode).  ws must hold
+// stream_workspace_bytes(m, n) bytes.
+size_t stream_workspace_bytes(int64_t m, int64_t n) {
+  const int64_t chunks = gemv_t_chunks(m);
+  size_t b = 0;
+  b += sizeof(float) * (size_t)(m * n);          // R
+  b += sizeof(float) * (size_t)(chunks * n);     // partials
+  b += sizeof(float) * (size_t)(m + n);          // x, y
+  b += sizeof(double) * 4096;                    // norm partials
+  b += sizeof(double) * 8;                       // a2, r2, trace state
+  b += sizeof(int32_t) * 8;                      // nnz counters
+  b += sizeof(long long) * EXTERND_STATS_LEN;    // local stats
+  b += 64 * 8;                                   // alignment slack
+  return b;
+}
+
+static inline char* align_up(char* p, size_t a) {
+  return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + a - 1) & ~(uintptr_t)(a - 1));
+}
+
+hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
+  const int64_t m = a.m, n = a.n, k = a.k;
+  const int64_t wm = (m + 15) / 16, wn = (n + 15) / 16;
+  const int64_t chunks = gemv_t_chunks(m);
+  char* p = align_up(static_cast<char*>(ws), 256);
+  float* R = reinterpret_cast<float*>(p); p = align_up(p + sizeof(float) * m * n, 256);
+  float* partial = reinterpret_cast<float*>(p); p = align_up(p + sizeof(float) * chunks * n, 256);
+  float* x = reinterpret_cast<float*>(p); p = align_up(p + sizeof(float) * m, 256);
+  float* y = reinterpret_cast<float*>(p); p = align_up(p + sizeof(float) * n, 256);
+  double* npart = reinterpret_cast<double*>(p); p = align_up(p + sizeof(double) * 4096, 256);
+  double* a2 = reinterpret_cast<double*>(p);
+  double* r2 = a2 + 1;
+  double* tstate = a2 + 2;
+  p = align_up(p + sizeof(double) * 8, 256);
+  int32_t* nnz_u = reinterpret_cast<int32_t*>(p);
+  int32_t* nnz_v = nnz_u + 1;
+  p = align_up(p + sizeof(int32_t) * 8, 256);
+  long long* st = reinterpret_cast<long long*>(p);
+
+  hipError_t e;
+  if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_set_f64, dim3(1), dim3(1), 0, s, tstate, a2);
+  if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
+
+  // The deflation of component i-1 is normally fused into component i's first
+  // R^T u step; `pending` says whether it still has to be applied.
+  bool pending = false;
+  for (int64_t i = 0; i < k; ++i) {
+    uint32_t* ub = a.B2 + i * wm;
+    uint32_t* vc = a.C2 + i * wn;
+    const uint32_t* ub_prev = i > 0 ? a.B2 + (i - 1) * wm : nullptr;
+    const uint32_t* vc_prev = i > 0 ? a.C2 + (i - 1) * wn : nullptr;
+    hipLaunchKernelGGL(k_start_codes, dim3(grid1(wm, 256, 1 << 30)), dim3(256), 0, s, a.seed, i, m, ub);
+    const bool cap = (i == a.capture_component);
+    if (cap && (a.capture_R || a.capture_Rcol)) {
+      if (pending) {
+        if ((e = launch_deflate(R, m, n, ub_prev, vc_prev, a.D + i - 1, s)) != hipSuccess) return e;
+        pending = false;
+      }
+      if (a.capture_R && (e = launch_copy_f32(R, a.capture_R, m * n, s)) != hipSuccess) return e;
+      if (a.capture_Rcol && (e = launch_copy_f32(R, a.capture_Rcol, m * n, s)) != hipSuccess) return e;
+    }
+    for (int t = 0; t < a.iters; ++t) {
+      const bool fuse = (t == 0 && pending);
+      e = launch_gemv_t(R, m, n, ub, partial, y, fuse ? a.D + i - 1 : nullptr,
+                        fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s);
+      if (e != hipSuccess) return e;
+      pending = false;
+      if ((e = launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_V, nnz_v);
+      if ((e = launch_gemv_n(R, m, n, vc, x, s)) != hipSuccess) return e;
+      if ((e = launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_U, nnz_u);
+      if (cap) {
+        if (a.capture_y && (e = launch_copy_f32(y, a.capture_y + (int64_t)t * n, n, s)) != hipSuccess) return e;
+        if (a.capture_x && (e = launch_copy_f32(x, a.capture_x + (int64_t)t * m, m, s)) != hipSuccess) return e;
+        if (a.capture_v) hipLaunchKernelGGL(k_codes_to_i8, dim3(grid1(n, 256, 1 << 30)), dim3(256), 0, s, vc, n, a.capture_v + (int64_t)t * n);
+        if (a.capture_u) hipLaunchKernelGGL(k_codes_to_i8, dim3(grid1(m, 256, 1 << 30)), dim3(256), 0, s, ub, m, a.capture_u + (int64_t)t * m);
+      }
+    }
+    hipLaunchKernelGGL(k_scale, dim3(1), dim3(kTernT), 0, s, x, m, ub, nnz_u, nnz_v, a.D, i, tstate,
+                       a.trace, st);
+    pending = true;
+    if (cap && a.capture_d && (e = launch_copy_f32(a.D + i, a.capture_d, 1, s)) != hipSuccess) return e;
+    if (cap && a.capture_R_next) {
+      if ((e = launch_deflate(R, m, n, ub, vc, a.D + i, s)) != hipSuccess) return e;
+      pending = false;
+      if ((e = launch_copy_f32(R, a.capture_R_next, m * n, s)) != hipSuccess) return e;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // Deflate the last component and measure the final residual.
+  if (pending) {
+    if ((e = launch_deflate(R, m, n, a.B2 + (k - 1) * wm, a.C2 + (k - 1) * wn, a.D + k - 1, s)) != hipSuccess) return e;
+  }
+  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
+  if ((e = launch_energy_finish(a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, s)) != hipSuccess) return e;
+  if (a.stats) {
+    hipLaunchKernelGGL(k_copy_i64, dim3(1), dim3(64), 0, s, st, a.stats, (int64_t)EXTERND_STATS_LEN);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace externd

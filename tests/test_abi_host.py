@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/externd.h, and rejects bad arguments on the host before
+any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "externd.h")
+LIB = os.path.join(ROOT, "ternary_rank_weight_amd", "libexternd.so")
+
+
+@pytest.fixture(scope="module")
+def clib():
+    if not os.path.exists(LIB):
+        from ternary_rank_weight_amd import build as b
+        b.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(externd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("externd_decompose", "externd_energy", "externd_reconstruct"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(clib):
+    for name in declared_functions():
+        assert hasattr(clib, name), name
+
+
+def test_binding_lists_every_symbol():
+    import ternary_rank_weight_amd as trw
+    assert set(trw.ABI_SYMBOLS) == set(declared_functions())
+
+
+def test_rank_and_block_width(clib):
+    import ternary_rank_weight_amd as trw
+    assert trw.rank(2560, 2560, 2.0) == 5120
+    assert trw.rank(9728, 2560, 3.0) == 7680
+    assert trw.rank(4096, 4096, 3.5) == 14336
+    assert trw.rank(10, 3, 0.5) == 2
+    assert trw.rank(0, 3, 1.0) == -1
+    assert trw.block_width(2560, 2560, 64) == 64
+    assert trw.block_width(1024, 2560, 256) == 128
+    assert trw.block_width(15, 100, 64) == 1
+    assert trw.block_width(100, 100, 0) == 1
+
+
+def test_rank_matches_oracle():
+    import oracle
+    import ternary_rank_weight_amd as trw
+    for (m, n, mu) in [(256, 256, 2.0), (100, 37, 1.3), (7, 9, 0.5), (4096, 2560, 2.5), (3, 3, 0.1667)]:
+        assert trw.rank(m, n, mu) == oracle.rank_for(m, n, mu)
+    for (m, n, b) in [(2560, 2560, 64), (1024, 2560, 256), (15, 100, 64), (64, 64, 1), (64, 64, 9)]:
+        assert trw.block_width(m, n, b) == oracle.block_width(m, n, b)
+
+
+def _decompose_args(clib):
+    f = clib.externd_decompose
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return f
+
+
+@pytest.mark.parametrize("case", [
+    dict(A=0), dict(energy=0), dict(m=0), dict(n=-3), dict(mu=0.0), dict(mu=float("nan")),
+    dict(mu=float("inf")), dict(tau=-0.1), dict(tau=float("nan")), dict(iters=0),
+    dict(B2=0), dict(D=0),
+])
+def test_decompose_rejects_bad_arguments(clib, case):
+    f = _decompose_args(clib)
+    fake = 0x1000  # never dereferenced: validation fails first
+    a = dict(A=fake, m=16, n=16, mu=1.0, tau=0.7, iters=15, block=0, B2=fake, C2=fake, D=fake,
+             energy=fake)
+    a.update(case)
+    st = f(a["A"] or None, a["m"], a["n"], a["mu"], a["tau"], a["iters"], a["block"], None,
+           a["B2"] or None, a["C2"] or None, a["D"] or None, a["energy"] or None, None)
+    assert st == 1  # EXTERND_EINVAL
+    clib.externd_last_error.restype = ctypes.c_char_p
+    assert clib.externd_last_error()
+
+
+def test_status_strings(clib):
+    clib.externd_status_string.restype = ctypes.c_char_p
+    assert clib.externd_status_string(0) == b"ok"
+    assert clib.externd_status_string(1) == b"invalid argument"
+    assert clib.externd_status_string(99) == b"unknown status"
+
+
+def test_single_step_entry_points_validate(clib):
+    fake = ctypes.c_void_p(0x1000)
+    clib.externd_ternarize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert clib.externd_ternarize(fake, 0, ctypes.c_float(0.7), None, fake, None) == 1
+    assert clib.externd_ternarize(None, 10, ctypes.c_float(0.7), None, fake, None) == 1
+    clib.externd_deflate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+    assert clib.externd_deflate(fake, 4, 4, fake, fake, ctypes.c_float(float("nan")), None) == 1
+    clib.externd_energy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    assert clib.externd_energy(fake, 4, 4, None, None, None, 3, None, fake) == 1
