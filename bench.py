@@ -1,0 +1,184 @@
+"""Benchmark: ExTernD decomposition of a 2560 x 2560 LLM-shaped matrix on one GPU.
+
+One step = the whole hot path over one synthetic input: the sequential
+greedy ALS (k = 5120 components) followed by the block ALS (b = 64, 80
+blocks) of the same matrix, mu = 2, tau = 0.7, 15 iterations.  Prints one
+JSON line (rank 0) with components/s, the sequential kernel's roofline
+figures and the fp64 oracle's rate on a bounded sample as a CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--modes seq,block]
+                    [--cpu-sample N | --no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and MFMA), published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--modes", default="seq,block")
+    ap.add_argument("--cpu-sample", type=int, default=200,
+                    help="components of the oracle's sequential run timed as the CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2])
+    return ap.parse_args()
+
+
+def seq_alg_bytes(m, n, k, iters, sum_nnz_u):
+    """Bytes a streaming implementation must move for the sequential path.
+
+    Per component: the first R^T u0 pass reads all of R (u0 is dense); each
+    of the `iters` R v passes reads all of R; the R^T u passes of iterations
+    2..iters read only rows where u is nonzero; the deflation rewrites the
+    rows where the final u is nonzero.  That is 4 n ((iters+1) m + sum_t nnz(u_t))
+    with t over the iters u vectors of the component.
+    """
+    return 4.0 * n * ((iters + 1) * m * k + sum_nnz_u)
+
+
+def block_alg_flops(m, n, k, b, iters):
+    """Dense-contraction flops of the block path: per block, 2*iters
+    contractions R^T U / R V of 2 m n b flops plus one rank-b deflation."""
+    nblocks = (k + b - 1) // b
+    return 2.0 * m * n * b * (2 * iters + 1) * nblocks
+
+
+def cpu_baseline(A, c, sample):
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    t = time.perf_counter()
+    r = oracle.decompose_seq(A, c["mu"], c["tau"], c["iters"], c["seed"], k=sample)
+    dt = time.perf_counter() - t
+    return {"value": round(sample / dt, 3), "unit": "components/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {sample} of {oracle.rank_for(A.shape[0], A.shape[1], c['mu'])} "
+                      f"components of the sequential decomposition of the same "
+                      f"{A.shape[0]}x{A.shape[1]} matrix, fp64 numpy oracle "
+                      f"({dt:.1f} s, E after sample {r.E:.4f})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synthetic
+    import ternary_rank_weight_amd as trw
+
+    torch.cuda.set_device(0)
+    c = synthetic.CONFIGS[args.config]
+    A = synthetic.config_matrix(args.config)
+    m, n = A.shape
+    Ad = torch.from_numpy(A).cuda()
+    k = trw.rank(m, n, c["mu"])
+    modes = [s for s in args.modes.split(",") if s]
+    block = c.get("block", 64) or 64
+    b = trw.block_width(m, n, block)
+
+    outs = {}
+
+    def run_step(record):
+        ev = {}
+        for md in modes:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if md == "seq":
+                outs[md] = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], 0, c["seed"], stats=True,
+                                         out=outs.get(md))
+            else:
+                outs[md] = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], block, c["seed"],
+                                         stats=True, out=outs.get(md))
+            e1.record()
+            ev[md] = (e0, e1)
+        if record is not None:
+            record.append(ev)
+
+    for _ in range(args.warmup):
+        run_step(None)
+    torch.cuda.synchronize()
+    records = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(records)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_mode = {}
+    for md in modes:
+        ms = [r[md][0].elapsed_time(r[md][1]) for r in records]
+        res = outs[md]
+        E = float(res.energy.item())
+        per_mode[md] = {"ms": float(np.mean(ms)), "ms_min": float(np.min(ms)), "k": k,
+                        "components_per_s": k / (float(np.mean(ms)) / 1e3), "energy": E,
+                        "stats": {kk: res.stat(kk) for kk in trw.STAT}}
+    step_ms = sum(per_mode[md]["ms"] for md in modes)
+    total_components = k * len(modes)
+    value = total_components / (step_ms / 1e3)
+
+    roofline = None
+    if "seq" in per_mode:
+        s = per_mode["seq"]
+        alg = seq_alg_bytes(m, n, k, c["iters"], s["stats"]["sum_nnz_u"])
+        achieved = alg / (s["ms"] / 1e3) / 1e9
+        s["alg_bytes"] = alg
+        s["gbps"] = achieved
+        roofline = {"bound": "hbm", "kernel": "k_seq_resident", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None}
+    if "block" in per_mode:
+        bm = per_mode["block"]
+        fl = block_alg_flops(m, n, k, b, c["iters"])
+        bm["alg_tflops"] = fl / (bm["ms"] / 1e3) / 1e12
+        bm["b"] = b
+
+    cpu = None
+    if not args.no_cpu and args.cpu_sample > 0:
+        cpu = cpu_baseline(A, c, min(args.cpu_sample, k))
+
+    line = {
+        "metric": "ALS components/sec + achieved HBM GB/s at 2560x2560 mu=2 tau=0.7; energy E",
+        "value": round(value, 2),
+        "unit": "components/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{m}x{n} LLM-shaped synthetic matrix (Student-t(5), bf16-rounded, "
+                               f"lognormal rows, 16 outlier columns), mu={c['mu']}, tau={c['tau']}, "
+                               f"{c['iters']} iterations, k={k}; step = " + " + ".join(
+                                   {"seq": "sequential greedy ALS",
+                                    "block": f"block ALS b={b}"}[md] for md in modes),
+                   "m": m, "n": n, "mu": c["mu"], "tau": c["tau"], "iters": c["iters"], "k": k,
+                   "block": b, "seed": c["seed"]},
+        "modes": {md: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
+                       for kk, vv in per_mode[md].items()} for md in modes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,12 +17,13 @@ Readings where the page leaves a step open (each one is listed in the design doc):
 * The mean is computed in a fixed, order-free way so that two
   implementations fed identical inputs agree bit for bit:
     M = max |x_j|; e = frexp exponent of M (M < 2**e);
-    L = ceil(log2 N); s = 62 - e - L;
-    q_j = floor(|x_j| * 2**s) as an exact int64 (each < 2**(62-L));
-    S = float64(sum_j q_j) * 2**-s  (one round-to-nearest-even conversion);
+    L = ceil(log2 N); s = 52 - e - L;
+    q_j = floor(|x_j| * 2**s) as an exact integer (each < 2**(52-L));
+    S = (sum_j q_j) * 2**-s, the sum being < 2**52 and hence exact in float64;
     thr = (tau * S) / N in float64, tau being the float32 value widened.
-  Every q_j is exact and the int64 sum cannot overflow, so S differs from the
-  exact sum of |x| by less than N * 2**-s, i.e. by a relative 2**-47 or so.
+  Every q_j and their sum are exact, so S is below the exact sum of |x| by
+  less than N * 2**-s and thr below tau * mean|x| by less than tau * 2**-s
+  (a relative 2**-37 or so for a typical vector).
 * The comparison is strict (|x_i| > thr); sign(0) = 0.
 * Fallback when nothing passes: the smallest index i with |x_i| = M keeps
   its sign. When x is identically zero the result is +1 at index 0.
@@ -53,11 +54,11 @@ def mean_abs_threshold(x, tau):
     if big == 0.0:
         return 0.0, 0.0
     _, e = math.frexp(big)          # big = f * 2**e with 0.5 <= f < 1
-    s = 62 - e - _ceil_log2(n)
+    s = 52 - e - _ceil_log2(n)
     q = np.floor(np.ldexp(a, s)).astype(np.int64)
     total = int(q.sum(dtype=np.int64))
-    assert 0 <= total < (1 << 62)
-    S = math.ldexp(float(total), -s)  # Python int -> float rounds to nearest even
+    assert 0 <= total < (1 << 52)
+    S = math.ldexp(float(total), -s)  # exact: total < 2**52
     tau64 = float(np.float32(tau))
     thr = (tau64 * S) / float(n)
     return thr, big

@@ -31,27 +31,34 @@ __host__ __device__ inline float start_sign(uint64_t base, uint64_t row) {
 
 // ---------------------------------------------------------------------------
 // Fixed-point mean used by T_tau (§2.2).  For a vector of length N with
-// maximum magnitude M > 0: e = frexp exponent of M, s = 62 - e - ceil(log2 N),
-// q_j = floor(|x_j| * 2^s) (exact int64), S = double(sum q) * 2^-s and
-// thr = (tau * S) / N.  Integer sums make the result independent of the
-// reduction order and of the grid shape.
+// maximum magnitude M > 0: e = frexp exponent of M, s = 52 - e - ceil(log2 N),
+// q_j = floor(|x_j| * 2^s) (exact integers, each < 2^(52 - ceil(log2 N))),
+// S = (sum q) * 2^-s (the sum is < 2^52, so exact in fp64 in any order) and
+// thr = (tau * S) / N.  The result does not depend on the reduction order
+// or on the grid shape.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int ceil_log2_i64(int64_t n) {
-  int l = 0;
-  while ((int64_t(1) << l) < n) ++l;
-  return l;
-}
-__device__ inline int fixed_point_shift(float maxabs, int64_t N) {
+__device__ inline int ceil_log2_i32(int n) { return n <= 1 ? 0 : 32 - __clz(n - 1); }
+__device__ inline int fixed_point_shift(float maxabs, int N) {
   int e;
   (void)frexp((double)maxabs, &e);
-  return 62 - e - ceil_log2_i64(N);
+  return 52 - e - ceil_log2_i32(N);
 }
-__device__ inline int64_t fixed_point_q(float v, int s) {
-  return (int64_t)floor(ldexp((double)fabsf(v), s));
+// q = floor(|x| * 2^s), an exact integer held in an fp64 (|x| * 2^s is exact
+// and below 2^52).
+__device__ inline double fixed_point_q(float absval, int s) {
+  return floor(ldexp((double)absval, s));
 }
-__device__ inline double fixed_point_threshold(int64_t qsum, int s, float tau, int64_t N) {
-  double S = ldexp((double)qsum, -s);
+__device__ inline double fixed_point_threshold(double qsum, int s, float tau, int64_t N) {
+  const double S = ldexp(qsum, -s);
   return ((double)tau * S) / (double)N;
+}
+// Bits of the largest fp32 value <= thr (thr >= 0).  For a finite fp32
+// magnitude a, a > thr exactly when bits(a) > the returned bits.
+__device__ inline uint32_t threshold_bits(double thr) {
+  const float f = (float)thr;
+  uint32_t b = __float_as_uint(f);
+  if ((double)f > thr) b -= 1u;
+  return b;
 }
 
 // ---------------------------------------------------------------------------
@@ -112,6 +119,75 @@ __device__ inline int block_min_i(int v, int* scratch) {
 #pragma unroll
   for (int i = 1; i < T / kWave; ++i) r = min(r, scratch[i]);
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions with DPP row operations (fixed combination order):
+// xor-1 and xor-2 inside quads, half-row and row mirrors, then the two row
+// broadcasts; lane 63 ends up holding the full result.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWMASK>
+__device__ inline int dpp_i32(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ inline float dpp_f32(float identity, float v) {
+  return __int_as_float(dpp_i32<CTRL, ROWMASK>(__float_as_int(identity), __float_as_int(v)));
+}
+template <int CTRL, int ROWMASK>
+__device__ inline double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROWMASK>(0, (int)(b & 0xffffffffll));
+  const int hi = dpp_i32<CTRL, ROWMASK>(0, (int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// Sum over the wave; the result is valid in lane 63.
+__device__ inline float wave_sum_to63(float v) {
+  v += dpp_f32<0xB1, 0xF>(0.f, v);
+  v += dpp_f32<0x4E, 0xF>(0.f, v);
+  v += dpp_f32<0x141, 0xF>(0.f, v);
+  v += dpp_f32<0x140, 0xF>(0.f, v);
+  v += dpp_f32<0x142, 0xA>(0.f, v);
+  v += dpp_f32<0x143, 0xC>(0.f, v);
+  return v;
+}
+__device__ inline double wave_sum_to63(double v) {
+  v += dpp_f64<0xB1, 0xF>(v);
+  v += dpp_f64<0x4E, 0xF>(v);
+  v += dpp_f64<0x141, 0xF>(v);
+  v += dpp_f64<0x140, 0xF>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  return v;
+}
+// Maximum over the wave of non-negative values; valid in lane 63.
+__device__ inline float wave_max_to63(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xF>(0.f, v));
+  v = fmaxf(v, dpp_f32<0x4E, 0xF>(0.f, v));
+  v = fmaxf(v, dpp_f32<0x141, 0xF>(0.f, v));
+  v = fmaxf(v, dpp_f32<0x140, 0xF>(0.f, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(0.f, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(0.f, v));
+  return v;
+}
+// Maximum over the wave of unsigned values; valid in lane 63.
+__device__ inline uint32_t wave_umax_to63(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i32<0xB1, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i32<0x4E, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i32<0x141, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i32<0x140, 0xF>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i32<0x142, 0xA>(0, (int)v));
+  v = max(v, (uint32_t)dpp_i32<0x143, 0xC>(0, (int)v));
+  return v;
+}
+__device__ inline float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ inline double lane63(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
 // 2-bit code of a ternary value: 0 -> 00, +1 -> 01, -1 -> 11.

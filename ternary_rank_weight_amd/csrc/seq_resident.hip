@@ -64,30 +64,115 @@ __device__ inline unsigned long long ll_pack(unsigned round, float v) {
   return ((unsigned long long)round << 32) | (unsigned long long)__float_as_uint(v);
 }
 
-// Sum acc[l] over the T threads of the block for l < L.  Result lands in
-// out[l] (LDS).  Fixed order: 16 lanes per output each add 16 strided
-// entries, then an xor butterfly over the 16 lanes.
+// Sum acc[l] over the T threads for l < L (DPP inside each wave, then the
+// waves in index order) and publish output l < nvalid as slot[base + l].
 template <int T, int L>
-__device__ inline void reduce_outputs(const float (&acc)[L], float* red, float* out) {
-  constexpr int P = 16;           // lanes per output
-  constexpr int S = T + 1;        // padded stride against bank conflicts
+__device__ inline void reduce_publish(const float (&acc)[L], float* red, int nvalid,
+                                      unsigned long long* slot, int base, unsigned round) {
   const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
+  float sums[L];
 #pragma unroll
-  for (int l = 0; l < L; ++l) red[l * S + t] = acc[l];
-  __syncthreads();
-  for (int base = 0; base < L; base += T / P) {
-    const int l = base + t / P;
-    const int part = t % P;
-    float s = 0.f;
-    if (l < L) {
+  for (int l = 0; l < L; ++l) sums[l] = wave_sum_to63(acc[l]);
+  if (lane == kWave - 1) {
 #pragma unroll
-      for (int q = 0; q < T / P; ++q) s += red[l * S + part + P * q];
-    }
-#pragma unroll
-    for (int off = P / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-    if (l < L && part == 0) out[l] = s;
+    for (int l = 0; l < L; ++l) red[w * L + l] = sums[l];
   }
   __syncthreads();
+  if (t < nvalid) {
+    float s = red[t];
+#pragma unroll
+    for (int q = 1; q < T / kWave; ++q) s += red[q * L + t];
+    __hip_atomic_store(slot + base + t, ll_pack(round, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Block reductions with one barrier each.  buf is double[T/64][4]; two
+// consecutive reductions must use different buffers.
+template <int T>
+__device__ inline uint32_t block_umax_flag(uint32_t v, bool bad, double (*buf)[4], bool& any_bad) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
+  const uint32_t mw = wave_umax_to63(v);
+  const bool bw = __any(bad);
+  if (lane == kWave - 1) {
+    buf[w][0] = (double)mw;
+    buf[w][1] = bw ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  uint32_t r = 0u;
+  bool b = false;
+#pragma unroll
+  for (int q = 0; q < T / kWave; ++q) {
+    r = max(r, (uint32_t)buf[q][0]);
+    b = b || buf[q][1] != 0.0;
+  }
+  any_bad = b;
+  return r;
+}
+template <int T, int NV>
+__device__ inline void block_sum_f64(double (&v)[NV], double (*buf)[4]) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const double s = wave_sum_to63(v[i]);
+    if (lane == kWave - 1) buf[w][i] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    double r = buf[0][i];
+#pragma unroll
+    for (int q = 1; q < T / kWave; ++q) r += buf[q][i];
+    v[i] = r;
+  }
+}
+template <int T>
+__device__ inline int block_min_idx(int v, double (*buf)[4]) {
+  const int t = threadIdx.x;
+  const int w = t / kWave;
+  v = wave_min_i(v);
+  if ((t & (kWave - 1)) == 0) buf[w][0] = (double)v;
+  __syncthreads();
+  int r = INT32_MAX;
+#pragma unroll
+  for (int q = 0; q < T / kWave; ++q) r = min(r, (int)buf[q][0]);
+  return r;
+}
+
+// Morton spread of 16 bits: bit e -> bit 2e.
+__device__ inline uint32_t spread16(uint32_t x) {
+  x &= 0xffffu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  x = (x | (x << 1)) & 0x55555555u;
+  return x;
+}
+
+// Write the 2-bit codes of a distributed ternary vector val[j] = t[tid + T*j]
+// (length N) into dst[0 .. ceil(N/16)); workgroup g of G writes the words
+// w with w % G == g.  Uses wave ballots, no LDS and no barrier.
+template <int T, int K>
+__device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, int g, int G) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int words = (N + 15) / 16;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const unsigned long long nz = __ballot(val[j] != 0.f);
+    const unsigned long long ng = __ballot(val[j] < 0.f);
+    const int row_base = (t & ~(kWave - 1)) + T * j;
+    if (lane < 4) {
+      const int w = (row_base >> 4) + lane;
+      if (w < words && w % G == g) {
+        const uint32_t a = (uint32_t)(nz >> (16 * lane)) & 0xffffu;
+        const uint32_t b = (uint32_t)(ng >> (16 * lane)) & 0xffffu;
+        dst[w] = spread16(a) | (spread16(b) << 1);
+      }
+    }
+  }
 }
 
 // Read the n (or m) published words of the current round into val[j] for
@@ -128,45 +213,57 @@ __device__ inline bool gather(const unsigned long long* slot, int N, unsigned ro
   return ok;
 }
 
-// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond N).
-// Identical in every workgroup.  Writes T_tau(x) to out in the same layout and
-// returns this thread's count of nonzeros.
+// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond N),
+// identical in every workgroup.  `bad` folds a failed gather into the first
+// reduction: if any thread of the block has it set, returns false and the
+// caller leaves.  bufs[0..1] are used alternately (see block_umax_flag).
+// Writes T_tau(x) to out in the same layout; cnt gets this thread's nonzeros.
 template <int T, int K>
-__device__ inline int ternarize_dist(const float (&val)[K], int N, float tau, float (&out)[K],
-                                     double* scratch, int& fallback) {
+__device__ inline bool ternarize_dist(const float (&val)[K], bool bad, int N, float tau,
+                                      float (&out)[K], double (*bufs)[T / kWave][4], int& cnt,
+                                      int& fallback) {
   const int t = threadIdx.x;
-  float mx = 0.f;
+  uint32_t ab[K];
+  uint32_t mx = 0u;
 #pragma unroll
-  for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(val[j]));
-  const float M = block_max<T>(mx, reinterpret_cast<float*>(scratch));
-  int cnt = 0;
-  if (M == 0.f) {
+  for (int j = 0; j < K; ++j) {
+    ab[j] = __float_as_uint(val[j]) & 0x7fffffffu;
+    mx = max(mx, ab[j]);
+  }
+  bool any_bad;
+  const uint32_t Mb = block_umax_flag<T>(mx, bad, bufs[0], any_bad);
+  if (any_bad) return false;
+  cnt = 0;
+  if (Mb == 0u) {
 #pragma unroll
     for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
     fallback = 1;
-    return t == 0 ? 1 : 0;
+    cnt = t == 0 ? 1 : 0;
+    return true;
   }
-  const int s = fixed_point_shift(M, N);
-  long long q = 0;
+  const int s = fixed_point_shift(__uint_as_float(Mb), N);
+  // Every partial sum is an integer below 2^52, so the fp64 sums are exact.
+  double qs[1] = {0.0};
 #pragma unroll
-  for (int j = 0; j < K; ++j) q += fixed_point_q(val[j], s);
-  const long long Q = block_sum<T>(q, reinterpret_cast<long long*>(scratch));
-  const double thr = fixed_point_threshold(Q, s, tau, N);
+  for (int j = 0; j < K; ++j) qs[0] += fixed_point_q(__uint_as_float(ab[j]), s);
+  block_sum_f64<T, 1>(qs, bufs[1]);
+  const double thr = fixed_point_threshold(qs[0], s, tau, N);
+  const uint32_t tb = threshold_bits(thr);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const bool keep = (double)fabsf(val[j]) > thr;
+    const bool keep = ab[j] > tb;
     out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
     cnt += keep ? 1 : 0;
   }
   fallback = 0;
-  if ((double)M > thr) return cnt;
+  if (Mb > tb) return true;
   int first = INT32_MAX;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int idx = t + T * j;
-    if (idx < N && fabsf(val[j]) == M) first = min(first, idx);
+    if (idx < N && ab[j] == Mb) first = min(first, idx);
   }
-  const int pick = block_min_i<T>(first, reinterpret_cast<int*>(scratch));
+  const int pick = block_min_idx<T>(first, bufs[0]);
   cnt = 0;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -176,7 +273,7 @@ __device__ inline int ternarize_dist(const float (&val)[K], int N, float tau, fl
     }
   }
   fallback = 1;
-  return cnt;
+  return true;
 }
 
 // Copy this workgroup's rows of the row-resident residual to dst (m x n).
@@ -194,23 +291,19 @@ __device__ void dump_rows(const float* rrow, const ResArgs& a, int row0, float* 
 // of one component's intermediate vectors and residuals.
 template <int T, int KR, int LR, int KC, int LC, bool CAP>
 __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
+  constexpr int W = T / kWave;
   constexpr int LMAX = LR > LC ? LR : LC;
   __shared__ float rrow[LR * KR * T];
-  __shared__ float red[LMAX * (T + 1)];
-  __shared__ float outv[LMAX];
+  __shared__ float red[W * LMAX];
   __shared__ float u_own[LR];
   __shared__ float v_own[LC];
-  __shared__ uint8_t ub[KC * T];
-  __shared__ uint8_t vb[KR * T];
-  __shared__ double scratch[T / kWave];
-  __shared__ int s_bad;
+  __shared__ double bufs[3][W][4];
 
   const int t = threadIdx.x;
   const int g = blockIdx.x;
   const int m = a.m, n = a.n;
   const int row0 = g * a.RB, col0 = g * a.CB;
   const int wm = (m + 15) / 16, wn = (n + 15) / 16;
-  if (t == 0) s_bad = 0;
 
   if (*a.nonfinite > 0) {
     // Nothing sensible can be computed: zero this workgroup's share of the outputs.
@@ -303,6 +396,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
     double cpart = 0.0;  // u . x of the last iteration, this thread's share
     for (int it = 0; it < a.iters; ++it) {
       const bool cap = CAP && (i == a.cap_i) && capturer;
+      int cnt, fb;
       // ---- y = R^T u on the column copy; v = T_tau(y) ----
       {
         float acc[LC];
@@ -313,20 +407,15 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           for (int j = 0; j < KC; ++j) s = fmaf(u[j], rc[l][j], s);
           acc[l] = s;
         }
-        reduce_outputs<T, LC>(acc, red, outv);
         ++ry;
-        if (t < a.CB && col0 + t < n)
-          __hip_atomic_store(a.yslot + col0 + t, ll_pack(ry, outv[t]), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), a.yslot, col0, ry);
         float y[KR];
-        if (!gather<T, KR>(a.yslot, n, ry, y, a.err)) s_bad = 1;
-        __syncthreads();
-        if (s_bad) {
+        const bool bad = !gather<T, KR>(a.yslot, n, ry, y, a.err);
+        if (!ternarize_dist<T, KR>(y, bad, n, a.tau, v, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
-        int fb;
-        st_nnz_v += ternarize_dist<T, KR>(y, n, a.tau, v, scratch, fb);
+        st_nnz_v += cnt;
         st_fb += fb;
         if (cap) {
           for (int j = 0; j < KR; ++j) {
@@ -349,20 +438,15 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           for (int j = 0; j < KR; ++j) s = fmaf(v[j], rp[j * T], s);
           acc[l] = s;
         }
-        reduce_outputs<T, LR>(acc, red, outv);
         ++rx;
-        if (t < a.RB && row0 + t < m)
-          __hip_atomic_store(a.xslot + row0 + t, ll_pack(rx, outv[t]), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), a.xslot, row0, rx);
         float x[KC];
-        if (!gather<T, KC>(a.xslot, m, rx, x, a.err)) s_bad = 1;
-        __syncthreads();
-        if (s_bad) {
+        const bool bad = !gather<T, KC>(a.xslot, m, rx, x, a.err);
+        if (!ternarize_dist<T, KC>(x, bad, m, a.tau, u, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
-        int fb;
-        st_nnz_u += ternarize_dist<T, KC>(x, m, a.tau, u, scratch, fb);
+        st_nnz_u += cnt;
         st_fb += fb;
         if (it == a.iters - 1) {
 #pragma unroll
@@ -380,73 +464,63 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       }
     }
 
-    // ---- scale d = u.x / (nnz_u nnz_v) (§2.3 step 2) ----
-    long long counts = 0;
-#pragma unroll
-    for (int j = 0; j < KC; ++j) counts += (u[j] != 0.f) ? (1ll << 32) : 0ll;
-#pragma unroll
-    for (int j = 0; j < KR; ++j) counts += (v[j] != 0.f) ? 1ll : 0ll;
-    const double c = block_sum<T>(cpart, scratch);
-    const long long cnts = block_sum<T>(counts, reinterpret_cast<long long*>(scratch));
-    const double nu = (double)(cnts >> 32), nv = (double)(cnts & 0xffffffffll);
-    const double den = nu * nv;
-    d32 = (float)(c / den);
-    trace_state -= c * c / den;
-    st_b += (long long)nu;
-    st_c += (long long)nv;
-    if (g == 0 && t == 0) {
-      a.D[i] = d32;
-      if (a.trace) a.trace[i] = trace_state;
-      if (CAP && i == a.cap_i && a.cap_d) *a.cap_d = d32;
-    }
-
-    // ---- own-row u and own-column v for the deflation; codes for B2 / C2 ----
+    // ---- own-row u and own-column v for the next deflation ----
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
       const int row = t + T * j;
-      ub[row] = (uint8_t)code_of(u[j]);
       if (row >= row0 && row < row0 + a.RB && row < m) u_own[row - row0] = u[j];
     }
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
       const int col = t + T * j;
-      vb[col] = (uint8_t)code_of(v[j]);
       if (col >= col0 && col < col0 + a.CB && col < n) v_own[col - col0] = v[j];
     }
-    __syncthreads();
-    for (int w = g + a.G * t; w < wm; w += a.G * T) {
-      uint32_t word = 0;
-      for (int e = 0; e < 16; ++e)
-        if (w * 16 + e < m) word |= (uint32_t)ub[w * 16 + e] << (2 * e);
-      a.B2[(int64_t)i * wm + w] = word;
+
+    // ---- scale d = u.x / (nnz_u nnz_v) (§2.3 step 2); one barrier ----
+    {
+      double sums[3] = {cpart, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < KC; ++j) sums[1] += (u[j] != 0.f) ? 1.0 : 0.0;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) sums[2] += (v[j] != 0.f) ? 1.0 : 0.0;
+      block_sum_f64<T, 3>(sums, bufs[2]);
+      const double c = sums[0], nu = sums[1], nv = sums[2];
+      const double den = nu * nv;
+      d32 = (float)(c / den);
+      trace_state -= c * c / den;
+      st_b += (long long)nu;
+      st_c += (long long)nv;
+      if (g == 0 && t == 0) {
+        a.D[i] = d32;
+        if (a.trace) a.trace[i] = trace_state;
+        if (CAP && i == a.cap_i && a.cap_d) *a.cap_d = d32;
+      }
     }
-    for (int w = g + a.G * t; w < wn; w += a.G * T) {
-      uint32_t word = 0;
-      for (int e = 0; e < 16; ++e)
-        if (w * 16 + e < n) word |= (uint32_t)vb[w * 16 + e] << (2 * e);
-      a.C2[(int64_t)i * wn + w] = word;
-    }
-    __syncthreads();
+
+    // ---- 2-bit codes of u and v into B2 / C2 row i (ballots, no barrier) ----
+    store_codes<T, KC>(u, m, a.B2 + (int64_t)i * wm, g, a.G);
+    store_codes<T, KR>(v, n, a.C2 + (int64_t)i * wn, g, a.G);
   }
 
   // ---- ||R||^2 of the final residual over this workgroup's rows ----
-  double r2 = 0.0;
+  __syncthreads();
+  double r2[1] = {0.0};
 #pragma unroll
   for (int l = 0; l < LR; ++l)
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
       const double r = (double)rrow[(l * KR + j) * T + t];
-      r2 += r * r;
+      r2[0] += r * r;
     }
-  r2 = block_sum<T>(r2, scratch);
-  if (t == 0) a.r2_partial[g] = r2;
+  block_sum_f64<T, 1>(r2, bufs[0]);
+  if (t == 0) a.r2_partial[g] = r2[0];
 
   if (g == 0 && a.stats) {
-    const long long s_u = block_sum<T>(st_nnz_u, reinterpret_cast<long long*>(scratch));
-    const long long s_v = block_sum<T>(st_nnz_v, reinterpret_cast<long long*>(scratch));
+    double cnts[2] = {(double)st_nnz_u, (double)st_nnz_v};
+    block_sum_f64<T, 2>(cnts, bufs[1]);
     if (t == 0) {
-      a.stats[EXTERND_STAT_SUM_NNZ_U] = s_u;
-      a.stats[EXTERND_STAT_SUM_NNZ_V] = s_v;
+      a.stats[EXTERND_STAT_SUM_NNZ_U] = (long long)cnts[0];
+      a.stats[EXTERND_STAT_SUM_NNZ_V] = (long long)cnts[1];
       a.stats[EXTERND_STAT_NNZ_B] = st_b;
       a.stats[EXTERND_STAT_NNZ_C] = st_c;
       a.stats[EXTERND_STAT_FALLBACKS] = st_fb;

@@ -23,7 +23,6 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   __shared__ double scratch[kTernT / kWave];
   float* fs = reinterpret_cast<float*>(scratch);
   int* is = reinterpret_cast<int*>(scratch);
-  long long* ls = reinterpret_cast<long long*>(scratch);
   const int tid = threadIdx.x;
   float mx = 0.f;
   for (int64_t j = tid; j < N; j += kTernT) mx = fmaxf(mx, fabsf(x[j]));
@@ -37,10 +36,10 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
     }
     return;
   }
-  const int s = fixed_point_shift(M, N);
-  long long q = 0;
-  for (int64_t j = tid; j < N; j += kTernT) q += fixed_point_q(x[j], s);
-  const long long Q = block_sum<kTernT>(q, ls);
+  const int s = fixed_point_shift(M, (int)N);
+  double q = 0.0;  // integer-valued partial sums below 2^52: exact in any order
+  for (int64_t j = tid; j < N; j += kTernT) q += fixed_point_q(fabsf(x[j]), s);
+  const double Q = block_sum<kTernT>(q, scratch);
   const double thr = fixed_point_threshold(Q, s, tau, N);
   int cnt = 0;
   for (int64_t w = tid; w < words; w += kTernT) {

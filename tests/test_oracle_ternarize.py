@@ -30,14 +30,19 @@ def test_hand_worked_vectors(case):
 
 
 def test_threshold_is_mean_times_tau():
-    # S is within N * 2**-s of the exact sum; compare against math.fsum.
+    # The fixed-point sum truncates each |x_j| at 2**-s with
+    # s = 52 - e(M) - ceil(log2 N), so thr lies in (tau*mean - tau*2**-s, tau*mean]
+    # up to the final roundings; compare against math.fsum's exact sum.
     rng = np.random.default_rng(5)
     for n in (1, 2, 3, 17, 1000, 4097):
         x = rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6)
-        thr, big = oracle.mean_abs_threshold(x, 1.0)
-        exact = math.fsum(np.abs(x)) / n
-        assert big == np.abs(x).max()
-        assert abs(thr - exact) <= 1e-12 * exact
+        for tau in (1.0, 0.7):
+            thr, big = oracle.mean_abs_threshold(x, tau)
+            t64 = float(np.float32(tau))
+            exact = t64 * math.fsum(np.abs(x)) / n
+            s = 52 - math.frexp(big)[1] - (n - 1).bit_length()
+            assert big == np.abs(x).max()
+            assert exact - t64 * 2.0 ** -s - 4e-16 * exact <= thr <= exact * (1 + 4e-16)
 
 
 def test_sign_and_scale_invariance():
