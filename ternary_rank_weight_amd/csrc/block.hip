@@ -1,11 +1,649 @@
-// Block ALS path (ExTernD §2.4) — placeholder until the MFMA implementation lands.
+// Block ALS path (ExTernD §2.4): b components are fitted together.
+//
+// Per block, with U (m x b) and V (n x b) ternary and R the residual:
+//   repeat `iters` times:
+//     P  = R^T U                     (MFMA contraction over m)
+//     V  = T_col( P (U^T U + eps I)^-1 )
+//     Q  = R V                       (MFMA contraction over n)
+//     U  = T_col( Q (V^T V + eps I)^-1 )
+//   solve [(U^T U) o (V^T V)] d = diag(U^T R V)   (diag read off the last Q)
+//   R <- R - U diag(d) V^T           (MFMA rank-b update)
+// The Gram matrices of ternary factors are exact integers (popcounts of the
+// 2-bit codes); factorisations and solves run in fp64.  T_col applies the
+// mean-threshold ternarizer T_tau (§2.2) to each column.  U and V live as
+// 2-bit codes directly in their B2 / C2 output rows.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace externd {
 
-size_t block_workspace_bytes(int64_t m, int64_t n, int b) { return 256; }
+namespace {
 
-hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) { return hipErrorNotSupported; }
+constexpr int kMaxB = 128;  // widest block the kernels handle
+
+using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
+
+__device__ inline f4 mfma16x16x4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Ternary value of element e of a row of 2-bit codes.
+__device__ inline float tern(const uint32_t* row, int e) {
+  return value_of_code((row[e >> 4] >> (2 * (e & 15))) & 3u);
+}
+
+// ---------------------------------------------------------------------------
+// Starting block U0 (same rule as the sequential path, global component index).
+// ---------------------------------------------------------------------------
+__global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint32_t* __restrict__ B2) {
+  const int64_t wm = (m + 15) / 16;
+  const int64_t total = (int64_t)bb * wm;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t comp = idx / wm, w = idx % wm;
+    const uint64_t base = start_base(seed, (uint64_t)(c0 + comp));
+    uint32_t word = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t r = w * 16 + e;
+      if (r < m) word |= code_of(start_sign(base, (uint64_t)r)) << (2 * e);
+    }
+    B2[(c0 + comp) * wm + w] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact Gram matrix G = X^T X of a ternary block held as 2-bit code rows
+// (X's column i = code row i, length L).  Integer sums of popcounts,
+// accumulated with atomics (exact, so order-free).  G must be zeroed.
+// grid.x = pair tiles, grid.y = word chunks.
+// ---------------------------------------------------------------------------
+constexpr int kGramWords = 32;
+
+__global__ void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb, int* __restrict__ G) {
+  const int pairs = bb * (bb + 1) / 2;
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= pairs) return;
+  // p -> (i, j) with j <= i
+  int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+  while ((i + 1) * (i + 2) / 2 <= p) ++i;
+  while (i * (i + 1) / 2 > p) --i;
+  const int j = p - i * (i + 1) / 2;
+  const int64_t w0 = (int64_t)blockIdx.y * kGramWords;
+  const int64_t w1 = min(wl, w0 + kGramWords);
+  const uint32_t* a = codes + (int64_t)i * wl;
+  const uint32_t* b = codes + (int64_t)j * wl;
+  int acc = 0;
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t x = a[w], y = b[w];
+    const uint32_t both = x & y & 0x55555555u;
+    const uint32_t neg = ((x ^ y) >> 1) & both;
+    acc += __popc(both) - 2 * __popc(neg);
+  }
+  if (acc != 0) {
+    atomicAdd(G + i * bb + j, acc);
+    if (i != j) atomicAdd(G + j * bb + i, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cholesky of A = G + eps I (eps = 1e-6 trace(G)/b) in fp64 in LDS, then
+// Ginv = L^-T L^-1 written as fp32 (b x b row-major).  One workgroup.
+// `fail` is set if a pivot is not positive.
+// ---------------------------------------------------------------------------
+constexpr int kCholT = 256;
+
+__device__ void chol_lds(double* A, int bb, int* fail) {
+  const int t = threadIdx.x;
+  for (int k = 0; k < bb; ++k) {
+    __syncthreads();
+    const double piv = A[k * bb + k];
+    if (!(piv > 0.0)) {
+      if (t == 0) *fail = 1;
+      return;
+    }
+    // trailing update with the unscaled column k: A_ij -= A_ik A_jk / piv
+    const int rem = bb - k - 1;
+    const int npairs = rem * (rem + 1) / 2;
+    const double inv = 1.0 / piv;
+    for (int q = t; q < npairs; q += kCholT) {
+      int ii = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+      while ((ii + 1) * (ii + 2) / 2 <= q) ++ii;
+      while (ii * (ii + 1) / 2 > q) --ii;
+      const int jj = q - ii * (ii + 1) / 2;
+      const int i = k + 1 + ii, j = k + 1 + jj;
+      A[i * bb + j] -= A[i * bb + k] * A[j * bb + k] * inv;
+    }
+    __syncthreads();
+    const double lkk = sqrt(piv);
+    for (int i = k + 1 + t; i < bb; i += kCholT) A[i * bb + k] /= lkk;
+    if (t == 0) A[k * bb + k] = lkk;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kCholT) void k_chol_inv(const int* __restrict__ G, int bb,
+                                                     float* __restrict__ Ginv, int* __restrict__ fail) {
+  extern __shared__ double lds[];
+  double* A = lds;                      // bb * bb; L, then W = L^-1 in its lower triangle
+  double* tmp = lds + bb * bb;          // bb
+  const int t = threadIdx.x;
+  __shared__ double s_tr;
+  __shared__ int s_fail;
+  if (t == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < bb; ++i) tr += (double)G[i * bb + i];
+    s_tr = tr;
+    s_fail = 0;
+  }
+  __syncthreads();
+  const double eps = 1e-6 * s_tr / bb;
+  for (int e = t; e < bb * bb; e += kCholT) {
+    const int i = e / bb, j = e % bb;
+    A[e] = (double)G[e] + (i == j ? eps : 0.0);
+  }
+  chol_lds(A, bb, &s_fail);
+  __syncthreads();
+  if (s_fail) {
+    if (t == 0) *fail = 1;
+    return;
+  }
+  // In-place inversion of the lower-triangular L, columns right to left:
+  // W_jj = 1 / L_jj, W_ij = -(sum_{k=j+1..i} W_ik L_kj) / L_jj for i > j.
+  for (int j = bb - 1; j >= 0; --j) {
+    const double ljj = A[j * bb + j];
+    for (int i = j + 1 + t; i < bb; i += kCholT) {
+      double s = 0.0;
+      for (int k = j + 1; k <= i; ++k) s += A[i * bb + k] * A[k * bb + j];
+      tmp[i] = -s / ljj;
+    }
+    __syncthreads();
+    for (int i = j + 1 + t; i < bb; i += kCholT) A[i * bb + j] = tmp[i];
+    if (t == 0) A[j * bb + j] = 1.0 / ljj;
+    __syncthreads();
+  }
+  // Ginv = W^T W (symmetric), written as fp32
+  for (int e = t; e < bb * bb; e += kCholT) {
+    const int i = e / bb, j = e % bb;
+    double s = 0.0;
+    for (int k = max(i, j); k < bb; ++k) s += A[k * bb + i] * A[k * bb + j];
+    Ginv[e] = (float)s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Contraction 1: Pt_part[s][i][c] = sum_{r in chunk s} U[r][i] R[r][c].
+// grid (ceil(n/64), S); 4 waves, wave w owns columns c0 + 16w .. +15 and all
+// component sub-tiles.  K runs over rows in steps of 16 (4 MFMA 16x16x4);
+// lane (j + 16k) feeds row r + k + 4q at step q to both operands.
+// ---------------------------------------------------------------------------
+constexpr int kCT = 256;
+
+__global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__ R, int64_t m, int64_t n,
+                                                       const uint32_t* __restrict__ Ucodes, int64_t wm,
+                                                       int bb, int64_t rows_per_split,
+                                                       float* __restrict__ Pt_part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, k = lane >> 4;
+  const int64_t col = (int64_t)blockIdx.x * 64 + 16 * w + j;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t r_end = min(m, r_begin + rows_per_split);
+  const int nsub = (bb + 15) / 16;
+  f4 acc[kMaxB / 16];
+#pragma unroll
+  for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = r_begin; r < r_end; r += 16) {
+    float bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = r + k + 4 * q;
+      bv[q] = (row < r_end && col < n) ? R[row * n + col] : 0.f;
+    }
+    const int64_t word = r >> 4;  // r is a multiple of 16 within the split
+#pragma unroll
+    for (int s = 0; s < kMaxB / 16; ++s) {
+      if (s < nsub) {
+        const int comp = 16 * s + j;
+        const uint32_t cw = comp < bb ? Ucodes[(int64_t)comp * wm + word] : 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float av = value_of_code((cw >> (2 * (k + 4 * q))) & 3u);
+          acc[s] = mfma16x16x4(av, bv[q], acc[s]);
+        }
+      }
+    }
+  }
+  // D[i][c]: lane holds rows i = 4*(lane/16) + v of sub-tile s, column j
+#pragma unroll
+  for (int s = 0; s < kMaxB / 16; ++s) {
+    if (s < nsub) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int comp = 16 * s + 4 * k + v;
+        if (comp < bb && col < n)
+          Pt_part[((int64_t)blockIdx.y * bb + comp) * n + col] = acc[s][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Contraction 2: Qt_part[s][i][r] = sum_{c in chunk s} R[r][c] V[c][i].
+// grid (ceil(m/64), S); wave w owns rows r0 + 16w .. +15.  K runs over
+// columns in steps of 16: lane (i + 16k) loads R[row i][c + 4k .. +3] as one
+// float4 and feeds component q at MFMA step q (column c + 4k + q); the V
+// operand of lane (comp + 16k) uses the same column.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
+                                                      const uint32_t* __restrict__ Vcodes, int64_t wn,
+                                                      int bb, int64_t cols_per_split,
+                                                      float* __restrict__ Qt_part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, k = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 64 + 16 * w + i;
+  const int64_t c_begin = (int64_t)blockIdx.y * cols_per_split;
+  const int64_t c_end = min(n, c_begin + cols_per_split);
+  const int nsub = (bb + 15) / 16;
+  const bool vec_ok = (n % 4) == 0;
+  f4 acc[kMaxB / 16];
+#pragma unroll
+  for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c = c_begin; c < c_end; c += 16) {
+    float av[4];
+    const int64_t cc = c + 4 * k;
+    if (row < m && vec_ok && cc + 3 < c_end) {
+      const float4 x = *reinterpret_cast<const float4*>(R + row * n + cc);
+      av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[q] = (row < m && cc + q < c_end) ? R[row * n + cc + q] : 0.f;
+    }
+    const int64_t word = c >> 4;
+#pragma unroll
+    for (int s = 0; s < kMaxB / 16; ++s) {
+      if (s < nsub) {
+        const int comp = 16 * s + i;
+        const uint32_t cw = comp < bb ? Vcodes[(int64_t)comp * wn + word] : 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float bv = value_of_code((cw >> (2 * (4 * k + q))) & 3u);
+          acc[s] = mfma16x16x4(av[q], bv, acc[s]);
+        }
+      }
+    }
+  }
+  // D[row][comp]: lane holds rows 4*(lane/16)+v of the wave's 16, column comp = 16s + i
+#pragma unroll
+  for (int s = 0; s < kMaxB / 16; ++s) {
+    if (s < nsub) {
+      const int comp = 16 * s + i;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t rr = (int64_t)blockIdx.x * 64 + 16 * w + 4 * k + v;
+        if (comp < bb && rr < m) Qt_part[((int64_t)blockIdx.y * bb + comp) * m + rr] = acc[s][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decorrelated target: Xt[i][c] = sum_k Ginv[i][k] * (sum_s Part[s][k][c]).
+// grid ceil(L/64); 256 threads; the summed tile (bb x 64) and Ginv in LDS.
+// Writes the plain sums too (Sum[k][c]) when `sum_out` is non-null.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ Part, int S, int bb,
+                                                     int64_t L, const float* __restrict__ Ginv,
+                                                     float* __restrict__ Xt, float* __restrict__ sum_out) {
+  extern __shared__ float sm[];
+  float* Gs = sm;                   // bb * bb
+  float* Ps = sm + bb * bb;         // bb * 64
+  const int t = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  for (int e = t; e < bb * bb; e += 256) Gs[e] = Ginv[e];
+  for (int e = t; e < bb * 64; e += 256) {
+    const int kk = e / 64, cc = e % 64;
+    const int64_t c = c0 + cc;
+    float s = 0.f;
+    if (c < L)
+      for (int q = 0; q < S; ++q) s += Part[((int64_t)q * bb + kk) * L + c];
+    Ps[e] = s;
+    if (sum_out && c < L) sum_out[(int64_t)kk * L + c] = s;
+  }
+  __syncthreads();
+  const int cc = t & 63;
+  const int64_t c = c0 + cc;
+  for (int i = t >> 6; i < bb; i += 4) {
+    float s = 0.f;
+    for (int kk = 0; kk < bb; ++kk) s = fmaf(Gs[i * bb + kk], Ps[kk * 64 + cc], s);
+    if (c < L) Xt[(int64_t)i * L + c] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// T_tau (§2.2) of every row of Xt (bb rows of length L): one workgroup per
+// row.  Codes go to out_codes row i (row stride wl words); nnz[i] gets the
+// count; fallbacks counted in *fb.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 256;
+
+__global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__ Xt, int64_t L, float tau,
+                                                       uint32_t* __restrict__ out_codes, int64_t wl,
+                                                       int* __restrict__ nnz, long long* __restrict__ fb) {
+  __shared__ double scratch[kTT / kWave];
+  const int i = blockIdx.x;
+  const float* x = Xt + (int64_t)i * L;
+  uint32_t* codes = out_codes + (int64_t)i * wl;
+  const int t = threadIdx.x;
+  float mx = 0.f;
+  for (int64_t j = t; j < L; j += kTT) mx = fmaxf(mx, fabsf(x[j]));
+  const float M = block_max<kTT>(mx, reinterpret_cast<float*>(scratch));
+  if (M == 0.f) {
+    for (int64_t w = t; w < wl; w += kTT) codes[w] = (w == 0) ? 1u : 0u;
+    if (t == 0) {
+      nnz[i] = 1;
+      atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+    }
+    return;
+  }
+  const int s = fixed_point_shift(M, (int)L);
+  double q = 0.0;
+  for (int64_t j = t; j < L; j += kTT) q += fixed_point_q(fabsf(x[j]), s);
+  const double Q = block_sum<kTT>(q, scratch);
+  const double thr = fixed_point_threshold(Q, s, tau, L);
+  const uint32_t tb = threshold_bits(thr);
+  int cnt = 0;
+  for (int64_t w = t; w < wl; w += kTT) {
+    uint32_t word = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t j = w * 16 + e;
+      if (j < L) {
+        const float v = x[j];
+        if ((__float_as_uint(v) & 0x7fffffffu) > tb) {
+          word |= code_of(v) << (2 * e);
+          ++cnt;
+        }
+      }
+    }
+    codes[w] = word;
+  }
+  const uint32_t Mb = __float_as_uint(M);
+  if (Mb > tb) {
+    const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
+    if (t == 0) nnz[i] = total;
+    return;
+  }
+  int first = INT32_MAX;
+  for (int64_t j = t; j < L; j += kTT)
+    if (fabsf(x[j]) == M) { first = (int)j; break; }
+  const int idx = block_min_i<kTT>(first, reinterpret_cast<int*>(scratch));
+  __syncthreads();
+  if (t == 0) {
+    codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
+    nnz[i] = 1;
+    atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Joint scale solve (§2.4): rhs_j = u_j . q_j with q_j the last Q column,
+// M = (U^T U) o (V^T V); Cholesky without ridge, retried with the ridge on
+// failure; d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCholT) void k_joint_solve(const int* __restrict__ GU, const int* __restrict__ GV,
+                                                        int bb, const float* __restrict__ Qt, int64_t m,
+                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
+                                                        float* __restrict__ Dout, double* __restrict__ dscratch,
+                                                        double* __restrict__ trace_state,
+                                                        double* __restrict__ trace, int64_t blk,
+                                                        long long* __restrict__ retries) {
+  extern __shared__ double lds[];
+  double* A = lds;                 // bb * bb
+  double* rhs = lds + bb * bb;     // bb
+  double* d = rhs + bb;            // bb
+  __shared__ int fail;
+  const int t = threadIdx.x;
+  // rhs_j = sum_r u_rj q_rj, one wave per component (fixed order)
+  const int lane = t & 63, wv = t >> 6;
+  for (int j = wv; j < bb; j += kCholT / 64) {
+    const uint32_t* urow = Ucodes + (int64_t)j * wm;
+    double s = 0.0;
+    for (int64_t r = lane; r < m; r += 64) s += (double)tern(urow, (int)r) * (double)Qt[(int64_t)j * m + r];
+    s = wave_sum(s);
+    if (lane == 0) rhs[j] = s;
+  }
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    __syncthreads();
+    if (t == 0) fail = 0;
+    double tr = 0.0;
+    for (int i = 0; i < bb; ++i) tr += (double)GU[i * bb + i] * (double)GV[i * bb + i];
+    const double eps = attempt ? 1e-6 * tr / bb : 0.0;
+    for (int e = t; e < bb * bb; e += kCholT) {
+      const int i = e / bb, jj = e % bb;
+      A[e] = (double)GU[e] * (double)GV[e] + (i == jj ? eps : 0.0);
+    }
+    chol_lds(A, bb, &fail);
+    __syncthreads();
+    if (!fail) break;
+    if (t == 0 && retries) atomicAdd(reinterpret_cast<unsigned long long*>(retries), 1ull);
+  }
+  // L y = rhs (column-oriented, parallel updates), then L^T d = y
+  for (int e = t; e < bb; e += kCholT) d[e] = rhs[e];
+  __syncthreads();
+  for (int i = 0; i < bb; ++i) {
+    const double yi = d[i] / A[i * bb + i];
+    __syncthreads();
+    if (t == 0) d[i] = yi;
+    for (int kk = i + 1 + t; kk < bb; kk += kCholT) d[kk] -= A[kk * bb + i] * yi;
+    __syncthreads();
+  }
+  for (int i = bb - 1; i >= 0; --i) {
+    const double di = d[i] / A[i * bb + i];
+    __syncthreads();
+    if (t == 0) d[i] = di;
+    for (int kk = t; kk < i; kk += kCholT) d[kk] -= A[i * bb + kk] * di;
+    __syncthreads();
+  }
+  if (t == 0) {
+    double dec = 0.0;
+    for (int i = 0; i < bb; ++i) {
+      Dout[i] = (float)d[i];
+      dscratch[i] = (double)(float)d[i];
+      dec += d[i] * rhs[i];
+    }
+    const double tnew = trace_state[0] - dec;
+    trace_state[0] = tnew;
+    if (trace) trace[blk] = tnew;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rank-b deflation R <- R - U diag(d) V^T with fp32 MFMA (fp32 d; products
+// with ternary entries are exact, sums accumulate in fp32).  grid
+// (ceil(n/64), ceil(m/64)); wave w owns rows r0 + 16w .. +15 and four 16-wide
+// column sub-tiles; K runs over components in steps of 4.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, int64_t m, int64_t n,
+                                                       const uint32_t* __restrict__ Ucodes, int64_t wm,
+                                                       const uint32_t* __restrict__ Vcodes, int64_t wn,
+                                                       const double* __restrict__ d, int bb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 15, k = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * 64 + 16 * w;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  f4 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  const int64_t arow = r0 + i;
+  for (int kc = 0; kc < bb; kc += 4) {
+    const int comp = kc + k;
+    const bool ok = comp < bb;
+    const float a = (ok && arow < m) ? tern(Ucodes + (int64_t)comp * wm, (int)arow) : 0.f;
+    const float dc = ok ? (float)d[comp] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t col = c0 + 16 * s + i;
+      const float b = (ok && col < n) ? dc * tern(Vcodes + (int64_t)comp * wn, (int)col) : 0.f;
+      acc[s] = mfma16x16x4(a, b, acc[s]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t col = c0 + 16 * s + i;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = r0 + 4 * k + v;
+      if (row < m && col < n) R[row * n + col] -= acc[s][v];
+    }
+  }
+}
+
+__global__ void k_zero_i32(int* p, int64_t count) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
+       j += (int64_t)gridDim.x * blockDim.x)
+    p[j] = 0;
+}
+__global__ void k_sum_nnz(const int* __restrict__ nnz, int bb, long long* __restrict__ stat) {
+  if (threadIdx.x != 0 || blockIdx.x != 0 || !stat) return;
+  long long s = 0;
+  for (int i = 0; i < bb; ++i) s += nnz[i];
+  *stat += s;
+}
+__global__ void k_set_trace(double* ts, const double* a2) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) ts[0] = *a2;
+}
+__global__ void k_block_finish(const double* __restrict__ a2, const double* __restrict__ r2,
+                               const long long* __restrict__ nonfinite, double* __restrict__ energy,
+                               const long long* __restrict__ local, long long* __restrict__ stats) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double e;
+  if (*nonfinite > 0) e = __longlong_as_double(0x7ff8000000000000ll);
+  else if (*a2 == 0.0) e = 1.0;
+  else e = 1.0 - *r2 / *a2;
+  *energy = e;
+  if (stats) {
+    for (int i = 0; i < EXTERND_STATS_LEN; ++i) stats[i] = local[i];
+    stats[EXTERND_STAT_MODE] = 2;
+  }
+}
+
+inline unsigned grid1d(int64_t count, int threads, int64_t cap = 8192) {
+  int64_t g = (count + threads - 1) / threads;
+  return (unsigned)std::max<int64_t>(1, std::min(g, cap));
+}
+
+struct BlockLayout {
+  int S1, S2;            // K splits of the two contractions
+  int64_t rows_split, cols_split;
+  size_t bytes;
+};
+
+BlockLayout layout_for(int64_t m, int64_t n, int b) {
+  BlockLayout L{};
+  const int64_t tiles1 = (n + 63) / 64, tiles2 = (m + 63) / 64;
+  int64_t s1 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles1 - 1) / tiles1, (m + 255) / 256));
+  int64_t s2 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles2 - 1) / tiles2, (n + 255) / 256));
+  L.rows_split = ((m + s1 - 1) / s1 + 15) / 16 * 16;
+  L.cols_split = ((n + s2 - 1) / s2 + 15) / 16 * 16;
+  L.S1 = (int)((m + L.rows_split - 1) / L.rows_split);
+  L.S2 = (int)((n + L.cols_split - 1) / L.cols_split);
+  size_t by = 0;
+  by += sizeof(float) * (size_t)(m * n);                    // R
+  by += sizeof(float) * (size_t)L.S1 * b * n;               // Pt partials
+  by += sizeof(float) * (size_t)L.S2 * b * m;               // Qt partials
+  by += sizeof(float) * (size_t)b * (n + m);                // Vt, Ut
+  by += sizeof(float) * (size_t)b * m;                      // Qt (last sum)
+  by += sizeof(float) * (size_t)b * b;                      // Ginv
+  by += sizeof(int) * (size_t)b * b * 2;                    // Grams
+  by += sizeof(int) * (size_t)b * 2;                        // nnz
+  by += sizeof(double) * (size_t)(b + 4096 + 16);           // d, norm partials, scalars
+  by += sizeof(long long) * EXTERND_STATS_LEN + sizeof(int) * 4;
+  by += 16 * 256;
+  L.bytes = by;
+  return L;
+}
+
+inline char* bump(char*& p, size_t bytes) {
+  char* r = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
+  p = r + bytes;
+  return r;
+}
+
+}  // namespace
+
+size_t block_workspace_bytes(int64_t m, int64_t n, int b) { return layout_for(m, n, b).bytes; }
+
+hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
+  const int64_t m = a.m, n = a.n, k = a.k;
+  const int b = a.b;
+  if (b > kMaxB || b < 2) return hipErrorInvalidValue;
+  const BlockLayout L = layout_for(m, n, b);
+  const int64_t wm = (m + 15) / 16, wn = (n + 15) / 16;
+  char* p = static_cast<char*>(ws);
+  float* R = reinterpret_cast<float*>(bump(p, sizeof(float) * m * n));
+  float* Pt_part = reinterpret_cast<float*>(bump(p, sizeof(float) * L.S1 * b * n));
+  float* Qt_part = reinterpret_cast<float*>(bump(p, sizeof(float) * L.S2 * b * m));
+  float* Vt = reinterpret_cast<float*>(bump(p, sizeof(float) * b * n));
+  float* Ut = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
+  float* Qt = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
+  float* Ginv = reinterpret_cast<float*>(bump(p, sizeof(float) * b * b));
+  int* GU = reinterpret_cast<int*>(bump(p, sizeof(int) * b * b));
+  int* GV = reinterpret_cast<int*>(bump(p, sizeof(int) * b * b));
+  int* nnz = reinterpret_cast<int*>(bump(p, sizeof(int) * b * 2));
+  double* dvec = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
+  double* npart = reinterpret_cast<double*>(bump(p, sizeof(double) * 4096));
+  double* scal = reinterpret_cast<double*>(bump(p, sizeof(double) * 16));
+  long long* st = reinterpret_cast<long long*>(bump(p, sizeof(long long) * EXTERND_STATS_LEN));
+  int* fail = reinterpret_cast<int*>(bump(p, sizeof(int) * 4));
+  double* a2 = scal;
+  double* r2 = scal + 1;
+  double* tstate = scal + 2;
+
+  hipError_t e;
+  if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
+  if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
+
+  const size_t chol_lds = sizeof(double) * (b * b + b);
+  const size_t joint_lds = sizeof(double) * (b * b + 2 * b);
+  const size_t dec_lds = sizeof(float) * (b * b + b * 64);
+  const int64_t nblocks = (k + b - 1) / b;
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    const int64_t c0 = blk * b;
+    const int bb = (int)std::min<int64_t>(b, k - c0);
+    uint32_t* Uc = a.B2 + c0 * wm;
+    uint32_t* Vc = a.C2 + c0 * wn;
+    const int pairs = bb * (bb + 1) / 2;
+    hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2);
+    for (int it = 0; it < a.iters; ++it) {
+      // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U
+      hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GU, (int64_t)bb * bb);
+      hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Uc, wm, bb, GU);
+      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(kCholT), chol_lds, s, GU, bb, Ginv, fail);
+      hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + 63) / 64)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, Ginv, Vt, (float*)nullptr);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS);
+      hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz + b, bb, st + EXTERND_STAT_SUM_NNZ_V);
+      // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V
+      hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GV, (int64_t)bb * bb);
+      hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wn + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Vc, wn, bb, GV);
+      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(kCholT), chol_lds, s, GV, bb, Ginv, fail);
+      hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + 63) / 64)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, Ginv, Ut, Qt);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS);
+      hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz, bb, st + EXTERND_STAT_SUM_NNZ_U);
+    }
+    // joint scales from the final U, V and the last Q = R V
+    hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GU, (int64_t)bb * bb);
+    hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Uc, wm, bb, GU);
+    hipLaunchKernelGGL(k_joint_solve, dim3(1), dim3(kCholT), joint_lds, s, GU, GV, bb, Qt, m, Uc, wm, a.D + c0, dvec, tstate, a.trace, blk, st + EXTERND_STAT_RIDGE_RETRIES);
+    hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz, bb, st + EXTERND_STAT_NNZ_B);
+    hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz + b, bb, st + EXTERND_STAT_NNZ_C);
+    hipLaunchKernelGGL(k_block_deflate, dim3((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_block_finish, dim3(1), dim3(1), 0, s, a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, st, a.stats);
+  return hipGetLastError();
+}
 
 }  // namespace externd

@@ -1,0 +1,116 @@
+"""GPU checks of the block-ALS path (ExTernD §2.4) against the fp64 oracle.
+
+End to end the two trajectories diverge once any near-threshold entry of a
+ternarized column flips, so the energy is compared within 2e-3 of the
+oracle's; the energy the GPU reports must match an fp64 recomputation from
+its own factors to 1e-5; factors are ternary, the per-block residual trace
+never increases, and repeated runs are bit-identical.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _goldens():
+    p = os.path.join(HERE, "golden", "oracle_energies.json")
+    if not os.path.exists(p):
+        return {}
+    return json.load(open(p))["entries"]
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _factors(res):
+    B = oracle.unpack2(res.B2.cpu().numpy().view(np.uint32), res.m).T
+    C = oracle.unpack2(res.C2.cpu().numpy().view(np.uint32), res.n)
+    D = res.D.cpu().numpy().astype(np.float64)
+    return B, C, D
+
+
+@pytest.mark.parametrize("m,n,mu,tau,b", [(256, 256, 1.0, 0.7, 32), (300, 200, 1.3, 1.0, 16),
+                                          (128, 512, 2.0, 2.0, 16)])
+def test_block_small_vs_oracle(lib, m, n, mu, tau, b):
+    A = synthetic.gaussian(m, n, 7)
+    Ad = _dev(A)
+    res = lib.decompose(Ad, mu, tau, 15, b, 3, trace=True, stats=True)
+    E = float(res.energy.item())
+    ref = oracle.decompose_block(A, mu, tau, 15, b, 3)
+    assert abs(E - ref.E) <= 2e-3, (E, ref.E)
+    B, C, D = _factors(res)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+    assert abs(float(lib.energy(Ad, res.B2, res.C2, res.D).item()) - E) <= 1e-5
+    assert res.stat("mode") == 2
+    tr = res.trace.cpu().numpy()
+    assert tr.size == (res.k + b - 1) // b
+    assert np.all(np.diff(tr) <= 1e-9 * ref.norm_a2)
+    assert abs(1 - tr[-1] / ref.norm_a2 - E) <= 1e-4
+    assert abs(oracle.zero_fraction(B, C) - oracle.zero_fraction(ref.B, ref.C)) < 0.02
+    assert res.stat("nnz_b") == np.count_nonzero(B) and res.stat("nnz_c") == np.count_nonzero(C)
+    again = lib.decompose(Ad, mu, tau, 15, b, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(again.B2, res.B2) and torch.equal(again.C2, res.C2)
+    assert torch.equal(again.D, res.D) and torch.equal(again.energy, res.energy)
+
+
+def test_block_trailing_partial_block(lib):
+    A = synthetic.gaussian(200, 180, 2)
+    res = lib.decompose(_dev(A), 0.9, 0.7, 15, 16, 0, trace=True)   # k = 162 = 10*16 + 2
+    assert res.k == 162 and res.trace.numel() == 11
+    ref = oracle.decompose_block(A, 0.9, 0.7, 15, 16, 0)
+    assert abs(float(res.energy.item()) - ref.E) <= 2e-3
+    B, C, D = _factors(res)
+    assert abs(float(res.energy.item()) - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+
+
+def test_block_width_cap_falls_back_to_sequential(lib):
+    A = synthetic.gaussian(12, 100, 1)        # floor(12/8) = 1 -> sequential
+    res = lib.decompose(_dev(A), 1.0, 0.7, 15, 64, 0, stats=True)
+    assert res.stat("mode") in (0, 1)
+    ref = oracle.decompose_seq(A, 1.0, 0.7, 15, 0)
+    assert abs(float(res.energy.item()) - ref.E) <= 2e-3
+
+
+def test_block_structured_ternary_low_rank(lib):
+    # A = U* diag(d*) V*^T with b ternary components of disjoint supports: a
+    # sparse, exactly ternary input whose decorrelated targets are full of
+    # exact magnitude ties, so fp32 and fp64 trajectories split early and only
+    # trajectory-independent properties are checked.
+    m, n, b = 128, 96, 8
+    U = np.zeros((m, b)); V = np.zeros((n, b))
+    rng = np.random.default_rng(4)
+    for j in range(b):
+        U[16 * j:16 * j + 16, j] = rng.choice([-1, 1], 16)
+        V[12 * j:12 * j + 12, j] = rng.choice([-1, 1], 12)
+    d = 0.5 + 0.25 * np.arange(b)
+    A = ((U * d) @ V.T).astype(np.float32)
+    res = lib.decompose(_dev(A), 4 * b / 96, 0.7, 15, b, 0, trace=True)
+    E = float(res.energy.item())
+    B, C, D = _factors(res)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+    assert E > 0.95
+    assert np.all(np.diff(res.trace.cpu().numpy()) <= 0)
+
+
+def test_block_config2_full(lib):
+    g = _goldens().get("cfg2_block64")
+    if g is None:
+        pytest.skip("oracle golden for the 2560x2560 block run not generated")
+    c = synthetic.CONFIGS[2]
+    A = synthetic.config_matrix(2)
+    res = lib.decompose(_dev(A), c["mu"], c["tau"], c["iters"], c["block"], c["seed"], stats=True)
+    E = float(res.energy.item())
+    assert abs(E - g["E"]) <= 2e-3, (E, g["E"])
+    B, C, D = _factors(res)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+    assert abs(oracle.zero_fraction(B, C) - g["zero_fraction"]) < 0.01
