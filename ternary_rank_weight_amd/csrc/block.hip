@@ -86,14 +86,15 @@ __global__ void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb, i
 }
 
 // ---------------------------------------------------------------------------
-// Cholesky of A = G + eps I (eps = 1e-6 trace(G)/b) in fp64 in LDS, then
-// Ginv = L^-T L^-1 written as fp32 (b x b row-major).  One workgroup.
-// `fail` is set if a pivot is not positive.
+// Small dense fp64 linear algebra on one workgroup: an in-LDS Cholesky
+// factorisation (used by the joint scale solve) and the SPD inverse of a
+// Gram matrix (used to decorrelate the ALS targets).
 // ---------------------------------------------------------------------------
 constexpr int kCholT = 256;
 
 __device__ void chol_lds(double* A, int bb, int* fail) {
   const int t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;   // 16 x 16 thread grid
   for (int k = 0; k < bb; ++k) {
     __syncthreads();
     const double piv = A[k * bb + k];
@@ -101,17 +102,11 @@ __device__ void chol_lds(double* A, int bb, int* fail) {
       if (t == 0) *fail = 1;
       return;
     }
-    // trailing update with the unscaled column k: A_ij -= A_ik A_jk / piv
-    const int rem = bb - k - 1;
-    const int npairs = rem * (rem + 1) / 2;
+    // trailing update with the unscaled column k: A_ij -= A_ik A_jk / piv, k < j <= i
     const double inv = 1.0 / piv;
-    for (int q = t; q < npairs; q += kCholT) {
-      int ii = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
-      while ((ii + 1) * (ii + 2) / 2 <= q) ++ii;
-      while (ii * (ii + 1) / 2 > q) --ii;
-      const int jj = q - ii * (ii + 1) / 2;
-      const int i = k + 1 + ii, j = k + 1 + jj;
-      A[i * bb + j] -= A[i * bb + k] * A[j * bb + k] * inv;
+    for (int i = k + 1 + ti; i < bb; i += 16) {
+      const double aik = A[i * bb + k] * inv;
+      for (int j = k + 1 + tj; j <= i; j += 16) A[i * bb + j] -= aik * A[j * bb + k];
     }
     __syncthreads();
     const double lkk = sqrt(piv);
@@ -121,53 +116,163 @@ __device__ void chol_lds(double* A, int bb, int* fail) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kCholT) void k_chol_inv(const int* __restrict__ G, int bb,
-                                                     float* __restrict__ Ginv, int* __restrict__ fail) {
-  extern __shared__ double lds[];
-  double* A = lds;                      // bb * bb; L, then W = L^-1 in its lower triangle
-  double* tmp = lds + bb * bb;          // bb
+// Ginv = (G + eps I)^-1, eps = 1e-6 trace(G)/b, by blocked Gauss-Jordan
+// elimination in fp64, four pivots per step (no pivoting: the matrix is
+// symmetric positive definite, and so is every 4 x 4 pivot block of its
+// Schur complements).  With K the pivot rows and R the rest, one step maps
+//   A_KK -> P = A_KK^-1,   A_KR -> P A_KR,   A_RK -> -A_RK P,
+//   A_RR -> A_RR - (A_RK P) A_KR.
+// Thread (ti, tj) of a 16 x 16 grid keeps entries (ti + 16x, tj + 16y) in
+// registers; indices from bb up to 16 NA are padded with the identity, so a
+// trailing partial pivot block stays invertible and decoupled.  The owners of
+// the pivot rows and columns publish them in LDS (double-buffered, so one
+// barrier per step suffices) with the K x K part zeroed, and every thread
+// inverts the 4 x 4 pivot block itself.  G is integer valued and is zeroed
+// after being read so the next Gram accumulation starts from zero.  `fail` is
+// set when a pivot is not positive.  One workgroup.
+template <int NA>  // bb <= 16 * NA
+__global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int bb,
+                                                        float* __restrict__ Ginv, int* __restrict__ fail) {
+  __shared__ double prow[2][kMaxB][4];   // prow[j][l] = A[K_l][j], zero for j in K
+  __shared__ double pcol[2][kMaxB][4];   // pcol[i][l] = A[i][K_l], zero for i in K
+  __shared__ double pkk[2][4][4];        // A_KK
+  __shared__ double s_diag[kMaxB];
+  __shared__ double s_eps;
   const int t = threadIdx.x;
-  __shared__ double s_tr;
-  __shared__ int s_fail;
+  const int ti = t >> 4, tj = t & 15;
+  double a[NA][NA];
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y) {
+      const int i = ti + 16 * x, j = tj + 16 * y;
+      const bool in = i < bb && j < bb;
+      a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
+      if (in) G[i * bb + j] = 0;
+      if (in && i == j) s_diag[i] = a[x][y];
+    }
+  __syncthreads();
   if (t == 0) {
     double tr = 0.0;
-    for (int i = 0; i < bb; ++i) tr += (double)G[i * bb + i];
-    s_tr = tr;
-    s_fail = 0;
+    for (int i = 0; i < bb; ++i) tr += s_diag[i];
+    s_eps = 1e-6 * tr / bb;
   }
   __syncthreads();
-  const double eps = 1e-6 * s_tr / bb;
-  for (int e = t; e < bb * bb; e += kCholT) {
-    const int i = e / bb, j = e % bb;
-    A[e] = (double)G[e] + (i == j ? eps : 0.0);
-  }
-  chol_lds(A, bb, &s_fail);
-  __syncthreads();
-  if (s_fail) {
-    if (t == 0) *fail = 1;
-    return;
-  }
-  // In-place inversion of the lower-triangular L, columns right to left:
-  // W_jj = 1 / L_jj, W_ij = -(sum_{k=j+1..i} W_ik L_kj) / L_jj for i > j.
-  for (int j = bb - 1; j >= 0; --j) {
-    const double ljj = A[j * bb + j];
-    for (int i = j + 1 + t; i < bb; i += kCholT) {
-      double s = 0.0;
-      for (int k = j + 1; k <= i; ++k) s += A[i * bb + k] * A[k * bb + j];
-      tmp[i] = -s / ljj;
+  const double eps = s_eps;
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y)
+      if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
+  const int kq_r = ti >> 2, la = ti & 3;   // rows of a wave form one pivot quad
+  const int kq_c = tj >> 2, lc = tj & 3;
+  bool ok = true;
+  int step = 0;
+#pragma unroll
+  for (int kx = 0; kx < NA; ++kx) {
+    for (int kq = 0; kq < 4; ++kq, ++step) {
+      if (16 * kx + 4 * kq >= bb) break;   // uniform
+      const int bf = step & 1;
+      const bool rown = kq_r == kq;          // wave-uniform
+      const bool cown = kq_c == kq;
+      if (rown) {
+#pragma unroll
+        for (int y = 0; y < NA; ++y) prow[bf][tj + 16 * y][la] = (y == kx && cown) ? 0.0 : a[kx][y];
+        if (cown) pkk[bf][la][lc] = a[kx][kx];
+      }
+      if (cown) {
+#pragma unroll
+        for (int x = 0; x < NA; ++x) pcol[bf][ti + 16 * x][lc] = (x == kx && rown) ? 0.0 : a[x][kx];
+      }
+      __syncthreads();
+      // P = A_KK^-1 in registers; reciprocals by rcp and two Newton steps
+      double p[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) p[r][c] = pkk[bf][r][c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double piv = p[q][q];
+        ok = ok && (piv > 0.0);
+        double ip = __builtin_amdgcn_rcp(piv);
+        double e = fma(-piv, ip, 1.0);
+        ip = fma(ip, e, ip);
+        e = fma(-piv, ip, 1.0);
+        ip = fma(ip, e, ip);
+        double rq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rq[c] = (c == q) ? ip : p[q][c] * ip;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (r == q) continue;
+          const double f = p[r][q];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) p[r][c] = (c == q) ? -f * ip : fma(-f, rq[c], p[r][c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) p[q][c] = rq[c];
+      }
+      // w = A_RK P (zero on the pivot rows); rank-4 update of everything else
+      double w[NA][4], pr[NA][4];
+#pragma unroll
+      for (int x = 0; x < NA; ++x) {
+        double c4[4];
+#pragma unroll
+        for (int l = 0; l < 4; ++l) c4[l] = pcol[bf][ti + 16 * x][l];
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+          double s = c4[0] * p[0][l];
+#pragma unroll
+          for (int b = 1; b < 4; ++b) s = fma(c4[b], p[b][l], s);
+          w[x][l] = s;
+        }
+      }
+#pragma unroll
+      for (int y = 0; y < NA; ++y)
+#pragma unroll
+        for (int l = 0; l < 4; ++l) pr[y][l] = prow[bf][tj + 16 * y][l];
+#pragma unroll
+      for (int x = 0; x < NA; ++x)
+#pragma unroll
+        for (int y = 0; y < NA; ++y) {
+          double s = a[x][y];
+#pragma unroll
+          for (int l = 0; l < 4; ++l) s = fma(-w[x][l], pr[y][l], s);
+          a[x][y] = s;
+        }
+      // pivot rows become P A_KR (P itself on the pivot block); pivot columns -w
+      if (rown) {
+        double pa[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) pa[b] = la == 0 ? p[0][b] : la == 1 ? p[1][b] : la == 2 ? p[2][b] : p[3][b];
+#pragma unroll
+        for (int y = 0; y < NA; ++y) {
+          double s = pa[0] * pr[y][0];
+#pragma unroll
+          for (int b = 1; b < 4; ++b) s = fma(pa[b], pr[y][b], s);
+          a[kx][y] = s;
+        }
+        if (cown) a[kx][kx] = lc == 0 ? pa[0] : lc == 1 ? pa[1] : lc == 2 ? pa[2] : pa[3];
+      }
+      if (cown) {
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+          if (x == kx && rown) continue;
+          const double v = lc == 0 ? w[x][0] : lc == 1 ? w[x][1] : lc == 2 ? w[x][2] : w[x][3];
+          a[x][kx] = -v;
+        }
+      }
     }
-    __syncthreads();
-    for (int i = j + 1 + t; i < bb; i += kCholT) A[i * bb + j] = tmp[i];
-    if (t == 0) A[j * bb + j] = 1.0 / ljj;
-    __syncthreads();
   }
-  // Ginv = W^T W (symmetric), written as fp32
-  for (int e = t; e < bb * bb; e += kCholT) {
-    const int i = e / bb, j = e % bb;
-    double s = 0.0;
-    for (int k = max(i, j); k < bb; ++k) s += A[k * bb + i] * A[k * bb + j];
-    Ginv[e] = (float)s;
-  }
+  if (!ok && t == 0) *fail = 1;
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y) {
+      const int i = ti + 16 * x, j = tj + 16 * y;
+      if (i < bb && j < bb) Ginv[i * bb + j] = (float)a[x][y];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -191,8 +296,8 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
   f4 acc[kMaxB / 16];
 #pragma unroll
   for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t r = r_begin; r < r_end; r += 16) {
-    float bv[4];
+  // operands of one 16-row K step, loaded one step ahead of their use
+  auto load = [&](int64_t r, float (&bv)[4], uint32_t (&cw)[kMaxB / 16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t row = r + k + 4 * q;
@@ -201,15 +306,33 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
     const int64_t word = r >> 4;  // r is a multiple of 16 within the split
 #pragma unroll
     for (int s = 0; s < kMaxB / 16; ++s) {
+      const int comp = 16 * s + j;
+      cw[s] = (s < nsub && comp < bb) ? Ucodes[(int64_t)comp * wm + word] : 0u;
+    }
+  };
+  float bv[4];
+  uint32_t cw[kMaxB / 16];
+  if (r_begin < r_end) load(r_begin, bv, cw);
+  for (int64_t r = r_begin; r < r_end; r += 16) {
+    float bvn[4];
+    uint32_t cwn[kMaxB / 16];
+    const bool more = r + 16 < r_end;
+    if (more) load(r + 16, bvn, cwn);
+#pragma unroll
+    for (int s = 0; s < kMaxB / 16; ++s) {
       if (s < nsub) {
-        const int comp = 16 * s + j;
-        const uint32_t cw = comp < bb ? Ucodes[(int64_t)comp * wm + word] : 0u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float av = value_of_code((cw >> (2 * (k + 4 * q))) & 3u);
+          const float av = value_of_code((cw[s] >> (2 * (k + 4 * q))) & 3u);
           acc[s] = mfma16x16x4(av, bv[q], acc[s]);
         }
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[q] = bvn[q];
+#pragma unroll
+      for (int s = 0; s < kMaxB / 16; ++s) cw[s] = cwn[s];
     }
   }
   // D[i][c]: lane holds rows i = 4*(lane/16) + v of sub-tile s, column j
@@ -247,8 +370,7 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
   f4 acc[kMaxB / 16];
 #pragma unroll
   for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t c = c_begin; c < c_end; c += 16) {
-    float av[4];
+  auto load = [&](int64_t c, float (&av)[4], uint32_t (&cw)[kMaxB / 16]) {
     const int64_t cc = c + 4 * k;
     if (row < m && vec_ok && cc + 3 < c_end) {
       const float4 x = *reinterpret_cast<const float4*>(R + row * n + cc);
@@ -260,15 +382,33 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
     const int64_t word = c >> 4;
 #pragma unroll
     for (int s = 0; s < kMaxB / 16; ++s) {
+      const int comp = 16 * s + i;
+      cw[s] = (s < nsub && comp < bb) ? Vcodes[(int64_t)comp * wn + word] : 0u;
+    }
+  };
+  float av[4];
+  uint32_t cw[kMaxB / 16];
+  if (c_begin < c_end) load(c_begin, av, cw);
+  for (int64_t c = c_begin; c < c_end; c += 16) {
+    float avn[4];
+    uint32_t cwn[kMaxB / 16];
+    const bool more = c + 16 < c_end;
+    if (more) load(c + 16, avn, cwn);
+#pragma unroll
+    for (int s = 0; s < kMaxB / 16; ++s) {
       if (s < nsub) {
-        const int comp = 16 * s + i;
-        const uint32_t cw = comp < bb ? Vcodes[(int64_t)comp * wn + word] : 0u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float bv = value_of_code((cw >> (2 * (4 * k + q))) & 3u);
+          const float bv = value_of_code((cw[s] >> (2 * (4 * k + q))) & 3u);
           acc[s] = mfma16x16x4(av[q], bv, acc[s]);
         }
       }
+    }
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[q] = avn[q];
+#pragma unroll
+      for (int s = 0; s < kMaxB / 16; ++s) cw[s] = cwn[s];
     }
   }
   // D[row][comp]: lane holds rows 4*(lane/16)+v of the wave's 16, column comp = 16s + i
@@ -287,33 +427,39 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Decorrelated target: Xt[i][c] = sum_k Ginv[i][k] * (sum_s Part[s][k][c]).
-// grid ceil(L/64); 256 threads; the summed tile (bb x 64) and Ginv in LDS.
+// grid ceil(L/16); 256 threads; Ginv and the summed 16-column tile in LDS.
 // Writes the plain sums too (Sum[k][c]) when `sum_out` is non-null.
 // ---------------------------------------------------------------------------
+constexpr int kDecW = 16;
+
 __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ Part, int S, int bb,
                                                      int64_t L, const float* __restrict__ Ginv,
                                                      float* __restrict__ Xt, float* __restrict__ sum_out) {
   extern __shared__ float sm[];
   float* Gs = sm;                   // bb * bb
-  float* Ps = sm + bb * bb;         // bb * 64
+  float* Ps = sm + bb * bb;         // bb * kDecW
   const int t = threadIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecW;
+#pragma unroll 8
   for (int e = t; e < bb * bb; e += 256) Gs[e] = Ginv[e];
-  for (int e = t; e < bb * 64; e += 256) {
-    const int kk = e / 64, cc = e % 64;
+#pragma unroll 2
+  for (int e = t; e < bb * kDecW; e += 256) {
+    const int kk = e / kDecW, cc = e % kDecW;
     const int64_t c = c0 + cc;
     float s = 0.f;
-    if (c < L)
+    if (c < L) {
+#pragma unroll 8
       for (int q = 0; q < S; ++q) s += Part[((int64_t)q * bb + kk) * L + c];
+    }
     Ps[e] = s;
     if (sum_out && c < L) sum_out[(int64_t)kk * L + c] = s;
   }
   __syncthreads();
-  const int cc = t & 63;
+  const int cc = t % kDecW;
   const int64_t c = c0 + cc;
-  for (int i = t >> 6; i < bb; i += 4) {
+  for (int i = t / kDecW; i < bb; i += 256 / kDecW) {
     float s = 0.f;
-    for (int kk = 0; kk < bb; ++kk) s = fmaf(Gs[i * bb + kk], Ps[kk * 64 + cc], s);
+    for (int kk = 0; kk < bb; ++kk) s = fmaf(Gs[i * bb + kk], Ps[kk * kDecW + cc], s);
     if (c < L) Xt[(int64_t)i * L + c] = s;
   }
 }
@@ -327,7 +473,8 @@ constexpr int kTT = 256;
 
 __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__ Xt, int64_t L, float tau,
                                                        uint32_t* __restrict__ out_codes, int64_t wl,
-                                                       int* __restrict__ nnz, long long* __restrict__ fb) {
+                                                       int* __restrict__ nnz, long long* __restrict__ fb,
+                                                       long long* __restrict__ nnz_sum) {
   __shared__ double scratch[kTT / kWave];
   const int i = blockIdx.x;
   const float* x = Xt + (int64_t)i * L;
@@ -341,6 +488,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
     if (t == 0) {
       nnz[i] = 1;
       atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+      atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
     }
     return;
   }
@@ -368,7 +516,10 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   const uint32_t Mb = __float_as_uint(M);
   if (Mb > tb) {
     const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
-    if (t == 0) nnz[i] = total;
+    if (t == 0) {
+      nnz[i] = total;
+      atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), (unsigned long long)total);
+    }
     return;
   }
   int first = INT32_MAX;
@@ -380,6 +531,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
     codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
     nnz[i] = 1;
     atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+    atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
   }
 }
 
@@ -388,13 +540,14 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
 // M = (U^T U) o (V^T V); Cholesky without ridge, retried with the ridge on
 // failure; d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kCholT) void k_joint_solve(const int* __restrict__ GU, const int* __restrict__ GV,
+__global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, int* __restrict__ GV,
                                                         int bb, const float* __restrict__ Qt, int64_t m,
                                                         const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                         float* __restrict__ Dout, double* __restrict__ dscratch,
                                                         double* __restrict__ trace_state,
                                                         double* __restrict__ trace, int64_t blk,
-                                                        long long* __restrict__ retries) {
+                                                        long long* __restrict__ st, const int* __restrict__ nnz,
+                                                        int bstride) {
   extern __shared__ double lds[];
   double* A = lds;                 // bb * bb
   double* rhs = lds + bb * bb;     // bb
@@ -410,20 +563,25 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(const int* __restrict__ 
     s = wave_sum(s);
     if (lane == 0) rhs[j] = s;
   }
+  __shared__ double s_tr;
   for (int attempt = 0; attempt < 2; ++attempt) {
     __syncthreads();
     if (t == 0) fail = 0;
-    double tr = 0.0;
-    for (int i = 0; i < bb; ++i) tr += (double)GU[i * bb + i] * (double)GV[i * bb + i];
-    const double eps = attempt ? 1e-6 * tr / bb : 0.0;
-    for (int e = t; e < bb * bb; e += kCholT) {
-      const int i = e / bb, jj = e % bb;
-      A[e] = (double)GU[e] * (double)GV[e] + (i == jj ? eps : 0.0);
+#pragma unroll 8
+    for (int e = t; e < bb * bb; e += kCholT) A[e] = (double)GU[e] * (double)GV[e];
+    __syncthreads();
+    if (t == 0) {
+      double tr = 0.0;
+      for (int i = 0; i < bb; ++i) tr += A[i * bb + i];
+      s_tr = tr;
     }
+    __syncthreads();
+    const double eps = attempt ? 1e-6 * s_tr / bb : 0.0;
+    for (int i = t; i < bb; i += kCholT) A[i * bb + i] += eps;
     chol_lds(A, bb, &fail);
     __syncthreads();
     if (!fail) break;
-    if (t == 0 && retries) atomicAdd(reinterpret_cast<unsigned long long*>(retries), 1ull);
+    if (t == 0) atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_RIDGE_RETRIES), 1ull);
   }
   // L y = rhs (column-oriented, parallel updates), then L^T d = y
   for (int e = t; e < bb; e += kCholT) d[e] = rhs[e];
@@ -452,6 +610,17 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(const int* __restrict__ 
     const double tnew = trace_state[0] - dec;
     trace_state[0] = tnew;
     if (trace) trace[blk] = tnew;
+    long long nb = 0, nc = 0;
+    for (int i = 0; i < bb; ++i) {
+      nb += nnz[i];
+      nc += nnz[bstride + i];
+    }
+    st[EXTERND_STAT_NNZ_B] += nb;
+    st[EXTERND_STAT_NNZ_C] += nc;
+  }
+  for (int e = t; e < bb * bb; e += kCholT) {
+    GU[e] = 0;
+    GV[e] = 0;
   }
 }
 
@@ -501,12 +670,6 @@ __global__ void k_zero_i32(int* p, int64_t count) {
        j += (int64_t)gridDim.x * blockDim.x)
     p[j] = 0;
 }
-__global__ void k_sum_nnz(const int* __restrict__ nnz, int bb, long long* __restrict__ stat) {
-  if (threadIdx.x != 0 || blockIdx.x != 0 || !stat) return;
-  long long s = 0;
-  for (int i = 0; i < bb; ++i) s += nnz[i];
-  *stat += s;
-}
 __global__ void k_set_trace(double* ts, const double* a2) {
   if (threadIdx.x == 0 && blockIdx.x == 0) ts[0] = *a2;
 }
@@ -552,7 +715,7 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   by += sizeof(float) * (size_t)b * (n + m);                // Vt, Ut
   by += sizeof(float) * (size_t)b * m;                      // Qt (last sum)
   by += sizeof(float) * (size_t)b * b;                      // Ginv
-  by += sizeof(int) * (size_t)b * b * 2;                    // Grams
+  by += sizeof(int) * (size_t)b * b * 4;                    // Grams
   by += sizeof(int) * (size_t)b * 2;                        // nnz
   by += sizeof(double) * (size_t)(b + 4096 + 16);           // d, norm partials, scalars
   by += sizeof(long long) * EXTERND_STATS_LEN + sizeof(int) * 4;
@@ -565,6 +728,31 @@ inline char* bump(char*& p, size_t bytes) {
   char* r = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
   p = r + bytes;
   return r;
+}
+
+// A second stream (default priority) and two events for running the Gram and
+// inverse of one half-iteration beside its contraction.
+struct SideStream {
+  hipStream_t side = nullptr;
+  hipEvent_t ev_in = nullptr, ev_out = nullptr;
+  hipError_t init() {
+    hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_in, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_out, hipEventDisableTiming);
+    return e;
+  }
+  ~SideStream() {
+    if (ev_in) (void)hipEventDestroy(ev_in);
+    if (ev_out) (void)hipEventDestroy(ev_out);
+    if (side) (void)hipStreamDestroy(side);
+  }
+};
+
+void launch_inverse(int bb, int* G, float* Ginv, int* fail, hipStream_t st) {
+  if (bb <= 64)
+    hipLaunchKernelGGL(k_spd_inverse<4>, dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
+  else
+    hipLaunchKernelGGL(k_spd_inverse<8>, dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
 }
 
 }  // namespace
@@ -585,8 +773,10 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   float* Ut = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
   float* Qt = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
   float* Ginv = reinterpret_cast<float*>(bump(p, sizeof(float) * b * b));
-  int* GU = reinterpret_cast<int*>(bump(p, sizeof(int) * b * b));
-  int* GV = reinterpret_cast<int*>(bump(p, sizeof(int) * b * b));
+  int* GU = reinterpret_cast<int*>(bump(p, sizeof(int) * 4 * b * b));  // GU, GV, GUf, GVf
+  int* GV = GU + b * b;
+  int* GUf = GU + 2 * b * b;
+  int* GVf = GU + 3 * b * b;
   int* nnz = reinterpret_cast<int*>(bump(p, sizeof(int) * b * 2));
   double* dvec = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
   double* npart = reinterpret_cast<double*>(bump(p, sizeof(double) * 4096));
@@ -598,14 +788,16 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   double* tstate = scal + 2;
 
   hipError_t e;
+  SideStream ss;
+  if ((e = ss.init()) != hipSuccess) return e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
-  const size_t chol_lds = sizeof(double) * (b * b + b);
   const size_t joint_lds = sizeof(double) * (b * b + 2 * b);
-  const size_t dec_lds = sizeof(float) * (b * b + b * 64);
+  const size_t dec_lds = sizeof(float) * (b * b + b * kDecW);
+  hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
   const int64_t nblocks = (k + b - 1) / b;
   for (int64_t blk = 0; blk < nblocks; ++blk) {
     const int64_t c0 = blk * b;
@@ -613,31 +805,37 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     uint32_t* Uc = a.B2 + c0 * wm;
     uint32_t* Vc = a.C2 + c0 * wn;
     const int pairs = bb * (bb + 1) / 2;
+    const dim3 gram_u((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords));
+    const dim3 gram_v((pairs + 255) / 256, (unsigned)((wn + kGramWords - 1) / kGramWords));
     hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2);
     for (int it = 0; it < a.iters; ++it) {
-      // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U
-      hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GU, (int64_t)bb * bb);
-      hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Uc, wm, bb, GU);
-      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(kCholT), chol_lds, s, GU, bb, Ginv, fail);
+      // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
+      // inverse depend only on U's codes and run on the side stream while
+      // the contraction runs on the main one.
+      if ((e = hipEventRecord(ss.ev_in, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ss.side, ss.ev_in, 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, ss.side, Uc, wm, bb, GU);
+      launch_inverse(bb, GU, Ginv, fail, ss.side);
+      if ((e = hipEventRecord(ss.ev_out, ss.side)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + 63) / 64)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, Ginv, Vt, (float*)nullptr);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS);
-      hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz + b, bb, st + EXTERND_STAT_SUM_NNZ_V);
+      if ((e = hipStreamWaitEvent(s, ss.ev_out, 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, Ginv, Vt, (float*)nullptr);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V
-      hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GV, (int64_t)bb * bb);
-      hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wn + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Vc, wn, bb, GV);
-      hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(kCholT), chol_lds, s, GV, bb, Ginv, fail);
+      if ((e = hipEventRecord(ss.ev_in, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ss.side, ss.ev_in, 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, ss.side, Vc, wn, bb, GV);
+      launch_inverse(bb, GV, Ginv, fail, ss.side);
+      if ((e = hipEventRecord(ss.ev_out, ss.side)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + 63) / 64)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, Ginv, Ut, Qt);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS);
-      hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz, bb, st + EXTERND_STAT_SUM_NNZ_U);
+      if ((e = hipStreamWaitEvent(s, ss.ev_out, 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, Ginv, Ut, Qt);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U);
     }
     // joint scales from the final U, V and the last Q = R V
-    hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)bb * bb, 256)), dim3(256), 0, s, GU, (int64_t)bb * bb);
-    hipLaunchKernelGGL(k_gram, dim3((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords)), dim3(256), 0, s, Uc, wm, bb, GU);
-    hipLaunchKernelGGL(k_joint_solve, dim3(1), dim3(kCholT), joint_lds, s, GU, GV, bb, Qt, m, Uc, wm, a.D + c0, dvec, tstate, a.trace, blk, st + EXTERND_STAT_RIDGE_RETRIES);
-    hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz, bb, st + EXTERND_STAT_NNZ_B);
-    hipLaunchKernelGGL(k_sum_nnz, dim3(1), dim3(1), 0, s, nnz + b, bb, st + EXTERND_STAT_NNZ_C);
+    hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf);
+    hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
+    hipLaunchKernelGGL(k_joint_solve, dim3(1), dim3(kCholT), joint_lds, s, GUf, GVf, bb, Qt, m, Uc, wm, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
     hipLaunchKernelGGL(k_block_deflate, dim3((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
