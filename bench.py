@@ -22,6 +22,27 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and MFMA), published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
+# Measured HBM traffic of one k_seq_resident launch on the 2560 x 2560
+# workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
+# same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
+# reported only while the kernel's sources hash to the ones it was taken on.
+SEQ_TRAFFIC_BYTES = 53914193734
+SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
+                       "ternary_rank_weight_amd/csrc/device_common.hpp",
+                       "ternary_rank_weight_amd/csrc/kernels.hpp"]
+SEQ_TRAFFIC_SHA = "32703ca0786ab2ed"
+
+
+def seq_traffic(config):
+    import hashlib
+    h = hashlib.sha256()
+    for f in SEQ_TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if config != 2 or h.hexdigest()[:16] != SEQ_TRAFFIC_SHA:
+        return None
+    return SEQ_TRAFFIC_BYTES
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -33,7 +54,23 @@ def parse():
                     help="components of the oracle's sequential run timed as the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2])
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
+                         "exit; its HBM counters calibrate the per-kernel traffic figures")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": mib << 20, "copy_probe_bytes_written": mib << 20,
+                      "launches": 5}), flush=True)
 
 
 def seq_alg_bytes(m, n, k, iters, sum_nnz_u):
@@ -75,6 +112,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import numpy as np
     import torch
     import synthetic
@@ -106,12 +146,14 @@ def main():
                                          stats=True, out=outs.get(md))
             e1.record()
             ev[md] = (e0, e1)
+            print(f"[bench] {md} launched", file=sys.stderr, flush=True)
         if record is not None:
             record.append(ev)
 
     for _ in range(args.warmup):
         run_step(None)
     torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
     records = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -140,7 +182,8 @@ def main():
         s["gbps"] = achieved
         roofline = {"bound": "hbm", "kernel": "k_seq_resident", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": None}
+                    "traffic": seq_traffic(args.config), "traffic_unit": "bytes per launch",
+                    "alg_bytes_per_launch": alg}
     if "block" in per_mode:
         bm = per_mode["block"]
         fl = block_alg_flops(m, n, k, b, c["iters"])
