@@ -94,6 +94,13 @@ typedef struct externd_opts {
   int8_t* capture_v;      /* iters*n: v_t */
   int8_t* capture_u;      /* iters*m: u_t (u_0 is the seeded start) */
   float* capture_d;       /* 1: the component's scale */
+  /* Caller-owned device workspace (optional).  When non-NULL it must be
+   * 256-byte aligned and hold at least externd_workspace_bytes(...) bytes for
+   * the same arguments; the library then allocates nothing.  Its contents are
+   * scratch: nothing is expected in it and nothing is left for the caller.
+   * Two calls in flight at once must not share one workspace. */
+  void* workspace;
+  uint64_t workspace_bytes;
 } externd_opts;
 
 /*
@@ -107,8 +114,9 @@ typedef struct externd_opts {
  * Outputs (device): B2 [k][ceil(m/16)] u32, C2 [k][ceil(n/16)] u32, D [k] fp32,
  *   energy [1] fp64 = 1 - ||A - B diag(D) C||^2 / ||A||^2 of the fp32 residual
  *   (1 when ||A|| = 0; NaN when A has non-finite entries).
- * A is not modified.  Workspace is allocated stream-ordered and freed before
- * return is observed by the stream.
+ * A is not modified.  Workspace is opts->workspace when given (EXTERND_ENOMEM if
+ * smaller than externd_workspace_bytes, EXTERND_EINVAL if not 256-byte
+ * aligned), else allocated and freed stream-ordered on `stream`.
  */
 int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
                       int32_t iters, int32_t block, void* stream,
@@ -134,6 +142,14 @@ int32_t externd_block_width(int64_t m, int64_t n, int32_t block);
 
 /* 1 if the resident sequential kernel can hold an m x n residual on chip. */
 int32_t externd_resident_fits(int64_t m, int64_t n);
+
+/* Bytes of device workspace externd_decompose needs for these arguments
+ * (mode as in externd_opts.mode; it only matters for the sequential path).
+ * Without opts->workspace the library allocates this much stream-ordered
+ * (hipMallocAsync) and frees it stream-ordered before returning.  Returns 0
+ * for invalid arguments, or when the AUTO/RESIDENT choice needs the device
+ * and no gfx950 device is current; externd_last_error() says which. */
+uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, int32_t mode);
 
 /* ---- single-step entry points (the same device routines as the streaming path) ---- */
 

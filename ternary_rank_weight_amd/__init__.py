@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "decompose", "energy", "reconstruct", "rank", "block_width", "resident_fits",
+    "decompose", "energy", "reconstruct", "rank", "block_width", "resident_fits", "workspace_bytes",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
     "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
 ]
@@ -29,7 +29,7 @@ STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is missing; build it with "
-                      "`python -m ternary_rank_weight_amd.build`")
+                      "`python ternary_rank_weight_amd/build.py`")
 _lib = ctypes.CDLL(library_path)
 
 _p = ctypes.c_void_p
@@ -47,6 +47,7 @@ class _Opts(ctypes.Structure):
         ("capture_R", _p), ("capture_Rcol", _p), ("capture_R_next", _p),
         ("capture_y", _p), ("capture_x", _p), ("capture_v", _p), ("capture_u", _p),
         ("capture_d", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -64,6 +65,7 @@ _reconstruct = _sig("externd_reconstruct", ctypes.c_int, [_p, _p, _p, _i64, _i64
 _rank = _sig("externd_rank", ctypes.c_int64, [_i64, _i64, _f32])
 _block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
 _resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
+_workspace_bytes = _sig("externd_workspace_bytes", ctypes.c_uint64, [_i64, _i64, _f32, _i32, _i32])
 _ternarize = _sig("externd_ternarize", ctypes.c_int, [_p, _i64, _f32, _p, _p, _p])
 _gemv_t = _sig("externd_gemv_t", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
 _gemv_n = _sig("externd_gemv_n", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
@@ -73,7 +75,8 @@ _last_error = _sig("externd_last_error", ctypes.c_char_p, [])
 
 # Every exported symbol of the C ABI, for load checks.
 ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_rank",
-               "externd_block_width", "externd_resident_fits", "externd_ternarize",
+               "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
+               "externd_ternarize",
                "externd_gemv_t", "externd_gemv_n", "externd_deflate",
                "externd_status_string", "externd_last_error")
 
@@ -120,6 +123,11 @@ def resident_fits(m, n):
     return bool(_resident_fits(m, n))
 
 
+def workspace_bytes(m, n, mu, block=0, mode=MODE_AUTO):
+    """Device workspace externd_decompose needs for these arguments (0: invalid)."""
+    return int(_workspace_bytes(m, n, mu, block, mode))
+
+
 class Decomposition:
     """Device outputs of one decomposition.
 
@@ -139,12 +147,15 @@ class Decomposition:
 
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
-              capture=None, out=None):
+              capture=None, out=None, workspace=None):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
     intermediate vectors and residuals are recorded (sequential path only).
     out: optional Decomposition whose B2/C2/D/energy buffers are reused.
+    workspace: optional contiguous CUDA tensor used as the library's scratch
+    memory (at least workspace_bytes(...) bytes, 256-byte aligned); the
+    library then allocates nothing.
     """
     _need(A, torch.float32, "A")
     if A.dim() != 2:
@@ -172,6 +183,12 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     opts.trace = _ptr(tr)
     opts.stats = _ptr(st)
     opts.capture_component = -1
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+                or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous CUDA tensor")
+        opts.workspace = _ptr(workspace)
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
     cap = None
     if capture is not None:
         cap = {

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -64,12 +65,14 @@ bool bad_size(int64_t m, int64_t n) {
          m * n > (int64_t(1) << 40);
 }
 
-// Stream-ordered workspace: allocated on the stream, freed on the stream.
+// Stream-ordered workspace: allocated on the stream, freed on the stream
+// (or borrowed from the caller, then never freed here).
 struct Workspace {
   void* ptr = nullptr;
   hipStream_t s = nullptr;
+  bool owned = false;
   ~Workspace() {
-    if (ptr) (void)hipFreeAsync(ptr, s);
+    if (ptr && owned) (void)hipFreeAsync(ptr, s);
   }
 };
 
@@ -80,6 +83,20 @@ int alloc_ws(Workspace& w, size_t bytes, hipStream_t s) {
     w.ptr = nullptr;
     return fail(EXTERND_ENOMEM, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
   }
+  w.owned = true;
+  return EXTERND_OK;
+}
+
+// The caller's workspace when opts provides one (checked against `bytes`),
+// else a stream-ordered allocation.
+int get_ws(Workspace& w, const externd_opts& o, size_t bytes, hipStream_t s) {
+  if (!o.workspace) return alloc_ws(w, bytes, s);
+  if (o.workspace_bytes < bytes)
+    return fail(EXTERND_ENOMEM, "workspace of %llu bytes < %zu needed",
+                (unsigned long long)o.workspace_bytes, bytes);
+  w.ptr = o.workspace;
+  w.s = s;
+  w.owned = false;
   return EXTERND_OK;
 }
 
@@ -121,6 +138,22 @@ int32_t externd_resident_fits(int64_t m, int64_t n) {
   return externd::resident_fits(m, n, cus) ? 1 : 0;
 }
 
+uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, int32_t mode) {
+  if (bad_size(m, n)) return (fail(EXTERND_EINVAL, "bad shape"), 0);
+  if (!std::isfinite(mu) || mu <= 0.f) return (fail(EXTERND_EINVAL, "mu must be finite and > 0"), 0);
+  if (mode < -1 || mode > 1) return (fail(EXTERND_EINVAL, "bad mode %d", mode), 0);
+  const int b = externd_block_width(m, n, block);
+  if (b > 1) return externd::block_workspace_bytes(m, n, b);
+  if (mode == EXTERND_MODE_STREAMING) return externd::stream_workspace_bytes(m, n);
+  int cus = 0;
+  if (check_device(&cus) != EXTERND_OK) return 0;
+  const bool fits = externd::resident_fits(m, n, cus);
+  if (mode == EXTERND_MODE_RESIDENT && !fits)
+    return (fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel",
+                 (long long)m, (long long)n), 0);
+  return fits ? externd::resident_workspace_bytes(m, n) : externd::stream_workspace_bytes(m, n);
+}
+
 int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau, int32_t iters,
                       int32_t block, void* stream, uint32_t* B2, uint32_t* C2, float* D,
                       double* energy, const externd_opts* opts) {
@@ -143,6 +176,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     o = *opts;
   }
   if (o.mode < -1 || o.mode > 1) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
+  if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
+    return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
   int cus = 0;
   int st = check_device(&cus);
   if (st != EXTERND_OK) return st;
@@ -166,7 +201,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.trace = o.trace;
     ba.stats = reinterpret_cast<long long*>(o.stats);
     Workspace w;
-    if ((st = alloc_ws(w, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
+    if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);
     if (e != hipSuccess) return hip_fail(e, "block decomposition");
     return EXTERND_OK;
@@ -209,12 +244,12 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   Workspace w;
   hipError_t e;
   if (mode == EXTERND_MODE_RESIDENT) {
-    if ((st = alloc_ws(w, externd::resident_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+    if ((st = get_ws(w, o, externd::resident_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
     int grid = 0;
     e = externd::run_resident_seq(sa, w.ptr, cus, s, &grid);
     if (e != hipSuccess) return hip_fail(e, "resident decomposition");
   } else {
-    if ((st = alloc_ws(w, externd::stream_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+    if ((st = get_ws(w, o, externd::stream_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
     e = externd::run_stream_seq(sa, w.ptr, s);
     if (e != hipSuccess) return hip_fail(e, "streaming decomposition");
   }

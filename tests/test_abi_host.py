@@ -15,8 +15,8 @@ LIB = os.path.join(ROOT, "ternary_rank_weight_amd", "libexternd.so")
 @pytest.fixture(scope="module")
 def clib():
     if not os.path.exists(LIB):
-        from ternary_rank_weight_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__.build()
     return ctypes.CDLL(LIB)
 
 
@@ -111,3 +111,33 @@ def test_single_step_entry_points_validate(clib):
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                     ctypes.c_void_p]
     assert clib.externd_energy(fake, 4, 4, None, None, None, 3, None, fake) == 1
+
+
+def test_workspace_bytes_without_device():
+    import ternary_rank_weight_amd as trw
+    # block and streaming sizes depend on the shape only
+    blk = trw.workspace_bytes(2560, 2560, 2.0, 64)
+    assert blk > 0 and blk == trw.workspace_bytes(2560, 2560, 3.0, 64)
+    assert trw.workspace_bytes(9728, 2560, 3.0, 128) > blk
+    st = trw.workspace_bytes(2560, 2560, 2.0, 0, trw.MODE_STREAMING)
+    assert st > 0
+    assert trw.workspace_bytes(0, 5, 1.0, 0, trw.MODE_STREAMING) == 0
+    assert trw.workspace_bytes(5, 5, float("nan"), 0, trw.MODE_STREAMING) == 0
+    assert trw.workspace_bytes(5, 5, 1.0, 0, 7) == 0
+
+
+def test_decompose_rejects_misaligned_workspace(clib):
+    import ternary_rank_weight_amd as trw
+    f = _decompose_args(clib)
+    f.argtypes = f.argtypes[:-1] + [ctypes.POINTER(trw._Opts)]
+    o = trw._Opts()
+    o.struct_size = ctypes.sizeof(trw._Opts)
+    o.mode = trw.MODE_AUTO
+    o.capture_component = -1
+    o.workspace = ctypes.c_void_p(0x1000 + 8)
+    o.workspace_bytes = 1 << 30
+    fake = 0x1000
+    st = f(fake, 16, 16, 1.0, 0.7, 15, 0, None, fake, fake, fake, fake, ctypes.byref(o))
+    assert st == 1
+    clib.externd_last_error.restype = ctypes.c_char_p
+    assert b"aligned" in clib.externd_last_error()

@@ -1,0 +1,52 @@
+"""Caller-owned workspace: decompositions run in a workspace the caller
+allocated (filled with garbage first, reused across calls) give bit-identical
+outputs to runs where the library allocates its own; a workspace smaller
+than externd_workspace_bytes is rejected with EXTERND_ENOMEM."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+def _aligned_workspace(nbytes):
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + nbytes]
+    assert ws.data_ptr() % 256 == 0
+    ws.fill_(0xA5)
+    return ws
+
+
+CASES = [  # (m, n, mu, tau, block, mode)
+    (256, 256, 2.0, 0.7, 0, 1),     # resident sequential
+    (300, 200, 0.5, 0.7, 0, 0),     # streaming sequential
+    (256, 256, 1.0, 0.7, 32, -1),   # block
+]
+
+
+@pytest.mark.parametrize("m,n,mu,tau,block,mode", CASES)
+def test_caller_workspace_matches_library_allocation(lib, m, n, mu, tau, block, mode):
+    A = torch.from_numpy(synthetic.gaussian(m, n, 5)).cuda()
+    need = lib.workspace_bytes(m, n, mu, block, mode)
+    assert need > 0
+    ref = lib.decompose(A, mu, tau, 15, block, 1, mode=mode, stats=True)
+    ws = _aligned_workspace(need)
+    for _ in range(2):   # the second call finds the first call's leftovers
+        got = lib.decompose(A, mu, tau, 15, block, 1, mode=mode, stats=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got.B2, ref.B2) and torch.equal(got.C2, ref.C2)
+        assert torch.equal(got.D, ref.D) and torch.equal(got.energy, ref.energy)
+        assert torch.equal(got.stats, ref.stats)
+
+
+def test_workspace_too_small_is_rejected(lib):
+    A = torch.from_numpy(synthetic.gaussian(64, 48, 1)).cuda()
+    need = lib.workspace_bytes(64, 48, 1.0, 0, lib.MODE_AUTO)
+    ws = _aligned_workspace(need - 256)
+    with pytest.raises(lib.ExterndError) as ei:
+        lib.decompose(A, 1.0, 0.7, 15, 0, 0, workspace=ws)
+    assert ei.value.status == 2
+    np.testing.assert_equal(need > 256, True)
