@@ -26,11 +26,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
 # same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
 # reported only while the kernel's sources hash to the ones it was taken on.
-SEQ_TRAFFIC_BYTES = 53914193734
+SEQ_TRAFFIC_BYTES = 38937725050
 SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
                        "ternary_rank_weight_amd/csrc/device_common.hpp",
                        "ternary_rank_weight_amd/csrc/kernels.hpp"]
-SEQ_TRAFFIC_SHA = "32703ca0786ab2ed"
+SEQ_TRAFFIC_SHA = "06e28fa14817eb6f"
 
 
 def seq_traffic(config):

@@ -13,12 +13,18 @@
 // and columns (row copy) it multiplies, so the vectors never move through LDS.
 //
 // Exchange.  After a half-step every workgroup publishes its finished outputs
-// (RB values of x or CB values of y) as 64-bit words {round:32 | value:32}
-// written with agent-scope atomic stores, then reads all m (or n) words with
-// agent-scope atomic loads until each carries the current round.  Value and
-// round share one atomic word, so no fence or grid barrier is needed; one
-// exchange per half-step, two per ALS iteration.  Every workgroup then holds
-// the whole vector and applies T_tau (§2.2) redundantly and identically.
+// (RB values of x or CB values of y) as 32-bit words whose lowest bit is
+// replaced by the parity of the round (the value keeps 31 bits: at most one
+// unit in the last place, always toward zero once the reader clears the bit),
+// written with agent-scope atomic stores.  It then reads all m (or n) words
+// with agent-scope atomic loads until each carries the current parity.  A
+// word cannot be overwritten with the next round of the same parity before
+// every workgroup has read it, because nobody publishes round r+1 before it
+// has gathered all of round r; coherence of the single word then rules out
+// reading a value two rounds old.  Value and tag share one atomic word, so no
+// fence or grid barrier is needed: one exchange per half-step, two per ALS
+// iteration.  Every workgroup then holds the whole vector (the same bits in
+// every workgroup) and applies T_tau (§2.2) redundantly and identically.
 //
 // Termination.  Every wait is bounded: a workgroup that waits too long sets a
 // device error flag and the whole grid returns; the host reports EHIP.
@@ -45,8 +51,8 @@ struct ResArgs {
   long long* stats;            // EXTERND_STATS_LEN, written by workgroup 0
   const double* a2;            // ||A||^2
   const long long* nonfinite;  // count of non-finite entries of A
-  unsigned long long* yslot;   // n words
-  unsigned long long* xslot;   // m words
+  unsigned* yslot;             // n words
+  unsigned* xslot;             // m words
   unsigned* err;
   double* r2_partial;          // G fp64
   int64_t cap_i;
@@ -60,15 +66,17 @@ struct ResArgs {
   float* cap_d;
 };
 
-__device__ inline unsigned long long ll_pack(unsigned round, float v) {
-  return ((unsigned long long)round << 32) | (unsigned long long)__float_as_uint(v);
+// Exchange word: the value with its lowest bit replaced by the round parity.
+__device__ inline unsigned xw_pack(unsigned round, float v) {
+  return (__float_as_uint(v) & ~1u) | (round & 1u);
 }
+__device__ inline float xw_value(unsigned w) { return __uint_as_float(w & ~1u); }
 
 // Sum acc[l] over the T threads for l < L (DPP inside each wave, then the
 // waves in index order) and publish output l < nvalid as slot[base + l].
 template <int T, int L>
 __device__ inline void reduce_publish(const float (&acc)[L], float* red, int nvalid,
-                                      unsigned long long* slot, int base, unsigned round) {
+                                      unsigned* slot, int base, unsigned round) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
   float sums[L];
@@ -83,7 +91,7 @@ __device__ inline void reduce_publish(const float (&acc)[L], float* red, int nva
     float s = red[t];
 #pragma unroll
     for (int q = 1; q < T / kWave; ++q) s += red[q * L + t];
-    __hip_atomic_store(slot + base + t, ll_pack(round, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot + base + t, xw_pack(round, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -178,22 +186,22 @@ __device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, 
 // Read the n (or m) published words of the current round into val[j] for
 // index t + T*j.  Returns false if a wait ran out.
 template <int T, int K>
-__device__ inline bool gather(const unsigned long long* slot, int N, unsigned round, float (&val)[K],
+__device__ inline bool gather(const unsigned* slot, int N, unsigned round, float (&val)[K],
                               const unsigned* err) {
   const int t = threadIdx.x;
-  unsigned long long w[K];
+  const unsigned par = round & 1u;
+  unsigned w[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int idx = t + T * j;
-    w[j] = idx < N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : ll_pack(round, 0.f);
+    w[j] = idx < N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : par;
   }
   unsigned spins = 0;
   bool ok = true;
   while (true) {
     bool all = true;
 #pragma unroll
-    for (int j = 0; j < K; ++j) all = all && (unsigned)(w[j] >> 32) == round;
+    for (int j = 0; j < K; ++j) all = all && (w[j] & 1u) == par;
     if (all) break;
     if (++spins > kSpinLimit) { ok = false; break; }
     if ((spins & 255u) == 0 &&
@@ -204,12 +212,12 @@ __device__ inline bool gather(const unsigned long long* slot, int N, unsigned ro
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int idx = t + T * j;
-      if ((unsigned)(w[j] >> 32) != round)
+      if ((w[j] & 1u) != par)
         w[j] = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 #pragma unroll
-  for (int j = 0; j < K; ++j) val[j] = ok ? __uint_as_float((unsigned)w[j]) : 0.f;
+  for (int j = 0; j < K; ++j) val[j] = ok ? xw_value(w[j]) : 0.f;
   return ok;
 }
 
@@ -645,8 +653,8 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   ra.stats = a.stats;
   ra.a2 = a2;
   ra.nonfinite = nonfinite;
-  ra.yslot = yslot;
-  ra.xslot = xslot;
+  ra.yslot = reinterpret_cast<unsigned*>(yslot);   // 32-bit words; zero = parity 0
+  ra.xslot = reinterpret_cast<unsigned*>(xslot);
   ra.err = err;
   ra.r2_partial = r2p;
   ra.cap_i = a.capture_component;
