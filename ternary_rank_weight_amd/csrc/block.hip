@@ -53,117 +53,83 @@ __global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint
 
 // ---------------------------------------------------------------------------
 // Exact Gram matrix G = X^T X of a ternary block held as 2-bit code rows
-// (X's column i = code row i, length L).  Integer sums of popcounts,
-// accumulated with atomics (exact, so order-free).  G must be zeroed.
-// grid.x = pair tiles, grid.y = word chunks.
+// (X's column i = code row i, wl words).  Workgroup (tile, split) owns the
+// 16 x 16 tile (I, J), I >= J, of G over the words [split * kGramSplit, ...):
+// it stages the 32 code rows of the tile in LDS with coalesced loads, thread
+// (r, c) takes the pair (16I + r, 16J + c), and the integer partial sums go to
+// G with atomics (exact, so order-free).  Per word pair, the product sum is
+// popcount(both nonzero) - 2 popcount(both nonzero, signs differ).  G must be
+// zeroed beforehand.
 // ---------------------------------------------------------------------------
-constexpr int kGramWords = 32;
+constexpr int kGramChunk = 64;    // words per LDS stage
+constexpr int kGramSplit = 64;    // words per workgroup (one LDS stage)
 
-__global__ void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb, int* __restrict__ G) {
-  const int pairs = bb * (bb + 1) / 2;
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= pairs) return;
-  // p -> (i, j) with j <= i
-  int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-  while ((i + 1) * (i + 2) / 2 <= p) ++i;
-  while (i * (i + 1) / 2 > p) --i;
-  const int j = p - i * (i + 1) / 2;
-  const int64_t w0 = (int64_t)blockIdx.y * kGramWords;
-  const int64_t w1 = min(wl, w0 + kGramWords);
-  const uint32_t* a = codes + (int64_t)i * wl;
-  const uint32_t* b = codes + (int64_t)j * wl;
-  int acc = 0;
-  for (int64_t w = w0; w < w1; ++w) {
-    const uint32_t x = a[w], y = b[w];
-    const uint32_t both = x & y & 0x55555555u;
-    const uint32_t neg = ((x ^ y) >> 1) & both;
-    acc += __popc(both) - 2 * __popc(neg);
+__global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb,
+                                              int* __restrict__ G) {
+  __shared__ uint32_t rows[32][kGramChunk + 1];
+  const int t = threadIdx.x;
+  // triangular tile index -> (I, J), J <= I
+  int I = 0;
+  while ((I + 1) * (I + 2) / 2 <= (int)blockIdx.x) ++I;
+  const int J = (int)blockIdx.x - I * (I + 1) / 2;
+  const int r = t >> 4, c = t & 15;
+  const int i = 16 * I + r, j = 16 * J + c;
+  const int64_t w_begin = (int64_t)blockIdx.y * kGramSplit;
+  const int64_t w_end = min(wl, w_begin + kGramSplit);
+  unsigned pos = 0u, neg = 0u;
+  for (int64_t w0 = w_begin; w0 < w_end; w0 += kGramChunk) {
+    const int cw = (int)min<int64_t>(kGramChunk, w_end - w0);
+    __syncthreads();
+    for (int e = t; e < 32 * kGramChunk; e += 256) {
+      const int row = e / kGramChunk, w = e % kGramChunk;
+      const int comp = row < 16 ? 16 * I + row : 16 * J + row - 16;
+      rows[row][w] = (w < cw && comp < bb) ? codes[(int64_t)comp * wl + w0 + w] : 0u;
+    }
+    __syncthreads();
+    for (int w = 0; w < cw; ++w) {
+      const uint32_t x = rows[r][w], y = rows[16 + c][w];
+      const uint32_t both = x & y & 0x55555555u;
+      pos += __popc(both);
+      neg += __popc(((x ^ y) >> 1) & both);
+    }
   }
-  if (acc != 0) {
+  const int acc = (int)pos - 2 * (int)neg;
+  if (i < bb && j < bb && acc != 0) {
     atomicAdd(G + i * bb + j, acc);
-    if (i != j) atomicAdd(G + j * bb + i, acc);
+    if (I != J) atomicAdd(G + j * bb + i, acc);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Small dense fp64 linear algebra on one workgroup: an in-LDS Cholesky
-// factorisation (used by the joint scale solve) and the SPD inverse of a
-// Gram matrix (used to decorrelate the ALS targets).
+// Small dense fp64 linear algebra on one workgroup: the inverse of a
+// symmetric positive definite matrix, used to decorrelate the ALS targets
+// and to solve for the joint scales.
 // ---------------------------------------------------------------------------
 constexpr int kCholT = 256;
 
-__device__ void chol_lds(double* A, int bb, int* fail) {
-  const int t = threadIdx.x;
-  const int ti = t >> 4, tj = t & 15;   // 16 x 16 thread grid
-  for (int k = 0; k < bb; ++k) {
-    __syncthreads();
-    const double piv = A[k * bb + k];
-    if (!(piv > 0.0)) {
-      if (t == 0) *fail = 1;
-      return;
-    }
-    // trailing update with the unscaled column k: A_ij -= A_ik A_jk / piv, k < j <= i
-    const double inv = 1.0 / piv;
-    for (int i = k + 1 + ti; i < bb; i += 16) {
-      const double aik = A[i * bb + k] * inv;
-      for (int j = k + 1 + tj; j <= i; j += 16) A[i * bb + j] -= aik * A[j * bb + k];
-    }
-    __syncthreads();
-    const double lkk = sqrt(piv);
-    for (int i = k + 1 + t; i < bb; i += kCholT) A[i * bb + k] /= lkk;
-    if (t == 0) A[k * bb + k] = lkk;
-  }
-  __syncthreads();
-}
-
-// Ginv = (G + eps I)^-1, eps = 1e-6 trace(G)/b, by blocked Gauss-Jordan
-// elimination in fp64, four pivots per step (no pivoting: the matrix is
-// symmetric positive definite, and so is every 4 x 4 pivot block of its
-// Schur complements).  With K the pivot rows and R the rest, one step maps
+// In-place inverse of a symmetric positive definite matrix held in registers
+// by blocked Gauss-Jordan elimination in fp64, four pivots per step (no
+// pivoting: every 4 x 4 pivot block of the Schur complements of an SPD matrix
+// is SPD).  With K the pivot rows and R the rest, one step maps
 //   A_KK -> P = A_KK^-1,   A_KR -> P A_KR,   A_RK -> -A_RK P,
 //   A_RR -> A_RR - (A_RK P) A_KR.
-// Thread (ti, tj) of a 16 x 16 grid keeps entries (ti + 16x, tj + 16y) in
-// registers; indices from bb up to 16 NA are padded with the identity, so a
-// trailing partial pivot block stays invertible and decoupled.  The owners of
-// the pivot rows and columns publish them in LDS (double-buffered, so one
-// barrier per step suffices) with the K x K part zeroed, and every thread
-// inverts the 4 x 4 pivot block itself.  G is integer valued and is zeroed
-// after being read so the next Gram accumulation starts from zero.  `fail` is
-// set when a pivot is not positive.  One workgroup.
+// Thread (ti, tj) of a 16 x 16 grid keeps entries (ti + 16x, tj + 16y);
+// entries from bb up to 16 NA must hold the identity, so a trailing partial
+// pivot block stays invertible and decoupled.  The owners of the pivot rows
+// and columns publish them in LDS (double-buffered, so one barrier per step
+// suffices) with the K x K part zeroed, and every thread inverts the 4 x 4
+// pivot block itself.  Returns false (the same in every thread) when a pivot
+// is not positive, i.e. when the matrix is not positive definite.
+struct GjShared {
+  double prow[2][kMaxB][4];   // prow[j][l] = A[K_l][j], zero for j in K
+  double pcol[2][kMaxB][4];   // pcol[i][l] = A[i][K_l], zero for i in K
+  double pkk[2][4][4];        // A_KK
+};
+
 template <int NA>  // bb <= 16 * NA
-__global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int bb,
-                                                        float* __restrict__ Ginv, int* __restrict__ fail) {
-  __shared__ double prow[2][kMaxB][4];   // prow[j][l] = A[K_l][j], zero for j in K
-  __shared__ double pcol[2][kMaxB][4];   // pcol[i][l] = A[i][K_l], zero for i in K
-  __shared__ double pkk[2][4][4];        // A_KK
-  __shared__ double s_diag[kMaxB];
-  __shared__ double s_eps;
+__device__ bool gj_inverse(double (&a)[NA][NA], int bb, GjShared& sh) {
   const int t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
-  double a[NA][NA];
-#pragma unroll
-  for (int x = 0; x < NA; ++x)
-#pragma unroll
-    for (int y = 0; y < NA; ++y) {
-      const int i = ti + 16 * x, j = tj + 16 * y;
-      const bool in = i < bb && j < bb;
-      a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
-      if (in) G[i * bb + j] = 0;
-      if (in && i == j) s_diag[i] = a[x][y];
-    }
-  __syncthreads();
-  if (t == 0) {
-    double tr = 0.0;
-    for (int i = 0; i < bb; ++i) tr += s_diag[i];
-    s_eps = 1e-6 * tr / bb;
-  }
-  __syncthreads();
-  const double eps = s_eps;
-#pragma unroll
-  for (int x = 0; x < NA; ++x)
-#pragma unroll
-    for (int y = 0; y < NA; ++y)
-      if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
   const int kq_r = ti >> 2, la = ti & 3;   // rows of a wave form one pivot quad
   const int kq_c = tj >> 2, lc = tj & 3;
   bool ok = true;
@@ -177,12 +143,12 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
       const bool cown = kq_c == kq;
       if (rown) {
 #pragma unroll
-        for (int y = 0; y < NA; ++y) prow[bf][tj + 16 * y][la] = (y == kx && cown) ? 0.0 : a[kx][y];
-        if (cown) pkk[bf][la][lc] = a[kx][kx];
+        for (int y = 0; y < NA; ++y) sh.prow[bf][tj + 16 * y][la] = (y == kx && cown) ? 0.0 : a[kx][y];
+        if (cown) sh.pkk[bf][la][lc] = a[kx][kx];
       }
       if (cown) {
 #pragma unroll
-        for (int x = 0; x < NA; ++x) pcol[bf][ti + 16 * x][lc] = (x == kx && rown) ? 0.0 : a[x][kx];
+        for (int x = 0; x < NA; ++x) sh.pcol[bf][ti + 16 * x][lc] = (x == kx && rown) ? 0.0 : a[x][kx];
       }
       __syncthreads();
       // P = A_KK^-1 in registers; reciprocals by rcp and two Newton steps
@@ -190,7 +156,7 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) p[r][c] = pkk[bf][r][c];
+        for (int c = 0; c < 4; ++c) p[r][c] = sh.pkk[bf][r][c];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const double piv = p[q][q];
@@ -219,7 +185,7 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
       for (int x = 0; x < NA; ++x) {
         double c4[4];
 #pragma unroll
-        for (int l = 0; l < 4; ++l) c4[l] = pcol[bf][ti + 16 * x][l];
+        for (int l = 0; l < 4; ++l) c4[l] = sh.pcol[bf][ti + 16 * x][l];
 #pragma unroll
         for (int l = 0; l < 4; ++l) {
           double s = c4[0] * p[0][l];
@@ -231,7 +197,7 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
 #pragma unroll
       for (int y = 0; y < NA; ++y)
 #pragma unroll
-        for (int l = 0; l < 4; ++l) pr[y][l] = prow[bf][tj + 16 * y][l];
+        for (int l = 0; l < 4; ++l) pr[y][l] = sh.prow[bf][tj + 16 * y][l];
 #pragma unroll
       for (int x = 0; x < NA; ++x)
 #pragma unroll
@@ -265,6 +231,46 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
       }
     }
   }
+  return ok;
+}
+
+// Ginv = (G + eps I)^-1 with eps = 1e-6 trace(G)/b (fp64, written as fp32).
+// G is integer valued and is zeroed after being read so the next Gram
+// accumulation starts from zero.  `fail` is set if G + eps I is not positive
+// definite.  One workgroup.
+template <int NA>  // bb <= 16 * NA
+__device__ __forceinline__ void spd_inverse_body(int* __restrict__ G, int bb, float* __restrict__ Ginv,
+                                 int* __restrict__ fail) {
+  __shared__ GjShared sh;
+  __shared__ double s_diag[kMaxB];
+  __shared__ double s_eps;
+  const int t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;
+  double a[NA][NA];
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y) {
+      const int i = ti + 16 * x, j = tj + 16 * y;
+      const bool in = i < bb && j < bb;
+      a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
+      if (in) G[i * bb + j] = 0;
+      if (in && i == j) s_diag[i] = a[x][y];
+    }
+  __syncthreads();
+  if (t == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < bb; ++i) tr += s_diag[i];
+    s_eps = 1e-6 * tr / bb;
+  }
+  __syncthreads();
+  const double eps = s_eps;
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y)
+      if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
+  const bool ok = gj_inverse<NA>(a, bb, sh);
   if (!ok && t == 0) *fail = 1;
 #pragma unroll
   for (int x = 0; x < NA; ++x)
@@ -275,6 +281,12 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
     }
 }
 
+template <int NA>
+__global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int bb,
+                                                        float* __restrict__ Ginv, int* __restrict__ fail) {
+  spd_inverse_body<NA>(G, bb, Ginv, fail);
+}
+
 // ---------------------------------------------------------------------------
 // Contraction 1: Pt_part[s][i][c] = sum_{r in chunk s} U[r][i] R[r][c].
 // grid (ceil(n/64), S); 4 waves, wave w owns columns c0 + 16w .. +15 and all
@@ -283,14 +295,13 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int
 // ---------------------------------------------------------------------------
 constexpr int kCT = 256;
 
-__global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__ R, int64_t m, int64_t n,
-                                                       const uint32_t* __restrict__ Ucodes, int64_t wm,
-                                                       int bb, int64_t rows_per_split,
-                                                       float* __restrict__ Pt_part) {
+__device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, int64_t m, int64_t n,
+                                   const uint32_t* __restrict__ Ucodes, int64_t wm, int bb,
+                                   int64_t rows_per_split, float* __restrict__ Pt_part, int bx, int by) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane & 15, k = lane >> 4;
-  const int64_t col = (int64_t)blockIdx.x * 64 + 16 * w + j;
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t col = (int64_t)bx * 64 + 16 * w + j;
+  const int64_t r_begin = (int64_t)by * rows_per_split;
   const int64_t r_end = min(m, r_begin + rows_per_split);
   const int nsub = (bb + 15) / 16;
   f4 acc[kMaxB / 16];
@@ -343,10 +354,17 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
       for (int v = 0; v < 4; ++v) {
         const int comp = 16 * s + 4 * k + v;
         if (comp < bb && col < n)
-          Pt_part[((int64_t)blockIdx.y * bb + comp) * n + col] = acc[s][v];
+          Pt_part[((int64_t)by * bb + comp) * n + col] = acc[s][v];
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__ R, int64_t m, int64_t n,
+                                                       const uint32_t* __restrict__ Ucodes, int64_t wm,
+                                                       int bb, int64_t rows_per_split,
+                                                       float* __restrict__ Pt_part) {
+  contract_ut_r_body(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,14 +374,13 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
 // float4 and feeds component q at MFMA step q (column c + 4k + q); the V
 // operand of lane (comp + 16k) uses the same column.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
-                                                      const uint32_t* __restrict__ Vcodes, int64_t wn,
-                                                      int bb, int64_t cols_per_split,
-                                                      float* __restrict__ Qt_part) {
+__device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, int64_t m, int64_t n,
+                                  const uint32_t* __restrict__ Vcodes, int64_t wn, int bb,
+                                  int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
-  const int64_t row = (int64_t)blockIdx.x * 64 + 16 * w + i;
-  const int64_t c_begin = (int64_t)blockIdx.y * cols_per_split;
+  const int64_t row = (int64_t)bx * 64 + 16 * w + i;
+  const int64_t c_begin = (int64_t)by * cols_per_split;
   const int64_t c_end = min(n, c_begin + cols_per_split);
   const int nsub = (bb + 15) / 16;
   const bool vec_ok = (n % 4) == 0;
@@ -418,11 +435,35 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
       const int comp = 16 * s + i;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t rr = (int64_t)blockIdx.x * 64 + 16 * w + 4 * k + v;
-        if (comp < bb && rr < m) Qt_part[((int64_t)blockIdx.y * bb + comp) * m + rr] = acc[s][v];
+        const int64_t rr = (int64_t)bx * 64 + 16 * w + 4 * k + v;
+        if (comp < bb && rr < m) Qt_part[((int64_t)by * bb + comp) * m + rr] = acc[s][v];
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
+                                                      const uint32_t* __restrict__ Vcodes, int64_t wn,
+                                                      int bb, int64_t cols_per_split,
+                                                      float* __restrict__ Qt_part) {
+  contract_r_v_body(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y);
+}
+
+// The contraction with one extra workgroup, (gridDim.x - 1, 0), that inverts
+// the Gram matrix of the same codes meanwhile: both depend only on the codes
+// and R, and the decorrelation needs both.  One launch instead of two keeps
+// them concurrent without a second stream.
+template <int NA, bool UT>
+__global__ __launch_bounds__(kCT) void k_contract_with_inverse(
+    const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
+    int bb, int64_t per_split, float* __restrict__ Part, int* __restrict__ G,
+    float* __restrict__ Ginv, int* __restrict__ fail) {
+  if ((int)blockIdx.x == (int)gridDim.x - 1) {
+    if (blockIdx.y == 0) spd_inverse_body<NA>(G, bb, Ginv, fail);
+    return;
+  }
+  if (UT) contract_ut_r_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
+  else contract_r_v_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,10 +515,13 @@ constexpr int kTT = 256;
 __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__ Xt, int64_t L, float tau,
                                                        uint32_t* __restrict__ out_codes, int64_t wl,
                                                        int* __restrict__ nnz, long long* __restrict__ fb,
-                                                       long long* __restrict__ nnz_sum) {
+                                                       long long* __restrict__ nnz_sum,
+                                                       const float* __restrict__ Qrows,
+                                                       double* __restrict__ rhs_out) {
   __shared__ double scratch[kTT / kWave];
   const int i = blockIdx.x;
   const float* x = Xt + (int64_t)i * L;
+  const float* qr = rhs_out ? Qrows + (int64_t)i * L : nullptr;
   uint32_t* codes = out_codes + (int64_t)i * wl;
   const int t = threadIdx.x;
   float mx = 0.f;
@@ -486,6 +530,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   if (M == 0.f) {
     for (int64_t w = t; w < wl; w += kTT) codes[w] = (w == 0) ? 1u : 0u;
     if (t == 0) {
+      if (rhs_out) rhs_out[i] = (double)qr[0];
       nnz[i] = 1;
       atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
       atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
@@ -499,6 +544,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   const double thr = fixed_point_threshold(Q, s, tau, L);
   const uint32_t tb = threshold_bits(thr);
   int cnt = 0;
+  double rq = 0.0;   // u_i . q_i over this thread's kept entries (joint scale rhs)
   for (int64_t w = t; w < wl; w += kTT) {
     uint32_t word = 0;
     for (int e = 0; e < 16; ++e) {
@@ -508,6 +554,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
         if ((__float_as_uint(v) & 0x7fffffffu) > tb) {
           word |= code_of(v) << (2 * e);
           ++cnt;
+          if (qr) rq += v > 0.f ? (double)qr[j] : -(double)qr[j];
         }
       }
     }
@@ -516,6 +563,10 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   const uint32_t Mb = __float_as_uint(M);
   if (Mb > tb) {
     const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
+    if (rhs_out) {
+      const double r = block_sum<kTT>(rq, scratch);
+      if (t == 0) rhs_out[i] = r;
+    }
     if (t == 0) {
       nnz[i] = total;
       atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), (unsigned long long)total);
@@ -529,6 +580,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   __syncthreads();
   if (t == 0) {
     codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
+    if (rhs_out) rhs_out[i] = x[idx] > 0.f ? (double)qr[idx] : -(double)qr[idx];
     nnz[i] = 1;
     atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
     atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
@@ -537,75 +589,81 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
 
 // ---------------------------------------------------------------------------
 // Joint scale solve (§2.4): rhs_j = u_j . q_j with q_j the last Q column,
-// M = (U^T U) o (V^T V); Cholesky without ridge, retried with the ridge on
-// failure; d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
+// M = (U^T U) o (V^T V), d = M^-1 rhs in fp64.  M is inverted without a
+// ridge; if it is not positive definite (a pivot is not positive, the same
+// test a Cholesky factorisation makes) it is inverted again with the ridge
+// and the retry is counted.  d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
 // ---------------------------------------------------------------------------
+template <int NA>  // bb <= 16 * NA
 __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, int* __restrict__ GV,
-                                                        int bb, const float* __restrict__ Qt, int64_t m,
-                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
+                                                        int bb, const double* __restrict__ rhs_in,
                                                         float* __restrict__ Dout, double* __restrict__ dscratch,
                                                         double* __restrict__ trace_state,
                                                         double* __restrict__ trace, int64_t blk,
                                                         long long* __restrict__ st, const int* __restrict__ nnz,
                                                         int bstride) {
-  extern __shared__ double lds[];
-  double* A = lds;                 // bb * bb
-  double* rhs = lds + bb * bb;     // bb
-  double* d = rhs + bb;            // bb
-  __shared__ int fail;
-  const int t = threadIdx.x;
-  // rhs_j = sum_r u_rj q_rj, one wave per component (fixed order)
-  const int lane = t & 63, wv = t >> 6;
-  for (int j = wv; j < bb; j += kCholT / 64) {
-    const uint32_t* urow = Ucodes + (int64_t)j * wm;
-    double s = 0.0;
-    for (int64_t r = lane; r < m; r += 64) s += (double)tern(urow, (int)r) * (double)Qt[(int64_t)j * m + r];
-    s = wave_sum(s);
-    if (lane == 0) rhs[j] = s;
-  }
+  __shared__ GjShared sh;
+  __shared__ double rhs[kMaxB];
+  __shared__ double dsol[kMaxB];
+  __shared__ double s_diag[kMaxB];
   __shared__ double s_tr;
-  for (int attempt = 0; attempt < 2; ++attempt) {
+  const int t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;
+  for (int j = t; j < bb; j += kCholT) rhs[j] = rhs_in[j];
+  // M = (U^T U) o (V^T V); solve without a ridge, retry once with one
+  double a[NA][NA];
+  bool ok = false;
+  for (int attempt = 0; attempt < 2 && !ok; ++attempt) {
+#pragma unroll
+    for (int x = 0; x < NA; ++x)
+#pragma unroll
+      for (int y = 0; y < NA; ++y) {
+        const int i = ti + 16 * x, j = tj + 16 * y;
+        const bool in = i < bb && j < bb;
+        a[x][y] = in ? (double)GU[i * bb + j] * (double)GV[i * bb + j] : (i == j ? 1.0 : 0.0);
+        if (in && i == j) s_diag[i] = a[x][y];
+      }
     __syncthreads();
-    if (t == 0) fail = 0;
-#pragma unroll 8
-    for (int e = t; e < bb * bb; e += kCholT) A[e] = (double)GU[e] * (double)GV[e];
-    __syncthreads();
-    if (t == 0) {
-      double tr = 0.0;
-      for (int i = 0; i < bb; ++i) tr += A[i * bb + i];
-      s_tr = tr;
+    if (attempt == 1) {
+      if (t == 0) {
+        double tr = 0.0;
+        for (int i = 0; i < bb; ++i) tr += s_diag[i];
+        s_tr = tr;
+        atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_RIDGE_RETRIES), 1ull);
+      }
+      __syncthreads();
+      const double eps = 1e-6 * s_tr / bb;
+#pragma unroll
+      for (int x = 0; x < NA; ++x)
+#pragma unroll
+        for (int y = 0; y < NA; ++y)
+          if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
     }
+    ok = gj_inverse<NA>(a, bb, sh);
     __syncthreads();
-    const double eps = attempt ? 1e-6 * s_tr / bb : 0.0;
-    for (int i = t; i < bb; i += kCholT) A[i * bb + i] += eps;
-    chol_lds(A, bb, &fail);
-    __syncthreads();
-    if (!fail) break;
-    if (t == 0) atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_RIDGE_RETRIES), 1ull);
   }
-  // L y = rhs (column-oriented, parallel updates), then L^T d = y
-  for (int e = t; e < bb; e += kCholT) d[e] = rhs[e];
+  // d = M^-1 rhs: partial sums over this thread's columns, then over the 16
+  // lanes of its row group (xor butterfly, fixed order)
+#pragma unroll
+  for (int x = 0; x < NA; ++x) {
+    double s = 0.0;
+#pragma unroll
+    for (int y = 0; y < NA; ++y) {
+      const int j = tj + 16 * y;
+      if (j < bb) s = fma(a[x][y], rhs[j], s);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+    const int i = ti + 16 * x;
+    if (tj == 0 && i < bb) dsol[i] = s;
+  }
   __syncthreads();
-  for (int i = 0; i < bb; ++i) {
-    const double yi = d[i] / A[i * bb + i];
-    __syncthreads();
-    if (t == 0) d[i] = yi;
-    for (int kk = i + 1 + t; kk < bb; kk += kCholT) d[kk] -= A[kk * bb + i] * yi;
-    __syncthreads();
-  }
-  for (int i = bb - 1; i >= 0; --i) {
-    const double di = d[i] / A[i * bb + i];
-    __syncthreads();
-    if (t == 0) d[i] = di;
-    for (int kk = t; kk < i; kk += kCholT) d[kk] -= A[i * bb + kk] * di;
-    __syncthreads();
-  }
   if (t == 0) {
     double dec = 0.0;
     for (int i = 0; i < bb; ++i) {
-      Dout[i] = (float)d[i];
-      dscratch[i] = (double)(float)d[i];
-      dec += d[i] * rhs[i];
+      Dout[i] = (float)dsol[i];
+      dscratch[i] = (double)(float)dsol[i];
+      dec += dsol[i] * rhs[i];
     }
     const double tnew = trace_state[0] - dec;
     trace_state[0] = tnew;
@@ -717,9 +775,9 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   by += sizeof(float) * (size_t)b * b;                      // Ginv
   by += sizeof(int) * (size_t)b * b * 4;                    // Grams
   by += sizeof(int) * (size_t)b * 2;                        // nnz
-  by += sizeof(double) * (size_t)(b + 4096 + 16);           // d, norm partials, scalars
+  by += sizeof(double) * (size_t)(2 * b + 4096 + 16);       // d, rhs, norm partials, scalars
   by += sizeof(long long) * EXTERND_STATS_LEN + sizeof(int) * 4;
-  by += 16 * 256;
+  by += 20 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
 }
@@ -729,24 +787,6 @@ inline char* bump(char*& p, size_t bytes) {
   p = r + bytes;
   return r;
 }
-
-// A second stream (default priority) and two events for running the Gram and
-// inverse of one half-iteration beside its contraction.
-struct SideStream {
-  hipStream_t side = nullptr;
-  hipEvent_t ev_in = nullptr, ev_out = nullptr;
-  hipError_t init() {
-    hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_in, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_out, hipEventDisableTiming);
-    return e;
-  }
-  ~SideStream() {
-    if (ev_in) (void)hipEventDestroy(ev_in);
-    if (ev_out) (void)hipEventDestroy(ev_out);
-    if (side) (void)hipStreamDestroy(side);
-  }
-};
 
 void launch_inverse(int bb, int* G, float* Ginv, int* fail, hipStream_t st) {
   if (bb <= 64)
@@ -779,6 +819,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   int* GVf = GU + 3 * b * b;
   int* nnz = reinterpret_cast<int*>(bump(p, sizeof(int) * b * 2));
   double* dvec = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
+  double* rhs = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
   double* npart = reinterpret_cast<double*>(bump(p, sizeof(double) * 4096));
   double* scal = reinterpret_cast<double*>(bump(p, sizeof(double) * 16));
   long long* st = reinterpret_cast<long long*>(bump(p, sizeof(long long) * EXTERND_STATS_LEN));
@@ -788,14 +829,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   double* tstate = scal + 2;
 
   hipError_t e;
-  SideStream ss;
-  if ((e = ss.init()) != hipSuccess) return e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
-  const size_t joint_lds = sizeof(double) * (b * b + 2 * b);
   const size_t dec_lds = sizeof(float) * (b * b + b * kDecW);
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
   const int64_t nblocks = (k + b - 1) / b;
@@ -804,38 +842,41 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const int bb = (int)std::min<int64_t>(b, k - c0);
     uint32_t* Uc = a.B2 + c0 * wm;
     uint32_t* Vc = a.C2 + c0 * wn;
-    const int pairs = bb * (bb + 1) / 2;
-    const dim3 gram_u((pairs + 255) / 256, (unsigned)((wm + kGramWords - 1) / kGramWords));
-    const dim3 gram_v((pairs + 255) / 256, (unsigned)((wn + kGramWords - 1) / kGramWords));
+    const int nt = (bb + 15) / 16;
+    const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + kGramSplit - 1) / kGramSplit));
+    const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
     hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2);
     for (int it = 0; it < a.iters; ++it) {
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
-      // inverse depend only on U's codes and run on the side stream while
-      // the contraction runs on the main one.
-      if ((e = hipEventRecord(ss.ev_in, s)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(ss.side, ss.ev_in, 0)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, ss.side, Uc, wm, bb, GU);
-      launch_inverse(bb, GU, Ginv, fail, ss.side);
-      if ((e = hipEventRecord(ss.ev_out, ss.side)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
-      if ((e = hipStreamWaitEvent(s, ss.ev_out, 0)) != hipSuccess) return e;
+      // inverse depend only on U's codes: up to b = 64 the inverse runs as one
+      // extra workgroup of the contraction launch, concurrently with it.
+      hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
+      if (bb <= 64) {
+        hipLaunchKernelGGL((k_contract_with_inverse<4, true>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, GU, Ginv, fail);
+      } else {
+        launch_inverse(bb, GU, Ginv, fail, s);
+        hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
+      }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, Ginv, Vt, (float*)nullptr);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V
-      if ((e = hipEventRecord(ss.ev_in, s)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(ss.side, ss.ev_in, 0)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, ss.side, Vc, wn, bb, GV);
-      launch_inverse(bb, GV, Ginv, fail, ss.side);
-      if ((e = hipEventRecord(ss.ev_out, ss.side)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
-      if ((e = hipStreamWaitEvent(s, ss.ev_out, 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
+      if (bb <= 64) {
+        hipLaunchKernelGGL((k_contract_with_inverse<4, false>), dim3((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, GV, Ginv, fail);
+      } else {
+        launch_inverse(bb, GV, Ginv, fail, s);
+        hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
+      }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, Ginv, Ut, Qt);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U);
+      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
     }
     // joint scales from the final U, V and the last Q = R V
     hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf);
     hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
-    hipLaunchKernelGGL(k_joint_solve, dim3(1), dim3(kCholT), joint_lds, s, GUf, GVf, bb, Qt, m, Uc, wm, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
+    if (bb <= 64)
+      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
+    else
+      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
     hipLaunchKernelGGL(k_block_deflate, dim3((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
