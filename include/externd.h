@@ -65,6 +65,8 @@ enum externd_stat {
   EXTERND_STAT_GRID = 7,        /* workgroups of the resident kernel (0 otherwise) */
   EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
   EXTERND_STAT_TIMEOUTS = 9,    /* resident mode: 1 if an exchange wait ran out (energy is NaN) */
+  EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode: Gram inverses whose Newton-Schulz
+                                    iteration stopped before reaching its tolerance */
   EXTERND_STATS_LEN = 16
 };
 

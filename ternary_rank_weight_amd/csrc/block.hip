@@ -35,8 +35,10 @@ __device__ inline float tern(const uint32_t* row, int e) {
 // ---------------------------------------------------------------------------
 // Starting block U0 (same rule as the sequential path, global component index).
 // ---------------------------------------------------------------------------
-__global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint32_t* __restrict__ B2) {
+__global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint32_t* __restrict__ B2,
+                              int* __restrict__ warm_flags) {
   const int64_t wm = (m + 15) / 16;
+  if (blockIdx.x == 0 && threadIdx.x < 2) warm_flags[threadIdx.x] = 0;
   const int64_t total = (int64_t)bb * wm;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -449,17 +451,196 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
   contract_r_v_body(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y);
 }
 
+
+// ---------------------------------------------------------------------------
+// Decorrelation inverse for b <= 64: X = (G + eps I)^-1, eps = 1e-6 trace(G)/b,
+// by the Newton-Schulz iteration  R = I - G'X,  X <- X + X R  on fp32 MFMA in
+// one workgroup (256 threads; wave w owns the 16-row tile band w).  Since
+// R_{k+1} = R_k^2, the Frobenius norm of R squares each step while it is
+// below 1.  The start is the previous inverse of the same side (consecutive
+// ALS iterations change the codes little), or X0 = I / ||G'||_inf, which
+// converges for every symmetric positive definite G'.  A warm start whose
+// residual norm exceeds 1/2 is replaced by the scaled identity.  The
+// iteration stops when ||R||_F < 1e-5, or once ||R||_F < 1e-3 stops falling
+// by more than half (the fp32 floor); a run that does not get there within 40
+// steps is counted in stats[EXTERND_STAT_INVERSE_UNCONVERGED].  The result
+// differs from the fp64 inverse by about 1e-6 relative.  G (integer valued)
+// is zeroed after being read so the next Gram accumulation starts from zero.
+// ---------------------------------------------------------------------------
+constexpr int kNsB = 64, kNsS = 65;
+struct NsShared {
+  float G[kNsB * kNsS];
+  float X[kNsB * kNsS];
+  float R[kNsB * kNsS];
+  double red[kCT / kWave];
+};
+
+__device__ inline double ns_block_sum(double v, double* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int q = 1; q < kCT / kWave; ++q) r += red[q];
+  return r;
+}
+__device__ inline double ns_block_max(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int q = 1; q < kCT / kWave; ++q) r = fmax(r, red[q]);
+  return r;
+}
+// acc[J] (tile (w, J)) += A(rows 16w..16w+15) * B(columns 16J..16J+15), K = 64;
+// A and B in LDS with row stride kNsS.
+__device__ inline void ns_mm(const float* A, const float* B, f4 (&acc)[4]) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int i = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < kNsB; k0 += 4) {
+    const float a = A[(16 * w + i) * kNsS + k0 + k];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) acc[J] = mfma16x16x4(a, B[(k0 + k) * kNsS + 16 * J + i], acc[J]);
+  }
+}
+
+__device__ __forceinline__ void ns_inverse_body(int* __restrict__ G, int bb, float* __restrict__ X,
+                                                int* __restrict__ warm_flag,
+                                                long long* __restrict__ unconverged) {
+  __shared__ NsShared sh;
+  constexpr int kPer = kNsB * kNsB / kCT;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
+  const int i16 = lane & 15, kq = lane >> 4;
+  const int warm = *warm_flag;
+  // G' = G + eps I in LDS, the identity beyond bb; all loads issued first
+  double trp = 0.0;
+  {
+    int gv[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
+      gv[q] = (r < bb && c < bb) ? G[r * bb + c] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
+      float v = (r == c) ? 1.f : 0.f;
+      if (r < bb && c < bb) {
+        v = (float)gv[q];
+        if (r == c) trp += v;
+        G[r * bb + c] = 0;
+      }
+      sh.G[r * kNsS + c] = v;
+    }
+  }
+  const double tr = ns_block_sum(trp, sh.red);
+  const float eps = (float)(1e-6 * tr / bb);
+  for (int r = t; r < bb; r += kCT) sh.G[r * kNsS + r] += eps;
+  __syncthreads();
+  double rs = 0.0;
+  {
+    const int row = t >> 2, part = t & 3;   // four threads per row
+    for (int c = part; c < kNsB; c += 4) rs += fabs((double)sh.G[row * kNsS + c]);
+    rs += __shfl_xor(rs, 1);
+    rs += __shfl_xor(rs, 2);
+  }
+  const float alpha = (float)(1.0 / ns_block_max(rs, sh.red));
+  auto init_scaled = [&]() {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
+      sh.X[r * kNsS + c] = (r == c) ? alpha : 0.f;
+    }
+  };
+  if (warm) {
+    float xv[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
+      xv[q] = (r < bb && c < bb) ? X[r * bb + c] : ((r == c) ? 1.f : 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = t + kCT * q;
+      sh.X[(e / kNsB) * kNsS + e % kNsB] = xv[q];
+    }
+  } else {
+    init_scaled();
+  }
+  __syncthreads();
+  bool warm_now = warm != 0;
+  double prev = 1e300;
+  bool conv = false;
+  for (int it = 0; it < 40; ++it) {
+    f4 acc[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
+    ns_mm(sh.G, sh.X, acc);
+    double rp = 0.0;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * w + 4 * kq + v, c = 16 * J + i16;
+        const float rv = ((r == c) ? 1.f : 0.f) - acc[J][v];
+        sh.R[r * kNsS + c] = rv;
+        rp += (double)rv * (double)rv;
+      }
+    const double rn2 = ns_block_sum(rp, sh.red);   // its barriers also publish R
+    if (rn2 < 1e-10) {
+      conv = true;
+      break;
+    }
+    if (!(rn2 < 1e30) || (warm_now && rn2 > 0.25)) {
+      if (!warm_now) break;   // not finite from the scaled identity: give up
+      warm_now = false;       // poor warm start: restart from the scaled identity
+      init_scaled();
+      __syncthreads();
+      prev = 1e300;
+      continue;
+    }
+    if (rn2 < 1e-6 && rn2 > 0.25 * prev) {
+      conv = true;
+      break;
+    }
+    prev = rn2;
+    f4 y[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) y[J][v] = sh.X[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16];
+    ns_mm(sh.X, sh.R, y);
+    __syncthreads();
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sh.X[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16] = y[J][v];
+    __syncthreads();
+  }
+  for (int e = t; e < bb * bb; e += kCT) X[e] = sh.X[(e / bb) * kNsS + (e % bb)];
+  if (t == 0) {
+    *warm_flag = 1;
+    if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(unconverged), 1ull);
+  }
+}
+
 // The contraction with one extra workgroup, (gridDim.x - 1, 0), that inverts
 // the Gram matrix of the same codes meanwhile: both depend only on the codes
 // and R, and the decorrelation needs both.  One launch instead of two keeps
 // them concurrent without a second stream.
-template <int NA, bool UT>
+template <bool UT>
 __global__ __launch_bounds__(kCT) void k_contract_with_inverse(
     const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
     int bb, int64_t per_split, float* __restrict__ Part, int* __restrict__ G,
-    float* __restrict__ Ginv, int* __restrict__ fail) {
+    float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ unconverged) {
   if ((int)blockIdx.x == (int)gridDim.x - 1) {
-    if (blockIdx.y == 0) spd_inverse_body<NA>(G, bb, Ginv, fail);
+    if (blockIdx.y == 0) ns_inverse_body(G, bb, Ginv, warm_flag, unconverged);
     return;
   }
   if (UT) contract_ut_r_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
@@ -772,7 +953,7 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   by += sizeof(float) * (size_t)L.S2 * b * m;               // Qt partials
   by += sizeof(float) * (size_t)b * (n + m);                // Vt, Ut
   by += sizeof(float) * (size_t)b * m;                      // Qt (last sum)
-  by += sizeof(float) * (size_t)b * b;                      // Ginv
+  by += sizeof(float) * (size_t)2 * b * b;                  // Ginv of the U and V sides
   by += sizeof(int) * (size_t)b * b * 4;                    // Grams
   by += sizeof(int) * (size_t)b * 2;                        // nnz
   by += sizeof(double) * (size_t)(2 * b + 4096 + 16);       // d, rhs, norm partials, scalars
@@ -812,7 +993,8 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   float* Vt = reinterpret_cast<float*>(bump(p, sizeof(float) * b * n));
   float* Ut = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
   float* Qt = reinterpret_cast<float*>(bump(p, sizeof(float) * b * m));
-  float* Ginv = reinterpret_cast<float*>(bump(p, sizeof(float) * b * b));
+  float* GinvU = reinterpret_cast<float*>(bump(p, sizeof(float) * 2 * b * b));   // U side, V side
+  float* GinvV = GinvU + b * b;
   int* GU = reinterpret_cast<int*>(bump(p, sizeof(int) * 4 * b * b));  // GU, GV, GUf, GVf
   int* GV = GU + b * b;
   int* GUf = GU + 2 * b * b;
@@ -824,6 +1006,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   double* scal = reinterpret_cast<double*>(bump(p, sizeof(double) * 16));
   long long* st = reinterpret_cast<long long*>(bump(p, sizeof(long long) * EXTERND_STATS_LEN));
   int* fail = reinterpret_cast<int*>(bump(p, sizeof(int) * 4));
+  int* warm = fail + 2;   // Newton-Schulz warm-start flags, U side and V side
   double* a2 = scal;
   double* r2 = scal + 1;
   double* tstate = scal + 2;
@@ -845,29 +1028,30 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const int nt = (bb + 15) / 16;
     const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + kGramSplit - 1) / kGramSplit));
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
-    hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2);
+    hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2, warm);
     for (int it = 0; it < a.iters; ++it) {
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
-      // inverse depend only on U's codes: up to b = 64 the inverse runs as one
-      // extra workgroup of the contraction launch, concurrently with it.
+      // inverse depend only on U's codes: up to b = 64 the inverse (Newton-
+      // Schulz) runs as one extra workgroup of the contraction launch,
+      // concurrently with it; wider blocks invert by Gauss-Jordan first.
       hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
       if (bb <= 64) {
-        hipLaunchKernelGGL((k_contract_with_inverse<4, true>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, GU, Ginv, fail);
+        hipLaunchKernelGGL((k_contract_with_inverse<true>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, GU, GinvU, warm, st + EXTERND_STAT_INVERSE_UNCONVERGED);
       } else {
-        launch_inverse(bb, GU, Ginv, fail, s);
+        launch_inverse(bb, GU, GinvU, fail, s);
         hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
       }
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, Ginv, Vt, (float*)nullptr);
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
       hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V
       hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
       if (bb <= 64) {
-        hipLaunchKernelGGL((k_contract_with_inverse<4, false>), dim3((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, GV, Ginv, fail);
+        hipLaunchKernelGGL((k_contract_with_inverse<false>), dim3((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, GV, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED);
       } else {
-        launch_inverse(bb, GV, Ginv, fail, s);
+        launch_inverse(bb, GV, GinvV, fail, s);
         hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
       }
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, Ginv, Ut, Qt);
+      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
       hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
     }
     // joint scales from the final U, V and the last Q = R V
