@@ -92,6 +92,53 @@ def block_alg_flops(m, n, k, b, iters):
     return 2.0 * m * n * b * (2 * iters + 1) * nblocks
 
 
+def _random_codes(torch, rows, L, gen):
+    """Valid 2-bit code rows (no 0b10 code, zero padding), uniformly random."""
+    w = torch.randint(-2**31, 2**31 - 1, (rows, (L + 15) // 16), dtype=torch.int64,
+                      device="cuda", generator=gen).to(torch.int32)
+    w = w | ((w >> 1) & 0x55555555)          # a set sign bit forces the nonzero bit
+    if L % 16:
+        w[:, -1] &= (1 << (2 * (L % 16))) - 1
+    return w.contiguous()
+
+
+def measure_inference(trw, outs, m, n, reps=20):
+    """y = B (diag(D) (C x)) (externd_apply) on the block run's factors and on
+    a 16384 x 16384, k = 32768 set of random factors; HIP events around
+    `reps` calls.  Algorithmic bytes per call: both code arrays, D, x, y."""
+    import torch
+    res = []
+    cases = []
+    if "block" in outs:
+        r = outs["block"]
+        cases.append((f"{m}x{n} block-ALS factors, k={r.k}", r.B2, r.C2, r.D, m, n))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    M = N = 16384
+    K = 32768
+    cases.append((f"{M}x{N} random 2-bit factors, k={K}", _random_codes(torch, K, M, gen),
+                  _random_codes(torch, K, N, gen), torch.randn(K, device="cuda", generator=gen) * 0.01, M, N))
+    for name, B2, C2, D, mm, nn in cases:
+        x = torch.randn(nn, device="cuda", generator=gen)
+        for _ in range(3):
+            trw.apply(B2, C2, D, mm, nn, x)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            trw.apply(B2, C2, D, mm, nn, x)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        k = D.numel()
+        alg = 4.0 * k * ((mm + 15) // 16 + (nn + 15) // 16) + 4.0 * (k + mm + nn)
+        gbps = alg / us / 1e3
+        res.append({"workload": name, "us_per_call": round(us, 2), "alg_bytes": alg,
+                    "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)})
+    return res
+
+
 def cpu_baseline(A, c, sample):
     import numpy as np
     import oracle
@@ -190,6 +237,8 @@ def main():
         bm["alg_tflops"] = fl / (bm["ms"] / 1e3) / 1e12
         bm["b"] = b
 
+    inference = measure_inference(trw, outs, m, n)
+
     cpu = None
     if not args.no_cpu and args.cpu_sample > 0:
         cpu = cpu_baseline(A, c, min(args.cpu_sample, k))
@@ -217,6 +266,7 @@ def main():
         "modes": {md: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                        for kk, vv in per_mode[md].items()} for md in modes},
         "roofline": roofline,
+        "inference": inference,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

@@ -135,6 +135,14 @@ int externd_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2,
 int externd_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D,
                         int64_t m, int64_t n, int64_t k, void* stream, float* A_hat);
 
+/* Inference with the factors (§2.6): y = B (diag(D) (C x)) for x of length n,
+ * y of length m.  C x and B w are sums of signed copies (no multiplies; k
+ * multiplies for w = D * C x), accumulated in fp32 in a fixed order.  B2, C2,
+ * D as produced by externd_decompose; k may be 0 (y = 0).  Workspace of about
+ * 4 (k + m k / 64) bytes is allocated and freed stream-ordered. */
+int externd_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m, int64_t n,
+                  int64_t k, const float* x, void* stream, float* y);
+
 /* k = mu * min(m, n) rounded half away from zero in fp64 (§2.1); -1 on bad input. */
 int64_t externd_rank(int64_t m, int64_t n, float mu);
 

@@ -28,6 +28,15 @@ def reconstruct(B, C, D):
     return (Bf * Df[None, :]) @ Cf
 
 
+def apply_factors(B, C, D, x):
+    """Inference with the factors (§2.6): y = B (diag(D) (C x)) in fp64."""
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return B @ (D * (C @ x))
+
+
 def energy_from_factors(A, B, C, D):
     """E = 1 - ||A - B diag(D) C||^2 / ||A||^2 in fp64, from the factors alone (§2.1)."""
     A64 = np.asarray(A, dtype=np.float64)

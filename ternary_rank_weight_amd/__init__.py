@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "decompose", "energy", "reconstruct", "rank", "block_width", "resident_fits", "workspace_bytes",
+    "decompose", "energy", "reconstruct", "apply", "rank", "block_width", "resident_fits", "workspace_bytes",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
     "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
 ]
@@ -63,6 +63,7 @@ _decompose = _sig("externd_decompose", ctypes.c_int,
                   [_p, _i64, _i64, _f32, _f32, _i32, _i32, _p, _p, _p, _p, _p, ctypes.POINTER(_Opts)])
 _energy = _sig("externd_energy", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _p, _p])
 _reconstruct = _sig("externd_reconstruct", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p])
+_apply = _sig("externd_apply", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p])
 _rank = _sig("externd_rank", ctypes.c_int64, [_i64, _i64, _f32])
 _block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
 _resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
@@ -75,7 +76,8 @@ _status_string = _sig("externd_status_string", ctypes.c_char_p, [ctypes.c_int])
 _last_error = _sig("externd_last_error", ctypes.c_char_p, [])
 
 # Every exported symbol of the C ABI, for load checks.
-ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_rank",
+ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_apply",
+               "externd_rank",
                "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
                "externd_ternarize",
                "externd_gemv_t", "externd_gemv_n", "externd_deflate",
@@ -232,6 +234,17 @@ def reconstruct(B2, C2, D, m, n):
     out = torch.empty((m, n), dtype=torch.float32, device=D.device)
     _check(_reconstruct(_ptr(B2), _ptr(C2), _ptr(D), m, n, k, _stream(), _ptr(out)))
     return out
+
+
+def apply(B2, C2, D, m, n, x):
+    """y = B (diag(D) (C x)) from the 2-bit factors (§2.6); x: float32 (n,)."""
+    _need(x, torch.float32, "x")
+    if x.numel() != n:
+        raise ValueError("x must have n entries")
+    k = D.numel()
+    y = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_apply(_ptr(B2), _ptr(C2), _ptr(D), m, n, k, _ptr(x), _stream(), _ptr(y)))
+    return y
 
 
 def ternarize(x, tau):

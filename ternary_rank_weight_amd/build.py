@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libexternd.so")
-SOURCES = ["abi.cpp", "seq_stream.hip", "seq_resident.hip", "factors.hip", "block.hip"]
+SOURCES = ["abi.cpp", "seq_stream.hip", "seq_resident.hip", "factors.hip", "block.hip", "apply.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -117,6 +117,22 @@ const char* externd_status_string(int status) {
 
 const char* externd_last_error(void) { return g_last_error.c_str(); }
 
+int externd_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m, int64_t n,
+                  int64_t k, const float* x, void* stream, float* y) {
+  if (!x || !y) return fail(EXTERND_EINVAL, "null x or y pointer");
+  if (bad_size(m, n) || k < 0 || k > (int64_t(1) << 31))
+    return fail(EXTERND_EINVAL, "bad shape");
+  if (k > 0 && (!B2 || !C2 || !D)) return fail(EXTERND_EINVAL, "null factor pointer");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w;
+  if ((st = alloc_ws(w, externd::apply_workspace_bytes(m, k), s)) != EXTERND_OK) return st;
+  hipError_t e = externd::run_apply(B2, C2, D, m, n, k, x, y, w.ptr, s);
+  if (e != hipSuccess) return hip_fail(e, "apply");
+  return EXTERND_OK;
+}
+
 int64_t externd_rank(int64_t m, int64_t n, float mu) {
   if (m <= 0 || n <= 0 || !std::isfinite(mu) || mu < 0.f) return -1;
   const double v = (double)mu * (double)(m < n ? m : n);

@@ -87,4 +87,9 @@ hipError_t run_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2, 
 hipError_t run_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m,
                            int64_t n, int64_t k, float* out, hipStream_t s);
 
+// inference y = B diag(D) C x from 2-bit factors (apply.hip)
+size_t apply_workspace_bytes(int64_t m, int64_t k);
+hipError_t run_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m, int64_t n, int64_t k,
+                     const float* x, float* y, void* ws, hipStream_t s);
+
 }  // namespace externd

@@ -63,3 +63,25 @@ def test_init_signs_matches_scalar_hash_and_is_balanced():
     assert abs(a @ b) / 50_000 < 0.02 and abs(a @ c) / 50_000 < 0.02
     Ub = oracle.init_block(0, 4, 3, 64)
     assert np.array_equal(Ub[:, 1], oracle.init_signs(0, 5, 64))
+
+
+def test_apply_factors_pins():
+    # y = B (diag(D) (C x)) must equal the dense product (B diag(D) C) x, and on
+    # one-hot inputs it returns the columns of the reconstruction.
+    rng = np.random.default_rng(12)
+    for (m, n, k) in [(5, 7, 3), (37, 53, 20), (1, 9, 4), (8, 1, 2)]:
+        B = rng.integers(-1, 2, size=(m, k)).astype(np.int8)
+        C = rng.integers(-1, 2, size=(k, n)).astype(np.int8)
+        D = rng.standard_normal(k)
+        x = rng.standard_normal(n)
+        dense = oracle.reconstruct(B, C, D)
+        np.testing.assert_allclose(oracle.apply_factors(B, C, D, x), dense @ x, rtol=1e-12, atol=1e-12)
+        for j in range(n):
+            e = np.zeros(n)
+            e[j] = 1.0
+            np.testing.assert_allclose(oracle.apply_factors(B, C, D, e), dense[:, j], rtol=0, atol=1e-12)
+    # a single component: y = d u (v . x)
+    u = np.array([1, 0, -1], dtype=np.int8)
+    v = np.array([[0, 1, 1, -1]], dtype=np.int8)
+    x = np.array([0.5, 2.0, -1.0, 3.0])
+    assert oracle.apply_factors(u[:, None], v, np.array([0.25]), x).tolist() == [-0.5, 0.0, 0.5]
