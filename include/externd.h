@@ -103,6 +103,7 @@ typedef struct externd_opts {
    * Two calls in flight at once must not share one workspace. */
   void* workspace;
   uint64_t workspace_bytes;
+  double* norm_a2;        /* device, optional: receives ||A||_F^2 (fp64) */
 } externd_opts;
 
 /*
@@ -145,6 +146,19 @@ int externd_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_
 
 /* k = mu * min(m, n) rounded half away from zero in fp64 (§2.1); -1 on bad input. */
 int64_t externd_rank(int64_t m, int64_t n, float mu);
+
+/* Rank needed for a target energy (§3.3: choosing mu per matrix), read off
+ * one decomposition's trace thanks to the greedy prefix property: the run at
+ * a smaller rank is the prefix of the run at a larger one (in block mode the
+ * smaller rank must be a whole number of blocks).  HOST arrays: trace[j] is
+ * ||R||^2 after component j (sequential, step = 1) or after block j (block
+ * mode, step = b); total is the decomposition's k; norm_a2 its ||A||^2
+ * (externd_opts.norm_a2).  Returns the smallest c = min((j+1) step, total)
+ * with 1 - trace[j] / norm_a2 >= target, 0 when norm_a2 = 0, -1 when no
+ * prefix reaches the target, and -2 on invalid arguments.  mu = c / min(m, n)
+ * reproduces c through externd_rank. */
+int64_t externd_rank_for_energy(const double* trace, int64_t len, int64_t total, int32_t step,
+                                double norm_a2, double target);
 
 /* Block width actually used for a request: min(block, floor(min(m,n)/8)),
  * 1 meaning sequential (§2.4). */

@@ -214,3 +214,19 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
     return SeqResult(B, C, D, trace, E, norm_a2,
                      {"decrease": decrease, "b": b, "ridge_retries": ridge_retries})
+
+
+def rank_for_energy(trace, norm_a2, target, step=1, total=None):
+    """Smallest prefix rank reaching energy >= target (§3.3 choosing mu per
+    matrix), by the greedy prefix property: trace[j] is ||R||^2 after
+    component j (step 1) or block j (step b).  0 for a zero matrix, -1 if no
+    prefix reaches the target."""
+    trace = np.asarray(trace, dtype=np.float64)
+    if total is None:
+        total = trace.size * step
+    if norm_a2 == 0.0:
+        return 0
+    for j, t in enumerate(trace):
+        if 1.0 - t / norm_a2 >= target:
+            return min((j + 1) * step, total)
+    return -1

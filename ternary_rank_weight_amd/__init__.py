@@ -15,6 +15,7 @@ import torch
 
 __all__ = [
     "decompose", "energy", "reconstruct", "apply", "rank", "block_width", "resident_fits", "workspace_bytes",
+    "rank_for_energy", "mu_for_energy",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
     "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
 ]
@@ -49,6 +50,7 @@ class _Opts(ctypes.Structure):
         ("capture_y", _p), ("capture_x", _p), ("capture_v", _p), ("capture_u", _p),
         ("capture_d", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
+        ("norm_a2", _p),
     ]
 
 
@@ -68,6 +70,8 @@ _rank = _sig("externd_rank", ctypes.c_int64, [_i64, _i64, _f32])
 _block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
 _resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
 _workspace_bytes = _sig("externd_workspace_bytes", ctypes.c_uint64, [_i64, _i64, _f32, _i32, _i32])
+_rank_for_energy = _sig("externd_rank_for_energy", ctypes.c_int64,
+                        [ctypes.POINTER(ctypes.c_double), _i64, _i64, _i32, ctypes.c_double, ctypes.c_double])
 _ternarize = _sig("externd_ternarize", ctypes.c_int, [_p, _i64, _f32, _p, _p, _p])
 _gemv_t = _sig("externd_gemv_t", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
 _gemv_n = _sig("externd_gemv_n", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
@@ -79,6 +83,7 @@ _last_error = _sig("externd_last_error", ctypes.c_char_p, [])
 ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_apply",
                "externd_rank",
                "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
+               "externd_rank_for_energy",
                "externd_ternarize",
                "externd_gemv_t", "externd_gemv_n", "externd_deflate",
                "externd_status_string", "externd_last_error")
@@ -140,10 +145,11 @@ class Decomposition:
     capture: dict of captured tensors when requested.
     """
 
-    def __init__(self, m, n, k, B2, C2, D, energy, trace, stats, capture):
+    def __init__(self, m, n, k, B2, C2, D, energy, trace, stats, capture, norm_a2=None, block=1):
         self.m, self.n, self.k = m, n, k
         self.B2, self.C2, self.D, self.energy = B2, C2, D, energy
         self.trace, self.stats, self.capture = trace, stats, capture
+        self.norm_a2, self.block = norm_a2, block
 
     def stat(self, name):
         return int(self.stats[STAT[name]].item())
@@ -179,12 +185,14 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     ntrace = ((k + b - 1) // b) if b > 1 else k
     tr = torch.empty((max(ntrace, 1),), dtype=torch.float64, device=dev) if trace else None
     st = torch.zeros((STATS_LEN,), dtype=torch.int64, device=dev) if stats else None
+    na2 = torch.empty((1,), dtype=torch.float64, device=dev) if trace else None
     opts = _Opts()
     opts.struct_size = ctypes.sizeof(_Opts)
     opts.seed = seed
     opts.mode = mode
     opts.trace = _ptr(tr)
     opts.stats = _ptr(st)
+    opts.norm_a2 = _ptr(na2)
     opts.capture_component = -1
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
@@ -215,7 +223,35 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
         opts.capture_d = _ptr(cap["d"])
     _check(_decompose(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
                       _ptr(D), _ptr(E), ctypes.byref(opts)))
-    return Decomposition(m, n, k, B2, C2, D, E, tr, st, cap)
+    return Decomposition(m, n, k, B2, C2, D, E, tr, st, cap, na2, b)
+
+
+def rank_for_energy(trace, total, step, norm_a2, target):
+    """Smallest prefix rank whose energy reaches target (host-side scan of a
+    trace; see externd_rank_for_energy).  -1 if none does."""
+    import numpy as np
+    tr = np.ascontiguousarray(np.asarray(trace, dtype=np.float64))
+    r = int(_rank_for_energy(tr.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), tr.size, int(total),
+                             int(step), float(norm_a2), float(target)))
+    if r == -2:
+        raise ExterndError(1)
+    return r
+
+
+def mu_for_energy(A, target, mu_max, tau, iters=15, block=0, seed=0):
+    """Smallest mu (a multiple of 1/min(m, n), and of b/min(m, n) in block
+    mode) whose decomposition reaches energy >= target, from one run at
+    mu_max (§3.3).  Returns (mu, k, energy_at_k) or None if mu_max is short."""
+    res = decompose(A, mu_max, tau, iters, block, seed, trace=True)
+    torch.cuda.synchronize()
+    tr = res.trace.cpu().numpy()
+    a2 = float(res.norm_a2.item())
+    c = rank_for_energy(tr, res.k, res.block, a2, target)
+    if c < 0:
+        return None
+    m, n = A.shape
+    e = 1.0 if a2 == 0.0 or c == 0 else 1.0 - tr[(c + res.block - 1) // res.block - 1] / a2
+    return c / min(m, n), c, e
 
 
 def energy(A, B2, C2, D):

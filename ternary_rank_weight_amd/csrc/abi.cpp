@@ -141,6 +141,21 @@ int64_t externd_rank(int64_t m, int64_t n, float mu) {
   return (int64_t)whole + ((v - whole) >= 0.5 ? 1 : 0);
 }
 
+int64_t externd_rank_for_energy(const double* trace, int64_t len, int64_t total, int32_t step,
+                                double norm_a2, double target) {
+  if (len < 0 || total < 0 || step < 1 || (len > 0 && !trace) || !std::isfinite(target) ||
+      !std::isfinite(norm_a2) || norm_a2 < 0.0)
+    return (fail(EXTERND_EINVAL, "bad arguments to externd_rank_for_energy"), -2);
+  if (norm_a2 == 0.0) return 0;
+  for (int64_t j = 0; j < len; ++j) {
+    if (1.0 - trace[j] / norm_a2 >= target) {
+      const int64_t c = (j + 1) * (int64_t)step;
+      return c < total ? c : total;
+    }
+  }
+  return -1;
+}
+
 int32_t externd_block_width(int64_t m, int64_t n, int32_t block) {
   if (block <= 1 || m <= 0 || n <= 0) return 1;
   const int64_t cap = (m < n ? m : n) / 8;
@@ -216,6 +231,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.energy = energy;
     ba.trace = o.trace;
     ba.stats = reinterpret_cast<long long*>(o.stats);
+    ba.norm_a2 = o.norm_a2;
     Workspace w;
     if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);
@@ -237,6 +253,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   sa.energy = energy;
   sa.trace = o.trace;
   sa.stats = reinterpret_cast<long long*>(o.stats);
+  sa.norm_a2 = o.norm_a2;
   sa.capture_component = o.capture_component;
   if (o.capture_component >= 0) {
     if (o.capture_component >= k) return fail(EXTERND_EINVAL, "capture_component >= k");

@@ -1066,6 +1066,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   }
   if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_block_finish, dim3(1), dim3(1), 0, s, a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, st, a.stats);
+  if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct SeqArgs {
   int8_t* capture_v;
   int8_t* capture_u;
   float* capture_d;
+  double* norm_a2;   // optional output: ||A||^2
 };
 
 // Arguments of one block-mode decomposition.
@@ -47,6 +48,7 @@ struct BlockArgs {
   double* energy;
   double* trace;
   long long* stats;
+  double* norm_a2;   // optional output: ||A||^2
 };
 
 // streaming sequential path and single-step kernels (seq_stream.hip)
@@ -64,6 +66,7 @@ hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_code
                           const uint32_t* v_codes, const float* dptr, hipStream_t s);
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
                         double* out, long long* nonfinite, hipStream_t s);
+hipError_t launch_copy_f64(const double* src, double* dst, int64_t count, hipStream_t s);
 hipError_t launch_energy_finish(const double* a2, const double* r2, const long long* nonfinite,
                                 double* energy, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t v, hipStream_t s);

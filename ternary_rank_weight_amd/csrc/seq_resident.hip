@@ -676,6 +676,7 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_resident_finish, dim3(1), dim3(64), 0, s, r2p, ra.G, a2, nonfinite, err,
                      a.energy, a.stats);
+  if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -357,6 +357,15 @@ hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t 
   return hipGetLastError();
 }
 
+__global__ void k_copy_f64(const double* __restrict__ src, double* __restrict__ dst, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+hipError_t launch_copy_f64(const double* src, double* dst, int64_t count, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_f64, dim3(1), dim3(64), 0, s, src, dst, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_energy_finish(const double* a2, const double* r2, const long long* nonfinite,
                                 double* energy, hipStream_t s) {
   hipLaunchKernelGGL(k_energy_finish, dim3(1), dim3(64), 0, s, a2, r2, nonfinite, energy, nullptr);
@@ -467,6 +476,7 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   }
   if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
   if ((e = launch_energy_finish(a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, s)) != hipSuccess) return e;
+  if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   if (a.stats) {
     hipLaunchKernelGGL(k_copy_i64, dim3(1), dim3(64), 0, s, st, a.stats, (int64_t)EXTERND_STATS_LEN);
   }

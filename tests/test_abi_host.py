@@ -141,3 +141,23 @@ def test_decompose_rejects_misaligned_workspace(clib):
     assert st == 1
     clib.externd_last_error.restype = ctypes.c_char_p
     assert b"aligned" in clib.externd_last_error()
+
+
+def test_rank_for_energy_matches_oracle(clib):
+    import numpy as np
+    import oracle
+    import ternary_rank_weight_amd as trw
+    rng = np.random.default_rng(3)
+    for step, total in ((1, 40), (8, 37), (64, 5120)):
+        n = (total + step - 1) // step
+        tr = np.sort(rng.uniform(0.0, 10.0, n))[::-1].copy()
+        for target in (-1.0, 0.0, 0.1, 0.5, 0.9, 1.0 - tr[-1] / 10.0, 0.999999, 2.0):
+            want = oracle.rank_for_energy(tr, 10.0, target, step=step, total=total)
+            assert trw.rank_for_energy(tr, total, step, 10.0, target) == want
+    assert trw.rank_for_energy([], 0, 1, 0.0, 0.5) == 0
+    with pytest.raises(trw.ExterndError):
+        trw.rank_for_energy([1.0], 1, 0, 1.0, 0.5)
+    with pytest.raises(trw.ExterndError):
+        trw.rank_for_energy([1.0], 1, 1, -1.0, 0.5)
+    with pytest.raises(trw.ExterndError):
+        trw.rank_for_energy([1.0], 1, 1, 1.0, float("nan"))

@@ -189,3 +189,34 @@ def test_energy_grows_with_mu():
     es = [oracle.decompose_seq(A, mu, 0.7, seed=0).E for mu in (0.5, 1.0, 2.0, 3.0)]
     assert all(b >= a for a, b in zip(es, es[1:]))
     assert es[-1] > 0.99
+
+
+def test_rank_for_energy_matches_separate_runs():
+    # Choosing mu per matrix (§3.3): the rank the trace scan picks must be the
+    # smallest rank whose own, separate decomposition reaches the target --
+    # found here by brute force over every rank.
+    A = _small(24, 20, 11)
+    a2 = float(np.sum(A.astype(np.float64) ** 2))
+    big = oracle.decompose_seq(A, 1.5, 0.7, seed=4)
+    energies = [oracle.decompose_seq(A, 0.0, 0.7, seed=4, k=c).E for c in range(1, big.D.size + 1)]
+    for target in (0.0, 0.3, 0.6, 0.9, 0.99, energies[-1], 1.0 + 1e-9):
+        want = next((c for c, e in zip(range(1, len(energies) + 1), energies) if e >= target), -1)
+        assert oracle.rank_for_energy(big.trace, a2, target) == want
+
+
+def test_rank_for_energy_block_steps():
+    A = _small(64, 48, 12)
+    a2 = float(np.sum(A.astype(np.float64) ** 2))
+    big = oracle.decompose_block(A, 1.0, 0.7, block=6, seed=2)   # k = 48: 8 blocks of 6
+    b = big.extra["b"]
+    assert b == 6
+    for nb in range(1, big.trace.size + 1):
+        small = oracle.decompose_block(A, 0.0, 0.7, block=6, seed=2, k=nb * b)
+        assert small.E == 1.0 - big.trace[nb - 1] / a2
+        target = small.E
+        got = oracle.rank_for_energy(big.trace, a2, target, step=b, total=big.D.size)
+        assert got <= nb * b and got % b == 0
+    assert oracle.rank_for_energy(big.trace, a2, 2.0, step=b) == -1
+    assert oracle.rank_for_energy([], 0.0, 0.5) == 0
+    # a trailing partial block is capped at the decomposition's rank
+    assert oracle.rank_for_energy([5.0, 1.0], 10.0, 0.85, step=4, total=7) == 7
