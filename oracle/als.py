@@ -9,7 +9,8 @@ Sources (ExTernD: Expanded-Rank Ternary Decomposition Ternary LLM PTQ with
 Accuracy Approaching Any Quantization Level):
   §2.1  representation, k = mu * min(m, n), energy E
   §2.3  greedy sequential ALS: alternating ternary fit, optimal scale, deflation
-  §2.4  batched block ALS with decorrelated targets and a joint scale solve
+  §2.4  batched block ALS with decorrelated targets and a joint scale solve,
+        and refinement sweeps over the extracted blocks
   Appendix (monotone residual): the residual norm never increases.
 
 Readings (listed with their reasons in the design doc):
@@ -24,6 +25,9 @@ Readings (listed with their reasons in the design doc):
     [(U^T U) o (V^T V)] d = diag(U^T R V) is solved by Cholesky; if that fails
     it is retried with the same kind of ridge and the event is counted.
   * ||A|| = 0 gives E = 1.
+  * Refinement sweeps restart each block's iterations from its stored U and
+    keep the refit only if ||R||^2 does not grow, so the energy never falls
+    (the pages report a monotone rise).
 """
 import math
 
@@ -151,13 +155,47 @@ def _cholesky_solve(G, rhs, eps):
     return np.linalg.solve(Lc.T, z)
 
 
-def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None):
+def _fit_block(R, U, tau, iters):
+    """The alternating block iterations of §2.4 from the starting block U.
+    Returns (U, V, Q) with Q = R V from the last iteration."""
+    V = None
+    Q = None
+    for _ in range(iters):
+        P = R.T @ U
+        GU = U.T @ U
+        V = ternarize_columns(_cholesky_solve(GU, P.T, ridge(GU)).T, tau).astype(np.float64)
+        Q = R @ V
+        GV = V.T @ V
+        U = ternarize_columns(_cholesky_solve(GV, Q.T, ridge(GV)).T, tau).astype(np.float64)
+    return U, V, Q
+
+
+def _joint_scales(U, V, Q):
+    """Solve [(U^T U) o (V^T V)] d = diag(U^T R V) (§2.4); diag(U^T R V) is
+    read off Q = R V.  Returns (d, rhs, retried)."""
+    rhs = np.sum(U * Q, axis=0)
+    Mjs = (U.T @ U) * (V.T @ V)
+    try:
+        return _cholesky_solve(Mjs, rhs, 0.0), rhs, False
+    except np.linalg.LinAlgError:
+        return _cholesky_solve(Mjs, rhs, ridge(Mjs)), rhs, True
+
+
+def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None, sweeps=0):
     """Batched block ALS with decorrelated targets (§2.4).  Returns SeqResult.
 
     Each iteration:  P = R^T U;  V <- T_col( P (U^T U + eps I)^-1 );
                      Q = R V;    U <- T_col( Q (V^T V + eps I)^-1 ).
     Then diag(U^T R V) is read off the last Q, the b scales solve
     [(U^T U) o (V^T V)] d = diag(U^T R V), and R <- R - U diag(d) V^T.
+
+    sweeps: refinement sweeps after extraction (§2.4, refinement).  Each sweep
+    visits the blocks in order: the block's contribution is added back to R,
+    the block iterations run again starting from its stored U, the scales are
+    solved jointly, and the refitted block replaces the stored one when it
+    leaves ||R||^2 no larger than before the visit; otherwise the stored block
+    is deflated again.  extra["sweep_trace"][s] is ||R||^2 after sweep s and
+    extra["sweep_kept_old"] counts the visits that kept the stored block.
 
     force_width: run the block iteration with exactly this width, bypassing
     the cap and the fall-back to sequential mode (used to pin b = 1 against
@@ -169,6 +207,8 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
         k = rank_for(m, n, mu)
     b = block_width(m, n, block) if force_width is None else int(force_width)
     if b == 1 and force_width is None:
+        if sweeps:
+            raise ValueError("refinement sweeps need block mode (b >= 2)")
         res = decompose_seq(A, mu, tau, iters, seed, k)
         res.extra["b"] = 1
         return res
@@ -184,36 +224,43 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     for blk in range(nblocks):
         c0 = blk * b
         bb = min(b, k - c0)
-        U = init_block(seed, c0, bb, m)
-        V = None
-        Q = None
-        GU = GV = None
-        for _ in range(iters):
-            P = R.T @ U
-            GU = U.T @ U
-            V = ternarize_columns(_cholesky_solve(GU, P.T, ridge(GU)).T, tau).astype(np.float64)
-            Q = R @ V
-            GV = V.T @ V
-            U = ternarize_columns(_cholesky_solve(GV, Q.T, ridge(GV)).T, tau).astype(np.float64)
-        GU = U.T @ U
-        GV = V.T @ V
-        rhs = np.sum(U * Q, axis=0)
-        Mjs = GU * GV
-        try:
-            d = _cholesky_solve(Mjs, rhs, 0.0)
-        except np.linalg.LinAlgError:
-            ridge_retries += 1
-            d = _cholesky_solve(Mjs, rhs, ridge(Mjs))
+        U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters)
+        d, rhs, retried = _joint_scales(U, V, Q)
+        ridge_retries += int(retried)
         R -= (U * d) @ V.T
         B[:, c0:c0 + bb] = U.astype(np.int8)
         C[c0:c0 + bb, :] = V.T.astype(np.int8)
         D[c0:c0 + bb] = d
         trace[blk] = float(np.sum(R * R))
         decrease[blk] = float(d @ rhs)
-    last = trace[-1] if nblocks > 0 else norm_a2
+    sweep_trace = np.zeros(sweeps, dtype=np.float64)
+    kept_old = 0
+    r2 = trace[-1] if nblocks > 0 else norm_a2
+    for sw in range(sweeps):
+        for blk in range(nblocks):
+            c0 = blk * b
+            bb = min(b, k - c0)
+            Uo = B[:, c0:c0 + bb].astype(np.float64)
+            Vo = C[c0:c0 + bb, :].T.astype(np.float64)
+            Rp = R + (Uo * D[c0:c0 + bb]) @ Vo.T
+            U, V, Q = _fit_block(Rp, Uo, tau, iters)
+            d, _, retried = _joint_scales(U, V, Q)
+            ridge_retries += int(retried)
+            Rn = Rp - (U * d) @ V.T
+            r2n = float(np.sum(Rn * Rn))
+            if r2n <= r2:
+                R, r2 = Rn, r2n
+                B[:, c0:c0 + bb] = U.astype(np.int8)
+                C[c0:c0 + bb, :] = V.T.astype(np.int8)
+                D[c0:c0 + bb] = d
+            else:
+                kept_old += 1
+        sweep_trace[sw] = r2
+    last = r2
     E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
     return SeqResult(B, C, D, trace, E, norm_a2,
-                     {"decrease": decrease, "b": b, "ridge_retries": ridge_retries})
+                     {"decrease": decrease, "b": b, "ridge_retries": ridge_retries,
+                      "sweep_trace": sweep_trace, "sweep_kept_old": kept_old})
 
 
 def rank_for_energy(trace, norm_a2, target, step=1, total=None):

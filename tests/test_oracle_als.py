@@ -220,3 +220,44 @@ def test_rank_for_energy_block_steps():
     assert oracle.rank_for_energy([], 0.0, 0.5) == 0
     # a trailing partial block is capped at the decomposition's rank
     assert oracle.rank_for_energy([5.0, 1.0], 10.0, 0.85, step=4, total=7) == 7
+
+
+def test_sweep_on_a_single_block_continues_the_iterations():
+    # With one block, adding it back restores R = A, and the refit starts
+    # from the stored U, so it is the same run continued: one sweep of 15
+    # iterations equals extraction with 30 when the refit is kept, and keeps
+    # the 15-iteration block otherwise (whichever leaves less residual).
+    # seeds 2 and 9 keep the stored block, 8 and 16 take the refit; with
+    # 3 iterations every case takes it
+    for seed, it in ((2, 15), (8, 15), (9, 15), (16, 15), (1, 3), (4, 3)):
+        A = _small(48, 40, 20 + seed)
+        r15 = oracle.decompose_block(A, 0.0, 0.7, iters=it, block=5, seed=seed, k=5)
+        r30 = oracle.decompose_block(A, 0.0, 0.7, iters=2 * it, block=5, seed=seed, k=5)
+        assert not np.array_equal(r15.B, r30.B)
+        sw = oracle.decompose_block(A, 0.0, 0.7, iters=it, block=5, seed=seed, k=5, sweeps=1)
+        want = r30 if r30.E >= r15.E else r15
+        assert np.array_equal(sw.B, want.B) and np.array_equal(sw.C, want.C)
+        np.testing.assert_allclose(sw.D, want.D, rtol=1e-12, atol=0)
+        assert abs(sw.E - max(r15.E, r30.E)) <= 1e-12
+        assert sw.extra["sweep_kept_old"] == (0 if r30.E >= r15.E else 1)
+
+
+def test_sweeps_are_monotone_and_consistent():
+    A = _small(96, 80, 31)
+    base = oracle.decompose_block(A, 1.0, 0.7, block=10, seed=5)
+    sw = oracle.decompose_block(A, 1.0, 0.7, block=10, seed=5, sweeps=4)
+    tr = sw.extra["sweep_trace"]
+    a2 = sw.norm_a2
+    # never above the extraction's residual, never rising from sweep to sweep
+    assert tr[0] <= base.trace[-1] and np.all(np.diff(tr) <= 0)
+    # the recorded residual is the residual of the returned factors
+    R = A.astype(np.float64) - oracle.reconstruct(sw.B, sw.C, sw.D)
+    np.testing.assert_allclose(np.sum(R * R), tr[-1], rtol=1e-10)
+    assert sw.E == 1.0 - tr[-1] / a2
+    # the pages report a clear gain on Gaussian-like matrices
+    assert sw.E > base.E + 1e-3
+    # zero sweeps is the plain extraction
+    z = oracle.decompose_block(A, 1.0, 0.7, block=10, seed=5, sweeps=0)
+    assert np.array_equal(z.B, base.B) and np.array_equal(z.D, base.D) and z.E == base.E
+    with pytest.raises(ValueError):
+        oracle.decompose_block(_small(12, 12, 1), 1.0, 0.7, block=10, sweeps=1)
