@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=200,
                     help="components of the oracle's sequential run timed as the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweeps", type=int, default=10,
+                    help="refinement sweeps measured after the block run (0: skip)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
@@ -137,6 +139,29 @@ def measure_inference(trw, outs, m, n, reps=20):
         res.append({"workload": name, "us_per_call": round(us, 2), "alg_bytes": alg,
                     "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)})
     return res
+
+
+def measure_sweeps(trw, Ad, c, block, sweeps, block_ms, block_energy):
+    """Refinement sweeps (§2.4) after block extraction on the same matrix:
+    one run of extraction + `sweeps` sweeps between HIP events; the time per
+    sweep is that run less the block extraction's mean time, over `sweeps`."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    r = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], block, c["seed"], trace=True, stats=True,
+                      sweeps=sweeps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    a2 = float(r.norm_a2.item())
+    per_sweep = [round(1.0 - float(t) / a2, 6) for t in r.sweep_trace.cpu().numpy()]
+    E = float(r.energy.item())
+    return {"sweeps": sweeps, "ms_total": round(ms, 3),
+            "ms_per_sweep": round((ms - block_ms) / sweeps, 3),
+            "energy_extraction": round(block_energy, 6), "energy_after": round(E, 6),
+            "gain_points": round(100.0 * (E - block_energy), 4),
+            "energy_per_sweep": per_sweep, "visits_kept_old": r.stat("sweep_kept_old")}
 
 
 def cpu_baseline(A, c, sample):
@@ -238,6 +263,11 @@ def main():
         bm["b"] = b
 
     inference = measure_inference(trw, outs, m, n)
+    sweeps = None
+    if "block" in per_mode and args.sweeps > 0:
+        print("[bench] sweeps", file=sys.stderr, flush=True)
+        sweeps = measure_sweeps(trw, Ad, c, block, args.sweeps, per_mode["block"]["ms"],
+                                per_mode["block"]["energy"])
 
     cpu = None
     if not args.no_cpu and args.cpu_sample > 0:
@@ -267,6 +297,7 @@ def main():
                        for kk, vv in per_mode[md].items()} for md in modes},
         "roofline": roofline,
         "inference": inference,
+        "sweeps": sweeps,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

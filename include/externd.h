@@ -67,6 +67,7 @@ enum externd_stat {
   EXTERND_STAT_TIMEOUTS = 9,    /* resident mode: 1 if an exchange wait ran out (energy is NaN) */
   EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode: Gram inverses whose Newton-Schulz
                                     iteration stopped before reaching its tolerance */
+  EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
   EXTERND_STATS_LEN = 16
 };
 
@@ -104,6 +105,17 @@ typedef struct externd_opts {
   void* workspace;
   uint64_t workspace_bytes;
   double* norm_a2;        /* device, optional: receives ||A||_F^2 (fp64) */
+  /* Refinement sweeps (§2.4, block mode only; EXTERND_EINVAL when the block
+   * width is 1).  After extraction every sweep revisits the blocks in order:
+   * the block is added back to R, its iterations run again from its stored U,
+   * the scales are solved jointly, and the refit replaces the block when its
+   * predicted decrease of ||R||^2 is at least the stored block's (measured
+   * exactly while adding it back), else the stored block is deflated again.
+   * The energy therefore never falls from sweep to sweep (up to the fp32
+   * rounding of the deflations). */
+  int32_t sweeps;         /* default 0 */
+  int32_t reserved2;
+  double* sweep_trace;    /* device, optional: sweeps entries, predicted ||R||^2 after each sweep */
 } externd_opts;
 
 /*

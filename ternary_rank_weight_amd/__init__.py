@@ -27,7 +27,7 @@ MODE_AUTO, MODE_STREAMING, MODE_RESIDENT = -1, 0, 1
 STATS_LEN = 16
 STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
         "nonfinite": 5, "mode": 6, "grid": 7, "ridge_retries": 8, "timeouts": 9,
-        "inverse_unconverged": 10}
+        "inverse_unconverged": 10, "sweep_kept_old": 11}
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is missing; build it with "
@@ -51,6 +51,7 @@ class _Opts(ctypes.Structure):
         ("capture_d", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
         ("norm_a2", _p),
+        ("sweeps", _i32), ("reserved2", _i32), ("sweep_trace", _p),
     ]
 
 
@@ -156,7 +157,7 @@ class Decomposition:
 
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
-              capture=None, out=None, workspace=None):
+              capture=None, out=None, workspace=None, sweeps=0):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
@@ -165,6 +166,8 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     workspace: optional contiguous CUDA tensor used as the library's scratch
     memory (at least workspace_bytes(...) bytes, 256-byte aligned); the
     library then allocates nothing.
+    sweeps: refinement sweeps after extraction (block mode only); with
+    trace=True their predicted ||R||^2 values land in .sweep_trace.
     """
     _need(A, torch.float32, "A")
     if A.dim() != 2:
@@ -186,6 +189,7 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     tr = torch.empty((max(ntrace, 1),), dtype=torch.float64, device=dev) if trace else None
     st = torch.zeros((STATS_LEN,), dtype=torch.int64, device=dev) if stats else None
     na2 = torch.empty((1,), dtype=torch.float64, device=dev) if trace else None
+    swt = torch.empty((sweeps,), dtype=torch.float64, device=dev) if trace and sweeps > 0 else None
     opts = _Opts()
     opts.struct_size = ctypes.sizeof(_Opts)
     opts.seed = seed
@@ -193,6 +197,8 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     opts.trace = _ptr(tr)
     opts.stats = _ptr(st)
     opts.norm_a2 = _ptr(na2)
+    opts.sweeps = int(sweeps)
+    opts.sweep_trace = _ptr(swt)
     opts.capture_component = -1
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
@@ -223,7 +229,9 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
         opts.capture_d = _ptr(cap["d"])
     _check(_decompose(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
                       _ptr(D), _ptr(E), ctypes.byref(opts)))
-    return Decomposition(m, n, k, B2, C2, D, E, tr, st, cap, na2, b)
+    res = Decomposition(m, n, k, B2, C2, D, E, tr, st, cap, na2, b)
+    res.sweep_trace = swt
+    return res
 
 
 def rank_for_energy(trace, total, step, norm_a2, target):

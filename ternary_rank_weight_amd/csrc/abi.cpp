@@ -207,13 +207,16 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     o = *opts;
   }
   if (o.mode < -1 || o.mode > 1) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
+  if (o.sweeps < 0) return fail(EXTERND_EINVAL, "sweeps must be >= 0");
   if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
     return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
+  const int b = externd_block_width(m, n, block);
+  if (o.sweeps > 0 && b == 1)
+    return fail(EXTERND_EINVAL, "refinement sweeps need block mode (block width %d)", b);
   int cus = 0;
   int st = check_device(&cus);
   if (st != EXTERND_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int b = externd_block_width(m, n, block);
 
   if (b > 1) {
     externd::BlockArgs ba{};
@@ -232,6 +235,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.trace = o.trace;
     ba.stats = reinterpret_cast<long long*>(o.stats);
     ba.norm_a2 = o.norm_a2;
+    ba.sweeps = o.sweeps;
+    ba.sweep_trace = o.sweep_trace;
     Workspace w;
     if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);

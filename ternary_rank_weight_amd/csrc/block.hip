@@ -782,15 +782,25 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
                                                         double* __restrict__ trace_state,
                                                         double* __restrict__ trace, int64_t blk,
                                                         long long* __restrict__ st, const int* __restrict__ nnz,
-                                                        int bstride) {
+                                                        int bstride, const double* __restrict__ dpart,
+                                                        int64_t ndpart, const double* __restrict__ dold,
+                                                        int* __restrict__ accept) {
   __shared__ GjShared sh;
   __shared__ double rhs[kMaxB];
   __shared__ double dsol[kMaxB];
   __shared__ double s_diag[kMaxB];
   __shared__ double s_tr;
+  __shared__ double red[kCholT / kWave];
   const int t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
   for (int j = t; j < bb; j += kCholT) rhs[j] = rhs_in[j];
+  // sweep visit: the exact rise of ||R||^2 when the stored block was added back
+  double added = 0.0;
+  if (dpart) {
+    double p = 0.0;
+    for (int64_t j = t; j < ndpart; j += kCholT) p += dpart[j];
+    added = block_sum<kCholT>(p, red);
+  }
   // M = (U^T U) o (V^T V); solve without a ridge, retry once with one
   double a[NA][NA];
   bool ok = false;
@@ -841,21 +851,33 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
   __syncthreads();
   if (t == 0) {
     double dec = 0.0;
-    for (int i = 0; i < bb; ++i) {
-      Dout[i] = (float)dsol[i];
-      dscratch[i] = (double)(float)dsol[i];
-      dec += dsol[i] * rhs[i];
+    for (int i = 0; i < bb; ++i) dec += dsol[i] * rhs[i];
+    // On a sweep visit the refit replaces the stored block when it lowers
+    // ||R||^2 at least as much as the stored block did; otherwise the stored
+    // block (codes restored by k_sweep_restore) is deflated again.
+    const bool take = !dpart || dec >= added;
+    if (take) {
+      for (int i = 0; i < bb; ++i) {
+        Dout[i] = (float)dsol[i];
+        dscratch[i] = (double)(float)dsol[i];
+      }
+    } else {
+      for (int i = 0; i < bb; ++i) dscratch[i] = dold[i];
+      atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_SWEEP_KEPT_OLD), 1ull);
     }
-    const double tnew = trace_state[0] - dec;
+    if (accept) *accept = take ? 1 : 0;
+    const double tnew = take ? trace_state[0] + added - dec : trace_state[0];
     trace_state[0] = tnew;
     if (trace) trace[blk] = tnew;
-    long long nb = 0, nc = 0;
-    for (int i = 0; i < bb; ++i) {
-      nb += nnz[i];
-      nc += nnz[bstride + i];
+    if (!dpart) {
+      long long nb = 0, nc = 0;
+      for (int i = 0; i < bb; ++i) {
+        nb += nnz[i];
+        nc += nnz[bstride + i];
+      }
+      st[EXTERND_STAT_NNZ_B] += nb;
+      st[EXTERND_STAT_NNZ_C] += nc;
     }
-    st[EXTERND_STAT_NNZ_B] += nb;
-    st[EXTERND_STAT_NNZ_C] += nc;
   }
   for (int e = t; e < bb * bb; e += kCholT) {
     GU[e] = 0;
@@ -867,12 +889,17 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
 // Rank-b deflation R <- R - U diag(d) V^T with fp32 MFMA (fp32 d; products
 // with ternary entries are exact, sums accumulate in fp32).  grid
 // (ceil(n/64), ceil(m/64)); wave w owns rows r0 + 16w .. +15 and four 16-wide
-// column sub-tiles; K runs over components in steps of 4.
+// column sub-tiles; K runs over components in steps of 4.  With a negated d
+// the same kernel adds a block back.  When dpart is given, each workgroup
+// also writes the exact change of ||R||^2 over its tile (sum of new^2 - old^2
+// in fp64, fixed order) to dpart[tile].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, int64_t m, int64_t n,
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        const uint32_t* __restrict__ Vcodes, int64_t wn,
-                                                       const double* __restrict__ d, int bb) {
+                                                       const double* __restrict__ d, int bb,
+                                                       double* __restrict__ dpart) {
+  __shared__ double red[256 / kWave];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
   const int64_t r0 = (int64_t)blockIdx.y * 64 + 16 * w;
@@ -893,15 +920,69 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
       acc[s] = mfma16x16x4(a, b, acc[s]);
     }
   }
+  double change = 0.0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t col = c0 + 16 * s + i;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t row = r0 + 4 * k + v;
-      if (row < m && col < n) R[row * n + col] -= acc[s][v];
+      if (row < m && col < n) {
+        const float old = R[row * n + col];
+        const float upd = old - acc[s][v];
+        R[row * n + col] = upd;
+        change += (double)upd * (double)upd - (double)old * (double)old;
+      }
     }
   }
+  if (dpart) {
+    const double tot = block_sum<256>(change, red);
+    if (threadIdx.x == 0) dpart[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Refinement sweeps (§2.4).  Before a block is revisited its codes and
+// scales are saved (the refit overwrites the codes in place), -d is staged
+// for adding it back, and the Newton-Schulz warm starts are reset.
+// ---------------------------------------------------------------------------
+__global__ void k_sweep_prepare(int bb, const uint32_t* __restrict__ Uc, int64_t wm,
+                                const uint32_t* __restrict__ Vc, int64_t wn, const float* __restrict__ D,
+                                uint32_t* __restrict__ saved, double* __restrict__ dold,
+                                double* __restrict__ dneg, int* __restrict__ warm_flags) {
+  const int64_t nu = (int64_t)bb * wm, total = nu + (int64_t)bb * wn;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t0 < 2) warm_flags[t0] = 0;
+  if (t0 < bb) {
+    dold[t0] = (double)D[t0];
+    dneg[t0] = -(double)D[t0];
+  }
+  for (int64_t idx = t0; idx < total; idx += (int64_t)gridDim.x * blockDim.x)
+    saved[idx] = idx < nu ? Uc[idx] : Vc[idx - nu];
+}
+
+// Put the saved codes back when the joint solve kept the stored block.
+__global__ void k_sweep_restore(const int* __restrict__ accept, int bb, uint32_t* __restrict__ Uc, int64_t wm,
+                                uint32_t* __restrict__ Vc, int64_t wn, const uint32_t* __restrict__ saved) {
+  if (*accept) return;
+  const int64_t nu = (int64_t)bb * wm, total = nu + (int64_t)bb * wn;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    if (idx < nu) Uc[idx] = saved[idx];
+    else Vc[idx - nu] = saved[idx];
+  }
+}
+
+// Nonzero codes in `words` 2-bit code words, added to *count (exact).
+__global__ void k_count_nonzero(const uint32_t* __restrict__ codes, int64_t words, long long* __restrict__ count) {
+  long long c = 0;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t x = codes[w];
+    c += __popc((x | (x >> 1)) & 0x55555555u);
+  }
+  c = wave_sum(c);
+  if ((threadIdx.x & (kWave - 1)) == 0 && c)
+    atomicAdd(reinterpret_cast<unsigned long long*>(count), (unsigned long long)c);
 }
 
 __global__ void k_zero_i32(int* p, int64_t count) {
@@ -958,7 +1039,9 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   by += sizeof(int) * (size_t)b * 2;                        // nnz
   by += sizeof(double) * (size_t)(2 * b + 4096 + 16);       // d, rhs, norm partials, scalars
   by += sizeof(long long) * EXTERND_STATS_LEN + sizeof(int) * 4;
-  by += 20 * 256;   // alignment slack of the bump allocations
+  by += sizeof(uint32_t) * (size_t)b * ((m + 15) / 16 + (n + 15) / 16);   // sweeps: saved codes
+  by += sizeof(double) * (size_t)(2 * b + ((n + 63) / 64) * ((m + 63) / 64)) + sizeof(int);
+  by += 25 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
 }
@@ -1007,6 +1090,13 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   long long* st = reinterpret_cast<long long*>(bump(p, sizeof(long long) * EXTERND_STATS_LEN));
   int* fail = reinterpret_cast<int*>(bump(p, sizeof(int) * 4));
   int* warm = fail + 2;   // Newton-Schulz warm-start flags, U side and V side
+  // refinement sweeps: saved codes and scales of the visited block, -d, the
+  // per-tile rise of ||R||^2 from adding it back, the keep/replace flag
+  uint32_t* saved = reinterpret_cast<uint32_t*>(bump(p, sizeof(uint32_t) * b * (wm + wn)));
+  double* dold = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
+  double* dneg = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
+  double* dpart = reinterpret_cast<double*>(bump(p, sizeof(double) * ((n + 63) / 64) * ((m + 63) / 64)));
+  int* accept = reinterpret_cast<int*>(bump(p, sizeof(int)));
   double* a2 = scal;
   double* r2 = scal + 1;
   double* tstate = scal + 2;
@@ -1019,16 +1109,19 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
 
   const size_t dec_lds = sizeof(float) * (b * b + b * kDecW);
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
-  const int64_t nblocks = (k + b - 1) / b;
-  for (int64_t blk = 0; blk < nblocks; ++blk) {
-    const int64_t c0 = blk * b;
-    const int bb = (int)std::min<int64_t>(b, k - c0);
-    uint32_t* Uc = a.B2 + c0 * wm;
-    uint32_t* Vc = a.C2 + c0 * wn;
+  const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
+  const int64_t ndpart = (int64_t)defl_grid.x * defl_grid.y;
+
+  // The block iterations from the U held in Uc, then the joint scale solve
+  // (d -> Dout) and the deflation.  trace/tidx: where the predicted ||R||^2
+  // goes (may be null).  On a sweep visit dpart holds the exact rise of
+  // ||R||^2 from adding the stored block back, dold its scales and saved its
+  // codes; the solve keeps whichever block lowers ||R||^2 more.
+  auto fit_block = [&](int bb, uint32_t* Uc, uint32_t* Vc, float* Dout, double* trace, int64_t tidx,
+                       const double* dpart, const double* dold, const uint32_t* saved) {
     const int nt = (bb + 15) / 16;
     const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + kGramSplit - 1) / kGramSplit));
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
-    hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2, warm);
     for (int it = 0; it < a.iters; ++it) {
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
       // inverse depend only on U's codes: up to b = 64 the inverse (Newton-
@@ -1057,12 +1150,44 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     // joint scales from the final U, V and the last Q = R V
     hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf);
     hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
+    int* acc = dpart ? accept : nullptr;
     if (bb <= 64)
-      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
+      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
     else
-      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, a.D + c0, dvec, tstate, a.trace, blk, st, nnz, b);
-    hipLaunchKernelGGL(k_block_deflate, dim3((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64)), dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+    if (dpart)
+      hipLaunchKernelGGL(k_sweep_restore, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, accept, bb, Uc, wm, Vc, wn, saved);
+    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr);
+    return hipGetLastError();
+  };
+
+  const int64_t nblocks = (k + b - 1) / b;
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    const int64_t c0 = blk * b;
+    const int bb = (int)std::min<int64_t>(b, k - c0);
+    hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2, warm);
+    if ((e = fit_block(bb, a.B2 + c0 * wm, a.C2 + c0 * wn, a.D + c0, a.trace, blk, nullptr, nullptr, nullptr)) != hipSuccess)
+      return e;
+  }
+  // Refinement sweeps (§2.4): add each block back, refit it from its stored
+  // U, keep the better of the two.
+  for (int sw = 0; sw < a.sweeps; ++sw) {
+    for (int64_t blk = 0; blk < nblocks; ++blk) {
+      const int64_t c0 = blk * b;
+      const int bb = (int)std::min<int64_t>(b, k - c0);
+      uint32_t* Uc = a.B2 + c0 * wm;
+      uint32_t* Vc = a.C2 + c0 * wn;
+      hipLaunchKernelGGL(k_sweep_prepare, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, bb, Uc, wm, Vc, wn, a.D + c0, saved, dold, dneg, warm);
+      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart);
+      double* tr = (blk == nblocks - 1) ? a.sweep_trace : nullptr;
+      if ((e = fit_block(bb, Uc, Vc, a.D + c0, tr, sw, dpart, dold, saved)) != hipSuccess) return e;
+    }
+  }
+  if (a.sweeps > 0 && k > 0) {
+    // the factors changed: count their nonzeros afresh
+    if ((e = launch_fill_i64(st + EXTERND_STAT_NNZ_B, 2, 0, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wm, 256, 1024)), dim3(256), 0, s, a.B2, k * wm, st + EXTERND_STAT_NNZ_B);
+    hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wn, 256, 1024)), dim3(256), 0, s, a.C2, k * wn, st + EXTERND_STAT_NNZ_C);
   }
   if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_block_finish, dim3(1), dim3(1), 0, s, a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, st, a.stats);

@@ -49,6 +49,8 @@ struct BlockArgs {
   double* trace;
   long long* stats;
   double* norm_a2;   // optional output: ||A||^2
+  int sweeps;          // refinement sweeps after extraction
+  double* sweep_trace; // optional output: predicted ||R||^2 after each sweep
 };
 
 // streaming sequential path and single-step kernels (seq_stream.hip)

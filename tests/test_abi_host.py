@@ -161,3 +161,16 @@ def test_rank_for_energy_matches_oracle(clib):
         trw.rank_for_energy([1.0], 1, 1, -1.0, 0.5)
     with pytest.raises(trw.ExterndError):
         trw.rank_for_energy([1.0], 1, 1, 1.0, float("nan"))
+
+
+def test_decompose_rejects_bad_sweeps(clib):
+    import ternary_rank_weight_amd as trw
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    for sweeps, block in ((1, 0), (1, 1), (-1, 8)):
+        o = trw._Opts()
+        o.struct_size = ctypes.sizeof(trw._Opts)
+        o.mode = -1
+        o.capture_component = -1
+        o.sweeps = sweeps
+        st = trw._decompose(fake, 64, 64, 1.0, 0.7, 15, block, None, fake, fake, fake, fake, ctypes.byref(o))
+        assert st == 1, (sweeps, block)
