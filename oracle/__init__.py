@@ -25,7 +25,8 @@ rule and the ridge eps.
 from .ternarize import mean_abs_threshold, ternarize, ternarize_columns, optimal_projection
 from .init_rule import splitmix64_mix, init_hash, init_signs, init_block
 from .als import (rank_for, block_width, ridge, decompose_seq, decompose_block, rank1_fit,
-                  rank_for_energy)
+                  rank_for_energy, importance_weights, weighted_norm2, block_u_target,
+                  block_v_target)
 from .factors import (reconstruct, apply_factors, energy_from_factors, pack2, unpack2,
                       zero_fraction, bpw_eff, bpw_packed2)
 
@@ -33,7 +34,8 @@ __all__ = [
     "mean_abs_threshold", "ternarize", "ternarize_columns", "optimal_projection",
     "splitmix64_mix", "init_hash", "init_signs", "init_block",
     "rank_for", "block_width", "ridge", "decompose_seq", "decompose_block", "rank1_fit",
-    "rank_for_energy",
+    "rank_for_energy", "importance_weights", "weighted_norm2", "block_u_target",
+    "block_v_target",
     "reconstruct", "apply_factors", "energy_from_factors", "pack2", "unpack2", "zero_fraction",
     "bpw_eff", "bpw_packed2",
 ]

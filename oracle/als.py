@@ -11,6 +11,7 @@ Accuracy Approaching Any Quantization Level):
   §2.3  greedy sequential ALS: alternating ternary fit, optimal scale, deflation
   §2.4  batched block ALS with decorrelated targets and a joint scale solve,
         and refinement sweeps over the extracted blocks
+  §2.5  importance-weighted ALS (column weights h~ = h / max(h) + lambda)
   Appendix (monotone residual): the residual norm never increases.
 
 Readings (listed with their reasons in the design doc):
@@ -37,7 +38,8 @@ from .init_rule import init_signs, init_block
 from .ternarize import ternarize, ternarize_columns
 
 __all__ = ["rank_for", "block_width", "ridge", "decompose_seq", "decompose_block",
-           "rank1_fit", "SeqResult"]
+           "rank1_fit", "SeqResult", "rank_for_energy", "importance_weights", "weighted_norm2",
+           "block_u_target", "block_v_target"]
 
 
 def rank_for(m, n, mu):
@@ -79,12 +81,35 @@ class SeqResult:
         self.extra = extra or {}
 
 
-def rank1_fit(R, u0, tau, iters):
+def importance_weights(h, lam):
+    """Column weights of the importance-weighted objective (§2.5):
+    h~ = h / max(h) + lambda, for per-input-channel second moments h >= 0."""
+    h = np.asarray(h, dtype=np.float64)
+    if h.ndim != 1 or not np.all(np.isfinite(h)) or np.any(h < 0) or not np.isfinite(lam) or lam < 0:
+        raise ValueError("h must be finite and >= 0, lambda finite and >= 0")
+    mx = float(h.max()) if h.size else 0.0
+    if mx == 0.0 and lam == 0.0:
+        raise ValueError("all weights would be zero")
+    return (h / mx if mx > 0 else np.zeros_like(h)) + float(lam)
+
+
+def weighted_norm2(R, w):
+    """sum_ij w_j R_ij^2 (w = None: the plain squared Frobenius norm)."""
+    R = np.asarray(R, dtype=np.float64)
+    return float(np.sum(R * R)) if w is None else float(np.sum((R * R) @ w))
+
+
+def rank1_fit(R, u0, tau, iters, w=None):
     """Alternating ternary fit of one component against residual R (§2.3 steps 1-2).
 
-    Returns dict with u, v (int8), d, c = u^T R v, the history of the
-    intermediate vectors (y_t = R^T u, v_t, x_t = R v, u_t) and nnz counts.
-    R is not modified.
+    w: optional column weights h~ (§2.5).  The v update keeps the plain
+    target R^T u (the weights cancel column by column); the u update targets
+    x = R diag(w) v, and d is the weighted least-squares scale
+    u^T R diag(w) v / (||u||^2 v^T diag(w) v).
+
+    Returns dict with u, v (int8), d, c = u^T R diag(w) v, the history of the
+    intermediate vectors (y_t = R^T u, v_t, x_t = R diag(w) v, u_t), nnz counts
+    and sv = v^T diag(w) v.  R is not modified.
     """
     u = np.asarray(u0, dtype=np.float64)
     hist = []
@@ -93,30 +118,34 @@ def rank1_fit(R, u0, tau, iters):
     for _ in range(iters):
         y = R.T @ u
         v = ternarize(y, tau).astype(np.float64)
-        x = R @ v
+        x = R @ v if w is None else R @ (w * v)
         u_new = ternarize(x, tau).astype(np.float64)
         hist.append((y, v.copy(), x, u_new.copy()))
         u = u_new
     nu = float(np.count_nonzero(u))
     nv = float(np.count_nonzero(v))
+    sv = nv if w is None else float(w @ (v * v))
     c = float(u @ x)
-    d = c / (nu * nv)
+    d = c / (nu * sv)
     return {"u": u.astype(np.int8), "v": v.astype(np.int8), "d": d, "c": c,
-            "nnz_u": int(nu), "nnz_v": int(nv), "hist": hist}
+            "nnz_u": int(nu), "nnz_v": int(nv), "sv": sv, "hist": hist}
 
 
-def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None):
+def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=None):
     """Greedy sequential ALS (§2.3).  Returns SeqResult.
 
     record: optional set of component indices whose rank1_fit history and
     pre-deflation residual are kept in result.extra["records"].
+    weights: optional column weights h~ (importance_weights, §2.5); the
+    trace, norm_a2 and E are then the weighted ones.
     """
+    w = None if weights is None else np.asarray(weights, dtype=np.float64)
     A = np.asarray(A)
     m, n = A.shape
     if k is None:
         k = rank_for(m, n, mu)
     R = A.astype(np.float64, copy=True)
-    norm_a2 = float(np.sum(R * R))
+    norm_a2 = weighted_norm2(R, w)
     B = np.zeros((m, k), dtype=np.int8)
     C = np.zeros((k, n), dtype=np.int8)
     D = np.zeros(k, dtype=np.float64)
@@ -128,7 +157,7 @@ def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None):
         u0 = init_signs(seed, i, m)
         if record is not None and i in record:
             records[i] = {"R": R.copy()}
-        fit = rank1_fit(R, u0, tau, iters)
+        fit = rank1_fit(R, u0, tau, iters, w)
         u = fit["u"].astype(np.float64)
         v = fit["v"].astype(np.float64)
         d = fit["d"]
@@ -136,8 +165,8 @@ def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None):
         B[:, i] = fit["u"]
         C[i, :] = fit["v"]
         D[i] = d
-        trace[i] = float(np.sum(R * R))
-        decrease[i] = fit["c"] ** 2 / (fit["nnz_u"] * fit["nnz_v"])
+        trace[i] = weighted_norm2(R, w)
+        decrease[i] = fit["c"] ** 2 / (fit["nnz_u"] * fit["sv"])
         sum_nnz_u += sum(int(np.count_nonzero(h[3])) for h in fit["hist"])
         if record is not None and i in record:
             records[i]["fit"] = fit
@@ -155,33 +184,49 @@ def _cholesky_solve(G, rhs, eps):
     return np.linalg.solve(Lc.T, z)
 
 
-def _fit_block(R, U, tau, iters):
+def block_v_target(R, U):
+    """Decorrelated V target [(U^T U + eps I)^-1 U^T R]^T (§2.4).  With column
+    weights it is unchanged: each column's weight cancels (§2.5)."""
+    GU = U.T @ U
+    return _cholesky_solve(GU, (R.T @ U).T, ridge(GU)).T
+
+
+def block_u_target(R, V, w=None):
+    """Decorrelated U target Q (V^T diag(w) V + eps I)^-1 with Q = R diag(w) V
+    (§2.4; §2.5 for the weights, w = None meaning all ones).  Returns
+    (target, Q)."""
+    Vw = V if w is None else V * w[:, None]
+    Q = R @ Vw
+    GV = V.T @ Vw
+    return _cholesky_solve(GV, Q.T, ridge(GV)).T, Q
+
+
+def _fit_block(R, U, tau, iters, w=None):
     """The alternating block iterations of §2.4 from the starting block U.
-    Returns (U, V, Q) with Q = R V from the last iteration."""
+    Returns (U, V, Q) with Q = R diag(w) V from the last iteration."""
     V = None
     Q = None
     for _ in range(iters):
-        P = R.T @ U
-        GU = U.T @ U
-        V = ternarize_columns(_cholesky_solve(GU, P.T, ridge(GU)).T, tau).astype(np.float64)
-        Q = R @ V
-        GV = V.T @ V
-        U = ternarize_columns(_cholesky_solve(GV, Q.T, ridge(GV)).T, tau).astype(np.float64)
+        V = ternarize_columns(block_v_target(R, U), tau).astype(np.float64)
+        T, Q = block_u_target(R, V, w)
+        U = ternarize_columns(T, tau).astype(np.float64)
     return U, V, Q
 
 
-def _joint_scales(U, V, Q):
-    """Solve [(U^T U) o (V^T V)] d = diag(U^T R V) (§2.4); diag(U^T R V) is
-    read off Q = R V.  Returns (d, rhs, retried)."""
+def _joint_scales(U, V, Q, w=None):
+    """Solve [(U^T U) o (V^T diag(w) V)] d = diag(U^T R diag(w) V) (§2.4,
+    §2.5); the right side is read off Q = R diag(w) V.  Returns (d, rhs,
+    retried)."""
     rhs = np.sum(U * Q, axis=0)
-    Mjs = (U.T @ U) * (V.T @ V)
+    Mjs = (U.T @ U) * (V.T @ (V if w is None else V * w[:, None]))
     try:
         return _cholesky_solve(Mjs, rhs, 0.0), rhs, False
     except np.linalg.LinAlgError:
         return _cholesky_solve(Mjs, rhs, ridge(Mjs)), rhs, True
 
 
-def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None, sweeps=0):
+def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None, sweeps=0,
+                    weights=None):
     """Batched block ALS with decorrelated targets (§2.4).  Returns SeqResult.
 
     Each iteration:  P = R^T U;  V <- T_col( P (U^T U + eps I)^-1 );
@@ -200,7 +245,12 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     force_width: run the block iteration with exactly this width, bypassing
     the cap and the fall-back to sequential mode (used to pin b = 1 against
     the sequential algorithm).
+
+    weights: optional column weights h~ (importance_weights, §2.5): the U
+    update and the joint solve use R diag(w) and V^T diag(w) V, the V update
+    keeps the plain R; trace, norm_a2 and E are the weighted ones.
     """
+    w = None if weights is None else np.asarray(weights, dtype=np.float64)
     A = np.asarray(A)
     m, n = A.shape
     if k is None:
@@ -209,11 +259,11 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     if b == 1 and force_width is None:
         if sweeps:
             raise ValueError("refinement sweeps need block mode (b >= 2)")
-        res = decompose_seq(A, mu, tau, iters, seed, k)
+        res = decompose_seq(A, mu, tau, iters, seed, k, weights=w)
         res.extra["b"] = 1
         return res
     R = A.astype(np.float64, copy=True)
-    norm_a2 = float(np.sum(R * R))
+    norm_a2 = weighted_norm2(R, w)
     B = np.zeros((m, k), dtype=np.int8)
     C = np.zeros((k, n), dtype=np.int8)
     D = np.zeros(k, dtype=np.float64)
@@ -224,14 +274,14 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     for blk in range(nblocks):
         c0 = blk * b
         bb = min(b, k - c0)
-        U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters)
-        d, rhs, retried = _joint_scales(U, V, Q)
+        U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters, w)
+        d, rhs, retried = _joint_scales(U, V, Q, w)
         ridge_retries += int(retried)
         R -= (U * d) @ V.T
         B[:, c0:c0 + bb] = U.astype(np.int8)
         C[c0:c0 + bb, :] = V.T.astype(np.int8)
         D[c0:c0 + bb] = d
-        trace[blk] = float(np.sum(R * R))
+        trace[blk] = weighted_norm2(R, w)
         decrease[blk] = float(d @ rhs)
     sweep_trace = np.zeros(sweeps, dtype=np.float64)
     kept_old = 0
@@ -243,11 +293,11 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
             Uo = B[:, c0:c0 + bb].astype(np.float64)
             Vo = C[c0:c0 + bb, :].T.astype(np.float64)
             Rp = R + (Uo * D[c0:c0 + bb]) @ Vo.T
-            U, V, Q = _fit_block(Rp, Uo, tau, iters)
-            d, _, retried = _joint_scales(U, V, Q)
+            U, V, Q = _fit_block(Rp, Uo, tau, iters, w)
+            d, _, retried = _joint_scales(U, V, Q, w)
             ridge_retries += int(retried)
             Rn = Rp - (U * d) @ V.T
-            r2n = float(np.sum(Rn * Rn))
+            r2n = weighted_norm2(Rn, w)
             if r2n <= r2:
                 R, r2 = Rn, r2n
                 B[:, c0:c0 + bb] = U.astype(np.int8)

@@ -37,14 +37,22 @@ def apply_factors(B, C, D, x):
     return B @ (D * (C @ x))
 
 
-def energy_from_factors(A, B, C, D):
-    """E = 1 - ||A - B diag(D) C||^2 / ||A||^2 in fp64, from the factors alone (§2.1)."""
+def energy_from_factors(A, B, C, D, weights=None):
+    """E = 1 - ||A - B diag(D) C||^2 / ||A||^2 in fp64, from the factors alone
+    (§2.1).  weights: optional column weights h~; both norms are then the
+    weighted sums sum_ij h~_j X_ij^2 (§2.5)."""
     A64 = np.asarray(A, dtype=np.float64)
-    na2 = float(np.sum(A64 * A64))
+    diff = A64 - reconstruct(B, C, D)
+    if weights is None:
+        na2 = float(np.sum(A64 * A64))
+        r2 = float(np.sum(diff * diff))
+    else:
+        w = np.asarray(weights, dtype=np.float64)
+        na2 = float(np.sum((A64 * A64) @ w))
+        r2 = float(np.sum((diff * diff) @ w))
     if na2 == 0.0:
         return 1.0
-    diff = A64 - reconstruct(B, C, D)
-    return 1.0 - float(np.sum(diff * diff)) / na2
+    return 1.0 - r2 / na2
 
 
 def pack2(T):

@@ -261,3 +261,126 @@ def test_sweeps_are_monotone_and_consistent():
     assert np.array_equal(z.B, base.B) and np.array_equal(z.D, base.D) and z.E == base.E
     with pytest.raises(ValueError):
         oracle.decompose_block(_small(12, 12, 1), 1.0, 0.7, block=10, sweeps=1)
+
+
+# ---- importance-weighted ALS (§2.5) ----------------------------------------
+
+def _skewed_h(n, seed, sigma=1.5):
+    rng = np.random.default_rng(seed)
+    return np.exp(sigma * rng.standard_normal(n))
+
+
+def test_importance_weights_rule():
+    h = np.array([0.5, 2.0, 1.0, 0.0])
+    np.testing.assert_array_equal(oracle.importance_weights(h, 0.0), [0.25, 1.0, 0.5, 0.0])
+    np.testing.assert_array_equal(oracle.importance_weights(h, 0.5), [0.75, 1.5, 1.0, 0.5])
+    np.testing.assert_array_equal(oracle.importance_weights(np.zeros(3), 2.0), [2.0, 2.0, 2.0])
+    for bad in ((np.zeros(3), 0.0), (np.array([1.0, -1.0]), 0.0), (np.array([1.0, np.nan]), 0.0),
+                (np.ones(2), -1.0)):
+        with pytest.raises(ValueError):
+            oracle.importance_weights(*bad)
+
+
+@pytest.mark.parametrize("lam", [0.0, 3.0])
+def test_uniform_weights_reduce_to_the_plain_algorithm(lam):
+    # a flat importance vector gives h~ = 1 + lambda; for 1 and 4 (powers of
+    # two) every step scales exactly, T_tau is scale free and d cancels the
+    # factor, so the weighted run is the plain run bit for bit
+    A = _small(40, 32, 9)
+    w = oracle.importance_weights(np.full(32, 0.37), lam)
+    s0 = oracle.decompose_seq(A, 1.0, 0.7, seed=3)
+    s1 = oracle.decompose_seq(A, 1.0, 0.7, seed=3, weights=w)
+    assert np.array_equal(s0.B, s1.B) and np.array_equal(s0.C, s1.C)
+    np.testing.assert_array_equal(s0.D, s1.D)
+    assert s1.E == s0.E
+    b0 = oracle.decompose_block(A, 1.0, 0.7, block=4, seed=3)
+    b1 = oracle.decompose_block(A, 1.0, 0.7, block=4, seed=3, weights=w)
+    assert np.array_equal(b0.B, b1.B) and np.array_equal(b0.C, b1.C)
+    np.testing.assert_allclose(b1.D, b0.D, rtol=1e-12)
+    assert abs(b1.E - b0.E) <= 1e-12
+
+
+def test_large_lambda_approaches_the_plain_algorithm():
+    A = _small(40, 32, 10)
+    w = oracle.importance_weights(_skewed_h(32, 1), 1e9)
+    s0 = oracle.decompose_seq(A, 1.0, 0.7, seed=1)
+    s1 = oracle.decompose_seq(A, 1.0, 0.7, seed=1, weights=w)
+    assert abs(s1.E - s0.E) <= 1e-6
+
+
+def test_weighted_scale_is_weighted_least_squares():
+    A = _small(30, 24, 11)
+    w = oracle.importance_weights(_skewed_h(24, 2), 0.0)
+    res = oracle.decompose_seq(A, 0.5, 0.7, seed=2, record={0, 5}, weights=w)
+    for i, rec in res.extra["records"].items():
+        R = rec["R"]
+        u = res.B[:, i].astype(np.float64)
+        v = res.C[i].astype(np.float64)
+        sw = np.sqrt(w)
+        X = (np.outer(u, v) * sw).reshape(-1, 1)
+        y = (R * sw).reshape(-1)
+        d_ls = np.linalg.lstsq(X, y, rcond=None)[0][0]
+        assert abs(res.D[i] - d_ls) <= 1e-12 * max(1.0, abs(d_ls))
+        # each half-step's target is, up to a positive factor (T_tau is scale
+        # free), the weighted least-squares fit of the free vector: for v the
+        # weights cancel column by column, for u they do not
+        hist = res.extra["records"][i]["fit"]["hist"]
+        for t in range(1, len(hist)):
+            up = hist[t - 1][3]
+            y, vt, x, _ = hist[t]
+            v_ls = np.array([np.linalg.lstsq((up * sw[j])[:, None], R[:, j] * sw[j], rcond=None)[0][0]
+                             for j in range(R.shape[1])])
+            np.testing.assert_allclose(y / np.sum(up * up), v_ls, rtol=1e-10, atol=1e-14)
+            u_ls = np.array([np.linalg.lstsq((vt * sw)[:, None], R[r] * sw, rcond=None)[0][0]
+                             for r in range(R.shape[0])])
+            np.testing.assert_allclose(x / np.sum(w * vt * vt), u_ls, rtol=1e-10, atol=1e-14)
+
+
+def test_block_targets_are_weighted_least_squares():
+    # U target: rows of min_U ||(R - U V^T) diag(sqrt w)||^2; V target: the
+    # weights cancel column by column, so it is the plain least-squares fit
+    rng = np.random.default_rng(5)
+    R = rng.standard_normal((20, 18))
+    V = rng.choice([-1.0, 0.0, 1.0], size=(18, 4))
+    U = rng.choice([-1.0, 0.0, 1.0], size=(20, 4))
+    w = oracle.importance_weights(_skewed_h(18, 3), 0.1)
+    T, Q = oracle.block_u_target(R, V, w)
+    sw = np.sqrt(w)
+    for i in range(20):
+        x = np.linalg.lstsq(V * sw[:, None], R[i] * sw, rcond=None)[0]
+        np.testing.assert_allclose(T[i], x, rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(Q, R @ (V * w[:, None]), rtol=1e-13)
+    TV = oracle.block_v_target(R, U)
+    for j in range(18):
+        x_w = np.linalg.lstsq(U * sw[j], R[:, j] * sw[j], rcond=None)[0]
+        np.testing.assert_allclose(TV[j], x_w, rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("block", [0, 6])
+def test_weighted_runs_are_monotone_and_consistent(block):
+    A = _small(64, 48, 12)
+    w = oracle.importance_weights(_skewed_h(48, 4), 0.0)
+    dec = oracle.decompose_block if block else (lambda *a, **k: oracle.decompose_seq(*a[:3], **k))
+    kw = dict(seed=1, weights=w)
+    if block:
+        kw["block"] = block
+    r = dec(A, 1.0, 0.7, **kw)
+    assert np.all(np.diff(r.trace) <= 1e-12 * r.norm_a2)
+    assert abs(r.E - oracle.energy_from_factors(A, r.B, r.C, r.D, weights=w)) <= 1e-12
+    assert r.norm_a2 == pytest.approx(float(np.sum((A.astype(np.float64) ** 2) @ w)), rel=1e-14)
+
+
+@pytest.mark.parametrize("block", [0, 6])
+def test_weighting_raises_the_weighted_energy(block):
+    # §2.5: on a skewed importance vector the weighted algorithm preserves
+    # more weighted energy than the plain one
+    A = _small(64, 48, 13)
+    w = oracle.importance_weights(_skewed_h(48, 5, sigma=2.0), 0.0)
+    if block:
+        r0 = oracle.decompose_block(A, 1.0, 0.7, block=block, seed=2)
+        r1 = oracle.decompose_block(A, 1.0, 0.7, block=block, seed=2, weights=w)
+    else:
+        r0 = oracle.decompose_seq(A, 1.0, 0.7, seed=2)
+        r1 = oracle.decompose_seq(A, 1.0, 0.7, seed=2, weights=w)
+    e0 = oracle.energy_from_factors(A, r0.B, r0.C, r0.D, weights=w)
+    assert r1.E > e0 + 0.01, (r1.E, e0)
