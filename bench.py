@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=200,
                     help="components of the oracle's sequential run timed as the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-importance", dest="importance", action="store_false",
+                    help="skip the importance-weighted runs")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2])
@@ -164,6 +166,29 @@ def measure_sweeps(trw, Ad, c, block, sweeps, block_ms, block_energy):
             "energy_per_sweep": per_sweep, "visits_kept_old": r.stat("sweep_kept_old")}
 
 
+def measure_importance(trw, Ad, c, block, modes, sigma=1.5):
+    """Importance-weighted ALS (§2.5) on the same matrix with a synthetic
+    skewed importance vector (lognormal, sigma 1.5, lambda 0): time and
+    weighted energy per mode, one run each between HIP events, next to the
+    plain run's time."""
+    import torch
+    import synthetic
+    h = torch.from_numpy(synthetic.importance(Ad.shape[1], 11, sigma)).cuda()
+    out = {}
+    for md in modes:
+        blk = 0 if md == "seq" else block
+        trw.decompose(Ad, c["mu"], c["tau"], c["iters"], blk, c["seed"], importance=h)   # warm
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], blk, c["seed"], importance=h)
+        e1.record()
+        torch.cuda.synchronize()
+        out[md] = {"ms": round(e0.elapsed_time(e1), 3), "weighted_energy": round(float(r.energy.item()), 6)}
+    return {"importance": f"lognormal(0, {sigma}) over the {Ad.shape[1]} input columns, lambda 0",
+            "modes": out}
+
+
 def cpu_baseline(A, c, sample):
     import numpy as np
     import oracle
@@ -263,6 +288,10 @@ def main():
         bm["b"] = b
 
     inference = measure_inference(trw, outs, m, n)
+    importance = None
+    if args.importance:
+        print("[bench] importance", file=sys.stderr, flush=True)
+        importance = measure_importance(trw, Ad, c, block, modes)
     sweeps = None
     if "block" in per_mode and args.sweeps > 0:
         print("[bench] sweeps", file=sys.stderr, flush=True)
@@ -298,6 +327,7 @@ def main():
         "roofline": roofline,
         "inference": inference,
         "sweeps": sweeps,
+        "importance_weighted": importance,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

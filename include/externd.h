@@ -116,6 +116,18 @@ typedef struct externd_opts {
   int32_t sweeps;         /* default 0 */
   int32_t reserved2;
   double* sweep_trace;    /* device, optional: sweeps entries, predicted ||R||^2 after each sweep */
+  /* Importance-weighted ALS (§2.5, every mode).  importance: device, n
+   * per-input-channel second moments h >= 0 (e.g. from an importance matrix);
+   * the column weights are w_j = h_j / max(h) + importance_lambda, computed
+   * in fp32 on the device (w = lambda when h is all zero).  The objective is
+   * sum_ij w_j (A - B diag(D) C)_ij^2: the u update targets R diag(w) v, the v
+   * update keeps the plain R^T u, d = u^T R diag(w) v / (|u|^2 v^T diag(w) v)
+   * (0 when v^T diag(w) v = 0), block mode uses the Gram V^T diag(w) V, and
+   * energy, trace, sweep_trace and norm_a2 are the weighted sums.  Negative or
+   * non-finite entries of h count as non-finite input (energy NaN). */
+  const float* importance;
+  float importance_lambda; /* >= 0, finite (default 0) */
+  int32_t reserved3;
 } externd_opts;
 
 /*

@@ -14,10 +14,13 @@ these stand in for them with the same shapes):
   16 distinct uniformly drawn columns multiplied by 10.
 * ``low_rank_plus_noise(m, n, seed)``: U diag(s) V^T with U (m x 256) and
   V (n x 256) iid N(0,1), s_i = i^-0.8, plus iid N(0, 0.005^2).
+* ``importance(n, seed, sigma)``: per-input-channel second moments standing
+  in for an importance matrix (none is available): exp(sigma * N(0,1)),
+  a skewed positive vector.
 """
 import numpy as np
 
-__all__ = ["gaussian", "llm_like", "low_rank_plus_noise", "round_bf16",
+__all__ = ["gaussian", "llm_like", "low_rank_plus_noise", "importance", "round_bf16",
            "layer_shapes", "config_matrix", "CONFIGS"]
 
 
@@ -56,6 +59,11 @@ def low_rank_plus_noise(m, n, seed, rank=256, decay=0.8, noise=0.005):
     s = np.arange(1, r + 1, dtype=np.float64) ** (-decay)
     a = (U * s[None, :]) @ V.T + noise * rng.standard_normal((m, n))
     return a.astype(np.float32)
+
+
+def importance(n, seed, sigma=1.5):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.exp(sigma * rng.standard_normal(n)).astype(np.float32)
 
 
 def layer_shapes():

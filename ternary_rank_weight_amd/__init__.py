@@ -52,6 +52,7 @@ class _Opts(ctypes.Structure):
         ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
         ("norm_a2", _p),
         ("sweeps", _i32), ("reserved2", _i32), ("sweep_trace", _p),
+        ("importance", _p), ("importance_lambda", ctypes.c_float), ("reserved3", _i32),
     ]
 
 
@@ -157,7 +158,7 @@ class Decomposition:
 
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
-              capture=None, out=None, workspace=None, sweeps=0):
+              capture=None, out=None, workspace=None, sweeps=0, importance=None, lam=0.0):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
@@ -168,6 +169,9 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     library then allocates nothing.
     sweeps: refinement sweeps after extraction (block mode only); with
     trace=True their predicted ||R||^2 values land in .sweep_trace.
+    importance: optional (n,) float32 CUDA tensor of per-input-channel second
+    moments h; the column weights are h / max(h) + lam (importance-weighted
+    ALS), and energy / trace / norm_a2 become weighted.
     """
     _need(A, torch.float32, "A")
     if A.dim() != 2:
@@ -199,6 +203,12 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     opts.norm_a2 = _ptr(na2)
     opts.sweeps = int(sweeps)
     opts.sweep_trace = _ptr(swt)
+    if importance is not None:
+        _need(importance, torch.float32, "importance")
+        if importance.dim() != 1 or importance.numel() != n:
+            raise ValueError("importance must have n entries")
+        opts.importance = _ptr(importance)
+    opts.importance_lambda = float(lam)
     opts.capture_component = -1
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \

@@ -208,6 +208,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   }
   if (o.mode < -1 || o.mode > 1) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
   if (o.sweeps < 0) return fail(EXTERND_EINVAL, "sweeps must be >= 0");
+  if (!std::isfinite(o.importance_lambda) || o.importance_lambda < 0.f)
+    return fail(EXTERND_EINVAL, "importance_lambda must be finite and >= 0");
   if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
     return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
   const int b = externd_block_width(m, n, block);
@@ -237,6 +239,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.norm_a2 = o.norm_a2;
     ba.sweeps = o.sweeps;
     ba.sweep_trace = o.sweep_trace;
+    ba.importance = o.importance;
+    ba.lambda = o.importance_lambda;
     Workspace w;
     if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);
@@ -259,6 +263,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   sa.trace = o.trace;
   sa.stats = reinterpret_cast<long long*>(o.stats);
   sa.norm_a2 = o.norm_a2;
+  sa.importance = o.importance;
+  sa.lambda = o.importance_lambda;
   sa.capture_component = o.capture_component;
   if (o.capture_component >= 0) {
     if (o.capture_component >= k) return fail(EXTERND_EINVAL, "capture_component >= k");

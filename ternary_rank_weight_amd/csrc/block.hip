@@ -103,6 +103,65 @@ __global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes
 }
 
 // ---------------------------------------------------------------------------
+// Weighted Gram matrix G = X^T diag(wt) X (§2.5) of a ternary block held as
+// 2-bit code rows over L columns.  Workgroup (tile, split) stages the 32 code
+// rows of its 16 x 16 tile and the weights of its kGramSplit words in LDS;
+// thread (r, c) adds +-wt over the columns where both codes are nonzero, in
+// fp64 and in column order, and writes the split's partial for (i, j) (and
+// (j, i)) to Gpart[split].  Every split writes every entry below bb, so no
+// zeroing is needed; k_gram_w_reduce then sums the splits in order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gram_w_partial(const uint32_t* __restrict__ codes, int64_t wl, int bb,
+                                                        const float* __restrict__ wt, int64_t L,
+                                                        double* __restrict__ Gpart) {
+  __shared__ uint32_t rows[32][kGramSplit + 1];
+  __shared__ float ws[kGramSplit * 16];
+  const int t = threadIdx.x;
+  int I = 0;
+  while ((I + 1) * (I + 2) / 2 <= (int)blockIdx.x) ++I;
+  const int J = (int)blockIdx.x - I * (I + 1) / 2;
+  const int r = t >> 4, c = t & 15;
+  const int i = 16 * I + r, j = 16 * J + c;
+  const int64_t w0 = (int64_t)blockIdx.y * kGramSplit;
+  const int cw = (int)min<int64_t>(kGramSplit, wl - w0);
+  for (int e = t; e < 32 * kGramSplit; e += 256) {
+    const int row = e / kGramSplit, w = e % kGramSplit;
+    const int comp = row < 16 ? 16 * I + row : 16 * J + row - 16;
+    rows[row][w] = (w < cw && comp < bb) ? codes[(int64_t)comp * wl + w0 + w] : 0u;
+  }
+  for (int e = t; e < kGramSplit * 16; e += 256) {
+    const int64_t col = w0 * 16 + e;
+    ws[e] = col < L ? wt[col] : 0.f;
+  }
+  __syncthreads();
+  double acc = 0.0;
+  for (int w = 0; w < cw; ++w) {
+    const uint32_t x = rows[r][w], y = rows[16 + c][w];
+    uint32_t both = x & y & 0x55555555u;
+    const uint32_t diff = (x ^ y) >> 1;
+    while (both) {
+      const int b = __ffs(both) - 1;   // even: the low bit of element b / 2
+      const double wv = (double)ws[w * 16 + (b >> 1)];
+      acc += ((diff >> b) & 1u) ? -wv : wv;
+      both &= both - 1u;
+    }
+  }
+  if (i < bb && j < bb) {
+    double* Gs = Gpart + (int64_t)blockIdx.y * bb * bb;
+    Gs[i * bb + j] = acc;
+    if (I != J) Gs[j * bb + i] = acc;
+  }
+}
+
+__global__ void k_gram_w_reduce(const double* __restrict__ Gpart, int splits, int bb, double* __restrict__ G) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= bb * bb) return;
+  double s = 0.0;
+  for (int q = 0; q < splits; ++q) s += Gpart[(int64_t)q * bb * bb + e];
+  G[e] = s;
+}
+
+// ---------------------------------------------------------------------------
 // Small dense fp64 linear algebra on one workgroup: the inverse of a
 // symmetric positive definite matrix, used to decorrelate the ALS targets
 // and to solve for the joint scales.
@@ -240,8 +299,15 @@ __device__ bool gj_inverse(double (&a)[NA][NA], int bb, GjShared& sh) {
 // G is integer valued and is zeroed after being read so the next Gram
 // accumulation starts from zero.  `fail` is set if G + eps I is not positive
 // definite.  One workgroup.
-template <int NA>  // bb <= 16 * NA
-__device__ __forceinline__ void spd_inverse_body(int* __restrict__ G, int bb, float* __restrict__ Ginv,
+// G is an exact integer Gram (int, zeroed after reading so the next
+// accumulation starts from zero) or a weighted one (double, left as is).
+template <typename GT>
+__device__ inline void consume_gram(GT* G, int e) {
+  if constexpr (sizeof(GT) == sizeof(int)) G[e] = 0;
+}
+
+template <int NA, typename GT>  // bb <= 16 * NA
+__device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ Ginv,
                                  int* __restrict__ fail) {
   __shared__ GjShared sh;
   __shared__ double s_diag[kMaxB];
@@ -256,7 +322,7 @@ __device__ __forceinline__ void spd_inverse_body(int* __restrict__ G, int bb, fl
       const int i = ti + 16 * x, j = tj + 16 * y;
       const bool in = i < bb && j < bb;
       a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
-      if (in) G[i * bb + j] = 0;
+      if (in) consume_gram(G, i * bb + j);
       if (in && i == j) s_diag[i] = a[x][y];
     }
   __syncthreads();
@@ -283,10 +349,10 @@ __device__ __forceinline__ void spd_inverse_body(int* __restrict__ G, int bb, fl
     }
 }
 
-template <int NA>
-__global__ __launch_bounds__(kCholT) void k_spd_inverse(int* __restrict__ G, int bb,
+template <int NA, typename GT>
+__global__ __launch_bounds__(kCholT) void k_spd_inverse(GT* __restrict__ G, int bb,
                                                         float* __restrict__ Ginv, int* __restrict__ fail) {
-  spd_inverse_body<NA>(G, bb, Ginv, fail);
+  spd_inverse_body<NA, GT>(G, bb, Ginv, fail);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,9 +442,12 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
 // float4 and feeds component q at MFMA step q (column c + 4k + q); the V
 // operand of lane (comp + 16k) uses the same column.
 // ---------------------------------------------------------------------------
+// With W, the V operand is diag(wt) V (§2.5): Q = R diag(wt) V.
+template <bool W>
 __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, int64_t m, int64_t n,
                                   const uint32_t* __restrict__ Vcodes, int64_t wn, int bb,
-                                  int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by) {
+                                  int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by,
+                                  const float* __restrict__ wt) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
   const int64_t row = (int64_t)bx * 64 + 16 * w + i;
@@ -389,7 +458,7 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
   f4 acc[kMaxB / 16];
 #pragma unroll
   for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int64_t c, float (&av)[4], uint32_t (&cw)[kMaxB / 16]) {
+  auto load = [&](int64_t c, float (&av)[4], float (&wq)[4], uint32_t (&cw)[kMaxB / 16]) {
     const int64_t cc = c + 4 * k;
     if (row < m && vec_ok && cc + 3 < c_end) {
       const float4 x = *reinterpret_cast<const float4*>(R + row * n + cc);
@@ -398,6 +467,10 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 #pragma unroll
       for (int q = 0; q < 4; ++q) av[q] = (row < m && cc + q < c_end) ? R[row * n + cc + q] : 0.f;
     }
+    if constexpr (W) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wq[q] = cc + q < c_end ? wt[cc + q] : 0.f;
+    }
     const int64_t word = c >> 4;
 #pragma unroll
     for (int s = 0; s < kMaxB / 16; ++s) {
@@ -405,20 +478,21 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
       cw[s] = (s < nsub && comp < bb) ? Vcodes[(int64_t)comp * wn + word] : 0u;
     }
   };
-  float av[4];
+  float av[4], wq[4] = {1.f, 1.f, 1.f, 1.f};
   uint32_t cw[kMaxB / 16];
-  if (c_begin < c_end) load(c_begin, av, cw);
+  if (c_begin < c_end) load(c_begin, av, wq, cw);
   for (int64_t c = c_begin; c < c_end; c += 16) {
-    float avn[4];
+    float avn[4], wqn[4];
     uint32_t cwn[kMaxB / 16];
     const bool more = c + 16 < c_end;
-    if (more) load(c + 16, avn, cwn);
+    if (more) load(c + 16, avn, wqn, cwn);
 #pragma unroll
     for (int s = 0; s < kMaxB / 16; ++s) {
       if (s < nsub) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float bv = value_of_code((cw[s] >> (2 * (4 * k + q))) & 3u);
+          float bv = value_of_code((cw[s] >> (2 * (4 * k + q))) & 3u);
+          if constexpr (W) bv *= wq[q];
           acc[s] = mfma16x16x4(av[q], bv, acc[s]);
         }
       }
@@ -426,6 +500,10 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
     if (more) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) av[q] = avn[q];
+      if constexpr (W) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wq[q] = wqn[q];
+      }
 #pragma unroll
       for (int s = 0; s < kMaxB / 16; ++s) cw[s] = cwn[s];
     }
@@ -444,11 +522,12 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
   }
 }
 
+template <bool W>
 __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
                                                       const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                       int bb, int64_t cols_per_split,
-                                                      float* __restrict__ Qt_part) {
-  contract_r_v_body(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y);
+                                                      float* __restrict__ Qt_part, const float* __restrict__ wt) {
+  contract_r_v_body<W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt);
 }
 
 
@@ -509,7 +588,8 @@ __device__ inline void ns_mm(const float* A, const float* B, f4 (&acc)[4]) {
   }
 }
 
-__device__ __forceinline__ void ns_inverse_body(int* __restrict__ G, int bb, float* __restrict__ X,
+template <typename GT>
+__device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ X,
                                                 int* __restrict__ warm_flag,
                                                 long long* __restrict__ unconverged) {
   __shared__ NsShared sh;
@@ -521,11 +601,11 @@ __device__ __forceinline__ void ns_inverse_body(int* __restrict__ G, int bb, flo
   // G' = G + eps I in LDS, the identity beyond bb; all loads issued first
   double trp = 0.0;
   {
-    int gv[kPer];
+    GT gv[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
-      gv[q] = (r < bb && c < bb) ? G[r * bb + c] : 0;
+      gv[q] = (r < bb && c < bb) ? G[r * bb + c] : (GT)0;
     }
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -533,8 +613,8 @@ __device__ __forceinline__ void ns_inverse_body(int* __restrict__ G, int bb, flo
       float v = (r == c) ? 1.f : 0.f;
       if (r < bb && c < bb) {
         v = (float)gv[q];
-        if (r == c) trp += v;
-        G[r * bb + c] = 0;
+        if (r == c) trp += (double)gv[q];
+        consume_gram(G, r * bb + c);
       }
       sh.G[r * kNsS + c] = v;
     }
@@ -634,17 +714,24 @@ __device__ __forceinline__ void ns_inverse_body(int* __restrict__ G, int bb, flo
 // the Gram matrix of the same codes meanwhile: both depend only on the codes
 // and R, and the decorrelation needs both.  One launch instead of two keeps
 // them concurrent without a second stream.
-template <bool UT>
+// With W (V side only) the contraction is R diag(wt) V and G is the weighted
+// Gram V^T diag(wt) V in fp64 (§2.5).
+template <bool UT, bool W>
 __global__ __launch_bounds__(kCT) void k_contract_with_inverse(
     const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
-    int bb, int64_t per_split, float* __restrict__ Part, int* __restrict__ G,
-    float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ unconverged) {
+    int bb, int64_t per_split, float* __restrict__ Part, void* __restrict__ G,
+    float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ unconverged,
+    const float* __restrict__ wt) {
+  static_assert(!(UT && W), "weights apply to the V-side contraction only");
   if ((int)blockIdx.x == (int)gridDim.x - 1) {
-    if (blockIdx.y == 0) ns_inverse_body(G, bb, Ginv, warm_flag, unconverged);
+    if (blockIdx.y == 0) {
+      if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, unconverged);
+      else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, unconverged);
+    }
     return;
   }
-  if (UT) contract_ut_r_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
-  else contract_r_v_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
+  if constexpr (UT) contract_ut_r_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
+  else contract_r_v_body<W>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y, wt);
 }
 
 // ---------------------------------------------------------------------------
@@ -775,8 +862,10 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
 // test a Cholesky factorisation makes) it is inverted again with the ridge
 // and the retry is counted.  d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
 // ---------------------------------------------------------------------------
+// GVw (optional): the weighted Gram V^T diag(wt) V in place of GV (§2.5).
 template <int NA>  // bb <= 16 * NA
 __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, int* __restrict__ GV,
+                                                        const double* __restrict__ GVw,
                                                         int bb, const double* __restrict__ rhs_in,
                                                         float* __restrict__ Dout, double* __restrict__ dscratch,
                                                         double* __restrict__ trace_state,
@@ -811,7 +900,8 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
       for (int y = 0; y < NA; ++y) {
         const int i = ti + 16 * x, j = tj + 16 * y;
         const bool in = i < bb && j < bb;
-        a[x][y] = in ? (double)GU[i * bb + j] * (double)GV[i * bb + j] : (i == j ? 1.0 : 0.0);
+        a[x][y] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
+                     : (i == j ? 1.0 : 0.0);
         if (in && i == j) s_diag[i] = a[x][y];
       }
     __syncthreads();
@@ -892,13 +982,13 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
 // column sub-tiles; K runs over components in steps of 4.  With a negated d
 // the same kernel adds a block back.  When dpart is given, each workgroup
 // also writes the exact change of ||R||^2 over its tile (sum of new^2 - old^2
-// in fp64, fixed order) to dpart[tile].
+// in fp64, fixed order; weighted by wt[col] when given) to dpart[tile].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, int64_t m, int64_t n,
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                        const double* __restrict__ d, int bb,
-                                                       double* __restrict__ dpart) {
+                                                       double* __restrict__ dpart, const float* __restrict__ wt) {
   __shared__ double red[256 / kWave];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
@@ -931,7 +1021,8 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
         const float old = R[row * n + col];
         const float upd = old - acc[s][v];
         R[row * n + col] = upd;
-        change += (double)upd * (double)upd - (double)old * (double)old;
+        const double ch = (double)upd * (double)upd - (double)old * (double)old;
+        change += wt ? ch * (double)wt[col] : ch;
       }
     }
   }
@@ -1041,7 +1132,10 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   by += sizeof(long long) * EXTERND_STATS_LEN + sizeof(int) * 4;
   by += sizeof(uint32_t) * (size_t)b * ((m + 15) / 16 + (n + 15) / 16);   // sweeps: saved codes
   by += sizeof(double) * (size_t)(2 * b + ((n + 63) / 64) * ((m + 63) / 64)) + sizeof(int);
-  by += 25 * 256;   // alignment slack of the bump allocations
+  // importance weights: column weights, weighted Gram and its split partials
+  by += sizeof(float) * (size_t)n;
+  by += sizeof(double) * (size_t)b * b * (1 + ((n + 15) / 16 + kGramSplit - 1) / kGramSplit);
+  by += 28 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
 }
@@ -1052,11 +1146,12 @@ inline char* bump(char*& p, size_t bytes) {
   return r;
 }
 
-void launch_inverse(int bb, int* G, float* Ginv, int* fail, hipStream_t st) {
+template <typename GT>
+void launch_inverse(int bb, GT* G, float* Ginv, int* fail, hipStream_t st) {
   if (bb <= 64)
-    hipLaunchKernelGGL(k_spd_inverse<4>, dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
+    hipLaunchKernelGGL((k_spd_inverse<4, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
   else
-    hipLaunchKernelGGL(k_spd_inverse<8>, dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
+    hipLaunchKernelGGL((k_spd_inverse<8, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
 }
 
 }  // namespace
@@ -1097,13 +1192,23 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   double* dneg = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
   double* dpart = reinterpret_cast<double*>(bump(p, sizeof(double) * ((n + 63) / 64) * ((m + 63) / 64)));
   int* accept = reinterpret_cast<int*>(bump(p, sizeof(int)));
+  // importance weighting (§2.5): column weights wt, the weighted V-side Gram
+  // V^T diag(wt) V and its per-split partials
+  const bool W = a.importance != nullptr;
+  const int wsplits = (int)((wn + kGramSplit - 1) / kGramSplit);
+  float* wt = reinterpret_cast<float*>(bump(p, sizeof(float) * n));
+  double* GVw = reinterpret_cast<double*>(bump(p, sizeof(double) * b * b));
+  double* Gwpart = reinterpret_cast<double*>(bump(p, sizeof(double) * b * b * wsplits));
+  if (!W) wt = nullptr;
   double* a2 = scal;
   double* r2 = scal + 1;
   double* tstate = scal + 2;
 
   hipError_t e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
-  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
+  if (W && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
+    return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
@@ -1129,35 +1234,50 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       // concurrently with it; wider blocks invert by Gauss-Jordan first.
       hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
       if (bb <= 64) {
-        hipLaunchKernelGGL((k_contract_with_inverse<true>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, GU, GinvU, warm, st + EXTERND_STAT_INVERSE_UNCONVERGED);
+        hipLaunchKernelGGL((k_contract_with_inverse<true, false>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)nullptr);
       } else {
         launch_inverse(bb, GU, GinvU, fail, s);
         hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
       hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
-      // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V
-      hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
-      if (bb <= 64) {
-        hipLaunchKernelGGL((k_contract_with_inverse<false>), dim3((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, GV, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED);
+      // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V;  weighted (§2.5):
+      // Q = R diag(wt) V and the Gram V^T diag(wt) V
+      const dim3 cgrid2((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2);
+      if (W) {
+        hipLaunchKernelGGL(k_gram_w_partial, dim3(gram_v.x, (unsigned)wsplits), dim3(256), 0, s, Vc, wn, bb, wt, n, Gwpart);
+        hipLaunchKernelGGL(k_gram_w_reduce, dim3((unsigned)((bb * bb + 255) / 256)), dim3(256), 0, s, Gwpart, wsplits, bb, GVw);
+        if (bb <= 64) {
+          hipLaunchKernelGGL((k_contract_with_inverse<false, true>), cgrid2, dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)wt);
+        } else {
+          launch_inverse(bb, GVw, GinvV, fail, s);
+          hipLaunchKernelGGL(k_contract_r_v<true>, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)wt);
+        }
       } else {
-        launch_inverse(bb, GV, GinvV, fail, s);
-        hipLaunchKernelGGL(k_contract_r_v, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part);
+        hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
+        if (bb <= 64) {
+          hipLaunchKernelGGL((k_contract_with_inverse<false, false>), cgrid2, dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)nullptr);
+        } else {
+          launch_inverse(bb, GV, GinvV, fail, s);
+          hipLaunchKernelGGL(k_contract_r_v<false>, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)nullptr);
+        }
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
       hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
     }
-    // joint scales from the final U, V and the last Q = R V
+    // joint scales from the final U, V and the last Q = R V (weighted: the
+    // last V-side Gram GVw already belongs to the final V)
     hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf);
-    hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
+    if (!W) hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
     int* acc = dpart ? accept : nullptr;
+    const double* gvw = W ? GVw : nullptr;
     if (bb <= 64)
-      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
     else
-      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
     if (dpart)
       hipLaunchKernelGGL(k_sweep_restore, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, accept, bb, Uc, wm, Vc, wn, saved);
-    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr);
+    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr, (const float*)nullptr);
     return hipGetLastError();
   };
 
@@ -1178,7 +1298,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       uint32_t* Uc = a.B2 + c0 * wm;
       uint32_t* Vc = a.C2 + c0 * wn;
       hipLaunchKernelGGL(k_sweep_prepare, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, bb, Uc, wm, Vc, wn, a.D + c0, saved, dold, dneg, warm);
-      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart);
+      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart, (const float*)wt);
       double* tr = (blk == nblocks - 1) ? a.sweep_trace : nullptr;
       if ((e = fit_block(bb, Uc, Vc, a.D + c0, tr, sw, dpart, dold, saved)) != hipSuccess) return e;
     }
@@ -1189,7 +1309,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wm, 256, 1024)), dim3(256), 0, s, a.B2, k * wm, st + EXTERND_STAT_NNZ_B);
     hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wn, 256, 1024)), dim3(256), 0, s, a.C2, k * wn, st + EXTERND_STAT_NNZ_C);
   }
-  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s, wt, n)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_block_finish, dim3(1), dim3(1), 0, s, a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, st, a.stats);
   if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   return hipGetLastError();

@@ -32,6 +32,8 @@ struct SeqArgs {
   int8_t* capture_u;
   float* capture_d;
   double* norm_a2;   // optional output: ||A||^2
+  const float* importance;   // optional: n per-input-channel second moments h (§2.5)
+  float lambda;              // column weights h / max(h) + lambda
 };
 
 // Arguments of one block-mode decomposition.
@@ -51,6 +53,8 @@ struct BlockArgs {
   double* norm_a2;   // optional output: ||A||^2
   int sweeps;          // refinement sweeps after extraction
   double* sweep_trace; // optional output: predicted ||R||^2 after each sweep
+  const float* importance;   // optional: n per-input-channel second moments h (§2.5)
+  float lambda;              // column weights h / max(h) + lambda
 };
 
 // streaming sequential path and single-step kernels (seq_stream.hip)
@@ -58,16 +62,22 @@ size_t stream_workspace_bytes(int64_t m, int64_t n);
 hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s);
 int64_t gemv_t_chunks(int64_t m);
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
-                            long long* fallbacks, hipStream_t s);
+                            long long* fallbacks, hipStream_t s, const float* wt = nullptr,
+                            double* wsum = nullptr);
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
                          const uint32_t* vprev, hipStream_t s);
 hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
-                         hipStream_t s);
+                         hipStream_t s, const float* wt = nullptr);
 hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
                           const uint32_t* v_codes, const float* dptr, hipStream_t s);
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
-                        double* out, long long* nonfinite, hipStream_t s);
+                        double* out, long long* nonfinite, hipStream_t s, const float* wt = nullptr,
+                        int64_t ncols = 0);
+// Column weights wt[j] = h[j] / max(h) + lambda in fp32 (§2.5); negative or
+// non-finite h entries are added to *nonfinite.
+hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, float* wt,
+                                     long long* nonfinite, hipStream_t s);
 hipError_t launch_copy_f64(const double* src, double* dst, int64_t count, hipStream_t s);
 hipError_t launch_energy_finish(const double* a2, const double* r2, const long long* nonfinite,
                                 double* energy, hipStream_t s);

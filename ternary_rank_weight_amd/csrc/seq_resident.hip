@@ -49,7 +49,8 @@ struct ResArgs {
   float* D;
   double* trace;
   long long* stats;            // EXTERND_STATS_LEN, written by workgroup 0
-  const double* a2;            // ||A||^2
+  const double* a2;            // ||A||^2 (weighted when wt is set)
+  const float* wt;             // optional column weights (§2.5), n floats
   const long long* nonfinite;  // count of non-finite entries of A
   unsigned* yslot;             // n words
   unsigned* xslot;             // m words
@@ -348,6 +349,14 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   for (int j = 0; j < KC; ++j) u[j] = 0.f;
 #pragma unroll
   for (int j = 0; j < KR; ++j) v[j] = 0.f;
+  // column weights of this thread's columns (§2.5); exactly 1 when unweighted,
+  // which leaves every product and sum below unchanged
+  float wv[KR];
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    const int col = t + T * j;
+    wv[j] = (a.wt && col < n) ? a.wt[col] : 1.f;
+  }
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
   long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
@@ -435,15 +444,18 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           }
         }
       }
-      // ---- x = R v on the row copy; u = T_tau(x) ----
+      // ---- x = R diag(w) v on the row copy; u = T_tau(x) ----
       {
+        float vw[KR];
+#pragma unroll
+        for (int j = 0; j < KR; ++j) vw[j] = v[j] * wv[j];
         float acc[LR];
 #pragma unroll
         for (int l = 0; l < LR; ++l) {
           const float* rp = rrow + l * KR * T + t;
           float s = 0.f;
 #pragma unroll
-          for (int j = 0; j < KR; ++j) s = fmaf(v[j], rp[j * T], s);
+          for (int j = 0; j < KR; ++j) s = fmaf(vw[j], rp[j * T], s);
           acc[l] = s;
         }
         ++rx;
@@ -484,18 +496,21 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       if (col >= col0 && col < col0 + a.CB && col < n) v_own[col - col0] = v[j];
     }
 
-    // ---- scale d = u.x / (nnz_u nnz_v) (§2.3 step 2); one barrier ----
+    // ---- scale d = u.x / (nnz_u v^T diag(w) v) (§2.3 step 2, §2.5); one barrier ----
     {
-      double sums[3] = {cpart, 0.0, 0.0};
+      double sums[4] = {cpart, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int j = 0; j < KC; ++j) sums[1] += (u[j] != 0.f) ? 1.0 : 0.0;
 #pragma unroll
-      for (int j = 0; j < KR; ++j) sums[2] += (v[j] != 0.f) ? 1.0 : 0.0;
-      block_sum_f64<T, 3>(sums, bufs[2]);
+      for (int j = 0; j < KR; ++j) {
+        sums[2] += (v[j] != 0.f) ? 1.0 : 0.0;
+        sums[3] += (v[j] != 0.f) ? (double)wv[j] : 0.0;
+      }
+      block_sum_f64<T, 4>(sums, bufs[2]);
       const double c = sums[0], nu = sums[1], nv = sums[2];
-      const double den = nu * nv;
-      d32 = (float)(c / den);
-      trace_state -= c * c / den;
+      const double den = nu * sums[3];
+      d32 = den > 0.0 ? (float)(c / den) : 0.f;
+      trace_state -= den > 0.0 ? c * c / den : 0.0;
       st_b += (long long)nu;
       st_c += (long long)nv;
       if (g == 0 && t == 0) {
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
       const double r = (double)rrow[(l * KR + j) * T + t];
-      r2[0] += r * r;
+      r2[0] += r * r * (double)wv[j];
     }
   block_sum_f64<T, 1>(r2, bufs[0]);
   if (t == 0) a.r2_partial[g] = r2[0];
@@ -601,7 +616,7 @@ bool resident_fits(int64_t m, int64_t n, int num_cus) {
 
 size_t resident_workspace_bytes(int64_t m, int64_t n) {
   return sizeof(unsigned long long) * (size_t)(m + n) + sizeof(double) * (256 + 4096 + 8) +
-         sizeof(long long) * 8 + sizeof(unsigned) * 64 + 256 * 8;
+         sizeof(long long) * 8 + sizeof(unsigned) * 64 + sizeof(float) * (size_t)n + 256 * 9;
 }
 
 static inline char* align256(char* p) {
@@ -626,13 +641,16 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   long long* nonfinite = reinterpret_cast<long long*>(p);
   p = align256(p + sizeof(long long) * 8);
   unsigned* err = reinterpret_cast<unsigned*>(p);
+  p = align256(p + sizeof(unsigned) * 64);
+  float* wt = a.importance ? reinterpret_cast<float*>(p) : nullptr;   // column weights (§2.5)
 
   hipError_t e;
   hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)a.n);
   hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)a.m);
   if ((e = launch_fill_i64(nonfinite, 1, 0, s)) != hipSuccess) return e;
   if ((e = launch_fill_u32(err, 1, 0u, s)) != hipSuccess) return e;
-  if ((e = launch_norm2(a.A, a.m * a.n, npart, 4096, a2, nonfinite, s)) != hipSuccess) return e;
+  if (wt && (e = launch_importance_weights(a.importance, a.n, a.lambda, wt, nonfinite, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, a.m * a.n, npart, 4096, a2, nonfinite, s, wt, a.n)) != hipSuccess) return e;
   if (a.stats && (e = launch_fill_i64(a.stats, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
 
   ResArgs ra{};
@@ -652,6 +670,7 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   ra.trace = a.trace;
   ra.stats = a.stats;
   ra.a2 = a2;
+  ra.wt = wt;
   ra.nonfinite = nonfinite;
   ra.yslot = reinterpret_cast<unsigned*>(yslot);   // 32-bit words; zero = parity 0
   ra.xslot = reinterpret_cast<unsigned*>(xslot);

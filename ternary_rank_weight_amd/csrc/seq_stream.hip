@@ -19,7 +19,10 @@ constexpr int kTernT = 1024;
 __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ x, int64_t N,
                                                       float tau, uint32_t* __restrict__ codes,
                                                       int32_t* __restrict__ nnz_out,
-                                                      long long* __restrict__ fallbacks) {
+                                                      long long* __restrict__ fallbacks,
+                                                      const float* __restrict__ wt,
+                                                      double* __restrict__ wsum) {
+  // wsum (with wt): sum of wt over the kept entries, i.e. v^T diag(wt) v (§2.5)
   __shared__ double scratch[kTernT / kWave];
   float* fs = reinterpret_cast<float*>(scratch);
   int* is = reinterpret_cast<int*>(scratch);
@@ -32,6 +35,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
     for (int64_t w = tid; w < words; w += kTernT) codes[w] = (w == 0) ? 1u : 0u;
     if (tid == 0) {
       if (nnz_out) *nnz_out = 1;
+      if (wsum) *wsum = (double)wt[0];
       if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
     }
     return;
@@ -42,6 +46,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   const double Q = block_sum<kTernT>(q, scratch);
   const double thr = fixed_point_threshold(Q, s, tau, N);
   int cnt = 0;
+  double ws = 0.0;
   for (int64_t w = tid; w < words; w += kTernT) {
     uint32_t word = 0;
     for (int e = 0; e < 16; ++e) {
@@ -51,6 +56,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
         if ((double)fabsf(v) > thr) {
           word |= code_of(v) << (2 * e);
           ++cnt;
+          if (wsum) ws += (double)wt[j];
         }
       }
     }
@@ -58,6 +64,10 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   }
   if ((double)M > thr) {
     const int total = block_sum<kTernT>(cnt, is);
+    if (wsum) {
+      const double wt_total = block_sum<kTernT>(ws, scratch);
+      if (tid == 0) *wsum = wt_total;
+    }
     if (tid == 0 && nnz_out) *nnz_out = total;
     return;
   }
@@ -70,6 +80,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   if (tid == 0) {
     codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
     if (nnz_out) *nnz_out = 1;
+    if (wsum) *wsum = (double)wt[idx];
     if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
   }
 }
@@ -129,18 +140,23 @@ __global__ void k_sum_chunks(const float* __restrict__ partial, int64_t chunks, 
 }
 
 // x = R v: one wave per row, lanes stride the row; masked add/sub as FMA with
-// v in {-1, 0, 1} (exact products).
+// v in {-1, 0, 1} (exact products).  With column weights wt the target is
+// x = R diag(wt) v (§2.5): each product uses wt_c v_c (exact sign change).
 constexpr int kGnT = 256;
 
 __global__ __launch_bounds__(kGnT) void k_gemv_n(const float* __restrict__ R, int64_t m,
                                                  int64_t n, const uint32_t* __restrict__ v_codes,
-                                                 float* __restrict__ x) {
+                                                 float* __restrict__ x, const float* __restrict__ wt) {
   const int64_t row = (int64_t)blockIdx.x * (kGnT / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= m) return;
   const float* rp = R + row * n;
   float acc = 0.f;
-  for (int64_t c = lane; c < n; c += kWave) acc = fmaf(code_at(v_codes, c), rp[c], acc);
+  if (wt) {
+    for (int64_t c = lane; c < n; c += kWave) acc = fmaf(code_at(v_codes, c) * wt[c], rp[c], acc);
+  } else {
+    for (int64_t c = lane; c < n; c += kWave) acc = fmaf(code_at(v_codes, c), rp[c], acc);
+  }
   acc = wave_sum(acc);
   if (lane == 0) x[row] = acc;
 }
@@ -174,6 +190,9 @@ __global__ void k_start_codes(uint64_t seed, int64_t comp, int64_t m, uint32_t* 
 }
 
 // d = (u . x) / (nnz_u nnz_v) in fp64, stored as fp32 in D[i]; trace update.
+// With column weights, x = R diag(wt) v and the v factor of the denominator
+// is v^T diag(wt) v (*sv); d = 0 when that is zero (every weight on supp(v)
+// is zero, so u . x = 0 too and any d fits equally).
 __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, int64_t m,
                                                   const uint32_t* __restrict__ u_codes,
                                                   const int32_t* __restrict__ nnz_u,
@@ -181,16 +200,17 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
                                                   float* __restrict__ D, int64_t i,
                                                   double* __restrict__ trace_state,
                                                   double* __restrict__ trace,
-                                                  long long* __restrict__ stats) {
+                                                  long long* __restrict__ stats,
+                                                  const double* __restrict__ sv) {
   __shared__ double scratch[kTernT / kWave];
   double acc = 0.0;
   for (int64_t r = threadIdx.x; r < m; r += kTernT) acc += (double)code_at(u_codes, r) * (double)x[r];
   const double c = block_sum<kTernT>(acc, scratch);
   if (threadIdx.x == 0) {
-    const double den = (double)(*nnz_u) * (double)(*nnz_v);
-    const double d = c / den;
+    const double den = (double)(*nnz_u) * (sv ? *sv : (double)(*nnz_v));
+    const double d = den > 0.0 ? c / den : 0.0;
     D[i] = (float)d;
-    const double t = trace_state[0] - c * c / den;
+    const double t = trace_state[0] - (den > 0.0 ? c * c / den : 0.0);
     trace_state[0] = t;
     if (trace) trace[i] = t;
     if (stats) {
@@ -213,16 +233,26 @@ constexpr int kNormT = 256;
 __global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restrict__ A, int64_t total,
                                                           int64_t per_block,
                                                           double* __restrict__ partial,
-                                                          long long* __restrict__ nonfinite) {
+                                                          long long* __restrict__ nonfinite,
+                                                          const float* __restrict__ wt, int64_t ncols) {
+  // with column weights wt (ncols columns): sum_j wt_j A_ij^2 (§2.5)
   __shared__ double scratch[kNormT / kWave];
   const int64_t b0 = (int64_t)blockIdx.x * per_block;
   const int64_t b1 = min(total, b0 + per_block);
   double acc = 0.0;
   long long bad = 0;
-  for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
-    const float v = A[j];
-    if (!isfinite(v)) ++bad;
-    acc += (double)v * (double)v;
+  if (wt) {
+    for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
+      const float v = A[j];
+      if (!isfinite(v)) ++bad;
+      acc += (double)v * (double)v * (double)wt[j % ncols];
+    }
+  } else {
+    for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
+      const float v = A[j];
+      if (!isfinite(v)) ++bad;
+      acc += (double)v * (double)v;
+    }
   }
   const double s = block_sum<kNormT>(acc, scratch);
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
@@ -230,6 +260,26 @@ __global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restric
     const long long b = block_sum<kNormT>(bad, reinterpret_cast<long long*>(scratch));
     if (threadIdx.x == 0 && b) atomicAdd(reinterpret_cast<unsigned long long*>(nonfinite), (unsigned long long)b);
   }
+}
+
+// Column weights from per-input-channel second moments (§2.5): one workgroup
+// takes M = max(h), then wt_j = fl32(h_j / M) + lambda (wt = lambda if M = 0).
+// Negative or non-finite entries of h are counted into *nonfinite.
+__global__ __launch_bounds__(kTernT) void k_importance_weights(const float* __restrict__ h, int64_t n,
+                                                               float lambda, float* __restrict__ wt,
+                                                               long long* __restrict__ nonfinite) {
+  __shared__ double scratch[kTernT / kWave];
+  float mx = 0.f;
+  long long bad = 0;
+  for (int64_t j = threadIdx.x; j < n; j += kTernT) {
+    const float v = h[j];
+    if (!isfinite(v) || v < 0.f) ++bad;
+    else mx = fmaxf(mx, v);
+  }
+  const float M = block_max<kTernT>(mx, reinterpret_cast<float*>(scratch));
+  for (int64_t j = threadIdx.x; j < n; j += kTernT) wt[j] = (M > 0.f ? h[j] / M : 0.f) + lambda;
+  const long long b = block_sum<kTernT>(bad, reinterpret_cast<long long*>(scratch));
+  if (threadIdx.x == 0 && b) atomicAdd(reinterpret_cast<unsigned long long*>(nonfinite), (unsigned long long)b);
 }
 
 __global__ void k_sum_partials(const double* __restrict__ partial, int64_t count,
@@ -311,8 +361,14 @@ hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t
 }
 
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
-                            long long* fallbacks, hipStream_t s) {
-  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks);
+                            long long* fallbacks, hipStream_t s, const float* wt, double* wsum) {
+  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum);
+  return hipGetLastError();
+}
+
+hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, float* wt,
+                                     long long* nonfinite, hipStream_t s) {
+  hipLaunchKernelGGL(k_importance_weights, dim3(1), dim3(kTernT), 0, s, h, n, lambda, wt, nonfinite);
   return hipGetLastError();
 }
 
@@ -331,10 +387,10 @@ hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes
 }
 
 hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
-                         hipStream_t s) {
+                         hipStream_t s, const float* wt) {
   const unsigned rows_per_block = kGnT / kWave;
   dim3 grid((unsigned)((m + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL(k_gemv_n, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x);
+  hipLaunchKernelGGL(k_gemv_n, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x, wt);
   return hipGetLastError();
 }
 
@@ -347,12 +403,14 @@ hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_code
 }
 
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
-                        double* out, long long* nonfinite, hipStream_t s) {
+                        double* out, long long* nonfinite, hipStream_t s, const float* wt,
+                        int64_t ncols) {
   int64_t blocks = std::min<int64_t>(partial_cap, std::max<int64_t>(1, (total + 65535) / 65536));
   const int64_t per_block = (total + blocks - 1) / blocks;
   if (total == 0) blocks = 1;
+  if (wt && ncols < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_norm2_partial, dim3((unsigned)blocks), dim3(kNormT), 0, s, A, total,
-                     std::max<int64_t>(per_block, 1), partial, nonfinite);
+                     std::max<int64_t>(per_block, 1), partial, nonfinite, wt, ncols);
   hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(64), 0, s, partial, blocks, out);
   return hipGetLastError();
 }
@@ -390,7 +448,8 @@ size_t stream_workspace_bytes(int64_t m, int64_t n) {
   b += sizeof(double) * 8;                       // a2, r2, trace state
   b += sizeof(int32_t) * 8;                      // nnz counters
   b += sizeof(long long) * EXTERND_STATS_LEN;    // local stats
-  b += 64 * 8;                                   // alignment slack
+  b += sizeof(float) * (size_t)n + sizeof(double) * 8;   // column weights, v^T diag(wt) v
+  b += 64 * 10;                                  // alignment slack
   return b;
 }
 
@@ -416,10 +475,16 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   int32_t* nnz_v = nnz_u + 1;
   p = align_up(p + sizeof(int32_t) * 8, 256);
   long long* st = reinterpret_cast<long long*>(p);
+  p = align_up(p + sizeof(long long) * EXTERND_STATS_LEN, 256);
+  float* wt = a.importance ? reinterpret_cast<float*>(p) : nullptr;   // column weights (§2.5)
+  p = align_up(p + sizeof(float) * n, 256);
+  double* sv = a.importance ? reinterpret_cast<double*>(p) : nullptr;  // v^T diag(wt) v
 
   hipError_t e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
-  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess) return e;
+  if (wt && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
+    return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_set_f64, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
@@ -447,9 +512,9 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
                         fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s);
       if (e != hipSuccess) return e;
       pending = false;
-      if ((e = launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s)) != hipSuccess) return e;
+      if ((e = launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_V, nnz_v);
-      if ((e = launch_gemv_n(R, m, n, vc, x, s)) != hipSuccess) return e;
+      if ((e = launch_gemv_n(R, m, n, vc, x, s, wt)) != hipSuccess) return e;
       if ((e = launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_U, nnz_u);
       if (cap) {
@@ -460,7 +525,7 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
       }
     }
     hipLaunchKernelGGL(k_scale, dim3(1), dim3(kTernT), 0, s, x, m, ub, nnz_u, nnz_v, a.D, i, tstate,
-                       a.trace, st);
+                       a.trace, st, (const double*)sv);
     pending = true;
     if (cap && a.capture_d && (e = launch_copy_f32(a.D + i, a.capture_d, 1, s)) != hipSuccess) return e;
     if (cap && a.capture_R_next) {
@@ -474,7 +539,7 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   if (pending) {
     if ((e = launch_deflate(R, m, n, a.B2 + (k - 1) * wm, a.C2 + (k - 1) * wn, a.D + k - 1, s)) != hipSuccess) return e;
   }
-  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s, wt, n)) != hipSuccess) return e;
   if ((e = launch_energy_finish(a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, s)) != hipSuccess) return e;
   if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   if (a.stats) {

@@ -163,14 +163,16 @@ def test_rank_for_energy_matches_oracle(clib):
         trw.rank_for_energy([1.0], 1, 1, 1.0, float("nan"))
 
 
-def test_decompose_rejects_bad_sweeps(clib):
+def test_decompose_rejects_bad_sweeps_and_lambda(clib):
     import ternary_rank_weight_amd as trw
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    for sweeps, block in ((1, 0), (1, 1), (-1, 8)):
+    for sweeps, block, lam in ((1, 0, 0.0), (1, 1, 0.0), (-1, 8, 0.0), (0, 8, -1.0), (0, 0, float("nan")),
+                               (0, 0, float("inf"))):
         o = trw._Opts()
         o.struct_size = ctypes.sizeof(trw._Opts)
         o.mode = -1
         o.capture_component = -1
         o.sweeps = sweeps
+        o.importance_lambda = lam
         st = trw._decompose(fake, 64, 64, 1.0, 0.7, 15, block, None, fake, fake, fake, fake, ctypes.byref(o))
-        assert st == 1, (sweeps, block)
+        assert st == 1, (sweeps, block, lam)
