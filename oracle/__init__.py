@@ -22,7 +22,8 @@ pages print no worked example for them; the oracle's own result is the
 reference) and the two free choices the pages leave open, the starting vector
 rule and the ridge eps.
 """
-from .ternarize import mean_abs_threshold, ternarize, ternarize_columns, optimal_projection
+from .ternarize import (mean_abs_threshold, ternarize, ternarize_columns, optimal_projection,
+                        project_columns)
 from .init_rule import splitmix64_mix, init_hash, init_signs, init_block
 from .als import (rank_for, block_width, ridge, decompose_seq, decompose_block, rank1_fit,
                   rank_for_energy, importance_weights, weighted_norm2, block_u_target,
@@ -31,7 +32,7 @@ from .factors import (reconstruct, apply_factors, energy_from_factors, pack2, un
                       zero_fraction, bpw_eff, bpw_packed2)
 
 __all__ = [
-    "mean_abs_threshold", "ternarize", "ternarize_columns", "optimal_projection",
+    "mean_abs_threshold", "ternarize", "ternarize_columns", "optimal_projection", "project_columns",
     "splitmix64_mix", "init_hash", "init_signs", "init_block",
     "rank_for", "block_width", "ridge", "decompose_seq", "decompose_block", "rank1_fit",
     "rank_for_energy", "importance_weights", "weighted_norm2", "block_u_target",

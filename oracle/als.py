@@ -35,7 +35,16 @@ import math
 import numpy as np
 
 from .init_rule import init_signs, init_block
-from .ternarize import ternarize, ternarize_columns
+from .ternarize import ternarize, ternarize_columns, optimal_projection, project_columns
+
+
+def _tern(x, tau, projection):
+    """The ternarizer of one vector: T_tau, or the optimal projection (§2.2)."""
+    return optimal_projection(x)[0] if projection else ternarize(x, tau)
+
+
+def _tern_cols(X, tau, projection):
+    return project_columns(X) if projection else ternarize_columns(X, tau)
 
 __all__ = ["rank_for", "block_width", "ridge", "decompose_seq", "decompose_block",
            "rank1_fit", "SeqResult", "rank_for_energy", "importance_weights", "weighted_norm2",
@@ -99,7 +108,7 @@ def weighted_norm2(R, w):
     return float(np.sum(R * R)) if w is None else float(np.sum((R * R) @ w))
 
 
-def rank1_fit(R, u0, tau, iters, w=None):
+def rank1_fit(R, u0, tau, iters, w=None, projection=False):
     """Alternating ternary fit of one component against residual R (§2.3 steps 1-2).
 
     w: optional column weights h~ (§2.5).  The v update keeps the plain
@@ -117,9 +126,9 @@ def rank1_fit(R, u0, tau, iters, w=None):
     v = None
     for _ in range(iters):
         y = R.T @ u
-        v = ternarize(y, tau).astype(np.float64)
+        v = _tern(y, tau, projection).astype(np.float64)
         x = R @ v if w is None else R @ (w * v)
-        u_new = ternarize(x, tau).astype(np.float64)
+        u_new = _tern(x, tau, projection).astype(np.float64)
         hist.append((y, v.copy(), x, u_new.copy()))
         u = u_new
     nu = float(np.count_nonzero(u))
@@ -131,13 +140,15 @@ def rank1_fit(R, u0, tau, iters, w=None):
             "nnz_u": int(nu), "nnz_v": int(nv), "sv": sv, "hist": hist}
 
 
-def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=None):
+def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=None, projection=False):
     """Greedy sequential ALS (§2.3).  Returns SeqResult.
 
     record: optional set of component indices whose rank1_fit history and
     pre-deflation residual are kept in result.extra["records"].
     weights: optional column weights h~ (importance_weights, §2.5); the
     trace, norm_a2 and E are then the weighted ones.
+    projection: ternarize with the optimal ternary projection instead of
+    T_tau (§2.2; tau is then unused).
     """
     w = None if weights is None else np.asarray(weights, dtype=np.float64)
     A = np.asarray(A)
@@ -157,7 +168,7 @@ def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=Non
         u0 = init_signs(seed, i, m)
         if record is not None and i in record:
             records[i] = {"R": R.copy()}
-        fit = rank1_fit(R, u0, tau, iters, w)
+        fit = rank1_fit(R, u0, tau, iters, w, projection)
         u = fit["u"].astype(np.float64)
         v = fit["v"].astype(np.float64)
         d = fit["d"]
@@ -201,15 +212,15 @@ def block_u_target(R, V, w=None):
     return _cholesky_solve(GV, Q.T, ridge(GV)).T, Q
 
 
-def _fit_block(R, U, tau, iters, w=None):
+def _fit_block(R, U, tau, iters, w=None, projection=False):
     """The alternating block iterations of §2.4 from the starting block U.
     Returns (U, V, Q) with Q = R diag(w) V from the last iteration."""
     V = None
     Q = None
     for _ in range(iters):
-        V = ternarize_columns(block_v_target(R, U), tau).astype(np.float64)
+        V = _tern_cols(block_v_target(R, U), tau, projection).astype(np.float64)
         T, Q = block_u_target(R, V, w)
-        U = ternarize_columns(T, tau).astype(np.float64)
+        U = _tern_cols(T, tau, projection).astype(np.float64)
     return U, V, Q
 
 
@@ -226,7 +237,7 @@ def _joint_scales(U, V, Q, w=None):
 
 
 def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width=None, sweeps=0,
-                    weights=None):
+                    weights=None, projection=False):
     """Batched block ALS with decorrelated targets (§2.4).  Returns SeqResult.
 
     Each iteration:  P = R^T U;  V <- T_col( P (U^T U + eps I)^-1 );
@@ -249,6 +260,8 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     weights: optional column weights h~ (importance_weights, §2.5): the U
     update and the joint solve use R diag(w) and V^T diag(w) V, the V update
     keeps the plain R; trace, norm_a2 and E are the weighted ones.
+
+    projection: ternarize with the optimal ternary projection (§2.2).
     """
     w = None if weights is None else np.asarray(weights, dtype=np.float64)
     A = np.asarray(A)
@@ -259,7 +272,7 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     if b == 1 and force_width is None:
         if sweeps:
             raise ValueError("refinement sweeps need block mode (b >= 2)")
-        res = decompose_seq(A, mu, tau, iters, seed, k, weights=w)
+        res = decompose_seq(A, mu, tau, iters, seed, k, weights=w, projection=projection)
         res.extra["b"] = 1
         return res
     R = A.astype(np.float64, copy=True)
@@ -274,7 +287,7 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     for blk in range(nblocks):
         c0 = blk * b
         bb = min(b, k - c0)
-        U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters, w)
+        U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters, w, projection)
         d, rhs, retried = _joint_scales(U, V, Q, w)
         ridge_retries += int(retried)
         R -= (U * d) @ V.T
@@ -293,7 +306,7 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
             Uo = B[:, c0:c0 + bb].astype(np.float64)
             Vo = C[c0:c0 + bb, :].T.astype(np.float64)
             Rp = R + (Uo * D[c0:c0 + bb]) @ Vo.T
-            U, V, Q = _fit_block(Rp, Uo, tau, iters, w)
+            U, V, Q = _fit_block(Rp, Uo, tau, iters, w, projection)
             d, _, retried = _joint_scales(U, V, Q, w)
             ridge_retries += int(retried)
             Rn = Rp - (U * d) @ V.T

@@ -32,7 +32,8 @@ import math
 
 import numpy as np
 
-__all__ = ["mean_abs_threshold", "ternarize", "ternarize_columns", "optimal_projection"]
+__all__ = ["mean_abs_threshold", "ternarize", "ternarize_columns", "optimal_projection",
+           "project_columns"]
 
 
 def _ceil_log2(n):
@@ -92,24 +93,56 @@ def ternarize_columns(X, tau):
     return out
 
 
+def _fixed_point_magnitudes(a):
+    """q_j = floor(|x_j| * 2**s) with the shift of mean_abs_threshold (exact
+    integers, every partial sum below 2**52)."""
+    big = float(a.max())
+    _, e = math.frexp(big)
+    s = 52 - e - _ceil_log2(a.size)
+    return np.floor(np.ldexp(a, s)).astype(np.int64)
+
+
 def optimal_projection(x):
     """Closed-form argmin over ternary t and real alpha of ||x - alpha t||_2.
 
     Page §2.2: sort |x| in decreasing order and keep the prefix of length s
     that maximises (1/sqrt(s)) * (sum of the s largest |x|).  Returns
-    (t, alpha) with t in {-1,0,1}^N and alpha the least-squares scale
-    (the mean of the kept |x|).  Ties in the prefix score keep the shortest
-    prefix; entries of equal |x| are taken in index order.
+    (t, alpha) with t in {-1,0,1}^N and alpha the least-squares scale (the
+    mean of the kept |x|).
+
+    Readings (so that two implementations agree bit for bit): the order is
+    that of |x| with equal values taken in index order; the prefix sums are
+    those of the fixed-point magnitudes q_j of mean_abs_threshold (exact
+    integers), and prefixes s and r are compared exactly as Q_s^2 r against
+    Q_r^2 s, the shortest prefix winning a tie.  This chooses the optimum of
+    the magnitudes truncated to about 2**-37 relative.  x identically zero
+    gives +1 at index 0 (as for T_tau).
     """
     xv = np.asarray(x, dtype=np.float64)
     a = np.abs(xv)
-    order = np.argsort(-a, kind="stable")
-    csum = np.cumsum(a[order])
-    sizes = np.arange(1, a.size + 1, dtype=np.float64)
-    score = csum / np.sqrt(sizes)
-    s = int(np.argmax(score)) + 1
     t = np.zeros(a.size, dtype=np.int8)
-    sel = order[:s]
+    if a.size == 0:
+        raise ValueError("empty vector")
+    if float(a.max()) == 0.0:
+        t[0] = 1
+        return t, 0.0
+    order = np.argsort(-a, kind="stable")
+    q = _fixed_point_magnitudes(a)[order]
+    best, best_q, run = 1, int(q[0]), int(q[0])
+    for size in range(2, a.size + 1):
+        run += int(q[size - 1])
+        if run * run * best > best_q * best_q * size:
+            best, best_q = size, run
+    sel = order[:best]
     t[sel] = np.where(xv[sel] > 0, 1, np.where(xv[sel] < 0, -1, 0)).astype(np.int8)
-    alpha = float(csum[s - 1] / s)
+    alpha = float(np.sum(a[sel]) / best)
     return t, alpha
+
+
+def project_columns(X):
+    """Optimal ternary projection of every column of X (block ALS variant)."""
+    X = np.asarray(X, dtype=np.float64)
+    out = np.empty(X.shape, dtype=np.int8)
+    for j in range(X.shape[1]):
+        out[:, j] = optimal_projection(X[:, j])[0]
+    return out

@@ -131,3 +131,48 @@ def test_threshold_ties_optimal_projection_on_gaussians():
     assert copt == pytest.approx(cap(t_opt), abs=0.003)
     assert copt >= c07
     assert c07 / copt > 0.995
+
+
+def test_optimal_projection_is_global_not_first_peak():
+    # the prefix score S_s / sqrt(s) is not unimodal: with one large entry and
+    # many equal smaller ones it dips at s = 2 and then rises past s = 1
+    x = np.array([1.0] + [0.3] * 40)
+    score = np.cumsum(np.abs(x)) / np.sqrt(np.arange(1, x.size + 1))
+    assert score[1] < score[0] < score[-1]
+    t, alpha = oracle.optimal_projection(x)
+    assert np.count_nonzero(t) == x.size
+    assert alpha == pytest.approx(np.mean(np.abs(x)))
+
+
+def test_optimal_projection_ties_and_degenerate_inputs():
+    t, a = oracle.optimal_projection(np.zeros(5))
+    assert list(t) == [1, 0, 0, 0, 0] and a == 0.0
+    # within a run of equal magnitudes the score is quasi-convex in s, so a
+    # run is kept whole or not at all: here the run wins (1, 1.34, 1.62,
+    # 1.85, 1.65), there the single large entry does (2, 1.77, 1.73, 1.75)
+    t, _ = oracle.optimal_projection(np.array([-0.9, 1.0, 0.9, -0.9, 0.0]))
+    assert list(t) == [-1, 1, 1, -1, 0]
+    t, _ = oracle.optimal_projection(np.array([-0.5, 2.0, 0.5, -0.5]))
+    assert list(t) == [0, 1, 0, 0]
+    # among entries of equal magnitude the order is by index
+    t, _ = oracle.optimal_projection(np.array([0.1, 0.1, 3.0, 0.1]))
+    assert list(t) == [0, 0, 1, 0]
+    t, _ = oracle.optimal_projection(np.array([-2.0]))
+    assert list(t) == [-1]
+
+
+def test_projection_decompositions_match_the_threshold_form():
+    # §2.2: the optimal projection empirically ties T_0.7, and each greedy
+    # step still never raises ||R||^2
+    rng = np.random.default_rng(3)
+    A = (0.02 * rng.standard_normal((48, 40))).astype(np.float32)
+    for block in (0, 5):
+        if block:
+            rp = oracle.decompose_block(A, 1.0, 0.7, block=block, seed=1, projection=True)
+            rt = oracle.decompose_block(A, 1.0, 0.7, block=block, seed=1)
+        else:
+            rp = oracle.decompose_seq(A, 1.0, 0.7, seed=1, projection=True)
+            rt = oracle.decompose_seq(A, 1.0, 0.7, seed=1)
+        assert np.all(np.diff(rp.trace) <= 1e-12 * rp.norm_a2)
+        assert abs(rp.E - rt.E) < 0.02
+        assert rp.E == pytest.approx(oracle.energy_from_factors(A, rp.B, rp.C, rp.D), abs=1e-12)
