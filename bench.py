@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-importance", dest="importance", action="store_false",
                     help="skip the importance-weighted runs")
+    ap.add_argument("--no-projection", dest="projection", action="store_false",
+                    help="skip the block run with the optimal ternary projection")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2])
@@ -189,6 +191,21 @@ def measure_importance(trw, Ad, c, block, modes, sigma=1.5):
             "modes": out}
 
 
+def measure_projection(trw, Ad, c, block):
+    """Block ALS with the optimal ternary projection (§2.2) in place of T_tau
+    on the same matrix: one run between HIP events, and its energy."""
+    import torch
+    trw.decompose(Ad, c["mu"], c["tau"], c["iters"], block, c["seed"], projection=True)   # warm
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    r = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], block, c["seed"], projection=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"mode": f"block ALS b={trw.block_width(Ad.shape[0], Ad.shape[1], block)}",
+            "ms": round(e0.elapsed_time(e1), 3), "energy": round(float(r.energy.item()), 6)}
+
+
 def cpu_baseline(A, c, sample):
     import numpy as np
     import oracle
@@ -292,6 +309,10 @@ def main():
     if args.importance:
         print("[bench] importance", file=sys.stderr, flush=True)
         importance = measure_importance(trw, Ad, c, block, modes)
+    projection = None
+    if "block" in per_mode and args.projection:
+        print("[bench] projection", file=sys.stderr, flush=True)
+        projection = measure_projection(trw, Ad, c, block)
     sweeps = None
     if "block" in per_mode and args.sweeps > 0:
         print("[bench] sweeps", file=sys.stderr, flush=True)
@@ -328,6 +349,7 @@ def main():
         "inference": inference,
         "sweeps": sweeps,
         "importance_weighted": importance,
+        "optimal_projection": projection,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

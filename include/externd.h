@@ -53,6 +53,8 @@ enum externd_mode {
   EXTERND_MODE_RESIDENT = 1    /* one cooperative kernel, R kept in LDS/VGPRs */
 };
 
+enum externd_ternarizer { EXTERND_TERN_MEAN = 0, EXTERND_TERN_PROJECTION = 1 };
+
 /* Indices into the optional int64 statistics array (EXTERND_STATS_LEN entries). */
 enum externd_stat {
   EXTERND_STAT_SUM_NNZ_U = 0,   /* sum over components and iterations of nnz(u_t) */
@@ -114,7 +116,13 @@ typedef struct externd_opts {
    * The energy therefore never falls from sweep to sweep (up to the fp32
    * rounding of the deflations). */
   int32_t sweeps;         /* default 0 */
-  int32_t reserved2;
+  /* Ternarizer (§2.2): EXTERND_TERN_MEAN (default) is T_tau; with
+   * EXTERND_TERN_PROJECTION every ternarization is the optimal ternary
+   * projection (keep the s largest |x| maximising their sum over sqrt(s);
+   * tau is unused).  The projection runs in streaming and block mode only
+   * (AUTO picks streaming) and needs m, n <= 16384; otherwise
+   * EXTERND_EUNSUPPORTED. */
+  int32_t ternarizer;
   double* sweep_trace;    /* device, optional: sweeps entries, predicted ||R||^2 after each sweep */
   /* Importance-weighted ALS (§2.5, every mode).  importance: device, n
    * per-input-channel second moments h >= 0 (e.g. from an importance matrix);
@@ -205,6 +213,13 @@ uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, 
  * be NULL) receives the number of nonzeros. */
 int externd_ternarize(const float* x, int64_t N, float tau, void* stream,
                       uint32_t* codes, int32_t* nnz);
+
+/* codes = the optimal ternary projection of a length-N fp32 vector (§2.2):
+ * the s largest |x_j| keep their signs, s maximising their sum over sqrt(s);
+ * the sort takes equal magnitudes in index order, and prefixes are compared
+ * exactly on the fixed-point magnitudes of T_tau's mean.  1 <= N <= 16384
+ * (EXTERND_EUNSUPPORTED above).  nnz as for externd_ternarize. */
+int externd_project(const float* x, int64_t N, void* stream, uint32_t* codes, int32_t* nnz);
 
 /* y = R^T u for R (m x n) and u given as 2-bit codes of length m (§2.3 step 1). */
 int externd_gemv_t(const float* R, int64_t m, int64_t n, const uint32_t* u_codes,

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "decompose", "energy", "reconstruct", "apply", "rank", "block_width", "resident_fits", "workspace_bytes",
-    "rank_for_energy", "mu_for_energy",
+    "rank_for_energy", "mu_for_energy", "project",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
     "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
 ]
@@ -51,7 +51,7 @@ class _Opts(ctypes.Structure):
         ("capture_d", _p),
         ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
         ("norm_a2", _p),
-        ("sweeps", _i32), ("reserved2", _i32), ("sweep_trace", _p),
+        ("sweeps", _i32), ("ternarizer", _i32), ("sweep_trace", _p),
         ("importance", _p), ("importance_lambda", ctypes.c_float), ("reserved3", _i32),
     ]
 
@@ -75,6 +75,7 @@ _workspace_bytes = _sig("externd_workspace_bytes", ctypes.c_uint64, [_i64, _i64,
 _rank_for_energy = _sig("externd_rank_for_energy", ctypes.c_int64,
                         [ctypes.POINTER(ctypes.c_double), _i64, _i64, _i32, ctypes.c_double, ctypes.c_double])
 _ternarize = _sig("externd_ternarize", ctypes.c_int, [_p, _i64, _f32, _p, _p, _p])
+_project = _sig("externd_project", ctypes.c_int, [_p, _i64, _p, _p, _p])
 _gemv_t = _sig("externd_gemv_t", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
 _gemv_n = _sig("externd_gemv_n", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
 _deflate = _sig("externd_deflate", ctypes.c_int, [_p, _i64, _i64, _p, _p, _f32, _p])
@@ -86,7 +87,7 @@ ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "ex
                "externd_rank",
                "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
                "externd_rank_for_energy",
-               "externd_ternarize",
+               "externd_ternarize", "externd_project",
                "externd_gemv_t", "externd_gemv_n", "externd_deflate",
                "externd_status_string", "externd_last_error")
 
@@ -158,7 +159,8 @@ class Decomposition:
 
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
-              capture=None, out=None, workspace=None, sweeps=0, importance=None, lam=0.0):
+              capture=None, out=None, workspace=None, sweeps=0, importance=None, lam=0.0,
+              projection=False):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
@@ -172,6 +174,8 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     importance: optional (n,) float32 CUDA tensor of per-input-channel second
     moments h; the column weights are h / max(h) + lam (importance-weighted
     ALS), and energy / trace / norm_a2 become weighted.
+    projection: use the optimal ternary projection instead of T_tau
+    (streaming or block mode; AUTO picks streaming).
     """
     _need(A, torch.float32, "A")
     if A.dim() != 2:
@@ -209,6 +213,7 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
             raise ValueError("importance must have n entries")
         opts.importance = _ptr(importance)
     opts.importance_lambda = float(lam)
+    opts.ternarizer = 1 if projection else 0
     opts.capture_component = -1
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
@@ -308,6 +313,16 @@ def ternarize(x, tau):
     codes = torch.empty(((N + 15) // 16,), dtype=torch.int32, device=x.device)
     nnz = torch.empty((1,), dtype=torch.int32, device=x.device)
     _check(_ternarize(_ptr(x), N, tau, _stream(), _ptr(codes), _ptr(nnz)))
+    return codes, nnz
+
+
+def project(x):
+    """Optimal ternary projection of a float32 vector (§2.2) -> (codes, nnz)."""
+    _need(x, torch.float32, "x")
+    N = x.numel()
+    codes = torch.empty(((N + 15) // 16,), dtype=torch.int32, device=x.device)
+    nnz = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _check(_project(_ptr(x), N, _stream(), _ptr(codes), _ptr(nnz)))
     return codes, nnz
 
 

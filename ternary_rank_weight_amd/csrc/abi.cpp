@@ -210,6 +210,14 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   if (o.sweeps < 0) return fail(EXTERND_EINVAL, "sweeps must be >= 0");
   if (!std::isfinite(o.importance_lambda) || o.importance_lambda < 0.f)
     return fail(EXTERND_EINVAL, "importance_lambda must be finite and >= 0");
+  if (o.ternarizer != EXTERND_TERN_MEAN && o.ternarizer != EXTERND_TERN_PROJECTION)
+    return fail(EXTERND_EINVAL, "bad ternarizer %d", o.ternarizer);
+  const bool projection = o.ternarizer == EXTERND_TERN_PROJECTION;
+  if (projection && (m > externd::kProjMaxN || n > externd::kProjMaxN))
+    return fail(EXTERND_EUNSUPPORTED, "the optimal projection takes vectors of at most %d entries",
+                externd::kProjMaxN);
+  if (projection && o.mode == EXTERND_MODE_RESIDENT)
+    return fail(EXTERND_EUNSUPPORTED, "the optimal projection runs in streaming or block mode");
   if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
     return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
   const int b = externd_block_width(m, n, block);
@@ -241,6 +249,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.sweep_trace = o.sweep_trace;
     ba.importance = o.importance;
     ba.lambda = o.importance_lambda;
+    ba.projection = projection ? 1 : 0;
     Workspace w;
     if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);
@@ -265,6 +274,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   sa.norm_a2 = o.norm_a2;
   sa.importance = o.importance;
   sa.lambda = o.importance_lambda;
+  sa.projection = projection ? 1 : 0;
   sa.capture_component = o.capture_component;
   if (o.capture_component >= 0) {
     if (o.capture_component >= k) return fail(EXTERND_EINVAL, "capture_component >= k");
@@ -281,7 +291,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   }
   const bool fits = externd::resident_fits(m, n, cus);
   int mode = o.mode;
-  if (mode == EXTERND_MODE_AUTO) mode = fits ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
+  if (mode == EXTERND_MODE_AUTO) mode = (fits && !projection) ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
   if (mode == EXTERND_MODE_RESIDENT && !fits)
     return fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel", (long long)m,
                 (long long)n);
@@ -336,6 +346,18 @@ int externd_ternarize(const float* x, int64_t N, float tau, void* stream, uint32
   if (st != EXTERND_OK) return st;
   hipError_t e = externd::launch_ternarize(x, N, tau, codes, nnz, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ternarize");
+  return EXTERND_OK;
+}
+
+int externd_project(const float* x, int64_t N, void* stream, uint32_t* codes, int32_t* nnz) {
+  if (!x || !codes) return fail(EXTERND_EINVAL, "null pointer");
+  if (N <= 0) return fail(EXTERND_EINVAL, "bad length");
+  if (N > externd::kProjMaxN)
+    return fail(EXTERND_EUNSUPPORTED, "the optimal projection takes at most %d entries", externd::kProjMaxN);
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipError_t e = externd::launch_project(x, N, codes, nnz, nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "project");
   return EXTERND_OK;
 }
 

@@ -14,6 +14,7 @@
 // 2-bit codes directly in their B2 / C2 output rows.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "projection.hpp"
 
 namespace externd {
 
@@ -856,6 +857,67 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// The optimal ternary projection (§2.2) of every row of Xt, the alternative
+// to T_tau; outputs as for k_row_ternarize.
+// ---------------------------------------------------------------------------
+template <int PMAX>
+__global__ __launch_bounds__(kTT) void k_row_project(const float* __restrict__ Xt, int64_t L,
+                                                     uint32_t* __restrict__ out_codes, int64_t wl,
+                                                     int* __restrict__ nnz, long long* __restrict__ fb,
+                                                     long long* __restrict__ nnz_sum,
+                                                     const float* __restrict__ Qrows,
+                                                     double* __restrict__ rhs_out) {
+  __shared__ uint64_t keys[PMAX];
+  __shared__ ProjScratch sc;
+  __shared__ double scratch[kTT / kWave];
+  const int i = blockIdx.x;
+  const float* x = Xt + (int64_t)i * L;
+  const float* qr = rhs_out ? Qrows + (int64_t)i * L : nullptr;
+  uint32_t* codes = out_codes + (int64_t)i * wl;
+  const int t = threadIdx.x;
+  float mx = 0.f;
+  for (int64_t j = t; j < L; j += kTT) mx = fmaxf(mx, fabsf(x[j]));
+  const float M = block_max<kTT>(mx, reinterpret_cast<float*>(scratch));
+  if (M == 0.f) {
+    for (int64_t w = t; w < wl; w += kTT) codes[w] = (w == 0) ? 1u : 0u;
+    if (t == 0) {
+      if (rhs_out) rhs_out[i] = (double)qr[0];
+      nnz[i] = 1;
+      atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+      atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
+    }
+    return;
+  }
+  const uint64_t K = projection_threshold<kTT>(x, (int)L, M, keys, sc);
+  int cnt = 0;
+  double rq = 0.0;
+  for (int64_t w = t; w < wl; w += kTT) {
+    uint32_t word = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t j = w * 16 + e;
+      if (j < L) {
+        const float v = x[j];
+        if (proj_key(v, (int)j) >= K) {
+          word |= code_of(v) << (2 * e);
+          ++cnt;
+          if (qr) rq += v > 0.f ? (double)qr[j] : -(double)qr[j];
+        }
+      }
+    }
+    codes[w] = word;
+  }
+  const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
+  if (rhs_out) {
+    const double r = block_sum<kTT>(rq, scratch);
+    if (t == 0) rhs_out[i] = r;
+  }
+  if (t == 0) {
+    nnz[i] = total;
+    atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), (unsigned long long)total);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Joint scale solve (§2.4): rhs_j = u_j . q_j with q_j the last Q column,
 // M = (U^T U) o (V^T V), d = M^-1 rhs in fp64.  M is inverted without a
 // ridge; if it is not positive definite (a pivot is not positive, the same
@@ -1224,6 +1286,16 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   // codes; the solve keeps whichever block lowers ||R||^2 more.
   auto fit_block = [&](int bb, uint32_t* Uc, uint32_t* Vc, float* Dout, double* trace, int64_t tidx,
                        const double* dpart, const double* dold, const uint32_t* saved) {
+    // column-wise ternarizer: T_tau, or the optimal projection (§2.2)
+    auto row_tern = [&](const float* Xt, int64_t L, uint32_t* codes, int64_t wl, int* nz, long long* nz_sum,
+                        const float* Qrows, double* rhs_out) {
+      if (!a.projection)
+        hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Xt, L, a.tau, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
+      else if (L <= 4096)
+        hipLaunchKernelGGL(k_row_project<4096>, dim3(bb), dim3(kTT), 0, s, Xt, L, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
+      else
+        hipLaunchKernelGGL(k_row_project<kProjMaxN>, dim3(bb), dim3(kTT), 0, s, Xt, L, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
+    };
     const int nt = (bb + 15) / 16;
     const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + kGramSplit - 1) / kGramSplit));
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
@@ -1240,7 +1312,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Vt, n, a.tau, Vc, wn, nnz + b, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
+      row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V;  weighted (§2.5):
       // Q = R diag(wt) V and the Gram V^T diag(wt) V
       const dim3 cgrid2((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2);
@@ -1263,7 +1335,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         }
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
-      hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Ut, m, a.tau, Uc, wm, nnz, st + EXTERND_STAT_FALLBACKS, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
+      row_tern(Ut, m, Uc, wm, nnz, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
     }
     // joint scales from the final U, V and the last Q = R V (weighted: the
     // last V-side Gram GVw already belongs to the final V)

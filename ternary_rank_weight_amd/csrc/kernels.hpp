@@ -34,6 +34,7 @@ struct SeqArgs {
   double* norm_a2;   // optional output: ||A||^2
   const float* importance;   // optional: n per-input-channel second moments h (§2.5)
   float lambda;              // column weights h / max(h) + lambda
+  int projection;            // 1: optimal ternary projection instead of T_tau (§2.2)
 };
 
 // Arguments of one block-mode decomposition.
@@ -55,6 +56,7 @@ struct BlockArgs {
   double* sweep_trace; // optional output: predicted ||R||^2 after each sweep
   const float* importance;   // optional: n per-input-channel second moments h (§2.5)
   float lambda;              // column weights h / max(h) + lambda
+  int projection;            // 1: optimal ternary projection instead of T_tau (§2.2)
 };
 
 // streaming sequential path and single-step kernels (seq_stream.hip)
@@ -64,6 +66,10 @@ int64_t gemv_t_chunks(int64_t m);
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
                             long long* fallbacks, hipStream_t s, const float* wt = nullptr,
                             double* wsum = nullptr);
+// Optimal ternary projection of one vector (§2.2), 1 <= N <= kProjMaxN.
+constexpr int kProjMaxN = 16384;   // longest vector it takes (128 KB of sort keys in LDS)
+hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
+                          hipStream_t s, const float* wt = nullptr, double* wsum = nullptr);
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
                          const uint32_t* vprev, hipStream_t s);

@@ -6,6 +6,7 @@
 // R <- R - d u v^T.  T_tau is the mean-threshold ternarizer of §2.2.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "projection.hpp"
 
 namespace externd {
 
@@ -83,6 +84,59 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
     if (wsum) *wsum = (double)wt[idx];
     if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
   }
+}
+
+// ---------------------------------------------------------------------------
+// The optimal ternary projection of one vector (§2.2) by a single workgroup,
+// the alternative to T_tau: same outputs (codes, nnz, fallback count for an
+// all-zero vector, weighted support sum).  PMAX >= the padded length.
+// ---------------------------------------------------------------------------
+template <int PMAX>
+__global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x, int64_t N,
+                                                    uint32_t* __restrict__ codes, int32_t* __restrict__ nnz_out,
+                                                    long long* __restrict__ fallbacks,
+                                                    const float* __restrict__ wt, double* __restrict__ wsum) {
+  __shared__ uint64_t keys[PMAX];
+  __shared__ ProjScratch sc;
+  __shared__ double scratch[kTernT / kWave];
+  const int tid = threadIdx.x;
+  float mx = 0.f;
+  for (int64_t j = tid; j < N; j += kTernT) mx = fmaxf(mx, fabsf(x[j]));
+  const float M = block_max<kTernT>(mx, reinterpret_cast<float*>(scratch));
+  const int64_t words = (N + 15) / 16;
+  if (M == 0.f) {
+    for (int64_t w = tid; w < words; w += kTernT) codes[w] = (w == 0) ? 1u : 0u;
+    if (tid == 0) {
+      if (nnz_out) *nnz_out = 1;
+      if (wsum) *wsum = (double)wt[0];
+      if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
+    }
+    return;
+  }
+  const uint64_t K = projection_threshold<kTernT>(x, (int)N, M, keys, sc);
+  int cnt = 0;
+  double ws = 0.0;
+  for (int64_t w = tid; w < words; w += kTernT) {
+    uint32_t word = 0;
+    for (int e = 0; e < 16; ++e) {
+      const int64_t j = w * 16 + e;
+      if (j < N) {
+        const float v = x[j];
+        if (proj_key(v, (int)j) >= K) {
+          word |= code_of(v) << (2 * e);
+          ++cnt;
+          if (wsum) ws += (double)wt[j];
+        }
+      }
+    }
+    codes[w] = word;
+  }
+  const int total = block_sum<kTernT>(cnt, reinterpret_cast<int*>(scratch));
+  if (wsum) {
+    const double wt_total = block_sum<kTernT>(ws, scratch);
+    if (tid == 0) *wsum = wt_total;
+  }
+  if (tid == 0 && nnz_out) *nnz_out = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -366,6 +420,16 @@ hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* code
   return hipGetLastError();
 }
 
+hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
+                          hipStream_t s, const float* wt, double* wsum) {
+  if (N < 1 || N > kProjMaxN) return hipErrorInvalidValue;
+  if (N <= 4096)
+    hipLaunchKernelGGL(k_project<4096>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum);
+  else
+    hipLaunchKernelGGL(k_project<kProjMaxN>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum);
+  return hipGetLastError();
+}
+
 hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, float* wt,
                                      long long* nonfinite, hipStream_t s) {
   hipLaunchKernelGGL(k_importance_weights, dim3(1), dim3(kTernT), 0, s, h, n, lambda, wt, nonfinite);
@@ -512,10 +576,14 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
                         fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s);
       if (e != hipSuccess) return e;
       pending = false;
-      if ((e = launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv)) != hipSuccess) return e;
+      e = a.projection ? launch_project(y, n, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv)
+                       : launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv);
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_V, nnz_v);
       if ((e = launch_gemv_n(R, m, n, vc, x, s, wt)) != hipSuccess) return e;
-      if ((e = launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s)) != hipSuccess) return e;
+      e = a.projection ? launch_project(x, m, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s)
+                       : launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s);
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_U, nnz_u);
       if (cap) {
         if (a.capture_y && (e = launch_copy_f32(y, a.capture_y + (int64_t)t * n, n, s)) != hipSuccess) return e;

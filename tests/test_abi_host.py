@@ -176,3 +176,22 @@ def test_decompose_rejects_bad_sweeps_and_lambda(clib):
         o.importance_lambda = lam
         st = trw._decompose(fake, 64, 64, 1.0, 0.7, 15, block, None, fake, fake, fake, fake, ctypes.byref(o))
         assert st == 1, (sweeps, block, lam)
+
+
+def test_projection_option_limits(clib):
+    import ternary_rank_weight_amd as trw
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    for m, n, tern, mode, want in ((16385, 16, 1, -1, 4), (16, 16385, 1, -1, 4), (64, 64, 1, 1, 4),
+                                   (64, 64, 2, -1, 1), (64, 64, -1, -1, 1)):
+        o = trw._Opts()
+        o.struct_size = ctypes.sizeof(trw._Opts)
+        o.mode = mode
+        o.capture_component = -1
+        o.ternarizer = tern
+        st = trw._decompose(fake, m, n, 0.01, 0.7, 15, 0, None, fake, fake, fake, fake, ctypes.byref(o))
+        assert st == want, (m, n, tern, mode)
+    clib.externd_project.restype = ctypes.c_int
+    clib.externd_project.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert clib.externd_project(fake, 0, None, fake, None) == 1
+    assert clib.externd_project(fake, 16385, None, fake, None) == 4
