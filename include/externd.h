@@ -70,6 +70,8 @@ enum externd_stat {
   EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode: Gram inverses whose Newton-Schulz
                                     iteration stopped before reaching its tolerance */
   EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
+  EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode: Newton-Schulz steps over all Gram inverses */
+  EXTERND_STAT_NS_RESTARTS = 13,    /* block mode: warm starts replaced by the scaled identity */
   EXTERND_STATS_LEN = 16
 };
 

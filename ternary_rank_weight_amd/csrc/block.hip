@@ -357,178 +357,190 @@ __global__ __launch_bounds__(kCholT) void k_spd_inverse(GT* __restrict__ G, int 
 }
 
 // ---------------------------------------------------------------------------
-// Contraction 1: Pt_part[s][i][c] = sum_{r in chunk s} U[r][i] R[r][c].
-// grid (ceil(n/64), S); 4 waves, wave w owns columns c0 + 16w .. +15 and all
-// component sub-tiles.  K runs over rows in steps of 16 (4 MFMA 16x16x4);
-// lane (j + 16k) feeds row r + k + 4q at step q to both operands.
+// The two contractions.  A workgroup (4 waves) takes 64 outputs (columns of
+// R for P = U^T R, rows of R for Q = R V) and one split of the contracted
+// dimension, walked in chunks of 256: the chunk's 2-bit codes of all the
+// block's components are staged in LDS (double buffered, one barrier per
+// chunk), then 16 steps of 16 run fully unrolled, so every load of R is
+// independent and issued early.  Loads read clamped addresses and select 0
+// outside the matrix (no branches).  Each step issues NSUB x 4 MFMA
+// 16x16x4, interleaved over the NSUB component sub-tiles; ternary values are
+// decoded from the codes by two shifts (exact).  Components from bb up to
+// 16 NSUB have zero codes.
 // ---------------------------------------------------------------------------
 constexpr int kCT = 256;
+constexpr int kChunk = 256;   // rows (or columns) per staged chunk
+constexpr int kCW = kChunk / 16;   // code words per component per chunk
 
+__device__ inline float tdec(uint32_t word, int sh) { return (float)((int)(word << (30 - sh)) >> 30); }
+
+// Stage the code words [w0, w0 + kCW) of components 0 .. 16 NSUB - 1.
+template <int NSUB>
+__device__ inline void stage_codes(uint32_t (*cs)[kCW + 1], const uint32_t* __restrict__ codes, int64_t wl,
+                                   int bb, int64_t w0) {
+  constexpr int kPer = (16 * NSUB * kCW + kCT - 1) / kCT;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + kCT * p;
+    const int comp = e / kCW, w = e % kCW;
+    const bool ok = e < 16 * NSUB * kCW && comp < bb && w0 + w < wl;
+    const uint32_t x = codes[ok ? (int64_t)comp * wl + w0 + w : 0];
+    v[p] = ok ? x : 0u;
+  }
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + kCT * p;
+    if (e < 16 * NSUB * kCW) cs[e / kCW][e % kCW] = v[p];
+  }
+}
+
+// Pt_part[split][i][c] = sum over the split's rows r of U[r][i] R[r][c].
+// Wave w owns columns 64 bx + 16 w + j (j = lane % 16); lane (j + 16k) feeds
+// row 16 step + k + 4q at MFMA q of a step to both operands.
+template <int NSUB>
 __device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, int64_t m, int64_t n,
                                    const uint32_t* __restrict__ Ucodes, int64_t wm, int bb,
                                    int64_t rows_per_split, float* __restrict__ Pt_part, int bx, int by) {
+  __shared__ uint32_t cs[2][16 * NSUB][kCW + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane & 15, k = lane >> 4;
   const int64_t col = (int64_t)bx * 64 + 16 * w + j;
+  const bool colok = col < n;
+  const float* Rc = R + (colok ? col : 0);
   const int64_t r_begin = (int64_t)by * rows_per_split;
   const int64_t r_end = min(m, r_begin + rows_per_split);
-  const int nsub = (bb + 15) / 16;
-  f4 acc[kMaxB / 16];
+  f4 acc[NSUB];
 #pragma unroll
-  for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  // operands of one 16-row K step, loaded one step ahead of their use
-  auto load = [&](int64_t r, float (&bv)[4], uint32_t (&cw)[kMaxB / 16]) {
+  for (int s = 0; s < NSUB; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  int buf = 0;
+  for (int64_t cb = r_begin; cb < r_end; cb += kChunk, buf ^= 1) {
+    stage_codes<NSUB>(cs[buf], Ucodes, wm, bb, cb >> 4);
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t row = r + k + 4 * q;
-      bv[q] = (row < r_end && col < n) ? R[row * n + col] : 0.f;
-    }
-    const int64_t word = r >> 4;  // r is a multiple of 16 within the split
+    for (int st = 0; st < kCW; ++st) {
+      float bv[4];
 #pragma unroll
-    for (int s = 0; s < kMaxB / 16; ++s) {
-      const int comp = 16 * s + j;
-      cw[s] = (s < nsub && comp < bb) ? Ucodes[(int64_t)comp * wm + word] : 0u;
-    }
-  };
-  float bv[4];
-  uint32_t cw[kMaxB / 16];
-  if (r_begin < r_end) load(r_begin, bv, cw);
-  for (int64_t r = r_begin; r < r_end; r += 16) {
-    float bvn[4];
-    uint32_t cwn[kMaxB / 16];
-    const bool more = r + 16 < r_end;
-    if (more) load(r + 16, bvn, cwn);
-#pragma unroll
-    for (int s = 0; s < kMaxB / 16; ++s) {
-      if (s < nsub) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float av = value_of_code((cw[s] >> (2 * (k + 4 * q))) & 3u);
-          acc[s] = mfma16x16x4(av, bv[q], acc[s]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = cb + 16 * st + k + 4 * q;
+        const bool ok = row < r_end && colok;
+        const float x = Rc[(ok ? row : r_begin) * n];
+        bv[q] = ok ? x : 0.f;
       }
-    }
-    if (more) {
+      uint32_t cw[NSUB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bv[q] = bvn[q];
+      for (int s = 0; s < NSUB; ++s) cw[s] = cs[buf][16 * s + j][st];
 #pragma unroll
-      for (int s = 0; s < kMaxB / 16; ++s) cw[s] = cwn[s];
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x4(tdec(cw[s], 2 * (k + 4 * q)), bv[q], acc[s]);
+      }
     }
   }
-  // D[i][c]: lane holds rows i = 4*(lane/16) + v of sub-tile s, column j
+  // D[i][c]: lane holds components 16 s + 4 k + v, column j
 #pragma unroll
-  for (int s = 0; s < kMaxB / 16; ++s) {
-    if (s < nsub) {
+  for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int comp = 16 * s + 4 * k + v;
-        if (comp < bb && col < n)
-          Pt_part[((int64_t)by * bb + comp) * n + col] = acc[s][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int comp = 16 * s + 4 * k + v;
+      if (comp < bb && colok) Pt_part[((int64_t)by * bb + comp) * n + col] = acc[s][v];
     }
   }
 }
 
+template <int NSUB>
 __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__ R, int64_t m, int64_t n,
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        int bb, int64_t rows_per_split,
                                                        float* __restrict__ Pt_part) {
-  contract_ut_r_body(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y);
+  contract_ut_r_body<NSUB>(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y);
 }
 
-// ---------------------------------------------------------------------------
-// Contraction 2: Qt_part[s][i][r] = sum_{c in chunk s} R[r][c] V[c][i].
-// grid (ceil(m/64), S); wave w owns rows r0 + 16w .. +15.  K runs over
-// columns in steps of 16: lane (i + 16k) loads R[row i][c + 4k .. +3] as one
-// float4 and feeds component q at MFMA step q (column c + 4k + q); the V
-// operand of lane (comp + 16k) uses the same column.
-// ---------------------------------------------------------------------------
-// With W, the V operand is diag(wt) V (§2.5): Q = R diag(wt) V.
-template <bool W>
+// Qt_part[split][i][r] = sum over the split's columns c of R[r][c] V[c][i]
+// (with W: R[r][c] wt[c] V[c][i], §2.5).  Wave w owns rows 64 bx + 16 w + i
+// (i = lane % 16); lane (i + 16k) loads R[row][16 step + 4k .. + 3] as one
+// float4 and feeds column 4k + q at MFMA q of a step; the V operand of lane
+// (comp + 16k) uses the same column.
+template <int NSUB, bool W>
 __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, int64_t m, int64_t n,
                                   const uint32_t* __restrict__ Vcodes, int64_t wn, int bb,
                                   int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by,
                                   const float* __restrict__ wt) {
+  __shared__ uint32_t cs[2][16 * NSUB][kCW + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
   const int64_t row = (int64_t)bx * 64 + 16 * w + i;
+  const bool rowok = row < m;
+  const float* Rr = R + (rowok ? row : 0) * n;
   const int64_t c_begin = (int64_t)by * cols_per_split;
   const int64_t c_end = min(n, c_begin + cols_per_split);
-  const int nsub = (bb + 15) / 16;
   const bool vec_ok = (n % 4) == 0;
-  f4 acc[kMaxB / 16];
+  f4 acc[NSUB];
 #pragma unroll
-  for (int s = 0; s < kMaxB / 16; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int64_t c, float (&av)[4], float (&wq)[4], uint32_t (&cw)[kMaxB / 16]) {
-    const int64_t cc = c + 4 * k;
-    if (row < m && vec_ok && cc + 3 < c_end) {
-      const float4 x = *reinterpret_cast<const float4*>(R + row * n + cc);
-      av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
-    } else {
+  for (int s = 0; s < NSUB; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  int buf = 0;
+  for (int64_t cb = c_begin; cb < c_end; cb += kChunk, buf ^= 1) {
+    stage_codes<NSUB>(cs[buf], Vcodes, wn, bb, cb >> 4);
+    __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) av[q] = (row < m && cc + q < c_end) ? R[row * n + cc + q] : 0.f;
-    }
-    if constexpr (W) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wq[q] = cc + q < c_end ? wt[cc + q] : 0.f;
-    }
-    const int64_t word = c >> 4;
-#pragma unroll
-    for (int s = 0; s < kMaxB / 16; ++s) {
-      const int comp = 16 * s + i;
-      cw[s] = (s < nsub && comp < bb) ? Vcodes[(int64_t)comp * wn + word] : 0u;
-    }
-  };
-  float av[4], wq[4] = {1.f, 1.f, 1.f, 1.f};
-  uint32_t cw[kMaxB / 16];
-  if (c_begin < c_end) load(c_begin, av, wq, cw);
-  for (int64_t c = c_begin; c < c_end; c += 16) {
-    float avn[4], wqn[4];
-    uint32_t cwn[kMaxB / 16];
-    const bool more = c + 16 < c_end;
-    if (more) load(c + 16, avn, wqn, cwn);
-#pragma unroll
-    for (int s = 0; s < kMaxB / 16; ++s) {
-      if (s < nsub) {
+    for (int st = 0; st < kCW; ++st) {
+      const int64_t cc = cb + 16 * st + 4 * k;
+      float av[4], wq[4];
+      if (vec_ok && cc + 3 < c_end) {
+        const float4 x = *reinterpret_cast<const float4*>(Rr + cc);
+        av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+        if constexpr (W) {
+          const float4 y = *reinterpret_cast<const float4*>(wt + cc);
+          wq[0] = y.x; wq[1] = y.y; wq[2] = y.z; wq[3] = y.w;
+        }
+      } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float bv = value_of_code((cw[s] >> (2 * (4 * k + q))) & 3u);
+          const bool ok = cc + q < c_end;
+          const float x = Rr[ok ? cc + q : c_begin];
+          av[q] = ok ? x : 0.f;
+          if constexpr (W) {
+            const float y = wt[ok ? cc + q : c_begin];
+            wq[q] = ok ? y : 0.f;
+          }
+        }
+      }
+      if (!rowok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) av[q] = 0.f;
+      }
+      uint32_t cw[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) cw[s] = cs[buf][16 * s + i][st];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          float bv = tdec(cw[s], 2 * (4 * k + q));
           if constexpr (W) bv *= wq[q];
           acc[s] = mfma16x16x4(av[q], bv, acc[s]);
         }
       }
     }
-    if (more) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) av[q] = avn[q];
-      if constexpr (W) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wq[q] = wqn[q];
-      }
-#pragma unroll
-      for (int s = 0; s < kMaxB / 16; ++s) cw[s] = cwn[s];
-    }
   }
-  // D[row][comp]: lane holds rows 4*(lane/16)+v of the wave's 16, column comp = 16s + i
+  // D[row][comp]: lane holds rows 4 (lane / 16) + v of the wave's 16, column comp = 16 s + i
 #pragma unroll
-  for (int s = 0; s < kMaxB / 16; ++s) {
-    if (s < nsub) {
-      const int comp = 16 * s + i;
+  for (int s = 0; s < NSUB; ++s) {
+    const int comp = 16 * s + i;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t rr = (int64_t)bx * 64 + 16 * w + 4 * k + v;
-        if (comp < bb && rr < m) Qt_part[((int64_t)by * bb + comp) * m + rr] = acc[s][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int64_t rr = (int64_t)bx * 64 + 16 * w + 4 * k + v;
+      if (comp < bb && rr < m) Qt_part[((int64_t)by * bb + comp) * m + rr] = acc[s][v];
     }
   }
 }
 
-template <bool W>
+template <int NSUB, bool W>
 __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
                                                       const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                       int bb, int64_t cols_per_split,
                                                       float* __restrict__ Qt_part, const float* __restrict__ wt) {
-  contract_r_v_body<W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt);
+  contract_r_v_body<NSUB, W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt);
 }
 
 
@@ -538,33 +550,29 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
 // one workgroup (256 threads; wave w owns the 16-row tile band w).  Since
 // R_{k+1} = R_k^2, the Frobenius norm of R squares each step while it is
 // below 1.  The start is the previous inverse of the same side (consecutive
-// ALS iterations change the codes little), or X0 = I / ||G'||_inf, which
-// converges for every symmetric positive definite G'.  A warm start whose
-// residual norm exceeds 1/2 is replaced by the scaled identity.  The
+// ALS iterations change the codes little), else the Jacobi guess
+// X0 = diag(G')^-1; a warm start whose residual norm exceeds 1/2 is replaced
+// by the Jacobi guess, and a Jacobi start whose residual grows by
+// X0 = I / ||G'||_inf, which converges for every symmetric positive definite G'.  All loads
+// are issued first; the residual norm is summed in fp32 (wave DPP sums, the
+// wave partials published with R by one barrier), and the iterate is double
+// buffered, so a step costs two barriers.  The
 // iteration stops when ||R||_F < 1e-5, or once ||R||_F < 1e-3 stops falling
 // by more than half (the fp32 floor); a run that does not get there within 40
-// steps is counted in stats[EXTERND_STAT_INVERSE_UNCONVERGED].  The result
+// steps is counted in stats[EXTERND_STAT_INVERSE_UNCONVERGED]; the steps
+// taken and the replaced warm starts are counted too.  The result
 // differs from the fp64 inverse by about 1e-6 relative.  G (integer valued)
 // is zeroed after being read so the next Gram accumulation starts from zero.
 // ---------------------------------------------------------------------------
 constexpr int kNsB = 64, kNsS = 65;
 struct NsShared {
   float G[kNsB * kNsS];
-  float X[kNsB * kNsS];
+  float X[2][kNsB * kNsS];   // current and next iterate
   float R[kNsB * kNsS];
-  double red[kCT / kWave];
+  float red[kCT / kWave];    // per-wave partials of ||R||_F^2
+  double dred[kCT / kWave];
 };
 
-__device__ inline double ns_block_sum(double v, double* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int q = 1; q < kCT / kWave; ++q) r += red[q];
-  return r;
-}
 __device__ inline double ns_block_max(double v, double* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
@@ -592,78 +600,105 @@ __device__ inline void ns_mm(const float* A, const float* B, f4 (&acc)[4]) {
 template <typename GT>
 __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ X,
                                                 int* __restrict__ warm_flag,
-                                                long long* __restrict__ unconverged) {
+                                                long long* __restrict__ stats) {
   __shared__ NsShared sh;
-  constexpr int kPer = kNsB * kNsB / kCT;
+  constexpr int kPer = kNsB * kNsB / kCT;   // entries per thread: rows w + 4q, column lane
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
   const int i16 = lane & 15, kq = lane >> 4;
   const int warm = *warm_flag;
-  // G' = G + eps I in LDS, the identity beyond bb; all loads issued first
-  double trp = 0.0;
-  {
-    GT gv[kPer];
+  // every load first: G (and the previous inverse when warm)
+  GT gv[kPer];
+  float xv[kPer];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
-      gv[q] = (r < bb && c < bb) ? G[r * bb + c] : (GT)0;
-    }
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
-      float v = (r == c) ? 1.f : 0.f;
-      if (r < bb && c < bb) {
-        v = (float)gv[q];
-        if (r == c) trp += (double)gv[q];
-        consume_gram(G, r * bb + c);
-      }
-      sh.G[r * kNsS + c] = v;
-    }
+  for (int q = 0; q < kPer; ++q) {
+    const int r = w + 4 * q;
+    gv[q] = (r < bb && lane < bb) ? G[r * bb + lane] : (GT)0;
   }
-  const double tr = ns_block_sum(trp, sh.red);
-  const float eps = (float)(1e-6 * tr / bb);
-  for (int r = t; r < bb; r += kCT) sh.G[r * kNsS + r] += eps;
-  __syncthreads();
-  double rs = 0.0;
-  {
-    const int row = t >> 2, part = t & 3;   // four threads per row
-    for (int c = part; c < kNsB; c += 4) rs += fabs((double)sh.G[row * kNsS + c]);
-    rs += __shfl_xor(rs, 1);
-    rs += __shfl_xor(rs, 2);
-  }
-  const float alpha = (float)(1.0 / ns_block_max(rs, sh.red));
-  auto init_scaled = [&]() {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
-      sh.X[r * kNsS + c] = (r == c) ? alpha : 0.f;
-    }
-  };
   if (warm) {
-    float xv[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int e = t + kCT * q, r = e / kNsB, c = e % kNsB;
-      xv[q] = (r < bb && c < bb) ? X[r * bb + c] : ((r == c) ? 1.f : 0.f);
+      const int r = w + 4 * q;
+      xv[q] = (r < bb && lane < bb) ? X[r * bb + lane] : ((r == lane) ? 1.f : 0.f);
     }
+  }
+  // trace (each thread holds at most one diagonal entry), eps = 1e-6 trace / b
+  double trp = 0.0;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = t + kCT * q;
-      sh.X[(e / kNsB) * kNsS + e % kNsB] = xv[q];
+  for (int q = 0; q < kPer; ++q) {
+    const int r = w + 4 * q;
+    if (r < bb && lane < bb) {
+      consume_gram(G, r * bb + lane);
+      if (r == lane) trp = (double)gv[q];
     }
-  } else {
-    init_scaled();
+  }
+  trp = wave_sum_to63(trp);
+  if (lane == kWave - 1) sh.dred[w] = trp;
+  __syncthreads();
+  double tr = sh.dred[0];
+#pragma unroll
+  for (int q = 1; q < kCT / kWave; ++q) tr += sh.dred[q];
+  const float eps = (float)(1e-6 * tr / bb);
+  // G' = G + eps I in LDS (the identity beyond bb)
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int r = w + 4 * q;
+    float v = (r == lane) ? 1.f : 0.f;
+    if (r < bb && lane < bb) {
+      v = (float)gv[q];
+      if (r == lane) v += eps;
+    }
+    sh.G[r * kNsS + lane] = v;
+  }
+  int cur = 0;
+  if (warm) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) sh.X[0][(w + 4 * q) * kNsS + lane] = xv[q];
   }
   __syncthreads();
-  bool warm_now = warm != 0;
-  double prev = 1e300;
-  bool conv = false;
+  // X0 = I / ||G'||_inf (the largest absolute row sum), for a cold start or a
+  // rejected warm one
+  auto init_scaled = [&](float* Xd) {
+    double rs = 0.0;
+    {
+      const int row = t >> 2, part = t & 3;   // four threads per row
+      for (int c = part; c < kNsB; c += 4) rs += fabs((double)sh.G[row * kNsS + c]);
+      rs += __shfl_xor(rs, 1);
+      rs += __shfl_xor(rs, 2);
+    }
+    const float alpha = (float)(1.0 / ns_block_max(rs, sh.dred));
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int r = w + 4 * q;
+      Xd[r * kNsS + lane] = (r == lane) ? alpha : 0.f;
+    }
+    __syncthreads();
+  };
+  // X0 = diag(1 / G'_ii): the Gram of decorrelated ternary columns is close
+  // to diagonal, so this is usually far better than the scaled identity; it
+  // can diverge when the columns are strongly correlated (the residual then
+  // grows), and the scaled identity takes over.
+  auto init_jacobi = [&](float* Xd) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int r = w + 4 * q;
+      Xd[r * kNsS + lane] = (r == lane) ? 1.f / sh.G[r * kNsS + r] : 0.f;
+    }
+    __syncthreads();
+  };
+  int start = warm ? 0 : 1;   // 0 warm, 1 Jacobi, 2 scaled identity
+  if (!warm) init_jacobi(sh.X[0]);
+  float prev = 3.0e38f;
+  bool conv = false, restarted = false;
+  int iters_done = 0, since_start = 0;
   for (int it = 0; it < 40; ++it) {
+    ++iters_done;
+    float* Xc = sh.X[cur];
     f4 acc[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
-    ns_mm(sh.G, sh.X, acc);
-    double rp = 0.0;
+    ns_mm(sh.G, Xc, acc);
+    float rp = 0.f;
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -671,43 +706,58 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
         const int r = 16 * w + 4 * kq + v, c = 16 * J + i16;
         const float rv = ((r == c) ? 1.f : 0.f) - acc[J][v];
         sh.R[r * kNsS + c] = rv;
-        rp += (double)rv * (double)rv;
+        rp = fmaf(rv, rv, rp);
       }
-    const double rn2 = ns_block_sum(rp, sh.red);   // its barriers also publish R
-    if (rn2 < 1e-10) {
+    rp = wave_sum_to63(rp);
+    if (lane == kWave - 1) sh.red[w] = rp;
+    __syncthreads();   // publishes R and the partial norms
+    float rn2 = sh.red[0];
+#pragma unroll
+    for (int q = 1; q < kCT / kWave; ++q) rn2 += sh.red[q];
+    if (rn2 < 1e-10f) {
       conv = true;
       break;
     }
-    if (!(rn2 < 1e30) || (warm_now && rn2 > 0.25)) {
-      if (!warm_now) break;   // not finite from the scaled identity: give up
-      warm_now = false;       // poor warm start: restart from the scaled identity
-      init_scaled();
-      __syncthreads();
-      prev = 1e300;
+    const bool bad = !(rn2 < 1e30f) || (start == 0 && rn2 > 0.25f) ||
+                     (start == 1 && since_start > 0 && rn2 > prev);
+    if (bad) {
+      if (start == 2) break;  // not finite from the scaled identity: give up
+      restarted = true;       // poor warm start: Jacobi; diverging Jacobi: scaled identity
+      if (start == 0) init_jacobi(Xc);
+      else init_scaled(Xc);
+      ++start;
+      since_start = 0;
+      prev = 3.0e38f;
       continue;
     }
-    if (rn2 < 1e-6 && rn2 > 0.25 * prev) {
+    ++since_start;
+    if (rn2 < 1e-6f && rn2 > 0.25f * prev) {
       conv = true;
       break;
     }
     prev = rn2;
+    // X_next = X + X R
     f4 y[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) y[J][v] = sh.X[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16];
-    ns_mm(sh.X, sh.R, y);
-    __syncthreads();
+      for (int v = 0; v < 4; ++v) y[J][v] = Xc[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16];
+    ns_mm(Xc, sh.R, y);
+    float* Xn = sh.X[cur ^ 1];
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sh.X[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16] = y[J][v];
-    __syncthreads();
+      for (int v = 0; v < 4; ++v) Xn[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16] = y[J][v];
+    __syncthreads();   // X_next complete; every read of R and X done
+    cur ^= 1;
   }
-  for (int e = t; e < bb * bb; e += kCT) X[e] = sh.X[(e / bb) * kNsS + (e % bb)];
+  const float* Xf = sh.X[cur];
+  for (int e = t; e < bb * bb; e += kCT) X[e] = Xf[(e / bb) * kNsS + (e % bb)];
   if (t == 0) {
     *warm_flag = 1;
-    if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(unconverged), 1ull);
+    if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_INVERSE_UNCONVERGED), 1ull);
+    atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_ITERATIONS), (unsigned long long)iters_done);
+    if (restarted) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_RESTARTS), 1ull);
   }
 }
 
@@ -717,22 +767,22 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
 // them concurrent without a second stream.
 // With W (V side only) the contraction is R diag(wt) V and G is the weighted
 // Gram V^T diag(wt) V in fp64 (§2.5).
-template <bool UT, bool W>
+template <bool UT, bool W, int NSUB>
 __global__ __launch_bounds__(kCT) void k_contract_with_inverse(
     const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
     int bb, int64_t per_split, float* __restrict__ Part, void* __restrict__ G,
-    float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ unconverged,
+    float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ stats,
     const float* __restrict__ wt) {
   static_assert(!(UT && W), "weights apply to the V-side contraction only");
   if ((int)blockIdx.x == (int)gridDim.x - 1) {
     if (blockIdx.y == 0) {
-      if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, unconverged);
-      else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, unconverged);
+      if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats);
+      else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats);
     }
     return;
   }
-  if constexpr (UT) contract_ut_r_body(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
-  else contract_r_v_body<W>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y, wt);
+  if constexpr (UT) contract_ut_r_body<NSUB>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
+  else contract_r_v_body<NSUB, W>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y, wt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,8 +1227,13 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   const int64_t tiles1 = (n + 63) / 64, tiles2 = (m + 63) / 64;
   int64_t s1 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles1 - 1) / tiles1, (m + 255) / 256));
   int64_t s2 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles2 - 1) / tiles2, (n + 255) / 256));
-  L.rows_split = ((m + s1 - 1) / s1 + 15) / 16 * 16;
-  L.cols_split = ((n + s2 - 1) / s2 + 15) / 16 * 16;
+  // splits are whole 256-long chunks of the contracted dimension when they
+  // can be (the contraction stages codes per chunk), else multiples of 16
+  auto round_split = [](int64_t len) {
+    return len >= kChunk ? (len + kChunk - 1) / kChunk * kChunk : (len + 15) / 16 * 16;
+  };
+  L.rows_split = round_split((m + s1 - 1) / s1);
+  L.cols_split = round_split((n + s2 - 1) / s2);
   L.S1 = (int)((m + L.rows_split - 1) / L.rows_split);
   L.S2 = (int)((n + L.cols_split - 1) / L.cols_split);
   size_t by = 0;
@@ -1214,6 +1269,20 @@ void launch_inverse(int bb, GT* G, float* Ginv, int* fail, hipStream_t st) {
     hipLaunchKernelGGL((k_spd_inverse<4, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
   else
     hipLaunchKernelGGL((k_spd_inverse<8, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
+}
+
+// The combined contraction + inverse launch for bb <= 64, by sub-tile count.
+template <bool UT, bool W>
+void launch_combined(int bb, dim3 grid, hipStream_t s, const float* R, int64_t m, int64_t n, const uint32_t* codes,
+                     int64_t wl, int64_t per_split, float* Part, void* G, float* Ginv, int* warm, long long* st,
+                     const float* wt) {
+  const int nsub = (bb + 15) / 16;
+  if (nsub == 1)
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 1>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
+  else if (nsub == 2)
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 2>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
+  else
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 4>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
 }
 
 }  // namespace
@@ -1306,10 +1375,10 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       // concurrently with it; wider blocks invert by Gauss-Jordan first.
       hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
       if (bb <= 64) {
-        hipLaunchKernelGGL((k_contract_with_inverse<true, false>), dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)nullptr);
+        launch_combined<true, false>(bb, dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st, (const float*)nullptr);
       } else {
         launch_inverse(bb, GU, GinvU, fail, s);
-        hipLaunchKernelGGL(k_contract_ut_r, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
+        hipLaunchKernelGGL(k_contract_ut_r<8>, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
       row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
@@ -1320,18 +1389,18 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         hipLaunchKernelGGL(k_gram_w_partial, dim3(gram_v.x, (unsigned)wsplits), dim3(256), 0, s, Vc, wn, bb, wt, n, Gwpart);
         hipLaunchKernelGGL(k_gram_w_reduce, dim3((unsigned)((bb * bb + 255) / 256)), dim3(256), 0, s, Gwpart, wsplits, bb, GVw);
         if (bb <= 64) {
-          hipLaunchKernelGGL((k_contract_with_inverse<false, true>), cgrid2, dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)wt);
+          launch_combined<false, true>(bb, cgrid2, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st, (const float*)wt);
         } else {
           launch_inverse(bb, GVw, GinvV, fail, s);
-          hipLaunchKernelGGL(k_contract_r_v<true>, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)wt);
+          hipLaunchKernelGGL((k_contract_r_v<8, true>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)wt);
         }
       } else {
         hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
         if (bb <= 64) {
-          hipLaunchKernelGGL((k_contract_with_inverse<false, false>), cgrid2, dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st + EXTERND_STAT_INVERSE_UNCONVERGED, (const float*)nullptr);
+          launch_combined<false, false>(bb, cgrid2, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st, (const float*)nullptr);
         } else {
           launch_inverse(bb, GV, GinvV, fail, s);
-          hipLaunchKernelGGL(k_contract_r_v<false>, dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)nullptr);
+          hipLaunchKernelGGL((k_contract_r_v<8, false>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)nullptr);
         }
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
