@@ -79,16 +79,18 @@ def copy_probe(mib):
                       "launches": 5}), flush=True)
 
 
-def seq_alg_bytes(m, n, k, iters, sum_nnz_u):
+def seq_alg_bytes(m, n, k, iterations, sum_nnz_u):
     """Bytes a streaming implementation must move for the sequential path.
 
     Per component: the first R^T u0 pass reads all of R (u0 is dense); each
-    of the `iters` R v passes reads all of R; the R^T u passes of iterations
-    2..iters read only rows where u is nonzero; the deflation rewrites the
-    rows where the final u is nonzero.  That is 4 n ((iters+1) m + sum_t nnz(u_t))
-    with t over the iters u vectors of the component.
+    R v pass reads all of R; the R^T u passes of the later iterations read
+    only rows where u is nonzero; the deflation rewrites the rows where the
+    final u is nonzero.  Over the decomposition that is
+    4 n ((iterations + k) m + sum_t nnz(u_t)), iterations being the ALS
+    iterations run over all components and t running over the u vectors of
+    those iterations.
     """
-    return 4.0 * n * ((iters + 1) * m * k + sum_nnz_u)
+    return 4.0 * n * ((iterations + k) * m + sum_nnz_u)
 
 
 def block_alg_flops(m, n, k, b, iters):
@@ -290,7 +292,7 @@ def main():
     roofline = None
     if "seq" in per_mode:
         s = per_mode["seq"]
-        alg = seq_alg_bytes(m, n, k, c["iters"], s["stats"]["sum_nnz_u"])
+        alg = seq_alg_bytes(m, n, k, s["stats"]["iterations"] or k * c["iters"], s["stats"]["sum_nnz_u"])
         achieved = alg / (s["ms"] / 1e3) / 1e9
         s["alg_bytes"] = alg
         s["gbps"] = achieved

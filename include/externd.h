@@ -66,12 +66,14 @@ enum externd_stat {
   EXTERND_STAT_MODE = 6,        /* mode actually run (0 streaming, 1 resident, 2 block) */
   EXTERND_STAT_GRID = 7,        /* workgroups of the resident kernel (0 otherwise) */
   EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
-  EXTERND_STAT_TIMEOUTS = 9,    /* resident mode: 1 if an exchange wait ran out (energy is NaN) */
+  EXTERND_STAT_TIMEOUTS = 9,    /* waits that ran out (energy is NaN): resident exchange, or
+                                   block mode's Gram-before-inverse wait */
   EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode: Gram inverses whose Newton-Schulz
                                     iteration stopped before reaching its tolerance */
   EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
   EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode: Newton-Schulz steps over all Gram inverses */
-  EXTERND_STAT_NS_RESTARTS = 13,    /* block mode: warm starts replaced by the scaled identity */
+  EXTERND_STAT_NS_RESTARTS = 13,    /* block mode: warm starts replaced by another start */
+  EXTERND_STAT_ITERATIONS = 14,     /* ALS iterations run, over all components (blocks) */
   EXTERND_STATS_LEN = 16
 };
 

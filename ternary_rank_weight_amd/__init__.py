@@ -27,7 +27,8 @@ MODE_AUTO, MODE_STREAMING, MODE_RESIDENT = -1, 0, 1
 STATS_LEN = 16
 STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
         "nonfinite": 5, "mode": 6, "grid": 7, "ridge_retries": 8, "timeouts": 9,
-        "inverse_unconverged": 10, "sweep_kept_old": 11, "ns_iterations": 12, "ns_restarts": 13}
+        "inverse_unconverged": 10, "sweep_kept_old": 11, "ns_iterations": 12, "ns_restarts": 13,
+        "iterations": 14}
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is missing; build it with "

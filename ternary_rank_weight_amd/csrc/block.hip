@@ -67,17 +67,17 @@ __global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint
 constexpr int kGramChunk = 64;    // words per LDS stage
 constexpr int kGramSplit = 64;    // words per workgroup (one LDS stage)
 
-__global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb,
-                                              int* __restrict__ G) {
-  __shared__ uint32_t rows[32][kGramChunk + 1];
+__device__ __forceinline__ void gram_tile_body(const uint32_t* __restrict__ codes, int64_t wl, int bb,
+                                               int* __restrict__ G, int tile, int split,
+                                               uint32_t (*rows)[kGramChunk + 1]) {
   const int t = threadIdx.x;
   // triangular tile index -> (I, J), J <= I
   int I = 0;
-  while ((I + 1) * (I + 2) / 2 <= (int)blockIdx.x) ++I;
-  const int J = (int)blockIdx.x - I * (I + 1) / 2;
+  while ((I + 1) * (I + 2) / 2 <= tile) ++I;
+  const int J = tile - I * (I + 1) / 2;
   const int r = t >> 4, c = t & 15;
   const int i = 16 * I + r, j = 16 * J + c;
-  const int64_t w_begin = (int64_t)blockIdx.y * kGramSplit;
+  const int64_t w_begin = (int64_t)split * kGramSplit;
   const int64_t w_end = min(wl, w_begin + kGramSplit);
   unsigned pos = 0u, neg = 0u;
   for (int64_t w0 = w_begin; w0 < w_end; w0 += kGramChunk) {
@@ -101,6 +101,12 @@ __global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes
     atomicAdd(G + i * bb + j, acc);
     if (I != J) atomicAdd(G + j * bb + i, acc);
   }
+}
+
+__global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb,
+                                              int* __restrict__ G) {
+  __shared__ uint32_t rows[32][kGramChunk + 1];
+  gram_tile_body(codes, wl, bb, G, (int)blockIdx.x, (int)blockIdx.y, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -399,10 +405,13 @@ __device__ inline void stage_codes(uint32_t (*cs)[kCW + 1], const uint32_t* __re
 // Wave w owns columns 64 bx + 16 w + j (j = lane % 16); lane (j + 16k) feeds
 // row 16 step + k + 4q at MFMA q of a step to both operands.
 template <int NSUB>
+using CodeStage = uint32_t[2][16 * NSUB][kCW + 1];
+
+template <int NSUB>
 __device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, int64_t m, int64_t n,
                                    const uint32_t* __restrict__ Ucodes, int64_t wm, int bb,
-                                   int64_t rows_per_split, float* __restrict__ Pt_part, int bx, int by) {
-  __shared__ uint32_t cs[2][16 * NSUB][kCW + 1];
+                                   int64_t rows_per_split, float* __restrict__ Pt_part, int bx, int by,
+                                   CodeStage<NSUB>& cs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane & 15, k = lane >> 4;
   const int64_t col = (int64_t)bx * 64 + 16 * w + j;
@@ -453,7 +462,8 @@ __global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        int bb, int64_t rows_per_split,
                                                        float* __restrict__ Pt_part) {
-  contract_ut_r_body<NSUB>(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y);
+  __shared__ CodeStage<NSUB> cs;
+  contract_ut_r_body<NSUB>(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y, cs);
 }
 
 // Qt_part[split][i][r] = sum over the split's columns c of R[r][c] V[c][i]
@@ -465,8 +475,7 @@ template <int NSUB, bool W>
 __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, int64_t m, int64_t n,
                                   const uint32_t* __restrict__ Vcodes, int64_t wn, int bb,
                                   int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by,
-                                  const float* __restrict__ wt) {
-  __shared__ uint32_t cs[2][16 * NSUB][kCW + 1];
+                                  const float* __restrict__ wt, CodeStage<NSUB>& cs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, k = lane >> 4;
   const int64_t row = (int64_t)bx * 64 + 16 * w + i;
@@ -540,7 +549,8 @@ __global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ 
                                                       const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                       int bb, int64_t cols_per_split,
                                                       float* __restrict__ Qt_part, const float* __restrict__ wt) {
-  contract_r_v_body<NSUB, W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt);
+  __shared__ CodeStage<NSUB> cs;
+  contract_r_v_body<NSUB, W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt, cs);
 }
 
 
@@ -600,8 +610,7 @@ __device__ inline void ns_mm(const float* A, const float* B, f4 (&acc)[4]) {
 template <typename GT>
 __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ X,
                                                 int* __restrict__ warm_flag,
-                                                long long* __restrict__ stats) {
-  __shared__ NsShared sh;
+                                                long long* __restrict__ stats, NsShared& sh) {
   constexpr int kPer = kNsB * kNsB / kCT;   // entries per thread: rows w + 4q, column lane
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
@@ -761,28 +770,66 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   }
 }
 
-// The contraction with one extra workgroup, (gridDim.x - 1, 0), that inverts
-// the Gram matrix of the same codes meanwhile: both depend only on the codes
-// and R, and the decorrelation needs both.  One launch instead of two keeps
-// them concurrent without a second stream.
-// With W (V side only) the contraction is R diag(wt) V and G is the weighted
-// Gram V^T diag(wt) V in fp64 (§2.5).
+// One launch per half-step for b <= 64 (1-D grid, roles by block index, in
+// dispatch order):
+//   [0, ngram)        Gram tiles: (tile, split) of the exact Gram of the codes,
+//                     added into G with atomics; each then bumps *gram_done
+//                     (release);
+//   ngram             the Newton-Schulz inverse of G' (weighted: G given),
+//                     after *gram_done has reached gram_target (acquire; a
+//                     bounded wait, counted in stats[TIMEOUTS] if it runs out);
+//   the rest          the contraction, (bx, by) = (c % tiles, c / tiles).
+// Only the inverse waits, and only on workgroups dispatched before it, so the
+// wait always ends.  The roles share one LDS union.  *gram_done counts up over
+// the whole decomposition; the host passes the running target.
+constexpr unsigned kGramSpinLimit = 1u << 22;
+
+template <int NSUB>
+union HalfStepLds {
+  NsShared ns;
+  CodeStage<NSUB> cs;
+  uint32_t rows[32][kGramChunk + 1];
+};
+
 template <bool UT, bool W, int NSUB>
 __global__ __launch_bounds__(kCT) void k_contract_with_inverse(
     const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
     int bb, int64_t per_split, float* __restrict__ Part, void* __restrict__ G,
     float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ stats,
-    const float* __restrict__ wt) {
+    const float* __restrict__ wt, int ngram, int gsplits, int tiles,
+    unsigned long long* __restrict__ gram_done, unsigned long long gram_target) {
   static_assert(!(UT && W), "weights apply to the V-side contraction only");
-  if ((int)blockIdx.x == (int)gridDim.x - 1) {
-    if (blockIdx.y == 0) {
-      if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats);
-      else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats);
+  __shared__ HalfStepLds<NSUB> lds;
+  const int idx = (int)blockIdx.x;
+  if (idx < ngram) {
+    if constexpr (!W) {
+      gram_tile_body(codes, wl, bb, static_cast<int*>(G), idx / gsplits, idx % gsplits, lds.rows);
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(gram_done, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
-  if constexpr (UT) contract_ut_r_body<NSUB>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y);
-  else contract_r_v_body<NSUB, W>(R, m, n, codes, wl, bb, per_split, Part, blockIdx.x, blockIdx.y, wt);
+  if (idx == ngram) {
+    if (ngram > 0) {
+      if (threadIdx.x == 0) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(gram_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gram_target) {
+          if (++spins > kGramSpinLimit) {
+            atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_TIMEOUTS), 1ull);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __syncthreads();
+    }
+    if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+    else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+    return;
+  }
+  const int c = idx - ngram - 1;
+  if constexpr (UT) contract_ut_r_body<NSUB>(R, m, n, codes, wl, bb, per_split, Part, c % tiles, c / tiles, lds.cs);
+  else contract_r_v_body<NSUB, W>(R, m, n, codes, wl, bb, per_split, Part, c % tiles, c / tiles, wt, lds.cs);
 }
 
 // ---------------------------------------------------------------------------
@@ -829,7 +876,7 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
 // row.  Codes go to out_codes row i (row stride wl words); nnz[i] gets the
 // count; fallbacks counted in *fb.
 // ---------------------------------------------------------------------------
-constexpr int kTT = 256;
+constexpr int kTT = 512;
 
 __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__ Xt, int64_t L, float tau,
                                                        uint32_t* __restrict__ out_codes, int64_t wl,
@@ -1201,7 +1248,7 @@ __global__ void k_block_finish(const double* __restrict__ a2, const double* __re
                                const long long* __restrict__ local, long long* __restrict__ stats) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   double e;
-  if (*nonfinite > 0) e = __longlong_as_double(0x7ff8000000000000ll);
+  if (*nonfinite > 0 || local[EXTERND_STAT_TIMEOUTS] > 0) e = __longlong_as_double(0x7ff8000000000000ll);
   else if (*a2 == 0.0) e = 1.0;
   else e = 1.0 - *r2 / *a2;
   *energy = e;
@@ -1252,7 +1299,8 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   // importance weights: column weights, weighted Gram and its split partials
   by += sizeof(float) * (size_t)n;
   by += sizeof(double) * (size_t)b * b * (1 + ((n + 15) / 16 + kGramSplit - 1) / kGramSplit);
-  by += 28 * 256;   // alignment slack of the bump allocations
+  by += sizeof(unsigned long long) * 2;   // Gram tile counters
+  by += 29 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
 }
@@ -1271,18 +1319,22 @@ void launch_inverse(int bb, GT* G, float* Ginv, int* fail, hipStream_t st) {
     hipLaunchKernelGGL((k_spd_inverse<8, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
 }
 
-// The combined contraction + inverse launch for bb <= 64, by sub-tile count.
+// The combined launch for bb <= 64, by sub-tile count.  ngram Gram tiles
+// (0 when G is computed beforehand), one inverse, tiles x splits contraction
+// workgroups.
 template <bool UT, bool W>
-void launch_combined(int bb, dim3 grid, hipStream_t s, const float* R, int64_t m, int64_t n, const uint32_t* codes,
-                     int64_t wl, int64_t per_split, float* Part, void* G, float* Ginv, int* warm, long long* st,
-                     const float* wt) {
+void launch_combined(int bb, int tiles, int splits, int ngram, int gsplits, hipStream_t s, const float* R, int64_t m,
+                     int64_t n, const uint32_t* codes, int64_t wl, int64_t per_split, float* Part, void* G,
+                     float* Ginv, int* warm, long long* st, const float* wt, unsigned long long* gram_done,
+                     unsigned long long gram_target) {
   const int nsub = (bb + 15) / 16;
+  const dim3 grid((unsigned)(ngram + 1 + tiles * splits));
   if (nsub == 1)
-    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 1>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 1>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
   else if (nsub == 2)
-    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 2>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 2>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
   else
-    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 4>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt);
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 4>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
 }
 
 }  // namespace
@@ -1323,6 +1375,10 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   double* dneg = reinterpret_cast<double*>(bump(p, sizeof(double) * b));
   double* dpart = reinterpret_cast<double*>(bump(p, sizeof(double) * ((n + 63) / 64) * ((m + 63) / 64)));
   int* accept = reinterpret_cast<int*>(bump(p, sizeof(int)));
+  // Gram tiles finished inside the combined launches (U side, V side),
+  // counting up over the whole decomposition
+  unsigned long long* gram_done = reinterpret_cast<unsigned long long*>(bump(p, sizeof(unsigned long long) * 2));
+  unsigned long long gram_issued[2] = {0ull, 0ull};
   // importance weighting (§2.5): column weights wt, the weighted V-side Gram
   // V^T diag(wt) V and its per-split partials
   const bool W = a.importance != nullptr;
@@ -1345,6 +1401,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
 
   const size_t dec_lds = sizeof(float) * (b * b + b * kDecW);
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
+  if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 2, 0, s)) != hipSuccess) return e;
   const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
   const int64_t ndpart = (int64_t)defl_grid.x * defl_grid.y;
 
@@ -1373,10 +1430,13 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       // inverse depend only on U's codes: up to b = 64 the inverse (Newton-
       // Schulz) runs as one extra workgroup of the contraction launch,
       // concurrently with it; wider blocks invert by Gauss-Jordan first.
-      hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
       if (bb <= 64) {
-        launch_combined<true, false>(bb, dim3((unsigned)((n + 63) / 64 + 1), (unsigned)L.S1), s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st, (const float*)nullptr);
+        // the Gram of U is computed inside the launch, ahead of its inverse
+        const int ng = (int)(gram_u.x * gram_u.y);
+        gram_issued[0] += (unsigned long long)ng;
+        launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st, (const float*)nullptr, gram_done, gram_issued[0]);
       } else {
+        hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
         launch_inverse(bb, GU, GinvU, fail, s);
         hipLaunchKernelGGL(k_contract_ut_r<8>, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
       }
@@ -1384,21 +1444,22 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V;  weighted (§2.5):
       // Q = R diag(wt) V and the Gram V^T diag(wt) V
-      const dim3 cgrid2((unsigned)((m + 63) / 64 + 1), (unsigned)L.S2);
       if (W) {
         hipLaunchKernelGGL(k_gram_w_partial, dim3(gram_v.x, (unsigned)wsplits), dim3(256), 0, s, Vc, wn, bb, wt, n, Gwpart);
         hipLaunchKernelGGL(k_gram_w_reduce, dim3((unsigned)((bb * bb + 255) / 256)), dim3(256), 0, s, Gwpart, wsplits, bb, GVw);
         if (bb <= 64) {
-          launch_combined<false, true>(bb, cgrid2, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st, (const float*)wt);
+          launch_combined<false, true>(bb, (int)((m + 63) / 64), L.S2, 0, 1, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st, (const float*)wt, gram_done + 1, 0ull);
         } else {
           launch_inverse(bb, GVw, GinvV, fail, s);
           hipLaunchKernelGGL((k_contract_r_v<8, true>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)wt);
         }
       } else {
-        hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
         if (bb <= 64) {
-          launch_combined<false, false>(bb, cgrid2, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st, (const float*)nullptr);
+          const int ng = (int)(gram_v.x * gram_v.y);
+          gram_issued[1] += (unsigned long long)ng;
+          launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
         } else {
+          hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
           launch_inverse(bb, GV, GinvV, fail, s);
           hipLaunchKernelGGL((k_contract_r_v<8, false>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)nullptr);
         }
@@ -1450,6 +1511,8 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wm, 256, 1024)), dim3(256), 0, s, a.B2, k * wm, st + EXTERND_STAT_NNZ_B);
     hipLaunchKernelGGL(k_count_nonzero, dim3(grid1d(k * wn, 256, 1024)), dim3(256), 0, s, a.C2, k * wn, st + EXTERND_STAT_NNZ_C);
   }
+  if ((e = launch_fill_i64(st + EXTERND_STAT_ITERATIONS, 1, (long long)(nblocks * a.iters * (1 + a.sweeps)), s)) != hipSuccess)
+    return e;
   if ((e = launch_norm2(R, m * n, npart, 4096, r2, nullptr, s, wt, n)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_block_finish, dim3(1), dim3(1), 0, s, a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, st, a.stats);
   if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;

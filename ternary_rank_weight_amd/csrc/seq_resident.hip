@@ -549,6 +549,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       a.stats[EXTERND_STAT_FALLBACKS] = st_fb;
       a.stats[EXTERND_STAT_MODE] = EXTERND_MODE_RESIDENT;
       a.stats[EXTERND_STAT_GRID] = a.G;
+      a.stats[EXTERND_STAT_ITERATIONS] = (long long)a.k * a.iters;
     }
   }
 }

@@ -611,6 +611,8 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   if ((e = launch_energy_finish(a2, r2, st + EXTERND_STAT_NONFINITE, a.energy, s)) != hipSuccess) return e;
   if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   if (a.stats) {
+    // the streaming path runs every iteration of every component
+    if ((e = launch_fill_i64(st + EXTERND_STAT_ITERATIONS, 1, (long long)(k * a.iters), s)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_copy_i64, dim3(1), dim3(64), 0, s, st, a.stats, (int64_t)EXTERND_STATS_LEN);
   }
   return hipGetLastError();
