@@ -356,11 +356,6 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
     }
 }
 
-template <int NA, typename GT>
-__global__ __launch_bounds__(kCholT) void k_spd_inverse(GT* __restrict__ G, int bb,
-                                                        float* __restrict__ Ginv, int* __restrict__ fail) {
-  spd_inverse_body<NA, GT>(G, bb, Ginv, fail);
-}
 
 // ---------------------------------------------------------------------------
 // The two contractions.  A workgroup (4 waves) takes 64 outputs (columns of
@@ -457,14 +452,6 @@ __device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, 
   }
 }
 
-template <int NSUB>
-__global__ __launch_bounds__(kCT) void k_contract_ut_r(const float* __restrict__ R, int64_t m, int64_t n,
-                                                       const uint32_t* __restrict__ Ucodes, int64_t wm,
-                                                       int bb, int64_t rows_per_split,
-                                                       float* __restrict__ Pt_part) {
-  __shared__ CodeStage<NSUB> cs;
-  contract_ut_r_body<NSUB>(R, m, n, Ucodes, wm, bb, rows_per_split, Pt_part, blockIdx.x, blockIdx.y, cs);
-}
 
 // Qt_part[split][i][r] = sum over the split's columns c of R[r][c] V[c][i]
 // (with W: R[r][c] wt[c] V[c][i], §2.5).  Wave w owns rows 64 bx + 16 w + i
@@ -544,14 +531,6 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
   }
 }
 
-template <int NSUB, bool W>
-__global__ __launch_bounds__(kCT) void k_contract_r_v(const float* __restrict__ R, int64_t m, int64_t n,
-                                                      const uint32_t* __restrict__ Vcodes, int64_t wn,
-                                                      int bb, int64_t cols_per_split,
-                                                      float* __restrict__ Qt_part, const float* __restrict__ wt) {
-  __shared__ CodeStage<NSUB> cs;
-  contract_r_v_body<NSUB, W>(R, m, n, Vcodes, wn, bb, cols_per_split, Qt_part, blockIdx.x, blockIdx.y, wt, cs);
-}
 
 
 // ---------------------------------------------------------------------------
@@ -770,12 +749,13 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   }
 }
 
-// One launch per half-step for b <= 64 (1-D grid, roles by block index, in
-// dispatch order):
+// One launch per half-step (1-D grid, roles by block index, in dispatch
+// order):
 //   [0, ngram)        Gram tiles: (tile, split) of the exact Gram of the codes,
 //                     added into G with atomics; each then bumps *gram_done
 //                     (release);
-//   ngram             the Newton-Schulz inverse of G' (weighted: G given),
+//   ngram             the inverse of G' (weighted: G given): Newton-Schulz up
+//                     to b = 64, fp64 Gauss-Jordan beyond,
 //                     after *gram_done has reached gram_target (acquire; a
 //                     bounded wait, counted in stats[TIMEOUTS] if it runs out);
 //   the rest          the contraction, (bx, by) = (c % tiles, c / tiles).
@@ -788,6 +768,11 @@ template <int NSUB>
 union HalfStepLds {
   NsShared ns;
   CodeStage<NSUB> cs;
+  uint32_t rows[32][kGramChunk + 1];
+};
+template <>
+union HalfStepLds<8> {   // b > 64: the Gauss-Jordan body brings its own LDS
+  CodeStage<8> cs;
   uint32_t rows[32][kGramChunk + 1];
 };
 
@@ -823,8 +808,13 @@ __global__ __launch_bounds__(kCT) void k_contract_with_inverse(
       }
       __syncthreads();
     }
-    if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats, lds.ns);
-    else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+    if constexpr (NSUB == 8) {   // b > 64: Gauss-Jordan in fp64; *warm_flag gets 1 if G' is not SPD
+      if constexpr (W) spd_inverse_body<8, double>(static_cast<double*>(G), bb, Ginv, warm_flag);
+      else spd_inverse_body<8, int>(static_cast<int*>(G), bb, Ginv, warm_flag);
+    } else {
+      if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+      else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+    }
     return;
   }
   const int c = idx - ngram - 1;
@@ -1311,15 +1301,8 @@ inline char* bump(char*& p, size_t bytes) {
   return r;
 }
 
-template <typename GT>
-void launch_inverse(int bb, GT* G, float* Ginv, int* fail, hipStream_t st) {
-  if (bb <= 64)
-    hipLaunchKernelGGL((k_spd_inverse<4, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
-  else
-    hipLaunchKernelGGL((k_spd_inverse<8, GT>), dim3(1), dim3(kCholT), 0, st, G, bb, Ginv, fail);
-}
 
-// The combined launch for bb <= 64, by sub-tile count.  ngram Gram tiles
+// The combined launch, by sub-tile count.  ngram Gram tiles
 // (0 when G is computed beforehand), one inverse, tiles x splits contraction
 // workgroups.
 template <bool UT, bool W>
@@ -1329,7 +1312,9 @@ void launch_combined(int bb, int tiles, int splits, int ngram, int gsplits, hipS
                      unsigned long long gram_target) {
   const int nsub = (bb + 15) / 16;
   const dim3 grid((unsigned)(ngram + 1 + tiles * splits));
-  if (nsub == 1)
+  if (nsub > 4)
+    hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 8>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
+  else if (nsub == 1)
     hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 1>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
   else if (nsub == 2)
     hipLaunchKernelGGL((k_contract_with_inverse<UT, W, 2>), grid, dim3(kCT), 0, s, R, m, n, codes, wl, bb, per_split, Part, G, Ginv, warm, st, wt, ngram, gsplits, tiles, gram_done, gram_target);
@@ -1430,15 +1415,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       // inverse depend only on U's codes: up to b = 64 the inverse (Newton-
       // Schulz) runs as one extra workgroup of the contraction launch,
       // concurrently with it; wider blocks invert by Gauss-Jordan first.
-      if (bb <= 64) {
+      {
         // the Gram of U is computed inside the launch, ahead of its inverse
         const int ng = (int)(gram_u.x * gram_u.y);
         gram_issued[0] += (unsigned long long)ng;
-        launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, warm, st, (const float*)nullptr, gram_done, gram_issued[0]);
-      } else {
-        hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GU);
-        launch_inverse(bb, GU, GinvU, fail, s);
-        hipLaunchKernelGGL(k_contract_ut_r<8>, dim3((unsigned)((n + 63) / 64), (unsigned)L.S1), dim3(kCT), 0, s, R, m, n, Uc, wm, bb, L.rows_split, Pt_part);
+        launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, bb <= 64 ? warm : fail, st, (const float*)nullptr, gram_done, gram_issued[0]);
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
       row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
@@ -1447,22 +1428,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       if (W) {
         hipLaunchKernelGGL(k_gram_w_partial, dim3(gram_v.x, (unsigned)wsplits), dim3(256), 0, s, Vc, wn, bb, wt, n, Gwpart);
         hipLaunchKernelGGL(k_gram_w_reduce, dim3((unsigned)((bb * bb + 255) / 256)), dim3(256), 0, s, Gwpart, wsplits, bb, GVw);
-        if (bb <= 64) {
-          launch_combined<false, true>(bb, (int)((m + 63) / 64), L.S2, 0, 1, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, warm + 1, st, (const float*)wt, gram_done + 1, 0ull);
-        } else {
-          launch_inverse(bb, GVw, GinvV, fail, s);
-          hipLaunchKernelGGL((k_contract_r_v<8, true>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)wt);
-        }
+        launch_combined<false, true>(bb, (int)((m + 63) / 64), L.S2, 0, 1, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)wt, gram_done + 1, 0ull);
       } else {
-        if (bb <= 64) {
-          const int ng = (int)(gram_v.x * gram_v.y);
-          gram_issued[1] += (unsigned long long)ng;
-          launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, warm + 1, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
-        } else {
-          hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GV);
-          launch_inverse(bb, GV, GinvV, fail, s);
-          hipLaunchKernelGGL((k_contract_r_v<8, false>), dim3((unsigned)((m + 63) / 64), (unsigned)L.S2), dim3(kCT), 0, s, R, m, n, Vc, wn, bb, L.cols_split, Qt_part, (const float*)nullptr);
-        }
+        const int ng = (int)(gram_v.x * gram_v.y);
+        gram_issued[1] += (unsigned long long)ng;
+        launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
       }
       hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
       row_tern(Ut, m, Uc, wm, nnz, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
