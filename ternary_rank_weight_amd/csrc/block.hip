@@ -839,17 +839,41 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
   const int64_t c0 = (int64_t)blockIdx.x * kDecW;
 #pragma unroll 8
   for (int e = t; e < bb * bb; e += 256) Gs[e] = Ginv[e];
-#pragma unroll 2
-  for (int e = t; e < bb * kDecW; e += 256) {
-    const int kk = e / kDecW, cc = e % kDecW;
-    const int64_t c = c0 + cc;
-    float s = 0.f;
-    if (c < L) {
-#pragma unroll 8
-      for (int q = 0; q < S; ++q) s += Part[((int64_t)q * bb + kk) * L + c];
+  // the split sums, in split order; up to 8 splits of every entry of this
+  // thread are loaded before any is added
+  constexpr int kQ = 8;
+  for (int e0 = t; e0 < bb * kDecW; e0 += 4 * 256) {
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < S; q0 += kQ) {
+      float v[4][kQ];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u;
+        const int kk = e / kDecW, cc = e % kDecW;
+        const int64_t c = c0 + cc;
+        const bool ok = e < bb * kDecW && c < L;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          const bool okq = ok && q0 + q < S;
+          const float x = Part[okq ? ((int64_t)(q0 + q) * bb + kk) * L + c : 0];
+          v[u][q] = okq ? x : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) s4[u] += v[u][q];
     }
-    Ps[e] = s;
-    if (sum_out && c < L) sum_out[(int64_t)kk * L + c] = s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + 256 * u;
+      if (e < bb * kDecW) {
+        const int kk = e / kDecW, cc = e % kDecW;
+        const int64_t c = c0 + cc;
+        Ps[e] = s4[u];
+        if (sum_out && c < L) sum_out[(int64_t)kk * L + c] = s4[u];
+      }
+    }
   }
   __syncthreads();
   const int cc = t % kDecW;
