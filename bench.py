@@ -26,11 +26,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
 # same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
 # reported only while the kernel's sources hash to the ones it was taken on.
-SEQ_TRAFFIC_BYTES = 38937725050
+SEQ_TRAFFIC_BYTES = 38576916325
 SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
-                       "ternary_rank_weight_amd/csrc/device_common.hpp",
-                       "ternary_rank_weight_amd/csrc/kernels.hpp"]
-SEQ_TRAFFIC_SHA = "06e28fa14817eb6f"
+                       "ternary_rank_weight_amd/csrc/device_common.hpp"]
+SEQ_TRAFFIC_SHA = "02e837a922544f93"
 
 
 def seq_traffic(config):
@@ -49,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--modes", default="seq,block")
+    ap.add_argument("--modes", default=None,
+                    help="comma-separated subset of seq,block (default: seq,block; block for config 3)")
     ap.add_argument("--cpu-sample", type=int, default=200,
                     help="components of the oracle's sequential run timed as the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -59,7 +59,9 @@ def parse():
                     help="skip the block run with the optimal ternary projection")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3],
+                    help="1: 256x256 Gaussian; 2: 2560x2560 LLM-shaped (default); "
+                         "3: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
                          "exit; its HBM counters calibrate the per-kernel traffic figures")
@@ -208,19 +210,29 @@ def measure_projection(trw, Ad, c, block):
             "ms": round(e0.elapsed_time(e1), 3), "energy": round(float(r.energy.item()), 6)}
 
 
-def cpu_baseline(A, c, sample):
+def cpu_baseline(A, c, sample, block=0):
+    """The oracle timed on a bounded sample: the first `sample` components of
+    the sequential decomposition, or for block mode alone (block > 0) the
+    first ceil(sample / b) blocks of the block decomposition."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
+    m, n = A.shape
+    k_all = oracle.rank_for(m, n, c["mu"])
     t = time.perf_counter()
-    r = oracle.decompose_seq(A, c["mu"], c["tau"], c["iters"], c["seed"], k=sample)
+    if block:
+        b = oracle.block_width(m, n, block)
+        sample = min(k_all, -(-sample // b) * b)
+        r = oracle.decompose_block(A, c["mu"], c["tau"], c["iters"], block, c["seed"], k=sample)
+        what = f"block decomposition (b={b})"
+    else:
+        r = oracle.decompose_seq(A, c["mu"], c["tau"], c["iters"], c["seed"], k=sample)
+        what = "sequential decomposition"
     dt = time.perf_counter() - t
     return {"value": round(sample / dt, 3), "unit": "components/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"first {sample} of {oracle.rank_for(A.shape[0], A.shape[1], c['mu'])} "
-                      f"components of the sequential decomposition of the same "
-                      f"{A.shape[0]}x{A.shape[1]} matrix, fp64 numpy oracle "
-                      f"({dt:.1f} s, E after sample {r.E:.4f})"}
+            "sample": f"first {sample} of {k_all} components of the {what} of the same "
+                      f"{m}x{n} matrix, fp64 numpy oracle ({dt:.1f} s, E after sample {r.E:.4f})"}
 
 
 def main():
@@ -242,6 +254,8 @@ def main():
     m, n = A.shape
     Ad = torch.from_numpy(A).cuda()
     k = trw.rank(m, n, c["mu"])
+    if args.modes is None:
+        args.modes = "block" if args.config == 3 else "seq,block"
     modes = [s for s in args.modes.split(",") if s]
     block = c.get("block", 64) or 64
     b = trw.block_width(m, n, block)
@@ -304,7 +318,14 @@ def main():
         bm = per_mode["block"]
         fl = block_alg_flops(m, n, k, b, c["iters"])
         bm["alg_tflops"] = fl / (bm["ms"] / 1e3) / 1e12
+        bm["alg_flops"] = fl
         bm["b"] = b
+        if roofline is None:
+            # block mode alone: its dense contractions on fp32 MFMA
+            roofline = {"bound": "mfma", "kernel": "block ALS pipeline",
+                        "achieved": round(bm["alg_tflops"], 3), "peak": FP32_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(bm["alg_tflops"] / FP32_PEAK_TFLOPS, 4),
+                        "traffic": None, "alg_flops_per_run": fl}
 
     inference = measure_inference(trw, outs, m, n)
     importance = None
@@ -323,7 +344,7 @@ def main():
 
     cpu = None
     if not args.no_cpu and args.cpu_sample > 0:
-        cpu = cpu_baseline(A, c, min(args.cpu_sample, k))
+        cpu = cpu_baseline(A, c, min(args.cpu_sample, k), 0 if "seq" in modes else block)
 
     line = {
         "metric": "ALS components/sec + achieved HBM GB/s at 2560x2560 mu=2 tau=0.7; energy E",
