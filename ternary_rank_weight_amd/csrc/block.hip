@@ -176,129 +176,161 @@ __global__ void k_gram_w_reduce(const double* __restrict__ Gpart, int splits, in
 constexpr int kCholT = 256;
 
 // In-place inverse of a symmetric positive definite matrix held in registers
-// by blocked Gauss-Jordan elimination in fp64, four pivots per step (no
-// pivoting: every 4 x 4 pivot block of the Schur complements of an SPD matrix
-// is SPD).  With K the pivot rows and R the rest, one step maps
-//   A_KK -> P = A_KK^-1,   A_KR -> P A_KR,   A_RK -> -A_RK P,
-//   A_RR -> A_RR - (A_RK P) A_KR.
-// Thread (ti, tj) of a 16 x 16 grid keeps entries (ti + 16x, tj + 16y);
-// entries from bb up to 16 NA must hold the identity, so a trailing partial
-// pivot block stays invertible and decoupled.  The owners of the pivot rows
-// and columns publish them in LDS (double-buffered, so one barrier per step
-// suffices) with the K x K part zeroed, and every thread inverts the 4 x 4
-// pivot block itself.  Returns false (the same in every thread) when a pivot
-// is not positive, i.e. when the matrix is not positive definite.
+// by the block sweep operator in fp64, four pivots per step (no pivoting:
+// every 4 x 4 pivot block of the Schur complements of an SPD matrix is SPD).
+// With K the pivot rows and R the rest, one step maps
+//   A_KK -> -P,  P = A_KK^-1,   A_KR -> P A_KR,   A_RK -> A_RK P,
+//   A_RR -> A_RR - (A_RK P) A_KR,
+// which keeps the matrix symmetric; after every block has been swept it
+// holds -A^-1, negated at the end.  Because of the symmetry only the pivot
+// rows are published: column j of them is also row j of the pivot columns.
+// Thread (ti, tj) of a 16 x 16 grid keeps the NA x NA block of entries
+// (NA ti + x, NA tj + y) (gj_index); entries from bb up to 16 NA must hold
+// the identity, so a trailing partial pivot block stays invertible and
+// decoupled.  The pivot rows of a step are rows 4h .. 4h + 3 of thread row
+// q; the step loop runs over q with h unrolled, so every register index is a
+// constant.  The owners publish the pivot rows in LDS (double-buffered, so
+// one barrier per step suffices) with the K x K part zeroed, and every
+// thread inverts the 4 x 4 pivot block itself.  The pivot rows then go
+// through the same rank-4 update as the rest, with w = I - P in place of
+// A_RK P, which turns A_KR into P A_KR.  Returns false (the same in every
+// thread) when a pivot is not positive, i.e. when the matrix is not positive
+// definite.
 struct GjShared {
-  double prow[2][kMaxB][4];   // prow[j][l] = A[K_l][j], zero for j in K
-  double pcol[2][kMaxB][4];   // pcol[i][l] = A[i][K_l], zero for i in K
-  double pkk[2][4][4];        // A_KK
+  double prow[2][kMaxB / 16][16][4];   // prow[y][tj][l] = A[K_l][NA tj + y], zero for columns in K
+  double pkk[2][4][4];                 // A_KK
 };
 
-template <int NA>  // bb <= 16 * NA
-__device__ bool gj_inverse(double (&a)[NA][NA], int bb, GjShared& sh) {
+template <int NA>
+__device__ inline int gj_index(int tq, int x) { return NA * tq + x; }
+
+// The 4 x 4 inverse of a symmetric positive definite block by Gauss-Jordan;
+// reciprocals by rcp and two Newton steps.  ok is cleared on a non-positive
+// pivot.
+__device__ inline void gj_inverse4(double (&p)[4][4], bool& ok) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double piv = p[q][q];
+    ok = ok && (piv > 0.0);
+    double ip = __builtin_amdgcn_rcp(piv);
+    double e = fma(-piv, ip, 1.0);
+    ip = fma(ip, e, ip);
+    e = fma(-piv, ip, 1.0);
+    ip = fma(ip, e, ip);
+    double rq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rq[c] = (c == q) ? ip : p[q][c] * ip;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r == q) continue;
+      const double f = p[r][q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p[r][c] = (c == q) ? -f * ip : fma(-f, rq[c], p[r][c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p[q][c] = rq[c];
+  }
+}
+
+// One sweep step on the pivot rows 4h .. 4h + 3 of thread row q.  prow is
+// laid out [y][tj][l], so the 16 threads of a row group read consecutive
+// 32-byte rows.
+template <int NA, int H>
+__device__ __forceinline__ void gj_step(double (&a)[NA][NA], int q, int bf, GjShared& sh, bool& ok) {
   const int t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
-  const int kq_r = ti >> 2, la = ti & 3;   // rows of a wave form one pivot quad
-  const int kq_c = tj >> 2, lc = tj & 3;
-  bool ok = true;
-  int step = 0;
+  const bool rown = ti == q, cown = tj == q;
+  if (rown) {
 #pragma unroll
-  for (int kx = 0; kx < NA; ++kx) {
-    for (int kq = 0; kq < 4; ++kq, ++step) {
-      if (16 * kx + 4 * kq >= bb) break;   // uniform
-      const int bf = step & 1;
-      const bool rown = kq_r == kq;          // wave-uniform
-      const bool cown = kq_c == kq;
-      if (rown) {
+    for (int y = 0; y < NA; ++y)
 #pragma unroll
-        for (int y = 0; y < NA; ++y) sh.prow[bf][tj + 16 * y][la] = (y == kx && cown) ? 0.0 : a[kx][y];
-        if (cown) sh.pkk[bf][la][lc] = a[kx][kx];
-      }
-      if (cown) {
+      for (int l = 0; l < 4; ++l)
+        sh.prow[bf][y][tj][l] = (cown && y / 4 == H) ? 0.0 : a[4 * H + l][y];
+    if (cown) {
 #pragma unroll
-        for (int x = 0; x < NA; ++x) sh.pcol[bf][ti + 16 * x][lc] = (x == kx && rown) ? 0.0 : a[x][kx];
-      }
-      __syncthreads();
-      // P = A_KK^-1 in registers; reciprocals by rcp and two Newton steps
-      double p[4][4];
+      for (int l = 0; l < 4; ++l)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sh.pkk[bf][l][c] = a[4 * H + l][4 * H + c];
+    }
+  }
+  __syncthreads();
+  double p[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p[r][c] = sh.pkk[bf][r][c];
+  gj_inverse4(p, ok);
+  // w = A_RK P from the published rows (A_RK = A_KR^T; zero on the pivot
+  // rows); independent products side by side
+  double w[NA][4];
+#pragma unroll
+  for (int x = 0; x < NA; ++x) {
+    const double c0 = sh.prow[bf][x][ti][0];
+#pragma unroll
+    for (int l = 0; l < 4; ++l) w[x][l] = c0 * p[0][l];
+  }
+#pragma unroll
+  for (int b = 1; b < 4; ++b)
+#pragma unroll
+    for (int x = 0; x < NA; ++x) {
+      const double cb = sh.prow[bf][x][ti][b];
+#pragma unroll
+      for (int l = 0; l < 4; ++l) w[x][l] = fma(cb, p[b][l], w[x][l]);
+    }
+  // pivot columns become A_RK P and the pivot block -P; the rank-4 update
+  // leaves both as they are (prow is zero on the pivot columns)
+  if (cown) {
+#pragma unroll
+    for (int x = 0; x < NA; ++x) {
+      if (rown && x / 4 == H) continue;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) a[x][4 * H + l] = w[x][l];
+    }
+    if (rown) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) p[r][c] = sh.pkk[bf][r][c];
+        for (int c = 0; c < 4; ++c) a[4 * H + r][4 * H + c] = -p[r][c];
+    }
+  }
+  if (rown) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const double piv = p[q][q];
-        ok = ok && (piv > 0.0);
-        double ip = __builtin_amdgcn_rcp(piv);
-        double e = fma(-piv, ip, 1.0);
-        ip = fma(ip, e, ip);
-        e = fma(-piv, ip, 1.0);
-        ip = fma(ip, e, ip);
-        double rq[4];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) rq[c] = (c == q) ? ip : p[q][c] * ip;
+      for (int l = 0; l < 4; ++l) w[4 * H + r][l] = (r == l ? 1.0 : 0.0) - p[r][l];
+  }
+  // rank-4 update
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (r == q) continue;
-          const double f = p[r][q];
+  for (int y = 0; y < NA; ++y) {
+    double pr[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) p[r][c] = (c == q) ? -f * ip : fma(-f, rq[c], p[r][c]);
-        }
+    for (int l = 0; l < 4; ++l) pr[l] = sh.prow[bf][y][tj][l];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) p[q][c] = rq[c];
-      }
-      // w = A_RK P (zero on the pivot rows); rank-4 update of everything else
-      double w[NA][4], pr[NA][4];
+    for (int l = 0; l < 4; ++l)
 #pragma unroll
-      for (int x = 0; x < NA; ++x) {
-        double c4[4];
-#pragma unroll
-        for (int l = 0; l < 4; ++l) c4[l] = sh.pcol[bf][ti + 16 * x][l];
-#pragma unroll
-        for (int l = 0; l < 4; ++l) {
-          double s = c4[0] * p[0][l];
-#pragma unroll
-          for (int b = 1; b < 4; ++b) s = fma(c4[b], p[b][l], s);
-          w[x][l] = s;
-        }
-      }
-#pragma unroll
-      for (int y = 0; y < NA; ++y)
-#pragma unroll
-        for (int l = 0; l < 4; ++l) pr[y][l] = sh.prow[bf][tj + 16 * y][l];
-#pragma unroll
-      for (int x = 0; x < NA; ++x)
-#pragma unroll
-        for (int y = 0; y < NA; ++y) {
-          double s = a[x][y];
-#pragma unroll
-          for (int l = 0; l < 4; ++l) s = fma(-w[x][l], pr[y][l], s);
-          a[x][y] = s;
-        }
-      // pivot rows become P A_KR (P itself on the pivot block); pivot columns -w
-      if (rown) {
-        double pa[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) pa[b] = la == 0 ? p[0][b] : la == 1 ? p[1][b] : la == 2 ? p[2][b] : p[3][b];
-#pragma unroll
-        for (int y = 0; y < NA; ++y) {
-          double s = pa[0] * pr[y][0];
-#pragma unroll
-          for (int b = 1; b < 4; ++b) s = fma(pa[b], pr[y][b], s);
-          a[kx][y] = s;
-        }
-        if (cown) a[kx][kx] = lc == 0 ? pa[0] : lc == 1 ? pa[1] : lc == 2 ? pa[2] : pa[3];
-      }
-      if (cown) {
-#pragma unroll
-        for (int x = 0; x < NA; ++x) {
-          if (x == kx && rown) continue;
-          const double v = lc == 0 ? w[x][0] : lc == 1 ? w[x][1] : lc == 2 ? w[x][2] : w[x][3];
-          a[x][kx] = -v;
-        }
+      for (int x = 0; x < NA; ++x) a[x][y] = fma(-w[x][l], pr[l], a[x][y]);
+  }
+}
+
+template <int NA>  // bb <= 16 * NA, NA a multiple of 4
+__device__ bool gj_inverse(double (&a)[NA][NA], int bb, GjShared& sh) {
+  static_assert(NA % 4 == 0 && NA <= 8, "four-pivot sub-blocks, at most 128 x 128");
+  bool ok = true;
+  int step = 0;
+  for (int q = 0; q < 16 && NA * q < bb; ++q) {
+    gj_step<NA, 0>(a, q, step & 1, sh, ok);
+    ++step;
+    if constexpr (NA == 8) {
+      if (NA * q + 4 < bb) {   // uniform
+        gj_step<NA, 1>(a, q, step & 1, sh, ok);
+        ++step;
       }
     }
   }
+#pragma unroll
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NA; ++y) a[x][y] = -a[x][y];
   return ok;
 }
 
@@ -326,7 +358,7 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
   for (int x = 0; x < NA; ++x)
 #pragma unroll
     for (int y = 0; y < NA; ++y) {
-      const int i = ti + 16 * x, j = tj + 16 * y;
+      const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
       const bool in = i < bb && j < bb;
       a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
       if (in) consume_gram(G, i * bb + j);
@@ -344,71 +376,128 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
   for (int x = 0; x < NA; ++x)
 #pragma unroll
     for (int y = 0; y < NA; ++y)
-      if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
+      if (gj_index<NA>(ti, x) == gj_index<NA>(tj, y) && gj_index<NA>(ti, x) < bb) a[x][y] += eps;
   const bool ok = gj_inverse<NA>(a, bb, sh);
   if (!ok && t == 0) *fail = 1;
 #pragma unroll
   for (int x = 0; x < NA; ++x)
 #pragma unroll
     for (int y = 0; y < NA; ++y) {
-      const int i = ti + 16 * x, j = tj + 16 * y;
+      const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
       if (i < bb && j < bb) Ginv[i * bb + j] = (float)a[x][y];
     }
 }
 
 
 // ---------------------------------------------------------------------------
-// The two contractions.  A workgroup (4 waves) takes 64 outputs (columns of
-// R for P = U^T R, rows of R for Q = R V) and one split of the contracted
-// dimension, walked in chunks of 256: the chunk's 2-bit codes of all the
-// block's components are staged in LDS (double buffered, one barrier per
-// chunk), then 16 steps of 16 run fully unrolled, so every load of R is
-// independent and issued early.  Loads read clamped addresses and select 0
-// outside the matrix (no branches).  Each step issues NSUB x 4 MFMA
-// 16x16x4, interleaved over the NSUB component sub-tiles; ternary values are
-// decoded from the codes by two shifts (exact).  Components from bb up to
-// 16 NSUB have zero codes.
+// The two contractions, on bf16 MFMA (16x16x32) with exact fp32 inputs.  A
+// residual entry x is split as x = h + mid + lo, three bf16 numbers whose sum
+// is exact (each part keeps 8 significant bits of the 24: h is x with the
+// low 16 bits cleared, mid the same of x - h, lo what remains), and the
+// ternary factor is exact in bf16, so every product is exact and each of the
+// three MFMA passes accumulates in fp32, like an fp32 contraction.
+//
+// A workgroup (4 waves) takes 64 outputs (columns of R for P = U^T R, rows of
+// R for Q = R V) and one split of the contracted dimension, walked in chunks
+// of 64.  Per chunk the block's codes are decoded once into bf16 rows in LDS
+// (double buffered, one barrier per chunk), each wave loads its R values,
+// splits them, and runs 3 x NSUB MFMAs per 32-long slab, the ternary operand
+// read from LDS.  Loads read clamped addresses and select 0 outside the
+// matrix (no branches).  Components from bb up to 16 NSUB have zero codes.
 // ---------------------------------------------------------------------------
 constexpr int kCT = 256;
-constexpr int kChunk = 256;   // rows (or columns) per staged chunk
-constexpr int kCW = kChunk / 16;   // code words per component per chunk
+constexpr int kChunk = 256;    // splits of the contracted dimension are whole multiples of this when long enough
+constexpr int kAC = 64;        // rows (or columns) per staged chunk
+constexpr int kAS = kAC + 8;   // bf16 per staged component row (16 bytes of padding: conflict-free reads)
 
-__device__ inline float tdec(uint32_t word, int sh) { return (float)((int)(word << (30 - sh)) >> 30); }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Stage the code words [w0, w0 + kCW) of components 0 .. 16 NSUB - 1.
+__device__ inline f4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Decoded ternary rows of the chunk: a[buf][component][row in chunk].
 template <int NSUB>
-__device__ inline void stage_codes(uint32_t (*cs)[kCW + 1], const uint32_t* __restrict__ codes, int64_t wl,
-                                   int bb, int64_t w0) {
-  constexpr int kPer = (16 * NSUB * kCW + kCT - 1) / kCT;
-  uint32_t v[kPer];
+struct TernStage {
+  unsigned short a[2][16 * NSUB][kAS];
+};
+
+// The 16 2-bit codes of a word as 16 bf16 (two per dword).  For a code c in
+// {0, 1, 3}, c * 0x3F80 + (c & 2) * 0x80 is 0, 0x3F80 (+1) or 0xBF80 (-1);
+// the pair (c0, c1) is first spread to bits 0 and 16 by one multiply.
+__device__ inline void decode16(uint32_t w, uint32_t (&o)[8]) {
 #pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + kCT * p;
-    const int comp = e / kCW, w = e % kCW;
-    const bool ok = e < 16 * NSUB * kCW && comp < bb && w0 + w < wl;
-    const uint32_t x = codes[ok ? (int64_t)comp * wl + w0 + w : 0];
-    v[p] = ok ? x : 0u;
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t y = (w >> (4 * p)) & 0xFu;
+    const uint32_t z = (y * 0x4001u) & 0x30003u;
+    o[p] = z * 0x3F80u + (z & 0x20002u) * 0x80u;
   }
+}
+
+// Decode the code words [w0, w0 + 4) of components 0 .. 16 NSUB - 1.
+template <int NSUB>
+__device__ inline void stage_decode(TernStage<NSUB>& st, int buf, const uint32_t* __restrict__ codes, int64_t wl,
+                                    int bb, int64_t w0) {
+  constexpr int kWords = 16 * NSUB * (kAC / 16);
+  for (int e = threadIdx.x; e < kWords; e += kCT) {
+    const int comp = e / (kAC / 16), wi = e % (kAC / 16);
+    const bool ok = comp < bb && w0 + wi < wl;
+    const uint32_t x = codes[ok ? (int64_t)comp * wl + w0 + wi : 0];
+    uint32_t o[8];
+    decode16(ok ? x : 0u, o);
+    u32x4* dst = reinterpret_cast<u32x4*>(&st.a[buf][comp][wi * 16]);
+    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+// x = h + mid + lo exactly, as three bf16x8 operands.
+__device__ inline void split3(const float (&x)[8], bf16x8& h, bf16x8& mid, bf16x8& lo) {
+  uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + kCT * p;
-    if (e < 16 * NSUB * kCW) cs[e / kCW][e % kCW] = v[p];
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u0 = __float_as_uint(x[2 * p]), u1 = __float_as_uint(x[2 * p + 1]);
+    const float r0 = x[2 * p] - __uint_as_float(u0 & 0xFFFF0000u);
+    const float r1 = x[2 * p + 1] - __uint_as_float(u1 & 0xFFFF0000u);
+    const uint32_t v0 = __float_as_uint(r0), v1 = __float_as_uint(r1);
+    const float l0 = r0 - __uint_as_float(v0 & 0xFFFF0000u);
+    const float l1 = r1 - __uint_as_float(v1 & 0xFFFF0000u);
+    hw[p] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // the high halves of u0, u1
+    mw[p] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+    lw[p] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+  }
+  h = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+  mid = __builtin_bit_cast(bf16x8, u32x4{mw[0], mw[1], mw[2], mw[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+}
+
+// The 3 NSUB MFMAs of one 32-long slab: the ternary operand of lane
+// (i + 16 g) is component 16 sub + i at positions 8 g .. 8 g + 7 of the slab.
+template <int NSUB>
+__device__ inline void slab_mfma(const TernStage<NSUB>& st, int buf, int slab, int i, int g, const float (&x)[8],
+                                 f4 (&acc)[NSUB]) {
+  bf16x8 h, mid, lo;
+  split3(x, h, mid, lo);
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st.a[buf][16 * sub + i][32 * slab + 8 * g]);
+    acc[sub] = mfma16x16x32bf16(a, h, acc[sub]);
+    acc[sub] = mfma16x16x32bf16(a, mid, acc[sub]);
+    acc[sub] = mfma16x16x32bf16(a, lo, acc[sub]);
   }
 }
 
 // Pt_part[split][i][c] = sum over the split's rows r of U[r][i] R[r][c].
-// Wave w owns columns 64 bx + 16 w + j (j = lane % 16); lane (j + 16k) feeds
-// row 16 step + k + 4q at MFMA q of a step to both operands.
-template <int NSUB>
-using CodeStage = uint32_t[2][16 * NSUB][kCW + 1];
-
+// Wave w owns columns 64 bx + 16 w + j (j = lane % 16); lane (j + 16 g)
+// supplies rows 8 g .. 8 g + 7 of each slab of its column.
 template <int NSUB>
 __device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, int64_t m, int64_t n,
                                    const uint32_t* __restrict__ Ucodes, int64_t wm, int bb,
                                    int64_t rows_per_split, float* __restrict__ Pt_part, int bx, int by,
-                                   CodeStage<NSUB>& cs) {
+                                   TernStage<NSUB>& st) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j = lane & 15, k = lane >> 4;
+  const int j = lane & 15, g = lane >> 4;
   const int64_t col = (int64_t)bx * 64 + 16 * w + j;
   const bool colok = col < n;
   const float* Rc = R + (colok ? col : 0);
@@ -418,54 +507,45 @@ __device__ __forceinline__ void contract_ut_r_body(const float* __restrict__ R, 
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
   int buf = 0;
-  for (int64_t cb = r_begin; cb < r_end; cb += kChunk, buf ^= 1) {
-    stage_codes<NSUB>(cs[buf], Ucodes, wm, bb, cb >> 4);
-    __syncthreads();
+  for (int64_t cb = r_begin; cb < r_end; cb += kAC, buf ^= 1) {
+    float xv[kAC / 32][8];
 #pragma unroll
-    for (int st = 0; st < kCW; ++st) {
-      float bv[4];
+    for (int s = 0; s < kAC / 32; ++s)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = cb + 16 * st + k + 4 * q;
+      for (int e = 0; e < 8; ++e) {
+        const int64_t row = cb + 32 * s + 8 * g + e;
         const bool ok = row < r_end && colok;
         const float x = Rc[(ok ? row : r_begin) * n];
-        bv[q] = ok ? x : 0.f;
+        xv[s][e] = ok ? x : 0.f;
       }
-      uint32_t cw[NSUB];
+    stage_decode<NSUB>(st, buf, Ucodes, wm, bb, cb >> 4);
+    __syncthreads();
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) cw[s] = cs[buf][16 * s + j][st];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x4(tdec(cw[s], 2 * (k + 4 * q)), bv[q], acc[s]);
-      }
-    }
+    for (int s = 0; s < kAC / 32; ++s) slab_mfma<NSUB>(st, buf, s, j, g, xv[s], acc);
   }
-  // D[i][c]: lane holds components 16 s + 4 k + v, column j
+  // D[i][c]: lane holds components 16 s + 4 g + v, column j
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int comp = 16 * s + 4 * k + v;
+      const int comp = 16 * s + 4 * g + v;
       if (comp < bb && colok) Pt_part[((int64_t)by * bb + comp) * n + col] = acc[s][v];
     }
   }
 }
 
-
 // Qt_part[split][i][r] = sum over the split's columns c of R[r][c] V[c][i]
-// (with W: R[r][c] wt[c] V[c][i], §2.5).  Wave w owns rows 64 bx + 16 w + i
-// (i = lane % 16); lane (i + 16k) loads R[row][16 step + 4k .. + 3] as one
-// float4 and feeds column 4k + q at MFMA q of a step; the V operand of lane
-// (comp + 16k) uses the same column.
+// (with W: fl(R[r][c] wt[c]) V[c][i], §2.5).  Wave w owns rows
+// 64 bx + 16 w + j (j = lane % 16); lane (j + 16 g) loads columns
+// 8 g .. 8 g + 7 of each slab of its row as two float4.
 template <int NSUB, bool W>
 __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, int64_t m, int64_t n,
                                   const uint32_t* __restrict__ Vcodes, int64_t wn, int bb,
                                   int64_t cols_per_split, float* __restrict__ Qt_part, int bx, int by,
-                                  const float* __restrict__ wt, CodeStage<NSUB>& cs) {
+                                  const float* __restrict__ wt, TernStage<NSUB>& st) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = lane & 15, k = lane >> 4;
-  const int64_t row = (int64_t)bx * 64 + 16 * w + i;
+  const int j = lane & 15, g = lane >> 4;
+  const int64_t row = (int64_t)bx * 64 + 16 * w + j;
   const bool rowok = row < m;
   const float* Rr = R + (rowok ? row : 0) * n;
   const int64_t c_begin = (int64_t)by * cols_per_split;
@@ -475,58 +555,48 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
   int buf = 0;
-  for (int64_t cb = c_begin; cb < c_end; cb += kChunk, buf ^= 1) {
-    stage_codes<NSUB>(cs[buf], Vcodes, wn, bb, cb >> 4);
-    __syncthreads();
+  for (int64_t cb = c_begin; cb < c_end; cb += kAC, buf ^= 1) {
+    float xv[kAC / 32][8];
 #pragma unroll
-    for (int st = 0; st < kCW; ++st) {
-      const int64_t cc = cb + 16 * st + 4 * k;
-      float av[4], wq[4];
-      if (vec_ok && cc + 3 < c_end) {
-        const float4 x = *reinterpret_cast<const float4*>(Rr + cc);
-        av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+    for (int s = 0; s < kAC / 32; ++s) {
+      const int64_t cc = cb + 32 * s + 8 * g;
+      if (vec_ok && cc + 7 < c_end) {
+        const float4 x0 = *reinterpret_cast<const float4*>(Rr + cc);
+        const float4 x1 = *reinterpret_cast<const float4*>(Rr + cc + 4);
+        xv[s][0] = x0.x; xv[s][1] = x0.y; xv[s][2] = x0.z; xv[s][3] = x0.w;
+        xv[s][4] = x1.x; xv[s][5] = x1.y; xv[s][6] = x1.z; xv[s][7] = x1.w;
         if constexpr (W) {
-          const float4 y = *reinterpret_cast<const float4*>(wt + cc);
-          wq[0] = y.x; wq[1] = y.y; wq[2] = y.z; wq[3] = y.w;
+          const float4 y0 = *reinterpret_cast<const float4*>(wt + cc);
+          const float4 y1 = *reinterpret_cast<const float4*>(wt + cc + 4);
+          xv[s][0] *= y0.x; xv[s][1] *= y0.y; xv[s][2] *= y0.z; xv[s][3] *= y0.w;
+          xv[s][4] *= y1.x; xv[s][5] *= y1.y; xv[s][6] *= y1.z; xv[s][7] *= y1.w;
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool ok = cc + q < c_end;
-          const float x = Rr[ok ? cc + q : c_begin];
-          av[q] = ok ? x : 0.f;
-          if constexpr (W) {
-            const float y = wt[ok ? cc + q : c_begin];
-            wq[q] = ok ? y : 0.f;
-          }
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = cc + e < c_end;
+          float x = Rr[ok ? cc + e : c_begin];
+          if constexpr (W) x *= wt[ok ? cc + e : c_begin];
+          xv[s][e] = ok ? x : 0.f;
         }
       }
       if (!rowok) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = 0.f;
-      }
-      uint32_t cw[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) cw[s] = cs[buf][16 * s + i][st];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          float bv = tdec(cw[s], 2 * (4 * k + q));
-          if constexpr (W) bv *= wq[q];
-          acc[s] = mfma16x16x4(av[q], bv, acc[s]);
-        }
+        for (int e = 0; e < 8; ++e) xv[s][e] = 0.f;
       }
     }
+    stage_decode<NSUB>(st, buf, Vcodes, wn, bb, cb >> 4);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kAC / 32; ++s) slab_mfma<NSUB>(st, buf, s, j, g, xv[s], acc);
   }
-  // D[row][comp]: lane holds rows 4 (lane / 16) + v of the wave's 16, column comp = 16 s + i
+  // D[i][r]: lane holds components 16 s + 4 g + v, row 64 bx + 16 w + j
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    const int comp = 16 * s + i;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t rr = (int64_t)bx * 64 + 16 * w + 4 * k + v;
-      if (comp < bb && rr < m) Qt_part[((int64_t)by * bb + comp) * m + rr] = acc[s][v];
+      const int comp = 16 * s + 4 * g + v;
+      if (comp < bb && rowok) Qt_part[((int64_t)by * bb + comp) * m + row] = acc[s][v];
     }
   }
 }
@@ -770,12 +840,12 @@ constexpr unsigned kGramSpinLimit = 1u << 22;
 template <int NSUB>
 union HalfStepLds {
   NsShared ns;
-  CodeStage<NSUB> cs;
+  TernStage<NSUB> cs;
   uint32_t rows[32][kGramChunk + 1];
 };
 template <>
 union HalfStepLds<8> {   // b > 64: the Gauss-Jordan body brings its own LDS
-  CodeStage<8> cs;
+  TernStage<8> cs;
   uint32_t rows[32][kGramChunk + 1];
 };
 
@@ -1074,7 +1144,7 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     for (int x = 0; x < NA; ++x)
 #pragma unroll
       for (int y = 0; y < NA; ++y) {
-        const int i = ti + 16 * x, j = tj + 16 * y;
+        const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
         const bool in = i < bb && j < bb;
         a[x][y] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
                      : (i == j ? 1.0 : 0.0);
@@ -1094,7 +1164,7 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
       for (int x = 0; x < NA; ++x)
 #pragma unroll
         for (int y = 0; y < NA; ++y)
-          if (ti + 16 * x == tj + 16 * y && ti + 16 * x < bb) a[x][y] += eps;
+          if (gj_index<NA>(ti, x) == gj_index<NA>(tj, y) && gj_index<NA>(ti, x) < bb) a[x][y] += eps;
     }
     ok = gj_inverse<NA>(a, bb, sh);
     __syncthreads();
@@ -1106,12 +1176,12 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     double s = 0.0;
 #pragma unroll
     for (int y = 0; y < NA; ++y) {
-      const int j = tj + 16 * y;
+      const int j = gj_index<NA>(tj, y);
       if (j < bb) s = fma(a[x][y], rhs[j], s);
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-    const int i = ti + 16 * x;
+    const int i = gj_index<NA>(ti, x);
     if (tj == 0 && i < bb) dsol[i] = s;
   }
   __syncthreads();
