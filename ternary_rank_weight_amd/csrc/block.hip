@@ -175,195 +175,188 @@ __global__ void k_gram_w_reduce(const double* __restrict__ Gpart, int splits, in
 // ---------------------------------------------------------------------------
 constexpr int kCholT = 256;
 
-// In-place inverse of a symmetric positive definite matrix held in registers
-// by the block sweep operator in fp64, four pivots per step (no pivoting:
-// every 4 x 4 pivot block of the Schur complements of an SPD matrix is SPD).
-// With K the pivot rows and R the rest, one step maps
+// Inverse of a symmetric positive definite matrix (b <= 16 T) on one
+// workgroup of 4 waves, by the block sweep operator in fp64 with 16 x 16
+// pivot blocks and fp64 MFMA (16x16x4) updates.  One step on the pivot
+// block K (R the rest) maps
 //   A_KK -> -P,  P = A_KK^-1,   A_KR -> P A_KR,   A_RK -> A_RK P,
 //   A_RR -> A_RR - (A_RK P) A_KR,
 // which keeps the matrix symmetric; after every block has been swept it
-// holds -A^-1, negated at the end.  Because of the symmetry only the pivot
-// rows are published: column j of them is also row j of the pivot columns.
-// Thread (ti, tj) of a 16 x 16 grid keeps the NA x NA block of entries
-// (NA ti + x, NA tj + y) (gj_index); entries from bb up to 16 NA must hold
-// the identity, so a trailing partial pivot block stays invertible and
-// decoupled.  The pivot rows of a step are rows 4h .. 4h + 3 of thread row
-// q; the step loop runs over q with h unrolled, so every register index is a
-// constant.  The owners publish the pivot rows in LDS (double-buffered, so
-// one barrier per step suffices) with the K x K part zeroed, and every
-// thread inverts the 4 x 4 pivot block itself.  The pivot rows then go
-// through the same rank-4 update as the rest, with w = I - P in place of
-// A_RK P, which turns A_KR into P A_KR.  Returns false (the same in every
-// thread) when a pivot is not positive, i.e. when the matrix is not positive
-// definite.
-struct GjShared {
-  double prow[2][kMaxB / 16][16][4];   // prow[y][tj][l] = A[K_l][NA tj + y], zero for columns in K
-  double pkk[2][4][4];                 // A_KK
+// holds -A^-1, negated at the end.  No pivoting is needed: every pivot block
+// of the Schur complements of an SPD matrix is SPD.
+//
+// Layout: the matrix is a T x T grid of 16 x 16 tiles in the fp64 MFMA
+// accumulator layout (lane j + 16 g, register v holds row g + 4 v, column j
+// of the tile); wave w keeps the tile rows w, w + 4 (acc[r][J] is tile
+// (w + 4 r, J)).  Entries from b up to 16 T must hold the identity.  Per
+// step the owner of tile row K publishes it in LDS; every wave inverts A_KK
+// itself (sweep16), and by the symmetry of P and of the matrix the MFMA
+// operands come straight from P's registers and the published row:
+//   W^T = P A_KI  (its registers are the A operand of the update),
+//   W = A_IK P    (the new tile A_IK),
+//   A_IJ -= W A_KJ for J != K,  and for the pivot row itself
+//   A_KJ -= (I - P) A_KJ, i.e. A_KJ -> P A_KJ.
+// ok is cleared (uniformly) when a pivot is not positive, i.e. when the
+// matrix is not positive definite.
+// ---------------------------------------------------------------------------
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+template <int T>
+struct SweepShared {
+  double prow[16][16 * T + 2];   // the published tile row (rows of the pivot block)
 };
 
-template <int NA>
-__device__ inline int gj_index(int tq, int x) { return NA * tq + x; }
+__device__ inline d4 mfma16x16x4f64(double a, double b, d4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+__device__ inline double bpermute_f64(int src_lane, double v) {
+  const int a = src_lane << 2;
+  const int lo = __builtin_amdgcn_ds_bpermute(a, __double2loint(v));
+  const int hi = __builtin_amdgcn_ds_bpermute(a, __double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+__device__ inline double readlane_f64(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
 
-// The 4 x 4 inverse of a symmetric positive definite block by Gauss-Jordan;
-// reciprocals by rcp and two Newton steps.  ok is cleared on a non-positive
-// pivot.
-__device__ inline void gj_inverse4(double (&p)[4][4], bool& ok) {
+// Sweep of a 16 x 16 SPD tile inside one wave, pivot by pivot (reciprocals
+// by rcp and two Newton steps; the pivot row comes from the lane group that
+// holds it, the pivot column from the same row by symmetry).  Leaves -A^-1.
+__device__ inline void sweep16(d4& p, bool& ok) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const double piv = p[q][q];
-    ok = ok && (piv > 0.0);
-    double ip = __builtin_amdgcn_rcp(piv);
-    double e = fma(-piv, ip, 1.0);
-    ip = fma(ip, e, ip);
-    e = fma(-piv, ip, 1.0);
-    ip = fma(ip, e, ip);
-    double rq[4];
+  for (int pp = 0; pp < 16; ++pp) {
+    const int gp = pp & 3, vp = pp >> 2;
+    const double app = readlane_f64(p[vp], pp + 16 * gp);
+    ok = ok && (app > 0.0);
+    double inv = __builtin_amdgcn_rcp(app);
+    double e = fma(-app, inv, 1.0);
+    inv = fma(inv, e, inv);
+    e = fma(-app, inv, 1.0);
+    inv = fma(inv, e, inv);
+    const double rj = bpermute_f64(j + 16 * gp, p[vp]);   // A[pp][j]
+    double ci[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rq[c] = (c == q) ? ip : p[q][c] * ip;
+    for (int v = 0; v < 4; ++v) ci[v] = bpermute_f64(g + 4 * v + 16 * gp, p[vp]);   // A[pp][g + 4v]
+    const double rjs = rj * inv;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r == q) continue;
-      const double f = p[r][q];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) p[r][c] = (c == q) ? -f * ip : fma(-f, rq[c], p[r][c]);
+    for (int v = 0; v < 4; ++v) {
+      const int i = g + 4 * v;
+      const double sc = ci[v] * inv;
+      double nv = fma(-sc, rj, p[v]);
+      nv = (j == pp) ? sc : nv;
+      nv = (i == pp) ? rjs : nv;
+      nv = (i == pp && j == pp) ? -inv : nv;
+      p[v] = nv;
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) p[q][c] = rq[c];
   }
 }
 
-// One sweep step on the pivot rows 4h .. 4h + 3 of thread row q.  prow is
-// laid out [y][tj][l], so the 16 threads of a row group read consecutive
-// 32-byte rows.
-template <int NA, int H>
-__device__ __forceinline__ void gj_step(double (&a)[NA][NA], int q, int bf, GjShared& sh, bool& ok) {
-  const int t = threadIdx.x;
-  const int ti = t >> 4, tj = t & 15;
-  const bool rown = ti == q, cown = tj == q;
-  if (rown) {
-#pragma unroll
-    for (int y = 0; y < NA; ++y)
-#pragma unroll
-      for (int l = 0; l < 4; ++l)
-        sh.prow[bf][y][tj][l] = (cown && y / 4 == H) ? 0.0 : a[4 * H + l][y];
-    if (cown) {
-#pragma unroll
-      for (int l = 0; l < 4; ++l)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sh.pkk[bf][l][c] = a[4 * H + l][4 * H + c];
-    }
-  }
-  __syncthreads();
-  double p[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) p[r][c] = sh.pkk[bf][r][c];
-  gj_inverse4(p, ok);
-  // w = A_RK P from the published rows (A_RK = A_KR^T; zero on the pivot
-  // rows); independent products side by side
-  double w[NA][4];
-#pragma unroll
-  for (int x = 0; x < NA; ++x) {
-    const double c0 = sh.prow[bf][x][ti][0];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) w[x][l] = c0 * p[0][l];
-  }
-#pragma unroll
-  for (int b = 1; b < 4; ++b)
-#pragma unroll
-    for (int x = 0; x < NA; ++x) {
-      const double cb = sh.prow[bf][x][ti][b];
-#pragma unroll
-      for (int l = 0; l < 4; ++l) w[x][l] = fma(cb, p[b][l], w[x][l]);
-    }
-  // pivot columns become A_RK P and the pivot block -P; the rank-4 update
-  // leaves both as they are (prow is zero on the pivot columns)
-  if (cown) {
-#pragma unroll
-    for (int x = 0; x < NA; ++x) {
-      if (rown && x / 4 == H) continue;
-#pragma unroll
-      for (int l = 0; l < 4; ++l) a[x][4 * H + l] = w[x][l];
-    }
-    if (rown) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) a[4 * H + r][4 * H + c] = -p[r][c];
-    }
-  }
-  if (rown) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int l = 0; l < 4; ++l) w[4 * H + r][l] = (r == l ? 1.0 : 0.0) - p[r][l];
-  }
-  // rank-4 update
-#pragma unroll
-  for (int y = 0; y < NA; ++y) {
-    double pr[4];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) pr[l] = sh.prow[bf][y][tj][l];
-#pragma unroll
-    for (int l = 0; l < 4; ++l)
-#pragma unroll
-      for (int x = 0; x < NA; ++x) a[x][y] = fma(-w[x][l], pr[l], a[x][y]);
-  }
-}
-
-template <int NA>  // bb <= 16 * NA, NA a multiple of 4
-__device__ bool gj_inverse(double (&a)[NA][NA], int bb, GjShared& sh) {
-  static_assert(NA % 4 == 0 && NA <= 8, "four-pivot sub-blocks, at most 128 x 128");
+template <int T>
+__device__ bool sweep_inverse(d4 (&acc)[(T + 3) / 4][T], int bb, SweepShared<T>& sh) {
+  constexpr int TR = (T + 3) / 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
   bool ok = true;
-  int step = 0;
-  for (int q = 0; q < 16 && NA * q < bb; ++q) {
-    gj_step<NA, 0>(a, q, step & 1, sh, ok);
-    ++step;
-    if constexpr (NA == 8) {
-      if (NA * q + 4 < bb) {   // uniform
-        gj_step<NA, 1>(a, q, step & 1, sh, ok);
-        ++step;
+  const int nK = (bb + 15) / 16;
+  for (int K = 0; K < nK; ++K) {
+    if (w == (K & 3)) {
+#pragma unroll
+      for (int r = 0; r < TR; ++r)
+        if (r == (K >> 2)) {
+#pragma unroll
+          for (int J = 0; J < T; ++J)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sh.prow[g + 4 * v][16 * J + j] = acc[r][J][v];
+        }
+    }
+    __syncthreads();
+    d4 p;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = sh.prow[g + 4 * v][16 * K + j];
+    sweep16(p, ok);
+    p = -p;   // P = A_KK^-1; by symmetry lane i + 16 k, register s also holds P[i][4 s + k]
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      const int I = w + 4 * r;
+      if (I >= T) continue;
+      if (I == K) {
+        double wa[4];   // -(I - P) as the A operand
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wa[q] = p[q] - (j == 4 * q + g ? 1.0 : 0.0);
+#pragma unroll
+        for (int J = 0; J < T; ++J) {
+          if (J == K) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[r][J] = mfma16x16x4f64(wa[q], sh.prow[4 * q + g][16 * J + j], acc[r][J]);
+        }
+#pragma unroll
+        for (int J = 0; J < T; ++J)
+          if (J == K) acc[r][J] = -p;
+      } else {
+        d4 wt = {0.0, 0.0, 0.0, 0.0}, wi = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const double ak = sh.prow[4 * q + g][16 * I + j];
+          wt = mfma16x16x4f64(p[q], ak, wt);   // W^T = P A_KI
+          wi = mfma16x16x4f64(ak, p[q], wi);   // W = A_IK P
+        }
+#pragma unroll
+        for (int J = 0; J < T; ++J) {
+          if (J == K) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[r][J] = mfma16x16x4f64(-wt[q], sh.prow[4 * q + g][16 * J + j], acc[r][J]);
+        }
+#pragma unroll
+        for (int J = 0; J < T; ++J)
+          if (J == K) acc[r][J] = wi;
       }
     }
+    __syncthreads();
   }
 #pragma unroll
-  for (int x = 0; x < NA; ++x)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-    for (int y = 0; y < NA; ++y) a[x][y] = -a[x][y];
+    for (int J = 0; J < T; ++J) acc[r][J] = -acc[r][J];
   return ok;
 }
 
+// Row and column of entry v of tile (w + 4 r, J) held by this lane.
+__device__ inline int sweep_row(int r, int v) { return 16 * ((threadIdx.x >> 6) + 4 * r) + ((threadIdx.x >> 4) & 3) + 4 * v; }
+__device__ inline int sweep_col(int J) { return 16 * J + (threadIdx.x & 15); }
+
 // Ginv = (G + eps I)^-1 with eps = 1e-6 trace(G)/b (fp64, written as fp32).
-// G is integer valued and is zeroed after being read so the next Gram
-// accumulation starts from zero.  `fail` is set if G + eps I is not positive
-// definite.  One workgroup.
-// G is an exact integer Gram (int, zeroed after reading so the next
+// G is an exact integer Gram (int, zeroed after being read so the next
 // accumulation starts from zero) or a weighted one (double, left as is).
+// `fail` is set if G + eps I is not positive definite.  One workgroup.
 template <typename GT>
 __device__ inline void consume_gram(GT* G, int e) {
   if constexpr (sizeof(GT) == sizeof(int)) G[e] = 0;
 }
 
-template <int NA, typename GT>  // bb <= 16 * NA
+template <int T, typename GT>  // bb <= 16 T
 __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ Ginv,
                                  int* __restrict__ fail) {
-  __shared__ GjShared sh;
+  constexpr int TR = (T + 3) / 4;
+  __shared__ SweepShared<T> sh;
   __shared__ double s_diag[kMaxB];
   __shared__ double s_eps;
-  const int t = threadIdx.x;
-  const int ti = t >> 4, tj = t & 15;
-  double a[NA][NA];
+  const int t = threadIdx.x, w = t >> 6;
+  d4 acc[TR][T];
 #pragma unroll
-  for (int x = 0; x < NA; ++x)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-    for (int y = 0; y < NA; ++y) {
-      const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
-      const bool in = i < bb && j < bb;
-      a[x][y] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
-      if (in) consume_gram(G, i * bb + j);
-      if (in && i == j) s_diag[i] = a[x][y];
-    }
+    for (int J = 0; J < T; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = sweep_row(r, v), j = sweep_col(J);
+        const bool in = w + 4 * r < T && i < bb && j < bb;
+        acc[r][J][v] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
+        if (in) consume_gram(G, i * bb + j);
+        if (in && i == j) s_diag[i] = acc[r][J][v];
+      }
   __syncthreads();
   if (t == 0) {
     double tr = 0.0;
@@ -373,19 +366,23 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
   __syncthreads();
   const double eps = s_eps;
 #pragma unroll
-  for (int x = 0; x < NA; ++x)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-    for (int y = 0; y < NA; ++y)
-      if (gj_index<NA>(ti, x) == gj_index<NA>(tj, y) && gj_index<NA>(ti, x) < bb) a[x][y] += eps;
-  const bool ok = gj_inverse<NA>(a, bb, sh);
+    for (int J = 0; J < T; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (sweep_row(r, v) == sweep_col(J) && sweep_col(J) < bb) acc[r][J][v] += eps;
+  const bool ok = sweep_inverse<T>(acc, bb, sh);
   if (!ok && t == 0) *fail = 1;
 #pragma unroll
-  for (int x = 0; x < NA; ++x)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-    for (int y = 0; y < NA; ++y) {
-      const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
-      if (i < bb && j < bb) Ginv[i * bb + j] = (float)a[x][y];
-    }
+    for (int J = 0; J < T; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = sweep_row(r, v), j = sweep_col(J);
+        if (w + 4 * r < T && i < bb && j < bb) Ginv[i * bb + j] = (float)acc[r][J][v];
+      }
 }
 
 
@@ -850,7 +847,7 @@ union HalfStepLds<8> {   // b > 64: the Gauss-Jordan body brings its own LDS
 };
 
 template <bool UT, bool W, int NSUB>
-__global__ __launch_bounds__(kCT) void k_contract_with_inverse(
+__global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k_contract_with_inverse(
     const float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ codes, int64_t wl,
     int bb, int64_t per_split, float* __restrict__ Part, void* __restrict__ G,
     float* __restrict__ Ginv, int* __restrict__ warm_flag, long long* __restrict__ stats,
@@ -1109,7 +1106,7 @@ __global__ __launch_bounds__(kTT) void k_row_project(const float* __restrict__ X
 // and the retry is counted.  d -> D[c0 + j]; ||R||^2 prediction -= d . rhs.
 // ---------------------------------------------------------------------------
 // GVw (optional): the weighted Gram V^T diag(wt) V in place of GV (§2.5).
-template <int NA>  // bb <= 16 * NA
+template <int T>  // bb <= 16 T
 __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, int* __restrict__ GV,
                                                         const double* __restrict__ GVw,
                                                         int bb, const double* __restrict__ rhs_in,
@@ -1120,14 +1117,14 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
                                                         int bstride, const double* __restrict__ dpart,
                                                         int64_t ndpart, const double* __restrict__ dold,
                                                         int* __restrict__ accept) {
-  __shared__ GjShared sh;
+  constexpr int TR = (T + 3) / 4;
+  __shared__ SweepShared<T> sh;
   __shared__ double rhs[kMaxB];
   __shared__ double dsol[kMaxB];
   __shared__ double s_diag[kMaxB];
   __shared__ double s_tr;
   __shared__ double red[kCholT / kWave];
-  const int t = threadIdx.x;
-  const int ti = t >> 4, tj = t & 15;
+  const int t = threadIdx.x, w = t >> 6;
   for (int j = t; j < bb; j += kCholT) rhs[j] = rhs_in[j];
   // sweep visit: the exact rise of ||R||^2 when the stored block was added back
   double added = 0.0;
@@ -1137,19 +1134,23 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     added = block_sum<kCholT>(p, red);
   }
   // M = (U^T U) o (V^T V); solve without a ridge, retry once with one
-  double a[NA][NA];
+  d4 acc[TR][T];
   bool ok = false;
-  for (int attempt = 0; attempt < 2 && !ok; ++attempt) {
 #pragma unroll
-    for (int x = 0; x < NA; ++x)
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (ok) break;   // uniform
 #pragma unroll
-      for (int y = 0; y < NA; ++y) {
-        const int i = gj_index<NA>(ti, x), j = gj_index<NA>(tj, y);
-        const bool in = i < bb && j < bb;
-        a[x][y] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
-                     : (i == j ? 1.0 : 0.0);
-        if (in && i == j) s_diag[i] = a[x][y];
-      }
+    for (int r = 0; r < TR; ++r)
+#pragma unroll
+      for (int J = 0; J < T; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = sweep_row(r, v), j = sweep_col(J);
+          const bool in = w + 4 * r < T && i < bb && j < bb;
+          acc[r][J][v] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
+                            : (i == j ? 1.0 : 0.0);
+          if (in && i == j) s_diag[i] = acc[r][J][v];
+        }
     __syncthreads();
     if (attempt == 1) {
       if (t == 0) {
@@ -1161,28 +1162,34 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
       __syncthreads();
       const double eps = 1e-6 * s_tr / bb;
 #pragma unroll
-      for (int x = 0; x < NA; ++x)
+      for (int r = 0; r < TR; ++r)
 #pragma unroll
-        for (int y = 0; y < NA; ++y)
-          if (gj_index<NA>(ti, x) == gj_index<NA>(tj, y) && gj_index<NA>(ti, x) < bb) a[x][y] += eps;
+        for (int J = 0; J < T; ++J)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (sweep_row(r, v) == sweep_col(J) && sweep_col(J) < bb) acc[r][J][v] += eps;
     }
-    ok = gj_inverse<NA>(a, bb, sh);
+    ok = sweep_inverse<T>(acc, bb, sh);
     __syncthreads();
   }
-  // d = M^-1 rhs: partial sums over this thread's columns, then over the 16
-  // lanes of its row group (xor butterfly, fixed order)
+  // d = M^-1 rhs: per lane the sum over its columns of every tile of the row,
+  // then over the 16 lanes of its group (xor butterfly, fixed order)
 #pragma unroll
-  for (int x = 0; x < NA; ++x) {
-    double s = 0.0;
+  for (int r = 0; r < TR; ++r) {
+    if (w + 4 * r >= T) continue;
 #pragma unroll
-    for (int y = 0; y < NA; ++y) {
-      const int j = gj_index<NA>(tj, y);
-      if (j < bb) s = fma(a[x][y], rhs[j], s);
+    for (int v = 0; v < 4; ++v) {
+      double s = 0.0;
+#pragma unroll
+      for (int J = 0; J < T; ++J) {
+        const int j = sweep_col(J);
+        if (j < bb) s = fma(acc[r][J][v], rhs[j], s);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+      const int i = sweep_row(r, v);
+      if ((t & 15) == 0 && i < bb) dsol[i] = s;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-    const int i = gj_index<NA>(ti, x);
-    if (tj == 0 && i < bb) dsol[i] = s;
   }
   __syncthreads();
   if (t == 0) {
@@ -1540,7 +1547,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     if (!W) hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
     int* acc = dpart ? accept : nullptr;
     const double* gvw = W ? GVw : nullptr;
-    if (bb <= 64)
+    if (bb <= 16)
+      hipLaunchKernelGGL(k_joint_solve<1>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+    else if (bb <= 32)
+      hipLaunchKernelGGL(k_joint_solve<2>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+    else if (bb <= 64)
       hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
     else
       hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
