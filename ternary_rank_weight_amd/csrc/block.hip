@@ -894,25 +894,26 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // ---------------------------------------------------------------------------
 // Decorrelated target: Xt[i][c] = sum_k Ginv[i][k] * (sum_s Part[s][k][c]).
-// grid ceil(L/16); 256 threads; Ginv and the summed 16-column tile in LDS.
-// Writes the plain sums too (Sum[k][c]) when `sum_out` is non-null.
+// grid ceil(L/DW), DW = 16 or 32 columns; 256 threads.  The split partials
+// are summed in split order into an LDS tile of bb x DW (rows bb .. up to a
+// multiple of 4 are zero), then the product runs on fp32 MFMA (16x16x4):
+// wave w takes the 16-row tiles w and w + 4 and every 16-column tile.  Ginv is symmetric, so
+// the A operand of lane (i + 16k), Ginv[16 I + i][4 s + k], is read as
+// Ginv[4 s + k][16 I + i]: 16 lanes read 64 contiguous bytes.  Writes the
+// plain sums too (Sum[k][c]) when `sum_out` is non-null.
 // ---------------------------------------------------------------------------
-constexpr int kDecW = 16;
-
+template <int kDecW>
 __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ Part, int S, int bb,
                                                      int64_t L, const float* __restrict__ Ginv,
                                                      float* __restrict__ Xt, float* __restrict__ sum_out) {
-  extern __shared__ float sm[];
-  float* Gs = sm;                   // bb * bb
-  float* Ps = sm + bb * bb;         // bb * kDecW
+  __shared__ float Ps[kMaxB][kDecW + 1];
   const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kDecW;
-#pragma unroll 8
-  for (int e = t; e < bb * bb; e += 256) Gs[e] = Ginv[e];
-  // the split sums, in split order; up to 8 splits of every entry of this
+  const int kb4 = (bb + 3) & ~3;
+  // the split sums, in split order; up to 8 splits of 4 entries of this
   // thread are loaded before any is added
   constexpr int kQ = 8;
-  for (int e0 = t; e0 < bb * kDecW; e0 += 4 * 256) {
+  for (int e0 = t; e0 < kb4 * kDecW; e0 += 4 * 256) {
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < S; q0 += kQ) {
       float v[4][kQ];
@@ -921,7 +922,7 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
         const int e = e0 + 256 * u;
         const int kk = e / kDecW, cc = e % kDecW;
         const int64_t c = c0 + cc;
-        const bool ok = e < bb * kDecW && c < L;
+        const bool ok = kk < bb && c < L;
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
           const bool okq = ok && q0 + q < S;
@@ -937,21 +938,45 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + 256 * u;
-      if (e < bb * kDecW) {
+      if (e < kb4 * kDecW) {
         const int kk = e / kDecW, cc = e % kDecW;
         const int64_t c = c0 + cc;
-        Ps[e] = s4[u];
-        if (sum_out && c < L) sum_out[(int64_t)kk * L + c] = s4[u];
+        Ps[kk][cc] = s4[u];
+        if (sum_out && kk < bb && c < L) sum_out[(int64_t)kk * L + c] = s4[u];
       }
     }
   }
   __syncthreads();
-  const int cc = t % kDecW;
-  const int64_t c = c0 + cc;
-  for (int i = t / kDecW; i < bb; i += 256 / kDecW) {
-    float s = 0.f;
-    for (int kk = 0; kk < bb; ++kk) s = fmaf(Gs[i * bb + kk], Ps[kk * kDecW + cc], s);
-    if (c < L) Xt[(int64_t)i * L + c] = s;
+  const int lane = t & 63, w = t >> 6;
+  const int j = lane & 15, k = lane >> 4;
+  const int rt = (bb + 15) / 16;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int I = w + 4 * r;
+    if (I >= rt) continue;   // uniform per wave
+    const int row = 16 * I + j;   // A operand row of this lane
+    constexpr int CT = kDecW / 16;
+    f4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < kb4; s0 += 4) {
+      const int kk = s0 + k;
+      const bool ok = kk < bb && row < bb;
+      const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
+      const float av = ok ? a : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x4(av, Ps[kk][16 * ct + j], acc[ct]);
+    }
+    // D[4k + v][j]: row 16 I + 4 k + v, column 16 ct + j
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int64_t c = c0 + 16 * ct + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * I + 4 * k + v;
+        if (i < bb && c < L) Xt[(int64_t)i * L + c] = acc[ct][v];
+      }
+    }
   }
 }
 
@@ -1406,6 +1431,16 @@ inline char* bump(char*& p, size_t bytes) {
 }
 
 
+// The decorrelation: 32-column tiles for b > 64 (the product dominates),
+// 16-column ones below (more workgroups for the split sums).
+inline void launch_decorrelate(int bb, hipStream_t s, const float* Part, int S, int64_t L, const float* Ginv,
+                               float* Xt, float* sum_out) {
+  if (bb > 64)
+    hipLaunchKernelGGL(k_decorrelate<32>, dim3((unsigned)((L + 31) / 32)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
+  else
+    hipLaunchKernelGGL(k_decorrelate<16>, dim3((unsigned)((L + 15) / 16)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
+}
+
 // The combined launch, by sub-tile count.  ngram Gram tiles
 // (0 when G is computed beforehand), one inverse, tiles x splits contraction
 // workgroups.
@@ -1488,7 +1523,6 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
-  const size_t dec_lds = sizeof(float) * (b * b + b * kDecW);
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
   if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 2, 0, s)) != hipSuccess) return e;
   const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
@@ -1525,7 +1559,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         gram_issued[0] += (unsigned long long)ng;
         launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, bb <= 64 ? warm : fail, st, (const float*)nullptr, gram_done, gram_issued[0]);
       }
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((n + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Pt_part, L.S1, bb, n, GinvU, Vt, (float*)nullptr);
+      launch_decorrelate(bb, s, Pt_part, L.S1, n, GinvU, Vt, (float*)nullptr);
       row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V;  weighted (§2.5):
       // Q = R diag(wt) V and the Gram V^T diag(wt) V
@@ -1538,7 +1572,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         gram_issued[1] += (unsigned long long)ng;
         launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
       }
-      hipLaunchKernelGGL(k_decorrelate, dim3((unsigned)((m + kDecW - 1) / kDecW)), dim3(256), dec_lds, s, Qt_part, L.S2, bb, m, GinvV, Ut, Qt);
+      launch_decorrelate(bb, s, Qt_part, L.S2, m, GinvV, Ut, Qt);
       row_tern(Ut, m, Uc, wm, nnz, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
     }
     // joint scales from the final U, V and the last Q = R V (weighted: the
