@@ -910,41 +910,40 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
   const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kDecW;
   const int kb4 = (bb + 3) & ~3;
-  // the split sums, in split order; up to 8 splits of 4 entries of this
-  // thread are loaded before any is added
-  constexpr int kQ = 8;
-  for (int e0 = t; e0 < kb4 * kDecW; e0 += 4 * 256) {
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int q0 = 0; q0 < S; q0 += kQ) {
-      float v[4][kQ];
+  // the split sums, in split order: every entry of this thread (E of them)
+  // loads QB splits before any is added
+  constexpr int E = kMaxB * kDecW / 256;
+  constexpr int QB = kDecW == 32 ? 4 : 8;
+  float acc_s[E];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + 256 * u;
-        const int kk = e / kDecW, cc = e % kDecW;
-        const int64_t c = c0 + cc;
-        const bool ok = kk < bb && c < L;
+  for (int u = 0; u < E; ++u) acc_s[u] = 0.f;
+  for (int q0 = 0; q0 < S; q0 += QB) {
+    float v[E][QB];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          const bool okq = ok && q0 + q < S;
-          const float x = Part[okq ? ((int64_t)(q0 + q) * bb + kk) * L + c : 0];
-          v[u][q] = okq ? x : 0.f;
-        }
-      }
+    for (int u = 0; u < E; ++u) {
+      const int e = t + 256 * u;
+      const int kk = e / kDecW, cc = e % kDecW;
+      const int64_t c = c0 + cc;
+      const bool ok = kk < bb && c < L;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) s4[u] += v[u][q];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + 256 * u;
-      if (e < kb4 * kDecW) {
-        const int kk = e / kDecW, cc = e % kDecW;
-        const int64_t c = c0 + cc;
-        Ps[kk][cc] = s4[u];
-        if (sum_out && kk < bb && c < L) sum_out[(int64_t)kk * L + c] = s4[u];
+      for (int q = 0; q < QB; ++q) {
+        const bool okq = ok && q0 + q < S;
+        const float x = Part[okq ? ((int64_t)(q0 + q) * bb + kk) * L + c : 0];
+        v[u][q] = okq ? x : 0.f;
       }
     }
+#pragma unroll
+    for (int u = 0; u < E; ++u)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) acc_s[u] += v[u][q];
+  }
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    const int e = t + 256 * u;
+    const int kk = e / kDecW, cc = e % kDecW;
+    const int64_t c = c0 + cc;
+    if (kk < kb4) Ps[kk][cc] = acc_s[u];
+    if (sum_out && kk < bb && c < L) sum_out[(int64_t)kk * L + c] = acc_s[u];
   }
   __syncthreads();
   const int lane = t & 63, w = t >> 6;
@@ -959,13 +958,20 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
     f4 acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < kb4; s0 += 4) {
-      const int kk = s0 + k;
+    // every A operand of the row tile first (at most kMaxB / 4 per lane)
+    float av[kMaxB / 4];
+#pragma unroll
+    for (int q = 0; q < kMaxB / 4; ++q) {
+      const int kk = 4 * q + k;
       const bool ok = kk < bb && row < bb;
       const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
-      const float av = ok ? a : 0.f;
+      av[q] = ok ? a : 0.f;
+    }
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x4(av, Ps[kk][16 * ct + j], acc[ct]);
+    for (int q = 0; q < kMaxB / 4; ++q) {
+      if (4 * q >= kb4) break;   // uniform
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x4(av[q], Ps[4 * q + k][16 * ct + j], acc[ct]);
     }
     // D[4k + v][j]: row 16 I + 4 k + v, column 16 ct + j
 #pragma unroll
