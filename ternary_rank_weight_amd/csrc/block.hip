@@ -1260,47 +1260,96 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
 }
 
 // ---------------------------------------------------------------------------
-// Rank-b deflation R <- R - U diag(d) V^T with fp32 MFMA (fp32 d; products
-// with ternary entries are exact, sums accumulate in fp32).  grid
-// (ceil(n/64), ceil(m/64)); wave w owns rows r0 + 16w .. +15 and four 16-wide
-// column sub-tiles; K runs over components in steps of 4.  With a negated d
-// the same kernel adds a block back.  When dpart is given, each workgroup
-// also writes the exact change of ||R||^2 over its tile (sum of new^2 - old^2
-// in fp64, fixed order; weighted by wt[col] when given) to dpart[tile].
+// Rank-b deflation R <- R - U diag(d) V^T on bf16 MFMA (16x16x32).  Each
+// fp32 scale is split exactly as d = h + mid + lo (three bf16, as in the
+// contractions), so every product of a ternary entry with a part is exact
+// and the three passes accumulate in fp32.  A workgroup takes a 64 x 64
+// tile: the block's codes for its rows (U) and columns (V) are decoded into
+// LDS once, U as bf16 [row][component] and V times each part of d as
+// [part][column][component], so the operands of lane (i + 16 g) are 8
+// consecutive components (16 bytes).  Wave w owns rows 16 w .. 16 w + 15 of
+// the tile and its four 16-column sub-tiles.  With a negated d the same
+// kernel adds a block back.  When dpart is given, each workgroup also writes
+// the exact change of ||R||^2 over its tile (sum of new^2 - old^2 in fp64,
+// fixed order; weighted by wt[col] when given) to dpart[tile].
 // ---------------------------------------------------------------------------
+constexpr int kDfS = kMaxB + 8;   // bf16 per staged row (16 bytes of padding: conflict-free reads)
+
+struct DeflateLds {
+  unsigned short u[64][kDfS];      // U[r0 + row][component]
+  unsigned short v[3][64][kDfS];   // part p of d times V[c0 + col][component]
+};
+
 __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, int64_t m, int64_t n,
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                        const double* __restrict__ d, int bb,
                                                        double* __restrict__ dpart, const float* __restrict__ wt) {
+  __shared__ DeflateLds st;
   __shared__ double red[256 / kWave];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = lane & 15, k = lane >> 4;
-  const int64_t r0 = (int64_t)blockIdx.y * 64 + 16 * w;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int kb = (bb + 31) & ~31;   // components padded to whole 32-long slabs (zero codes)
+  // stage: 4 code words (64 rows or columns) per component and side
+  for (int e = t; e < 2 * kb * 4; e += 256) {
+    const bool vside = e >= kb * 4;
+    const int ee = vside ? e - kb * 4 : e;
+    const int comp = ee >> 2, wi = ee & 3;
+    const int64_t w0 = (vside ? c0 : r0) / 16 + wi;
+    const int64_t wl = vside ? wn : wm;
+    const bool ok = comp < bb && w0 < wl;
+    const uint32_t x = (vside ? Vcodes : Ucodes)[ok ? (int64_t)comp * wl + w0 : 0];
+    uint32_t o[8];
+    decode16(ok ? x : 0u, o);
+    if (!vside) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        st.u[16 * wi + 2 * p][comp] = (unsigned short)(o[p] & 0xFFFFu);
+        st.u[16 * wi + 2 * p + 1][comp] = (unsigned short)(o[p] >> 16);
+      }
+    } else {
+      // the parts of d[comp] as bf16 bits (d = h + mid + lo exactly)
+      const float df = ok ? (float)d[comp] : 0.f;
+      const uint32_t u0 = __float_as_uint(df);
+      const float r1 = df - __uint_as_float(u0 & 0xFFFF0000u);
+      const uint32_t u1 = __float_as_uint(r1);
+      const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+      const uint32_t part[3] = {u0 >> 16, u1 >> 16, __float_as_uint(r2) >> 16};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t tv = (o[p] >> (16 * h)) & 0xFFFFu;   // 0, 0x3F80 or 0xBF80
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            st.v[q][16 * wi + 2 * p + h][comp] = (unsigned short)(tv ? (part[q] ^ (tv & 0x8000u)) : 0u);
+        }
+      }
+    }
+  }
+  __syncthreads();
   f4 acc[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
-  const int64_t arow = r0 + i;
-  for (int kc = 0; kc < bb; kc += 4) {
-    const int comp = kc + k;
-    const bool ok = comp < bb;
-    const float a = (ok && arow < m) ? tern(Ucodes + (int64_t)comp * wm, (int)arow) : 0.f;
-    const float dc = ok ? (float)d[comp] : 0.f;
+  for (int k0 = 0; k0 < kb; k0 += 32) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st.u[16 * w + i][k0 + 8 * g]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t col = c0 + 16 * s + i;
-      const float b = (ok && col < n) ? dc * tern(Vcodes + (int64_t)comp * wn, (int)col) : 0.f;
-      acc[s] = mfma16x16x4(a, b, acc[s]);
-    }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        acc[s] = mfma16x16x32bf16(a, *reinterpret_cast<const bf16x8*>(&st.v[q][16 * s + i][k0 + 8 * g]), acc[s]);
   }
+  // D[4g + v][i]: row r0 + 16 w + 4 g + v, column c0 + 16 s + i
   double change = 0.0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t col = c0 + 16 * s + i;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t row = r0 + 4 * k + v;
+      const int64_t row = r0 + 16 * w + 4 * g + v;
       if (row < m && col < n) {
         const float old = R[row * n + col];
         const float upd = old - acc[s][v];
