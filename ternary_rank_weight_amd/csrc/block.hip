@@ -9,9 +9,12 @@
 //   solve [(U^T U) o (V^T V)] d = diag(U^T R V)   (diag read off the last Q)
 //   R <- R - U diag(d) V^T           (MFMA rank-b update)
 // The Gram matrices of ternary factors are exact integers (popcounts of the
-// 2-bit codes); factorisations and solves run in fp64.  T_col applies the
-// mean-threshold ternarizer T_tau (§2.2) to each column.  U and V live as
-// 2-bit codes directly in their B2 / C2 output rows.
+// 2-bit codes).  The regularised Gram inverse is exact fp64 for b > 64 and
+// fp32 Newton-Schulz to 1e-4 below; the joint scale solve is fp64.  The
+// contractions and the deflation are fp32-accurate (exact products, fp32
+// sums) on bf16 MFMA.  T_col applies the mean-threshold ternarizer T_tau
+// (§2.2) to each column.  U and V live as 2-bit codes directly in their
+// B2 / C2 output rows.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "projection.hpp"
