@@ -39,7 +39,12 @@ def _factors(res):
 
 
 @pytest.mark.parametrize("m,n,mu,tau,b", [(256, 256, 1.0, 0.7, 32), (300, 200, 1.3, 1.0, 16),
-                                          (128, 512, 2.0, 2.0, 16)])
+                                          (128, 512, 2.0, 2.0, 16),
+                                          # b = 40: partial 16-component sub-tiles in the b <= 64 path
+                                          (320, 400, 0.5, 1.0, 40),
+                                          # b = 100 (k = 270: blocks of 100, 100 and 70) on a ragged
+                                          # shape: the fp64 sweep inverse with partial pivot tiles
+                                          (900, 1000, 0.3, 0.7, 100)])
 def test_block_small_vs_oracle(lib, m, n, mu, tau, b):
     A = synthetic.gaussian(m, n, 7)
     Ad = _dev(A)

@@ -25,7 +25,7 @@ def _factors(res):
 
 
 @pytest.mark.parametrize("m,n,mu,tau,b,sweeps", [(256, 256, 1.0, 0.7, 32, 3), (300, 200, 1.3, 1.0, 16, 2),
-                                                 (200, 180, 0.9, 0.7, 16, 2)])
+                                                 (200, 180, 0.9, 0.7, 16, 2), (900, 1000, 0.3, 0.7, 100, 1)])
 def test_sweeps_vs_oracle(lib, m, n, mu, tau, b, sweeps):
     A = synthetic.gaussian(m, n, 7)
     Ad = _dev(A)
