@@ -119,3 +119,27 @@ def test_block_config2_full(lib):
     B, C, D = _factors(res)
     assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
     assert abs(oracle.zero_fraction(B, C) - g["zero_fraction"]) < 0.01
+
+
+@pytest.mark.parametrize("m,n,b", [(600, 700, 48), (900, 1000, 100)])
+def test_block_first_half_step_vs_oracle(lib, m, n, b):
+    # One block, one iteration: the block's V codes are T_tau applied column by
+    # column to the decorrelated target [(U0^T U0 + eps I)^-1 U0^T A]^T of the
+    # seeded start U0 (§2.4), so they follow the GPU's contraction, Gram
+    # inverse and decorrelation at full size.  The GPU computes the target in
+    # fp32 (with a Newton-Schulz inverse to 1e-4 for b <= 64, an exact fp64
+    # one beyond); a code may differ only where the fp64 target sits that
+    # close to its column's threshold.
+    A = synthetic.gaussian(m, n, 11)
+    mu = (b + 0.25) / min(m, n)
+    assert oracle.rank_for(m, n, mu) == b
+    res = lib.decompose(_dev(A), mu, 0.7, 1, b, 5)
+    C = oracle.unpack2(res.C2.cpu().numpy().view(np.uint32), n)   # b x n
+    U0 = oracle.init_block(5, 0, b, m)
+    target = oracle.block_v_target(A.astype(np.float64), U0)       # n x b
+    ref = oracle.ternarize_columns(target, 0.7)
+    mism = C.T != ref
+    assert mism.sum() <= 1e-3 * mism.size, int(mism.sum())
+    for r, j in zip(*np.nonzero(mism)):
+        thr, _ = oracle.mean_abs_threshold(target[:, j], 0.7)
+        assert abs(abs(target[r, j]) - thr) <= 3e-4 * thr, (r, j, target[r, j], thr)
