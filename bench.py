@@ -59,9 +59,10 @@ def parse():
                     help="skip the block run with the optimal ternary projection")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3],
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
                     help="1: 256x256 Gaussian; 2: 2560x2560 LLM-shaped (default); "
-                         "3: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128")
+                         "3: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128; "
+                         "4: the seven matrices of one 4B-class layer, mu=2.5, block b=128, back to back")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
                          "exit; its HBM counters calibrate the per-kernel traffic figures")
@@ -235,6 +236,89 @@ def cpu_baseline(A, c, sample, block=0):
                       f"{m}x{n} matrix, fp64 numpy oracle ({dt:.1f} s, E after sample {r.E:.4f})"}
 
 
+def run_layer(args):
+    """The seven matrices of one transformer layer (q, k, v, o, gate, up,
+    down), decomposed back to back on one stream in block mode; a step is the
+    whole layer."""
+    import numpy as np
+    import torch
+    import synthetic
+    import ternary_rank_weight_amd as trw
+
+    torch.cuda.set_device(0)
+    c = synthetic.CONFIGS[4]
+    shapes = synthetic.layer_shapes()
+    host = {name: synthetic.config_matrix(4, name) for name, _, _ in shapes}
+    dev = {name: torch.from_numpy(A).cuda() for name, A in host.items()}
+    outs = {}
+
+    def step():
+        for name, _, _ in shapes:
+            outs[name] = trw.decompose(dev[name], c["mu"], c["tau"], c["iters"], c["block"], c["seed"],
+                                       stats=True, out=outs.get(name))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        ev.append((e0, e1))
+        print("[bench] layer launched", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    per = {}
+    total_k = 0
+    flops = 0.0
+    for name, m, n in shapes:
+        k = trw.rank(m, n, c["mu"])
+        b = trw.block_width(m, n, c["block"])
+        total_k += k
+        fl = block_alg_flops(m, n, k, b, c["iters"])
+        flops += fl
+        per[name] = {"m": m, "n": n, "k": k, "b": b, "energy": round(float(outs[name].energy.item()), 6),
+                     "alg_tflop": round(fl / 1e12, 3)}
+    tflops = flops / (ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu and args.cpu_sample > 0:
+        cpu = cpu_baseline(host["q"], c, min(args.cpu_sample, trw.rank(4096, 2560, c["mu"])), c["block"])
+        cpu["sample"] += " (the layer's q matrix)"
+    line = {
+        "metric": "ALS components/sec + achieved HBM GB/s at 2560x2560 mu=2 tau=0.7; energy E",
+        "value": round(total_k / (ms / 1e3), 2),
+        "unit": "components/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "one 4B-class transformer layer as 7 LLM-shaped synthetic matrices "
+                               "(q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728), "
+                               f"mu={c['mu']}, tau={c['tau']}, {c['iters']} iterations, block ALS b={c['block']}, "
+                               "back to back on one stream; step = the whole layer",
+                   "mu": c["mu"], "tau": c["tau"], "iters": c["iters"], "block": c["block"], "k_total": total_k,
+                   "seed": c["seed"]},
+        "matrices": per,
+        "roofline": {"bound": "mfma", "kernel": "block ALS pipeline", "achieved": round(tflops, 3),
+                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+                     "traffic": None, "alg_flops_per_step": flops},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,6 +326,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.config == 4:
+        run_layer(args)
         return
     import numpy as np
     import torch
