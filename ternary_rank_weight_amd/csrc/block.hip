@@ -344,10 +344,10 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
                                  int* __restrict__ fail) {
   constexpr int TR = (T + 3) / 4;
   __shared__ SweepShared<T> sh;
-  __shared__ double s_diag[kMaxB];
-  __shared__ double s_eps;
+  __shared__ double red[kCholT / kWave];
   const int t = threadIdx.x, w = t >> 6;
   d4 acc[TR][T];
+  double diag = 0.0;   // this lane's diagonal entries (integer valued when G is: any order is exact)
 #pragma unroll
   for (int r = 0; r < TR; ++r)
 #pragma unroll
@@ -358,16 +358,9 @@ __device__ __forceinline__ void spd_inverse_body(GT* __restrict__ G, int bb, flo
         const bool in = w + 4 * r < T && i < bb && j < bb;
         acc[r][J][v] = in ? (double)G[i * bb + j] : (i == j ? 1.0 : 0.0);
         if (in) consume_gram(G, i * bb + j);
-        if (in && i == j) s_diag[i] = acc[r][J][v];
+        if (in && i == j) diag += acc[r][J][v];
       }
-  __syncthreads();
-  if (t == 0) {
-    double tr = 0.0;
-    for (int i = 0; i < bb; ++i) tr += s_diag[i];
-    s_eps = 1e-6 * tr / bb;
-  }
-  __syncthreads();
-  const double eps = s_eps;
+  const double eps = 1e-6 * block_sum<kCholT>(diag, red) / bb;
 #pragma unroll
   for (int r = 0; r < TR; ++r)
 #pragma unroll
