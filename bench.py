@@ -57,6 +57,8 @@ def parse():
                     help="skip the importance-weighted runs")
     ap.add_argument("--no-projection", dest="projection", action="store_false",
                     help="skip the block run with the optimal ternary projection")
+    ap.add_argument("--no-streaming", dest="streaming", action="store_false",
+                    help="skip the streaming-versus-resident comparison of the sequential mode")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
@@ -209,6 +211,32 @@ def measure_projection(trw, Ad, c, block):
     torch.cuda.synchronize()
     return {"mode": f"block ALS b={trw.block_width(Ad.shape[0], Ad.shape[1], block)}",
             "ms": round(e0.elapsed_time(e1), 3), "energy": round(float(r.energy.item()), 6)}
+
+
+def measure_streaming(trw, Ad, c, k=256):
+    """The sequential decomposition's first k components in the streaming
+    mode (R in HBM, a few kernels per half-step) and in the resident mode, on
+    the same matrix: event times, components/s and the algorithmic bytes rate
+    of each (the same byte model as the roofline)."""
+    import torch
+    m, n = Ad.shape
+    mu = (k + 0.25) / min(m, n)
+    out = {"components": k}
+    for name, mode in (("streaming", trw.MODE_STREAMING), ("resident", trw.MODE_RESIDENT)):
+        trw.decompose(Ad, mu, c["tau"], c["iters"], 0, c["seed"], mode=mode)   # warm
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = trw.decompose(Ad, mu, c["tau"], c["iters"], 0, c["seed"], mode=mode, stats=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        alg = seq_alg_bytes(m, n, k, r.stat("iterations") or k * c["iters"], r.stat("sum_nnz_u"))
+        gbps = alg / (ms / 1e3) / 1e9
+        out[name] = {"ms": round(ms, 3), "components_per_s": round(k / (ms / 1e3), 1),
+                     "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                     "energy": round(float(r.energy.item()), 6)}
+    return out
 
 
 def cpu_baseline(A, c, sample, block=0):
@@ -423,6 +451,10 @@ def main():
     if "block" in per_mode and args.projection:
         print("[bench] projection", file=sys.stderr, flush=True)
         projection = measure_projection(trw, Ad, c, block)
+    streaming = None
+    if "seq" in per_mode and args.streaming:
+        print("[bench] streaming", file=sys.stderr, flush=True)
+        streaming = measure_streaming(trw, Ad, c)
     sweeps = None
     if "block" in per_mode and args.sweeps > 0:
         print("[bench] sweeps", file=sys.stderr, flush=True)
@@ -460,6 +492,7 @@ def main():
         "sweeps": sweeps,
         "importance_weighted": importance,
         "optimal_projection": projection,
+        "seq_streaming_vs_resident": streaming,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
