@@ -65,11 +65,12 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s);
 int64_t gemv_t_chunks(int64_t m);
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
                             long long* fallbacks, hipStream_t s, const float* wt = nullptr,
-                            double* wsum = nullptr);
+                            double* wsum = nullptr, long long* nnz_sum = nullptr);
 // Optimal ternary projection of one vector (§2.2), 1 <= N <= kProjMaxN.
 constexpr int kProjMaxN = 16384;   // longest vector it takes (128 KB of sort keys in LDS)
 hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
-                          hipStream_t s, const float* wt = nullptr, double* wsum = nullptr);
+                          hipStream_t s, const float* wt = nullptr, double* wsum = nullptr,
+                          long long* nnz_sum = nullptr);
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
                          const uint32_t* vprev, hipStream_t s);

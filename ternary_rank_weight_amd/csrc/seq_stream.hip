@@ -22,8 +22,10 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
                                                       int32_t* __restrict__ nnz_out,
                                                       long long* __restrict__ fallbacks,
                                                       const float* __restrict__ wt,
-                                                      double* __restrict__ wsum) {
-  // wsum (with wt): sum of wt over the kept entries, i.e. v^T diag(wt) v (§2.5)
+                                                      double* __restrict__ wsum,
+                                                      long long* __restrict__ nnz_sum) {
+  // wsum (with wt): sum of wt over the kept entries, i.e. v^T diag(wt) v (§2.5);
+  // nnz_sum (optional) accumulates the nonzero count (one workgroup, stream order)
   __shared__ double scratch[kTernT / kWave];
   float* fs = reinterpret_cast<float*>(scratch);
   int* is = reinterpret_cast<int*>(scratch);
@@ -36,6 +38,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
     for (int64_t w = tid; w < words; w += kTernT) codes[w] = (w == 0) ? 1u : 0u;
     if (tid == 0) {
       if (nnz_out) *nnz_out = 1;
+      if (nnz_sum) *nnz_sum += 1;
       if (wsum) *wsum = (double)wt[0];
       if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
     }
@@ -70,6 +73,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
       if (tid == 0) *wsum = wt_total;
     }
     if (tid == 0 && nnz_out) *nnz_out = total;
+  if (tid == 0 && nnz_sum) *nnz_sum += total;
     return;
   }
   // Nothing passed: keep the smallest index holding the largest magnitude.
@@ -81,6 +85,7 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   if (tid == 0) {
     codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
     if (nnz_out) *nnz_out = 1;
+      if (nnz_sum) *nnz_sum += 1;
     if (wsum) *wsum = (double)wt[idx];
     if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
   }
@@ -95,7 +100,8 @@ template <int PMAX>
 __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x, int64_t N,
                                                     uint32_t* __restrict__ codes, int32_t* __restrict__ nnz_out,
                                                     long long* __restrict__ fallbacks,
-                                                    const float* __restrict__ wt, double* __restrict__ wsum) {
+                                                    const float* __restrict__ wt, double* __restrict__ wsum,
+                                                    long long* __restrict__ nnz_sum) {
   __shared__ uint64_t keys[PMAX];
   __shared__ ProjScratch sc;
   __shared__ double scratch[kTernT / kWave];
@@ -108,6 +114,7 @@ __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x,
     for (int64_t w = tid; w < words; w += kTernT) codes[w] = (w == 0) ? 1u : 0u;
     if (tid == 0) {
       if (nnz_out) *nnz_out = 1;
+      if (nnz_sum) *nnz_sum += 1;
       if (wsum) *wsum = (double)wt[0];
       if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
     }
@@ -137,6 +144,7 @@ __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x,
     if (tid == 0) *wsum = wt_total;
   }
   if (tid == 0 && nnz_out) *nnz_out = total;
+  if (tid == 0 && nnz_sum) *nnz_sum += total;
 }
 
 // ---------------------------------------------------------------------------
@@ -274,9 +282,6 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
   }
 }
 
-__global__ void k_add_stat(long long* stats, int idx, const int32_t* val) {
-  if (threadIdx.x == 0 && stats) stats[idx] += *val;
-}
 
 // ---------------------------------------------------------------------------
 // Squared Frobenius norm with a fixed reduction order, plus a count of
@@ -415,18 +420,19 @@ hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t
 }
 
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
-                            long long* fallbacks, hipStream_t s, const float* wt, double* wsum) {
-  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum);
+                            long long* fallbacks, hipStream_t s, const float* wt, double* wsum,
+                            long long* nnz_sum) {
+  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum, nnz_sum);
   return hipGetLastError();
 }
 
 hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
-                          hipStream_t s, const float* wt, double* wsum) {
+                          hipStream_t s, const float* wt, double* wsum, long long* nnz_sum) {
   if (N < 1 || N > kProjMaxN) return hipErrorInvalidValue;
   if (N <= 4096)
-    hipLaunchKernelGGL(k_project<4096>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum);
+    hipLaunchKernelGGL(k_project<4096>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum, nnz_sum);
   else
-    hipLaunchKernelGGL(k_project<kProjMaxN>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum);
+    hipLaunchKernelGGL(k_project<kProjMaxN>, dim3(1), dim3(kTernT), 0, s, x, N, codes, nnz, fallbacks, wt, wsum, nnz_sum);
   return hipGetLastError();
 }
 
@@ -576,15 +582,17 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
                         fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s);
       if (e != hipSuccess) return e;
       pending = false;
-      e = a.projection ? launch_project(y, n, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv)
-                       : launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv);
+      e = a.projection ? launch_project(y, n, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv,
+                                        st + EXTERND_STAT_SUM_NNZ_V)
+                       : launch_ternarize(y, n, a.tau, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv,
+                                          st + EXTERND_STAT_SUM_NNZ_V);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_V, nnz_v);
       if ((e = launch_gemv_n(R, m, n, vc, x, s, wt)) != hipSuccess) return e;
-      e = a.projection ? launch_project(x, m, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s)
-                       : launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s);
+      e = a.projection ? launch_project(x, m, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s, nullptr, nullptr,
+                                        st + EXTERND_STAT_SUM_NNZ_U)
+                       : launch_ternarize(x, m, a.tau, ub, nnz_u, st + EXTERND_STAT_FALLBACKS, s, nullptr, nullptr,
+                                          st + EXTERND_STAT_SUM_NNZ_U);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_add_stat, dim3(1), dim3(64), 0, s, st, (int)EXTERND_STAT_SUM_NNZ_U, nnz_u);
       if (cap) {
         if (a.capture_y && (e = launch_copy_f32(y, a.capture_y + (int64_t)t * n, n, s)) != hipSuccess) return e;
         if (a.capture_x && (e = launch_copy_f32(x, a.capture_x + (int64_t)t * m, m, s)) != hipSuccess) return e;
