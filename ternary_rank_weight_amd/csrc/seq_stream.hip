@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x,
 // R_rc <- fl32(R_rc - d u'_r v'_c), written back.
 // ---------------------------------------------------------------------------
 constexpr int kGtT = 256;     // columns per workgroup
-constexpr int kGtRows = 64;   // rows per chunk
+constexpr int kGtRows = 128;  // rows per chunk
 
 __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
@@ -192,12 +192,97 @@ __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
   if (incol) partial[(int64_t)blockIdx.y * n + c] = acc;
 }
 
+// The same partial products for n % 4 == 0, built for bandwidth: a
+// workgroup takes 256 columns (one float4 per lane) and the chunk's rows,
+// wave w the rows r0 + w + 4i.  The rows a wave needs (u_r != 0, or
+// u_prev_r != 0 for the fused deflation) are decided from its code words, and
+// their loads are issued 8 at a time before any is used; the four waves
+// sums are combined in LDS in wave order.
+constexpr int kGtBatch = 8;
+
+__global__ __launch_bounds__(256) void k_gemv_t_vec(
+    float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
+    float* __restrict__ partial, const float* __restrict__ dprev,
+    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev) {
+  __shared__ float4 red[3][kWave];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int64_t n4 = n >> 2;
+  const int64_t c4 = (int64_t)blockIdx.x * kWave + lane;   // float4 column
+  const bool incol = c4 < n4;
+  const int64_t r0 = (int64_t)blockIdx.y * kGtRows;
+  float4* R4 = reinterpret_cast<float4*>(R);
+  const float d = dprev ? *dprev : 0.f;
+  float vp[4] = {0.f, 0.f, 0.f, 0.f};
+  bool vany = false;
+  if (dprev && incol) {
+    const uint32_t word = vprev[c4 >> 2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vp[e] = value_of_code((word >> (8 * (c4 & 3) + 2 * e)) & 3u);
+      vany = vany || vp[e] != 0.f;
+    }
+  }
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < kGtRows / 4; i0 += kGtBatch) {
+    float4 v[kGtBatch];
+    float ur[kGtBatch], up[kGtBatch];
+#pragma unroll
+    for (int k = 0; k < kGtBatch; ++k) {
+      const int64_t r = r0 + w + 4 * (i0 + k);
+      const bool inrow = r < m;
+      const float uc = code_at(u_codes, inrow ? r : 0);
+      const float pc = dprev ? code_at(uprev, inrow ? r : 0) : 0.f;
+      ur[k] = inrow ? uc : 0.f;
+      up[k] = inrow ? pc : 0.f;
+      const bool need = incol && (ur[k] != 0.f || up[k] != 0.f);
+      const float4 x = R4[need ? r * n4 + c4 : 0];
+      v[k] = need ? x : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < kGtBatch; ++k) {
+      float4 val = v[k];
+      if (up[k] != 0.f && vany) {
+        val.x = vp[0] != 0.f ? fmaf(-d, up[k] * vp[0], val.x) : val.x;
+        val.y = vp[1] != 0.f ? fmaf(-d, up[k] * vp[1], val.y) : val.y;
+        val.z = vp[2] != 0.f ? fmaf(-d, up[k] * vp[2], val.z) : val.z;
+        val.w = vp[3] != 0.f ? fmaf(-d, up[k] * vp[3], val.w) : val.w;
+        R4[(r0 + w + 4 * (i0 + k)) * n4 + c4] = val;
+      }
+      acc.x = fmaf(ur[k], val.x, acc.x);
+      acc.y = fmaf(ur[k], val.y, acc.y);
+      acc.z = fmaf(ur[k], val.z, acc.z);
+      acc.w = fmaf(ur[k], val.w, acc.w);
+    }
+  }
+  if (w > 0) red[w - 1][lane] = acc;
+  __syncthreads();
+  if (w == 0 && incol) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const float4 o = red[q][lane];
+      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+    }
+    reinterpret_cast<float4*>(partial)[(int64_t)blockIdx.y * n4 + c4] = acc;
+  }
+}
+
 __global__ void k_sum_chunks(const float* __restrict__ partial, int64_t chunks, int64_t n,
                              float* __restrict__ y) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
+  // chunk order; eight loads in flight
   float acc = 0.f;
-  for (int64_t q = 0; q < chunks; ++q) acc += partial[q * n + c];
+  for (int64_t q0 = 0; q0 < chunks; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = q0 + k < chunks;
+      const float x = partial[ok ? (q0 + k) * n + c : c];
+      v[k] = ok ? x : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += v[k];
+  }
   y[c] = acc;
 }
 
@@ -221,6 +306,56 @@ __global__ __launch_bounds__(kGnT) void k_gemv_n(const float* __restrict__ R, in
   }
   acc = wave_sum(acc);
   if (lane == 0) x[row] = acc;
+}
+
+// The same for n % 4 == 0, built for bandwidth: lane l reads float4 column
+// l + 64 i of the row, 8 loads (and their code words) issued before any is
+// used; the four partial lanes of the float4 are added at the end.
+constexpr int kGnBatch = 8;
+
+template <bool W>
+__global__ __launch_bounds__(kGnT) void k_gemv_n_vec(const float* __restrict__ R, int64_t m,
+                                                     int64_t n, const uint32_t* __restrict__ v_codes,
+                                                     float* __restrict__ x, const float* __restrict__ wt) {
+  const int64_t row = (int64_t)blockIdx.x * (kGnT / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= m) return;
+  const int64_t n4 = n >> 2;
+  const float4* rp = reinterpret_cast<const float4*>(R + row * n);
+  const float4* w4 = reinterpret_cast<const float4*>(wt);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i0 = 0; i0 < n4; i0 += (int64_t)kWave * kGnBatch) {
+    float4 v[kGnBatch], ww[kGnBatch];
+    uint32_t cw[kGnBatch];
+#pragma unroll
+    for (int k = 0; k < kGnBatch; ++k) {
+      const int64_t i = i0 + lane + (int64_t)kWave * k;
+      const bool ok = i < n4;
+      const float4 a = rp[ok ? i : 0];
+      const uint32_t c = v_codes[ok ? i >> 2 : 0];
+      v[k] = ok ? a : float4{0.f, 0.f, 0.f, 0.f};
+      cw[k] = ok ? (c >> (8 * (i & 3))) & 0xFFu : 0u;
+      if constexpr (W) {
+        const float4 b = w4[ok ? i : 0];
+        ww[k] = b;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGnBatch; ++k) {
+      float t0 = value_of_code(cw[k] & 3u), t1 = value_of_code((cw[k] >> 2) & 3u);
+      float t2 = value_of_code((cw[k] >> 4) & 3u), t3 = value_of_code((cw[k] >> 6) & 3u);
+      if constexpr (W) {
+        t0 *= ww[k].x; t1 *= ww[k].y; t2 *= ww[k].z; t3 *= ww[k].w;
+      }
+      acc.x = fmaf(t0, v[k].x, acc.x);
+      acc.y = fmaf(t1, v[k].y, acc.y);
+      acc.z = fmaf(t2, v[k].z, acc.z);
+      acc.w = fmaf(t3, v[k].w, acc.w);
+    }
+  }
+  float sum = (acc.x + acc.y) + (acc.z + acc.w);
+  sum = wave_sum(sum);
+  if (lane == 0) x[row] = sum;
 }
 
 // R <- R - d u v^T (one rounding per entry), d read from device memory.
@@ -448,9 +583,14 @@ hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes
                          float* y, const float* dprev, const uint32_t* uprev,
                          const uint32_t* vprev, hipStream_t s) {
   const int64_t chunks = gemv_t_chunks(m);
-  dim3 grid((unsigned)((n + kGtT - 1) / kGtT), (unsigned)chunks);
-  hipLaunchKernelGGL(k_gemv_t_partial, grid, dim3(kGtT), 0, s, R, m, n, u_codes, partial, dprev,
-                     uprev, vprev);
+  if ((n & 3) == 0) {
+    dim3 grid((unsigned)((n / 4 + kWave - 1) / kWave), (unsigned)chunks);
+    hipLaunchKernelGGL(k_gemv_t_vec, grid, dim3(256), 0, s, R, m, n, u_codes, partial, dprev, uprev, vprev);
+  } else {
+    dim3 grid((unsigned)((n + kGtT - 1) / kGtT), (unsigned)chunks);
+    hipLaunchKernelGGL(k_gemv_t_partial, grid, dim3(kGtT), 0, s, R, m, n, u_codes, partial, dprev,
+                       uprev, vprev);
+  }
   hipLaunchKernelGGL(k_sum_chunks, dim3(grid1(n, 256, 1 << 30)), dim3(256), 0, s, partial, chunks,
                      n, y);
   return hipGetLastError();
@@ -460,7 +600,12 @@ hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v
                          hipStream_t s, const float* wt) {
   const unsigned rows_per_block = kGnT / kWave;
   dim3 grid((unsigned)((m + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL(k_gemv_n, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x, wt);
+  if ((n & 3) == 0 && wt)
+    hipLaunchKernelGGL(k_gemv_n_vec<true>, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x, wt);
+  else if ((n & 3) == 0)
+    hipLaunchKernelGGL(k_gemv_n_vec<false>, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x, wt);
+  else
+    hipLaunchKernelGGL(k_gemv_n, grid, dim3(kGnT), 0, s, R, m, n, v_codes, x, wt);
   return hipGetLastError();
 }
 
