@@ -91,6 +91,99 @@ __global__ __launch_bounds__(kTernT) void k_ternarize(const float* __restrict__ 
   }
 }
 
+// The same rule for N <= 256 K with the vector held in registers: one read of
+// x, and the codes packed from wave ballots (wave w of pass j covers entries
+// 256 j + 64 w .. + 63, i.e. code words 16 j + 4 w .. + 3).  Outputs as
+// k_ternarize.
+__device__ inline uint32_t spread_bits16(uint32_t v) {   // bit e -> bit 2e
+  v &= 0xffffu;
+  v = (v | (v << 8)) & 0x00FF00FFu;
+  v = (v | (v << 4)) & 0x0F0F0F0Fu;
+  v = (v | (v << 2)) & 0x33333333u;
+  v = (v | (v << 1)) & 0x55555555u;
+  return v;
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__ x, int64_t N, float tau,
+                                                       uint32_t* __restrict__ codes, int32_t* __restrict__ nnz_out,
+                                                       long long* __restrict__ fallbacks,
+                                                       const float* __restrict__ wt, double* __restrict__ wsum,
+                                                       long long* __restrict__ nnz_sum) {
+  constexpr int T = 256;
+  __shared__ double scratch[T / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  float v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = tid + (int64_t)T * j;
+    const float a = x[idx < N ? idx : 0];
+    v[j] = idx < N ? a : 0.f;
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  const float M = block_max<T>(mx, reinterpret_cast<float*>(scratch));
+  const int64_t words = (N + 15) / 16;
+  if (M == 0.f) {
+    for (int64_t q = tid; q < words; q += T) codes[q] = (q == 0) ? 1u : 0u;
+    if (tid == 0) {
+      if (nnz_out) *nnz_out = 1;
+      if (nnz_sum) *nnz_sum += 1;
+      if (wsum) *wsum = (double)wt[0];
+      if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
+    }
+    return;
+  }
+  const int s = fixed_point_shift(M, (int)N);
+  double q = 0.0;   // integer-valued partial sums below 2^52: exact in any order
+#pragma unroll
+  for (int j = 0; j < K; ++j) q += fixed_point_q(fabsf(v[j]), s);
+  const double thr = fixed_point_threshold(block_sum<T>(q, scratch), s, tau, N);
+  int cnt = 0;
+  double ws = 0.0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = tid + (int64_t)T * j;
+    const bool keep = idx < N && (double)fabsf(v[j]) > thr;
+    const unsigned long long nz = __ballot(keep);
+    const unsigned long long ng = __ballot(keep && v[j] < 0.f);
+    cnt += keep ? 1 : 0;
+    if (wsum && keep) ws += (double)wt[idx];
+    if (lane < 4) {
+      const int64_t wd = (int64_t)16 * j + 4 * w + lane;
+      if (wd < words)
+        codes[wd] = spread_bits16((uint32_t)(nz >> (16 * lane))) | (spread_bits16((uint32_t)(ng >> (16 * lane))) << 1);
+    }
+  }
+  if ((double)M > thr) {
+    const int total = block_sum<T>(cnt, reinterpret_cast<int*>(scratch));
+    if (wsum) {
+      const double wt_total = block_sum<T>(ws, scratch);
+      if (tid == 0) *wsum = wt_total;
+    }
+    if (tid == 0 && nnz_out) *nnz_out = total;
+    if (tid == 0 && nnz_sum) *nnz_sum += total;
+    return;
+  }
+  // Nothing passed: keep the smallest index holding the largest magnitude.
+  int first = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = tid + (int64_t)T * j;
+    if (idx < N && fabsf(v[j]) == M) first = min(first, (int)idx);
+  }
+  const int pick = block_min_i<T>(first, reinterpret_cast<int*>(scratch));
+  __syncthreads();  // the zero code words written above are visible block-wide below
+  if (tid == 0) {
+    codes[pick >> 4] = code_of(x[pick]) << (2 * (pick & 15));
+    if (nnz_out) *nnz_out = 1;
+    if (nnz_sum) *nnz_sum += 1;
+    if (wsum) *wsum = (double)wt[pick];
+    if (fallbacks) atomicAdd(reinterpret_cast<unsigned long long*>(fallbacks), 1ull);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The optimal ternary projection of one vector (§2.2) by a single workgroup,
 // the alternative to T_tau: same outputs (codes, nnz, fallback count for an
@@ -193,24 +286,38 @@ __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
 }
 
 // The same partial products for n % 4 == 0, built for bandwidth: a
-// workgroup takes 256 columns (one float4 per lane) and the chunk's rows,
-// wave w the rows r0 + w + 4i.  The rows a wave needs (u_r != 0, or
-// u_prev_r != 0 for the fused deflation) are decided from its code words, and
-// their loads are issued 8 at a time before any is used; the four waves
-// sums are combined in LDS in wave order.
-constexpr int kGtBatch = 8;
+// workgroup takes 256 columns (one float4 per lane) and the chunk's 128 rows,
+// wave w the rows r0 + w + 4i.  The chunk's code words are read first; then
+// every row load of the wave is issued before any is used, unconditionally
+// (a row the wave does not need reads row 0's entries and is multiplied by
+// u_r = 0), so no load waits on a branch.  The four waves' sums are combined
+// in LDS in wave order.
+constexpr int kGtWave = kGtRows / 4;   // rows per wave
 
 __global__ __launch_bounds__(256) void k_gemv_t_vec(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
     float* __restrict__ partial, const float* __restrict__ dprev,
     const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev) {
+  static_assert(kGtRows == 128, "eight code words per chunk");
   __shared__ float4 red[3][kWave];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int64_t n4 = n >> 2;
   const int64_t c4 = (int64_t)blockIdx.x * kWave + lane;   // float4 column
   const bool incol = c4 < n4;
+  const int64_t c4s = incol ? c4 : 0;
   const int64_t r0 = (int64_t)blockIdx.y * kGtRows;
+  const int64_t wm = (m + 15) >> 4;
   float4* R4 = reinterpret_cast<float4*>(R);
+  // the chunk's code words: rows r0 .. r0 + 127
+  uint32_t uw[8], pw[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t wi = (r0 >> 4) + q;
+    const uint32_t a = u_codes[wi < wm ? wi : 0];
+    const uint32_t b = dprev ? uprev[wi < wm ? wi : 0] : 0u;
+    uw[q] = wi < wm ? a : 0u;
+    pw[q] = wi < wm ? b : 0u;
+  }
   const float d = dprev ? *dprev : 0.f;
   float vp[4] = {0.f, 0.f, 0.f, 0.f};
   bool vany = false;
@@ -222,37 +329,33 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
       vany = vany || vp[e] != 0.f;
     }
   }
+  float4 v[kGtWave];
+  float ur[kGtWave], up[kGtWave];
+#pragma unroll
+  for (int k = 0; k < kGtWave; ++k) {
+    // row r0 + w + 4k: word k / 4 of the chunk, entry w + 4 (k % 4)
+    const int sh = 2 * (w + 4 * (k & 3));
+    ur[k] = value_of_code((uw[k >> 2] >> sh) & 3u);
+    up[k] = value_of_code((pw[k >> 2] >> sh) & 3u);
+    const int64_t r = r0 + w + 4 * k;
+    const bool need = r < m && (ur[k] != 0.f || up[k] != 0.f);
+    v[k] = R4[need ? r * n4 + c4s : c4s];
+  }
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; i0 < kGtRows / 4; i0 += kGtBatch) {
-    float4 v[kGtBatch];
-    float ur[kGtBatch], up[kGtBatch];
 #pragma unroll
-    for (int k = 0; k < kGtBatch; ++k) {
-      const int64_t r = r0 + w + 4 * (i0 + k);
-      const bool inrow = r < m;
-      const float uc = code_at(u_codes, inrow ? r : 0);
-      const float pc = dprev ? code_at(uprev, inrow ? r : 0) : 0.f;
-      ur[k] = inrow ? uc : 0.f;
-      up[k] = inrow ? pc : 0.f;
-      const bool need = incol && (ur[k] != 0.f || up[k] != 0.f);
-      const float4 x = R4[need ? r * n4 + c4 : 0];
-      v[k] = need ? x : float4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kGtWave; ++k) {
+    float4 val = v[k];
+    if (up[k] != 0.f && vany) {
+      val.x = vp[0] != 0.f ? fmaf(-d, up[k] * vp[0], val.x) : val.x;
+      val.y = vp[1] != 0.f ? fmaf(-d, up[k] * vp[1], val.y) : val.y;
+      val.z = vp[2] != 0.f ? fmaf(-d, up[k] * vp[2], val.z) : val.z;
+      val.w = vp[3] != 0.f ? fmaf(-d, up[k] * vp[3], val.w) : val.w;
+      R4[(r0 + w + 4 * k) * n4 + c4] = val;
     }
-#pragma unroll
-    for (int k = 0; k < kGtBatch; ++k) {
-      float4 val = v[k];
-      if (up[k] != 0.f && vany) {
-        val.x = vp[0] != 0.f ? fmaf(-d, up[k] * vp[0], val.x) : val.x;
-        val.y = vp[1] != 0.f ? fmaf(-d, up[k] * vp[1], val.y) : val.y;
-        val.z = vp[2] != 0.f ? fmaf(-d, up[k] * vp[2], val.z) : val.z;
-        val.w = vp[3] != 0.f ? fmaf(-d, up[k] * vp[3], val.w) : val.w;
-        R4[(r0 + w + 4 * (i0 + k)) * n4 + c4] = val;
-      }
-      acc.x = fmaf(ur[k], val.x, acc.x);
-      acc.y = fmaf(ur[k], val.y, acc.y);
-      acc.z = fmaf(ur[k], val.z, acc.z);
-      acc.w = fmaf(ur[k], val.w, acc.w);
-    }
+    acc.x = fmaf(ur[k], val.x, acc.x);
+    acc.y = fmaf(ur[k], val.y, acc.y);
+    acc.z = fmaf(ur[k], val.z, acc.z);
+    acc.w = fmaf(ur[k], val.w, acc.w);
   }
   if (w > 0) red[w - 1][lane] = acc;
   __syncthreads();
@@ -270,18 +373,18 @@ __global__ void k_sum_chunks(const float* __restrict__ partial, int64_t chunks, 
                              float* __restrict__ y) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= n) return;
-  // chunk order; eight loads in flight
+  // chunk order; 32 loads in flight
   float acc = 0.f;
-  for (int64_t q0 = 0; q0 < chunks; q0 += 8) {
-    float v[8];
+  for (int64_t q0 = 0; q0 < chunks; q0 += 32) {
+    float v[32];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 32; ++k) {
       const bool ok = q0 + k < chunks;
       const float x = partial[ok ? (q0 + k) * n + c : c];
       v[k] = ok ? x : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc += v[k];
+    for (int k = 0; k < 32; ++k) acc += v[k];
   }
   y[c] = acc;
 }
@@ -557,7 +660,12 @@ hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t
 hipError_t launch_ternarize(const float* x, int64_t N, float tau, uint32_t* codes, int32_t* nnz,
                             long long* fallbacks, hipStream_t s, const float* wt, double* wsum,
                             long long* nnz_sum) {
-  hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum, nnz_sum);
+  if (N <= 1024)
+    hipLaunchKernelGGL(k_ternarize_reg<4>, dim3(1), dim3(256), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum, nnz_sum);
+  else if (N <= 4096)
+    hipLaunchKernelGGL(k_ternarize_reg<16>, dim3(1), dim3(256), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum, nnz_sum);
+  else
+    hipLaunchKernelGGL(k_ternarize, dim3(1), dim3(kTernT), 0, s, x, N, tau, codes, nnz, fallbacks, wt, wsum, nnz_sum);
   return hipGetLastError();
 }
 
