@@ -821,7 +821,7 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
 //                     added into G with atomics; each then bumps *gram_done
 //                     (release);
 //   ngram             the inverse of G' (weighted: G given): Newton-Schulz up
-//                     to b = 64, fp64 Gauss-Jordan beyond,
+//                     to b = 64, the fp64 MFMA block sweep beyond,
 //                     after *gram_done has reached gram_target (acquire; a
 //                     bounded wait, counted in stats[TIMEOUTS] if it runs out);
 //   the rest          the contraction, (bx, by) = (c % tiles, c / tiles).
@@ -837,7 +837,7 @@ union HalfStepLds {
   uint32_t rows[32][kGramChunk + 1];
 };
 template <>
-union HalfStepLds<8> {   // b > 64: the Gauss-Jordan body brings its own LDS
+union HalfStepLds<8> {   // b > 64: the sweep inverse brings its own LDS
   TernStage<8> cs;
   uint32_t rows[32][kGramChunk + 1];
 };
@@ -874,7 +874,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       __syncthreads();
     }
-    if constexpr (NSUB == 8) {   // b > 64: Gauss-Jordan in fp64; *warm_flag gets 1 if G' is not SPD
+    if constexpr (NSUB == 8) {   // b > 64: the fp64 sweep; *warm_flag gets 1 if G' is not SPD
       if constexpr (W) spd_inverse_body<8, double>(static_cast<double*>(G), bb, Ginv, warm_flag);
       else spd_inverse_body<8, int>(static_cast<int*>(G), bb, Ginv, warm_flag);
     } else {
@@ -1601,9 +1601,9 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
     for (int it = 0; it < a.iters; ++it) {
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
-      // inverse depend only on U's codes: up to b = 64 the inverse (Newton-
-      // Schulz) runs as one extra workgroup of the contraction launch,
-      // concurrently with it; wider blocks invert by Gauss-Jordan first.
+      // inverse depend only on U's codes, so they run as the first
+      // workgroups of the contraction launch, concurrently with it
+      // (Newton-Schulz up to b = 64, the fp64 sweep beyond).
       {
         // the Gram of U is computed inside the launch, ahead of its inverse
         const int ng = (int)(gram_u.x * gram_u.y);
