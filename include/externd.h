@@ -68,11 +68,12 @@ enum externd_stat {
   EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
   EXTERND_STAT_TIMEOUTS = 9,    /* waits that ran out (energy is NaN): resident exchange, or
                                    block mode's Gram-before-inverse wait */
-  EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode: Gram inverses whose Newton-Schulz
-                                    iteration stopped before reaching its tolerance */
+  EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode, b <= 64: Gram inverses whose Newton-
+                                    Schulz iteration stopped before reaching its tolerance
+                                    (wider blocks invert exactly in fp64: always 0) */
   EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
-  EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode: Newton-Schulz steps over all Gram inverses */
-  EXTERND_STAT_NS_RESTARTS = 13,    /* block mode: warm starts replaced by another start */
+  EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode, b <= 64: Newton-Schulz steps over all Gram inverses */
+  EXTERND_STAT_NS_RESTARTS = 13,    /* block mode, b <= 64: warm starts replaced by another start */
   EXTERND_STAT_ITERATIONS = 14,     /* ALS iterations run, over all components (blocks) */
   EXTERND_STATS_LEN = 16
 };
