@@ -1064,6 +1064,103 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
   }
 }
 
+// The same for rows of L <= 512 K with the row held in registers: one read of
+// the row, and the codes packed from wave ballots (wave w of pass j covers
+// entries 512 j + 64 w .. + 63, i.e. code words 32 j + 4 w .. + 3).
+__device__ inline uint32_t spread_bits16(uint32_t v) {   // bit e -> bit 2e
+  v &= 0xffffu;
+  v = (v | (v << 8)) & 0x00FF00FFu;
+  v = (v | (v << 4)) & 0x0F0F0F0Fu;
+  v = (v | (v << 2)) & 0x33333333u;
+  v = (v | (v << 1)) & 0x55555555u;
+  return v;
+}
+
+template <int K>
+__global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restrict__ Xt, int64_t L, float tau,
+                                                           uint32_t* __restrict__ out_codes, int64_t wl,
+                                                           int* __restrict__ nnz, long long* __restrict__ fb,
+                                                           long long* __restrict__ nnz_sum,
+                                                           const float* __restrict__ Qrows,
+                                                           double* __restrict__ rhs_out) {
+  __shared__ double scratch[kTT / kWave];
+  const int i = blockIdx.x;
+  const float* x = Xt + (int64_t)i * L;
+  const float* qr = rhs_out ? Qrows + (int64_t)i * L : nullptr;
+  uint32_t* codes = out_codes + (int64_t)i * wl;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  float v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = t + (int64_t)kTT * j;
+    const float a = x[idx < L ? idx : 0];
+    v[j] = idx < L ? a : 0.f;
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  const float M = block_max<kTT>(mx, reinterpret_cast<float*>(scratch));
+  if (M == 0.f) {
+    for (int64_t q = t; q < wl; q += kTT) codes[q] = (q == 0) ? 1u : 0u;
+    if (t == 0) {
+      if (rhs_out) rhs_out[i] = (double)qr[0];
+      nnz[i] = 1;
+      atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+      atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
+    }
+    return;
+  }
+  const int s = fixed_point_shift(M, (int)L);
+  double q = 0.0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) q += fixed_point_q(fabsf(v[j]), s);
+  const double thr = fixed_point_threshold(block_sum<kTT>(q, scratch), s, tau, L);
+  const uint32_t tb = threshold_bits(thr);
+  int cnt = 0;
+  double rq = 0.0;   // u_i . q_i over this thread's kept entries (joint scale rhs)
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = t + (int64_t)kTT * j;
+    const bool keep = idx < L && (__float_as_uint(v[j]) & 0x7fffffffu) > tb;
+    const unsigned long long nz = __ballot(keep);
+    const unsigned long long ng = __ballot(keep && v[j] < 0.f);
+    cnt += keep ? 1 : 0;
+    if (qr && keep) rq += v[j] > 0.f ? (double)qr[idx] : -(double)qr[idx];
+    if (lane < 4) {
+      const int64_t wd = (int64_t)32 * j + 4 * w + lane;
+      if (wd < wl)
+        codes[wd] = spread_bits16((uint32_t)(nz >> (16 * lane))) | (spread_bits16((uint32_t)(ng >> (16 * lane))) << 1);
+    }
+  }
+  if (__float_as_uint(M) > tb) {
+    const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
+    if (rhs_out) {
+      const double r = block_sum<kTT>(rq, scratch);
+      if (t == 0) rhs_out[i] = r;
+    }
+    if (t == 0) {
+      nnz[i] = total;
+      atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), (unsigned long long)total);
+    }
+    return;
+  }
+  int first = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t idx = t + (int64_t)kTT * j;
+    if (idx < L && fabsf(v[j]) == M) first = min(first, (int)idx);
+  }
+  const int idx = block_min_i<kTT>(first, reinterpret_cast<int*>(scratch));
+  __syncthreads();   // the zero code words written above are visible block-wide below
+  if (t == 0) {
+    codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
+    if (rhs_out) rhs_out[i] = x[idx] > 0.f ? (double)qr[idx] : -(double)qr[idx];
+    nnz[i] = 1;
+    atomicAdd(reinterpret_cast<unsigned long long*>(fb), 1ull);
+    atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), 1ull);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The optimal ternary projection (§2.2) of every row of Xt, the alternative
 // to T_tau; outputs as for k_row_ternarize.
@@ -1589,7 +1686,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     // column-wise ternarizer: T_tau, or the optimal projection (§2.2)
     auto row_tern = [&](const float* Xt, int64_t L, uint32_t* codes, int64_t wl, int* nz, long long* nz_sum,
                         const float* Qrows, double* rhs_out) {
-      if (!a.projection)
+      if (!a.projection && L <= 5 * kTT)
+        hipLaunchKernelGGL(k_row_ternarize_reg<5>, dim3(bb), dim3(kTT), 0, s, Xt, L, a.tau, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
+      else if (!a.projection && L <= 20 * kTT)
+        hipLaunchKernelGGL(k_row_ternarize_reg<20>, dim3(bb), dim3(kTT), 0, s, Xt, L, a.tau, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
+      else if (!a.projection)
         hipLaunchKernelGGL(k_row_ternarize, dim3(bb), dim3(kTT), 0, s, Xt, L, a.tau, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
       else if (L <= 4096)
         hipLaunchKernelGGL(k_row_project<4096>, dim3(bb), dim3(kTT), 0, s, Xt, L, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
