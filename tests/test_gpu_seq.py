@@ -293,3 +293,26 @@ def test_reconstruct_matches_oracle(lib):
     B, C, D = _factors(res)
     ref = oracle.reconstruct(B, C, D)
     assert np.max(np.abs(Ah - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_streaming_beyond_resident_limit(lib):
+    # The config-3 matrix (9728 x 2560) does not fit on chip, so AUTO runs the
+    # streaming kernels (float4 GEMVs, register T_tau).  The first 32
+    # components against the oracle's, with the per-component trace.
+    c = synthetic.CONFIGS[3]
+    A = synthetic.config_matrix(3)
+    m, n = A.shape
+    assert not lib.resident_fits(m, n)
+    mu = 32.25 / min(m, n)
+    Ad = _dev(A)
+    res = lib.decompose(Ad, mu, c["tau"], c["iters"], 0, c["seed"], trace=True, stats=True)
+    E = float(res.energy.item())
+    assert res.k == 32 and res.stat("mode") == 0
+    ref = oracle.decompose_seq(A, mu, c["tau"], c["iters"], c["seed"])
+    assert abs(E - ref.E) <= 2e-3, (E, ref.E)
+    B, C, D = _factors(res)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+    tr = res.trace.cpu().numpy()
+    assert np.all(np.diff(tr) <= 1e-9 * ref.norm_a2)
+    assert np.max(np.abs(tr - np.asarray(ref.trace))) <= 2e-3 * ref.norm_a2
+    assert res.stat("nnz_b") == np.count_nonzero(B) and res.stat("nnz_c") == np.count_nonzero(C)
