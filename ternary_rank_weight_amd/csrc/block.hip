@@ -610,8 +610,9 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 // are issued first; the residual norm is summed in fp32 (wave DPP sums, the
 // wave partials published with R by one barrier), and the iterate is double
 // buffered, so a step costs two barriers.  The
-// iteration stops when ||R||_F < 1e-4, or once ||R||_F < 1e-3 stops falling
-// by more than half (the fp32 floor); a run that does not get there within 40
+// iteration stops when ||R||_F < 1e-4, after the update of a step that found
+// ||R||_F < 1e-2 (the next residual is its square, so it is not computed), or
+// once ||R||_F < 1e-3 stops falling by more than half (the fp32 floor); a run that does not get there within 40
 // steps is counted in stats[EXTERND_STAT_INVERSE_UNCONVERGED]; the steps
 // taken and the replaced warm starts are counted too.  The result is within
 // 1e-4 relative of the exact inverse (usually far closer: each step squares
@@ -790,6 +791,8 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
       break;
     }
     prev = rn2;
+    // below 1e-2 the step's own result has residual R^2 < 1e-4: no check after it
+    const bool last = rn2 < 1e-4f;
     // X_next = X + X R
     f4 y[4];
 #pragma unroll
@@ -804,6 +807,10 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
       for (int v = 0; v < 4; ++v) Xn[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16] = y[J][v];
     __syncthreads();   // X_next complete; every read of R and X done
     cur ^= 1;
+    if (last) {
+      conv = true;
+      break;
+    }
   }
   const float* Xf = sh.X[cur];
   for (int e = t; e < bb * bb; e += kCT) X[e] = Xf[(e / bb) * kNsS + (e % bb)];
