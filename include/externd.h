@@ -72,7 +72,7 @@ enum externd_stat {
                                     Schulz iteration stopped before reaching its tolerance
                                     (wider blocks invert exactly in fp64: always 0) */
   EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
-  EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode, b <= 64: Newton-Schulz steps over all Gram inverses */
+  EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode, b <= 64: Newton-Schulz residual evaluations over all Gram inverses */
   EXTERND_STAT_NS_RESTARTS = 13,    /* block mode, b <= 64: warm starts replaced by another start */
   EXTERND_STAT_ITERATIONS = 14,     /* ALS iterations run, over all components (blocks) */
   EXTERND_STATS_LEN = 16
