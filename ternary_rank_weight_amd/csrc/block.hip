@@ -1546,8 +1546,12 @@ struct BlockLayout {
 BlockLayout layout_for(int64_t m, int64_t n, int b) {
   BlockLayout L{};
   const int64_t tiles1 = (n + 63) / 64, tiles2 = (m + 63) / 64;
-  int64_t s1 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles1 - 1) / tiles1, (m + 255) / 256));
-  int64_t s2 = std::max<int64_t>(1, std::min<int64_t>((512 + tiles2 - 1) / tiles2, (n + 255) / 256));
+  // contraction workgroups per launch: about two per CU; for b <= 64, where
+  // the inverse bounds the launch, about one (fewer split partials for the
+  // decorrelation to sum)
+  const int64_t target = b <= 64 ? 256 : 512;
+  int64_t s1 = std::max<int64_t>(1, std::min<int64_t>((target + tiles1 - 1) / tiles1, (m + 255) / 256));
+  int64_t s2 = std::max<int64_t>(1, std::min<int64_t>((target + tiles2 - 1) / tiles2, (n + 255) / 256));
   // splits are whole 256-long chunks of the contracted dimension when they
   // can be (the contraction stages codes per chunk), else multiples of 16
   auto round_split = [](int64_t len) {
