@@ -60,7 +60,7 @@ __global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint
 // ---------------------------------------------------------------------------
 // Exact Gram matrix G = X^T X of a ternary block held as 2-bit code rows
 // (X's column i = code row i, wl words).  Workgroup (tile, split) owns the
-// 16 x 16 tile (I, J), I >= J, of G over the words [split * kGramSplit, ...):
+// 16 x 16 tile (I, J), I >= J, of G over the words [split * words, ...):
 // it stages the 32 code rows of the tile in LDS with coalesced loads, thread
 // (r, c) takes the pair (16I + r, 16J + c), and the integer partial sums go to
 // G with atomics (exact, so order-free).  Per word pair, the product sum is
@@ -68,10 +68,13 @@ __global__ void k_block_start(uint64_t seed, int64_t c0, int bb, int64_t m, uint
 // zeroed beforehand.
 // ---------------------------------------------------------------------------
 constexpr int kGramChunk = 64;    // words per LDS stage
-constexpr int kGramSplit = 64;    // words per workgroup (one LDS stage)
+// words per Gram workgroup: 32 for b <= 64, 64 above (measured best at
+// 2560 x 2560, b = 64 and 9728 x 2560, b = 128)
+inline int gram_words(int b) { return b <= 64 ? 32 : 64; }
+constexpr int kGramSplit = 64;    // words per workgroup of the weighted Gram (one LDS stage)
 
 __device__ __forceinline__ void gram_tile_body(const uint32_t* __restrict__ codes, int64_t wl, int bb,
-                                               int* __restrict__ G, int tile, int split,
+                                               int* __restrict__ G, int tile, int split, int words,
                                                uint32_t (*rows)[kGramChunk + 1]) {
   const int t = threadIdx.x;
   // triangular tile index -> (I, J), J <= I
@@ -80,8 +83,8 @@ __device__ __forceinline__ void gram_tile_body(const uint32_t* __restrict__ code
   const int J = tile - I * (I + 1) / 2;
   const int r = t >> 4, c = t & 15;
   const int i = 16 * I + r, j = 16 * J + c;
-  const int64_t w_begin = (int64_t)split * kGramSplit;
-  const int64_t w_end = min(wl, w_begin + kGramSplit);
+  const int64_t w_begin = (int64_t)split * words;
+  const int64_t w_end = min(wl, w_begin + words);
   unsigned pos = 0u, neg = 0u;
   for (int64_t w0 = w_begin; w0 < w_end; w0 += kGramChunk) {
     const int cw = (int)min<int64_t>(kGramChunk, w_end - w0);
@@ -107,9 +110,9 @@ __device__ __forceinline__ void gram_tile_body(const uint32_t* __restrict__ code
 }
 
 __global__ __launch_bounds__(256) void k_gram(const uint32_t* __restrict__ codes, int64_t wl, int bb,
-                                              int* __restrict__ G) {
+                                              int* __restrict__ G, int words) {
   __shared__ uint32_t rows[32][kGramChunk + 1];
-  gram_tile_body(codes, wl, bb, G, (int)blockIdx.x, (int)blockIdx.y, rows);
+  gram_tile_body(codes, wl, bb, G, (int)blockIdx.x, (int)blockIdx.y, words, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -861,7 +864,9 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int idx = (int)blockIdx.x;
   if (idx < ngram) {
     if constexpr (!W) {
-      gram_tile_body(codes, wl, bb, static_cast<int*>(G), idx / gsplits, idx % gsplits, lds.rows);
+      // gram_words(bb), as a constant: NSUB > 4 exactly when bb > 64
+      gram_tile_body(codes, wl, bb, static_cast<int*>(G), idx / gsplits, idx % gsplits, NSUB > 4 ? 64 : 32,
+                     lds.rows);
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_fetch_add(gram_done, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1709,8 +1714,9 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         hipLaunchKernelGGL(k_row_project<kProjMaxN>, dim3(bb), dim3(kTT), 0, s, Xt, L, codes, wl, nz, st + EXTERND_STAT_FALLBACKS, nz_sum, Qrows, rhs_out);
     };
     const int nt = (bb + 15) / 16;
-    const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + kGramSplit - 1) / kGramSplit));
-    const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + kGramSplit - 1) / kGramSplit));
+    const int gw = gram_words(bb);
+    const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + gw - 1) / gw));
+    const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + gw - 1) / gw));
     for (int it = 0; it < a.iters; ++it) {
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
       // inverse depend only on U's codes, so they run as the first
@@ -1740,8 +1746,8 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     }
     // joint scales from the final U, V and the last Q = R V (weighted: the
     // last V-side Gram GVw already belongs to the final V)
-    hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf);
-    if (!W) hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf);
+    hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf, gw);
+    if (!W) hipLaunchKernelGGL(k_gram, gram_v, dim3(256), 0, s, Vc, wn, bb, GVf, gw);
     int* acc = dpart ? accept : nullptr;
     const double* gvw = W ? GVw : nullptr;
     if (bb <= 16)
