@@ -910,17 +910,18 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
 // Ginv[4 s + k][16 I + i]: 16 lanes read 64 contiguous bytes.  Writes the
 // plain sums too (Sum[k][c]) when `sum_out` is non-null.
 // ---------------------------------------------------------------------------
-template <int kDecW>
+template <int kDecW, int kRows>
 __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ Part, int S, int bb,
                                                      int64_t L, const float* __restrict__ Ginv,
                                                      float* __restrict__ Xt, float* __restrict__ sum_out) {
-  __shared__ float Ps[kMaxB][kDecW + 1];
+  static_assert(kRows == 64 || kRows == kMaxB, "row capacity");
+  __shared__ float Ps[kRows][kDecW + 1];
   const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kDecW;
   const int kb4 = (bb + 3) & ~3;
   // the split sums, in split order: every entry of this thread (E of them)
   // loads QB splits before any is added
-  constexpr int E = kMaxB * kDecW / 256;
+  constexpr int E = kRows * kDecW / 256;
   constexpr int QB = kDecW == 32 ? 4 : 8;
   float acc_s[E];
 #pragma unroll
@@ -966,17 +967,17 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
     f4 acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-    // every A operand of the row tile first (at most kMaxB / 4 per lane)
-    float av[kMaxB / 4];
+    // every A operand of the row tile first (at most kRows / 4 per lane)
+    float av[kRows / 4];
 #pragma unroll
-    for (int q = 0; q < kMaxB / 4; ++q) {
+    for (int q = 0; q < kRows / 4; ++q) {
       const int kk = 4 * q + k;
       const bool ok = kk < bb && row < bb;
       const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
       av[q] = ok ? a : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < kMaxB / 4; ++q) {
+    for (int q = 0; q < kRows / 4; ++q) {
       if (4 * q >= kb4) break;   // uniform
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma16x16x4(av[q], Ps[4 * q + k][16 * ct + j], acc[ct]);
@@ -1596,13 +1597,14 @@ inline char* bump(char*& p, size_t bytes) {
 
 
 // The decorrelation: 32-column tiles for b > 64 (the product dominates),
-// 16-column ones below (more workgroups for the split sums).
+// 16-column ones below (more workgroups for the split sums), each sized for
+// its largest block.
 inline void launch_decorrelate(int bb, hipStream_t s, const float* Part, int S, int64_t L, const float* Ginv,
                                float* Xt, float* sum_out) {
   if (bb > 64)
-    hipLaunchKernelGGL(k_decorrelate<32>, dim3((unsigned)((L + 31) / 32)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
+    hipLaunchKernelGGL((k_decorrelate<32, kMaxB>), dim3((unsigned)((L + 31) / 32)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
   else
-    hipLaunchKernelGGL(k_decorrelate<16>, dim3((unsigned)((L + 15) / 16)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
+    hipLaunchKernelGGL((k_decorrelate<16, 64>), dim3((unsigned)((L + 15) / 16)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
 }
 
 // The combined launch, by sub-tile count.  ngram Gram tiles
