@@ -1399,6 +1399,21 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
   const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t c0 = (int64_t)blockIdx.x * 64;
   const int kb = (bb + 31) & ~31;   // components padded to whole 32-long slabs (zero codes)
+  // this thread's 16 residual entries, loaded first so that their latency
+  // overlaps the staging and the products: row r0 + 16 w + 4 g + v, column
+  // c0 + 16 s + i
+  float old[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t col = c0 + 16 * s + i;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = r0 + 16 * w + 4 * g + v;
+      const bool ok = row < m && col < n;
+      const float x = R[ok ? row * n + col : 0];
+      old[s][v] = ok ? x : 0.f;
+    }
+  }
   // stage: 4 code words (64 rows or columns) per component and side
   for (int e = t; e < 2 * kb * 4; e += 256) {
     const bool vside = e >= kb * 4;
@@ -1457,10 +1472,9 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
     for (int v = 0; v < 4; ++v) {
       const int64_t row = r0 + 16 * w + 4 * g + v;
       if (row < m && col < n) {
-        const float old = R[row * n + col];
-        const float upd = old - acc[s][v];
+        const float upd = old[s][v] - acc[s][v];
         R[row * n + col] = upd;
-        const double ch = (double)upd * (double)upd - (double)old * (double)old;
+        const double ch = (double)upd * (double)upd - (double)old[s][v] * (double)old[s][v];
         change += wt ? ch * (double)wt[col] : ch;
       }
     }
