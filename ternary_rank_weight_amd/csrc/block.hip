@@ -1610,12 +1610,14 @@ inline char* bump(char*& p, size_t bytes) {
 }
 
 
-// The decorrelation: 32-column tiles for b > 64 (the product dominates),
-// 16-column ones below (more workgroups for the split sums), each sized for
-// its largest block.
+// The decorrelation: 32-column tiles for b > 64 on rows longer than 4096
+// (the product dominates), 16-column ones otherwise (more workgroups for the
+// split sums), each sized for its largest block.
 inline void launch_decorrelate(int bb, hipStream_t s, const float* Part, int S, int64_t L, const float* Ginv,
                                float* Xt, float* sum_out) {
-  if (bb > 64)
+  if (bb > 64 && L <= 4096)   // short rows: few 32-column tiles, so 16
+    hipLaunchKernelGGL((k_decorrelate<16, kMaxB>), dim3((unsigned)((L + 15) / 16)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
+  else if (bb > 64)
     hipLaunchKernelGGL((k_decorrelate<32, kMaxB>), dim3((unsigned)((L + 31) / 32)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
   else
     hipLaunchKernelGGL((k_decorrelate<16, 64>), dim3((unsigned)((L + 15) / 16)), dim3(256), 0, s, Part, S, bb, L, Ginv, Xt, sum_out);
