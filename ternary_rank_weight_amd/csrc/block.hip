@@ -71,7 +71,7 @@ constexpr int kGramChunk = 64;    // words per LDS stage
 // words per Gram workgroup: 32 for b <= 64, 64 above (measured best at
 // 2560 x 2560, b = 64 and 9728 x 2560, b = 128)
 inline int gram_words(int b) { return b <= 64 ? 32 : 64; }
-constexpr int kGramSplit = 64;    // words per workgroup of the weighted Gram (one LDS stage)
+constexpr int kGramSplit = 16;    // words per workgroup of the weighted Gram (one LDS stage)
 
 __device__ __forceinline__ void gram_tile_body(const uint32_t* __restrict__ codes, int64_t wl, int bb,
                                                int* __restrict__ G, int tile, int split, int words,
@@ -150,13 +150,15 @@ __global__ __launch_bounds__(256) void k_gram_w_partial(const uint32_t* __restri
   double acc = 0.0;
   for (int w = 0; w < cw; ++w) {
     const uint32_t x = rows[r][w], y = rows[16 + c][w];
-    uint32_t both = x & y & 0x55555555u;
-    const uint32_t diff = (x ^ y) >> 1;
-    while (both) {
-      const int b = __ffs(both) - 1;   // even: the low bit of element b / 2
-      const double wv = (double)ws[w * 16 + (b >> 1)];
-      acc += ((diff >> b) & 1u) ? -wv : wv;
-      both &= both - 1u;
+    const uint32_t both = x & y & 0x55555555u;
+    const uint32_t neg = ((x ^ y) >> 1) & both;
+    // every element in column order, the ones not in both adding zero: the
+    // same additions as skipping them, without divergent loops
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const double wv = (double)ws[w * 16 + e];
+      const double sv = ((neg >> (2 * e)) & 1u) ? -wv : wv;
+      acc += ((both >> (2 * e)) & 1u) ? sv : 0.0;
     }
   }
   if (i < bb && j < bb) {
