@@ -625,14 +625,26 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 // an entry that close to its threshold would notice.  G (integer valued)
 // is zeroed after being read so the next Gram accumulation starts from zero.
 // ---------------------------------------------------------------------------
-constexpr int kNsB = 64, kNsS = 65;
+constexpr int kNsB = 64;
+// The products run on bf16 MFMA (16x16x32) with every fp32 operand split
+// exactly into three bf16 parts (x = h + m + l, 8 significant bits each),
+// taking the six products of parts whose order of magnitude reaches 2^-16
+// (hh, hm, mh, hl, lh, mm): as accurate as an fp32 product.  (Fewer parts in
+// the update X R let the slow start from the scaled identity diverge on
+// nearly singular Grams.)  X and R are kept transposed (Xt[c][k] = X[k][c]):
+// as B operands they are read along rows, X as the A operand of X R down
+// columns; G' is symmetric, so its store serves either way.  Each 64 x 64
+// part is stored without padding, the 16-byte chunks of row r permuted by
+// r mod 8, so the 16 rows one operand load touches fall in different banks.
 struct NsShared {
-  float G[kNsB * kNsS];
-  float X[2][kNsB * kNsS];   // current and next iterate
-  float R[kNsB * kNsS];
-  float red[kCT / kWave];    // per-wave partials of ||R||_F^2
+  unsigned short Gp[3][kNsB * kNsB];   // parts of G'
+  unsigned short Xt[3][kNsB * kNsB];   // parts of X, transposed
+  unsigned short Rt[3][kNsB * kNsB];   // parts of R, transposed
+  float red[kCT / kWave];              // per-wave partials of ||R||_F^2
   double dred[kCT / kWave];
 };
+// Index of element (row, k) of a stored part.
+__device__ inline int ns_at(int row, int k) { return row * kNsB + ((((k >> 3) ^ (row & 7))) << 3) + (k & 7); }
 
 __device__ inline double ns_block_max(double v, double* red) {
 #pragma unroll
@@ -645,16 +657,90 @@ __device__ inline double ns_block_max(double v, double* red) {
   for (int q = 1; q < kCT / kWave; ++q) r = fmax(r, red[q]);
   return r;
 }
-// acc[J] (tile (w, J)) += A(rows 16w..16w+15) * B(columns 16J..16J+15), K = 64;
-// A and B in LDS with row stride kNsS.
-__device__ inline void ns_mm(const float* A, const float* B, f4 (&acc)[4]) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int i = lane & 15, k = lane >> 4;
+
+// The three bf16 parts of x (bit patterns in the low halves): x = h + m + l exactly.
+__device__ inline void ns_split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t u = __float_as_uint(x);
+  const float r = x - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t v = __float_as_uint(r);
+  const float q = r - __uint_as_float(v & 0xFFFF0000u);
+  h = u >> 16;
+  m = v >> 16;
+  l = __float_as_uint(q) >> 16;
+}
+
+// The lane's 16 entries val[J][v], at (row 16 w + 4 g + v, column 16 J + j),
+// stored transposed as three parts: dst[p] element (16 J + j, 16 w + 4 g + v),
+// four consecutive entries per 8-byte store.
+__device__ inline void ns_store_t(unsigned short (*dst)[kNsB * kNsB], const f4 (&val)[4], int w, int j, int g) {
 #pragma unroll
-  for (int k0 = 0; k0 < kNsB; k0 += 4) {
-    const float a = A[(16 * w + i) * kNsS + k0 + k];
+  for (int J = 0; J < 4; ++J) {
+    uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) acc[J] = mfma16x16x4(a, B[(k0 + k) * kNsS + 16 * J + i], acc[J]);
+    for (int v = 0; v < 4; ++v) ns_split3(val[J][v], hp[v], mp[v], lp[v]);
+    const int at = ns_at(16 * J + j, 16 * w + 4 * g);
+    *reinterpret_cast<uint2*>(&dst[0][at]) = uint2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+    *reinterpret_cast<uint2*>(&dst[1][at]) = uint2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+    *reinterpret_cast<uint2*>(&dst[2][at]) = uint2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+  }
+}
+
+// Eight consecutive k (k0 a multiple of 8) of row `row`.
+__device__ inline bf16x8 ns_ld(const unsigned short* buf, int row, int k0) {
+  return *reinterpret_cast<const bf16x8*>(&buf[ns_at(row, k0)]);
+}
+// Elements (k0 .. k0 + 7, col): eight consecutive k down column col.
+__device__ inline bf16x8 ns_ld_col(const unsigned short* buf, int k0, int col) {
+  uint32_t q[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    q[e] = (uint32_t)buf[ns_at(k0 + 2 * e, col)] | ((uint32_t)buf[ns_at(k0 + 2 * e + 1, col)] << 16);
+  return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[2], q[3]});
+}
+__device__ inline f4 ns_mfma6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f4 acc) {
+  acc = mfma16x16x32bf16(a[0], b[0], acc);
+  acc = mfma16x16x32bf16(a[0], b[1], acc);
+  acc = mfma16x16x32bf16(a[1], b[0], acc);
+  acc = mfma16x16x32bf16(a[0], b[2], acc);
+  acc = mfma16x16x32bf16(a[2], b[0], acc);
+  acc = mfma16x16x32bf16(a[1], b[1], acc);
+  return acc;
+}
+
+// acc[J] += (G' X)(rows 16 w .., columns 16 J ..): A = G' rows, B[k][c] =
+// X[k][c] = Xt[c][k]; lane (i + 16 g) supplies k = 32 kc + 8 g .. + 7.
+__device__ inline void ns_gemm_gx(const NsShared& sh, int w, int i, int g, f4 (&acc)[4]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int k0 = 32 * kc + 8 * g;
+    bf16x8 a[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) a[p] = ns_ld(sh.Gp[p], 16 * w + i, k0);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      bf16x8 b[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) b[p] = ns_ld(sh.Xt[p], 16 * J + i, k0);
+      acc[J] = ns_mfma6(a, b, acc[J]);
+    }
+  }
+}
+// acc[J] += (X R)(rows 16 w .., columns 16 J ..): A[r][k] = X[r][k] = Xt[k][r]
+// (down a column of the transposed store), B[k][c] = R[k][c] = Rt[c][k].
+__device__ inline void ns_gemm_xr(const NsShared& sh, int w, int i, int g, f4 (&acc)[4]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int k0 = 32 * kc + 8 * g;
+    bf16x8 a[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) a[p] = ns_ld_col(sh.Xt[p], k0, 16 * w + i);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      bf16x8 b[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) b[p] = ns_ld(sh.Rt[p], 16 * J + i, k0);
+      acc[J] = ns_mfma6(a, b, acc[J]);
+    }
   }
 }
 
@@ -662,36 +748,41 @@ template <typename GT>
 __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, float* __restrict__ X,
                                                 int* __restrict__ warm_flag,
                                                 long long* __restrict__ stats, NsShared& sh) {
-  constexpr int kPer = kNsB * kNsB / kCT;   // entries per thread: rows w + 4q, column lane
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
-  const int i16 = lane & 15, kq = lane >> 4;
+  const int i16 = lane & 15, g = lane >> 4;
   const int warm = *warm_flag;
-  // every load first: G (and the previous inverse when warm)
-  GT gv[kPer];
-  float xv[kPer];
+  // this lane's entries: (r, c) = (16 w + 4 g + v, 16 J + i16); every load first
+  GT gv[4][4];
+  f4 xv[4];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int r = w + 4 * q;
-    gv[q] = (r < bb && lane < bb) ? G[r * bb + lane] : (GT)0;
-  }
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+      gv[J][v] = (r < bb && c < bb) ? G[r * bb + c] : (GT)0;
+    }
   if (warm) {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int r = w + 4 * q;
-      xv[q] = (r < bb && lane < bb) ? X[r * bb + lane] : ((r == lane) ? 1.f : 0.f);
-    }
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+        xv[J][v] = (r < bb && c < bb) ? X[r * bb + c] : ((r == c) ? 1.f : 0.f);
+      }
   }
-  // trace (each thread holds at most one diagonal entry), eps = 1e-6 trace / b
+  // trace (each diagonal entry is held by one lane), eps = 1e-6 trace / b
   double trp = 0.0;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int r = w + 4 * q;
-    if (r < bb && lane < bb) {
-      consume_gram(G, r * bb + lane);
-      if (r == lane) trp = (double)gv[q];
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+      if (r < bb && c < bb) {
+        consume_gram(G, r * bb + c);
+        if (r == c) trp = (double)gv[J][v];
+      }
     }
-  }
   trp = wave_sum_to63(trp);
   if (lane == kWave - 1) sh.dred[w] = trp;
   __syncthreads();
@@ -699,78 +790,84 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
 #pragma unroll
   for (int q = 1; q < kCT / kWave; ++q) tr += sh.dred[q];
   const float eps = (float)(1e-6 * tr / bb);
-  // G' = G + eps I in LDS (the identity beyond bb)
+  // G' = G + eps I (the identity beyond bb), fp32, then its parts in LDS
+  f4 gp[4];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int r = w + 4 * q;
-    float v = (r == lane) ? 1.f : 0.f;
-    if (r < bb && lane < bb) {
-      v = (float)gv[q];
-      if (r == lane) v += eps;
-    }
-    sh.G[r * kNsS + lane] = v;
-  }
-  int cur = 0;
-  if (warm) {
+  for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) sh.X[0][(w + 4 * q) * kNsS + lane] = xv[q];
-  }
-  __syncthreads();
-  // X0 = I / ||G'||_inf (the largest absolute row sum), for a cold start or a
-  // rejected warm one
-  auto init_scaled = [&](float* Xd) {
-    double rs = 0.0;
-    {
-      const int row = t >> 2, part = t & 3;   // four threads per row
-      for (int c = part; c < kNsB; c += 4) rs += fabs((double)sh.G[row * kNsS + c]);
-      rs += __shfl_xor(rs, 1);
-      rs += __shfl_xor(rs, 2);
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+      float x = (r == c) ? 1.f : 0.f;
+      if (r < bb && c < bb) {
+        x = (float)gv[J][v];
+        if (r == c) x += eps;
+      }
+      gp[J][v] = x;
     }
-    const float alpha = (float)(1.0 / ns_block_max(rs, sh.dred));
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int r = w + 4 * q;
-      Xd[r * kNsS + lane] = (r == lane) ? alpha : 0.f;
-    }
-    __syncthreads();
-  };
+  ns_store_t(sh.Gp, gp, w, i16, g);
   // X0 = diag(1 / G'_ii): the Gram of decorrelated ternary columns is close
   // to diagonal, so this is usually far better than the scaled identity; it
   // can diverge when the columns are strongly correlated (the residual then
   // grows), and the scaled identity takes over.
-  auto init_jacobi = [&](float* Xd) {
+  auto init_jacobi = [&]() {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int r = w + 4 * q;
-      Xd[r * kNsS + lane] = (r == lane) ? 1.f / sh.G[r * kNsS + r] : 0.f;
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+        xv[J][v] = (r == c) ? 1.f / gp[J][v] : 0.f;
+      }
+  };
+  // X0 = I / ||G'||_inf (the largest absolute row sum), for a cold start or
+  // a rejected warm one
+  auto init_scaled = [&]() {
+    double rs[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      double a = 0.0;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) a += fabs((double)gp[J][v]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o);   // the 16 lanes of the row
+      rs[v] = a;
     }
-    __syncthreads();
+    const double rmax = fmax(fmax(rs[0], rs[1]), fmax(rs[2], rs[3]));
+    const float alpha = (float)(1.0 / ns_block_max(rmax, sh.dred));
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+        xv[J][v] = (r == c) ? alpha : 0.f;
+      }
   };
   int start = warm ? 0 : 1;   // 0 warm, 1 Jacobi, 2 scaled identity
-  if (!warm) init_jacobi(sh.X[0]);
+  if (!warm) init_jacobi();
+  ns_store_t(sh.Xt, xv, w, i16, g);
+  __syncthreads();
   float prev = 3.0e38f;
   bool conv = false, restarted = false;
   int iters_done = 0, since_start = 0;
   for (int it = 0; it < 40; ++it) {
     ++iters_done;
-    float* Xc = sh.X[cur];
     f4 acc[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) acc[J] = f4{0.f, 0.f, 0.f, 0.f};
-    ns_mm(sh.G, Xc, acc);
+    ns_gemm_gx(sh, w, i16, g, acc);
     float rp = 0.f;
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = 16 * w + 4 * kq + v, c = 16 * J + i16;
+        const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
         const float rv = ((r == c) ? 1.f : 0.f) - acc[J][v];
-        sh.R[r * kNsS + c] = rv;
+        acc[J][v] = rv;
         rp = fmaf(rv, rv, rp);
       }
+    ns_store_t(sh.Rt, acc, w, i16, g);
     rp = wave_sum_to63(rp);
     if (lane == kWave - 1) sh.red[w] = rp;
-    __syncthreads();   // publishes R and the partial norms
+    __syncthreads();   // publishes R and the partial norms; every read of Xt by the product done
     float rn2 = sh.red[0];
 #pragma unroll
     for (int q = 1; q < kCT / kWave; ++q) rn2 += sh.red[q];
@@ -783,8 +880,10 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
     if (bad) {
       if (start == 2) break;  // not finite from the scaled identity: give up
       restarted = true;       // poor warm start: Jacobi; diverging Jacobi: scaled identity
-      if (start == 0) init_jacobi(Xc);
-      else init_scaled(Xc);
+      if (start == 0) init_jacobi();
+      else init_scaled();
+      ns_store_t(sh.Xt, xv, w, i16, g);
+      __syncthreads();
       ++start;
       since_start = 0;
       prev = 3.0e38f;
@@ -801,24 +900,27 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
     // X_next = X + X R
     f4 y[4];
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) y[J][v] = Xc[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16];
-    ns_mm(Xc, sh.R, y);
-    float* Xn = sh.X[cur ^ 1];
+    for (int J = 0; J < 4; ++J) y[J] = f4{0.f, 0.f, 0.f, 0.f};
+    ns_gemm_xr(sh, w, i16, g, y);
 #pragma unroll
     for (int J = 0; J < 4; ++J)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Xn[(16 * w + 4 * kq + v) * kNsS + 16 * J + i16] = y[J][v];
-    __syncthreads();   // X_next complete; every read of R and X done
-    cur ^= 1;
+      for (int v = 0; v < 4; ++v) xv[J][v] += y[J][v];
+    __syncthreads();   // every read of Xt and Rt done
+    ns_store_t(sh.Xt, xv, w, i16, g);
+    __syncthreads();
     if (last) {
       conv = true;
       break;
     }
   }
-  const float* Xf = sh.X[cur];
-  for (int e = t; e < bb * bb; e += kCT) X[e] = Xf[(e / bb) * kNsS + (e % bb)];
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+      if (r < bb && c < bb) X[r * bb + c] = xv[J][v];
+    }
   if (t == 0) {
     *warm_flag = 1;
     if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_INVERSE_UNCONVERGED), 1ull);
