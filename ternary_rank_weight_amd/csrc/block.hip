@@ -10,7 +10,8 @@
 //   R <- R - U diag(d) V^T           (MFMA rank-b update)
 // The Gram matrices of ternary factors are exact integers (popcounts of the
 // 2-bit codes).  The regularised Gram inverse is exact fp64 for b > 64 and
-// fp32 Newton-Schulz to 1e-4 below; the joint scale solve is fp64.  The
+// fp32-accurate Newton-Schulz to 1e-4 below (bf16 MFMA, split operands);
+// the joint scale solve is fp64.  The
 // contractions and the deflation are fp32-accurate (exact products, fp32
 // sums) on bf16 MFMA.  T_col applies the mean-threshold ternarizer T_tau
 // (§2.2) to each column.  U and V live as 2-bit codes directly in their
@@ -603,7 +604,7 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 
 // ---------------------------------------------------------------------------
 // Decorrelation inverse for b <= 64: X = (G + eps I)^-1, eps = 1e-6 trace(G)/b,
-// by the Newton-Schulz iteration  R = I - G'X,  X <- X + X R  on fp32 MFMA in
+// by the Newton-Schulz iteration  R = I - G'X,  X <- X + X R  on bf16 MFMA in
 // one workgroup (256 threads; wave w owns the 16-row tile band w).  Since
 // R_{k+1} = R_k^2, the Frobenius norm of R squares each step while it is
 // below 1.  The start is the previous inverse of the same side (consecutive
@@ -612,9 +613,10 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 // the iteration is sure to converge) is replaced by the Jacobi guess, so is a
 // warm start whose residual grows, and a Jacobi start whose residual grows by
 // X0 = I / ||G'||_inf, which converges for every symmetric positive definite G'.  All loads
-// are issued first; the residual norm is summed in fp32 (wave DPP sums, the
-// wave partials published with R by one barrier), and the iterate is double
-// buffered, so a step costs two barriers.  The
+// are issued first; each lane keeps its 16 entries of X and R in fp32
+// registers (the MFMA output layout) and stores their bf16 parts in LDS; the
+// residual norm is summed in fp32 (wave DPP sums, the wave partials published
+// with R by one barrier), and a step costs three barriers.  The
 // iteration stops when ||R||_F < 1e-4, after the update of a step that found
 // ||R||_F < 1e-2 (the next residual is its square, so it is not computed), or
 // once ||R||_F < 1e-3 stops falling by more than half (the fp32 floor); a run that does not get there within 40
