@@ -32,13 +32,13 @@ SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
 SEQ_TRAFFIC_SHA = "02e837a922544f93"
 
 
-def seq_traffic(config):
+def seq_traffic(workload):
     import hashlib
     h = hashlib.sha256()
     for f in SEQ_TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if config != 2 or h.hexdigest()[:16] != SEQ_TRAFFIC_SHA:
+    if workload != "llm2560" or h.hexdigest()[:16] != SEQ_TRAFFIC_SHA:
         return None
     return SEQ_TRAFFIC_BYTES
 
@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--modes", default=None,
-                    help="comma-separated subset of seq,block (default: seq,block; block for config 3)")
+                    help="comma-separated subset of seq,block (default: seq,block; block for mlp9728)")
     ap.add_argument("--cpu-sample", type=int, default=200,
                     help="components of the oracle's sequential run timed as the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -61,10 +61,10 @@ def parse():
                     help="skip the streaming-versus-resident comparison of the sequential mode")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
-                    help="1: 256x256 Gaussian; 2: 2560x2560 LLM-shaped (default); "
-                         "3: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128; "
-                         "4: the seven matrices of one 4B-class layer, mu=2.5, block b=128, back to back")
+    ap.add_argument("--workload", default="llm2560", choices=["gauss256", "llm2560", "mlp9728", "layer"],
+                    help="gauss256: 256x256 Gaussian; llm2560: 2560x2560 LLM-shaped (default); "
+                         "mlp9728: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128; "
+                         "layer: the seven matrices of one 4B-class layer, mu=2.5, block b=128, back to back")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
                          "exit; its HBM counters calibrate the per-kernel traffic figures")
@@ -274,9 +274,9 @@ def run_layer(args):
     import ternary_rank_weight_amd as trw
 
     torch.cuda.set_device(0)
-    c = synthetic.CONFIGS[4]
+    c = synthetic.WORKLOADS["layer"]
     shapes = synthetic.layer_shapes()
-    host = {name: synthetic.config_matrix(4, name) for name, _, _ in shapes}
+    host = {name: synthetic.workload_matrix("layer", name) for name, _, _ in shapes}
     dev = {name: torch.from_numpy(A).cuda() for name, A in host.items()}
     outs = {}
 
@@ -350,12 +350,12 @@ def run_layer(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the decomposition runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    if args.config == 4:
+    if args.workload == "layer":
         run_layer(args)
         return
     import numpy as np
@@ -364,13 +364,13 @@ def main():
     import ternary_rank_weight_amd as trw
 
     torch.cuda.set_device(0)
-    c = synthetic.CONFIGS[args.config]
-    A = synthetic.config_matrix(args.config)
+    c = synthetic.WORKLOADS[args.workload]
+    A = synthetic.workload_matrix(args.workload)
     m, n = A.shape
     Ad = torch.from_numpy(A).cuda()
     k = trw.rank(m, n, c["mu"])
     if args.modes is None:
-        args.modes = "block" if args.config == 3 else "seq,block"
+        args.modes = "block" if args.workload == "mlp9728" else "seq,block"
     modes = [s for s in args.modes.split(",") if s]
     block = c.get("block", 64) or 64
     b = trw.block_width(m, n, block)
@@ -427,7 +427,7 @@ def main():
         s["gbps"] = achieved
         roofline = {"bound": "hbm", "kernel": "k_seq_resident", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": seq_traffic(args.config), "traffic_unit": "bytes per launch",
+                    "traffic": seq_traffic(args.workload), "traffic_unit": "bytes per launch",
                     "alg_bytes_per_launch": alg}
     if "block" in per_mode:
         bm = per_mode["block"]

@@ -17,7 +17,7 @@ brute-force rank-1 optima on tiny matrices, exact recovery of ternary rank-1
 matrices, sign and power-of-two symmetries, the prefix property, block b=1 ==
 sequential, and a known-answer value of the SplitMix64 generator.
 
-Parity unpinned: the whole-trajectory energies on the synthetic configs (the
+Parity unpinned: the whole-trajectory energies on the synthetic workloads (the
 pages print no worked example for them; the oracle's own result is the
 reference) and the two free choices the pages leave open, the starting vector
 rule and the ridge eps.

@@ -21,7 +21,7 @@ these stand in for them with the same shapes):
 import numpy as np
 
 __all__ = ["gaussian", "llm_like", "low_rank_plus_noise", "importance", "round_bf16",
-           "layer_shapes", "config_matrix", "CONFIGS"]
+           "layer_shapes", "workload_matrix", "WORKLOADS"]
 
 
 def round_bf16(x):
@@ -72,20 +72,26 @@ def layer_shapes():
             ("gate", 9728, 2560), ("up", 9728, 2560), ("down", 2560, 9728)]
 
 
-# The five workloads: shapes, method knobs and the seed of each matrix.
-CONFIGS = {
-    1: dict(kind="gaussian", m=256, n=256, seed=0, mu=2.0, tau=0.7, iters=15, block=0),
-    2: dict(kind="llm_like", m=2560, n=2560, seed=1, mu=2.0, tau=0.7, iters=15, block=64),
-    3: dict(kind="llm_like", m=9728, n=2560, seed=2, mu=3.0, tau=1.0, iters=15, block=128),
-    4: dict(kind="layer", seed=3, mu=2.5, tau=0.7, iters=15, block=128),
-    5: dict(kind="low_rank", m=4096, n=4096, seed=4, mus=(1.0, 2.0, 3.0, 3.5),
-            taus=(0.7, 1.0, 2.0), iters=15, block=128),
+# The five workloads, by what they are: shapes, method knobs and the seed of
+# each matrix.
+#   gauss256     256 x 256 Gaussian, sequential
+#   llm2560      2560 x 2560 LLM-shaped, sequential and block b = 64
+#   mlp9728      9728 x 2560 LLM-shaped (an MLP matrix), block b = 128
+#   layer        the seven matrices of one 4B-class transformer layer, b = 128
+#   lowrank4096  4096 x 4096 low rank plus noise, mu and tau swept, b = 128
+WORKLOADS = {
+    "gauss256": dict(kind="gaussian", m=256, n=256, seed=0, mu=2.0, tau=0.7, iters=15, block=0),
+    "llm2560": dict(kind="llm_like", m=2560, n=2560, seed=1, mu=2.0, tau=0.7, iters=15, block=64),
+    "mlp9728": dict(kind="llm_like", m=9728, n=2560, seed=2, mu=3.0, tau=1.0, iters=15, block=128),
+    "layer": dict(kind="layer", seed=3, mu=2.5, tau=0.7, iters=15, block=128),
+    "lowrank4096": dict(kind="low_rank", m=4096, n=4096, seed=4, mus=(1.0, 2.0, 3.0, 3.5),
+                        taus=(0.7, 1.0, 2.0), iters=15, block=128),
 }
 
 
-def config_matrix(cfg, which=None):
-    """Build the input matrix of config `cfg` (for config 4, `which` names the layer matrix)."""
-    c = CONFIGS[cfg]
+def workload_matrix(name, which=None):
+    """Build the input matrix of workload `name` (for "layer", `which` names the layer matrix)."""
+    c = WORKLOADS[name]
     if c["kind"] == "gaussian":
         return gaussian(c["m"], c["n"], c["seed"])
     if c["kind"] == "llm_like":
@@ -97,4 +103,4 @@ def config_matrix(cfg, which=None):
         j = names.index(which)
         _, m, n = layer_shapes()[j]
         return llm_like(m, n, 1000 * c["seed"] + j)
-    raise ValueError(cfg)
+    raise ValueError(name)

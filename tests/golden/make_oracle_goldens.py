@@ -34,45 +34,45 @@ def _entry(name, A, res, mode, mu, tau, iters, block, seed, secs, extra=None):
 
 
 def jobs():
-    c = synthetic.CONFIGS
-    yield "cfg1_seq", lambda: _seq(1, c[1])
-    yield "cfg2_seq", lambda: _seq(2, c[2])
-    yield "cfg2_block64", lambda: _block(2, c[2], c[2]["block"])
-    yield "cfg3_block128", lambda: _block(3, c[3], c[3]["block"])
+    c = synthetic.WORKLOADS
+    yield "gauss256_seq", lambda: _seq("gauss256", c["gauss256"])
+    yield "llm2560_seq", lambda: _seq("llm2560", c["llm2560"])
+    yield "llm2560_block64", lambda: _block("llm2560", c["llm2560"], c["llm2560"]["block"])
+    yield "mlp9728_block128", lambda: _block("mlp9728", c["mlp9728"], c["mlp9728"]["block"])
     for name, _, _ in synthetic.layer_shapes():
-        yield f"cfg4_{name}_block128", (lambda nm: (lambda: _layer(nm, c[4])))(name)
-    for tau in c[5]["taus"]:
-        yield f"cfg5_tau{tau}", (lambda tt: (lambda: _sweep(c[5], tt)))(tau)
+        yield f"layer_{name}_block128", (lambda nm: (lambda: _layer(nm, c["layer"])))(name)
+    for tau in c["lowrank4096"]["taus"]:
+        yield f"lowrank4096_tau{tau}", (lambda tt: (lambda: _sweep(c["lowrank4096"], tt)))(tau)
 
 
-def _seq(cfg, c):
-    A = synthetic.config_matrix(cfg)
+def _seq(wl, c):
+    A = synthetic.workload_matrix(wl)
     t = time.time()
     r = oracle.decompose_seq(A, c["mu"], c["tau"], c["iters"], c["seed"])
-    return [_entry(f"cfg{cfg}_seq", A, r, "sequential", c["mu"], c["tau"], c["iters"], 0,
+    return [_entry(f"{wl}_seq", A, r, "sequential", c["mu"], c["tau"], c["iters"], 0,
                    c["seed"], time.time() - t, {"sum_nnz_u": int(r.extra["sum_nnz_u"])})]
 
 
-def _block(cfg, c, b):
-    A = synthetic.config_matrix(cfg)
+def _block(wl, c, b):
+    A = synthetic.workload_matrix(wl)
     t = time.time()
     r = oracle.decompose_block(A, c["mu"], c["tau"], c["iters"], b, c["seed"])
-    return [_entry(f"cfg{cfg}_block{b}", A, r, "block", c["mu"], c["tau"], c["iters"], b,
+    return [_entry(f"{wl}_block{b}", A, r, "block", c["mu"], c["tau"], c["iters"], b,
                    c["seed"], time.time() - t, {"ridge_retries": r.extra["ridge_retries"]})]
 
 
 def _layer(name, c):
-    A = synthetic.config_matrix(4, name)
+    A = synthetic.workload_matrix("layer", name)
     t = time.time()
     r = oracle.decompose_block(A, c["mu"], c["tau"], c["iters"], c["block"], c["seed"])
-    return [_entry(f"cfg4_{name}_block{c['block']}", A, r, "block", c["mu"], c["tau"],
+    return [_entry(f"layer_{name}_block{c['block']}", A, r, "block", c["mu"], c["tau"],
                    c["iters"], c["block"], c["seed"], time.time() - t)]
 
 
 def _sweep(c, tau):
     # One run at the largest mu; smaller mu are prefixes (greedy deflation),
     # read off the per-block trace at k = mu * min(m, n) (multiples of b).
-    A = synthetic.config_matrix(5)
+    A = synthetic.workload_matrix("lowrank4096")
     mus = c["mus"]
     t = time.time()
     r = oracle.decompose_block(A, max(mus), tau, c["iters"], c["block"], c["seed"])
@@ -84,7 +84,7 @@ def _sweep(c, tau):
         assert k % b == 0
         E = 1.0 - r.trace[k // b - 1] / r.norm_a2
         zf = oracle.zero_fraction(r.B[:, :k], r.C[:k])
-        out.append({"name": f"cfg5_tau{tau}_mu{mu}", "m": int(A.shape[0]), "n": int(A.shape[1]),
+        out.append({"name": f"lowrank4096_tau{tau}_mu{mu}", "m": int(A.shape[0]), "n": int(A.shape[1]),
                     "mode": "block", "mu": mu, "tau": tau, "iters": c["iters"], "block": b,
                     "seed": c["seed"], "k": k, "E": float(E), "zero_fraction": float(zf),
                     "seconds": round(secs, 2)})

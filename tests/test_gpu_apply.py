@@ -29,8 +29,8 @@ def _random_factors(m, n, k, seed):
 
 
 def test_apply_decomposed_factors(lib):
-    c = synthetic.CONFIGS[1]
-    A = synthetic.config_matrix(1)
+    c = synthetic.WORKLOADS["gauss256"]
+    A = synthetic.workload_matrix("gauss256")
     res = lib.decompose(torch.from_numpy(A).cuda(), c["mu"], c["tau"], c["iters"], 0, c["seed"])
     B = oracle.unpack2(res.B2.cpu().numpy().view(np.uint32), 256).T
     C = oracle.unpack2(res.C2.cpu().numpy().view(np.uint32), 256)

@@ -107,12 +107,12 @@ def test_block_structured_ternary_low_rank(lib):
     assert np.all(np.diff(res.trace.cpu().numpy()) <= 0)
 
 
-def test_block_config2_full(lib):
-    g = _goldens().get("cfg2_block64")
+def test_block_llm2560_full(lib):
+    g = _goldens().get("llm2560_block64")
     if g is None:
         pytest.skip("oracle golden for the 2560x2560 block run not generated")
-    c = synthetic.CONFIGS[2]
-    A = synthetic.config_matrix(2)
+    c = synthetic.WORKLOADS["llm2560"]
+    A = synthetic.workload_matrix("llm2560")
     res = lib.decompose(_dev(A), c["mu"], c["tau"], c["iters"], c["block"], c["seed"], stats=True)
     E = float(res.energy.item())
     assert abs(E - g["E"]) <= 2e-3, (E, g["E"])

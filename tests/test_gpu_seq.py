@@ -146,9 +146,9 @@ def _check_component(res, A, comp, tau, iters, seed):
 
 @pytest.mark.parametrize("mode", [1, 0])
 @pytest.mark.parametrize("comp", [0, 5, 511])
-def test_capture_parity_config1(lib, mode, comp):
-    c = synthetic.CONFIGS[1]
-    A = synthetic.config_matrix(1)
+def test_capture_parity_gauss256(lib, mode, comp):
+    c = synthetic.WORKLOADS["gauss256"]
+    A = synthetic.workload_matrix("gauss256")
     Ad = _dev(A)
     res = lib.decompose(Ad, c["mu"], c["tau"], c["iters"], 0, c["seed"], mode=mode, capture=comp,
                         stats=True)
@@ -170,9 +170,9 @@ def test_capture_parity_ragged(lib, m, n, comp):
     _check_component(res, A, comp, 1.0, 6, 3)
 
 
-def test_capture_parity_config2_full_size(lib):
-    c = synthetic.CONFIGS[2]
-    A = synthetic.config_matrix(2)
+def test_capture_parity_llm2560_full_size(lib):
+    c = synthetic.WORKLOADS["llm2560"]
+    A = synthetic.workload_matrix("llm2560")
     res = lib.decompose(_dev(A), c["mu"], c["tau"], c["iters"], 0, c["seed"], capture=2, stats=True)
     torch.cuda.synchronize()
     assert res.stat("mode") == 1 and res.stat("grid") == 256
@@ -184,9 +184,9 @@ def test_capture_parity_config2_full_size(lib):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("mode", [1, 0])
-def test_end_to_end_config1(lib, mode):
-    c = synthetic.CONFIGS[1]
-    A = synthetic.config_matrix(1)
+def test_end_to_end_gauss256(lib, mode):
+    c = synthetic.WORKLOADS["gauss256"]
+    A = synthetic.workload_matrix("gauss256")
     Ad = _dev(A)
     res = lib.decompose(Ad, c["mu"], c["tau"], c["iters"], 0, c["seed"], mode=mode, trace=True,
                         stats=True)
@@ -207,12 +207,12 @@ def test_end_to_end_config1(lib, mode):
     assert torch.equal(again.energy, res.energy)
 
 
-def test_end_to_end_config2_sequential(lib):
-    g = _goldens().get("cfg2_seq")
+def test_end_to_end_llm2560_sequential(lib):
+    g = _goldens().get("llm2560_seq")
     if g is None:
         pytest.skip("oracle golden for the 2560x2560 sequential run not generated")
-    c = synthetic.CONFIGS[2]
-    A = synthetic.config_matrix(2)
+    c = synthetic.WORKLOADS["llm2560"]
+    A = synthetic.workload_matrix("llm2560")
     Ad = _dev(A)
     res = lib.decompose(Ad, c["mu"], c["tau"], c["iters"], 0, c["seed"], stats=True)
     E = float(res.energy.item())
@@ -296,11 +296,11 @@ def test_reconstruct_matches_oracle(lib):
 
 
 def test_streaming_beyond_resident_limit(lib):
-    # The config-3 matrix (9728 x 2560) does not fit on chip, so AUTO runs the
+    # The 9728 x 2560 matrix does not fit on chip, so AUTO runs the
     # streaming kernels (float4 GEMVs, register T_tau).  The first 32
     # components against the oracle's, with the per-component trace.
-    c = synthetic.CONFIGS[3]
-    A = synthetic.config_matrix(3)
+    c = synthetic.WORKLOADS["mlp9728"]
+    A = synthetic.workload_matrix("mlp9728")
     m, n = A.shape
     assert not lib.resident_fits(m, n)
     mu = 32.25 / min(m, n)

@@ -85,10 +85,10 @@ def test_sweeps_need_block_mode(lib):
     assert ei.value.status == 1
 
 
-def test_sweeps_config2_full_size(lib):
+def test_sweeps_llm2560_full_size(lib):
     # the 2560 x 2560 LLM-shaped matrix, mu = 2, tau = 0.7, b = 64: one sweep
     # raises the energy and keeps the report consistent with the factors
-    A = synthetic.config_matrix(2)
+    A = synthetic.workload_matrix("llm2560")
     Ad = _dev(A)
     base = lib.decompose(Ad, 2.0, 0.7, 15, 64, 0)
     res = lib.decompose(Ad, 2.0, 0.7, 15, 64, 0, trace=True, stats=True, sweeps=1)

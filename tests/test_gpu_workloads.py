@@ -51,10 +51,10 @@ def _check_full(A, res, g, zf_tol=0.01):
     return E
 
 
-def test_config3_mlp_gate_block128(lib):
-    g = _golden("cfg3_block128")
-    c = synthetic.CONFIGS[3]
-    A = synthetic.config_matrix(3)
+def test_mlp9728_block128(lib):
+    g = _golden("mlp9728_block128")
+    c = synthetic.WORKLOADS["mlp9728"]
+    A = synthetic.workload_matrix("mlp9728")
     res = lib.decompose(torch.from_numpy(A).cuda(), c["mu"], c["tau"], c["iters"], c["block"],
                         c["seed"], stats=True)
     torch.cuda.synchronize()
@@ -63,10 +63,10 @@ def test_config3_mlp_gate_block128(lib):
     assert tuple(res.B2.shape) == (7680, 9728 // 16) and tuple(res.C2.shape) == (7680, 2560 // 16)
 
 
-def test_config4_layer_back_to_back(lib):
-    c = synthetic.CONFIGS[4]
+def test_layer_back_to_back(lib):
+    c = synthetic.WORKLOADS["layer"]
     shapes = synthetic.layer_shapes()
-    mats = {name: synthetic.config_matrix(4, name) for name, _, _ in shapes}
+    mats = {name: synthetic.workload_matrix("layer", name) for name, _, _ in shapes}
     dev = {name: torch.from_numpy(A).cuda() for name, A in mats.items()}
     # all seven decompositions queued on one stream before any check
     outs = {name: lib.decompose(dev[name], c["mu"], c["tau"], c["iters"], c["block"], c["seed"],
@@ -75,12 +75,12 @@ def test_config4_layer_back_to_back(lib):
     torch.cuda.synchronize()
     for name, m, n in shapes:
         assert mats[name].shape == (m, n)
-        _check_full(mats[name], outs[name], _golden(f"cfg4_{name}_block128"))
+        _check_full(mats[name], outs[name], _golden(f"layer_{name}_block128"))
 
 
-def test_config5_mu_tau_sweep(lib):
-    c = synthetic.CONFIGS[5]
-    A = synthetic.config_matrix(5)
+def test_lowrank4096_mu_tau_sweep(lib):
+    c = synthetic.WORKLOADS["lowrank4096"]
+    A = synthetic.workload_matrix("lowrank4096")
     Ad = torch.from_numpy(A).cuda()
     na2 = float(np.sum(A.astype(np.float64) ** 2))
     b = c["block"]
@@ -95,7 +95,7 @@ def test_config5_mu_tau_sweep(lib):
         assert abs(E_full - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
         es = []
         for mu in c["mus"]:
-            g = _golden(f"cfg5_tau{tau}_mu{mu}")
+            g = _golden(f"lowrank4096_tau{tau}_mu{mu}")
             k = oracle.rank_for(4096, 4096, mu)
             assert k % b == 0 and k == g["k"]
             E = 1.0 - tr[k // b - 1] / na2
