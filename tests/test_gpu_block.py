@@ -107,6 +107,26 @@ def test_block_structured_ternary_low_rank(lib):
     assert np.all(np.diff(res.trace.cpu().numpy()) <= 0)
 
 
+def test_block_rank_one_input_nearly_singular_grams(lib):
+    # A = d0 u* v*^T: every column of a 64-wide block is drawn to +-u* and
+    # +-v*, so the block's Gram matrices become nearly singular (only the
+    # eps ridge keeps them invertible) and the decorrelation inverse takes its
+    # slow start from the scaled identity.  The fit must still recover A.
+    m, n, b = 768, 512, 64          # b = 64 needs min(m, n) >= 8 b
+    rng = np.random.default_rng(11)
+    u = rng.choice([-1.0, 0.0, 1.0], m, p=[0.35, 0.3, 0.35])
+    v = rng.choice([-1.0, 0.0, 1.0], n, p=[0.35, 0.3, 0.35])
+    A = (0.75 * np.outer(u, v)).astype(np.float32)
+    res = lib.decompose(_dev(A), b / n, 0.7, 15, b, 0, stats=True)
+    E = float(res.energy.item())
+    B, C, D = _factors(res)
+    assert np.isfinite(E)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
+    assert E > 0.999
+    assert res.stat("timeouts") == 0
+    assert res.stat("ns_restarts") > 0   # the slow start was taken
+
+
 def test_block_llm2560_full(lib):
     g = _goldens().get("llm2560_block64")
     if g is None:
