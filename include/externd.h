@@ -68,15 +68,48 @@ enum externd_stat {
   EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
   EXTERND_STAT_TIMEOUTS = 9,    /* waits that ran out (energy is NaN): resident exchange, or
                                    block mode's Gram-before-inverse wait */
-  EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode, b <= 64: Gram inverses whose Newton-
-                                    Schulz iteration stopped before reaching its tolerance
-                                    (wider blocks invert exactly in fp64: always 0) */
+  EXTERND_STAT_INVERSE_UNCONVERGED = 10, /* block mode, b <= 64: Gram inverses whose fp64
+                                    residual ||I - (G + eps I) X||_F stayed at or above 1e-3
+                                    after the fp64 refinement (the inverse is then not known
+                                    to 1e-6); wider blocks invert exactly in fp64: always 0 */
   EXTERND_STAT_SWEEP_KEPT_OLD = 11, /* block mode: sweep visits that kept the stored block */
   EXTERND_STAT_NS_ITERATIONS = 12,  /* block mode, b <= 64: Newton-Schulz residual evaluations over all Gram inverses */
   EXTERND_STAT_NS_RESTARTS = 13,    /* block mode, b <= 64: warm starts replaced by another start */
   EXTERND_STAT_ITERATIONS = 14,     /* ALS iterations run, over all components (blocks) */
+  EXTERND_STAT_SAFEGUARD = 15,      /* components (sequential) or blocks (block mode) whose
+                                       decrease of ||R||^2 fell below the single-entry bound
+                                       max_ij w_j R_ij^2 of the residual before them, i.e.
+                                       where the §7 safeguard would replace the fit; counted
+                                       whether or not opts.safeguard applies it (extraction
+                                       only, not refinement sweeps) */
   EXTERND_STATS_LEN = 16
 };
+
+/*
+ * Test capture of one iteration of one block of the block path (§2.4), for
+ * checking every step of it on identical inputs.  Every pointer is a device
+ * buffer and may be NULL (that item is not recorded).  Rows are components:
+ * a row of P, Vt, Q or Ut holds one column of the paper's n x b or m x b
+ * matrix.  bb is the width of the captured block (b, or k mod b for a
+ * trailing partial block).  Only the extraction pass is captured, not
+ * refinement sweeps.
+ */
+typedef struct externd_block_capture {
+  int64_t block;       /* block index: components [block * b, block * b + bb) */
+  int32_t iteration;   /* ALS iteration whose two half-steps are recorded (0-based) */
+  int32_t reserved;
+  float* R;            /* m x n: the residual the block is fitted to */
+  uint32_t* U_in;      /* bb x ceil(m/16) code words: U entering the iteration */
+  float* P;            /* bb x n: U^T R, summed over the contraction's splits */
+  float* GinvU;        /* bb x bb: (U^T U + eps I)^-1 as applied */
+  float* Vt;           /* bb x n: decorrelated V target (P (U^T U + eps I)^-1)^T */
+  uint32_t* V;         /* bb x ceil(n/16): T_tau of each row of Vt */
+  float* Q;            /* bb x m: (R diag(w) V)^T (w = 1 unless importance weighted) */
+  float* GinvV;        /* bb x bb: (V^T diag(w) V + eps I)^-1 as applied */
+  float* Ut;           /* bb x m: decorrelated U target */
+  uint32_t* U_out;     /* bb x ceil(m/16): T_tau of each row of Ut */
+  double* rhs;         /* bb: u_j . q_j of the final iteration (joint-solve right side) */
+} externd_block_capture;
 
 /*
  * Optional knobs of externd_decompose.  Zero-initialise, set struct_size to
@@ -93,8 +126,10 @@ typedef struct externd_opts {
                              per-step decrease) or after each block (block mode:
                              ceil(k/b) entries) */
   int64_t* stats;         /* device, optional: EXTERND_STATS_LEN counters (overwritten) */
-  /* Test capture of one component of the sequential path (capture_component
-   * < 0 disables it).  Each pointer may be NULL. */
+  /* Test capture of one component of the sequential path.  It is enabled
+   * when capture_component >= 0 and at least one capture pointer is
+   * non-NULL (a zero-initialised opts captures nothing); each pointer may be
+   * NULL. */
   int64_t capture_component;
   float* capture_R;       /* m*n: residual before the component (row-resident copy) */
   float* capture_Rcol;    /* m*n: the same residual from the column-resident copy */
@@ -140,7 +175,16 @@ typedef struct externd_opts {
    * non-finite entries of h count as non-finite input (energy NaN). */
   const float* importance;
   float importance_lambda; /* >= 0, finite (default 0) */
-  int32_t reserved3;
+  /* Single-entry safeguard (appendix §7, monotone residual decrease): when
+   * the fitted component lowers ||R||^2 by less than max_ij w_j R_ij^2 (the
+   * decrease of the single entry e_r e_c^T with d = R_rc), replace it by that
+   * entry; the smallest row-major index r n + c takes a tie.  0 (default)
+   * leaves every fit as it is; stats[EXTERND_STAT_SAFEGUARD] counts the
+   * would-be replacements either way.  1 applies it: sequential path only,
+   * run in streaming mode (AUTO picks streaming; RESIDENT and block mode give
+   * EXTERND_EUNSUPPORTED). */
+  int32_t safeguard;
+  const externd_block_capture* block_capture; /* HOST pointer, optional (block mode) */
 } externd_opts;
 
 /*
@@ -150,7 +194,8 @@ typedef struct externd_opts {
  *   tau    >= 0, finite: threshold scale of T_tau (§2.2), used as fp32.
  *   iters  >= 1: alternating-fit iterations per component / block (§2.3: 15).
  *   block  <= 1: sequential greedy ALS; otherwise block ALS with
- *          b = externd_block_width(m, n, block) (falls back to sequential if < 2).
+ *          b = externd_block_width(m, n, block) (falls back to sequential if < 2;
+ *          EXTERND_EUNSUPPORTED if b > EXTERND_MAX_BLOCK).
  * Outputs (device): B2 [k][ceil(m/16)] u32, C2 [k][ceil(n/16)] u32, D [k] fp32,
  *   energy [1] fp64 = 1 - ||A - B diag(D) C||^2 / ||A||^2 of the fp32 residual
  *   (1 when ||A|| = 0; NaN when A has non-finite entries).
@@ -193,12 +238,18 @@ int64_t externd_rank(int64_t m, int64_t n, float mu);
  * (externd_opts.norm_a2).  Returns the smallest c = min((j+1) step, total)
  * with 1 - trace[j] / norm_a2 >= target, 0 when norm_a2 = 0, -1 when no
  * prefix reaches the target, and -2 on invalid arguments.  mu = c / min(m, n)
- * reproduces c through externd_rank. */
+ * reproduces c through externd_rank.  energy (HOST, may be NULL) receives the
+ * energy of the returned prefix: 1 - trace[j] / norm_a2, 1 when norm_a2 = 0,
+ * NaN when no prefix reaches the target or the arguments are invalid. */
 int64_t externd_rank_for_energy(const double* trace, int64_t len, int64_t total, int32_t step,
-                                double norm_a2, double target);
+                                double norm_a2, double target, double* energy);
 
-/* Block width actually used for a request: min(block, floor(min(m,n)/8)),
- * 1 meaning sequential (§2.4). */
+/* Block width of a request: min(block, floor(min(m,n)/8)), 1 meaning
+ * sequential (§2.4).  The block kernels take widths up to
+ * EXTERND_MAX_BLOCK: externd_decompose returns EXTERND_EUNSUPPORTED for a
+ * wider one (e.g. the pages' default 256 on a matrix with min(m, n) >=
+ * 2048), rather than silently narrowing the block. */
+#define EXTERND_MAX_BLOCK 128
 int32_t externd_block_width(int64_t m, int64_t n, int32_t block);
 
 /* 1 if the resident sequential kernel can hold an m x n residual on chip. */

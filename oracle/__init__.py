@@ -27,7 +27,7 @@ from .ternarize import (mean_abs_threshold, ternarize, ternarize_columns, optima
 from .init_rule import splitmix64_mix, init_hash, init_signs, init_block
 from .als import (rank_for, block_width, ridge, decompose_seq, decompose_block, rank1_fit,
                   rank_for_energy, importance_weights, weighted_norm2, block_u_target,
-                  block_v_target)
+                  block_v_target, decorrelation_inverse, joint_scales, single_entry_bound)
 from .factors import (reconstruct, apply_factors, energy_from_factors, pack2, unpack2,
                       zero_fraction, bpw_eff, bpw_packed2)
 
@@ -36,7 +36,7 @@ __all__ = [
     "splitmix64_mix", "init_hash", "init_signs", "init_block",
     "rank_for", "block_width", "ridge", "decompose_seq", "decompose_block", "rank1_fit",
     "rank_for_energy", "importance_weights", "weighted_norm2", "block_u_target",
-    "block_v_target",
+    "block_v_target", "decorrelation_inverse", "joint_scales", "single_entry_bound",
     "reconstruct", "apply_factors", "energy_from_factors", "pack2", "unpack2", "zero_fraction",
     "bpw_eff", "bpw_packed2",
 ]

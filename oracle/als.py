@@ -29,6 +29,12 @@ Readings (listed with their reasons in the design doc):
   * Refinement sweeps restart each block's iterations from its stored U and
     keep the refit only if ||R||^2 does not grow, so the energy never falls
     (the pages report a monotone rise).
+  * Safeguard (appendix §7, which only names it): the single-entry bound is
+    max_ij w_j R_ij^2, the decrease of the one-entry component e_r e_c^T with
+    d = R_rc.  A fit whose decrease falls below it "would activate" the
+    safeguard and is counted; with safeguard=True (sequential mode) it is
+    replaced by that entry, the first in row-major order on a tie.  Block
+    mode counts blocks whose joint decrease d . rhs falls below the bound.
 """
 import math
 
@@ -48,7 +54,8 @@ def _tern_cols(X, tau, projection):
 
 __all__ = ["rank_for", "block_width", "ridge", "decompose_seq", "decompose_block",
            "rank1_fit", "SeqResult", "rank_for_energy", "importance_weights", "weighted_norm2",
-           "block_u_target", "block_v_target"]
+           "block_u_target", "block_v_target", "decorrelation_inverse", "joint_scales",
+           "single_entry_bound"]
 
 
 def rank_for(m, n, mu):
@@ -108,6 +115,18 @@ def weighted_norm2(R, w):
     return float(np.sum(R * R)) if w is None else float(np.sum((R * R) @ w))
 
 
+def single_entry_bound(R, w=None):
+    """The single-entry bound of appendix §7: the largest decrease of the
+    weighted residual norm one ternary entry can give, max_ij w_j R_ij^2
+    (the component e_r e_c^T with d = R_rc), and its position (r, c), the
+    first in row-major order on a tie."""
+    R = np.asarray(R, dtype=np.float64)
+    ent = R * R if w is None else (R * R) * np.asarray(w, dtype=np.float64)[None, :]
+    idx = int(np.argmax(ent))
+    r, c = divmod(idx, R.shape[1])
+    return float(ent[r, c]), r, c
+
+
 def rank1_fit(R, u0, tau, iters, w=None, projection=False):
     """Alternating ternary fit of one component against residual R (§2.3 steps 1-2).
 
@@ -140,7 +159,8 @@ def rank1_fit(R, u0, tau, iters, w=None, projection=False):
             "nnz_u": int(nu), "nnz_v": int(nv), "sv": sv, "hist": hist}
 
 
-def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=None, projection=False):
+def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=None, projection=False,
+                  safeguard=False):
     """Greedy sequential ALS (§2.3).  Returns SeqResult.
 
     record: optional set of component indices whose rank1_fit history and
@@ -149,12 +169,16 @@ def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=Non
     trace, norm_a2 and E are then the weighted ones.
     projection: ternarize with the optimal ternary projection instead of
     T_tau (§2.2; tau is then unused).
+    safeguard: replace a fit whose decrease of ||R||^2 falls below the
+    single-entry bound by that single entry (appendix §7).  Either way
+    extra["safeguard_would"] counts the components where it would.
     """
     w = None if weights is None else np.asarray(weights, dtype=np.float64)
     A = np.asarray(A)
     m, n = A.shape
     if k is None:
         k = rank_for(m, n, mu)
+    would = 0
     R = A.astype(np.float64, copy=True)
     norm_a2 = weighted_norm2(R, w)
     B = np.zeros((m, k), dtype=np.int8)
@@ -172,19 +196,32 @@ def decompose_seq(A, mu, tau, iters=15, seed=0, k=None, record=None, weights=Non
         u = fit["u"].astype(np.float64)
         v = fit["v"].astype(np.float64)
         d = fit["d"]
+        den = fit["nnz_u"] * fit["sv"]
+        dec = fit["c"] ** 2 / den if den > 0 else 0.0
+        bound, br, bc = single_entry_bound(R, w)
+        if dec < bound:
+            would += 1
+            if safeguard:
+                u = np.zeros(m)
+                v = np.zeros(n)
+                u[br] = 1.0
+                v[bc] = 1.0
+                d = float(R[br, bc])
+                dec = bound
         R -= d * np.outer(u, v)
-        B[:, i] = fit["u"]
-        C[i, :] = fit["v"]
+        B[:, i] = u.astype(np.int8)
+        C[i, :] = v.astype(np.int8)
         D[i] = d
         trace[i] = weighted_norm2(R, w)
-        decrease[i] = fit["c"] ** 2 / (fit["nnz_u"] * fit["sv"])
+        decrease[i] = dec
         sum_nnz_u += sum(int(np.count_nonzero(h[3])) for h in fit["hist"])
         if record is not None and i in record:
             records[i]["fit"] = fit
     last = trace[k - 1] if k > 0 else norm_a2
     E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
     return SeqResult(B, C, D, trace, E, norm_a2,
-                     {"decrease": decrease, "records": records, "sum_nnz_u": sum_nnz_u})
+                     {"decrease": decrease, "records": records, "sum_nnz_u": sum_nnz_u,
+                      "safeguard_would": would})
 
 
 def _cholesky_solve(G, rhs, eps):
@@ -193,6 +230,13 @@ def _cholesky_solve(G, rhs, eps):
     Lc = np.linalg.cholesky(Gr)
     z = np.linalg.solve(Lc, rhs)
     return np.linalg.solve(Lc.T, z)
+
+
+def decorrelation_inverse(G):
+    """(G + eps I)^-1 with the ridge eps of the decorrelated targets (§2.4),
+    by Cholesky in fp64."""
+    G = np.asarray(G, dtype=np.float64)
+    return _cholesky_solve(G, np.eye(G.shape[0]), ridge(G))
 
 
 def block_v_target(R, U):
@@ -222,6 +266,12 @@ def _fit_block(R, U, tau, iters, w=None, projection=False):
         T, Q = block_u_target(R, V, w)
         U = _tern_cols(T, tau, projection).astype(np.float64)
     return U, V, Q
+
+
+def joint_scales(U, V, Q, w=None):
+    """The joint scale solve of §2.4 (see _joint_scales): returns (d, rhs)."""
+    d, rhs, _ = _joint_scales(U, V, Q, w)
+    return d, rhs
 
 
 def _joint_scales(U, V, Q, w=None):
@@ -284,12 +334,15 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     trace = np.zeros(nblocks, dtype=np.float64)
     decrease = np.zeros(nblocks, dtype=np.float64)
     ridge_retries = 0
+    would = 0
     for blk in range(nblocks):
         c0 = blk * b
         bb = min(b, k - c0)
+        bound = single_entry_bound(R, w)[0]
         U, V, Q = _fit_block(R, init_block(seed, c0, bb, m), tau, iters, w, projection)
         d, rhs, retried = _joint_scales(U, V, Q, w)
         ridge_retries += int(retried)
+        would += int(float(d @ rhs) < bound)
         R -= (U * d) @ V.T
         B[:, c0:c0 + bb] = U.astype(np.int8)
         C[c0:c0 + bb, :] = V.T.astype(np.int8)
@@ -323,7 +376,8 @@ def decompose_block(A, mu, tau, iters=15, block=256, seed=0, k=None, force_width
     E = 1.0 - last / norm_a2 if norm_a2 > 0 else 1.0
     return SeqResult(B, C, D, trace, E, norm_a2,
                      {"decrease": decrease, "b": b, "ridge_retries": ridge_retries,
-                      "sweep_trace": sweep_trace, "sweep_kept_old": kept_old})
+                      "sweep_trace": sweep_trace, "sweep_kept_old": kept_old,
+                      "safeguard_would": would})
 
 
 def rank_for_energy(trace, norm_a2, target, step=1, total=None):

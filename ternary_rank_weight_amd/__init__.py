@@ -28,7 +28,7 @@ STATS_LEN = 16
 STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
         "nonfinite": 5, "mode": 6, "grid": 7, "ridge_retries": 8, "timeouts": 9,
         "inverse_unconverged": 10, "sweep_kept_old": 11, "ns_iterations": 12, "ns_restarts": 13,
-        "iterations": 14}
+        "iterations": 14, "safeguard": 15}
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is missing; build it with "
@@ -39,6 +39,14 @@ _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 _f32 = ctypes.c_float
+
+
+class _BlockCapture(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int64), ("iteration", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("R", _p), ("U_in", _p), ("P", _p), ("GinvU", _p), ("Vt", _p), ("V", _p),
+        ("Q", _p), ("GinvV", _p), ("Ut", _p), ("U_out", _p), ("rhs", _p),
+    ]
 
 
 class _Opts(ctypes.Structure):
@@ -53,7 +61,8 @@ class _Opts(ctypes.Structure):
         ("workspace", _p), ("workspace_bytes", ctypes.c_uint64),
         ("norm_a2", _p),
         ("sweeps", _i32), ("ternarizer", _i32), ("sweep_trace", _p),
-        ("importance", _p), ("importance_lambda", ctypes.c_float), ("reserved3", _i32),
+        ("importance", _p), ("importance_lambda", ctypes.c_float), ("safeguard", _i32),
+        ("block_capture", ctypes.POINTER(_BlockCapture)),
     ]
 
 
@@ -74,7 +83,8 @@ _block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
 _resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
 _workspace_bytes = _sig("externd_workspace_bytes", ctypes.c_uint64, [_i64, _i64, _f32, _i32, _i32])
 _rank_for_energy = _sig("externd_rank_for_energy", ctypes.c_int64,
-                        [ctypes.POINTER(ctypes.c_double), _i64, _i64, _i32, ctypes.c_double, ctypes.c_double])
+                        [ctypes.POINTER(ctypes.c_double), _i64, _i64, _i32, ctypes.c_double, ctypes.c_double,
+                         ctypes.POINTER(ctypes.c_double)])
 _ternarize = _sig("externd_ternarize", ctypes.c_int, [_p, _i64, _f32, _p, _p, _p])
 _project = _sig("externd_project", ctypes.c_int, [_p, _i64, _p, _p, _p])
 _gemv_t = _sig("externd_gemv_t", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p])
@@ -161,7 +171,7 @@ class Decomposition:
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
               capture=None, out=None, workspace=None, sweeps=0, importance=None, lam=0.0,
-              projection=False):
+              projection=False, safeguard=False, block_capture=None):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
@@ -177,6 +187,11 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
     ALS), and energy / trace / norm_a2 become weighted.
     projection: use the optimal ternary projection instead of T_tau
     (streaming or block mode; AUTO picks streaming).
+    safeguard: apply the single-entry safeguard (sequential path, streaming
+    mode); stats["safeguard"] counts the would-be replacements either way.
+    block_capture: (block index, iteration) of the block path to record; the
+    tensors land in .block_capture (R, U_in, P, GinvU, Vt, V, Q, GinvV, Ut,
+    U_out, rhs; rows are components, codes as int32 words).
     """
     _need(A, torch.float32, "A")
     if A.dim() != 2:
@@ -215,6 +230,7 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
         opts.importance = _ptr(importance)
     opts.importance_lambda = float(lam)
     opts.ternarizer = 1 if projection else 0
+    opts.safeguard = 1 if safeguard else 0
     opts.capture_component = -1
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
@@ -243,23 +259,46 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
         opts.capture_v = _ptr(cap["v"])
         opts.capture_u = _ptr(cap["u"])
         opts.capture_d = _ptr(cap["d"])
+    bcap = None
+    if block_capture is not None:
+        blk, it = block_capture
+        bb = min(b, k - blk * b) if b > 1 else 0
+        if b <= 1 or not 0 <= blk * b < k:
+            raise ValueError("block_capture needs block mode and a block index below ceil(k/b)")
+        wm, wn = (m + 15) // 16, (n + 15) // 16
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        bcap = {"R": torch.empty((m, n), **f32), "U_in": torch.empty((bb, wm), **i32),
+                "P": torch.empty((bb, n), **f32), "GinvU": torch.empty((bb, bb), **f32),
+                "Vt": torch.empty((bb, n), **f32), "V": torch.empty((bb, wn), **i32),
+                "Q": torch.empty((bb, m), **f32), "GinvV": torch.empty((bb, bb), **f32),
+                "Ut": torch.empty((bb, m), **f32), "U_out": torch.empty((bb, wm), **i32),
+                "rhs": torch.empty((bb,), dtype=torch.float64, device=dev)}
+        bc = _BlockCapture()
+        bc.block, bc.iteration = int(blk), int(it)
+        for name, tensor in bcap.items():
+            setattr(bc, name, _ptr(tensor))
+        opts.block_capture = ctypes.pointer(bc)
     _check(_decompose(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
                       _ptr(D), _ptr(E), ctypes.byref(opts)))
     res = Decomposition(m, n, k, B2, C2, D, E, tr, st, cap, na2, b)
     res.sweep_trace = swt
+    res.block_capture = bcap
     return res
 
 
-def rank_for_energy(trace, total, step, norm_a2, target):
+def rank_for_energy(trace, total, step, norm_a2, target, with_energy=False):
     """Smallest prefix rank whose energy reaches target (host-side scan of a
-    trace; see externd_rank_for_energy).  -1 if none does."""
+    trace; see externd_rank_for_energy).  -1 if none does.  with_energy:
+    return (rank, energy of that prefix) instead, the energy NaN for -1."""
     import numpy as np
     tr = np.ascontiguousarray(np.asarray(trace, dtype=np.float64))
+    e = ctypes.c_double(0.0)
     r = int(_rank_for_energy(tr.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), tr.size, int(total),
-                             int(step), float(norm_a2), float(target)))
+                             int(step), float(norm_a2), float(target), ctypes.byref(e)))
     if r == -2:
         raise ExterndError(1)
-    return r
+    return (r, e.value) if with_energy else r
 
 
 def mu_for_energy(A, target, mu_max, tau, iters=15, block=0, seed=0):
@@ -270,11 +309,10 @@ def mu_for_energy(A, target, mu_max, tau, iters=15, block=0, seed=0):
     torch.cuda.synchronize()
     tr = res.trace.cpu().numpy()
     a2 = float(res.norm_a2.item())
-    c = rank_for_energy(tr, res.k, res.block, a2, target)
+    c, e = rank_for_energy(tr, res.k, res.block, a2, target, with_energy=True)
     if c < 0:
         return None
     m, n = A.shape
-    e = 1.0 if a2 == 0.0 or c == 0 else 1.0 - tr[(c + res.block - 1) // res.block - 1] / a2
     return c / min(m, n), c, e
 
 

@@ -142,13 +142,19 @@ int64_t externd_rank(int64_t m, int64_t n, float mu) {
 }
 
 int64_t externd_rank_for_energy(const double* trace, int64_t len, int64_t total, int32_t step,
-                                double norm_a2, double target) {
+                                double norm_a2, double target, double* energy) {
+  if (energy) *energy = std::nan("");
   if (len < 0 || total < 0 || step < 1 || (len > 0 && !trace) || !std::isfinite(target) ||
       !std::isfinite(norm_a2) || norm_a2 < 0.0)
     return (fail(EXTERND_EINVAL, "bad arguments to externd_rank_for_energy"), -2);
-  if (norm_a2 == 0.0) return 0;
+  if (norm_a2 == 0.0) {
+    if (energy) *energy = 1.0;
+    return 0;
+  }
   for (int64_t j = 0; j < len; ++j) {
-    if (1.0 - trace[j] / norm_a2 >= target) {
+    const double e = 1.0 - trace[j] / norm_a2;
+    if (e >= target) {
+      if (energy) *energy = e;
       const int64_t c = (j + 1) * (int64_t)step;
       return c < total ? c : total;
     }
@@ -182,7 +188,7 @@ uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, 
   if (mode == EXTERND_MODE_RESIDENT && !fits)
     return (fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel",
                  (long long)m, (long long)n), 0);
-  return fits ? externd::resident_workspace_bytes(m, n) : externd::stream_workspace_bytes(m, n);
+  return fits ? externd::resident_workspace_bytes(m, n, externd_rank(m, n, mu)) : externd::stream_workspace_bytes(m, n);
 }
 
 int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau, int32_t iters,
@@ -220,9 +226,26 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     return fail(EXTERND_EUNSUPPORTED, "the optimal projection runs in streaming or block mode");
   if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
     return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
+  if (o.safeguard != 0 && o.safeguard != 1) return fail(EXTERND_EINVAL, "bad safeguard %d", o.safeguard);
   const int b = externd_block_width(m, n, block);
+  if (b > EXTERND_MAX_BLOCK)
+    return fail(EXTERND_EUNSUPPORTED, "block width %d exceeds the widest supported block, %d", b,
+                EXTERND_MAX_BLOCK);
   if (o.sweeps > 0 && b == 1)
     return fail(EXTERND_EINVAL, "refinement sweeps need block mode (block width %d)", b);
+  if (o.safeguard && b > 1)
+    return fail(EXTERND_EUNSUPPORTED, "the safeguard's replacement runs in the sequential path only");
+  if (o.safeguard && projection)
+    return fail(EXTERND_EUNSUPPORTED, "the safeguard is not combined with the optimal projection");
+  if (o.safeguard && o.mode == EXTERND_MODE_RESIDENT)
+    return fail(EXTERND_EUNSUPPORTED, "the safeguard's replacement runs in streaming mode");
+  const externd_block_capture* bc = o.block_capture;
+  if (bc && b > 1) {
+    const int64_t nblocks = (k + b - 1) / b;
+    if (bc->block < 0 || bc->block >= nblocks || bc->iteration < 0 || bc->iteration >= iters)
+      return fail(EXTERND_EINVAL, "block capture (block %lld, iteration %d) out of range",
+                  (long long)bc->block, bc->iteration);
+  }
   int cus = 0;
   int st = check_device(&cus);
   if (st != EXTERND_OK) return st;
@@ -250,6 +273,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     ba.importance = o.importance;
     ba.lambda = o.importance_lambda;
     ba.projection = projection ? 1 : 0;
+    ba.cap = bc;
     Workspace w;
     if ((st = get_ws(w, o, externd::block_workspace_bytes(m, n, b), s)) != EXTERND_OK) return st;
     hipError_t e = externd::run_block(ba, w.ptr, s);
@@ -275,8 +299,11 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   sa.importance = o.importance;
   sa.lambda = o.importance_lambda;
   sa.projection = projection ? 1 : 0;
+  sa.safeguard = o.safeguard;
+  const bool any_capture = o.capture_R || o.capture_Rcol || o.capture_R_next || o.capture_y ||
+                           o.capture_x || o.capture_v || o.capture_u || o.capture_d;
   sa.capture_component = o.capture_component;
-  if (o.capture_component >= 0) {
+  if (o.capture_component >= 0 && any_capture) {
     if (o.capture_component >= k) return fail(EXTERND_EINVAL, "capture_component >= k");
     sa.capture_R = o.capture_R;
     sa.capture_Rcol = o.capture_Rcol;
@@ -291,14 +318,15 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   }
   const bool fits = externd::resident_fits(m, n, cus);
   int mode = o.mode;
-  if (mode == EXTERND_MODE_AUTO) mode = (fits && !projection) ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
+  if (mode == EXTERND_MODE_AUTO)
+    mode = (fits && !projection && !o.safeguard) ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
   if (mode == EXTERND_MODE_RESIDENT && !fits)
     return fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel", (long long)m,
                 (long long)n);
   Workspace w;
   hipError_t e;
   if (mode == EXTERND_MODE_RESIDENT) {
-    if ((st = get_ws(w, o, externd::resident_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
+    if ((st = get_ws(w, o, externd::resident_workspace_bytes(m, n, k), s)) != EXTERND_OK) return st;
     int grid = 0;
     e = externd::run_resident_seq(sa, w.ptr, cus, s, &grid);
     if (e != hipSuccess) return hip_fail(e, "resident decomposition");

@@ -644,6 +644,7 @@ struct NsShared {
   unsigned short Rt[3][kNsB * kNsB];   // parts of R, transposed
   float red[kCT / kWave];              // per-wave partials of ||R||_F^2
   double dred[kCT / kWave];
+  double diag64[kNsB];                 // G_ii + eps in fp64 (the refinement's diagonal)
 };
 // Index of element (row, k) of a stored part.
 __device__ inline int ns_at(int row, int k) { return row * kNsB + ((((k >> 3) ^ (row & 7))) << 3) + (k & 7); }
@@ -699,6 +700,14 @@ __device__ inline bf16x8 ns_ld_col(const unsigned short* buf, int k0, int col) {
     q[e] = (uint32_t)buf[ns_at(k0 + 2 * e, col)] | ((uint32_t)buf[ns_at(k0 + 2 * e + 1, col)] << 16);
   return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[2], q[3]});
 }
+// Element (row, k) of a stored three-part value, in fp64: h + m + l is the
+// fp32 value exactly.
+__device__ inline double ns_value(const unsigned short (*buf)[kNsB * kNsB], int row, int k) {
+  const int at = ns_at(row, k);
+  return (double)__uint_as_float((uint32_t)buf[0][at] << 16) + (double)__uint_as_float((uint32_t)buf[1][at] << 16) +
+         (double)__uint_as_float((uint32_t)buf[2][at] << 16);
+}
+
 __device__ inline f4 ns_mfma6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f4 acc) {
   acc = mfma16x16x32bf16(a[0], b[0], acc);
   acc = mfma16x16x32bf16(a[0], b[1], acc);
@@ -791,7 +800,16 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   double tr = sh.dred[0];
 #pragma unroll
   for (int q = 1; q < kCT / kWave; ++q) tr += sh.dred[q];
-  const float eps = (float)(1e-6 * tr / bb);
+  const double eps64 = 1e-6 * tr / bb;
+  const float eps = (float)eps64;
+  // the exact diagonal of G' for the fp64 refinement (1 beyond bb)
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * g + v, c = 16 * J + i16;
+      if (r == c) sh.diag64[r] = r < bb ? (double)gv[J][v] + eps64 : 1.0;
+    }
   // G' = G + eps I (the identity beyond bb), fp32, then its parts in LDS
   f4 gp[4];
 #pragma unroll
@@ -916,6 +934,78 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
       break;
     }
   }
+  // fp64 refinement.  The fp32 iteration above cannot certify better than
+  // about 1e-4 (its residual is itself computed in fp32), so the residual
+  // R = I - G'X of the fp32 X is formed exactly enough in fp64 (fp64 MFMA
+  // 16x16x4; G' from its stored parts with the exact fp64 diagonal, X from
+  // its parts: every product is exact) and one more step X <- X + X R is
+  // taken, which leaves a residual of ||R||_F^2 (the update itself is the
+  // six-product bf16 form: it only needs the small correction X R to a few
+  // digits).  A step is accepted once the fp64 residual is below 1e-3, so
+  // the inverse is then known to about 1e-6 relative; otherwise (at most
+  // three rounds) it is counted as unconverged.  The fp64 MFMA layout: lane
+  // (j + 16 kk) supplies A[j][kk] and B[kk][j] of each 4-long k slice, and
+  // output register v of lane (j + 16 g) is entry (g + 4 v, j).
+  bool conv64 = false;
+  if (conv) {
+    __syncthreads();   // every read of Xt, Rt and red by the loop done
+    for (int round = 0; round < 3 && !conv64; ++round) {
+      d4 racc[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) racc[J] = d4{0.0, 0.0, 0.0, 0.0};
+      const int kk = g;   // this lane's k within a slice
+      for (int q = 0; q < kNsB / 4; ++q) {
+        const int kcol = 4 * q + kk, arow = 16 * w + i16;
+        const double a = arow == kcol ? sh.diag64[arow] : ns_value(sh.Gp, arow, kcol);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) racc[J] = mfma16x16x4f64(a, ns_value(sh.Xt, 16 * J + i16, kcol), racc[J]);
+      }
+      double rp = 0.0;
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 16 * w + g + 4 * v, c = 16 * J + i16;
+          const double rv = ((r == c) ? 1.0 : 0.0) - racc[J][v];
+          racc[J][v] = rv;
+          rp = fma(rv, rv, rp);
+        }
+      rp = wave_sum_to63(rp);
+      if (lane == kWave - 1) sh.dred[w] = rp;
+      // R (rounded to fp32: it only enters the small correction) as
+      // transposed parts: element (c, r) of Rt holds R[r][c]
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          uint32_t hp, mp, lp;
+          ns_split3((float)racc[J][v], hp, mp, lp);
+          const int at = ns_at(16 * J + i16, 16 * w + g + 4 * v);
+          sh.Rt[0][at] = (unsigned short)hp;
+          sh.Rt[1][at] = (unsigned short)mp;
+          sh.Rt[2][at] = (unsigned short)lp;
+        }
+      __syncthreads();
+      double rn64 = sh.dred[0];
+#pragma unroll
+      for (int q = 1; q < kCT / kWave; ++q) rn64 += sh.dred[q];
+      if (!(rn64 < 0.25)) break;   // too far for a single step: leave it counted
+      conv64 = rn64 < 1e-6;        // ||R||_F < 1e-3
+      f4 y[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) y[J] = f4{0.f, 0.f, 0.f, 0.f};
+      ns_gemm_xr(sh, w, i16, g, y);
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xv[J][v] += y[J][v];
+      __syncthreads();   // every read of Xt, Rt and dred done
+      if (!conv64) {
+        ns_store_t(sh.Xt, xv, w, i16, g);
+        __syncthreads();
+      }
+    }
+  }
 #pragma unroll
   for (int J = 0; J < 4; ++J)
 #pragma unroll
@@ -925,7 +1015,7 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
     }
   if (t == 0) {
     *warm_flag = 1;
-    if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_INVERSE_UNCONVERGED), 1ull);
+    if (!conv64) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_INVERSE_UNCONVERGED), 1ull);
     atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_ITERATIONS), (unsigned long long)iters_done);
     if (restarted) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_RESTARTS), 1ull);
   }
@@ -1359,7 +1449,8 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
                                                         long long* __restrict__ st, const int* __restrict__ nnz,
                                                         int bstride, const double* __restrict__ dpart,
                                                         int64_t ndpart, const double* __restrict__ dold,
-                                                        int* __restrict__ accept) {
+                                                        int* __restrict__ accept,
+                                                        unsigned long long* __restrict__ maxw2) {
   constexpr int TR = (T + 3) / 4;
   __shared__ SweepShared<T> sh;
   __shared__ double rhs[kMaxB];
@@ -1452,6 +1543,13 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
       atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_SWEEP_KEPT_OLD), 1ull);
     }
     if (accept) *accept = take ? 1 : 0;
+    // Single-entry safeguard check (appendix §7): would the best single entry
+    // of the residual this block was fitted to, max_ij w_j R_ij^2, have
+    // lowered ||R||^2 more than the block did?  Counted on extraction only;
+    // the bound is then reset for the deflation to raise it again.
+    if (!dpart && dec < __longlong_as_double((long long)*maxw2))
+      atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_SAFEGUARD), 1ull);
+    *maxw2 = 0ull;
     const double tnew = take ? trace_state[0] + added - dec : trace_state[0];
     trace_state[0] = tnew;
     if (trace) trace[blk] = tnew;
@@ -1496,7 +1594,8 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
                                                        const uint32_t* __restrict__ Ucodes, int64_t wm,
                                                        const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                        const double* __restrict__ d, int bb,
-                                                       double* __restrict__ dpart, const float* __restrict__ wt) {
+                                                       double* __restrict__ dpart, const float* __restrict__ wt,
+                                                       unsigned long long* __restrict__ maxw2) {
   __shared__ DeflateLds st;
   __shared__ double red[256 / kWave];
   const int t = threadIdx.x;
@@ -1570,7 +1669,7 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
         acc[s] = mfma16x16x32bf16(a, *reinterpret_cast<const bf16x8*>(&st.v[q][16 * s + i][k0 + 8 * g]), acc[s]);
   }
   // D[4g + v][i]: row r0 + 16 w + 4 g + v, column c0 + 16 s + i
-  double change = 0.0;
+  double change = 0.0, mx = 0.0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t col = c0 + 16 * s + i;
@@ -1582,9 +1681,13 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
         R[row * n + col] = upd;
         const double ch = (double)upd * (double)upd - (double)old[s][v] * (double)old[s][v];
         change += wt ? ch * (double)wt[col] : ch;
+        const double e = (double)upd * (double)upd;
+        mx = fmax(mx, wt ? e * (double)wt[col] : e);
       }
     }
   }
+  // the single-entry bound of the new residual (appendix §7), for the next block's check
+  if (maxw2) wave_max_nonneg_to(mx, maxw2);
   if (dpart) {
     const double tot = block_sum<256>(change, red);
     if (threadIdx.x == 0) dpart[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = tot;
@@ -1703,7 +1806,7 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   // importance weights: column weights, weighted Gram and its split partials
   by += sizeof(float) * (size_t)n;
   by += sizeof(double) * (size_t)b * b * (1 + ((n + 15) / 16 + kGramSplit - 1) / kGramSplit);
-  by += sizeof(unsigned long long) * 2;   // Gram tile counters
+  by += sizeof(unsigned long long) * 3;   // Gram tile counters, single-entry bound
   by += 29 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
@@ -1789,7 +1892,9 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   int* accept = reinterpret_cast<int*>(bump(p, sizeof(int)));
   // Gram tiles finished inside the combined launches (U side, V side),
   // counting up over the whole decomposition
-  unsigned long long* gram_done = reinterpret_cast<unsigned long long*>(bump(p, sizeof(unsigned long long) * 2));
+  unsigned long long* gram_done = reinterpret_cast<unsigned long long*>(bump(p, sizeof(unsigned long long) * 3));
+  // bits of the single-entry bound max_ij w_j R_ij^2 of the current residual
+  unsigned long long* sg_max = gram_done + 2;
   unsigned long long gram_issued[2] = {0ull, 0ull};
   // importance weighting (§2.5): column weights wt, the weighted V-side Gram
   // V^T diag(wt) V and its per-split partials
@@ -1807,12 +1912,13 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if (W && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
     return e;
-  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n)) != hipSuccess) return e;
+  if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 3, 0, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n, sg_max)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
-  if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 2, 0, s)) != hipSuccess) return e;
   const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
   const int64_t ndpart = (int64_t)defl_grid.x * defl_grid.y;
 
@@ -1821,8 +1927,11 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   // goes (may be null).  On a sweep visit dpart holds the exact rise of
   // ||R||^2 from adding the stored block back, dold its scales and saved its
   // codes; the solve keeps whichever block lowers ||R||^2 more.
+  // cap (optional): record iteration cap->iteration of this block and the
+  // final right-hand side (test capture, extraction only).
   auto fit_block = [&](int bb, uint32_t* Uc, uint32_t* Vc, float* Dout, double* trace, int64_t tidx,
-                       const double* dpart, const double* dold, const uint32_t* saved) {
+                       const double* dpart, const double* dold, const uint32_t* saved,
+                       const externd_block_capture* cap) -> hipError_t {
     // column-wise ternarizer: T_tau, or the optimal projection (§2.2)
     auto row_tern = [&](const float* Xt, int64_t L, uint32_t* codes, int64_t wl, int* nz, long long* nz_sum,
                         const float* Qrows, double* rhs_out) {
@@ -1841,7 +1950,15 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const int gw = gram_words(bb);
     const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + gw - 1) / gw));
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + gw - 1) / gw));
+    hipError_t ce = hipSuccess;
+    auto cap_copy = [&](const void* src, void* dst, int64_t words) {   // 4-byte words
+      if (dst && ce == hipSuccess)
+        ce = launch_copy_f32(static_cast<const float*>(src), static_cast<float*>(dst), words, s);
+    };
+    if (cap) cap_copy(R, cap->R, m * n);
     for (int it = 0; it < a.iters; ++it) {
+      const bool capit = cap && it == cap->iteration;
+      if (capit) cap_copy(Uc, cap->U_in, (int64_t)bb * wm);
       // V <- T_col( P (U^T U + eps I)^-1 ),  P = R^T U.  The Gram and its
       // inverse depend only on U's codes, so they run as the first
       // workgroups of the contraction launch, concurrently with it
@@ -1852,8 +1969,13 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         gram_issued[0] += (unsigned long long)ng;
         launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, bb <= 64 ? warm : fail, st, (const float*)nullptr, gram_done, gram_issued[0]);
       }
-      launch_decorrelate(bb, s, Pt_part, L.S1, n, GinvU, Vt, (float*)nullptr);
+      if (capit) cap_copy(GinvU, cap->GinvU, (int64_t)bb * bb);
+      launch_decorrelate(bb, s, Pt_part, L.S1, n, GinvU, Vt, capit ? cap->P : (float*)nullptr);
       row_tern(Vt, n, Vc, wn, nnz + b, st + EXTERND_STAT_SUM_NNZ_V, (const float*)nullptr, (double*)nullptr);
+      if (capit) {
+        cap_copy(Vt, cap->Vt, (int64_t)bb * n);
+        cap_copy(Vc, cap->V, (int64_t)bb * wn);
+      }
       // U <- T_col( Q (V^T V + eps I)^-1 ),  Q = R V;  weighted (§2.5):
       // Q = R diag(wt) V and the Gram V^T diag(wt) V
       if (W) {
@@ -1865,9 +1987,17 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         gram_issued[1] += (unsigned long long)ng;
         launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
       }
+      if (capit) cap_copy(GinvV, cap->GinvV, (int64_t)bb * bb);
       launch_decorrelate(bb, s, Qt_part, L.S2, m, GinvV, Ut, Qt);
       row_tern(Ut, m, Uc, wm, nnz, st + EXTERND_STAT_SUM_NNZ_U, (const float*)Qt, it == a.iters - 1 ? rhs : (double*)nullptr);
+      if (capit) {
+        cap_copy(Qt, cap->Q, (int64_t)bb * m);
+        cap_copy(Ut, cap->Ut, (int64_t)bb * m);
+        cap_copy(Uc, cap->U_out, (int64_t)bb * wm);
+      }
     }
+    if (cap && cap->rhs && ce == hipSuccess) ce = launch_copy_f64(rhs, cap->rhs, bb, s);
+    if (ce != hipSuccess) return ce;
     // joint scales from the final U, V and the last Q = R V (weighted: the
     // last V-side Gram GVw already belongs to the final V)
     hipLaunchKernelGGL(k_gram, gram_u, dim3(256), 0, s, Uc, wm, bb, GUf, gw);
@@ -1875,16 +2005,16 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     int* acc = dpart ? accept : nullptr;
     const double* gvw = W ? GVw : nullptr;
     if (bb <= 16)
-      hipLaunchKernelGGL(k_joint_solve<1>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<1>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
     else if (bb <= 32)
-      hipLaunchKernelGGL(k_joint_solve<2>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<2>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
     else if (bb <= 64)
-      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
     else
-      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc);
+      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
     if (dpart)
       hipLaunchKernelGGL(k_sweep_restore, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, accept, bb, Uc, wm, Vc, wn, saved);
-    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr, (const float*)nullptr);
+    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr, (const float*)wt, sg_max);
     return hipGetLastError();
   };
 
@@ -1893,7 +2023,9 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const int64_t c0 = blk * b;
     const int bb = (int)std::min<int64_t>(b, k - c0);
     hipLaunchKernelGGL(k_block_start, dim3(grid1d((int64_t)bb * wm, 256)), dim3(256), 0, s, a.seed, c0, bb, m, a.B2, warm);
-    if ((e = fit_block(bb, a.B2 + c0 * wm, a.C2 + c0 * wn, a.D + c0, a.trace, blk, nullptr, nullptr, nullptr)) != hipSuccess)
+    const externd_block_capture* cap = (a.cap && a.cap->block == blk) ? a.cap : nullptr;
+    if ((e = fit_block(bb, a.B2 + c0 * wm, a.C2 + c0 * wn, a.D + c0, a.trace, blk, nullptr, nullptr, nullptr, cap)) !=
+        hipSuccess)
       return e;
   }
   // Refinement sweeps (§2.4): add each block back, refit it from its stored
@@ -1905,9 +2037,9 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       uint32_t* Uc = a.B2 + c0 * wm;
       uint32_t* Vc = a.C2 + c0 * wn;
       hipLaunchKernelGGL(k_sweep_prepare, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, bb, Uc, wm, Vc, wn, a.D + c0, saved, dold, dneg, warm);
-      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart, (const float*)wt);
+      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart, (const float*)wt, sg_max);
       double* tr = (blk == nblocks - 1) ? a.sweep_trace : nullptr;
-      if ((e = fit_block(bb, Uc, Vc, a.D + c0, tr, sw, dpart, dold, saved)) != hipSuccess) return e;
+      if ((e = fit_block(bb, Uc, Vc, a.D + c0, tr, sw, dpart, dold, saved, nullptr)) != hipSuccess) return e;
     }
   }
   if (a.sweeps > 0 && k > 0) {

@@ -84,6 +84,20 @@ __device__ inline int wave_min_i(int v) {
   return v;
 }
 
+// Max of a non-negative fp64 value over the wave, raised into *slot with one
+// atomic per wave: the bit patterns of non-negative doubles are ordered like
+// their values, so an unsigned 64-bit max is the fp64 max.  Every lane of
+// the wave must call.
+__device__ inline void wave_max_nonneg_to(double v, unsigned long long* slot) {
+  unsigned long long b = (unsigned long long)__double_as_longlong(v);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(b, off, kWave);
+    b = o > b ? o : b;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0 && b != 0ull) atomicMax(slot, b);
+}
+
 template <int T, typename V>
 __device__ inline V block_sum(V v, V* scratch) {
   v = wave_sum(v);

@@ -35,6 +35,7 @@ struct SeqArgs {
   const float* importance;   // optional: n per-input-channel second moments h (§2.5)
   float lambda;              // column weights h / max(h) + lambda
   int projection;            // 1: optimal ternary projection instead of T_tau (§2.2)
+  int safeguard;             // 1: apply the single-entry safeguard (appendix §7; streaming only)
 };
 
 // Arguments of one block-mode decomposition.
@@ -57,6 +58,7 @@ struct BlockArgs {
   const float* importance;   // optional: n per-input-channel second moments h (§2.5)
   float lambda;              // column weights h / max(h) + lambda
   int projection;            // 1: optimal ternary projection instead of T_tau (§2.2)
+  const externd_block_capture* cap;   // optional test capture (host struct of device pointers)
 };
 
 // streaming sequential path and single-step kernels (seq_stream.hip)
@@ -71,16 +73,21 @@ constexpr int kProjMaxN = 16384;   // longest vector it takes (128 KB of sort ke
 hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
                           hipStream_t s, const float* wt = nullptr, double* wsum = nullptr,
                           long long* nnz_sum = nullptr);
+// maxw2 (optional, only with a dense u, so that every row is read): raised
+// to the bits of max w_c R_rc^2 of R after the fused deflation.
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
-                         const uint32_t* vprev, hipStream_t s);
+                         const uint32_t* vprev, hipStream_t s, unsigned long long* maxw2 = nullptr,
+                         const float* wt = nullptr);
 hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
                          hipStream_t s, const float* wt = nullptr);
 hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
                           const uint32_t* v_codes, const float* dptr, hipStream_t s);
+// ||A||_F^2 (weighted by wt[column] when given) in a fixed order; maxw2
+// (optional, zeroed by the caller) is raised to the bits of max wt_j A_ij^2.
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
                         double* out, long long* nonfinite, hipStream_t s, const float* wt = nullptr,
-                        int64_t ncols = 0);
+                        int64_t ncols = 0, unsigned long long* maxw2 = nullptr);
 // Column weights wt[j] = h[j] / max(h) + lambda in fp32 (§2.5); negative or
 // non-finite h entries are added to *nonfinite.
 hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, float* wt,
@@ -95,7 +102,7 @@ hipError_t launch_copy_f32(const float* a, float* b, int64_t count, hipStream_t 
 
 // resident sequential path (seq_resident.hip)
 bool resident_fits(int64_t m, int64_t n, int num_cus);
-size_t resident_workspace_bytes(int64_t m, int64_t n);
+size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s, int* grid_out);
 
 // block path (block.hip)

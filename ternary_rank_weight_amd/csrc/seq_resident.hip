@@ -27,7 +27,16 @@
 // every workgroup) and applies T_tau (§2.2) redundantly and identically.
 //
 // Termination.  Every wait is bounded: a workgroup that waits too long sets a
-// device error flag and the whole grid returns; the host reports EHIP.
+// device error flag and the whole grid returns; the energy is then NaN and
+// stats[EXTERND_STAT_TIMEOUTS] is set (the call itself still returns OK).
+//
+// Safeguard check (appendix §7).  Every thread keeps the largest w_j R_ij^2
+// of the column-copy entries it holds (each residual entry is held by exactly
+// one thread of one workgroup), so the single-entry bound max_ij w_j R_ij^2
+// is exceeded by the component's decrease everywhere or not: a thread whose
+// own maximum beats the decrease sets the component's bit in a bitmap (an
+// idempotent atomic OR, so no reduction or barrier is needed), and the bits
+// are counted at the end.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -56,6 +65,7 @@ struct ResArgs {
   unsigned* xslot;             // m words
   unsigned* err;
   double* r2_partial;          // G fp64
+  unsigned* sg_bits;           // ceil(k/32) words, zeroed: components failing the single-entry bound
   int64_t cap_i;
   float* cap_R;
   float* cap_Rcol;
@@ -357,6 +367,10 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
     const int col = t + T * j;
     wv[j] = (a.wt && col < n) ? a.wt[col] : 1.f;
   }
+  // weights of the column copy's columns (the same for every thread)
+  float wcol[LC];
+#pragma unroll
+  for (int l = 0; l < LC; ++l) wcol[l] = (a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f;
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
   long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
@@ -388,6 +402,17 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       }
     }
     if (i == a.k) break;
+    // this thread's share of the single-entry bound max_ij w_j R_ij^2 of the
+    // residual before component i (exact: w (|x|)^2 with x^2 exact in fp64)
+    double rmax2 = 0.0;
+#pragma unroll
+    for (int l = 0; l < LC; ++l) {
+      uint32_t mb = 0u;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) mb = max(mb, __float_as_uint(rc[l][j]) & 0x7fffffffu);
+      const double x = (double)__uint_as_float(mb);
+      rmax2 = fmax(rmax2, x * x * (double)wcol[l]);
+    }
     if (CAP && i == a.cap_i) {
       if (a.cap_R) dump_rows<T, KR, LR>(rrow, a, row0, a.cap_R);
       if (a.cap_Rcol) {
@@ -510,7 +535,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       const double c = sums[0], nu = sums[1], nv = sums[2];
       const double den = nu * sums[3];
       d32 = den > 0.0 ? (float)(c / den) : 0.f;
-      trace_state -= den > 0.0 ? c * c / den : 0.0;
+      const double dec = den > 0.0 ? c * c / den : 0.0;
+      trace_state -= dec;
+      if (__any(dec < rmax2) && (t & (kWave - 1)) == 0) atomicOr(a.sg_bits + (i >> 5), 1u << (i & 31));
       st_b += (long long)nu;
       st_c += (long long)nv;
       if (g == 0 && t == 0) {
@@ -562,7 +589,14 @@ __global__ void k_fill_u64(unsigned long long* p, int64_t count) {
 __global__ void k_resident_finish(const double* __restrict__ r2_partial, int G,
                                   const double* __restrict__ a2, const long long* __restrict__ nonfinite,
                                   const unsigned* __restrict__ err, double* __restrict__ energy,
-                                  long long* __restrict__ stats) {
+                                  long long* __restrict__ stats, const unsigned* __restrict__ sg_bits,
+                                  int64_t sg_words) {
+  if (stats && blockIdx.x == 0) {
+    long long c = 0;
+    for (int64_t q = threadIdx.x; q < sg_words; q += blockDim.x) c += __popc(sg_bits[q]);
+    c = wave_sum(c);
+    if (threadIdx.x == 0) stats[EXTERND_STAT_SAFEGUARD] = c;
+  }
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   double r2 = 0.0;
   for (int g = 0; g < G; ++g) r2 += r2_partial[g];
@@ -615,9 +649,10 @@ bool resident_fits(int64_t m, int64_t n, int num_cus) {
   return pick_tile(m, n, num_cus) >= 0;
 }
 
-size_t resident_workspace_bytes(int64_t m, int64_t n) {
+size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   return sizeof(unsigned long long) * (size_t)(m + n) + sizeof(double) * (256 + 4096 + 8) +
-         sizeof(long long) * 8 + sizeof(unsigned) * 64 + sizeof(float) * (size_t)n + 256 * 9;
+         sizeof(long long) * 8 + sizeof(unsigned) * 64 + sizeof(float) * (size_t)n +
+         sizeof(unsigned) * (size_t)((k + 31) / 32) + 256 * 10;
 }
 
 static inline char* align256(char* p) {
@@ -644,8 +679,12 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   unsigned* err = reinterpret_cast<unsigned*>(p);
   p = align256(p + sizeof(unsigned) * 64);
   float* wt = a.importance ? reinterpret_cast<float*>(p) : nullptr;   // column weights (§2.5)
+  p = align256(p + sizeof(float) * a.n);
+  unsigned* sg_bits = reinterpret_cast<unsigned*>(p);
+  const int64_t sg_words = (a.k + 31) / 32;
 
   hipError_t e;
+  if ((e = launch_fill_u32(sg_bits, sg_words, 0u, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)a.n);
   hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)a.m);
   if ((e = launch_fill_i64(nonfinite, 1, 0, s)) != hipSuccess) return e;
@@ -677,6 +716,7 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   ra.xslot = reinterpret_cast<unsigned*>(xslot);
   ra.err = err;
   ra.r2_partial = r2p;
+  ra.sg_bits = sg_bits;
   ra.cap_i = a.capture_component;
   ra.cap_R = a.capture_R;
   ra.cap_Rcol = a.capture_Rcol;
@@ -695,7 +735,7 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_resident_finish, dim3(1), dim3(64), 0, s, r2p, ra.G, a2, nonfinite, err,
-                     a.energy, a.stats);
+                     a.energy, a.stats, sg_bits, sg_words);
   if (a.norm_a2 && (e = launch_copy_f64(a2, a.norm_a2, 1, s)) != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -250,14 +250,18 @@ __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x,
 constexpr int kGtT = 256;     // columns per workgroup
 constexpr int kGtRows = 128;  // rows per chunk
 
+// maxw2 (optional, with a dense u): raised to max w_c R_rc^2 over the rows
+// read, after the fused deflation (the single-entry bound of appendix §7).
 __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
     float* __restrict__ partial, const float* __restrict__ dprev,
-    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev) {
+    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev,
+    unsigned long long* __restrict__ maxw2, const float* __restrict__ wt) {
   const int64_t c = (int64_t)blockIdx.x * kGtT + threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * kGtRows;
   const int64_t r1 = min(m, r0 + kGtRows);
   float acc = 0.f;
+  uint32_t mb = 0u;   // largest |R_rc| read (bits)
   const bool incol = c < n;
   if (dprev) {
     const float d = *dprev;
@@ -272,17 +276,28 @@ __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
           R[r * n + c] = val;
         }
         acc = fmaf(ur, val, acc);
+        mb = max(mb, __float_as_uint(val) & 0x7fffffffu);
       } else if (ur != 0.f && incol) {
-        acc = fmaf(ur, R[r * n + c], acc);
+        const float val = R[r * n + c];
+        acc = fmaf(ur, val, acc);
+        mb = max(mb, __float_as_uint(val) & 0x7fffffffu);
       }
     }
   } else {
     for (int64_t r = r0; r < r1; ++r) {
       const float ur = code_at(u_codes, r);
-      if (ur != 0.f && incol) acc = fmaf(ur, R[r * n + c], acc);
+      if (ur != 0.f && incol) {
+        const float val = R[r * n + c];
+        acc = fmaf(ur, val, acc);
+        mb = max(mb, __float_as_uint(val) & 0x7fffffffu);
+      }
     }
   }
   if (incol) partial[(int64_t)blockIdx.y * n + c] = acc;
+  if (maxw2) {
+    const double x = (double)__uint_as_float(mb);
+    wave_max_nonneg_to(incol ? x * x * (wt ? (double)wt[c] : 1.0) : 0.0, maxw2);
+  }
 }
 
 // The same partial products for n % 4 == 0, built for bandwidth: a
@@ -297,7 +312,8 @@ constexpr int kGtWave = kGtRows / 4;   // rows per wave
 __global__ __launch_bounds__(256) void k_gemv_t_vec(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
     float* __restrict__ partial, const float* __restrict__ dprev,
-    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev) {
+    const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev,
+    unsigned long long* __restrict__ maxw2, const float* __restrict__ wt) {
   static_assert(kGtRows == 128, "eight code words per chunk");
   __shared__ float4 red[3][kWave];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -342,6 +358,7 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
     v[k] = R4[need ? r * n4 + c4s : c4s];
   }
   float4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint32_t mb[4] = {0u, 0u, 0u, 0u};   // largest |R| per column over the rows read (bits)
 #pragma unroll
   for (int k = 0; k < kGtWave; ++k) {
     float4 val = v[k];
@@ -356,6 +373,23 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
     acc.y = fmaf(ur[k], val.y, acc.y);
     acc.z = fmaf(ur[k], val.z, acc.z);
     acc.w = fmaf(ur[k], val.w, acc.w);
+    if (maxw2 && r0 + w + 4 * k < m) {
+      mb[0] = max(mb[0], __float_as_uint(val.x) & 0x7fffffffu);
+      mb[1] = max(mb[1], __float_as_uint(val.y) & 0x7fffffffu);
+      mb[2] = max(mb[2], __float_as_uint(val.z) & 0x7fffffffu);
+      mb[3] = max(mb[3], __float_as_uint(val.w) & 0x7fffffffu);
+    }
+  }
+  if (maxw2) {
+    double mx = 0.0;
+    if (incol) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double x = (double)__uint_as_float(mb[e]);
+        mx = fmax(mx, x * x * (wt ? (double)wt[4 * c4 + e] : 1.0));
+      }
+    }
+    wave_max_nonneg_to(mx, maxw2);
   }
   if (w > 0) red[w - 1][lane] = acc;
   __syncthreads();
@@ -501,7 +535,9 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
                                                   double* __restrict__ trace_state,
                                                   double* __restrict__ trace,
                                                   long long* __restrict__ stats,
-                                                  const double* __restrict__ sv) {
+                                                  const double* __restrict__ sv,
+                                                  unsigned long long* __restrict__ maxw2,
+                                                  double* __restrict__ sg_state) {
   __shared__ double scratch[kTernT / kWave];
   double acc = 0.0;
   for (int64_t r = threadIdx.x; r < m; r += kTernT) acc += (double)code_at(u_codes, r) * (double)x[r];
@@ -510,13 +546,86 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
     const double den = (double)(*nnz_u) * (sv ? *sv : (double)(*nnz_v));
     const double d = den > 0.0 ? c / den : 0.0;
     D[i] = (float)d;
-    const double t = trace_state[0] - (den > 0.0 ? c * c / den : 0.0);
+    const double dec = den > 0.0 ? c * c / den : 0.0;
+    const double t = trace_state[0] - dec;
     trace_state[0] = t;
     if (trace) trace[i] = t;
     if (stats) {
       stats[EXTERND_STAT_NNZ_B] += *nnz_u;
       stats[EXTERND_STAT_NNZ_C] += *nnz_v;
     }
+    // Single-entry safeguard check (appendix §7) against the bound the
+    // component's first pass measured.  With sg_state (the safeguard
+    // applied), the decision and the fit's decrease are left for
+    // k_safeguard_argmax / k_safeguard_apply, which reset the bound;
+    // otherwise it is reset here.
+    const double bound = __longlong_as_double((long long)*maxw2);
+    const bool would = dec < bound;
+    if (would && stats) stats[EXTERND_STAT_SAFEGUARD] += 1;
+    if (sg_state) {
+      sg_state[0] = would ? 1.0 : 0.0;
+      sg_state[1] = dec;
+      reinterpret_cast<unsigned long long*>(sg_state)[2] = ~0ull;   // argmin index
+    } else {
+      *maxw2 = 0ull;
+    }
+  }
+}
+
+// The safeguard's replacement (appendix §7), when k_scale flagged it: the
+// position of the single-entry bound, the smallest row-major index r n + c
+// whose w_c R_rc^2 equals it (the same fp64 expression the bound was taken
+// over), found over R before component i's deflation.
+__global__ void k_safeguard_argmax(const float* __restrict__ R, int64_t m, int64_t n, const float* __restrict__ wt,
+                                   const unsigned long long* __restrict__ maxw2, double* __restrict__ sg_state) {
+  if (sg_state[0] == 0.0) return;
+  const double bound = __longlong_as_double((long long)*maxw2);
+  const int64_t total = m * n;
+  unsigned long long best = ~0ull;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const double x = (double)R[e];
+    const double v = x * x * (wt ? (double)wt[e % n] : 1.0);
+    if (v == bound && (unsigned long long)e < best) best = (unsigned long long)e;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(best, off, kWave);
+    best = o < best ? o : best;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0 && best != ~0ull)
+    atomicMin(reinterpret_cast<unsigned long long*>(sg_state) + 2, best);
+}
+
+// Replace component i by the single entry e_r e_c^T with d = R_rc: codes,
+// scale, predicted trace and nonzero counts; then reset the bound.
+__global__ void k_safeguard_apply(const float* __restrict__ R, int64_t m, int64_t n, const float* __restrict__ wt,
+                                  uint32_t* __restrict__ ub, int64_t wm, uint32_t* __restrict__ vc, int64_t wn,
+                                  float* __restrict__ D, int64_t i, double* __restrict__ trace_state,
+                                  double* __restrict__ trace, long long* __restrict__ stats,
+                                  const int32_t* __restrict__ nnz_u, const int32_t* __restrict__ nnz_v,
+                                  unsigned long long* __restrict__ maxw2, double* __restrict__ sg_state) {
+  const bool take = sg_state[0] != 0.0;
+  const unsigned long long idx = reinterpret_cast<const unsigned long long*>(sg_state)[2];
+  const bool ok = take && idx < (unsigned long long)(m * n);
+  if (ok) {
+    const int64_t r = (int64_t)(idx / (unsigned long long)n), c = (int64_t)(idx % (unsigned long long)n);
+    for (int64_t q = threadIdx.x; q < wm; q += blockDim.x) ub[q] = (q == r / 16) ? (1u << (2 * (r % 16))) : 0u;
+    for (int64_t q = threadIdx.x; q < wn; q += blockDim.x) vc[q] = (q == c / 16) ? (1u << (2 * (c % 16))) : 0u;
+    if (threadIdx.x == 0) {
+      const float rv = R[idx];
+      D[i] = rv;
+      const double x = (double)rv;
+      const double t = trace_state[0] + sg_state[1] - x * x * (wt ? (double)wt[c] : 1.0);
+      trace_state[0] = t;
+      if (trace) trace[i] = t;
+      stats[EXTERND_STAT_NNZ_B] += 1 - *nnz_u;
+      stats[EXTERND_STAT_NNZ_C] += 1 - *nnz_v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *maxw2 = 0ull;
+    sg_state[0] = 0.0;
   }
 }
 
@@ -531,26 +640,33 @@ __global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restric
                                                           int64_t per_block,
                                                           double* __restrict__ partial,
                                                           long long* __restrict__ nonfinite,
-                                                          const float* __restrict__ wt, int64_t ncols) {
-  // with column weights wt (ncols columns): sum_j wt_j A_ij^2 (§2.5)
+                                                          const float* __restrict__ wt, int64_t ncols,
+                                                          unsigned long long* __restrict__ maxw2) {
+  // with column weights wt (ncols columns): sum_j wt_j A_ij^2 (§2.5); maxw2
+  // (optional) is raised to the largest wt_j A_ij^2 (the single-entry bound)
   __shared__ double scratch[kNormT / kWave];
   const int64_t b0 = (int64_t)blockIdx.x * per_block;
   const int64_t b1 = min(total, b0 + per_block);
-  double acc = 0.0;
+  double acc = 0.0, mx = 0.0;
   long long bad = 0;
   if (wt) {
     for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
       const float v = A[j];
       if (!isfinite(v)) ++bad;
-      acc += (double)v * (double)v * (double)wt[j % ncols];
+      const double e = (double)v * (double)v * (double)wt[j % ncols];
+      acc += e;
+      mx = fmax(mx, e);
     }
   } else {
     for (int64_t j = b0 + threadIdx.x; j < b1; j += kNormT) {
       const float v = A[j];
       if (!isfinite(v)) ++bad;
-      acc += (double)v * (double)v;
+      const double e = (double)v * (double)v;
+      acc += e;
+      mx = fmax(mx, e);
     }
   }
+  if (maxw2) wave_max_nonneg_to(mx, maxw2);
   const double s = block_sum<kNormT>(acc, scratch);
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
   if (nonfinite) {
@@ -689,15 +805,16 @@ int64_t gemv_t_chunks(int64_t m) { return (m + kGtRows - 1) / kGtRows; }
 
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
-                         const uint32_t* vprev, hipStream_t s) {
+                         const uint32_t* vprev, hipStream_t s, unsigned long long* maxw2, const float* wt) {
   const int64_t chunks = gemv_t_chunks(m);
   if ((n & 3) == 0) {
     dim3 grid((unsigned)((n / 4 + kWave - 1) / kWave), (unsigned)chunks);
-    hipLaunchKernelGGL(k_gemv_t_vec, grid, dim3(256), 0, s, R, m, n, u_codes, partial, dprev, uprev, vprev);
+    hipLaunchKernelGGL(k_gemv_t_vec, grid, dim3(256), 0, s, R, m, n, u_codes, partial, dprev, uprev, vprev,
+                       maxw2, wt);
   } else {
     dim3 grid((unsigned)((n + kGtT - 1) / kGtT), (unsigned)chunks);
     hipLaunchKernelGGL(k_gemv_t_partial, grid, dim3(kGtT), 0, s, R, m, n, u_codes, partial, dprev,
-                       uprev, vprev);
+                       uprev, vprev, maxw2, wt);
   }
   hipLaunchKernelGGL(k_sum_chunks, dim3(grid1(n, 256, 1 << 30)), dim3(256), 0, s, partial, chunks,
                      n, y);
@@ -727,13 +844,13 @@ hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_code
 
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
                         double* out, long long* nonfinite, hipStream_t s, const float* wt,
-                        int64_t ncols) {
+                        int64_t ncols, unsigned long long* maxw2) {
   int64_t blocks = std::min<int64_t>(partial_cap, std::max<int64_t>(1, (total + 65535) / 65536));
   const int64_t per_block = (total + blocks - 1) / blocks;
   if (total == 0) blocks = 1;
   if (wt && ncols < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_norm2_partial, dim3((unsigned)blocks), dim3(kNormT), 0, s, A, total,
-                     std::max<int64_t>(per_block, 1), partial, nonfinite, wt, ncols);
+                     std::max<int64_t>(per_block, 1), partial, nonfinite, wt, ncols, maxw2);
   hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(64), 0, s, partial, blocks, out);
   return hipGetLastError();
 }
@@ -772,7 +889,8 @@ size_t stream_workspace_bytes(int64_t m, int64_t n) {
   b += sizeof(int32_t) * 8;                      // nnz counters
   b += sizeof(long long) * EXTERND_STATS_LEN;    // local stats
   b += sizeof(float) * (size_t)n + sizeof(double) * 8;   // column weights, v^T diag(wt) v
-  b += 64 * 10;                                  // alignment slack
+  b += sizeof(double) * 8;                       // single-entry bound and safeguard state
+  b += 256 * 12;                                 // alignment slack
   return b;
 }
 
@@ -802,8 +920,14 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   float* wt = a.importance ? reinterpret_cast<float*>(p) : nullptr;   // column weights (§2.5)
   p = align_up(p + sizeof(float) * n, 256);
   double* sv = a.importance ? reinterpret_cast<double*>(p) : nullptr;  // v^T diag(wt) v
+  p = align_up(p + sizeof(double) * 8, 256);
+  // bits of the single-entry bound of the current residual (appendix §7);
+  // the safeguard's state: flag, the fit's decrease, the argmax index
+  unsigned long long* maxw2 = reinterpret_cast<unsigned long long*>(p);
+  double* sg_state = reinterpret_cast<double*>(p) + 1;
 
   hipError_t e;
+  if ((e = launch_fill_i64(reinterpret_cast<long long*>(p), 4, 0, s)) != hipSuccess) return e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if (wt && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
     return e;
@@ -831,8 +955,9 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
     }
     for (int t = 0; t < a.iters; ++t) {
       const bool fuse = (t == 0 && pending);
+      // the first pass (dense u0, every row read) also measures the bound
       e = launch_gemv_t(R, m, n, ub, partial, y, fuse ? a.D + i - 1 : nullptr,
-                        fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s);
+                        fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s, t == 0 ? maxw2 : nullptr, wt);
       if (e != hipSuccess) return e;
       pending = false;
       e = a.projection ? launch_project(y, n, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv,
@@ -854,7 +979,13 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
       }
     }
     hipLaunchKernelGGL(k_scale, dim3(1), dim3(kTernT), 0, s, x, m, ub, nnz_u, nnz_v, a.D, i, tstate,
-                       a.trace, st, (const double*)sv);
+                       a.trace, st, (const double*)sv, maxw2, a.safeguard ? sg_state : (double*)nullptr);
+    if (a.safeguard) {
+      hipLaunchKernelGGL(k_safeguard_argmax, dim3(grid1(m * n, 256, 1024)), dim3(256), 0, s, R, m, n,
+                         (const float*)wt, (const unsigned long long*)maxw2, sg_state);
+      hipLaunchKernelGGL(k_safeguard_apply, dim3(1), dim3(256), 0, s, R, m, n, (const float*)wt, ub, wm, vc, wn,
+                         a.D, i, tstate, a.trace, st, nnz_u, nnz_v, maxw2, sg_state);
+    }
     pending = true;
     if (cap && a.capture_d && (e = launch_copy_f32(a.D + i, a.capture_d, 1, s)) != hipSuccess) return e;
     if (cap && a.capture_R_next) {

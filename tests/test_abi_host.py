@@ -155,6 +155,15 @@ def test_rank_for_energy_matches_oracle(clib):
             want = oracle.rank_for_energy(tr, 10.0, target, step=step, total=total)
             assert trw.rank_for_energy(tr, total, step, 10.0, target) == want
     assert trw.rank_for_energy([], 0, 1, 0.0, 0.5) == 0
+    # the prefix energy comes back from the C side with the rank
+    tr = np.array([8.0, 5.0, 2.0, 1.0])
+    c, e = trw.rank_for_energy(tr, 40, 10, 10.0, 0.75, with_energy=True)
+    assert c == 30 and e == 1.0 - 2.0 / 10.0
+    c, e = trw.rank_for_energy(tr, 35, 10, 10.0, 0.85, with_energy=True)
+    assert c == 35 and e == 0.9
+    c, e = trw.rank_for_energy(tr, 40, 10, 10.0, 0.95, with_energy=True)
+    assert c == -1 and np.isnan(e)
+    assert trw.rank_for_energy([], 0, 1, 0.0, 0.5, with_energy=True) == (0, 1.0)
     with pytest.raises(trw.ExterndError):
         trw.rank_for_energy([1.0], 1, 0, 1.0, 0.5)
     with pytest.raises(trw.ExterndError):
@@ -195,3 +204,49 @@ def test_projection_option_limits(clib):
                                      ctypes.c_void_p]
     assert clib.externd_project(fake, 0, None, fake, None) == 1
     assert clib.externd_project(fake, 16385, None, fake, None) == 4
+
+
+def _opts(trw, **kw):
+    o = trw._Opts()
+    o.struct_size = ctypes.sizeof(trw._Opts)
+    o.mode = -1
+    o.capture_component = -1
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def test_block_wider_than_the_kernels_is_refused(clib):
+    # the pages' default b = 256 on a 4096 x 4096 matrix: the width rule gives
+    # 256, above the widest block the kernels take, so the call is refused
+    # (EXTERND_EUNSUPPORTED) before any device work instead of narrowing b
+    import ternary_rank_weight_amd as trw
+    assert trw.block_width(4096, 4096, 256) == 256
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    st = trw._decompose(fake, 4096, 4096, 1.0, 0.7, 15, 256, None, fake, fake, fake, fake,
+                        ctypes.byref(_opts(trw)))
+    assert st == 4
+    clib.externd_last_error.restype = ctypes.c_char_p
+    assert b"128" in clib.externd_last_error()
+
+
+def test_safeguard_option_limits(clib):
+    import ternary_rank_weight_amd as trw
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    for kw, block, want in ((dict(safeguard=2), 0, 1), (dict(safeguard=-1), 0, 1),
+                            (dict(safeguard=1), 8, 4), (dict(safeguard=1, mode=1), 0, 4),
+                            (dict(safeguard=1, ternarizer=1), 0, 4)):
+        st = trw._decompose(fake, 64, 64, 1.0, 0.7, 15, block, None, fake, fake, fake, fake,
+                            ctypes.byref(_opts(trw, **kw)))
+        assert st == want, (kw, block)
+
+
+def test_block_capture_range_is_checked(clib):
+    import ternary_rank_weight_amd as trw
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    for blk, it in ((-1, 0), (8, 0), (0, -1), (0, 15)):   # 64 x 64, mu 1, b 8: 8 blocks, 15 iterations
+        bc = trw._BlockCapture()
+        bc.block, bc.iteration = blk, it
+        o = _opts(trw, block_capture=ctypes.pointer(bc))
+        st = trw._decompose(fake, 64, 64, 1.0, 0.7, 15, 8, None, fake, fake, fake, fake, ctypes.byref(o))
+        assert st == 1, (blk, it)

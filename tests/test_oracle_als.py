@@ -384,3 +384,64 @@ def test_weighting_raises_the_weighted_energy(block):
         r1 = oracle.decompose_seq(A, 1.0, 0.7, seed=2, weights=w)
     e0 = oracle.energy_from_factors(A, r0.B, r0.C, r0.D, weights=w)
     assert r1.E > e0 + 0.01, (r1.E, e0)
+
+
+# ---- the single-entry safeguard (appendix §7) ----
+
+def test_single_entry_bound_is_the_best_single_entry_fit():
+    # brute force over every one-entry ternary component +-e_r e_c^T with its
+    # least-squares scale: the decrease is w_c R_rc^2, the best one the bound
+    rng = np.random.default_rng(5)
+    R = rng.normal(size=(5, 4))
+    R[2, 1] = R[0, 3] = 3.0   # a tie: the first in row-major order wins
+    w = rng.uniform(0.5, 2.0, 4)
+    for weights in (None, w):
+        best, pos = -1.0, None
+        for r in range(5):
+            for c in range(4):
+                u = np.zeros(5); u[r] = 1.0
+                v = np.zeros(4); v[c] = 1.0
+                wc = 1.0 if weights is None else weights[c]
+                d = R[r, c]
+                after = R - d * np.outer(u, v)
+                dec = oracle.weighted_norm2(R, weights) - oracle.weighted_norm2(after, weights)
+                if dec > best + 1e-12:
+                    best, pos = dec, (r, c)
+        bound, r, c = oracle.single_entry_bound(R, weights)
+        assert abs(bound - best) <= 1e-12 * best and (r, c) == pos
+    assert oracle.single_entry_bound(R)[1:] == (0, 3)
+
+
+def test_safeguard_never_activates_on_gaussian_matrices():
+    # the pages: the ALS decrease is far larger than the single-entry bound
+    A = _small(64, 48, 3)
+    assert oracle.decompose_seq(A, 1.0, 0.7, 15, 0).extra["safeguard_would"] == 0
+    assert oracle.decompose_block(A, 1.0, 0.7, 15, 8, 0).extra["safeguard_would"] == 0
+
+
+def test_safeguard_replaces_a_dense_fit_by_the_dominant_entry():
+    # tau = 0 keeps every nonzero entry, so one iteration gives dense +-1
+    # vectors whose decrease c^2 / (m n) falls far below a dominant entry's
+    A = _small(12, 10, 1, 0.01)
+    A[3, 7] = 5.0
+    plain = oracle.decompose_seq(A, 0.2, 0.0, 1, 0)
+    assert plain.extra["safeguard_would"] >= 1
+    assert np.count_nonzero(plain.B[:, 0]) == 12 and np.count_nonzero(plain.C[0]) == 10
+    safe = oracle.decompose_seq(A, 0.2, 0.0, 1, 0, safeguard=True)
+    assert safe.extra["safeguard_would"] >= 1
+    assert np.array_equal(np.nonzero(safe.B[:, 0])[0], [3]) and np.array_equal(np.nonzero(safe.C[0])[0], [7])
+    assert safe.B[3, 0] == 1 and safe.C[0, 7] == 1 and safe.D[0] == float(A[3, 7])
+    assert safe.trace[0] < plain.trace[0]
+
+
+@pytest.mark.parametrize("tau,iters", [(0.0, 1), (0.7, 2), (2.0, 1)])
+def test_safeguard_gives_the_geometric_rate(tau, iters):
+    # with the safeguard every component lowers ||R||^2 by at least
+    # max R_ij^2 >= ||R||^2 / (m n), the geometric rate in m n of §7
+    m, n = 8, 6
+    A = _small(m, n, 9)
+    res = oracle.decompose_seq(A, 3.0, tau, iters, 0, safeguard=True)
+    prev = res.norm_a2
+    for t in res.trace:
+        assert t <= (1.0 - 1.0 / (m * n)) * prev * (1 + 1e-12) + 1e-300
+        prev = t
