@@ -208,6 +208,24 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
                       uint32_t* B2, uint32_t* C2, float* D, double* energy,
                       const externd_opts* opts);
 
+/*
+ * externd_decompose for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results, on the resident sequential
+ * path only (block widths above 1, EXTERND_MODE_STREAMING and shapes that do
+ * not fit on chip give EXTERND_EUNSUPPORTED; opts->workspace must be NULL).
+ * Its scratch memory is a static 256 KiB device array per GPU, held until
+ * the process ends, so it calls no allocator; a shape needing more scratch
+ * (8 (m + n) + 4 n + k / 8 bytes plus about 38 KB: 88 KB at 2560 x 2560 with
+ * k = 5120) gives EXTERND_ENOMEM.  All calls on
+ * one GPU share that array (each call clears what it needs first): calls
+ * that overlap on one GPU, on any streams, race and must not be issued.
+ */
+int externd_decompose_noalloc(const float* A, int64_t m, int64_t n, float mu, float tau,
+                              int32_t iters, int32_t block, void* stream,
+                              uint32_t* B2, uint32_t* C2, float* D, double* energy,
+                              const externd_opts* opts);
+
 /* energy = 1 - ||A - B diag(D) C||^2 / ||A||^2 accumulated in fp64 from the
  * 2-bit factors (§2.1).  k may be 0 (energy 0, or 1 for A = 0). */
 int externd_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2,

@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = [
-    "decompose", "energy", "reconstruct", "apply", "rank", "block_width", "resident_fits", "workspace_bytes",
+    "decompose", "decompose_noalloc", "energy", "reconstruct", "apply", "rank", "block_width", "resident_fits",
+    "workspace_bytes",
     "rank_for_energy", "mu_for_energy", "project",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
     "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
@@ -75,6 +76,8 @@ def _sig(name, res, args):
 
 _decompose = _sig("externd_decompose", ctypes.c_int,
                   [_p, _i64, _i64, _f32, _f32, _i32, _i32, _p, _p, _p, _p, _p, ctypes.POINTER(_Opts)])
+_decompose_noalloc = _sig("externd_decompose_noalloc", ctypes.c_int,
+                          [_p, _i64, _i64, _f32, _f32, _i32, _i32, _p, _p, _p, _p, _p, ctypes.POINTER(_Opts)])
 _energy = _sig("externd_energy", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _p, _p])
 _reconstruct = _sig("externd_reconstruct", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p])
 _apply = _sig("externd_apply", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p])
@@ -94,7 +97,7 @@ _status_string = _sig("externd_status_string", ctypes.c_char_p, [ctypes.c_int])
 _last_error = _sig("externd_last_error", ctypes.c_char_p, [])
 
 # Every exported symbol of the C ABI, for load checks.
-ABI_SYMBOLS = ("externd_decompose", "externd_energy", "externd_reconstruct", "externd_apply",
+ABI_SYMBOLS = ("externd_decompose", "externd_decompose_noalloc", "externd_energy", "externd_reconstruct", "externd_apply",
                "externd_rank",
                "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
                "externd_rank_for_energy",
@@ -171,7 +174,7 @@ class Decomposition:
 
 def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False, stats=False,
               capture=None, out=None, workspace=None, sweeps=0, importance=None, lam=0.0,
-              projection=False, safeguard=False, block_capture=None):
+              projection=False, safeguard=False, block_capture=None, _entry=None):
     """Run externd_decompose on the current stream.
 
     A: (m, n) float32 CUDA tensor.  capture: component index whose
@@ -279,12 +282,22 @@ def decompose(A, mu, tau, iters=15, block=0, seed=0, mode=MODE_AUTO, trace=False
         for name, tensor in bcap.items():
             setattr(bc, name, _ptr(tensor))
         opts.block_capture = ctypes.pointer(bc)
-    _check(_decompose(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
-                      _ptr(D), _ptr(E), ctypes.byref(opts)))
+    _check((_entry or _decompose)(_ptr(A), m, n, mu, tau, iters, block, _stream(), _ptr(B2), _ptr(C2),
+                                  _ptr(D), _ptr(E), ctypes.byref(opts)))
     res = Decomposition(m, n, k, B2, C2, D, E, tr, st, cap, na2, b)
     res.sweep_trace = swt
     res.block_capture = bcap
     return res
+
+
+def decompose_noalloc(A, mu, tau, iters=15, block=0, seed=0, **kw):
+    """Run externd_decompose_noalloc: decompose() on the resident sequential
+    path with the library's static scratch, for callers that cannot
+    allocate (the outputs here are still allocated by torch).  Takes the
+    keyword arguments of decompose() except workspace."""
+    if kw.get("workspace") is not None:
+        raise ValueError("decompose_noalloc brings its own scratch")
+    return decompose(A, mu, tau, iters, block, seed, _entry=_decompose_noalloc, **kw)
 
 
 def rank_for_energy(trace, total, step, norm_a2, target, with_energy=False):

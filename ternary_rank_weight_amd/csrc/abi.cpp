@@ -102,6 +102,10 @@ int get_ws(Workspace& w, const externd_opts& o, size_t bytes, hipStream_t s) {
 
 }  // namespace
 
+namespace externd {
+int report(int status, const char* msg) { return fail(status, "%s", msg); }
+}  // namespace externd
+
 extern "C" {
 
 const char* externd_status_string(int status) {

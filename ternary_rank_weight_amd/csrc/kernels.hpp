@@ -9,6 +9,9 @@
 
 namespace externd {
 
+// Sets the calling thread's externd_last_error() message; returns status.
+int report(int status, const char* msg);
+
 // Arguments of one sequential decomposition (device pointers).
 struct SeqArgs {
   const float* A;
