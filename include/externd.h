@@ -216,8 +216,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
  * not fit on chip give EXTERND_EUNSUPPORTED; opts->workspace must be NULL).
  * Its scratch memory is a static 256 KiB device array per GPU, held until
  * the process ends, so it calls no allocator; a shape needing more scratch
- * (8 (m + n) + 4 n + k / 8 bytes plus about 38 KB: 88 KB at 2560 x 2560 with
- * k = 5120) gives EXTERND_ENOMEM.  All calls on
+ * (16 KB (ceil(m/1024) + ceil(n/1024)) + 4 n + k / 8 bytes plus about 37 KB:
+ * 144 KB at 2560 x 2560 with k = 5120) gives EXTERND_ENOMEM.  All calls on
  * one GPU share that array (each call clears what it needs first): calls
  * that overlap on one GPU, on any streams, race and must not be issued.
  */

@@ -648,6 +648,9 @@ struct NsShared {
 };
 // Index of element (row, k) of a stored part.
 __device__ inline int ns_at(int row, int k) { return row * kNsB + ((((k >> 3) ^ (row & 7))) << 3) + (k & 7); }
+// Row stride (fp32 words) of the refinement's fp32 copies of G' and X.
+constexpr int kNsPad = 68;
+static_assert(kNsB * kNsPad * 4 <= 3 * kNsB * kNsB * 2, "an fp32 copy fits in the space of three bf16 parts");
 
 __device__ inline double ns_block_max(double v, double* red) {
 #pragma unroll
@@ -700,14 +703,6 @@ __device__ inline bf16x8 ns_ld_col(const unsigned short* buf, int k0, int col) {
     q[e] = (uint32_t)buf[ns_at(k0 + 2 * e, col)] | ((uint32_t)buf[ns_at(k0 + 2 * e + 1, col)] << 16);
   return __builtin_bit_cast(bf16x8, u32x4{q[0], q[1], q[2], q[3]});
 }
-// Element (row, k) of a stored three-part value, in fp64: h + m + l is the
-// fp32 value exactly.
-__device__ inline double ns_value(const unsigned short (*buf)[kNsB * kNsB], int row, int k) {
-  const int at = ns_at(row, k);
-  return (double)__uint_as_float((uint32_t)buf[0][at] << 16) + (double)__uint_as_float((uint32_t)buf[1][at] << 16) +
-         (double)__uint_as_float((uint32_t)buf[2][at] << 16);
-}
-
 __device__ inline f4 ns_mfma6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f4 acc) {
   acc = mfma16x16x32bf16(a[0], b[0], acc);
   acc = mfma16x16x32bf16(a[0], b[1], acc);
@@ -937,8 +932,8 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   // fp64 refinement.  The fp32 iteration above cannot certify better than
   // about 1e-4 (its residual is itself computed in fp32), so the residual
   // R = I - G'X of the fp32 X is formed exactly enough in fp64 (fp64 MFMA
-  // 16x16x4; G' from its stored parts with the exact fp64 diagonal, X from
-  // its parts: every product is exact) and one more step X <- X + X R is
+  // 16x16x4 on fp32 copies of G' and X, with the exact fp64 diagonal of G':
+  // every product is exact) and one more step X <- X + X R is
   // taken, which leaves a residual of ||R||_F^2 (the update itself is the
   // six-product bf16 form: it only needs the small correction X R to a few
   // digits).  A step is accepted once the fp64 residual is below 1e-3, so
@@ -948,17 +943,41 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   // output register v of lane (j + 16 g) is entry (g + 4 v, j).
   bool conv64 = false;
   if (conv) {
-    __syncthreads();   // every read of Xt, Rt and red by the loop done
+    __syncthreads();   // every read of Gp, Xt, Rt and red by the loop done
+    // fp32 copies for the fp64 products: G' row-major over the parts of G'
+    // (no longer needed), X transposed over the parts of R (rewritten
+    // below); rows padded to 68 words, so the 16 x 4 lanes of an operand
+    // load (row 16 w + i or 16 J + j, word 4 q + kk) hit 64 different banks
+    float* g32 = reinterpret_cast<float*>(&sh.Gp[0][0]);
+    float* xt32 = reinterpret_cast<float*>(&sh.Rt[0][0]);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) g32[(16 * w + 4 * g + v) * kNsPad + 16 * J + i16] = gp[J][v];
     for (int round = 0; round < 3 && !conv64; ++round) {
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xt32[(16 * J + i16) * kNsPad + 16 * w + 4 * g + v] = xv[J][v];
+      __syncthreads();
       d4 racc[4];
 #pragma unroll
       for (int J = 0; J < 4; ++J) racc[J] = d4{0.0, 0.0, 0.0, 0.0};
       const int kk = g;   // this lane's k within a slice
-      for (int q = 0; q < kNsB / 4; ++q) {
-        const int kcol = 4 * q + kk, arow = 16 * w + i16;
-        const double a = arow == kcol ? sh.diag64[arow] : ns_value(sh.Gp, arow, kcol);
+      const int arow = 16 * w + i16;
+      float av[kNsB / 4], bv[kNsB / 4][4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) racc[J] = mfma16x16x4f64(a, ns_value(sh.Xt, 16 * J + i16, kcol), racc[J]);
+      for (int q = 0; q < kNsB / 4; ++q) {
+        av[q] = g32[arow * kNsPad + 4 * q + kk];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) bv[q][J] = xt32[(16 * J + i16) * kNsPad + 4 * q + kk];
+      }
+#pragma unroll
+      for (int q = 0; q < kNsB / 4; ++q) {
+        const int kcol = 4 * q + kk;
+        const double a = arow == kcol ? sh.diag64[arow] : (double)av[q];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) racc[J] = mfma16x16x4f64(a, (double)bv[q][J], racc[J]);
       }
       double rp = 0.0;
 #pragma unroll
@@ -972,6 +991,7 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
         }
       rp = wave_sum_to63(rp);
       if (lane == kWave - 1) sh.dred[w] = rp;
+      __syncthreads();   // every read of xt32 done before Rt is rewritten
       // R (rounded to fp32: it only enters the small correction) as
       // transposed parts: element (c, r) of Rt holds R[r][c]
 #pragma unroll
@@ -1000,10 +1020,7 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
 #pragma unroll
         for (int v = 0; v < 4; ++v) xv[J][v] += y[J][v];
       __syncthreads();   // every read of Xt, Rt and dred done
-      if (!conv64) {
-        ns_store_t(sh.Xt, xv, w, i16, g);
-        __syncthreads();
-      }
+      if (!conv64) ns_store_t(sh.Xt, xv, w, i16, g);   // published by the next round's barrier
     }
   }
 #pragma unroll
@@ -1450,7 +1467,7 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
                                                         int bstride, const double* __restrict__ dpart,
                                                         int64_t ndpart, const double* __restrict__ dold,
                                                         int* __restrict__ accept,
-                                                        unsigned long long* __restrict__ maxw2) {
+                                                        const double* __restrict__ mpart, int64_t nmpart) {
   constexpr int TR = (T + 3) / 4;
   __shared__ SweepShared<T> sh;
   __shared__ double rhs[kMaxB];
@@ -1467,6 +1484,11 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     for (int64_t j = t; j < ndpart; j += kCholT) p += dpart[j];
     added = block_sum<kCholT>(p, red);
   }
+  // the single-entry bound of the residual this block was fitted to, from
+  // the per-wave partials of the launch that last wrote it (appendix §7)
+  double bmx = 0.0;
+  for (int64_t j = t; j < nmpart; j += kCholT) bmx = fmax(bmx, mpart[j]);
+  const double bound = block_max_f64<kCholT>(bmx, red);
   // M = (U^T U) o (V^T V); solve without a ridge, retry once with one
   d4 acc[TR][T];
   bool ok = false;
@@ -1545,11 +1567,9 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     if (accept) *accept = take ? 1 : 0;
     // Single-entry safeguard check (appendix §7): would the best single entry
     // of the residual this block was fitted to, max_ij w_j R_ij^2, have
-    // lowered ||R||^2 more than the block did?  Counted on extraction only;
-    // the bound is then reset for the deflation to raise it again.
-    if (!dpart && dec < __longlong_as_double((long long)*maxw2))
+    // lowered ||R||^2 more than the block did?  Counted on extraction only.
+    if (!dpart && dec < bound)
       atomicAdd(reinterpret_cast<unsigned long long*>(st + EXTERND_STAT_SAFEGUARD), 1ull);
-    *maxw2 = 0ull;
     const double tnew = take ? trace_state[0] + added - dec : trace_state[0];
     trace_state[0] = tnew;
     if (trace) trace[blk] = tnew;
@@ -1595,7 +1615,7 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
                                                        const uint32_t* __restrict__ Vcodes, int64_t wn,
                                                        const double* __restrict__ d, int bb,
                                                        double* __restrict__ dpart, const float* __restrict__ wt,
-                                                       unsigned long long* __restrict__ maxw2) {
+                                                       double* __restrict__ mpart) {
   __shared__ DeflateLds st;
   __shared__ double red[256 / kWave];
   const int t = threadIdx.x;
@@ -1687,7 +1707,7 @@ __global__ __launch_bounds__(256) void k_block_deflate(float* __restrict__ R, in
     }
   }
   // the single-entry bound of the new residual (appendix §7), for the next block's check
-  if (maxw2) wave_max_nonneg_to(mx, maxw2);
+  if (mpart) wave_max_nonneg_part(mx, mpart);
   if (dpart) {
     const double tot = block_sum<256>(change, red);
     if (threadIdx.x == 0) dpart[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = tot;
@@ -1766,6 +1786,13 @@ inline unsigned grid1d(int64_t count, int threads, int64_t cap = 8192) {
   return (unsigned)std::max<int64_t>(1, std::min(g, cap));
 }
 
+// Per-wave partial maxima of the single-entry bound a block decomposition
+// keeps: enough for the norm pass over A (at most 4096 workgroups) and for
+// a deflation (one 64 x 64 tile per workgroup), 4 waves each.
+inline int64_t sg_partials(int64_t m, int64_t n) {
+  return wave_partials(std::max<int64_t>(4096, ((n + 63) / 64) * ((m + 63) / 64)), 256);
+}
+
 struct BlockLayout {
   int S1, S2;            // K splits of the two contractions
   int64_t rows_split, cols_split;
@@ -1806,8 +1833,9 @@ BlockLayout layout_for(int64_t m, int64_t n, int b) {
   // importance weights: column weights, weighted Gram and its split partials
   by += sizeof(float) * (size_t)n;
   by += sizeof(double) * (size_t)b * b * (1 + ((n + 15) / 16 + kGramSplit - 1) / kGramSplit);
-  by += sizeof(unsigned long long) * 3;   // Gram tile counters, single-entry bound
-  by += 29 * 256;   // alignment slack of the bump allocations
+  by += sizeof(unsigned long long) * 2;   // Gram tile counters
+  by += sizeof(double) * (size_t)sg_partials(m, n);   // single-entry bound partials
+  by += 32 * 256;   // alignment slack of the bump allocations
   L.bytes = by;
   return L;
 }
@@ -1892,9 +1920,13 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   int* accept = reinterpret_cast<int*>(bump(p, sizeof(int)));
   // Gram tiles finished inside the combined launches (U side, V side),
   // counting up over the whole decomposition
-  unsigned long long* gram_done = reinterpret_cast<unsigned long long*>(bump(p, sizeof(unsigned long long) * 3));
-  // bits of the single-entry bound max_ij w_j R_ij^2 of the current residual
-  unsigned long long* sg_max = gram_done + 2;
+  unsigned long long* gram_done = reinterpret_cast<unsigned long long*>(bump(p, sizeof(unsigned long long) * 2));
+  // per-wave partial maxima of the single-entry bound max_ij w_j R_ij^2 of
+  // the current residual (appendix §7): left by the norm pass over A, then
+  // by each deflation; sg_n of them are valid
+  const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
+  double* sg_part = reinterpret_cast<double*>(bump(p, sizeof(double) * sg_partials(m, n)));
+  int64_t sg_n = 0;
   unsigned long long gram_issued[2] = {0ull, 0ull};
   // importance weighting (§2.5): column weights wt, the weighted V-side Gram
   // V^T diag(wt) V and its per-split partials
@@ -1912,14 +1944,14 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if (W && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
     return e;
-  if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 3, 0, s)) != hipSuccess) return e;
-  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n, sg_max)) != hipSuccess)
+  if ((e = launch_fill_i64(reinterpret_cast<long long*>(gram_done), 2, 0, s)) != hipSuccess) return e;
+  if ((e = launch_norm2(a.A, m * n, npart, 4096, a2, st + EXTERND_STAT_NONFINITE, s, wt, n, sg_part, &sg_n)) !=
+      hipSuccess)
     return e;
   hipLaunchKernelGGL(k_set_trace, dim3(1), dim3(1), 0, s, tstate, a2);
   if ((e = launch_copy_f32(a.A, R, m * n, s)) != hipSuccess) return e;
 
   hipLaunchKernelGGL(k_zero_i32, dim3(grid1d((int64_t)4 * b * b, 256)), dim3(256), 0, s, GU, (int64_t)4 * b * b);
-  const dim3 defl_grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
   const int64_t ndpart = (int64_t)defl_grid.x * defl_grid.y;
 
   // The block iterations from the U held in Uc, then the joint scale solve
@@ -2005,16 +2037,17 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     int* acc = dpart ? accept : nullptr;
     const double* gvw = W ? GVw : nullptr;
     if (bb <= 16)
-      hipLaunchKernelGGL(k_joint_solve<1>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
+      hipLaunchKernelGGL(k_joint_solve<1>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, (const double*)sg_part, sg_n);
     else if (bb <= 32)
-      hipLaunchKernelGGL(k_joint_solve<2>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
+      hipLaunchKernelGGL(k_joint_solve<2>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, (const double*)sg_part, sg_n);
     else if (bb <= 64)
-      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
+      hipLaunchKernelGGL(k_joint_solve<4>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, (const double*)sg_part, sg_n);
     else
-      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, sg_max);
+      hipLaunchKernelGGL(k_joint_solve<8>, dim3(1), dim3(kCholT), 0, s, GUf, GVf, gvw, bb, rhs, Dout, dvec, tstate, trace, tidx, st, nnz, b, dpart, ndpart, dold, acc, (const double*)sg_part, sg_n);
     if (dpart)
       hipLaunchKernelGGL(k_sweep_restore, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, accept, bb, Uc, wm, Vc, wn, saved);
-    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr, (const float*)wt, sg_max);
+    hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dvec, bb, (double*)nullptr, (const float*)wt, sg_part);
+    sg_n = wave_partials((int64_t)defl_grid.x * defl_grid.y, 256);
     return hipGetLastError();
   };
 
@@ -2037,7 +2070,8 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       uint32_t* Uc = a.B2 + c0 * wm;
       uint32_t* Vc = a.C2 + c0 * wn;
       hipLaunchKernelGGL(k_sweep_prepare, dim3(grid1d((int64_t)bb * (wm + wn), 256)), dim3(256), 0, s, bb, Uc, wm, Vc, wn, a.D + c0, saved, dold, dneg, warm);
-      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart, (const float*)wt, sg_max);
+      hipLaunchKernelGGL(k_block_deflate, defl_grid, dim3(256), 0, s, R, m, n, Uc, wm, Vc, wn, dneg, bb, dpart, (const float*)wt, sg_part);
+      sg_n = wave_partials((int64_t)defl_grid.x * defl_grid.y, 256);
       double* tr = (blk == nblocks - 1) ? a.sweep_trace : nullptr;
       if ((e = fit_block(bb, Uc, Vc, a.D + c0, tr, sw, dpart, dold, saved, nullptr)) != hipSuccess) return e;
     }

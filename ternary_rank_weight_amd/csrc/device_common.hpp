@@ -84,19 +84,21 @@ __device__ inline int wave_min_i(int v) {
   return v;
 }
 
-// Max of a non-negative fp64 value over the wave, raised into *slot with one
-// atomic per wave: the bit patterns of non-negative doubles are ordered like
-// their values, so an unsigned 64-bit max is the fp64 max.  Every lane of
-// the wave must call.
-__device__ inline void wave_max_nonneg_to(double v, unsigned long long* slot) {
-  unsigned long long b = (unsigned long long)__double_as_longlong(v);
+// Max of a non-negative fp64 value over the wave, stored by lane 0 into
+// part[wave index of the whole launch] (blockIdx.y-major, then blockIdx.x,
+// then the wave within the workgroup): one plain store per wave and no
+// atomics, the consumer taking the max of the launch's partials.  Every
+// lane of the wave must call.
+__device__ inline void wave_max_nonneg_part(double v, double* part) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned long long o = __shfl_xor(b, off, kWave);
-    b = o > b ? o : b;
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    part[wg * (blockDim.x / kWave) + threadIdx.x / kWave] = v;
   }
-  if ((threadIdx.x & (kWave - 1)) == 0 && b != 0ull) atomicMax(slot, b);
 }
+// Waves of a launch of grid x workgroups of `threads`: partials it leaves.
+inline int64_t wave_partials(int64_t workgroups, int threads) { return workgroups * (threads / kWave); }
 
 template <int T, typename V>
 __device__ inline V block_sum(V v, V* scratch) {
@@ -120,6 +122,19 @@ __device__ inline float block_max(float v, float* scratch) {
   float r = scratch[0];
 #pragma unroll
   for (int i = 1; i < T / kWave; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+template <int T>
+__device__ inline double block_max_f64(double v, double* scratch) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < T / kWave; ++i) r = fmax(r, scratch[i]);
   return r;
 }
 template <int T>

@@ -76,21 +76,24 @@ constexpr int kProjMaxN = 16384;   // longest vector it takes (128 KB of sort ke
 hipError_t launch_project(const float* x, int64_t N, uint32_t* codes, int32_t* nnz, long long* fallbacks,
                           hipStream_t s, const float* wt = nullptr, double* wsum = nullptr,
                           long long* nnz_sum = nullptr);
-// maxw2 (optional, only with a dense u, so that every row is read): raised
-// to the bits of max w_c R_rc^2 of R after the fused deflation.
+// mpart (optional, only with a dense u, so that every row is read):
+// gemv_t_max_partials(m, n) per-wave maxima of w_c R_rc^2 of R after the
+// fused deflation.
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
-                         const uint32_t* vprev, hipStream_t s, unsigned long long* maxw2 = nullptr,
+                         const uint32_t* vprev, hipStream_t s, double* mpart = nullptr,
                          const float* wt = nullptr);
+int64_t gemv_t_max_partials(int64_t m, int64_t n);
 hipError_t launch_gemv_n(const float* R, int64_t m, int64_t n, const uint32_t* v_codes, float* x,
                          hipStream_t s, const float* wt = nullptr);
 hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_codes,
                           const uint32_t* v_codes, const float* dptr, hipStream_t s);
-// ||A||_F^2 (weighted by wt[column] when given) in a fixed order; maxw2
-// (optional, zeroed by the caller) is raised to the bits of max wt_j A_ij^2.
+// ||A||_F^2 (weighted by wt[column] when given) in a fixed order; mpart
+// (optional, room for 4 partial_cap entries) receives per-wave maxima of
+// wt_j A_ij^2 and *nmpart their count.
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
                         double* out, long long* nonfinite, hipStream_t s, const float* wt = nullptr,
-                        int64_t ncols = 0, unsigned long long* maxw2 = nullptr);
+                        int64_t ncols = 0, double* mpart = nullptr, int64_t* nmpart = nullptr);
 // Column weights wt[j] = h[j] / max(h) + lambda in fp32 (§2.5); negative or
 // non-finite h entries are added to *nonfinite.
 hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, float* wt,

@@ -2,7 +2,7 @@
 // cannot allocate device memory (code under HIP graph capture, tight serving
 // loops, harnesses that forbid allocation).  It runs the resident sequential
 // path, whose scratch memory (exchange slots, partial sums, flags, the
-// safeguard bitmap: about (m + n) 8 bytes + 48 KB) lives in the file-scope
+// safeguard bitmap: 144 KB at 2560 x 2560, k = 5120) lives in the file-scope
 // device array `scratch` below instead of a stream-ordered allocation.
 //
 // `scratch` is a host-side stand-in in host code: its device address on the

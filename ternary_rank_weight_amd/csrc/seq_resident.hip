@@ -23,7 +23,15 @@
 // has gathered all of round r; coherence of the single word then rules out
 // reading a value two rounds old.  Value and tag share one atomic word, so no
 // fence or grid barrier is needed: one exchange per half-step, two per ALS
-// iteration.  Every workgroup then holds the whole vector (the same bits in
+// iteration.  Each word is published in kRep = 4 replicas, 4 KB-aligned
+// apart, and workgroup g gathers replica (g mod 8) / 2: with workgroups
+// dispatched round-robin over the 8 XCDs, each pair of XCDs reads its own
+// copy, so the misses of a replica's 64 readers meet in their XCDs' L2s and
+// no single set of lines serves the whole device (measured: 4 replicas read
+// by XCD pairs 612 ms at 2560 x 2560, k = 5120; one copy 678 ms; 8 copies,
+// one per XCD, 637 ms; copies that mix XCDs, or strides that are not 4 KB
+// multiples, were slower still).  The mapping only places the reads;
+// correctness does not depend on where a workgroup runs.  Every workgroup then holds the whole vector (the same bits in
 // every workgroup) and applies T_tau (§2.2) redundantly and identically.
 //
 // Termination.  Every wait is bounded: a workgroup that waits too long sets a
@@ -45,6 +53,11 @@ namespace externd {
 namespace {
 
 constexpr unsigned kSpinLimit = 1u << 21;
+constexpr int kRep = 4;   // replicas of every exchange word
+// words between replicas of a length-len slot array: a whole number of 4 KB
+__host__ __device__ inline int rep_stride(int len) { return (len + 1023) / 1024 * 1024; }
+// the replica workgroup g reads: one per pair of XCDs (round-robin dispatch)
+__device__ inline int rep_of(int g) { return (g & 7) >> 1; }
 
 struct ResArgs {
   const float* A;
@@ -61,8 +74,8 @@ struct ResArgs {
   const double* a2;            // ||A||^2 (weighted when wt is set)
   const float* wt;             // optional column weights (§2.5), n floats
   const long long* nonfinite;  // count of non-finite entries of A
-  unsigned* yslot;             // n words
-  unsigned* xslot;             // m words
+  unsigned* yslot;             // kRep replicas of n words, rep_stride(n) apart
+  unsigned* xslot;             // kRep replicas of m words, rep_stride(m) apart
   unsigned* err;
   double* r2_partial;          // G fp64
   unsigned* sg_bits;           // ceil(k/32) words, zeroed: components failing the single-entry bound
@@ -84,10 +97,11 @@ __device__ inline unsigned xw_pack(unsigned round, float v) {
 __device__ inline float xw_value(unsigned w) { return __uint_as_float(w & ~1u); }
 
 // Sum acc[l] over the T threads for l < L (DPP inside each wave, then the
-// waves in index order) and publish output l < nvalid as slot[base + l].
+// waves in index order) and publish output l < nvalid as slot[base + l] in
+// each of the kRep replicas, rstride words apart.
 template <int T, int L>
 __device__ inline void reduce_publish(const float (&acc)[L], float* red, int nvalid,
-                                      unsigned* slot, int base, unsigned round) {
+                                      unsigned* slot, int base, unsigned round, int rstride) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
   float sums[L];
@@ -102,7 +116,10 @@ __device__ inline void reduce_publish(const float (&acc)[L], float* red, int nva
     float s = red[t];
 #pragma unroll
     for (int q = 1; q < T / kWave; ++q) s += red[q * L + t];
-    __hip_atomic_store(slot + base + t, xw_pack(round, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned word = xw_pack(round, s);
+#pragma unroll
+    for (int r = 0; r < kRep; ++r)
+      __hip_atomic_store(slot + r * rstride + base + t, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -450,9 +467,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           acc[l] = s;
         }
         ++ry;
-        reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), a.yslot, col0, ry);
+        reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), a.yslot, col0, ry, rep_stride(n));
         float y[KR];
-        const bool bad = !gather<T, KR>(a.yslot, n, ry, y, a.err);
+        const bool bad = !gather<T, KR>(a.yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err);
         if (!ternarize_dist<T, KR>(y, bad, n, a.tau, v, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
@@ -484,9 +501,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           acc[l] = s;
         }
         ++rx;
-        reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), a.xslot, row0, rx);
+        reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), a.xslot, row0, rx, rep_stride(m));
         float x[KC];
-        const bool bad = !gather<T, KC>(a.xslot, m, rx, x, a.err);
+        const bool bad = !gather<T, KC>(a.xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err);
         if (!ternarize_dist<T, KC>(x, bad, m, a.tau, u, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
@@ -650,7 +667,7 @@ bool resident_fits(int64_t m, int64_t n, int num_cus) {
 }
 
 size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  return sizeof(unsigned long long) * (size_t)(m + n) + sizeof(double) * (256 + 4096 + 8) +
+  return sizeof(unsigned) * (size_t)kRep * (rep_stride((int)m) + rep_stride((int)n)) + sizeof(double) * (256 + 4096 + 8) +
          sizeof(long long) * 8 + sizeof(unsigned) * 64 + sizeof(float) * (size_t)n +
          sizeof(unsigned) * (size_t)((k + 31) / 32) + 256 * 10;
 }
@@ -665,9 +682,9 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   const Tile tl = kTiles[ti];
   char* p = align256(static_cast<char*>(ws));
   unsigned long long* yslot = reinterpret_cast<unsigned long long*>(p);
-  p = align256(p + sizeof(unsigned long long) * a.n);
+  p = align256(p + sizeof(unsigned) * kRep * rep_stride((int)a.n));
   unsigned long long* xslot = reinterpret_cast<unsigned long long*>(p);
-  p = align256(p + sizeof(unsigned long long) * a.m);
+  p = align256(p + sizeof(unsigned) * kRep * rep_stride((int)a.m));
   double* r2p = reinterpret_cast<double*>(p);
   p = align256(p + sizeof(double) * 256);
   double* npart = reinterpret_cast<double*>(p);
@@ -685,8 +702,9 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
 
   hipError_t e;
   if ((e = launch_fill_u32(sg_bits, sg_words, 0u, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)a.n);
-  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)a.m);
+  // every replica word starts at parity 0 (rep_stride is even: whole 8-byte fills)
+  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)kRep * rep_stride((int)a.n) / 2);
+  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)kRep * rep_stride((int)a.m) / 2);
   if ((e = launch_fill_i64(nonfinite, 1, 0, s)) != hipSuccess) return e;
   if ((e = launch_fill_u32(err, 1, 0u, s)) != hipSuccess) return e;
   if (wt && (e = launch_importance_weights(a.importance, a.n, a.lambda, wt, nonfinite, s)) != hipSuccess) return e;

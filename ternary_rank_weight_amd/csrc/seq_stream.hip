@@ -250,13 +250,14 @@ __global__ __launch_bounds__(kTernT) void k_project(const float* __restrict__ x,
 constexpr int kGtT = 256;     // columns per workgroup
 constexpr int kGtRows = 128;  // rows per chunk
 
-// maxw2 (optional, with a dense u): raised to max w_c R_rc^2 over the rows
-// read, after the fused deflation (the single-entry bound of appendix §7).
+// mpart (optional, with a dense u): per-wave partial maxima of w_c R_rc^2
+// over the rows read, after the fused deflation (the single-entry bound of
+// appendix §7), one per wave of the launch.
 __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
     float* __restrict__ partial, const float* __restrict__ dprev,
     const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev,
-    unsigned long long* __restrict__ maxw2, const float* __restrict__ wt) {
+    double* __restrict__ mpart, const float* __restrict__ wt) {
   const int64_t c = (int64_t)blockIdx.x * kGtT + threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * kGtRows;
   const int64_t r1 = min(m, r0 + kGtRows);
@@ -294,9 +295,9 @@ __global__ __launch_bounds__(kGtT) void k_gemv_t_partial(
     }
   }
   if (incol) partial[(int64_t)blockIdx.y * n + c] = acc;
-  if (maxw2) {
+  if (mpart) {
     const double x = (double)__uint_as_float(mb);
-    wave_max_nonneg_to(incol ? x * x * (wt ? (double)wt[c] : 1.0) : 0.0, maxw2);
+    wave_max_nonneg_part(incol ? x * x * (wt ? (double)wt[c] : 1.0) : 0.0, mpart);
   }
 }
 
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
     float* __restrict__ R, int64_t m, int64_t n, const uint32_t* __restrict__ u_codes,
     float* __restrict__ partial, const float* __restrict__ dprev,
     const uint32_t* __restrict__ uprev, const uint32_t* __restrict__ vprev,
-    unsigned long long* __restrict__ maxw2, const float* __restrict__ wt) {
+    double* __restrict__ mpart, const float* __restrict__ wt) {
   static_assert(kGtRows == 128, "eight code words per chunk");
   __shared__ float4 red[3][kWave];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -373,14 +374,14 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
     acc.y = fmaf(ur[k], val.y, acc.y);
     acc.z = fmaf(ur[k], val.z, acc.z);
     acc.w = fmaf(ur[k], val.w, acc.w);
-    if (maxw2 && r0 + w + 4 * k < m) {
+    if (mpart && r0 + w + 4 * k < m) {
       mb[0] = max(mb[0], __float_as_uint(val.x) & 0x7fffffffu);
       mb[1] = max(mb[1], __float_as_uint(val.y) & 0x7fffffffu);
       mb[2] = max(mb[2], __float_as_uint(val.z) & 0x7fffffffu);
       mb[3] = max(mb[3], __float_as_uint(val.w) & 0x7fffffffu);
     }
   }
-  if (maxw2) {
+  if (mpart) {
     double mx = 0.0;
     if (incol) {
 #pragma unroll
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(256) void k_gemv_t_vec(
         mx = fmax(mx, x * x * (wt ? (double)wt[4 * c4 + e] : 1.0));
       }
     }
-    wave_max_nonneg_to(mx, maxw2);
+    wave_max_nonneg_part(mx, mpart);
   }
   if (w > 0) red[w - 1][lane] = acc;
   __syncthreads();
@@ -536,12 +537,16 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
                                                   double* __restrict__ trace,
                                                   long long* __restrict__ stats,
                                                   const double* __restrict__ sv,
-                                                  unsigned long long* __restrict__ maxw2,
+                                                  const double* __restrict__ mpart, int64_t nmpart,
                                                   double* __restrict__ sg_state) {
   __shared__ double scratch[kTernT / kWave];
   double acc = 0.0;
   for (int64_t r = threadIdx.x; r < m; r += kTernT) acc += (double)code_at(u_codes, r) * (double)x[r];
   const double c = block_sum<kTernT>(acc, scratch);
+  // the single-entry bound of R before this component, from the first pass's partials
+  double bmx = 0.0;
+  for (int64_t q = threadIdx.x; q < nmpart; q += kTernT) bmx = fmax(bmx, mpart[q]);
+  const double bound = block_max_f64<kTernT>(bmx, scratch);
   if (threadIdx.x == 0) {
     const double den = (double)(*nnz_u) * (sv ? *sv : (double)(*nnz_v));
     const double d = den > 0.0 ? c / den : 0.0;
@@ -556,18 +561,15 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
     }
     // Single-entry safeguard check (appendix §7) against the bound the
     // component's first pass measured.  With sg_state (the safeguard
-    // applied), the decision and the fit's decrease are left for
-    // k_safeguard_argmax / k_safeguard_apply, which reset the bound;
-    // otherwise it is reset here.
-    const double bound = __longlong_as_double((long long)*maxw2);
+    // applied), the decision, the fit's decrease and the bound are left for
+    // k_safeguard_argmax / k_safeguard_apply.
     const bool would = dec < bound;
     if (would && stats) stats[EXTERND_STAT_SAFEGUARD] += 1;
     if (sg_state) {
       sg_state[0] = would ? 1.0 : 0.0;
       sg_state[1] = dec;
       reinterpret_cast<unsigned long long*>(sg_state)[2] = ~0ull;   // argmin index
-    } else {
-      *maxw2 = 0ull;
+      sg_state[3] = bound;
     }
   }
 }
@@ -577,9 +579,9 @@ __global__ __launch_bounds__(kTernT) void k_scale(const float* __restrict__ x, i
 // whose w_c R_rc^2 equals it (the same fp64 expression the bound was taken
 // over), found over R before component i's deflation.
 __global__ void k_safeguard_argmax(const float* __restrict__ R, int64_t m, int64_t n, const float* __restrict__ wt,
-                                   const unsigned long long* __restrict__ maxw2, double* __restrict__ sg_state) {
+                                   double* __restrict__ sg_state) {
   if (sg_state[0] == 0.0) return;
-  const double bound = __longlong_as_double((long long)*maxw2);
+  const double bound = sg_state[3];
   const int64_t total = m * n;
   unsigned long long best = ~0ull;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
@@ -597,13 +599,13 @@ __global__ void k_safeguard_argmax(const float* __restrict__ R, int64_t m, int64
 }
 
 // Replace component i by the single entry e_r e_c^T with d = R_rc: codes,
-// scale, predicted trace and nonzero counts; then reset the bound.
+// scale, predicted trace and nonzero counts.
 __global__ void k_safeguard_apply(const float* __restrict__ R, int64_t m, int64_t n, const float* __restrict__ wt,
                                   uint32_t* __restrict__ ub, int64_t wm, uint32_t* __restrict__ vc, int64_t wn,
                                   float* __restrict__ D, int64_t i, double* __restrict__ trace_state,
                                   double* __restrict__ trace, long long* __restrict__ stats,
                                   const int32_t* __restrict__ nnz_u, const int32_t* __restrict__ nnz_v,
-                                  unsigned long long* __restrict__ maxw2, double* __restrict__ sg_state) {
+                                  double* __restrict__ sg_state) {
   const bool take = sg_state[0] != 0.0;
   const unsigned long long idx = reinterpret_cast<const unsigned long long*>(sg_state)[2];
   const bool ok = take && idx < (unsigned long long)(m * n);
@@ -623,10 +625,7 @@ __global__ void k_safeguard_apply(const float* __restrict__ R, int64_t m, int64_
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    *maxw2 = 0ull;
-    sg_state[0] = 0.0;
-  }
+  if (threadIdx.x == 0) sg_state[0] = 0.0;
 }
 
 
@@ -641,9 +640,9 @@ __global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restric
                                                           double* __restrict__ partial,
                                                           long long* __restrict__ nonfinite,
                                                           const float* __restrict__ wt, int64_t ncols,
-                                                          unsigned long long* __restrict__ maxw2) {
-  // with column weights wt (ncols columns): sum_j wt_j A_ij^2 (§2.5); maxw2
-  // (optional) is raised to the largest wt_j A_ij^2 (the single-entry bound)
+                                                          double* __restrict__ mpart) {
+  // with column weights wt (ncols columns): sum_j wt_j A_ij^2 (§2.5); mpart
+  // (optional) receives per-wave maxima of wt_j A_ij^2 (the single-entry bound)
   __shared__ double scratch[kNormT / kWave];
   const int64_t b0 = (int64_t)blockIdx.x * per_block;
   const int64_t b1 = min(total, b0 + per_block);
@@ -666,7 +665,7 @@ __global__ __launch_bounds__(kNormT) void k_norm2_partial(const float* __restric
       mx = fmax(mx, e);
     }
   }
-  if (maxw2) wave_max_nonneg_to(mx, maxw2);
+  if (mpart) wave_max_nonneg_part(mx, mpart);
   const double s = block_sum<kNormT>(acc, scratch);
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
   if (nonfinite) {
@@ -803,18 +802,24 @@ hipError_t launch_importance_weights(const float* h, int64_t n, float lambda, fl
 
 int64_t gemv_t_chunks(int64_t m) { return (m + kGtRows - 1) / kGtRows; }
 
+int64_t gemv_t_max_partials(int64_t m, int64_t n) {
+  const int64_t chunks = gemv_t_chunks(m);
+  const int64_t wgs = (n & 3) == 0 ? (n / 4 + kWave - 1) / kWave * chunks : (n + kGtT - 1) / kGtT * chunks;
+  return wave_partials(wgs, 256);
+}
+
 hipError_t launch_gemv_t(float* R, int64_t m, int64_t n, const uint32_t* u_codes, float* partial,
                          float* y, const float* dprev, const uint32_t* uprev,
-                         const uint32_t* vprev, hipStream_t s, unsigned long long* maxw2, const float* wt) {
+                         const uint32_t* vprev, hipStream_t s, double* mpart, const float* wt) {
   const int64_t chunks = gemv_t_chunks(m);
   if ((n & 3) == 0) {
     dim3 grid((unsigned)((n / 4 + kWave - 1) / kWave), (unsigned)chunks);
     hipLaunchKernelGGL(k_gemv_t_vec, grid, dim3(256), 0, s, R, m, n, u_codes, partial, dprev, uprev, vprev,
-                       maxw2, wt);
+                       mpart, wt);
   } else {
     dim3 grid((unsigned)((n + kGtT - 1) / kGtT), (unsigned)chunks);
     hipLaunchKernelGGL(k_gemv_t_partial, grid, dim3(kGtT), 0, s, R, m, n, u_codes, partial, dprev,
-                       uprev, vprev, maxw2, wt);
+                       uprev, vprev, mpart, wt);
   }
   hipLaunchKernelGGL(k_sum_chunks, dim3(grid1(n, 256, 1 << 30)), dim3(256), 0, s, partial, chunks,
                      n, y);
@@ -844,13 +849,14 @@ hipError_t launch_deflate(float* R, int64_t m, int64_t n, const uint32_t* u_code
 
 hipError_t launch_norm2(const float* A, int64_t total, double* partial, int64_t partial_cap,
                         double* out, long long* nonfinite, hipStream_t s, const float* wt,
-                        int64_t ncols, unsigned long long* maxw2) {
+                        int64_t ncols, double* mpart, int64_t* nmpart) {
   int64_t blocks = std::min<int64_t>(partial_cap, std::max<int64_t>(1, (total + 65535) / 65536));
   const int64_t per_block = (total + blocks - 1) / blocks;
   if (total == 0) blocks = 1;
   if (wt && ncols < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_norm2_partial, dim3((unsigned)blocks), dim3(kNormT), 0, s, A, total,
-                     std::max<int64_t>(per_block, 1), partial, nonfinite, wt, ncols, maxw2);
+                     std::max<int64_t>(per_block, 1), partial, nonfinite, wt, ncols, mpart);
+  if (nmpart) *nmpart = wave_partials(blocks, kNormT);
   hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(64), 0, s, partial, blocks, out);
   return hipGetLastError();
 }
@@ -889,7 +895,8 @@ size_t stream_workspace_bytes(int64_t m, int64_t n) {
   b += sizeof(int32_t) * 8;                      // nnz counters
   b += sizeof(long long) * EXTERND_STATS_LEN;    // local stats
   b += sizeof(float) * (size_t)n + sizeof(double) * 8;   // column weights, v^T diag(wt) v
-  b += sizeof(double) * 8;                       // single-entry bound and safeguard state
+  b += sizeof(double) * 8;                       // safeguard state
+  b += sizeof(double) * (size_t)gemv_t_max_partials(m, n);   // single-entry bound partials
   b += 256 * 12;                                 // alignment slack
   return b;
 }
@@ -921,13 +928,16 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
   p = align_up(p + sizeof(float) * n, 256);
   double* sv = a.importance ? reinterpret_cast<double*>(p) : nullptr;  // v^T diag(wt) v
   p = align_up(p + sizeof(double) * 8, 256);
-  // bits of the single-entry bound of the current residual (appendix §7);
-  // the safeguard's state: flag, the fit's decrease, the argmax index
-  unsigned long long* maxw2 = reinterpret_cast<unsigned long long*>(p);
-  double* sg_state = reinterpret_cast<double*>(p) + 1;
+  // the safeguard's state: flag, the fit's decrease, the argmax index, the
+  // bound; then the per-wave partial maxima of the single-entry bound
+  // (appendix §7) left by each component's first pass
+  double* sg_state = reinterpret_cast<double*>(p);
+  p = align_up(p + sizeof(double) * 8, 256);
+  double* mpart = reinterpret_cast<double*>(p);
+  const int64_t nmpart = gemv_t_max_partials(m, n);
 
   hipError_t e;
-  if ((e = launch_fill_i64(reinterpret_cast<long long*>(p), 4, 0, s)) != hipSuccess) return e;
+  if ((e = launch_fill_i64(reinterpret_cast<long long*>(sg_state), 4, 0, s)) != hipSuccess) return e;
   if ((e = launch_fill_i64(st, EXTERND_STATS_LEN, 0, s)) != hipSuccess) return e;
   if (wt && (e = launch_importance_weights(a.importance, n, a.lambda, wt, st + EXTERND_STAT_NONFINITE, s)) != hipSuccess)
     return e;
@@ -957,7 +967,7 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
       const bool fuse = (t == 0 && pending);
       // the first pass (dense u0, every row read) also measures the bound
       e = launch_gemv_t(R, m, n, ub, partial, y, fuse ? a.D + i - 1 : nullptr,
-                        fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s, t == 0 ? maxw2 : nullptr, wt);
+                        fuse ? ub_prev : nullptr, fuse ? vc_prev : nullptr, s, t == 0 ? mpart : nullptr, wt);
       if (e != hipSuccess) return e;
       pending = false;
       e = a.projection ? launch_project(y, n, vc, nnz_v, st + EXTERND_STAT_FALLBACKS, s, wt, sv,
@@ -979,12 +989,13 @@ hipError_t run_stream_seq(const SeqArgs& a, void* ws, hipStream_t s) {
       }
     }
     hipLaunchKernelGGL(k_scale, dim3(1), dim3(kTernT), 0, s, x, m, ub, nnz_u, nnz_v, a.D, i, tstate,
-                       a.trace, st, (const double*)sv, maxw2, a.safeguard ? sg_state : (double*)nullptr);
+                       a.trace, st, (const double*)sv, (const double*)mpart, nmpart,
+                       a.safeguard ? sg_state : (double*)nullptr);
     if (a.safeguard) {
       hipLaunchKernelGGL(k_safeguard_argmax, dim3(grid1(m * n, 256, 1024)), dim3(256), 0, s, R, m, n,
-                         (const float*)wt, (const unsigned long long*)maxw2, sg_state);
+                         (const float*)wt, sg_state);
       hipLaunchKernelGGL(k_safeguard_apply, dim3(1), dim3(256), 0, s, R, m, n, (const float*)wt, ub, wm, vc, wn,
-                         a.D, i, tstate, a.trace, st, nnz_u, nnz_v, maxw2, sg_state);
+                         a.D, i, tstate, a.trace, st, nnz_u, nnz_v, sg_state);
     }
     pending = true;
     if (cap && a.capture_d && (e = launch_copy_f32(a.D + i, a.capture_d, 1, s)) != hipSuccess) return e;
