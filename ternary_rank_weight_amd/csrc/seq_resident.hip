@@ -41,10 +41,11 @@
 // Safeguard check (appendix §7).  Every thread keeps the largest w_j R_ij^2
 // of the column-copy entries it holds (each residual entry is held by exactly
 // one thread of one workgroup), so the single-entry bound max_ij w_j R_ij^2
-// is exceeded by the component's decrease everywhere or not: a thread whose
-// own maximum beats the decrease sets the component's bit in a bitmap (an
-// idempotent atomic OR, so no reduction or barrier is needed), and the bits
-// are counted at the end.
+// is exceeded by the component's decrease everywhere or not: a wave with a
+// thread whose own maximum beats the decrease sets the component's bit in
+// the workgroup's LDS window of 1024 components (an idempotent OR, so no
+// reduction or barrier is needed), every full window is ORed into the
+// global bitmap, and the bits are counted at the end.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   __shared__ float u_own[LR];
   __shared__ float v_own[LC];
   __shared__ double bufs[3][W][4];
+  __shared__ unsigned sg_win[32];   // safeguard bits of the current window of 1024 components
 
   const int t = threadIdx.x;
   const int g = blockIdx.x;
@@ -388,13 +390,25 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   float wcol[LC];
 #pragma unroll
   for (int l = 0; l < LC; ++l) wcol[l] = (a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f;
+  if (t < 32) sg_win[t] = 0u;   // published by the first barrier below
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
   long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
   double trace_state = *a.a2;
   const bool capturer = (g == 0);
 
+  const int sg_words = (a.k + 31) / 32;
   for (int i = 0; i <= a.k; ++i) {
+    // ---- a finished window of safeguard bits (or the last one) to the global bitmap ----
+    if (i > 0 && ((i & 1023) == 0 || i == a.k)) {
+      __syncthreads();
+      if (t < 32) {
+        const int word = ((i - 1) >> 10) * 32 + t;
+        const unsigned b = sg_win[t];
+        if (b != 0u && word < sg_words) atomicOr(a.sg_bits + word, b);
+        sg_win[t] = 0u;
+      }
+    }
     // ---- deflate component i-1 out of both copies (§2.3 step 3) ----
     if (i > 0) {
 #pragma unroll
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
       d32 = den > 0.0 ? (float)(c / den) : 0.f;
       const double dec = den > 0.0 ? c * c / den : 0.0;
       trace_state -= dec;
-      if (__any(dec < rmax2) && (t & (kWave - 1)) == 0) atomicOr(a.sg_bits + (i >> 5), 1u << (i & 31));
+      if (__any(dec < rmax2) && (t & (kWave - 1)) == 0) atomicOr(&sg_win[(i & 1023) >> 5], 1u << (i & 31));
       st_b += (long long)nu;
       st_c += (long long)nv;
       if (g == 0 && t == 0) {
