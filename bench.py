@@ -239,6 +239,36 @@ def measure_streaming(trw, Ad, c, k=256):
     return out
 
 
+def measure_streaming_large(trw, k=64, name="mlp9728"):
+    """The sequential decomposition on a shape past the resident limit
+    (9728 x 2560, the LLM-shaped MLP workload, mu for its first k components,
+    tau 0.7), in the persistent streaming mode and in the streaming kernel
+    chain: event time, components/s, the algorithmic bytes rate (the
+    roofline's byte model) and its fraction of the HBM peak."""
+    import torch
+    import synthetic
+    A = torch.from_numpy(synthetic.workload_matrix(name)).cuda()
+    m, n = A.shape
+    c = synthetic.WORKLOADS[name]
+    mu = (k + 0.25) / min(m, n)
+    out = {"workload": f"{m}x{n} LLM-shaped, first {k} components, tau 0.7, sequential mode"}
+    for label, mode in (("persistent", trw.MODE_PERSISTENT), ("streaming", trw.MODE_STREAMING)):
+        trw.decompose(A, mu, 0.7, c["iters"], 0, c["seed"], mode=mode)   # warm
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = trw.decompose(A, mu, 0.7, c["iters"], 0, c["seed"], mode=mode, stats=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        alg = seq_alg_bytes(m, n, k, r.stat("iterations") or k * c["iters"], r.stat("sum_nnz_u"))
+        gbps = alg / (ms / 1e3) / 1e9
+        out[label] = {"ms": round(ms, 3), "components_per_s": round(k / (ms / 1e3), 1), "alg_bytes": alg,
+                      "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                      "energy": round(float(r.energy.item()), 6), "safeguard": r.stat("safeguard")}
+    return out
+
+
 def cpu_baseline(A, c, sample, block=0):
     """The oracle timed on a bounded sample: the first `sample` components of
     the sequential decomposition, or for block mode alone (block > 0) the
@@ -455,6 +485,8 @@ def main():
     if "seq" in per_mode and args.streaming:
         print("[bench] streaming", file=sys.stderr, flush=True)
         streaming = measure_streaming(trw, Ad, c)
+        print("[bench] streaming 9728x2560", file=sys.stderr, flush=True)
+        streaming["large"] = measure_streaming_large(trw)
     sweeps = None
     if "block" in per_mode and args.sweeps > 0:
         print("[bench] sweeps", file=sys.stderr, flush=True)

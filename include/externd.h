@@ -48,9 +48,13 @@ enum externd_status {
 
 /* Execution modes of the sequential path. */
 enum externd_mode {
-  EXTERND_MODE_AUTO = -1,      /* resident when the shape fits on chip, else streaming */
-  EXTERND_MODE_STREAMING = 0,  /* R in device memory, one kernel per ALS half-step */
-  EXTERND_MODE_RESIDENT = 1    /* one cooperative kernel, R kept in LDS/VGPRs */
+  EXTERND_MODE_AUTO = -1,      /* resident when the shape fits on chip, else persistent streaming
+                                  when it applies, else streaming */
+  EXTERND_MODE_STREAMING = 0,  /* R in device memory, a few kernels per ALS half-step */
+  EXTERND_MODE_RESIDENT = 1,   /* one cooperative kernel, R kept in LDS/VGPRs */
+  EXTERND_MODE_PERSISTENT = 2  /* one cooperative kernel, R in device memory: n % 4 == 0,
+                                  m, n <= 10240 and at most 64 rows per CU; not with the
+                                  optimal projection or an applied safeguard */
 };
 
 enum externd_ternarizer { EXTERND_TERN_MEAN = 0, EXTERND_TERN_PROJECTION = 1 };
@@ -63,8 +67,9 @@ enum externd_stat {
   EXTERND_STAT_NNZ_C = 3,       /* nonzeros in the final C */
   EXTERND_STAT_FALLBACKS = 4,   /* T_tau calls that fell back to the single largest entry */
   EXTERND_STAT_NONFINITE = 5,   /* non-finite entries found in A (energy is NaN if > 0) */
-  EXTERND_STAT_MODE = 6,        /* mode actually run (0 streaming, 1 resident, 2 block) */
-  EXTERND_STAT_GRID = 7,        /* workgroups of the resident kernel (0 otherwise) */
+  EXTERND_STAT_MODE = 6,        /* mode actually run (0 streaming, 1 resident, 2 block,
+                                   3 persistent streaming) */
+  EXTERND_STAT_GRID = 7,        /* workgroups of the resident or persistent kernel (0 otherwise) */
   EXTERND_STAT_RIDGE_RETRIES = 8, /* block mode: joint scale solves retried with a ridge */
   EXTERND_STAT_TIMEOUTS = 9,    /* waits that ran out (energy is NaN): resident exchange, or
                                    block mode's Gram-before-inverse wait */

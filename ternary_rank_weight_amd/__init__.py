@@ -18,13 +18,13 @@ __all__ = [
     "workspace_bytes",
     "rank_for_energy", "mu_for_energy", "project",
     "ternarize", "gemv_t", "gemv_n", "deflate", "Decomposition", "ExterndError",
-    "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "library_path",
+    "STAT", "MODE_AUTO", "MODE_STREAMING", "MODE_RESIDENT", "MODE_PERSISTENT", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libexternd.so")
 
-MODE_AUTO, MODE_STREAMING, MODE_RESIDENT = -1, 0, 1
+MODE_AUTO, MODE_STREAMING, MODE_RESIDENT, MODE_PERSISTENT = -1, 0, 1, 2
 STATS_LEN = 16
 STAT = {"sum_nnz_u": 0, "sum_nnz_v": 1, "nnz_b": 2, "nnz_c": 3, "fallbacks": 4,
         "nonfinite": 5, "mode": 6, "grid": 7, "ridge_retries": 8, "timeouts": 9,

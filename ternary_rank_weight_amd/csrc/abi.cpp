@@ -65,6 +65,21 @@ bool bad_size(int64_t m, int64_t n) {
          m * n > (int64_t(1) << 40);
 }
 
+// The sequential mode a request runs in: AUTO takes the resident kernel when
+// the shape fits on chip (not with the projection or an applied safeguard),
+// else the persistent streaming kernel when it applies, else the streaming
+// kernel chain.  -1 when an explicit mode does not apply to the shape.
+int seq_mode(int requested, int64_t m, int64_t n, int cus, bool projection, bool safeguard) {
+  const bool res_ok = externd::resident_fits(m, n, cus) && !projection && !safeguard;
+  const bool per_ok = externd::persist_fits(m, n, cus) && !projection && !safeguard;
+  switch (requested) {
+    case EXTERND_MODE_RESIDENT: return res_ok ? EXTERND_MODE_RESIDENT : -1;
+    case EXTERND_MODE_PERSISTENT: return per_ok ? EXTERND_MODE_PERSISTENT : -1;
+    case EXTERND_MODE_STREAMING: return EXTERND_MODE_STREAMING;
+    default: return res_ok ? EXTERND_MODE_RESIDENT : (per_ok ? EXTERND_MODE_PERSISTENT : EXTERND_MODE_STREAMING);
+  }
+}
+
 // Stream-ordered workspace: allocated on the stream, freed on the stream
 // (or borrowed from the caller, then never freed here).
 struct Workspace {
@@ -182,17 +197,19 @@ int32_t externd_resident_fits(int64_t m, int64_t n) {
 uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, int32_t mode) {
   if (bad_size(m, n)) return (fail(EXTERND_EINVAL, "bad shape"), 0);
   if (!std::isfinite(mu) || mu <= 0.f) return (fail(EXTERND_EINVAL, "mu must be finite and > 0"), 0);
-  if (mode < -1 || mode > 1) return (fail(EXTERND_EINVAL, "bad mode %d", mode), 0);
+  if (mode < -1 || mode > 2) return (fail(EXTERND_EINVAL, "bad mode %d", mode), 0);
   const int b = externd_block_width(m, n, block);
   if (b > 1) return externd::block_workspace_bytes(m, n, b);
+  const int64_t k = externd_rank(m, n, mu);
   if (mode == EXTERND_MODE_STREAMING) return externd::stream_workspace_bytes(m, n);
   int cus = 0;
   if (check_device(&cus) != EXTERND_OK) return 0;
-  const bool fits = externd::resident_fits(m, n, cus);
-  if (mode == EXTERND_MODE_RESIDENT && !fits)
-    return (fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel",
-                 (long long)m, (long long)n), 0);
-  return fits ? externd::resident_workspace_bytes(m, n, externd_rank(m, n, mu)) : externd::stream_workspace_bytes(m, n);
+  const int md = seq_mode(mode, m, n, cus, false, false);
+  if (md < 0) return (fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the %s kernel", (long long)m, (long long)n,
+                           mode == EXTERND_MODE_RESIDENT ? "resident" : "persistent streaming"), 0);
+  if (md == EXTERND_MODE_RESIDENT) return externd::resident_workspace_bytes(m, n, k);
+  if (md == EXTERND_MODE_PERSISTENT) return externd::persist_workspace_bytes(m, n, k, cus);
+  return externd::stream_workspace_bytes(m, n);
 }
 
 int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau, int32_t iters,
@@ -216,7 +233,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
                   sizeof(externd_opts));
     o = *opts;
   }
-  if (o.mode < -1 || o.mode > 1) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
+  if (o.mode < -1 || o.mode > 2) return fail(EXTERND_EINVAL, "bad mode %d", o.mode);
   if (o.sweeps < 0) return fail(EXTERND_EINVAL, "sweeps must be >= 0");
   if (!std::isfinite(o.importance_lambda) || o.importance_lambda < 0.f)
     return fail(EXTERND_EINVAL, "importance_lambda must be finite and >= 0");
@@ -226,7 +243,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   if (projection && (m > externd::kProjMaxN || n > externd::kProjMaxN))
     return fail(EXTERND_EUNSUPPORTED, "the optimal projection takes vectors of at most %d entries",
                 externd::kProjMaxN);
-  if (projection && o.mode == EXTERND_MODE_RESIDENT)
+  if (projection && (o.mode == EXTERND_MODE_RESIDENT || o.mode == EXTERND_MODE_PERSISTENT))
     return fail(EXTERND_EUNSUPPORTED, "the optimal projection runs in streaming or block mode");
   if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u) != 0)
     return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned");
@@ -241,7 +258,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     return fail(EXTERND_EUNSUPPORTED, "the safeguard's replacement runs in the sequential path only");
   if (o.safeguard && projection)
     return fail(EXTERND_EUNSUPPORTED, "the safeguard is not combined with the optimal projection");
-  if (o.safeguard && o.mode == EXTERND_MODE_RESIDENT)
+  if (o.safeguard && (o.mode == EXTERND_MODE_RESIDENT || o.mode == EXTERND_MODE_PERSISTENT))
     return fail(EXTERND_EUNSUPPORTED, "the safeguard's replacement runs in streaming mode");
   const externd_block_capture* bc = o.block_capture;
   if (bc && b > 1) {
@@ -320,13 +337,10 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   } else {
     sa.capture_component = -1;
   }
-  const bool fits = externd::resident_fits(m, n, cus);
-  int mode = o.mode;
-  if (mode == EXTERND_MODE_AUTO)
-    mode = (fits && !projection && !o.safeguard) ? EXTERND_MODE_RESIDENT : EXTERND_MODE_STREAMING;
-  if (mode == EXTERND_MODE_RESIDENT && !fits)
-    return fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the resident kernel", (long long)m,
-                (long long)n);
+  const int mode = seq_mode(o.mode, m, n, cus, projection, o.safeguard != 0);
+  if (mode < 0)
+    return fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the %s kernel", (long long)m, (long long)n,
+                o.mode == EXTERND_MODE_RESIDENT ? "resident" : "persistent streaming");
   Workspace w;
   hipError_t e;
   if (mode == EXTERND_MODE_RESIDENT) {
@@ -334,6 +348,10 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     int grid = 0;
     e = externd::run_resident_seq(sa, w.ptr, cus, s, &grid);
     if (e != hipSuccess) return hip_fail(e, "resident decomposition");
+  } else if (mode == EXTERND_MODE_PERSISTENT) {
+    if ((st = get_ws(w, o, externd::persist_workspace_bytes(m, n, k, cus), s)) != EXTERND_OK) return st;
+    e = externd::run_persist_seq(sa, w.ptr, cus, s);
+    if (e != hipSuccess) return hip_fail(e, "persistent streaming decomposition");
   } else {
     if ((st = get_ws(w, o, externd::stream_workspace_bytes(m, n), s)) != EXTERND_OK) return st;
     e = externd::run_stream_seq(sa, w.ptr, s);

@@ -106,6 +106,12 @@ hipError_t launch_fill_f32(float* p, int64_t count, float v, hipStream_t s);
 hipError_t launch_fill_i64(long long* p, int64_t count, long long v, hipStream_t s);
 hipError_t launch_copy_f32(const float* a, float* b, int64_t count, hipStream_t s);
 
+// persistent streaming sequential path (seq_persist.hip): one cooperative
+// launch, R in device memory; n % 4 == 0 and the shapes its instantiations cover
+bool persist_fits(int64_t m, int64_t n, int num_cus);
+size_t persist_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus);
+hipError_t run_persist_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s);
+
 // resident sequential path (seq_resident.hip)
 bool resident_fits(int64_t m, int64_t n, int num_cus);
 size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k);

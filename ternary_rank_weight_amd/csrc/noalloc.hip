@@ -62,7 +62,7 @@ extern "C" int externd_decompose_noalloc(const float* A, int64_t m, int64_t n, f
   }
   if (o.workspace)
     return externd::report(EXTERND_EINVAL, "externd_decompose_noalloc brings its own scratch: opts.workspace must be NULL");
-  if (externd_block_width(m, n, block) > 1 || o.mode == EXTERND_MODE_STREAMING)
+  if (externd_block_width(m, n, block) > 1 || o.mode == EXTERND_MODE_STREAMING || o.mode == EXTERND_MODE_PERSISTENT)
     return externd::report(EXTERND_EUNSUPPORTED, "externd_decompose_noalloc runs the resident sequential path only");
   o.mode = EXTERND_MODE_RESIDENT;
   const uint64_t need = externd_workspace_bytes(m, n, mu, block, EXTERND_MODE_RESIDENT);

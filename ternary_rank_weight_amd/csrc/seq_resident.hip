@@ -48,17 +48,13 @@
 // global bitmap, and the bits are counted at the end.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "exchange.hpp"
 
 namespace externd {
 
 namespace {
 
-constexpr unsigned kSpinLimit = 1u << 21;
-constexpr int kRep = 4;   // replicas of every exchange word
-// words between replicas of a length-len slot array: a whole number of 4 KB
-__host__ __device__ inline int rep_stride(int len) { return (len + 1023) / 1024 * 1024; }
-// the replica workgroup g reads: one per pair of XCDs (round-robin dispatch)
-__device__ inline int rep_of(int g) { return (g & 7) >> 1; }
+using namespace xchg;
 
 struct ResArgs {
   const float* A;
@@ -90,228 +86,6 @@ struct ResArgs {
   int8_t* cap_u;
   float* cap_d;
 };
-
-// Exchange word: the value with its lowest bit replaced by the round parity.
-__device__ inline unsigned xw_pack(unsigned round, float v) {
-  return (__float_as_uint(v) & ~1u) | (round & 1u);
-}
-__device__ inline float xw_value(unsigned w) { return __uint_as_float(w & ~1u); }
-
-// Sum acc[l] over the T threads for l < L (DPP inside each wave, then the
-// waves in index order) and publish output l < nvalid as slot[base + l] in
-// each of the kRep replicas, rstride words apart.
-template <int T, int L>
-__device__ inline void reduce_publish(const float (&acc)[L], float* red, int nvalid,
-                                      unsigned* slot, int base, unsigned round, int rstride) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), w = t / kWave;
-  float sums[L];
-#pragma unroll
-  for (int l = 0; l < L; ++l) sums[l] = wave_sum_to63(acc[l]);
-  if (lane == kWave - 1) {
-#pragma unroll
-    for (int l = 0; l < L; ++l) red[w * L + l] = sums[l];
-  }
-  __syncthreads();
-  if (t < nvalid) {
-    float s = red[t];
-#pragma unroll
-    for (int q = 1; q < T / kWave; ++q) s += red[q * L + t];
-    const unsigned word = xw_pack(round, s);
-#pragma unroll
-    for (int r = 0; r < kRep; ++r)
-      __hip_atomic_store(slot + r * rstride + base + t, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Block reductions with one barrier each.  buf is double[T/64][4]; two
-// consecutive reductions must use different buffers.
-template <int T>
-__device__ inline uint32_t block_umax_flag(uint32_t v, bool bad, double (*buf)[4], bool& any_bad) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), w = t / kWave;
-  const uint32_t mw = wave_umax_to63(v);
-  const bool bw = __any(bad);
-  if (lane == kWave - 1) {
-    buf[w][0] = (double)mw;
-    buf[w][1] = bw ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  uint32_t r = 0u;
-  bool b = false;
-#pragma unroll
-  for (int q = 0; q < T / kWave; ++q) {
-    r = max(r, (uint32_t)buf[q][0]);
-    b = b || buf[q][1] != 0.0;
-  }
-  any_bad = b;
-  return r;
-}
-template <int T, int NV>
-__device__ inline void block_sum_f64(double (&v)[NV], double (*buf)[4]) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), w = t / kWave;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const double s = wave_sum_to63(v[i]);
-    if (lane == kWave - 1) buf[w][i] = s;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    double r = buf[0][i];
-#pragma unroll
-    for (int q = 1; q < T / kWave; ++q) r += buf[q][i];
-    v[i] = r;
-  }
-}
-template <int T>
-__device__ inline int block_min_idx(int v, double (*buf)[4]) {
-  const int t = threadIdx.x;
-  const int w = t / kWave;
-  v = wave_min_i(v);
-  if ((t & (kWave - 1)) == 0) buf[w][0] = (double)v;
-  __syncthreads();
-  int r = INT32_MAX;
-#pragma unroll
-  for (int q = 0; q < T / kWave; ++q) r = min(r, (int)buf[q][0]);
-  return r;
-}
-
-// Morton spread of 16 bits: bit e -> bit 2e.
-__device__ inline uint32_t spread16(uint32_t x) {
-  x &= 0xffffu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  x = (x | (x << 1)) & 0x55555555u;
-  return x;
-}
-
-// Write the 2-bit codes of a distributed ternary vector val[j] = t[tid + T*j]
-// (length N) into dst[0 .. ceil(N/16)); workgroup g of G writes the words
-// w with w % G == g.  Uses wave ballots, no LDS and no barrier.
-template <int T, int K>
-__device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, int g, int G) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const int words = (N + 15) / 16;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const unsigned long long nz = __ballot(val[j] != 0.f);
-    const unsigned long long ng = __ballot(val[j] < 0.f);
-    const int row_base = (t & ~(kWave - 1)) + T * j;
-    if (lane < 4) {
-      const int w = (row_base >> 4) + lane;
-      if (w < words && w % G == g) {
-        const uint32_t a = (uint32_t)(nz >> (16 * lane)) & 0xffffu;
-        const uint32_t b = (uint32_t)(ng >> (16 * lane)) & 0xffffu;
-        dst[w] = spread16(a) | (spread16(b) << 1);
-      }
-    }
-  }
-}
-
-// Read the n (or m) published words of the current round into val[j] for
-// index t + T*j.  Returns false if a wait ran out.
-template <int T, int K>
-__device__ inline bool gather(const unsigned* slot, int N, unsigned round, float (&val)[K],
-                              const unsigned* err) {
-  const int t = threadIdx.x;
-  const unsigned par = round & 1u;
-  unsigned w[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int idx = t + T * j;
-    w[j] = idx < N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : par;
-  }
-  unsigned spins = 0;
-  bool ok = true;
-  while (true) {
-    bool all = true;
-#pragma unroll
-    for (int j = 0; j < K; ++j) all = all && (w[j] & 1u) == par;
-    if (all) break;
-    if (++spins > kSpinLimit) { ok = false; break; }
-    if ((spins & 255u) == 0 &&
-        __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-      ok = false;
-      break;
-    }
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int idx = t + T * j;
-      if ((w[j] & 1u) != par)
-        w[j] = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < K; ++j) val[j] = ok ? xw_value(w[j]) : 0.f;
-  return ok;
-}
-
-// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond N),
-// identical in every workgroup.  `bad` folds a failed gather into the first
-// reduction: if any thread of the block has it set, returns false and the
-// caller leaves.  bufs[0..1] are used alternately (see block_umax_flag).
-// Writes T_tau(x) to out in the same layout; cnt gets this thread's nonzeros.
-template <int T, int K>
-__device__ inline bool ternarize_dist(const float (&val)[K], bool bad, int N, float tau,
-                                      float (&out)[K], double (*bufs)[T / kWave][4], int& cnt,
-                                      int& fallback) {
-  const int t = threadIdx.x;
-  uint32_t ab[K];
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    ab[j] = __float_as_uint(val[j]) & 0x7fffffffu;
-    mx = max(mx, ab[j]);
-  }
-  bool any_bad;
-  const uint32_t Mb = block_umax_flag<T>(mx, bad, bufs[0], any_bad);
-  if (any_bad) return false;
-  cnt = 0;
-  if (Mb == 0u) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
-    fallback = 1;
-    cnt = t == 0 ? 1 : 0;
-    return true;
-  }
-  const int s = fixed_point_shift(__uint_as_float(Mb), N);
-  // Every partial sum is an integer below 2^52, so the fp64 sums are exact.
-  double qs[1] = {0.0};
-#pragma unroll
-  for (int j = 0; j < K; ++j) qs[0] += fixed_point_q(__uint_as_float(ab[j]), s);
-  block_sum_f64<T, 1>(qs, bufs[1]);
-  const double thr = fixed_point_threshold(qs[0], s, tau, N);
-  const uint32_t tb = threshold_bits(thr);
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const bool keep = ab[j] > tb;
-    out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
-    cnt += keep ? 1 : 0;
-  }
-  fallback = 0;
-  if (Mb > tb) return true;
-  int first = INT32_MAX;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int idx = t + T * j;
-    if (idx < N && ab[j] == Mb) first = min(first, idx);
-  }
-  const int pick = block_min_idx<T>(first, bufs[0]);
-  cnt = 0;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    if (t + T * j == pick) {
-      out[j] = val[j] > 0.f ? 1.f : -1.f;
-      cnt = 1;
-    }
-  }
-  fallback = 1;
-  return true;
-}
 
 // Copy this workgroup's rows of the row-resident residual to dst (m x n).
 template <int T, int KR, int LR>

@@ -39,6 +39,7 @@ def _relnorm(a, b):
 CASES = [  # (m, n, mu, tau, block, mode, lam)
     (256, 256, 1.0, 0.7, 0, 1, 0.0),      # resident
     (300, 200, 1.0, 0.7, 0, 0, 0.0),      # streaming
+    (300, 200, 1.0, 0.7, 0, 2, 0.05),     # persistent streaming
     (256, 256, 1.0, 0.7, 0, 1, 0.05),
     (256, 256, 1.0, 0.7, 32, -1, 0.0),    # block, NS inverse
     (300, 200, 1.3, 1.0, 16, -1, 0.1),    # block, ragged
@@ -69,14 +70,14 @@ def test_weighted_vs_oracle(lib, m, n, mu, tau, block, mode, lam):
     assert abs(1 - tr[-1] / a2 - E) <= 1e-4
     assert res.stat("nnz_b") == np.count_nonzero(B) and res.stat("nnz_c") == np.count_nonzero(C)
     if mode >= 0:
-        assert res.stat("mode") == mode
+        assert res.stat("mode") == {0: 0, 1: 1, 2: 3}[mode]
     again = lib.decompose(Ad, mu, tau, 15, block, 2, mode=mode, importance=hd, lam=lam)
     torch.cuda.synchronize()
     assert torch.equal(again.B2, res.B2) and torch.equal(again.D, res.D)
     assert torch.equal(again.energy, res.energy)
 
 
-@pytest.mark.parametrize("block,mode", [(0, 1), (0, 0), (32, -1), (128, -1)])
+@pytest.mark.parametrize("block,mode", [(0, 1), (0, 0), (0, 2), (32, -1), (128, -1)])
 @pytest.mark.parametrize("level,lam", [(0.37, 0.0), (5.0, 3.0)])
 def test_flat_importance_is_the_plain_algorithm(lib, block, mode, level, lam):
     # weights exactly 1, or exactly 4 (every step scales by a power of two)
@@ -92,7 +93,7 @@ def test_flat_importance_is_the_plain_algorithm(lib, block, mode, level, lam):
     assert torch.equal(plain.energy, wtd.energy)
 
 
-@pytest.mark.parametrize("mode", [1, 0])
+@pytest.mark.parametrize("mode", [1, 0, 2])
 @pytest.mark.parametrize("comp", [0, 7])
 def test_weighted_capture_parity(lib, mode, comp):
     m, n, tau, iters, seed = 256, 200, 0.7, 6, 4
@@ -102,7 +103,7 @@ def test_weighted_capture_parity(lib, mode, comp):
     res = lib.decompose(_dev(A), 0.5, tau, iters, 0, seed, mode=mode, capture=comp, stats=True,
                         importance=_dev(h))
     torch.cuda.synchronize()
-    assert res.stat("mode") == mode
+    assert res.stat("mode") == {0: 0, 1: 1, 2: 3}[mode]
     cap = {k: v.cpu().numpy() for k, v in res.capture.items()}
     R64 = cap["R"].astype(np.float64)
     u = oracle.init_signs(seed, comp, m)
