@@ -23,6 +23,15 @@ __host__ __device__ inline int rep_stride(int len) { return (len + 1023) / 1024 
 // the replica workgroup g reads: one per pair of XCDs (round-robin dispatch)
 __device__ inline int rep_of(int g) { return (g & 7) >> 1; }
 
+// The thread index through an empty asm statement: index arithmetic built
+// from it inside a loop body stays there instead of being hoisted out of the
+// loop and kept live (or spilled to scratch) across the whole loop.
+__device__ inline int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Exchange word: the value with its lowest bit replaced by the round parity.
 __device__ inline unsigned xw_pack(unsigned round, float v) {
   return (__float_as_uint(v) & ~1u) | (round & 1u);
@@ -124,8 +133,8 @@ __device__ inline uint32_t spread16(uint32_t x) {
 // (length N) into dst[0 .. ceil(N/16)); workgroup g of G writes the words
 // w with w % G == g.  Uses wave ballots, no LDS and no barrier.
 template <int T, int K>
-__device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, int g, int G) {
-  const int t = threadIdx.x;
+__device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, int g, int G, int tid = -1) {
+  const int t = tid >= 0 ? tid : (int)threadIdx.x;
   const int lane = t & (kWave - 1);
   const int words = (N + 15) / 16;
 #pragma unroll
@@ -145,17 +154,18 @@ __device__ inline void store_codes(const float (&val)[K], int N, uint32_t* dst, 
 }
 
 // Read the n (or m) published words of the current round into val[j] for
-// index t + T*j.  Returns false if a wait ran out.
+// index t + T*j.  Returns false if a wait ran out.  tid: the thread index,
+// when the caller has one of its own (opaque_tid).
 template <int T, int K>
 __device__ inline bool gather(const unsigned* slot, int N, unsigned round, float (&val)[K],
-                              const unsigned* err) {
-  const int t = threadIdx.x;
+                              const unsigned* err, int tid = -1) {
+  const int t = tid >= 0 ? tid : (int)threadIdx.x;
   const unsigned par = round & 1u;
   unsigned w[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const int idx = t + T * j;
-    w[j] = idx < N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : par;
+    const unsigned idx = (unsigned)(t + T * j);
+    w[j] = idx < (unsigned)N ? __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : par;
   }
   unsigned spins = 0;
   bool ok = true;
@@ -172,7 +182,7 @@ __device__ inline bool gather(const unsigned* slot, int N, unsigned round, float
     }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const int idx = t + T * j;
+      const unsigned idx = (unsigned)(t + T * j);
       if ((w[j] & 1u) != par)
         w[j] = __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -190,8 +200,8 @@ __device__ inline bool gather(const unsigned* slot, int N, unsigned round, float
 template <int T, int K>
 __device__ inline bool ternarize_dist(const float (&val)[K], bool bad, int N, float tau,
                                       float (&out)[K], double (*bufs)[T / kWave][4], int& cnt,
-                                      int& fallback) {
-  const int t = threadIdx.x;
+                                      int& fallback, int tid = -1) {
+  const int t = tid >= 0 ? tid : (int)threadIdx.x;
   uint32_t ab[K];
   uint32_t mx = 0u;
 #pragma unroll
