@@ -160,10 +160,12 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
     const int col = t + T * j;
     wv[j] = (a.wt && col < n) ? a.wt[col] : 1.f;
   }
-  // weights of the column copy's columns (the same for every thread)
+  // weights of the column copy's columns (the same for every thread: scalar registers)
   float wcol[LC];
 #pragma unroll
-  for (int l = 0; l < LC; ++l) wcol[l] = (a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f;
+  for (int l = 0; l < LC; ++l)
+    wcol[l] = __int_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_int((a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f)));
   if (t < 32) sg_win[t] = 0u;   // published by the first barrier below
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
@@ -216,7 +218,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
 #pragma unroll
       for (int j = 0; j < KC; ++j) mb = max(mb, __float_as_uint(rc[l][j]) & 0x7fffffffu);
       const double x = (double)__uint_as_float(mb);
-      rmax2 = fmax(rmax2, x * x * (double)wcol[l]);
+      float wl = wcol[l];
+      asm volatile("" : "+s"(wl));   // converted here, not hoisted out of the loop as fp64
+      rmax2 = fmax(rmax2, x * x * (double)wl);
     }
     if (CAP && i == a.cap_i) {
       if (a.cap_R) dump_rows<T, KR, LR>(rrow, a, row0, a.cap_R);
