@@ -8,6 +8,11 @@ figures and the fp64 oracle's rate on a bounded sample as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--modes seq,block]
                     [--cpu-sample N | --no-cpu]
+                    [--workload gauss256|llm2560|mlp9728|layer|lowrank4096]
+
+The other workloads print a line of the same form for their own input:
+gauss256 adds the per-component energy trace, layer times the seven matrices
+of one transformer layer back to back, lowrank4096 times the mu x tau sweep.
 """
 import argparse
 import json
@@ -61,10 +66,13 @@ def parse():
                     help="skip the streaming-versus-resident comparison of the sequential mode")
     ap.add_argument("--sweeps", type=int, default=10,
                     help="refinement sweeps measured after the block run (0: skip)")
-    ap.add_argument("--workload", default="llm2560", choices=["gauss256", "llm2560", "mlp9728", "layer"],
-                    help="gauss256: 256x256 Gaussian; llm2560: 2560x2560 LLM-shaped (default); "
-                         "mlp9728: 9728x2560 LLM-shaped, mu=3, tau=1.0, block b=128; "
-                         "layer: the seven matrices of one 4B-class layer, mu=2.5, block b=128, back to back")
+    ap.add_argument("--workload", default="llm2560",
+                    choices=["gauss256", "llm2560", "mlp9728", "layer", "lowrank4096"],
+                    help="gauss256: 256x256 Gaussian, with the sequential energy trace; llm2560: "
+                         "2560x2560 LLM-shaped (default); mlp9728: 9728x2560 LLM-shaped, mu=3, tau=1.0, "
+                         "block b=128; layer: the seven matrices of one 4B-class layer, mu=2.5, block "
+                         "b=128, back to back; lowrank4096: the mu x tau sweep on a 4096x4096 rank-256 "
+                         "plus noise matrix, block b=128")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches) and "
                          "exit; its HBM counters calibrate the per-kernel traffic figures")
@@ -377,6 +385,110 @@ def run_layer(args):
     print(json.dumps(line), flush=True)
 
 
+def run_lowrank(args):
+    """The mu / tau sweep on the 4096 x 4096 rank-256-plus-noise matrix in
+    block mode (b = 128): every (mu, tau) pair is a separate decomposition,
+    reported with its energy and the zero fractions of its factors; a step is
+    the whole sweep (12 decompositions back to back on one stream).  Checks
+    that E does not fall as mu grows at fixed tau, and that the zero fraction
+    grows with tau at fixed mu."""
+    import numpy as np
+    import torch
+    import synthetic
+    import ternary_rank_weight_amd as trw
+
+    torch.cuda.set_device(0)
+    c = synthetic.WORKLOADS["lowrank4096"]
+    A = synthetic.workload_matrix("lowrank4096")
+    m, n = A.shape
+    Ad = torch.from_numpy(A).cuda()
+    runs = [(mu, tau) for tau in c["taus"] for mu in c["mus"]]
+    outs = {}
+
+    def step(record):
+        ev = {}
+        for mu, tau in runs:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            outs[(mu, tau)] = trw.decompose(Ad, mu, tau, c["iters"], c["block"], c["seed"], stats=True,
+                                            out=outs.get((mu, tau)))
+            e1.record()
+            ev[(mu, tau)] = (e0, e1)
+        if record is not None:
+            record.append(ev)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    records = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(records)
+        print("[bench] sweep launched", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    b = trw.block_width(m, n, c["block"])
+    sweep = []
+    total_k, total_ms, flops = 0, 0.0, 0.0
+    for mu, tau in runs:
+        r = outs[(mu, tau)]
+        ms = float(np.mean([rec[(mu, tau)][0].elapsed_time(rec[(mu, tau)][1]) for rec in records]))
+        k = r.k
+        nb, nc = r.stat("nnz_b"), r.stat("nnz_c")
+        fl = block_alg_flops(m, n, k, b, c["iters"])
+        total_k += k
+        total_ms += ms
+        flops += fl
+        sweep.append({"mu": mu, "tau": tau, "k": k, "ms": round(ms, 3),
+                      "components_per_s": round(k / (ms / 1e3), 1),
+                      "energy": round(float(r.energy.item()), 6),
+                      "zero_fraction_B": round(1.0 - nb / (k * m), 4),
+                      "zero_fraction_C": round(1.0 - nc / (k * n), 4),
+                      "zero_fraction": round(1.0 - (nb + nc) / (k * (m + n)), 4),
+                      "safeguard": r.stat("safeguard"), "timeouts": r.stat("timeouts"),
+                      "inverse_unconverged": r.stat("inverse_unconverged")})
+    by = {(e["mu"], e["tau"]): e for e in sweep}
+    e_monotone = {str(tau): all(by[(a, tau)]["energy"] <= by[(bb, tau)]["energy"]
+                                for a, bb in zip(c["mus"], c["mus"][1:])) for tau in c["taus"]}
+    z_increasing = {str(mu): all(by[(mu, a)]["zero_fraction"] < by[(mu, bb)]["zero_fraction"]
+                                 for a, bb in zip(c["taus"], c["taus"][1:])) for mu in c["mus"]}
+    tflops = flops / (total_ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu and args.cpu_sample > 0:
+        c1 = dict(c, mu=c["mus"][0], tau=c["taus"][0])
+        cpu = cpu_baseline(A, c1, min(args.cpu_sample, trw.rank(m, n, c1["mu"])), c["block"])
+        cpu["sample"] += f" (mu={c1['mu']}, tau={c1['tau']})"
+    line = {
+        "metric": "ALS components/sec + achieved HBM GB/s at 2560x2560 mu=2 tau=0.7; energy E",
+        "value": round(total_k / (total_ms / 1e3), 2),
+        "unit": "components/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{m}x{n} rank-256 structure (U diag(s) V^T, Gaussian U, V, s_i = i^-0.8) "
+                               f"plus N(0, 0.005^2) noise; mu in {list(c['mus'])} x tau in {list(c['taus'])}, "
+                               f"{c['iters']} iterations, block ALS b={b}; step = the 12 decompositions",
+                   "m": m, "n": n, "mus": list(c["mus"]), "taus": list(c["taus"]), "iters": c["iters"],
+                   "block": b, "seed": c["seed"], "k_total": total_k},
+        "sweep": sweep,
+        "checks": {"energy_nondecreasing_in_mu": e_monotone, "zero_fraction_increasing_in_tau": z_increasing},
+        "roofline": {"bound": "mfma", "kernel": "block ALS pipeline", "achieved": round(tflops, 3),
+                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+                     "traffic": None, "alg_flops_per_step": flops},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -387,6 +499,9 @@ def main():
         return
     if args.workload == "layer":
         run_layer(args)
+        return
+    if args.workload == "lowrank4096":
+        run_lowrank(args)
         return
     import numpy as np
     import torch
@@ -472,6 +587,14 @@ def main():
                         "unit": "TFLOP/s", "frac": round(bm["alg_tflops"] / FP32_PEAK_TFLOPS, 4),
                         "traffic": None, "alg_flops_per_run": fl}
 
+    trace = None
+    if args.workload == "gauss256" and "seq" in modes:
+        # the per-component energy trace of the sequential run (outside the timed region)
+        r = trw.decompose(Ad, c["mu"], c["tau"], c["iters"], 0, c["seed"], trace=True)
+        tr = r.trace.cpu().numpy()
+        na2 = float(r.norm_a2.item())
+        trace = {"what": "E after each component, 1 - ||R_i||^2 / ||A||^2, sequential mode",
+                 "energy": [round(1.0 - float(v) / na2, 7) for v in tr]}
     inference = measure_inference(trw, outs, m, n)
     importance = None
     if args.importance:
@@ -525,6 +648,7 @@ def main():
         "importance_weighted": importance,
         "optimal_projection": projection,
         "seq_streaming_vs_resident": streaming,
+        "trace": trace,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
