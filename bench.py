@@ -31,21 +31,44 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
 # same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
 # reported only while the kernel's sources hash to the ones it was taken on.
-SEQ_TRAFFIC_BYTES = 38576916325
+SEQ_TRAFFIC_BYTES = 46074910720
 SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
-                       "ternary_rank_weight_amd/csrc/device_common.hpp"]
-SEQ_TRAFFIC_SHA = "02e837a922544f93"
+                       "ternary_rank_weight_amd/csrc/device_common.hpp",
+                       "ternary_rank_weight_amd/csrc/exchange.hpp"]
+SEQ_TRAFFIC_SHA = "a864fc9a0c2937bd"
+
+# rocprofv3 counters of the block path on the 2560 x 2560 workload (b = 64),
+# per dispatch of the combined Gram / inverse / contraction launch: MFMA busy
+# cycles over active cycles x SIMDs, bf16 MFMA flops (MOPS x 512), and HBM
+# bytes (FETCH x 2.0, WRITE x 1.0) against the 26.2 MB of R it must read.
+# Reported only while the block sources hash to the ones they were taken on.
+BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0304,
+                  "bf16_mfma_flops": 2.5407e9, "fetch_bytes": 26761216, "write_bytes": 3423877,
+                  "R_bytes": 26214400}
+BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
+                         "ternary_rank_weight_amd/csrc/device_common.hpp"]
+BLOCK_COUNTER_SHA = "c59e54b0d1fc89eb"
+
+
+def _sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def seq_traffic(workload):
-    import hashlib
-    h = hashlib.sha256()
-    for f in SEQ_TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if workload != "llm2560" or h.hexdigest()[:16] != SEQ_TRAFFIC_SHA:
+    if workload != "llm2560" or _sources_sha(SEQ_TRAFFIC_SOURCES) != SEQ_TRAFFIC_SHA:
         return None
     return SEQ_TRAFFIC_BYTES
+
+
+def block_counters(workload, b):
+    if workload != "llm2560" or b != 64 or _sources_sha(BLOCK_COUNTER_SOURCES) != BLOCK_COUNTER_SHA:
+        return None
+    return dict(BLOCK_COUNTERS, source="profiles/block_als_b64_2560x2560.md")
 
 
 def parse():
@@ -570,9 +593,12 @@ def main():
         achieved = alg / (s["ms"] / 1e3) / 1e9
         s["alg_bytes"] = alg
         s["gbps"] = achieved
-        roofline = {"bound": "hbm", "kernel": "k_seq_resident", "achieved": round(achieved, 1),
+        kernel = {0: "streaming kernel chain", 1: "k_seq_resident", 3: "k_seq_persist"}.get(
+            s["stats"]["mode"], "sequential path")
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": seq_traffic(args.workload), "traffic_unit": "bytes per launch",
+                    "traffic": seq_traffic(args.workload) if kernel == "k_seq_resident" else None,
+                    "traffic_unit": "bytes per launch",
                     "alg_bytes_per_launch": alg}
     if "block" in per_mode:
         bm = per_mode["block"]
@@ -580,6 +606,7 @@ def main():
         bm["alg_tflops"] = fl / (bm["ms"] / 1e3) / 1e12
         bm["alg_flops"] = fl
         bm["b"] = b
+        bm["counters"] = block_counters(args.workload, b)
         if roofline is None:
             # block mode alone: its dense contractions on fp32 MFMA
             roofline = {"bound": "mfma", "kernel": "block ALS pipeline",
@@ -653,6 +680,13 @@ def main():
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
+    # explicit teardown before interpreter exit: every launch finished, the
+    # library's outputs and inputs released, torch's cached blocks returned
+    torch.cuda.synchronize()
+    outs.clear()
+    del Ad
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
