@@ -47,7 +47,7 @@ BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0304,
                   "R_bytes": 26214400}
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
                          "ternary_rank_weight_amd/csrc/device_common.hpp"]
-BLOCK_COUNTER_SHA = "c59e54b0d1fc89eb"
+BLOCK_COUNTER_SHA = "9b2f28496bb3ebac"
 
 
 def _sources_sha(files):

@@ -1048,9 +1048,14 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
 //                     after *gram_done has reached gram_target (acquire; a
 //                     bounded wait, counted in stats[TIMEOUTS] if it runs out);
 //   the rest          the contraction, (bx, by) = (c % tiles, c / tiles).
-// Only the inverse waits, and only on workgroups dispatched before it, so the
-// wait always ends.  The roles share one LDS union.  *gram_done counts up over
-// the whole decomposition; the host passes the running target.
+// Only the inverse waits, and no other workgroup waits on anything, so every
+// Gram workgroup runs to completion whatever order the workgroups are
+// dispatched in, and the wait ends.  HIP promises no dispatch order; the
+// Gram tiles have the lowest indices so that, with the in-index-order
+// dispatch of a 1-D grid seen on this hardware, they start first and the
+// inverse waits least.  The wait is bounded as well.  The roles share one
+// LDS union.  *gram_done counts up over the whole decomposition; the host
+// passes the running target.
 constexpr unsigned kGramSpinLimit = 1u << 22;
 
 template <int NSUB>
