@@ -164,22 +164,29 @@ def measure_inference(trw, outs, m, n, reps=20):
                   _random_codes(torch, K, N, gen), torch.randn(K, device="cuda", generator=gen) * 0.01, M, N))
     for name, B2, C2, D, mm, nn in cases:
         x = torch.randn(nn, device="cuda", generator=gen)
-        for _ in range(3):
-            trw.apply(B2, C2, D, mm, nn, x)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            trw.apply(B2, C2, D, mm, nn, x)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
         k = D.numel()
-        alg = 4.0 * k * ((mm + 15) // 16 + (nn + 15) // 16) + 4.0 * (k + mm + nn)
-        gbps = alg / us / 1e3
-        res.append({"workload": name, "us_per_call": round(us, 2), "alg_bytes": alg,
-                    "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)})
+        BT2 = trw.transpose_codes(B2, k, mm)   # B row by row, once per factorisation (not timed)
+        ws = torch.empty(trw.apply_rows_workspace_bytes(mm, nn, k), dtype=torch.uint8, device="cuda")
+        y = torch.empty(mm, dtype=torch.float32, device="cuda")
+        for form, call in (("B component-major, fp32 VALU (externd_apply)",
+                            lambda: trw.apply(B2, C2, D, mm, nn, x)),
+                           ("B row by row, int8 MFMA, caller workspace (externd_apply_rows)",
+                            lambda: trw.apply_rows(BT2, C2, D, mm, nn, x, out=y, workspace=ws))):
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            alg = 4.0 * k * ((mm + 15) // 16 + (nn + 15) // 16) + 4.0 * (k + mm + nn)
+            gbps = alg / us / 1e3
+            res.append({"workload": name, "form": form, "us_per_call": round(us, 2), "alg_bytes": alg,
+                        "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)})
     return res
 
 

@@ -249,6 +249,41 @@ int externd_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D,
 int externd_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m, int64_t n,
                   int64_t k, const float* x, void* stream, float* y);
 
+/* Transpose a 2-bit code matrix (the §2.6 storage: 16 codes per uint32, code
+ * j of a word in bits 2j, 2j+1): src holds `rows` rows of `cols` codes,
+ * ceil(cols/16) words per row; dst receives `cols` rows of `rows` codes,
+ * ceil(rows/16) words per row, zero padding.  externd_transpose_codes(B2, k,
+ * m, ...) turns the component-major B2 of externd_decompose into B row by
+ * row, the form externd_apply_rows reads (once per factorisation).  Device
+ * pointers owned by the caller, dst not overlapping src; enqueued on
+ * `stream`.  EXTERND_EINVAL for a negative size or a null pointer with
+ * nonzero sizes. */
+int externd_transpose_codes(const uint32_t* src, int64_t rows, int64_t cols, void* stream, uint32_t* dst);
+
+/* y = B (diag(D) (C x)) (§2.6) with B given row by row: BT2 holds m rows of
+ * ceil(k/16) words (externd_transpose_codes of B2); C2 and D as produced by
+ * externd_decompose; x has n entries, y receives m.  Both products run on
+ * int8 MFMA: the vector (x, then w = D (C x) in fp32) is rounded to fixed
+ * point with 30 bits below its largest magnitude and split into four int8
+ * digits, every ternary sum is an exact integer, and each output is
+ * converted once.  So the result is the exact one for the rounded vector
+ * (each entry moved by at most 2^-30 of the vector's largest magnitude),
+ * independent of summation order and bit-reproducible.  n, k <= 2^21
+ * (EXTERND_EINVAL beyond).  A non-finite entry of x, D or w makes y all
+ * NaN.  k may be 0 (y = 0).  workspace: NULL, and a workspace of
+ * externd_apply_rows_workspace_bytes(m, n, k) bytes (4 k plus a few KiB) is
+ * allocated and freed stream-ordered; or a caller device buffer, 256-byte
+ * aligned, of at least that many bytes (workspace_bytes), used instead, so
+ * that a loop of calls allocates nothing (EXTERND_EINVAL if too small or
+ * misaligned).  Calls that overlap on one workspace race. */
+int externd_apply_rows(const uint32_t* BT2, const uint32_t* C2, const float* D, int64_t m, int64_t n,
+                       int64_t k, const float* x, void* stream, float* y, void* workspace,
+                       size_t workspace_bytes);
+
+/* Workspace bytes externd_apply_rows needs for this shape on the current
+ * device; 0 for an invalid shape or device. */
+size_t externd_apply_rows_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
 /* k = mu * min(m, n) rounded half away from zero in fp64 (§2.1); -1 on bad input. */
 int64_t externd_rank(int64_t m, int64_t n, float mu);
 

@@ -81,6 +81,9 @@ _decompose_noalloc = _sig("externd_decompose_noalloc", ctypes.c_int,
 _energy = _sig("externd_energy", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i64, _p, _p])
 _reconstruct = _sig("externd_reconstruct", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p])
 _apply = _sig("externd_apply", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p])
+_apply_rows = _sig("externd_apply_rows", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, ctypes.c_size_t])
+_apply_rows_ws = _sig("externd_apply_rows_workspace_bytes", ctypes.c_size_t, [_i64, _i64, _i64])
+_transpose_codes = _sig("externd_transpose_codes", ctypes.c_int, [_p, _i64, _i64, _p, _p])
 _rank = _sig("externd_rank", ctypes.c_int64, [_i64, _i64, _f32])
 _block_width = _sig("externd_block_width", ctypes.c_int32, [_i64, _i64, _i32])
 _resident_fits = _sig("externd_resident_fits", ctypes.c_int32, [_i64, _i64])
@@ -98,7 +101,7 @@ _last_error = _sig("externd_last_error", ctypes.c_char_p, [])
 
 # Every exported symbol of the C ABI, for load checks.
 ABI_SYMBOLS = ("externd_decompose", "externd_decompose_noalloc", "externd_energy", "externd_reconstruct", "externd_apply",
-               "externd_rank",
+               "externd_apply_rows", "externd_apply_rows_workspace_bytes", "externd_transpose_codes", "externd_rank",
                "externd_block_width", "externd_resident_fits", "externd_workspace_bytes",
                "externd_rank_for_energy",
                "externd_ternarize", "externd_project",
@@ -356,6 +359,49 @@ def apply(B2, C2, D, m, n, x):
     y = torch.empty((m,), dtype=torch.float32, device=x.device)
     _check(_apply(_ptr(B2), _ptr(C2), _ptr(D), m, n, k, _ptr(x), _stream(), _ptr(y)))
     return y
+
+
+def transpose_codes(src, rows, cols):
+    """Transpose a 2-bit code matrix: src holds `rows` rows of `cols` codes
+    (ceil(cols/16) int32 words per row); returns `cols` rows of `rows` codes.
+    transpose_codes(B2, k, m) gives B row by row, the form apply_rows reads."""
+    _need(src, torch.int32, "src")
+    if src.numel() != rows * ((cols + 15) // 16):
+        raise ValueError("src must hold rows * ceil(cols/16) words")
+    dst = torch.empty((cols, (rows + 15) // 16), dtype=torch.int32, device=src.device)
+    _check(_transpose_codes(_ptr(src), rows, cols, _stream(), _ptr(dst)))
+    return dst
+
+
+def apply_rows_workspace_bytes(m, n, k):
+    """Device workspace apply_rows needs for this shape (0: invalid)."""
+    return int(_apply_rows_ws(m, n, k))
+
+
+def apply_rows(BT2, C2, D, m, n, x, out=None, workspace=None):
+    """y = B (diag(D) (C x)) (§2.6) with B row by row (BT2 = transpose_codes(B2,
+    k, m)), on int8 MFMA with the vectors in exact fixed point; x: float32 (n,).
+    out: optional float32 (m,) CUDA tensor written and returned; workspace:
+    optional contiguous CUDA tensor of at least apply_rows_workspace_bytes(m,
+    n, k) bytes (256-byte aligned), so that the call allocates nothing."""
+    _need(x, torch.float32, "x")
+    if x.numel() != n:
+        raise ValueError("x must have n entries")
+    k = D.numel()
+    if out is None:
+        out = torch.empty((m,), dtype=torch.float32, device=x.device)
+    else:
+        _need(out, torch.float32, "out")
+        if out.numel() != m:
+            raise ValueError("out must have m entries")
+    wsb = 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+                or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous CUDA tensor")
+        wsb = workspace.numel() * workspace.element_size()
+    _check(_apply_rows(_ptr(BT2), _ptr(C2), _ptr(D), m, n, k, _ptr(x), _stream(), _ptr(out), _ptr(workspace), wsb))
+    return out
 
 
 def ternarize(x, tau):

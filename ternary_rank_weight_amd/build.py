@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libexternd.so")
 SOURCES = ["abi.cpp", "seq_stream.hip", "seq_resident.hip", "factors.hip", "block.hip", "apply.hip",
-           "noalloc.hip", "seq_persist.hip"]
+           "noalloc.hip", "seq_persist.hip", "apply_rows.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -152,6 +152,48 @@ int externd_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_
   return EXTERND_OK;
 }
 
+int externd_transpose_codes(const uint32_t* src, int64_t rows, int64_t cols, void* stream, uint32_t* dst) {
+  if (rows < 0 || cols < 0 || rows > (int64_t(1) << 40) || cols > (int64_t(1) << 40))
+    return fail(EXTERND_EINVAL, "bad shape");
+  if (rows > 0 && cols > 0 && (!src || !dst)) return fail(EXTERND_EINVAL, "null code pointer");
+  int st = check_device(nullptr);
+  if (st != EXTERND_OK) return st;
+  hipError_t e = externd::run_codes_transpose(src, rows, cols, dst, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "transpose_codes");
+  return EXTERND_OK;
+}
+
+size_t externd_apply_rows_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (bad_size(m, n) || k < 0 || !externd::apply_rows_fits(m, n, k)) return 0;
+  int cus = 0;
+  if (check_device(&cus) != EXTERND_OK) return 0;
+  return externd::apply_rows_workspace_bytes(m, k, cus);
+}
+
+int externd_apply_rows(const uint32_t* BT2, const uint32_t* C2, const float* D, int64_t m, int64_t n, int64_t k,
+                       const float* x, void* stream, float* y, void* workspace, size_t workspace_bytes) {
+  if (!x || !y) return fail(EXTERND_EINVAL, "null x or y pointer");
+  if (bad_size(m, n) || k < 0 || !externd::apply_rows_fits(m, n, k))
+    return fail(EXTERND_EINVAL, "bad shape (n and k at most 2^21)");
+  if (k > 0 && (!BT2 || !C2 || !D)) return fail(EXTERND_EINVAL, "null factor pointer");
+  int cus = 0;
+  int st = check_device(&cus);
+  if (st != EXTERND_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = externd::apply_rows_workspace_bytes(m, k, cus);
+  Workspace w;
+  if (workspace) {
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0 || workspace_bytes < need)
+      return fail(EXTERND_EINVAL, "workspace must be 256-byte aligned and at least %zu bytes", need);
+    w.ptr = workspace;
+  } else if ((st = alloc_ws(w, need, s)) != EXTERND_OK) {
+    return st;
+  }
+  hipError_t e = externd::run_apply_rows(BT2, C2, D, m, n, k, x, y, w.ptr, cus, s);
+  if (e != hipSuccess) return hip_fail(e, "apply_rows");
+  return EXTERND_OK;
+}
+
 int64_t externd_rank(int64_t m, int64_t n, float mu) {
   if (m <= 0 || n <= 0 || !std::isfinite(mu) || mu < 0.f) return -1;
   const double v = (double)mu * (double)(m < n ? m : n);

@@ -128,6 +128,13 @@ hipError_t run_energy(const float* A, int64_t m, int64_t n, const uint32_t* B2, 
 hipError_t run_reconstruct(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m,
                            int64_t n, int64_t k, float* out, hipStream_t s);
 
+// inference y = B diag(D) C x with B row by row, on int8 MFMA (apply_rows.hip)
+bool apply_rows_fits(int64_t m, int64_t n, int64_t k);
+size_t apply_rows_workspace_bytes(int64_t m, int64_t k, int num_cus);
+hipError_t run_apply_rows(const uint32_t* BT2, const uint32_t* C2, const float* D, int64_t m, int64_t n, int64_t k,
+                          const float* x, float* y, void* ws, int num_cus, hipStream_t s);
+hipError_t run_codes_transpose(const uint32_t* src, int64_t rows, int64_t cols, uint32_t* dst, hipStream_t s);
+
 // inference y = B diag(D) C x from 2-bit factors (apply.hip)
 size_t apply_workspace_bytes(int64_t m, int64_t k);
 hipError_t run_apply(const uint32_t* B2, const uint32_t* C2, const float* D, int64_t m, int64_t n, int64_t k,
