@@ -17,6 +17,7 @@
 // (§2.2) to each column.  U and V live as 2-bit codes directly in their
 // B2 / C2 output rows.
 #include "device_common.hpp"
+#include "exchange.hpp"
 #include "kernels.hpp"
 #include "projection.hpp"
 
@@ -1038,15 +1039,467 @@ __device__ __forceinline__ void ns_inverse_body(GT* __restrict__ G, int bb, floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// (G + eps I)^-1 of an exact integer Gram, b <= 64, in one workgroup of four
+// waves: Newton-Schulz, X <- X + X R, in which every residual R = I - G'X is
+// computed exactly.  The weighted Gram (not integer) keeps the form above.
+//
+// Layout.  Wave w owns the columns 16 w .. 16 w + 15 of X and of R: lane
+// j + 16 g holds the 16 entries (rho(g, q), 16 w + j), q = 0 .. 15, with
+// rho(g, q) = 16 (q / 4) + 4 g + q % 4 -- the MFMA accumulator layout of the
+// column block's four 16 x 16 tiles.  Every product here is Y[:, w] =
+// A Z[:, w] with Z such a column block, and the contracted index is ordered
+// to suit it: operand slot (lane group g, element e) of chunk c of the
+// 16x16x32 bf16 MFMA stands for k = rho(g, 8 c + e), and slot (g, byte e) of
+// the 16x16x64 int8 MFMA for k = rho(g, e).  (Both MFMAs give the same
+// (lane group, element) to the same k in A and in B, so any such order
+// gives the full sum.)  The B operand is then the wave's own registers,
+// unmoved, and the result lands in the same layout.  The A operand entry of
+// output tile row I is A[16 I + i][rho(g, .)], which for a symmetric A is
+// exactly what lane i + 16 g of wave I holds: G is symmetric, and so is X up
+// to rounding (the exact iteration keeps symmetry; a perturbation of X only
+// changes the iterate, and the residual is always that of the X held).
+//
+// Exact residual.  |G_ij| <= L, the length of the contracted dimension
+// (below 2^23 here).  Per column, X is rounded to fixed point, Xq =
+// rint(X 2^s) with |Xq| < 2^30, which is X up to 2^-31 of the column's
+// largest entry (finer than fp32 keeps it); with L > 32639 the grid is 2^22
+// (within 2^-23).  G's balanced base-256 digits (two; three when L > 32639)
+// and Xq's (four; three) are multiplied on int8 MFMA, each int32 sum below
+// 3 * 64 * 128^2, and the digit products of one weight 256^d are
+// accumulated together.  Their recombination is an integer below 2^52,
+// formed in fp64 without rounding, so R = I - (G Xq + eps Xq) 2^-s carries
+// only the rounding of that last step.  (On a nearly singular G' no fp32 X
+// reaches a small residual: the iterate with the smallest one is returned
+// and the inverse is counted as unconverged.)
+//
+// A step: X rounded and the three bf16 parts of X written to LDS (two
+// buffers); R from registers alone; the partials of ||R||_F^2 to LDS; one
+// barrier; then, unless the iteration stops, X <- X + X R on bf16 MFMA with
+// both operands in three exact parts (A = the parts of X from LDS, B = the
+// parts of R in registers).  Stopping rule: ||R||_F < 1e-6 accepts X as it
+// is; ||R||_F < 1e-3 takes one more step (residual about ||R||_F^2) and
+// accepts.  Starts: the previous inverse of the same side when its residual
+// is below 1, else the Jacobi guess diag(G')^-1, else I / ||G'||_inf (the
+// last converges for any SPD matrix); a residual that grows restarts.
+// ---------------------------------------------------------------------------
+typedef int i4v __attribute__((ext_vector_type(4)));
+// Gram entries below this bound have three balanced base-256 digits; longer
+// contractions use the fp32 iteration with the fp64 refinement above.
+constexpr int64_t kNsxMaxL = 1 << 23;
+
+constexpr int kGlPad = 68;   // row stride of the Gram in LDS: the accesses below are conflict-free
+// the ten 16 x 16 tiles (I, J), I <= J, of a symmetric 64 x 64 Gram
+constexpr int kTileI[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
+constexpr int kTileJ[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+struct NsxShared {
+  union {   // G is read into registers before X's parts are first written (two barriers apart)
+    u32x4 xp[2][kCT / kWave][3][2][kWave];   // [buffer][wave][part][chunk][lane]: the parts of X
+    int gl[64 * kGlPad];                     // G, summed over the waves' quarters of the codes
+  };
+  i4v ga[kCT / kWave][3][kWave];           // [tile row][digit][lane]: G's digits, the A operand
+  float xbest[kCT / kWave][16][kWave];     // the iterate with the smallest residual so far
+  double red[2][kCT / kWave];              // per-wave partials of ||R||_F^2
+};
+
+__device__ inline int nsx_row(int g, int q) { return 16 * (q >> 2) + 4 * g + (q & 3); }
+
+// out[d] = byte d of a0, a1, a2, a3 (in that order): a 4 x 4 byte transpose.
+__device__ inline void bytes_transpose4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// The int8 operands of 16 integers of magnitude at most 0x7F7F7F7F: d[a]
+// holds their balanced base-256 digit a (value = sum_a 256^a d_a, each d_a in
+// [-128, 127]), byte q of the 16 for value q.  Adding 0x80808080 makes every
+// digit plus 128 a plain byte; the xor takes the 128 off again.
+template <int ND>
+__device__ inline void digits(const int (&v)[16], i4v (&d)[ND]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t o[4];
+    bytes_transpose4(((uint32_t)v[4 * r] + 0x80808080u) ^ 0x80808080u,
+                     ((uint32_t)v[4 * r + 1] + 0x80808080u) ^ 0x80808080u,
+                     ((uint32_t)v[4 * r + 2] + 0x80808080u) ^ 0x80808080u,
+                     ((uint32_t)v[4 * r + 3] + 0x80808080u) ^ 0x80808080u, o);
+#pragma unroll
+    for (int a = 0; a < ND; ++a) d[a][r] = (int)o[a];
+  }
+}
+
+__device__ inline i4v mfma_i8(i4v a, i4v b, i4v c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+
+// Eight consecutive values (8 c .. 8 c + 7) of a lane's 16 as the three bf16
+// parts of a 16x16x32 operand chunk.
+__device__ inline void nsx_parts(const float (&x)[16], int c, u32x4 (&p)[3]) {
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ns_split3(x[8 * c + e], h[e], m[e], l[e]);
+  p[0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  p[1] = u32x4{m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16)};
+  p[2] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+}
+
+// The 2-bit codes of a word as the int8 operand: byte 4 q + b holds code
+// 4 b + q of the word (the same order in A and B, so the products pair up).
+__device__ inline i4v nsx_unpack(uint32_t w) {
+  constexpr uint32_t kLut = 0xFF000100u;   // code 0 -> 0, 1 -> +1, 2 -> 0, 3 -> -1
+  i4v r;
+  r.x = (int)__builtin_amdgcn_perm(0u, kLut, w & 0x03030303u);
+  r.y = (int)__builtin_amdgcn_perm(0u, kLut, (w >> 2) & 0x03030303u);
+  r.z = (int)__builtin_amdgcn_perm(0u, kLut, (w >> 4) & 0x03030303u);
+  r.w = (int)__builtin_amdgcn_perm(0u, kLut, (w >> 6) & 0x03030303u);
+  return r;
+}
+
+// The Gram blocks [b0, b1) of four code words (see nsx_inverse_body): lane
+// i + 16 g reads block b0 + g, b0 + g + 4, ... of the components 16 I + i.
+// All loads of a batch are issued unconditionally from clamped addresses and
+// only masked where they are used, so they are in flight together.
+template <bool VEC>
+__device__ __forceinline__ void nsx_gram_accumulate(const uint32_t* __restrict__ codes, int64_t wl, int bb,
+                                                    int64_t b0, int64_t b1, int j, int g, i4v (&acc)[10]) {
+  const uint32_t* src[4];
+  bool has[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    has[I] = 16 * I + j < bb;
+    src[I] = codes + (int64_t)(has[I] ? 16 * I + j : 0) * wl;
+  }
+  constexpr int kGS = 4;   // rounds of four blocks per batch
+  for (int64_t sb = b0; sb < b1; sb += 4 * kGS) {
+    uint32_t cw[kGS][4][4];   // [round group][I][word]
+#pragma unroll
+    for (int st = 0; st < kGS; ++st) {
+      const int64_t kb = sb + 4 * st + g;
+      const int64_t kc = kb < b1 ? kb : b0;   // a block of the wave's range
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        if constexpr (VEC) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src[I] + 4 * kc);
+          cw[st][I][0] = v.x;
+          cw[st][I][1] = v.y;
+          cw[st][I][2] = v.z;
+          cw[st][I][3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t wd = 4 * kc + e;
+            cw[st][I][e] = src[I][wd < wl ? wd : wl - 1];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < kGS; ++st) {
+      if (sb + 4 * st < b1) {   // wave-uniform
+        const int64_t kb = sb + 4 * st + g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool okw = kb < b1 && 4 * kb + e < wl;
+          i4v u[4];
+#pragma unroll
+          for (int I = 0; I < 4; ++I) u[I] = nsx_unpack(okw && has[I] ? cw[st][I][e] : 0u);
+#pragma unroll
+          for (int tt = 0; tt < 10; ++tt) acc[tt] = mfma_i8(u[kTileI[tt]], u[kTileJ[tt]], acc[tt]);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ codes, int64_t wl, int bb, int64_t L,
+                                                 float* __restrict__ X, int* __restrict__ warm_flag,
+                                                 long long* __restrict__ stats, NsxShared& sh) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
+  const int j = lane & 15, g = lane >> 4;
+  const int col = 16 * w + j;
+  const bool three = L > 32639;
+  // the previous inverse, read now (from clamped addresses) and taken below
+  // when it is the warm start: its loads fly with the Gram's
+  const int warm = *warm_flag;
+  float xv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r = nsx_row(g, q);
+    xv[q] = X[min(r, bb - 1) * bb + min(col, bb - 1)];
+  }
+  // ---- G = C^T C of the bb code rows (components), exact, on int8 MFMA ----
+  // The code words are taken in blocks of four (64 entries); wave w takes a
+  // quarter of the blocks, lane group g the blocks g, g + 4, ... of it.  Lane
+  // i + 16 g reads the block of components 16 I + i (I = 0 .. 3) with one
+  // 16-byte load each, and word e of it is the lane's operand slot in MFMA
+  // round e: A of tile row I and B of tile column I at once.  Every round
+  // pairs, in every slot, the same code row of the two components, so the
+  // rounds sum G over all rows.  The ten tiles I <= J are accumulated and
+  // added, mirrored, into the LDS Gram (codes beyond bb are zero, so are
+  // their rows and columns).
+  for (int e = t; e < 64 * kGlPad; e += kCT) sh.gl[e] = 0;
+  {
+    const int64_t nblk = (wl + 3) / 4;
+    const int64_t b0 = nblk * w / 4, b1 = nblk * (w + 1) / 4;
+    // 16-byte loads when every block is aligned and whole, else word loads
+    const bool vec = ((reinterpret_cast<uintptr_t>(codes) & 15) == 0) && ((wl & 3) == 0);
+    i4v acc[10];
+#pragma unroll
+    for (int u = 0; u < 10; ++u) acc[u] = i4v{0, 0, 0, 0};
+    if (vec) nsx_gram_accumulate<true>(codes, wl, bb, b0, b1, j, g, acc);
+    else nsx_gram_accumulate<false>(codes, wl, bb, b0, b1, j, g, acc);
+    __syncthreads();   // the LDS Gram is zero
+#pragma unroll
+    for (int tt = 0; tt < 10; ++tt) {
+      const int I = kTileI[tt], J = kTileJ[tt];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * I + 4 * g + v, c = 16 * J + j;   // entry (r, c) of tile (I, J)
+        atomicAdd(&sh.gl[r * kGlPad + c], acc[tt][v]);
+        if (I != J) atomicAdd(&sh.gl[c * kGlPad + r], acc[tt][v]);
+      }
+    }
+    __syncthreads();   // G complete
+  }
+  // Wave w takes column block w of G (row block w by symmetry): entries
+  // (rho(g, q), 16 w + j), the identity beyond bb.  It leaves their digits in
+  // LDS as the A operand of tile row w, with its part of the trace, of
+  // ||G'||_inf, and the diagonal entry G_cc this lane's column meets
+  // (q = 4 w + j % 4 when g = j / 4).
+  const int r0 = col;
+  int gv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) gv[q] = sh.gl[nsx_row(g, q) * kGlPad + col];
+  double trp = 0.0, rsum = 0.0, gdiag = 1.0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int c = nsx_row(g, q);
+    if (c == r0) {
+      if (r0 >= bb) gv[q] = 1;
+      else trp += (double)gv[q];
+      gdiag = (double)gv[q];   // held by the lane with g = j / 4 only
+    }
+    rsum += fabs((double)gv[q]);
+  }
+  {
+    i4v d[3];
+    digits<3>(gv, d);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) sh.ga[w][a][lane] = d[a];
+  }
+  trp = wave_sum_to63(trp);
+  rsum += __shfl_xor(rsum, 16);
+  rsum += __shfl_xor(rsum, 32);
+  // the largest row sum of the wave's rows (eps is added below, to each row < bb)
+  double rmax = rsum;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) rmax = fmax(rmax, __shfl_xor(rmax, o));
+  if (lane == kWave - 1) {
+    sh.red[0][w] = trp;
+    sh.red[1][w] = rmax;
+  }
+  __syncthreads();   // digits, trace and row-sum partials visible
+  const double tr = (sh.red[0][0] + sh.red[0][1]) + (sh.red[0][2] + sh.red[0][3]);
+  const double eps64 = 1e-6 * tr / bb;
+  // ||G'||_inf: every row sum gains eps at most (rows below bb), an upper
+  // bound is all the scaled start needs
+  const double rmax_all = fmax(fmax(sh.red[1][0], sh.red[1][1]), fmax(sh.red[1][2], sh.red[1][3])) + eps64;
+  if (col < bb) gdiag += eps64;
+  const float alpha = (float)(1.0 / rmax_all);
+  auto init_jacobi = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] = nsx_row(g, q) == col ? (float)(1.0 / gdiag) : 0.f;
+  };
+  auto init_scaled = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] = nsx_row(g, q) == col ? alpha : 0.f;
+  };
+  if (warm) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = nsx_row(g, q);
+      if (!(r < bb && col < bb)) xv[q] = r == col ? 1.f : 0.f;
+    }
+  } else {
+    init_jacobi();
+  }
+  __syncthreads();   // red[] is reused by the iteration
+  int start = warm ? 0 : 1;   // 0 warm, 1 Jacobi, 2 scaled identity
+  double prev = 1e300, best = 1e300;
+  bool conv = false, restarted = false;
+  int evals = 0, since_start = 0, buf = 0;
+  for (int it = 0; it < 40; ++it) {
+    ++evals;
+    // the lane's indices again, opaque: the per-entry masks built from them
+    // stay in the step instead of being held (or spilled) across the loop
+    const int to = xchg::opaque_tid();
+    const int lane = to & (kWave - 1), w = to / kWave;
+    const int g = lane >> 4, col = 16 * w + (lane & 15);
+    // ---- X to fixed point per column: Xq = rint(X 2^s), |Xq| < 2^30 (2^22
+    // with three digits of G); X itself stays as it is ----
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, fabsf(xv[q]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool okx = mx > 0.f && mx < 3.0e38f;   // false for inf and NaN too
+    const int s = okx ? (three ? 21 : 29) - ilogbf(mx) : 0;
+    int xq[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xq[q] = okx ? __float2int_rn(ldexpf(xv[q], s)) : 0;
+    i4v xd[4];
+    digits<4>(xq, xd);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 p[3];
+      nsx_parts(xv, c, p);
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) sh.xp[buf][w][pp][c][lane] = p[pp];
+    }
+    // ---- R = I - (G Xq + eps Xq) 2^-s, exact up to the final rounding ----
+    const double sc = ldexp(1.0, -s);
+    double rp = okx ? 0.0 : __builtin_nan("");
+    float rf[16];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      i4v acc[5], ga[3];
+#pragma unroll
+      for (int d = 0; d < 5; ++d) acc[d] = i4v{0, 0, 0, 0};
+#pragma unroll
+      for (int a = 0; a < 3; ++a) ga[a] = sh.ga[I][a][lane];
+      // digit products of weight 256^d into acc[d]: two digits of G by
+      // four of Xq, or three by three
+      // (ordered so that products into one accumulator are four apart)
+      acc[0] = mfma_i8(ga[0], xd[0], acc[0]);
+      acc[1] = mfma_i8(ga[0], xd[1], acc[1]);
+      acc[2] = mfma_i8(ga[0], xd[2], acc[2]);
+      if (three) {
+        acc[3] = mfma_i8(ga[1], xd[2], acc[3]);
+        acc[4] = mfma_i8(ga[2], xd[2], acc[4]);
+        acc[1] = mfma_i8(ga[1], xd[0], acc[1]);
+        acc[2] = mfma_i8(ga[1], xd[1], acc[2]);
+        acc[3] = mfma_i8(ga[2], xd[1], acc[3]);
+        acc[2] = mfma_i8(ga[2], xd[0], acc[2]);
+      } else {
+        acc[3] = mfma_i8(ga[0], xd[3], acc[3]);
+        acc[4] = mfma_i8(ga[1], xd[3], acc[4]);
+        acc[1] = mfma_i8(ga[1], xd[0], acc[1]);
+        acc[2] = mfma_i8(ga[1], xd[1], acc[2]);
+        acc[3] = mfma_i8(ga[1], xd[2], acc[3]);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = 4 * I + v, r = nsx_row(g, q);
+        const int lo = acc[0][v] + (int)((uint32_t)acc[1][v] << 8);
+        const int hi = acc[2][v] + (int)((uint32_t)acc[3][v] << 8);
+        double T = fma((double)hi, 65536.0, (double)lo);
+        T = fma((double)acc[4][v], 4294967296.0, T);
+        const double gx = fma(r < bb ? eps64 : 0.0, (double)xq[q], T) * sc;
+        const double rv = (r == col ? 1.0 : 0.0) - gx;
+        rp = fma(rv, rv, rp);
+        rf[q] = (float)rv;
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one tile row at a time: bounded registers
+    }
+    rp = wave_sum_to63(rp);
+    if (lane == kWave - 1) sh.red[buf][w] = rp;
+    __syncthreads();   // the parts of X and the norm partials are visible
+    const double rn2 = (sh.red[buf][0] + sh.red[buf][1]) + (sh.red[buf][2] + sh.red[buf][3]);
+    if (rn2 < best) {   // kept for an iteration that does not converge
+      best = rn2;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sh.xbest[w][q][lane] = xv[q];
+    }
+    if (rn2 < 1e-12) {   // ||R||_F < 1e-6: X as it is
+      conv = true;
+      break;
+    }
+    const bool bad = !(rn2 < 1e30) || (start == 0 && since_start == 0 && rn2 >= 1.0) ||
+                     (start < 2 && since_start > 0 && rn2 > prev);
+    if (bad) {
+      if (start == 2) break;   // not finite from the scaled identity: give up
+      restarted = true;        // poor warm start: Jacobi; diverging Jacobi: scaled identity
+      if (start == 0) init_jacobi();
+      else init_scaled();
+      ++start;
+      since_start = 0;
+      prev = 1e300;
+      buf ^= 1;
+      continue;
+    }
+    ++since_start;
+    prev = rn2;
+    const bool last = rn2 < 1e-6;   // ||R||_F < 1e-3: one more step, then accept
+    // ---- X <- X + X R ----
+    u32x4 rb[2][3];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) nsx_parts(rf, c, rb[c]);
+    // the four tile rows' accumulators take turns, so consecutive MFMAs are
+    // independent; the products of ns_mfma6 grouped by the part of X
+    f4 y[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) y[I] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 b[3];
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) b[pp] = __builtin_bit_cast(bf16x8, rb[c][pp]);
+#pragma unroll
+      for (int pa = 0; pa < 3; ++pa) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) a[I] = __builtin_bit_cast(bf16x8, sh.xp[buf][I][pa][c][lane]);
+#pragma unroll
+        for (int pb = 0; pb < 3 - pa; ++pb)   // parts pa + pb <= 2: down to 2^-16
+#pragma unroll
+          for (int I = 0; I < 4; ++I) y[I] = mfma16x16x32bf16(a[I], b[pb], y[I]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] += y[q >> 2][q & 3];
+    buf ^= 1;
+    if (last) {
+      conv = true;
+      break;
+    }
+  }
+  if (!conv) {   // the best iterate met (each lane reads back its own entries)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xv[q] = sh.xbest[w][q][lane];
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r = nsx_row(g, q);
+    if (r < bb && col < bb) X[r * bb + col] = xv[q];
+  }
+  if (t == 0) {
+    *warm_flag = 1;
+    if (!conv) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_INVERSE_UNCONVERGED), 1ull);
+    atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_ITERATIONS), (unsigned long long)evals);
+    if (restarted) atomicAdd(reinterpret_cast<unsigned long long*>(stats + EXTERND_STAT_NS_RESTARTS), 1ull);
+  }
+}
+
 // One launch per half-step (1-D grid, roles by block index, in dispatch
 // order):
 //   [0, ngram)        Gram tiles: (tile, split) of the exact Gram of the codes,
 //                     added into G with atomics; each then bumps *gram_done
-//                     (release);
-//   ngram             the inverse of G' (weighted: G given): Newton-Schulz up
-//                     to b = 64, the fp64 MFMA block sweep beyond,
-//                     after *gram_done has reached gram_target (acquire; a
-//                     bounded wait, counted in stats[TIMEOUTS] if it runs out);
+//                     (release).  Only for b > 64 and for contractions of
+//                     2^23 and more: up to b = 64 the inverse workgroup forms
+//                     the Gram itself and ngram is 0;
+//   ngram             the inverse of G' (weighted: G given): the exact-residual
+//                     Newton-Schulz up to b = 64 (the fp32 one with the fp64
+//                     refinement for a weighted Gram or a contraction of 2^23
+//                     and more), the fp64 MFMA block sweep beyond; with Gram
+//                     tiles, after *gram_done has reached gram_target
+//                     (acquire; a bounded wait, counted in stats[TIMEOUTS] if
+//                     it runs out);
 //   the rest          the contraction, (bx, by) = (c % tiles, c / tiles).
 // Only the inverse waits, and no other workgroup waits on anything, so every
 // Gram workgroup runs to completion whatever order the workgroups are
@@ -1061,6 +1514,7 @@ constexpr unsigned kGramSpinLimit = 1u << 22;
 template <int NSUB>
 union HalfStepLds {
   NsShared ns;
+  NsxShared nsx;
   TernStage<NSUB> cs;
   uint32_t rows[32][kGramChunk + 1];
 };
@@ -1109,6 +1563,7 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
       else spd_inverse_body<8, int>(static_cast<int*>(G), bb, Ginv, warm_flag);
     } else {
       if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats, lds.ns);
+      else if ((UT ? m : n) < kNsxMaxL) nsx_inverse_body(codes, wl, bb, UT ? m : n, Ginv, warm_flag, stats, lds.nsx);
       else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats, lds.ns);
     }
     return;
@@ -1987,6 +2442,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
     const int gw = gram_words(bb);
     const dim3 gram_u((unsigned)(nt * (nt + 1) / 2), (unsigned)((wm + gw - 1) / gw));
     const dim3 gram_v((unsigned)(nt * (nt + 1) / 2), (unsigned)((wn + gw - 1) / gw));
+    const bool own_gu = bb <= 64 && m < kNsxMaxL, own_gv = bb <= 64 && n < kNsxMaxL;
     hipError_t ce = hipSuccess;
     auto cap_copy = [&](const void* src, void* dst, int64_t words) {   // 4-byte words
       if (dst && ce == hipSuccess)
@@ -2001,8 +2457,10 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
       // workgroups of the contraction launch, concurrently with it
       // (Newton-Schulz up to b = 64, the fp64 sweep beyond).
       {
-        // the Gram of U is computed inside the launch, ahead of its inverse
-        const int ng = (int)(gram_u.x * gram_u.y);
+        // the Gram of U is computed inside the launch, ahead of its inverse:
+        // by the inverse workgroup itself up to b = 64 (contractions shorter
+        // than 2^23), else by Gram workgroups
+        const int ng = own_gu ? 0 : (int)(gram_u.x * gram_u.y);
         gram_issued[0] += (unsigned long long)ng;
         launch_combined<true, false>(bb, (int)((n + 63) / 64), L.S1, ng, (int)gram_u.y, s, R, m, n, Uc, wm, L.rows_split, Pt_part, (void*)GU, GinvU, bb <= 64 ? warm : fail, st, (const float*)nullptr, gram_done, gram_issued[0]);
       }
@@ -2020,7 +2478,7 @@ hipError_t run_block(const BlockArgs& a, void* ws, hipStream_t s) {
         hipLaunchKernelGGL(k_gram_w_reduce, dim3((unsigned)((bb * bb + 255) / 256)), dim3(256), 0, s, Gwpart, wsplits, bb, GVw);
         launch_combined<false, true>(bb, (int)((m + 63) / 64), L.S2, 0, 1, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GVw, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)wt, gram_done + 1, 0ull);
       } else {
-        const int ng = (int)(gram_v.x * gram_v.y);
+        const int ng = own_gv ? 0 : (int)(gram_v.x * gram_v.y);
         gram_issued[1] += (unsigned long long)ng;
         launch_combined<false, false>(bb, (int)((m + 63) / 64), L.S2, ng, (int)gram_v.y, s, R, m, n, Vc, wn, L.cols_split, Qt_part, (void*)GV, GinvV, bb <= 64 ? warm + 1 : fail, st, (const float*)nullptr, gram_done + 1, gram_issued[1]);
       }
