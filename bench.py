@@ -39,15 +39,17 @@ SEQ_TRAFFIC_SHA = "a864fc9a0c2937bd"
 
 # rocprofv3 counters of the block path on the 2560 x 2560 workload (b = 64),
 # per dispatch of the combined Gram / inverse / contraction launch: MFMA busy
-# cycles over active cycles x SIMDs, bf16 MFMA flops (MOPS x 512), and HBM
+# cycles over active cycles x SIMDs, bf16 MFMA flops and int8 MFMA operations
+# (MOPS x 512), and HBM
 # bytes (FETCH x 2.0, WRITE x 1.0) against the 26.2 MB of R it must read.
 # Reported only while the block sources hash to the ones they were taken on.
-BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0304,
-                  "bf16_mfma_flops": 2.5407e9, "fetch_bytes": 26761216, "write_bytes": 3423877,
-                  "R_bytes": 26214400}
+BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0371,
+                  "bf16_mfma_flops": 2.5277e9, "int8_mfma_ops": 3.146e7, "fetch_bytes": 26733445,
+                  "write_bytes": 3293251, "R_bytes": 26214400}
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
-                         "ternary_rank_weight_amd/csrc/device_common.hpp"]
-BLOCK_COUNTER_SHA = "9b2f28496bb3ebac"
+                         "ternary_rank_weight_amd/csrc/device_common.hpp",
+                         "ternary_rank_weight_amd/csrc/exchange.hpp"]
+BLOCK_COUNTER_SHA = "e90f553ac3a08b4a"
 
 
 def _sources_sha(files):

@@ -1404,7 +1404,6 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
         rp = fma(rv, rv, rp);
         rf[q] = (float)rv;
       }
-      __builtin_amdgcn_sched_barrier(0);   // one tile row at a time: bounded registers
     }
     rp = wave_sum_to63(rp);
     if (lane == kWave - 1) sh.red[buf][w] = rp;
@@ -1458,7 +1457,6 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
         for (int pb = 0; pb < 3 - pa; ++pb)   // parts pa + pb <= 2: down to 2^-16
 #pragma unroll
           for (int I = 0; I < 4; ++I) y[I] = mfma16x16x32bf16(a[I], b[pb], y[I]);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
