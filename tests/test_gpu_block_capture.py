@@ -123,3 +123,12 @@ def test_block_capture_importance_weighted(lib, b):
     A = synthetic.llm_like(1100, 1024, 6)
     h = synthetic.importance(1024, 6)
     _check_block(lib, A, 0.5, 0.7, b, 2, 5, 15, 1, h=h, lam=0.01)
+
+
+def test_block_capture_tall_three_digit_gram(lib):
+    # m = 33001 > 32639: the U-side Gram's entries need three base-256 digits
+    # in the exact-residual inverse (b <= 64), and 2063 code words per row
+    # (not a multiple of four) take the Gram's word loads; the V side (n = 256)
+    # has two digits.
+    A = synthetic.gaussian(33001, 256, 21)
+    _check_block(lib, A, 0.3, 0.7, 32, 1, 3, 15, 4)
