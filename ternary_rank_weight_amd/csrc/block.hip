@@ -9,9 +9,10 @@
 //   solve [(U^T U) o (V^T V)] d = diag(U^T R V)   (diag read off the last Q)
 //   R <- R - U diag(d) V^T           (MFMA rank-b update)
 // The Gram matrices of ternary factors are exact integers (popcounts of the
-// 2-bit codes).  The regularised Gram inverse is exact fp64 for b > 64 and
-// fp32-accurate Newton-Schulz to 1e-4 below (bf16 MFMA, split operands);
-// the joint scale solve is fp64.  The
+// 2-bit codes, or int8 MFMA on the unpacked codes).  The regularised Gram
+// inverse is exact fp64 for b > 64; below, Newton-Schulz whose residuals are
+// exact (int8 MFMA on base-256 digits) is run to ||I - G'X||_F of about
+// 1e-6 (bf16 MFMA updates, split operands); the joint scale solve is fp64.  The
 // contractions and the deflation are fp32-accurate (exact products, fp32
 // sums) on bf16 MFMA.  T_col applies the mean-threshold ternarizer T_tau
 // (§2.2) to each column.  U and V live as 2-bit codes directly in their
@@ -604,9 +605,12 @@ __device__ __forceinline__ void contract_r_v_body(const float* __restrict__ R, i
 
 
 // ---------------------------------------------------------------------------
-// Decorrelation inverse for b <= 64: X = (G + eps I)^-1, eps = 1e-6 trace(G)/b,
+// Decorrelation inverse for a weighted Gram (b <= 64), and for an integer one
+// whose contraction is 2^23 long or more (the exact-residual form below
+// covers every other b <= 64): X = (G + eps I)^-1, eps = 1e-6 trace(G)/b,
 // by the Newton-Schulz iteration  R = I - G'X,  X <- X + X R  on bf16 MFMA in
-// one workgroup (256 threads; wave w owns the 16-row tile band w).  Since
+// one workgroup (256 threads; wave w owns the 16-row tile band w), followed
+// by one fp64 refinement.  Since
 // R_{k+1} = R_k^2, the Frobenius norm of R squares each step while it is
 // below 1.  The start is the previous inverse of the same side (consecutive
 // ALS iterations change the codes little), else the Jacobi guess
