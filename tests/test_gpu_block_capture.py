@@ -132,3 +132,11 @@ def test_block_capture_tall_three_digit_gram(lib):
     # has two digits.
     A = synthetic.gaussian(33001, 256, 21)
     _check_block(lib, A, 0.3, 0.7, 32, 1, 3, 15, 4)
+
+
+def test_block_capture_contraction_of_2_23_rows(lib):
+    # m = 2^23: the U-side Gram's entries could need a fourth base-256 digit,
+    # so that side takes the Gram workgroups and the fp32 Newton-Schulz with
+    # the fp64 refinement; the V side (n = 16) the exact-residual form.
+    A = synthetic.gaussian(1 << 23, 16, 22)
+    _check_block(lib, A, 0.5, 0.7, 2, 1, 3, 15, 5)
