@@ -49,7 +49,7 @@ BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0371,
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
                          "ternary_rank_weight_amd/csrc/device_common.hpp",
                          "ternary_rank_weight_amd/csrc/exchange.hpp"]
-BLOCK_COUNTER_SHA = "82e11a6ecd51f6f0"
+BLOCK_COUNTER_SHA = "2f228092b543069c"
 
 
 def _sources_sha(files):

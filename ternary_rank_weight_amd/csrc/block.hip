@@ -1275,7 +1275,6 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
   // LDS as the A operand of tile row w, with its part of the trace, of
   // ||G'||_inf, and the diagonal entry G_cc this lane's column meets
   // (q = 4 w + j % 4 when g = j / 4).
-  const int r0 = col;
   int gv[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) gv[q] = sh.gl[nsx_row(g, q) * kGlPad + col];
@@ -1283,8 +1282,8 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int c = nsx_row(g, q);
-    if (c == r0) {
-      if (r0 >= bb) gv[q] = 1;
+    if (c == col) {
+      if (col >= bb) gv[q] = 1;
       else trp += (double)gv[q];
       gdiag = (double)gv[q];   // held by the lane with g = j / 4 only
     }
