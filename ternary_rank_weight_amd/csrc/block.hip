@@ -1219,14 +1219,17 @@ __device__ __forceinline__ void nsx_gram_accumulate(const uint32_t* __restrict__
   }
 }
 
-__device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ codes, int64_t wl, int bb, int64_t L,
+// THREE: the contraction is longer than 32639 (G's entries take three
+// digits); a template parameter, so that no branch splits the step's tile
+// rows into separate basic blocks.
+template <bool THREE>
+__device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ codes, int64_t wl, int bb,
                                                  float* __restrict__ X, int* __restrict__ warm_flag,
                                                  long long* __restrict__ stats, NsxShared& sh) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
   const int j = lane & 15, g = lane >> 4;
   const int col = 16 * w + j;
-  const bool three = L > 32639;
   // the previous inverse, read now (from clamped addresses) and taken below
   // when it is the warm start: its loads fly with the Gram's
   const int warm = *warm_flag;
@@ -1351,7 +1354,7 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool okx = mx > 0.f && mx < 3.0e38f;   // false for inf and NaN too
-    const int s = okx ? (three ? 21 : 29) - ilogbf(mx) : 0;
+    const int s = okx ? (THREE ? 21 : 29) - ilogbf(mx) : 0;
     int xq[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) xq[q] = okx ? __float2int_rn(ldexpf(xv[q], s)) : 0;
@@ -1381,7 +1384,7 @@ __device__ __forceinline__ void nsx_inverse_body(const uint32_t* __restrict__ co
       acc[0] = mfma_i8(ga[0], xd[0], acc[0]);
       acc[1] = mfma_i8(ga[0], xd[1], acc[1]);
       acc[2] = mfma_i8(ga[0], xd[2], acc[2]);
-      if (three) {
+      if constexpr (THREE) {
         acc[3] = mfma_i8(ga[1], xd[2], acc[3]);
         acc[4] = mfma_i8(ga[2], xd[2], acc[4]);
         acc[1] = mfma_i8(ga[1], xd[0], acc[1]);
@@ -1564,7 +1567,8 @@ __global__ __launch_bounds__(kCT) __attribute__((amdgpu_waves_per_eu(2))) void k
       else spd_inverse_body<8, int>(static_cast<int*>(G), bb, Ginv, warm_flag);
     } else {
       if constexpr (W) ns_inverse_body(static_cast<double*>(G), bb, Ginv, warm_flag, stats, lds.ns);
-      else if ((UT ? m : n) < kNsxMaxL) nsx_inverse_body(codes, wl, bb, UT ? m : n, Ginv, warm_flag, stats, lds.nsx);
+      else if ((UT ? m : n) > 32639 && (UT ? m : n) < kNsxMaxL) nsx_inverse_body<true>(codes, wl, bb, Ginv, warm_flag, stats, lds.nsx);
+      else if ((UT ? m : n) < kNsxMaxL) nsx_inverse_body<false>(codes, wl, bb, Ginv, warm_flag, stats, lds.nsx);
       else ns_inverse_body(static_cast<int*>(G), bb, Ginv, warm_flag, stats, lds.ns);
     }
     return;
