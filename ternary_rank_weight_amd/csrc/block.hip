@@ -1597,6 +1597,24 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
   const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kDecW;
   const int kb4 = (bb + 3) & ~3;
+  const int lane = t & 63, w = t >> 6;
+  const int j = lane & 15, k = lane >> 4;
+  const int rt = (bb + 15) / 16;
+  // With 64 rows each wave needs one row tile of the inverse (16 values per
+  // lane): its loads are issued here, with the split partials', so that the
+  // two first reads of data the previous launch wrote overlap.  (With 128
+  // rows, 32 values per lane for each of two row tiles: loaded below.)
+  float av0[16];
+  if constexpr (kRows == 64) {
+    const int row = 16 * w + j;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int kk = 4 * q + k;
+      const bool ok = kk < bb && row < bb && w < rt;
+      const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
+      av0[q] = ok ? a : 0.f;
+    }
+  }
   // the split sums, in split order: every entry of this thread (E of them)
   // loads QB splits before any is added
   constexpr int E = kRows * kDecW / 256;
@@ -1633,9 +1651,6 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
     if (sum_out && kk < bb && c < L) sum_out[(int64_t)kk * L + c] = acc_s[u];
   }
   __syncthreads();
-  const int lane = t & 63, w = t >> 6;
-  const int j = lane & 15, k = lane >> 4;
-  const int rt = (bb + 15) / 16;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int I = w + 4 * r;
@@ -1647,12 +1662,17 @@ __global__ __launch_bounds__(256) void k_decorrelate(const float* __restrict__ P
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
     // every A operand of the row tile first (at most kRows / 4 per lane)
     float av[kRows / 4];
+    if constexpr (kRows == 64) {
 #pragma unroll
-    for (int q = 0; q < kRows / 4; ++q) {
-      const int kk = 4 * q + k;
-      const bool ok = kk < bb && row < bb;
-      const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
-      av[q] = ok ? a : 0.f;
+      for (int q = 0; q < 16; ++q) av[q] = av0[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < kRows / 4; ++q) {
+        const int kk = 4 * q + k;
+        const bool ok = kk < bb && row < bb;
+        const float a = Ginv[ok ? (int64_t)kk * bb + row : 0];
+        av[q] = ok ? a : 0.f;
+      }
     }
 #pragma unroll
     for (int q = 0; q < kRows / 4; ++q) {
