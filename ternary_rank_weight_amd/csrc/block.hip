@@ -1962,17 +1962,40 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
   __shared__ double red[kCholT / kWave];
   const int t = threadIdx.x, w = t >> 6;
   for (int j = t; j < bb; j += kCholT) rhs[j] = rhs_in[j];
+  // Loops over partials written by other launches: eight loads in flight
+  // per thread (clamped addresses, masked at use), not one round trip each.
+  constexpr int kLd = 8;
   // sweep visit: the exact rise of ||R||^2 when the stored block was added back
   double added = 0.0;
   if (dpart) {
     double p = 0.0;
-    for (int64_t j = t; j < ndpart; j += kCholT) p += dpart[j];
+    for (int64_t j0 = t; j0 < ndpart; j0 += (int64_t)kLd * kCholT) {
+      double x[kLd];
+#pragma unroll
+      for (int u = 0; u < kLd; ++u) {
+        const int64_t j = j0 + (int64_t)u * kCholT;
+        x[u] = dpart[j < ndpart ? j : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < kLd; ++u)
+        if (j0 + (int64_t)u * kCholT < ndpart) p += x[u];   // the same order as one at a time
+    }
     added = block_sum<kCholT>(p, red);
   }
   // the single-entry bound of the residual this block was fitted to, from
   // the per-wave partials of the launch that last wrote it (appendix §7)
   double bmx = 0.0;
-  for (int64_t j = t; j < nmpart; j += kCholT) bmx = fmax(bmx, mpart[j]);
+  for (int64_t j0 = t; j0 < nmpart; j0 += (int64_t)kLd * kCholT) {
+    double x[kLd];
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int64_t j = j0 + (int64_t)u * kCholT;
+      x[u] = mpart[j < nmpart ? j : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kLd; ++u)
+      if (j0 + (int64_t)u * kCholT < nmpart) bmx = fmax(bmx, x[u]);
+  }
   const double bound = block_max_f64<kCholT>(bmx, red);
   // M = (U^T U) o (V^T V); solve without a ridge, retry once with one
   d4 acc[TR][T];
@@ -1980,6 +2003,9 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
 #pragma unroll
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (ok) break;   // uniform
+    // up to b = 64 every entry is loaded from a clamped index,
+    // unconditionally, then masked, so that the loads are in flight together;
+    // at b = 128 that many live loads would spill, and they are taken one by one
 #pragma unroll
     for (int r = 0; r < TR; ++r)
 #pragma unroll
@@ -1988,9 +2014,24 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
         for (int v = 0; v < 4; ++v) {
           const int i = sweep_row(r, v), j = sweep_col(J);
           const bool in = w + 4 * r < T && i < bb && j < bb;
-          acc[r][J][v] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
-                            : (i == j ? 1.0 : 0.0);
-          if (in && i == j) s_diag[i] = acc[r][J][v];
+          if constexpr (T <= 4) {
+            const int ix = in ? i * bb + j : 0;
+            const double gu = (double)GU[ix];
+            const double gv = GVw ? GVw[ix] : (double)GV[ix];
+            acc[r][J][v] = in ? gu * gv : (i == j ? 1.0 : 0.0);
+          } else {
+            acc[r][J][v] = in ? (double)GU[i * bb + j] * (GVw ? GVw[i * bb + j] : (double)GV[i * bb + j])
+                              : (i == j ? 1.0 : 0.0);
+          }
+        }
+#pragma unroll
+    for (int r = 0; r < TR; ++r)
+#pragma unroll
+      for (int J = 0; J < T; ++J)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = sweep_row(r, v), j = sweep_col(J);
+          if (w + 4 * r < T && i < bb && i == j) s_diag[i] = acc[r][J][v];
         }
     __syncthreads();
     if (attempt == 1) {
@@ -2033,6 +2074,14 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     }
   }
   __syncthreads();
+  // the block's code counts, summed over the block (exact integers)
+  long long nbl = 0, ncl = 0;
+  if (!dpart && t < bb) {
+    nbl = nnz[t];
+    ncl = nnz[bstride + t];
+  }
+  const long long nb_sum = block_sum<kCholT>(nbl, reinterpret_cast<long long*>(red));
+  const long long nc_sum = block_sum<kCholT>(ncl, reinterpret_cast<long long*>(red));
   if (t == 0) {
     double dec = 0.0;
     for (int i = 0; i < bb; ++i) dec += dsol[i] * rhs[i];
@@ -2059,13 +2108,8 @@ __global__ __launch_bounds__(kCholT) void k_joint_solve(int* __restrict__ GU, in
     trace_state[0] = tnew;
     if (trace) trace[blk] = tnew;
     if (!dpart) {
-      long long nb = 0, nc = 0;
-      for (int i = 0; i < bb; ++i) {
-        nb += nnz[i];
-        nc += nnz[bstride + i];
-      }
-      st[EXTERND_STAT_NNZ_B] += nb;
-      st[EXTERND_STAT_NNZ_C] += nc;
+      st[EXTERND_STAT_NNZ_B] += nb_sum;
+      st[EXTERND_STAT_NNZ_C] += nc_sum;
     }
   }
   for (int e = t; e < bb * bb; e += kCholT) {
