@@ -43,13 +43,13 @@ SEQ_TRAFFIC_SHA = "a864fc9a0c2937bd"
 # (MOPS x 512), and HBM
 # bytes (FETCH x 2.0, WRITE x 1.0) against the 26.2 MB of R it must read.
 # Reported only while the block sources hash to the ones they were taken on.
-BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0371,
-                  "bf16_mfma_flops": 2.5277e9, "int8_mfma_ops": 3.146e7, "fetch_bytes": 26733445,
-                  "write_bytes": 3293251, "R_bytes": 26214400}
+BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0383,
+                  "bf16_mfma_flops": 2.5277e9, "int8_mfma_ops": 3.146e7, "fetch_bytes": 26728653,
+                  "write_bytes": 3293256, "R_bytes": 26214400}
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
                          "ternary_rank_weight_amd/csrc/device_common.hpp",
                          "ternary_rank_weight_amd/csrc/exchange.hpp"]
-BLOCK_COUNTER_SHA = "2f228092b543069c"
+BLOCK_COUNTER_SHA = "d49bb757e2290e70"
 
 
 def _sources_sha(files):
