@@ -44,7 +44,21 @@ def test_bpw_eq1():
     # mask entropy quoted on the pages for 43% zeros, H(0.43) ~ 0.99 bits
     h = -(0.43 * math.log2(0.43) + 0.57 * math.log2(0.57))
     assert round(h, 2) == 0.99
-    assert oracle.bpw_packed2(512, 256, 256) == pytest.approx((2 * 512 * 512 + 32 * 512) / 65536)
+    # fixed 2-bit codes, counted by hand: each of 512 components stores
+    # 256 + 256 codes of 2 bits (1024 bits) and one 32-bit scale, 1056 bits;
+    # 512 * 1056 = 540,672 bits over 256 * 256 = 65,536 weights = 8.25
+    assert oracle.bpw_packed2(512, 256, 256) == 8.25
+    # a tall matrix: 3 * (2 * (40 + 10) + 32) = 396 bits over 400 weights
+    assert oracle.bpw_packed2(3, 40, 10) == pytest.approx(0.99)
+
+
+def test_zero_fraction_hand_counted():
+    # B has 2 zeros of 6 entries, C has 3 of 6: 5 of 12 over both factors
+    B = np.array([[1, 0], [0, -1], [1, 1]], dtype=np.int8)
+    C = np.array([[0, 0, 1], [-1, 0, 1]], dtype=np.int8)
+    assert oracle.zero_fraction(B, C) == pytest.approx(5 / 12, abs=1e-15)
+    assert oracle.zero_fraction(np.zeros((4, 2)), np.zeros((2, 3))) == 1.0
+    assert oracle.zero_fraction(np.ones((4, 2)), -np.ones((2, 3))) == 0.0
 
 
 def test_splitmix64_known_answer():

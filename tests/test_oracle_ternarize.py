@@ -115,6 +115,24 @@ def test_optimal_projection_vs_brute_force():
             assert alpha == pytest.approx((x @ t) / np.count_nonzero(t), rel=1e-12)
 
 
+def test_project_columns_is_brute_force_per_column():
+    # every column of a 5 x 4 matrix separately: the ternary t that captures
+    # the most energy (x.t)^2 / ||t||^2 over all 3^5 - 1 candidates, in the
+    # column's own position (a transposed or shuffled result fails)
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((5, 4))
+    X[2, 1] = 0.0
+    P = oracle.project_columns(X)
+    assert P.shape == X.shape and P.dtype == np.int8
+    cands = [np.array(tt, dtype=np.float64) for tt in itertools.product((-1, 0, 1), repeat=5) if any(tt)]
+    for j in range(X.shape[1]):
+        x = X[:, j]
+        best = max((x @ tt) ** 2 / (tt @ tt) for tt in cands)
+        t = P[:, j].astype(np.float64)
+        assert (x @ t) ** 2 / (t @ t) == pytest.approx(best, rel=1e-12)
+        assert np.all(np.sign(t[t != 0]) == np.sign(x[t != 0]))
+
+
 def test_threshold_ties_optimal_projection_on_gaussians():
     # Continuum: a threshold at t sigma captures 2 phi(t)^2 / Q(t) of the
     # energy.  The optimum solves phi(t) = 2 t Q(t).  The pages say T_0.7
