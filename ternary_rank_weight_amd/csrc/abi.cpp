@@ -119,6 +119,7 @@ int get_ws(Workspace& w, const externd_opts& o, size_t bytes, hipStream_t s) {
 
 namespace externd {
 int report(int status, const char* msg) { return fail(status, "%s", msg); }
+thread_local bool g_single_placement = false;
 }  // namespace externd
 
 extern "C" {
@@ -249,7 +250,8 @@ uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, 
   const int md = seq_mode(mode, m, n, cus, false, false);
   if (md < 0) return (fail(EXTERND_EUNSUPPORTED, "%lld x %lld does not fit the %s kernel", (long long)m, (long long)n,
                            mode == EXTERND_MODE_RESIDENT ? "resident" : "persistent streaming"), 0);
-  if (md == EXTERND_MODE_RESIDENT) return externd::resident_workspace_bytes(m, n, k);
+  if (md == EXTERND_MODE_RESIDENT)
+    return externd::resident_workspace_bytes(m, n, k, externd::resident_place_candidates(m, n, k));
   if (md == EXTERND_MODE_PERSISTENT) return externd::persist_workspace_bytes(m, n, k, cus);
   return externd::stream_workspace_bytes(m, n);
 }
@@ -386,9 +388,10 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   Workspace w;
   hipError_t e;
   if (mode == EXTERND_MODE_RESIDENT) {
-    if ((st = get_ws(w, o, externd::resident_workspace_bytes(m, n, k), s)) != EXTERND_OK) return st;
+    const int cands = externd::g_single_placement ? 1 : externd::resident_place_candidates(m, n, k);
+    if ((st = get_ws(w, o, externd::resident_workspace_bytes(m, n, k, cands), s)) != EXTERND_OK) return st;
     int grid = 0;
-    e = externd::run_resident_seq(sa, w.ptr, cus, s, &grid);
+    e = externd::run_resident_seq(sa, w.ptr, cands, cus, s, &grid);
     if (e != hipSuccess) return hip_fail(e, "resident decomposition");
   } else if (mode == EXTERND_MODE_PERSISTENT) {
     if ((st = get_ws(w, o, externd::persist_workspace_bytes(m, n, k, cus), s)) != EXTERND_OK) return st;

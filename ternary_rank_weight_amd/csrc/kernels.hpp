@@ -114,8 +114,14 @@ hipError_t run_persist_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t 
 
 // resident sequential path (seq_resident.hip)
 bool resident_fits(int64_t m, int64_t n, int num_cus);
-size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k);
-hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s, int* grid_out);
+// Placements of the exchange words the resident path tries before the run
+// (1: no probe); the workspace holds `cands` placements.
+int resident_place_candidates(int64_t m, int64_t n, int64_t k);
+size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k, int cands);
+hipError_t run_resident_seq(const SeqArgs& a, void* ws, int cands, int num_cus, hipStream_t s, int* grid_out);
+// Set by externd_decompose_noalloc around its call: the resident path then
+// uses a single placement, which fits the static scratch.
+extern thread_local bool g_single_placement;
 
 // block path (block.hip)
 size_t block_workspace_bytes(int64_t m, int64_t n, int b);

@@ -65,7 +65,10 @@ extern "C" int externd_decompose_noalloc(const float* A, int64_t m, int64_t n, f
   if (externd_block_width(m, n, block) > 1 || o.mode == EXTERND_MODE_STREAMING || o.mode == EXTERND_MODE_PERSISTENT)
     return externd::report(EXTERND_EUNSUPPORTED, "externd_decompose_noalloc runs the resident sequential path only");
   o.mode = EXTERND_MODE_RESIDENT;
-  const uint64_t need = externd_workspace_bytes(m, n, mu, block, EXTERND_MODE_RESIDENT);
+  // one placement of the exchange words (no placement probe): the size of
+  // the static scratch does not grow with the probe's copies
+  uint64_t need = externd_workspace_bytes(m, n, mu, block, EXTERND_MODE_RESIDENT);
+  if (need > 0) need = externd::resident_workspace_bytes(m, n, externd_rank(m, n, mu), 1);
   if (need > kScratchBytes) {
     char msg[160];
     std::snprintf(msg, sizeof(msg), "needs %llu bytes of scratch, above the static %zu",
@@ -84,5 +87,8 @@ extern "C" int externd_decompose_noalloc(const float* A, int64_t m, int64_t n, f
   // can fall back to an allocation.
   o.workspace = p;
   o.workspace_bytes = kScratchBytes;
-  return externd_decompose(A, m, n, mu, tau, iters, block, stream, B2, C2, D, energy, &o);
+  externd::g_single_placement = true;
+  const int st = externd_decompose(A, m, n, mu, tau, iters, block, stream, B2, C2, D, energy, &o);
+  externd::g_single_placement = false;
+  return st;
 }

@@ -71,8 +71,10 @@ struct ResArgs {
   const double* a2;            // ||A||^2 (weighted when wt is set)
   const float* wt;             // optional column weights (§2.5), n floats
   const long long* nonfinite;  // count of non-finite entries of A
-  unsigned* yslot;             // kRep replicas of n words, rep_stride(n) apart
-  unsigned* xslot;             // kRep replicas of m words, rep_stride(m) apart
+  unsigned* yslot;             // kRep replicas of n words, rep_stride(n) apart (placement 0)
+  unsigned* xslot;             // kRep replicas of m words, rep_stride(m) apart (placement 0)
+  const int* place;            // the placement of the word arrays to use (see k_place_probe)
+  int64_t place_words;         // words between consecutive placements
   unsigned* err;
   double* r2_partial;          // G fp64
   unsigned* sg_bits;           // ceil(k/32) words, zeroed: components failing the single-entry bound
@@ -116,6 +118,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   const int m = a.m, n = a.n;
   const int row0 = g * a.RB, col0 = g * a.CB;
   const int wm = (m + 15) / 16, wn = (n + 15) / 16;
+  const int64_t poff = (int64_t)__builtin_amdgcn_readfirstlane(*a.place) * a.place_words;
+  unsigned* const yslot = a.yslot + poff;
+  unsigned* const xslot = a.xslot + poff;
 
   if (*a.nonfinite > 0) {
     // Nothing sensible can be computed: zero this workgroup's share of the outputs.
@@ -259,9 +264,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           acc[l] = s;
         }
         ++ry;
-        reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), a.yslot, col0, ry, rep_stride(n));
+        reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), yslot, col0, ry, rep_stride(n));
         float y[KR];
-        const bool bad = !gather<T, KR>(a.yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err);
+        const bool bad = !gather<T, KR>(yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err);
         if (!ternarize_dist<T, KR>(y, bad, n, a.tau, v, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
@@ -293,9 +298,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
           acc[l] = s;
         }
         ++rx;
-        reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), a.xslot, row0, rx, rep_stride(m));
+        reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), xslot, row0, rx, rep_stride(m));
         float x[KC];
-        const bool bad = !gather<T, KC>(a.xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err);
+        const bool bad = !gather<T, KC>(xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err);
         if (!ternarize_dist<T, KC>(x, bad, m, a.tau, u, bufs, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
@@ -390,6 +395,70 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   }
 }
 
+// Placement probe.  Where the exchange words sit in device memory changes
+// the time of the whole decomposition by up to 6 % (2560 x 2560: 512
+// components take 60.0 to 63.7 ms depending on the 2 KB step of the word
+// arrays' start within 16 KB, and which step is fastest differs from one
+// allocation to the next), so it cannot be fixed in advance.  The exchange
+// alone predicts it (correlation 0.92 over 32 placements): this kernel runs
+// `rounds` exchanges of y and x, exactly as k_seq_resident publishes and
+// gathers them but with no arithmetic between, on each candidate placement
+// in turn (disjoint copies of the word arrays, place_words apart, each
+// starting 2 KB later within 16 KB than the one before), and workgroup 0
+// stores the index of the fastest in *place.  The values exchanged are
+// never used, so the choice cannot change any result.  Waits are bounded;
+// if one runs out, placement 0 is kept.
+struct ProbeArgs {
+  int m, n, G, RB, CB;
+  unsigned* yslot;
+  unsigned* xslot;
+  int64_t place_words;
+  int cands, rounds;
+  unsigned* err;   // the probe's own flag
+  int* place;
+};
+
+template <int T, int KR, int LR, int KC, int LC>
+__global__ __launch_bounds__(T) void k_place_probe(ProbeArgs a) {
+  constexpr int W = T / kWave;
+  constexpr int LMAX = LR > LC ? LR : LC;
+  __shared__ float red[W * LMAX];
+  const int g = blockIdx.x;
+  const int m = a.m, n = a.n;
+  const int row0 = g * a.RB, col0 = g * a.CB;
+  float accy[LC], accx[LR];
+#pragma unroll
+  for (int l = 0; l < LC; ++l) accy[l] = 0.f;
+#pragma unroll
+  for (int l = 0; l < LR; ++l) accx[l] = 0.f;
+  bool ok = true;
+  unsigned long long best = ~0ull;
+  int best_c = 0;
+  for (int c = 0; c < a.cands && ok; ++c) {
+    unsigned* const ys = a.yslot + (int64_t)c * a.place_words;
+    unsigned* const xs = a.xslot + (int64_t)c * a.place_words;
+    __syncthreads();
+    const unsigned long long t0 = wall_clock64();
+    for (unsigned r = 1; r <= (unsigned)a.rounds && ok; ++r) {   // every placement starts at parity 0
+      reduce_publish<T, LC>(accy, red, min(a.CB, n - col0), ys, col0, r, rep_stride(n));
+      float y[KR];
+      ok = gather<T, KR>(ys + rep_of(g) * rep_stride(n), n, r, y, a.err);
+      ok = __syncthreads_and(ok);
+      reduce_publish<T, LR>(accx, red, min(a.RB, m - row0), xs, row0, r, rep_stride(m));
+      float x[KC];
+      if (ok) ok = gather<T, KC>(xs + rep_of(g) * rep_stride(m), m, r, x, a.err);
+      ok = __syncthreads_and(ok);
+    }
+    const unsigned long long dt = wall_clock64() - t0;
+    if (dt < best) {
+      best = dt;
+      best_c = c;
+    }
+  }
+  if (!ok && threadIdx.x == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (g == 0 && threadIdx.x == 0) *a.place = ok ? best_c : 0;
+}
+
 __global__ void k_fill_u64(unsigned long long* p, int64_t count) {
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
        j += (int64_t)gridDim.x * blockDim.x)
@@ -444,6 +513,13 @@ inline int pick_tile(int64_t m, int64_t n, int num_cus) {
 }
 
 template <int KR, int LR, int KC, int LC>
+hipError_t launch_probe(ProbeArgs& pa, hipStream_t s) {
+  void* args[] = {&pa};
+  return hipLaunchCooperativeKernel(reinterpret_cast<void*>(&k_place_probe<kResT, KR, LR, KC, LC>), dim3(pa.G),
+                                    dim3(kResT), args, 0, s);
+}
+
+template <int KR, int LR, int KC, int LC>
 hipError_t launch_tile(ResArgs& ra, hipStream_t s) {
   void* args[] = {&ra};
   void* fn = ra.cap_i >= 0 ? reinterpret_cast<void*>(&k_seq_resident<kResT, KR, LR, KC, LC, true>)
@@ -458,25 +534,39 @@ bool resident_fits(int64_t m, int64_t n, int num_cus) {
   return pick_tile(m, n, num_cus) >= 0;
 }
 
-size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  return sizeof(unsigned) * (size_t)kRep * (rep_stride((int)m) + rep_stride((int)n)) + sizeof(double) * (256 + 4096 + 8) +
-         sizeof(long long) * 8 + sizeof(unsigned) * 64 + sizeof(float) * (size_t)n +
-         sizeof(unsigned) * (size_t)((k + 31) / 32) + 256 * 10;
+// Placements of the exchange words tried by k_place_probe: disjoint copies
+// of the y and x word arrays, each starting 2 KB later within 16 KB.
+constexpr int kPlaceCands = 8;
+constexpr int kProbeRounds = 48;
+static int64_t place_words(int64_t m, int64_t n) {
+  const int64_t w = (int64_t)kRep * (rep_stride((int)m) + rep_stride((int)n));
+  return (w + 4095) / 4096 * 4096 + 512;   // a multiple of 16 KB, plus 2 KB
+}
+
+int resident_place_candidates(int64_t m, int64_t n, int64_t k) {
+  // the probe costs about 0.25 ms per candidate: worth it for long runs only
+  return (k >= 1024 && m * n >= (int64_t(1) << 20)) ? kPlaceCands : 1;
+}
+
+size_t resident_workspace_bytes(int64_t m, int64_t n, int64_t k, int cands) {
+  return sizeof(unsigned) * (size_t)(place_words(m, n) * cands) + sizeof(double) * (256 + 4096 + 8) +
+         sizeof(long long) * 8 + sizeof(unsigned) * 64 * 2 + sizeof(float) * (size_t)n +
+         sizeof(unsigned) * (size_t)((k + 31) / 32) + sizeof(int) * 64 + 256 * 12;
 }
 
 static inline char* align256(char* p) {
   return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
 }
 
-hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t s, int* grid_out) {
+hipError_t run_resident_seq(const SeqArgs& a, void* ws, int cands, int num_cus, hipStream_t s, int* grid_out) {
   const int ti = pick_tile(a.m, a.n, num_cus);
-  if (ti < 0) return hipErrorInvalidValue;
+  if (ti < 0 || cands < 1) return hipErrorInvalidValue;
   const Tile tl = kTiles[ti];
+  const int64_t pw = place_words(a.m, a.n);
   char* p = align256(static_cast<char*>(ws));
-  unsigned long long* yslot = reinterpret_cast<unsigned long long*>(p);
-  p = align256(p + sizeof(unsigned) * kRep * rep_stride((int)a.n));
-  unsigned long long* xslot = reinterpret_cast<unsigned long long*>(p);
-  p = align256(p + sizeof(unsigned) * kRep * rep_stride((int)a.m));
+  unsigned* yslot = reinterpret_cast<unsigned*>(p);   // placement c at yslot + c * pw
+  unsigned* xslot = yslot + (int64_t)kRep * rep_stride((int)a.n);
+  p = align256(p + sizeof(unsigned) * (size_t)(pw * cands));
   double* r2p = reinterpret_cast<double*>(p);
   p = align256(p + sizeof(double) * 256);
   double* npart = reinterpret_cast<double*>(p);
@@ -487,6 +577,10 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   p = align256(p + sizeof(long long) * 8);
   unsigned* err = reinterpret_cast<unsigned*>(p);
   p = align256(p + sizeof(unsigned) * 64);
+  unsigned* probe_err = reinterpret_cast<unsigned*>(p);
+  p = align256(p + sizeof(unsigned) * 64);
+  int* place = reinterpret_cast<int*>(p);
+  p = align256(p + sizeof(int) * 64);
   float* wt = a.importance ? reinterpret_cast<float*>(p) : nullptr;   // column weights (§2.5)
   p = align256(p + sizeof(float) * a.n);
   unsigned* sg_bits = reinterpret_cast<unsigned*>(p);
@@ -494,9 +588,36 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
 
   hipError_t e;
   if ((e = launch_fill_u32(sg_bits, sg_words, 0u, s)) != hipSuccess) return e;
-  // every replica word starts at parity 0 (rep_stride is even: whole 8-byte fills)
-  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, yslot, (int64_t)kRep * rep_stride((int)a.n) / 2);
-  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, xslot, (int64_t)kRep * rep_stride((int)a.m) / 2);
+  // every replica word of every placement starts at parity 0 (pw is even: whole 8-byte fills)
+  hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(yslot),
+                     pw * cands / 2);
+  if ((e = launch_fill_u32(reinterpret_cast<uint32_t*>(place), 1, 0u, s)) != hipSuccess) return e;
+  const int G = tile_grid(tl, a.m, a.n);
+  if (cands > 1) {
+    if ((e = launch_fill_u32(probe_err, 1, 0u, s)) != hipSuccess) return e;
+    ProbeArgs pa{};
+    pa.m = (int)a.m;
+    pa.n = (int)a.n;
+    pa.G = G;
+    pa.RB = (int)((a.m + G - 1) / G);
+    pa.CB = (int)((a.n + G - 1) / G);
+    pa.yslot = yslot;
+    pa.xslot = xslot;
+    pa.place_words = pw;
+    pa.cands = cands;
+    pa.rounds = kProbeRounds;
+    pa.err = probe_err;
+    pa.place = place;
+    switch (ti) {
+      case 0: e = launch_probe<1, 32, 1, 32>(pa, s); break;
+      case 1: e = launch_probe<2, 16, 2, 16>(pa, s); break;
+      default: e = launch_probe<5, 10, 5, 10>(pa, s); break;
+    }
+    if (e != hipSuccess) return e;
+    // the probe left every placement at some parity: back to 0
+    hipLaunchKernelGGL(k_fill_u64, dim3(64), dim3(256), 0, s, reinterpret_cast<unsigned long long*>(yslot),
+                       pw * cands / 2);
+  }
   if ((e = launch_fill_i64(nonfinite, 1, 0, s)) != hipSuccess) return e;
   if ((e = launch_fill_u32(err, 1, 0u, s)) != hipSuccess) return e;
   if (wt && (e = launch_importance_weights(a.importance, a.n, a.lambda, wt, nonfinite, s)) != hipSuccess) return e;
@@ -511,7 +632,7 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   ra.tau = a.tau;
   ra.iters = a.iters;
   ra.seed = a.seed;
-  ra.G = tile_grid(tl, a.m, a.n);
+  ra.G = G;
   ra.RB = (int)((a.m + ra.G - 1) / ra.G);
   ra.CB = (int)((a.n + ra.G - 1) / ra.G);
   ra.B2 = a.B2;
@@ -522,8 +643,10 @@ hipError_t run_resident_seq(const SeqArgs& a, void* ws, int num_cus, hipStream_t
   ra.a2 = a2;
   ra.wt = wt;
   ra.nonfinite = nonfinite;
-  ra.yslot = reinterpret_cast<unsigned*>(yslot);   // 32-bit words; zero = parity 0
-  ra.xslot = reinterpret_cast<unsigned*>(xslot);
+  ra.yslot = yslot;   // 32-bit words; zero = parity 0
+  ra.xslot = xslot;
+  ra.place = place;
+  ra.place_words = pw;
   ra.err = err;
   ra.r2_partial = r2p;
   ra.sg_bits = sg_bits;
