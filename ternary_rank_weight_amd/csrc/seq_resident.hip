@@ -112,6 +112,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   __shared__ float v_own[LC];
   __shared__ double bufs[3][W][4];
   __shared__ unsigned sg_win[32];   // safeguard bits of the current window of 1024 components
+  __shared__ double tslot[2];        // T_tau's reduction slots (ternarize_dist_at)
 
   const int t = threadIdx.x;
   const int g = blockIdx.x;
@@ -172,6 +173,10 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
     wcol[l] = __int_as_float(__builtin_amdgcn_readfirstlane(
         __float_as_int((a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f)));
   if (t < 32) sg_win[t] = 0u;   // published by the first barrier below
+  if (t == 0) {
+    tslot[0] = 0.0;
+    tslot[1] = 0.0;
+  }
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
   long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
         reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), yslot, col0, ry, rep_stride(n));
         float y[KR];
         const bool bad = !gather<T, KR>(yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err);
-        if (!ternarize_dist<T, KR>(y, bad, n, a.tau, v, bufs, cnt, fb)) {
+        if (!ternarize_dist_at<T, KR>(y, bad, n, a.tau, v, bufs, tslot, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
         reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), xslot, row0, rx, rep_stride(m));
         float x[KC];
         const bool bad = !gather<T, KC>(xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err);
-        if (!ternarize_dist<T, KC>(x, bad, m, a.tau, u, bufs, cnt, fb)) {
+        if (!ternarize_dist_at<T, KC>(x, bad, m, a.tau, u, bufs, tslot, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
