@@ -159,6 +159,7 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
   __shared__ double bufs[3][W][4];
   __shared__ unsigned sg_win[32];
   __shared__ int nlist[2];
+  __shared__ double tslot[2];   // T_tau's reduction slots (ternarize_dist_at)
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wv_id = t / kWave;
@@ -187,6 +188,10 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
     for (int q = t; q < L * n4; q += T) rcache[q] = src[q];
   }
   if (t < 32) sg_win[t] = 0u;
+  if (t == 0) {
+    tslot[0] = 0.0;
+    tslot[1] = 0.0;
+  }
   if (t < kRBMax) up_own[t] = 0.f;
   for (int c = t; c < KR * T; c += T) vpl[c] = 0;
   float d32 = 0.f;
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
         const int to = opaque_tid();
         float y[KR], v[KR];
         const bool bad = !gather<T, KR>(a.yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err, to);
-        if (!ternarize_dist<T, KR>(y, bad, n, a.tau, v, bufs, cnt, fb, to)) {
+        if (!ternarize_dist_at<T, KR>(y, bad, n, a.tau, v, bufs, tslot, cnt, fb, to)) {
           if (to == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
         const int to = opaque_tid();
         float x[KC], u[KC];
         const bool bad = !gather<T, KC>(a.xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err, to);
-        if (!ternarize_dist<T, KC>(x, bad, m, a.tau, u, bufs, cnt, fb, to)) {
+        if (!ternarize_dist_at<T, KC>(x, bad, m, a.tau, u, bufs, tslot, cnt, fb, to)) {
           if (to == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
