@@ -1777,7 +1777,12 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize(const float* __restrict__
 
 // The same for rows of L <= 512 K with the row held in registers: one read of
 // the row, and the codes packed from wave ballots (wave w of pass j covers
-// entries 512 j + 64 w .. + 63, i.e. code words 32 j + 4 w .. + 3).
+// entries 512 j + 64 w .. + 63, i.e. code words 32 j + 4 w .. + 3).  The
+// maximum and the fixed-point sum are reduced by DPP inside each wave and
+// one LDS atomic per wave (one barrier each; the sum's terms are exact
+// integers, so the order of the atomics cannot change it); the counts come
+// from the ballots, and the joint right-hand side is summed by DPP inside
+// each wave and by thread 0 over the waves in index order.
 __device__ inline uint32_t spread_bits16(uint32_t v) {   // bit e -> bit 2e
   v &= 0xffffu;
   v = (v | (v << 8)) & 0x00FF00FFu;
@@ -1794,12 +1799,21 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
                                                            long long* __restrict__ nnz_sum,
                                                            const float* __restrict__ Qrows,
                                                            double* __restrict__ rhs_out) {
-  __shared__ double scratch[kTT / kWave];
+  constexpr int W = kTT / kWave;
+  __shared__ int scratch[W];
+  __shared__ int wcnt[W];
+  __shared__ double wrq[W];
+  __shared__ unsigned s_max;   // bits of the largest |x| (LDS atomic max)
+  __shared__ double s_sum;     // the fixed-point sum (LDS atomic add of exact integers)
   const int i = blockIdx.x;
   const float* x = Xt + (int64_t)i * L;
   const float* qr = rhs_out ? Qrows + (int64_t)i * L : nullptr;
   uint32_t* codes = out_codes + (int64_t)i * wl;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  if (t == 0) {
+    s_max = 0u;
+    s_sum = 0.0;
+  }
   float v[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -1810,7 +1824,12 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
   float mx = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(v[j]));
-  const float M = block_max<kTT>(mx, reinterpret_cast<float*>(scratch));
+  const float wm = wave_max_to63(mx);
+  // one LDS atomic per wave; a wave whose entries are all NaN adds nothing,
+  // as a NaN operand of fmaxf adds nothing
+  if (lane == kWave - 1) atomicMax(&s_max, wm == wm ? __float_as_uint(wm) : 0u);
+  __syncthreads();
+  const float M = __uint_as_float(s_max);
   if (M == 0.f) {
     for (int64_t q = t; q < wl; q += kTT) codes[q] = (q == 0) ? 1u : 0u;
     if (t == 0) {
@@ -1825,9 +1844,14 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
   double q = 0.0;
 #pragma unroll
   for (int j = 0; j < K; ++j) q += fixed_point_q(fabsf(v[j]), s);
-  const double thr = fixed_point_threshold(block_sum<kTT>(q, scratch), s, tau, L);
+  // the terms are integers whose total is below 2^52: any order of the adds
+  // gives the same sum
+  const double qw = wave_sum_to63(q);
+  if (lane == kWave - 1) atomicAdd(&s_sum, qw);
+  __syncthreads();
+  const double thr = fixed_point_threshold(s_sum, s, tau, L);
   const uint32_t tb = threshold_bits(thr);
-  int cnt = 0;
+  int cnt = 0;       // this wave's kept entries (wave-uniform, from the ballots)
   double rq = 0.0;   // u_i . q_i over this thread's kept entries (joint scale rhs)
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -1835,7 +1859,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
     const bool keep = idx < L && (__float_as_uint(v[j]) & 0x7fffffffu) > tb;
     const unsigned long long nz = __ballot(keep);
     const unsigned long long ng = __ballot(keep && v[j] < 0.f);
-    cnt += keep ? 1 : 0;
+    cnt += __popcll(nz);
     if (qr && keep) rq += v[j] > 0.f ? (double)qr[idx] : -(double)qr[idx];
     if (lane < 4) {
       const int64_t wd = (int64_t)32 * j + 4 * w + lane;
@@ -1844,12 +1868,22 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
     }
   }
   if (__float_as_uint(M) > tb) {
-    const int total = block_sum<kTT>(cnt, reinterpret_cast<int*>(scratch));
-    if (rhs_out) {
-      const double r = block_sum<kTT>(rq, scratch);
-      if (t == 0) rhs_out[i] = r;
+    // per-wave parts in fixed order: DPP inside the wave, waves in index order
+    const double rqw = rhs_out ? wave_sum_to63(rq) : 0.0;
+    if (lane == kWave - 1) {
+      wcnt[w] = cnt;
+      wrq[w] = rqw;
     }
+    __syncthreads();
     if (t == 0) {
+      int total = 0;
+      double r = 0.0;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        total += wcnt[u];
+        r += wrq[u];
+      }
+      if (rhs_out) rhs_out[i] = r;
       nnz[i] = total;
       atomicAdd(reinterpret_cast<unsigned long long*>(nnz_sum), (unsigned long long)total);
     }
@@ -1861,7 +1895,7 @@ __global__ __launch_bounds__(kTT) void k_row_ternarize_reg(const float* __restri
     const int64_t idx = t + (int64_t)kTT * j;
     if (idx < L && fabsf(v[j]) == M) first = min(first, (int)idx);
   }
-  const int idx = block_min_i<kTT>(first, reinterpret_cast<int*>(scratch));
+  const int idx = block_min_i<kTT>(first, scratch);
   __syncthreads();   // the zero code words written above are visible block-wide below
   if (t == 0) {
     codes[idx >> 4] = code_of(x[idx]) << (2 * (idx & 15));
