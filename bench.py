@@ -43,13 +43,13 @@ SEQ_TRAFFIC_SHA = "4b6c48ca4111a213"
 # (MOPS x 512), and HBM
 # bytes (FETCH x 2.0, WRITE x 1.0) against the 26.2 MB of R it must read.
 # Reported only while the block sources hash to the ones they were taken on.
-BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0383,
-                  "bf16_mfma_flops": 2.5277e9, "int8_mfma_ops": 3.146e7, "fetch_bytes": 26728653,
-                  "write_bytes": 3293256, "R_bytes": 26214400}
+BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0378,
+                  "bf16_mfma_flops": 2.5281e9, "int8_mfma_ops": 3.220e7, "fetch_bytes": 26732544,
+                  "write_bytes": 3293286, "R_bytes": 26214400}
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
                          "ternary_rank_weight_amd/csrc/device_common.hpp",
                          "ternary_rank_weight_amd/csrc/exchange.hpp"]
-BLOCK_COUNTER_SHA = "d49bb757e2290e70"
+BLOCK_COUNTER_SHA = "bd6abb93c2ae3b62"
 
 
 def _sources_sha(files):
