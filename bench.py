@@ -31,11 +31,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
 # same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
 # reported only while the kernel's sources hash to the ones it was taken on.
-SEQ_TRAFFIC_BYTES = 47752681472
+SEQ_TRAFFIC_BYTES = 47902051776
 SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
                        "ternary_rank_weight_amd/csrc/device_common.hpp",
                        "ternary_rank_weight_amd/csrc/exchange.hpp"]
-SEQ_TRAFFIC_SHA = "4b6c48ca4111a213"
+SEQ_TRAFFIC_SHA = "face3a16d04f26d5"
 
 # rocprofv3 counters of the block path on the 2560 x 2560 workload (b = 64),
 # per dispatch of the combined Gram / inverse / contraction launch: MFMA busy
