@@ -220,9 +220,13 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
  * path only (block widths above 1, EXTERND_MODE_STREAMING and shapes that do
  * not fit on chip give EXTERND_EUNSUPPORTED; opts->workspace must be NULL).
  * Its scratch memory is a static 256 KiB device array per GPU, held until
- * the process ends, so it calls no allocator; a shape needing more scratch
- * (16 KB (ceil(m/1024) + ceil(n/1024)) + 4 n + k / 8 bytes plus about 37 KB:
- * 144 KB at 2560 x 2560 with k = 5120) gives EXTERND_ENOMEM.  All calls on
+ * the process ends, so it calls no allocator; it holds one placement of the
+ * exchange words (16 KB (ceil(m/1024) + ceil(n/1024)) rounded up to 16 KB,
+ * plus 2 KB), so this entry point skips the placement probe that
+ * externd_decompose runs for long decompositions (the factors are the
+ * same).  A shape needing more scratch (the words, 4 n + k / 8 bytes, and
+ * about 40 KB: 146.5 KiB at 2560 x 2560 with k = 5120) gives
+ * EXTERND_ENOMEM.  All calls on
  * one GPU share that array (each call clears what it needs first): calls
  * that overlap on one GPU, on any streams, race and must not be issued.
  */
@@ -316,7 +320,11 @@ int32_t externd_resident_fits(int64_t m, int64_t n);
 /* Bytes of device workspace externd_decompose needs for these arguments
  * (mode as in externd_opts.mode; it only matters for the sequential path).
  * Without opts->workspace the library allocates this much stream-ordered
- * (hipMallocAsync) and frees it stream-ordered before returning.  Returns 0
+ * (hipMallocAsync) and frees it stream-ordered before returning.  For the
+ * resident path of a long decomposition (k >= 1024 and m n >= 2^20) it
+ * includes 8 placements of the exchange words, which a short probe times
+ * before the run to keep the fastest (about 852 KB at 2560 x 2560, k =
+ * 5120; one placement otherwise).  Returns 0
  * for invalid arguments, or when the AUTO/RESIDENT choice needs the device
  * and no gfx950 device is current; externd_last_error() says which. */
 uint64_t externd_workspace_bytes(int64_t m, int64_t n, float mu, int32_t block, int32_t mode);
