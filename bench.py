@@ -37,6 +37,15 @@ SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
                        "ternary_rank_weight_amd/csrc/exchange.hpp"]
 SEQ_TRAFFIC_SHA = "face3a16d04f26d5"
 
+# Measured HBM traffic of one k_seq_persist launch on the 9728 x 2560 workload
+# (mu = 3, tau = 1.0, k = 7680), scaled the same way; reported only while the
+# kernel's sources hash to the ones it was taken on.
+PERSIST_TRAFFIC_BYTES = 10251129712800
+PERSIST_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_persist.hip",
+                           "ternary_rank_weight_amd/csrc/device_common.hpp",
+                           "ternary_rank_weight_amd/csrc/exchange.hpp"]
+PERSIST_TRAFFIC_SHA = "b0e29f2da38e7c22"
+
 # rocprofv3 counters of the block path on the 2560 x 2560 workload (b = 64),
 # per dispatch of the combined Gram / inverse / contraction launch: MFMA busy
 # cycles over active cycles x SIMDs, bf16 MFMA flops and int8 MFMA operations
@@ -61,10 +70,16 @@ def _sources_sha(files):
     return h.hexdigest()[:16]
 
 
-def seq_traffic(workload):
-    if workload != "llm2560" or _sources_sha(SEQ_TRAFFIC_SOURCES) != SEQ_TRAFFIC_SHA:
-        return None
-    return SEQ_TRAFFIC_BYTES
+def seq_traffic(workload, kernel="k_seq_resident"):
+    if kernel == "k_seq_resident":
+        if workload != "llm2560" or _sources_sha(SEQ_TRAFFIC_SOURCES) != SEQ_TRAFFIC_SHA:
+            return None
+        return SEQ_TRAFFIC_BYTES
+    if kernel == "k_seq_persist":
+        if workload != "mlp9728" or _sources_sha(PERSIST_TRAFFIC_SOURCES) != PERSIST_TRAFFIC_SHA:
+            return None
+        return PERSIST_TRAFFIC_BYTES
+    return None
 
 
 def block_counters(workload, b):
@@ -608,7 +623,7 @@ def main():
             s["stats"]["mode"], "sequential path")
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": seq_traffic(args.workload) if kernel == "k_seq_resident" else None,
+                    "traffic": seq_traffic(args.workload, kernel),
                     "traffic_unit": "bytes per launch",
                     "alg_bytes_per_launch": alg}
     if "block" in per_mode:
