@@ -67,27 +67,6 @@ __device__ inline void reduce_publish(const float (&acc)[L], float* red, int nva
 
 // Block reductions with one barrier each.  buf is double[T/64][4]; two
 // consecutive reductions must use different buffers.
-template <int T>
-__device__ inline uint32_t block_umax_flag(uint32_t v, bool bad, double (*buf)[4], bool& any_bad) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), w = t / kWave;
-  const uint32_t mw = wave_umax_to63(v);
-  const bool bw = __any(bad);
-  if (lane == kWave - 1) {
-    buf[w][0] = (double)mw;
-    buf[w][1] = bw ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  uint32_t r = 0u;
-  bool b = false;
-#pragma unroll
-  for (int q = 0; q < T / kWave; ++q) {
-    r = max(r, (uint32_t)buf[q][0]);
-    b = b || buf[q][1] != 0.0;
-  }
-  any_bad = b;
-  return r;
-}
 template <int T, int NV>
 __device__ inline void block_sum_f64(double (&v)[NV], double (*buf)[4]) {
   const int t = threadIdx.x;
@@ -192,72 +171,13 @@ __device__ inline bool gather(const unsigned* slot, int N, unsigned round, float
   return ok;
 }
 
-// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond N),
-// identical in every workgroup.  `bad` folds a failed gather into the first
-// reduction: if any thread of the block has it set, returns false and the
-// caller leaves.  bufs[0..1] are used alternately (see block_umax_flag).
-// Writes T_tau(x) to out in the same layout; cnt gets this thread's nonzeros.
-template <int T, int K>
-__device__ inline bool ternarize_dist(const float (&val)[K], bool bad, int N, float tau,
-                                      float (&out)[K], double (*bufs)[T / kWave][4], int& cnt,
-                                      int& fallback, int tid = -1) {
-  const int t = tid >= 0 ? tid : (int)threadIdx.x;
-  uint32_t ab[K];
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    ab[j] = __float_as_uint(val[j]) & 0x7fffffffu;
-    mx = max(mx, ab[j]);
-  }
-  bool any_bad;
-  const uint32_t Mb = block_umax_flag<T>(mx, bad, bufs[0], any_bad);
-  if (any_bad) return false;
-  cnt = 0;
-  if (Mb == 0u) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
-    fallback = 1;
-    cnt = t == 0 ? 1 : 0;
-    return true;
-  }
-  const int s = fixed_point_shift(__uint_as_float(Mb), N);
-  // Every partial sum is an integer below 2^52, so the fp64 sums are exact.
-  double qs[1] = {0.0};
-#pragma unroll
-  for (int j = 0; j < K; ++j) qs[0] += fixed_point_q(__uint_as_float(ab[j]), s);
-  block_sum_f64<T, 1>(qs, bufs[1]);
-  const double thr = fixed_point_threshold(qs[0], s, tau, N);
-  const uint32_t tb = threshold_bits(thr);
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const bool keep = ab[j] > tb;
-    out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
-    cnt += keep ? 1 : 0;
-  }
-  fallback = 0;
-  if (Mb > tb) return true;
-  int first = INT32_MAX;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int idx = t + T * j;
-    if (idx < N && ab[j] == Mb) first = min(first, idx);
-  }
-  const int pick = block_min_idx<T>(first, bufs[0]);
-  cnt = 0;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    if (t + T * j == pick) {
-      out[j] = val[j] > 0.f ? 1.f : -1.f;
-      cnt = 1;
-    }
-  }
-  fallback = 1;
-  return true;
-}
-
-
-// T_tau as ternarize_dist, with the two block reductions done by LDS
-// atomics, one per wave, into two slots: slot[0] takes the fixed-point sum
+// T_tau (§2.2) of a vector distributed as val[j] = x[t + T*j] (zeros beyond
+// N), identical in every workgroup.  `bad` folds a failed gather into the
+// first reduction: if any thread of the block has it set, returns false and
+// the caller leaves.  Writes T_tau(x) to out in the same layout; cnt gets
+// this thread's nonzeros, fallback whether the largest-entry rule applied.
+// The two block reductions are done by LDS atomics, one per wave, into two
+// slots: slot[0] takes the fixed-point sum
 // (fp64; its terms are integers whose total is below 2^52, so the order of
 // the adds cannot change it) and the low word of slot[1] the maximum
 // magnitude's bits (a failed gather adds 0xffffffff, above every finite
