@@ -255,5 +255,107 @@ __device__ inline bool ternarize_dist_at(const float (&val)[K], bool bad, int N,
   return true;
 }
 
+// ternarize_dist_at with the fixed-point sum formed before the first barrier,
+// at the shift of a guessed exponent eg of max|x| (block-uniform; the caller
+// keeps one guess per kind of vector).  When the true exponent equals eg the
+// sum is the one the plain rule forms (the same shift, the same integers) and
+// one barrier serves both reductions; otherwise the sum is formed again at
+// the true shift after a second barrier.  eg is replaced by the true
+// exponent.  Slots (LDS, clear at the caller's first barrier): slot[0..1]
+// the guessed-shift sums and the low words of slot[2..3] the maxima, both
+// taken by the parity of the call count `par` (the caller's count of calls,
+// +1 per call); slot[4] the second sum.  On entry thread 0 clears the other
+// parity's slots and slot[4]: every thread read them before the barrier
+// that separates two calls, which the caller keeps.  bufs[0] serves the
+// fallback's argmin.
+template <int T, int K>
+__device__ inline bool ternarize_dist_guess(const float (&val)[K], bool bad, int N, float tau,
+                                            float (&out)[K], double (*bufs)[T / kWave][4], double* slot,
+                                            unsigned par, int& eg, int& cnt, int& fallback, int tid = -1) {
+  const int t = tid >= 0 ? tid : (int)threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const unsigned p = par & 1u;
+  double* const gsum = slot + p;
+  unsigned* const mslot = reinterpret_cast<unsigned*>(slot + 2 + p);
+  if (t == 0) {
+    slot[p ^ 1u] = 0.0;
+    *reinterpret_cast<unsigned*>(slot + 2 + (p ^ 1u)) = 0u;
+    slot[4] = 0.0;
+  }
+  const int L = ceil_log2_i32(N);
+  const int sg = 52 - eg - L;
+  uint32_t ab[K];
+  uint32_t mx = 0u;
+  double qs = 0.0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    ab[j] = __float_as_uint(val[j]) & 0x7fffffffu;
+    mx = max(mx, ab[j]);
+    qs += fixed_point_q(__uint_as_float(ab[j]), sg);
+  }
+  if (bad) mx = 0xffffffffu;
+  const uint32_t mw = wave_umax_to63(mx);
+  const double qw = wave_sum_to63(qs);
+  if (lane == kWave - 1) {
+    atomicMax(mslot, mw);
+    atomicAdd(gsum, qw);
+  }
+  __syncthreads();
+  const uint32_t Mb = *mslot;
+  if (Mb == 0xffffffffu) return false;
+  cnt = 0;
+  if (Mb == 0u) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
+    fallback = 1;
+    cnt = t == 0 ? 1 : 0;
+    return true;
+  }
+  int e;
+  (void)frexp((double)__uint_as_float(Mb), &e);
+  e = __builtin_amdgcn_readfirstlane(e);
+  const int s = 52 - e - L;
+  double S;
+  if (e == eg) {
+    S = *gsum;
+  } else {
+    double q2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) q2 += fixed_point_q(__uint_as_float(ab[j]), s);
+    const double q2w = wave_sum_to63(q2);
+    if (lane == kWave - 1) atomicAdd(slot + 4, q2w);
+    __syncthreads();
+    S = slot[4];
+  }
+  eg = e;
+  const double thr = fixed_point_threshold(S, s, tau, N);
+  const uint32_t tb = threshold_bits(thr);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const bool keep = ab[j] > tb;
+    out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
+    cnt += keep ? 1 : 0;
+  }
+  fallback = 0;
+  if (Mb > tb) return true;
+  int first = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int idx = t + T * j;
+    if (idx < N && ab[j] == Mb) first = min(first, idx);
+  }
+  const int pick = block_min_idx<T>(first, bufs[0]);
+  cnt = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (t + T * j == pick) {
+      out[j] = val[j] > 0.f ? 1.f : -1.f;
+      cnt = 1;
+    }
+  }
+  fallback = 1;
+  return true;
+}
+
 }  // namespace xchg
 }  // namespace externd

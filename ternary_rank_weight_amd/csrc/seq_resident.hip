@@ -112,7 +112,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   __shared__ float v_own[LC];
   __shared__ double bufs[3][W][4];
   __shared__ unsigned sg_win[32];   // safeguard bits of the current window of 1024 components
-  __shared__ double tslot[2];        // T_tau's reduction slots (ternarize_dist_at)
+  __shared__ double tslot[6];        // T_tau's reduction slots (ternarize_dist_guess)
 
   const int t = threadIdx.x;
   const int g = blockIdx.x;
@@ -173,10 +173,7 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
     wcol[l] = __int_as_float(__builtin_amdgcn_readfirstlane(
         __float_as_int((a.wt && l < a.CB && col0 + l < n) ? a.wt[col0 + l] : 1.f)));
   if (t < 32) sg_win[t] = 0u;   // published by the first barrier below
-  if (t == 0) {
-    tslot[0] = 0.0;
-    tslot[1] = 0.0;
-  }
+  if (t < 6) tslot[t] = 0.0;
   float d32 = 0.f;
   unsigned ry = 0, rx = 0;
   long long st_nnz_u = 0, st_nnz_v = 0, st_fb = 0, st_b = 0, st_c = 0;
@@ -184,6 +181,9 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
   const bool capturer = (g == 0);
 
   const int sg_words = (a.k + 31) / 32;
+  // guesses of the exponent of max|y| and max|x| for T_tau (block-uniform),
+  // kept apart for the first, the second and the later iterations
+  int egy0 = 0, egy1 = 0, egy2 = 0, egx0 = 0, egx1 = 0, egx2 = 0;
   for (int i = 0; i <= a.k; ++i) {
     // ---- a finished window of safeguard bits (or the last one) to the global bitmap ----
     if (i > 0 && ((i & 1023) == 0 || i == a.k)) {
@@ -272,10 +272,12 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
         reduce_publish<T, LC>(acc, red, min(a.CB, n - col0), yslot, col0, ry, rep_stride(n));
         float y[KR];
         const bool bad = !gather<T, KR>(yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err);
-        if (!ternarize_dist_at<T, KR>(y, bad, n, a.tau, v, bufs, tslot, cnt, fb)) {
+        int eg = it == 0 ? egy0 : (it == 1 ? egy1 : egy2);
+        if (!ternarize_dist_guess<T, KR>(y, bad, n, a.tau, v, bufs, tslot, ry + rx, eg, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
+        if (it == 0) egy0 = eg; else if (it == 1) egy1 = eg; else egy2 = eg;
         st_nnz_v += cnt;
         st_fb += fb;
         if (cap) {
@@ -306,10 +308,12 @@ __global__ __launch_bounds__(T) void k_seq_resident(ResArgs a) {
         reduce_publish<T, LR>(acc, red, min(a.RB, m - row0), xslot, row0, rx, rep_stride(m));
         float x[KC];
         const bool bad = !gather<T, KC>(xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err);
-        if (!ternarize_dist_at<T, KC>(x, bad, m, a.tau, u, bufs, tslot, cnt, fb)) {
+        int eg = it == 0 ? egx0 : (it == 1 ? egx1 : egx2);
+        if (!ternarize_dist_guess<T, KC>(x, bad, m, a.tau, u, bufs, tslot, ry + rx, eg, cnt, fb)) {
           if (t == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
+        if (it == 0) egx0 = eg; else if (it == 1) egx1 = eg; else egx2 = eg;
         st_nnz_u += cnt;
         st_fb += fb;
         if (it == a.iters - 1) {
