@@ -159,7 +159,7 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
   __shared__ double bufs[3][W][4];
   __shared__ unsigned sg_win[32];
   __shared__ int nlist[2];
-  __shared__ double tslot[2];   // T_tau's reduction slots (ternarize_dist_at)
+  __shared__ double tslot[6];   // T_tau's reduction slots (ternarize_dist_guess)
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wv_id = t / kWave;
@@ -188,10 +188,7 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
     for (int q = t; q < L * n4; q += T) rcache[q] = src[q];
   }
   if (t < 32) sg_win[t] = 0u;
-  if (t == 0) {
-    tslot[0] = 0.0;
-    tslot[1] = 0.0;
-  }
+  if (t < 6) tslot[t] = 0.0;
   if (t < kRBMax) up_own[t] = 0.f;
   for (int c = t; c < KR * T; c += T) vpl[c] = 0;
   float d32 = 0.f;
@@ -200,6 +197,9 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
   double trace_state = *a.a2;
   const bool capturer = (g == 0);
   const int sg_words = (a.k + 31) / 32;
+  // guesses of the exponent of max|y| and max|x| for T_tau (block-uniform),
+  // kept apart for the first, the second and the later iterations
+  int egy0 = 0, egy1 = 0, egy2 = 0, egx0 = 0, egx1 = 0, egx2 = 0;
 
   for (int i = 0; i <= a.k; ++i) {
     if (i > 0 && ((i & 1023) == 0 || i == a.k)) {
@@ -408,10 +408,12 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
         const int to = opaque_tid();
         float y[KR], v[KR];
         const bool bad = !gather<T, KR>(a.yslot + rep_of(g) * rep_stride(n), n, ry, y, a.err, to);
-        if (!ternarize_dist_at<T, KR>(y, bad, n, a.tau, v, bufs, tslot, cnt, fb, to)) {
+        int eg = it == 0 ? egy0 : (it == 1 ? egy1 : egy2);
+        if (!ternarize_dist_guess<T, KR>(y, bad, n, a.tau, v, bufs, tslot, ry + rx, eg, cnt, fb, to)) {
           if (to == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
+        if (it == 0) egy0 = eg; else if (it == 1) egy1 = eg; else egy2 = eg;
         st_nnz_v += cnt;
         st_fb += fb;
 #pragma unroll
@@ -459,10 +461,12 @@ __global__ __launch_bounds__(T) void k_seq_persist(PerArgs a) {
         const int to = opaque_tid();
         float x[KC], u[KC];
         const bool bad = !gather<T, KC>(a.xslot + rep_of(g) * rep_stride(m), m, rx, x, a.err, to);
-        if (!ternarize_dist_at<T, KC>(x, bad, m, a.tau, u, bufs, tslot, cnt, fb, to)) {
+        int eg = it == 0 ? egx0 : (it == 1 ? egx1 : egx2);
+        if (!ternarize_dist_guess<T, KC>(x, bad, m, a.tau, u, bufs, tslot, ry + rx, eg, cnt, fb, to)) {
           if (to == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           return;
         }
+        if (it == 0) egx0 = eg; else if (it == 1) egx1 = eg; else egx2 = eg;
         st_nnz_u += cnt;
         st_fb += fb;
 #pragma unroll
