@@ -176,87 +176,12 @@ __device__ inline bool gather(const unsigned* slot, int N, unsigned round, float
 // first reduction: if any thread of the block has it set, returns false and
 // the caller leaves.  Writes T_tau(x) to out in the same layout; cnt gets
 // this thread's nonzeros, fallback whether the largest-entry rule applied.
-// The two block reductions are done by LDS atomics, one per wave, into two
-// slots: slot[0] takes the fixed-point sum
-// (fp64; its terms are integers whose total is below 2^52, so the order of
-// the adds cannot change it) and the low word of slot[1] the maximum
-// magnitude's bits (a failed gather adds 0xffffffff, above every finite
-// magnitude).  After each barrier every thread reads one slot instead of
-// one entry per wave.  Clearing: thread 0 clears the sum slot on entry
-// (every thread read it before the barrier that separates two calls) and
-// the maximum slot after the second barrier (every thread read it before
-// that barrier).  The caller clears both before its first barrier and keeps
-// at least one barrier between two calls.  bufs[0] serves the fallback's
-// argmin.
-template <int T, int K>
-__device__ inline bool ternarize_dist_at(const float (&val)[K], bool bad, int N, float tau,
-                                         float (&out)[K], double (*bufs)[T / kWave][4], double* slot,
-                                         int& cnt, int& fallback, int tid = -1) {
-  const int t = tid >= 0 ? tid : (int)threadIdx.x;
-  const int lane = t & (kWave - 1);
-  unsigned* const mslot = reinterpret_cast<unsigned*>(slot + 1);
-  if (t == 0) slot[0] = 0.0;
-  uint32_t ab[K];
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    ab[j] = __float_as_uint(val[j]) & 0x7fffffffu;
-    mx = max(mx, ab[j]);
-  }
-  if (bad) mx = 0xffffffffu;
-  const uint32_t mw = wave_umax_to63(mx);
-  if (lane == kWave - 1) atomicMax(mslot, mw);
-  __syncthreads();
-  const uint32_t Mb = *mslot;
-  if (Mb == 0xffffffffu) return false;
-  cnt = 0;
-  if (Mb == 0u) {   // both slots are still clear
-#pragma unroll
-    for (int j = 0; j < K; ++j) out[j] = (t + T * j == 0) ? 1.f : 0.f;
-    fallback = 1;
-    cnt = t == 0 ? 1 : 0;
-    return true;
-  }
-  const int s = fixed_point_shift(__uint_as_float(Mb), N);
-  double qs = 0.0;
-#pragma unroll
-  for (int j = 0; j < K; ++j) qs += fixed_point_q(__uint_as_float(ab[j]), s);
-  const double qw = wave_sum_to63(qs);
-  if (lane == kWave - 1) atomicAdd(slot, qw);
-  __syncthreads();
-  const double S = slot[0];
-  if (t == 0) *mslot = 0u;
-  const double thr = fixed_point_threshold(S, s, tau, N);
-  const uint32_t tb = threshold_bits(thr);
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const bool keep = ab[j] > tb;
-    out[j] = keep ? (val[j] > 0.f ? 1.f : -1.f) : 0.f;
-    cnt += keep ? 1 : 0;
-  }
-  fallback = 0;
-  if (Mb > tb) return true;
-  int first = INT32_MAX;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const int idx = t + T * j;
-    if (idx < N && ab[j] == Mb) first = min(first, idx);
-  }
-  const int pick = block_min_idx<T>(first, bufs[0]);
-  cnt = 0;
-#pragma unroll
-  for (int j = 0; j < K; ++j) {
-    if (t + T * j == pick) {
-      out[j] = val[j] > 0.f ? 1.f : -1.f;
-      cnt = 1;
-    }
-  }
-  fallback = 1;
-  return true;
-}
-
-// ternarize_dist_at with the fixed-point sum formed before the first barrier,
-// at the shift of a guessed exponent eg of max|x| (block-uniform; the caller
+// The block reductions are LDS atomics, one per wave after its DPP
+// reduction: the maximum magnitude's bits (a failed gather adds
+// 0xffffffff, above every finite magnitude) and the fixed-point sum, whose
+// terms are integers with a total below 2^52, so the order of the adds
+// cannot change it.  The sum is formed before the first barrier, at the
+// shift of a guessed exponent eg of max|x| (block-uniform; the caller
 // keeps one guess per kind of vector).  When the true exponent equals eg the
 // sum is the one the plain rule forms (the same shift, the same integers) and
 // one barrier serves both reductions; otherwise the sum is formed again at
