@@ -31,20 +31,20 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled by what the
 # same counters read for a plain 1 GiB copy (FETCH x 2.0, WRITE x 1.0).  It is
 # reported only while the kernel's sources hash to the ones it was taken on.
-SEQ_TRAFFIC_BYTES = 48173180288
+SEQ_TRAFFIC_BYTES = 47515127744
 SEQ_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_resident.hip",
                        "ternary_rank_weight_amd/csrc/device_common.hpp",
                        "ternary_rank_weight_amd/csrc/exchange.hpp"]
-SEQ_TRAFFIC_SHA = "92c9865a857901e7"
+SEQ_TRAFFIC_SHA = "c97be5df5c9f5a50"
 
 # Measured HBM traffic of one k_seq_persist launch on the 9728 x 2560 workload
 # (mu = 3, tau = 1.0, k = 7680), scaled the same way; reported only while the
 # kernel's sources hash to the ones it was taken on.
-PERSIST_TRAFFIC_BYTES = 10325848304480
+PERSIST_TRAFFIC_BYTES = 10250384020576
 PERSIST_TRAFFIC_SOURCES = ["ternary_rank_weight_amd/csrc/seq_persist.hip",
                            "ternary_rank_weight_amd/csrc/device_common.hpp",
                            "ternary_rank_weight_amd/csrc/exchange.hpp"]
-PERSIST_TRAFFIC_SHA = "0dce516f016d26a5"
+PERSIST_TRAFFIC_SHA = "4dbbebdf9a48a7bc"
 
 # rocprofv3 counters of the block path on the 2560 x 2560 workload (b = 64),
 # per dispatch of the combined Gram / inverse / contraction launch: MFMA busy
@@ -52,13 +52,13 @@ PERSIST_TRAFFIC_SHA = "0dce516f016d26a5"
 # (MOPS x 512), and HBM
 # bytes (FETCH x 2.0, WRITE x 1.0) against the 26.2 MB of R it must read.
 # Reported only while the block sources hash to the ones they were taken on.
-BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0378,
+BLOCK_COUNTERS = {"kernel": "k_contract_with_inverse", "mfma_busy_frac": 0.0375,
                   "bf16_mfma_flops": 2.5281e9, "int8_mfma_ops": 3.220e7, "fetch_bytes": 26732544,
                   "write_bytes": 3293286, "R_bytes": 26214400}
 BLOCK_COUNTER_SOURCES = ["ternary_rank_weight_amd/csrc/block.hip",
                          "ternary_rank_weight_amd/csrc/device_common.hpp",
                          "ternary_rank_weight_amd/csrc/exchange.hpp"]
-BLOCK_COUNTER_SHA = "3b2698fdcc997564"
+BLOCK_COUNTER_SHA = "0d5d5cd91db09a88"
 
 
 def _sources_sha(files):
