@@ -14,7 +14,7 @@ Accuracy Approaching Any Quantization Level):
   §2.5  importance-weighted ALS (column weights h~ = h / max(h) + lambda)
   Appendix (monotone residual): the residual norm never increases.
 
-Readings (listed with their reasons in the design doc):
+Readings where the pages leave a step open:
   * k = round-half-away(mu * min(m, n)) computed in fp64, mu widened from fp32.
   * One iteration is the V update followed by the U update; there are `iters`
     of them and no early stop.  The scale uses the final u and v, and u.x with

@@ -11,7 +11,7 @@ Definition on the page: entry i of T_tau(x) is sign(x_i) when |x_i| exceeds tau
 times the mean of |x| over the whole vector, else 0; when nothing would be
 kept, the single largest entry is kept instead.
 
-Readings where the page leaves a step open (each one is listed in the design doc):
+Readings where the page leaves a step open:
 
 * The mean is taken over the vector's own length N (m for u, n for v).
 * The mean is computed in a fixed, order-free way so that two
