@@ -50,3 +50,25 @@ def test_workspace_too_small_is_rejected(lib):
         lib.decompose(A, 1.0, 0.7, 15, 0, 0, workspace=ws)
     assert ei.value.status == 2
     np.testing.assert_equal(need > 256, True)
+
+
+@pytest.mark.parametrize("m,n,mu", [(1024, 1024, 1.0), (2048, 1536, 1.0)])
+def test_placement_probe_leaves_results_unchanged(lib, m, n, mu):
+    # Long resident runs time several placements of the exchange words first
+    # and use the fastest; where the words sit cannot change a result.  The
+    # no-allocation entry point uses one placement and no probe, so the two
+    # must agree bit for bit, also in a caller workspace full of leftovers.
+    A = torch.from_numpy(synthetic.llm_like(m, n, 7)).cuda()
+    k = lib.rank(m, n, mu)
+    assert k >= 1024 and m * n >= (1 << 20)   # the probe runs
+    ref = lib.decompose_noalloc(A, mu, 0.7, 15, 0, 3, trace=True, stats=True)
+    need = lib.workspace_bytes(m, n, mu, 0, lib.MODE_RESIDENT)
+    ws = _aligned_workspace(need)
+    for got in (lib.decompose(A, mu, 0.7, 15, 0, 3, mode=lib.MODE_RESIDENT, trace=True, stats=True),
+                lib.decompose(A, mu, 0.7, 15, 0, 3, mode=lib.MODE_RESIDENT, trace=True, stats=True,
+                              workspace=ws)):
+        torch.cuda.synchronize()
+        assert got.stat("mode") == 1 and got.stat("timeouts") == 0
+        assert torch.equal(got.B2, ref.B2) and torch.equal(got.C2, ref.C2)
+        assert torch.equal(got.D, ref.D) and torch.equal(got.energy, ref.energy)
+        assert torch.equal(got.trace, ref.trace)
