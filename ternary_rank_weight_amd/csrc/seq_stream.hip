@@ -110,9 +110,17 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
                                                        long long* __restrict__ fallbacks,
                                                        const float* __restrict__ wt, double* __restrict__ wsum,
                                                        long long* __restrict__ nnz_sum) {
-  constexpr int T = 256;
-  __shared__ double scratch[T / kWave];
+  constexpr int T = 256, W = T / kWave;
+  __shared__ int scratch[W];
+  __shared__ int wcnt[W];
+  __shared__ double wws[W];
+  __shared__ unsigned s_max;   // bits of the largest |x| (LDS atomic max)
+  __shared__ double s_sum;     // the fixed-point sum (LDS atomic add of exact integers)
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  if (tid == 0) {
+    s_max = 0u;
+    s_sum = 0.0;
+  }
   float v[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -123,7 +131,12 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
   float mx = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) mx = fmaxf(mx, fabsf(v[j]));
-  const float M = block_max<T>(mx, reinterpret_cast<float*>(scratch));
+  // DPP inside the wave, one LDS atomic per wave; a wave whose entries are
+  // all NaN adds nothing, as a NaN operand of fmaxf adds nothing
+  const float wm = wave_max_to63(mx);
+  if (lane == kWave - 1) atomicMax(&s_max, wm == wm ? __float_as_uint(wm) : 0u);
+  __syncthreads();
+  const float M = __uint_as_float(s_max);
   const int64_t words = (N + 15) / 16;
   if (M == 0.f) {
     for (int64_t q = tid; q < words; q += T) codes[q] = (q == 0) ? 1u : 0u;
@@ -139,8 +152,11 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
   double q = 0.0;   // integer-valued partial sums below 2^52: exact in any order
 #pragma unroll
   for (int j = 0; j < K; ++j) q += fixed_point_q(fabsf(v[j]), s);
-  const double thr = fixed_point_threshold(block_sum<T>(q, scratch), s, tau, N);
-  int cnt = 0;
+  const double qw = wave_sum_to63(q);
+  if (lane == kWave - 1) atomicAdd(&s_sum, qw);
+  __syncthreads();
+  const double thr = fixed_point_threshold(s_sum, s, tau, N);
+  int cnt = 0;       // this wave's kept entries (wave-uniform, from the ballots)
   double ws = 0.0;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -148,7 +164,7 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
     const bool keep = idx < N && (double)fabsf(v[j]) > thr;
     const unsigned long long nz = __ballot(keep);
     const unsigned long long ng = __ballot(keep && v[j] < 0.f);
-    cnt += keep ? 1 : 0;
+    cnt += __popcll(nz);
     if (wsum && keep) ws += (double)wt[idx];
     if (lane < 4) {
       const int64_t wd = (int64_t)16 * j + 4 * w + lane;
@@ -157,13 +173,25 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
     }
   }
   if ((double)M > thr) {
-    const int total = block_sum<T>(cnt, reinterpret_cast<int*>(scratch));
-    if (wsum) {
-      const double wt_total = block_sum<T>(ws, scratch);
-      if (tid == 0) *wsum = wt_total;
+    // per-wave parts in fixed order: DPP inside the wave, waves in index order
+    const double wsw = wsum ? wave_sum_to63(ws) : 0.0;
+    if (lane == kWave - 1) {
+      wcnt[w] = cnt;
+      wws[w] = wsw;
     }
-    if (tid == 0 && nnz_out) *nnz_out = total;
-    if (tid == 0 && nnz_sum) *nnz_sum += total;
+    __syncthreads();
+    if (tid == 0) {
+      int total = 0;
+      double wt_total = 0.0;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        total += wcnt[u];
+        wt_total += wws[u];
+      }
+      if (wsum) *wsum = wt_total;
+      if (nnz_out) *nnz_out = total;
+      if (nnz_sum) *nnz_sum += total;
+    }
     return;
   }
   // Nothing passed: keep the smallest index holding the largest magnitude.
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(256) void k_ternarize_reg(const float* __restrict__
     const int64_t idx = tid + (int64_t)T * j;
     if (idx < N && fabsf(v[j]) == M) first = min(first, (int)idx);
   }
-  const int pick = block_min_i<T>(first, reinterpret_cast<int*>(scratch));
+  const int pick = block_min_i<T>(first, scratch);
   __syncthreads();  // the zero code words written above are visible block-wide below
   if (tid == 0) {
     codes[pick >> 4] = code_of(x[pick]) << (2 * (pick & 15));
