@@ -10,9 +10,10 @@ It is a plain, slow, step-by-step transcription of the method on the pages of
 Approaching Any Quantization Level" (§2.1-§2.4, §2.6), in float64, with numpy
 matrix products and Cholesky factorisations as the only library steps.
 
-oracle/c/externd_oracle.c is a second, plain C transcription of T_tau and the
-greedy sequential decomposition (loaded by oracle/c_oracle.py, compiled by
-build() in __graft_entry__.py), pinned the same way in tests/test_oracle_c.py.
+oracle/c/externd_oracle.c is a second, plain C transcription of T_tau, the
+greedy sequential decomposition and the plain block ALS (loaded by
+oracle/c_oracle.py, compiled by build() in __graft_entry__.py), pinned the
+same way in tests/test_oracle_c.py.
 
 Pins (tests/test_oracle_*.py) tie it to what the pages and mathematics fix:
 hand-worked T_tau vectors, the Gaussian zero-fraction closed form, the

@@ -1,5 +1,6 @@
 /*
- * Plain C fp64 oracle of ExTernD's greedy sequential decomposition.
+ * Plain C fp64 oracle of ExTernD's greedy sequential decomposition and its
+ * batched block ALS.
  *
  * Test infrastructure: only tests, the smoke check and the benchmark's CPU
  * baseline may load this library.  It shares no code with the GPU library
@@ -14,6 +15,9 @@
  *   §2.3  per component: alternate v = T_tau(R^T u), u = T_tau(R v) for a
  *         fixed number of iterations, take d = u^T R v / (||u||^2 ||v||^2),
  *         subtract d u v^T from R.
+ *   §2.4  per block of b components: decorrelated targets through the
+ *         ridge-regularised inverse Grams, T_tau by columns, the joint
+ *         scale solve, the rank-b deflation (orc_decompose_block).
  *
  * Readings the pages leave open (the same ones the numpy oracle takes):
  *   - the mean is over the vector's own length N, in an exact fixed point:
@@ -29,7 +33,11 @@
  *     mix(x) = fin(x + 0x9E3779B97F4A7C15), fin as published;
  *   - one iteration is the v update then the u update; no early stop;
  *   - k = mu * min(m, n) rounded half away from zero (the caller passes k);
- *   - trace[i] = ||R||^2 after component i, recomputed from R.
+ *   - trace[i] = ||R||^2 after component i, recomputed from R;
+ *   - block mode: the ridge eps = 1e-6 trace(G) / b of each Gram G; the
+ *     joint solve by Cholesky, retried once with that kind of ridge when a
+ *     pivot is not positive; the starting vectors of a block are those of
+ *     its components' global indices.
  *
  * Everything is plain loops in fp64 in index order; nothing is blocked,
  * fused or reordered.
@@ -167,4 +175,182 @@ int orc_decompose_seq(const float* A, int64_t m, int64_t n, int64_t k, float tau
   *energy = norm_a2 > 0.0 ? 1.0 - r2 / norm_a2 : 1.0;
   free(R); free(u); free(x); free(v); free(y); free(tu); free(tv);
   return 0;
+}
+
+/*
+ * Batched block ALS (§2.4), plain: for each block of b components (the last
+ * block takes what is left), U0 is the start vectors of the block's
+ * components; each of `iters` iterations takes
+ *   V = T_tau by columns of [(U^T U + eps I)^-1 U^T R]^T,
+ *   U = T_tau by columns of R V (V^T V + eps I)^-1,
+ * with eps = 1e-6 trace(G) / b for each Gram G; then the b scales solve
+ * [(U^T U) o (V^T V)] d = diag(U^T R V) by Cholesky (retried once with the
+ * same kind of ridge when a pivot is not positive), and R <- R - U diag(d)
+ * V^T.  trace[blk] = ||R||^2 after each block.  Outputs as for
+ * orc_decompose_seq; *retries counts the ridge retries.  Returns 0, or -1
+ * when memory runs out.
+ */
+
+/* Cholesky factor of the symmetric matrix a (n x n, row-major) in place
+ * (lower triangle); 0 when a pivot is not positive. */
+static int cholesky(double* a, int n) {
+  for (int j = 0; j < n; ++j) {
+    double s = a[j * n + j];
+    for (int k = 0; k < j; ++k) s -= a[j * n + k] * a[j * n + k];
+    if (!(s > 0.0)) return 0;
+    const double ljj = sqrt(s);
+    a[j * n + j] = ljj;
+    for (int i = j + 1; i < n; ++i) {
+      double t = a[i * n + j];
+      for (int k = 0; k < j; ++k) t -= a[i * n + k] * a[j * n + k];
+      a[i * n + j] = t / ljj;
+    }
+  }
+  return 1;
+}
+
+/* x <- (L L^T)^-1 x for the vector x of length n held with stride `st`. */
+static void cholesky_solve(const double* L, int n, double* x, int64_t st) {
+  for (int i = 0; i < n; ++i) {
+    double t = x[i * st];
+    for (int k = 0; k < i; ++k) t -= L[i * n + k] * x[k * st];
+    x[i * st] = t / L[i * n + i];
+  }
+  for (int i = n - 1; i >= 0; --i) {
+    double t = x[i * st];
+    for (int k = i + 1; k < n; ++k) t -= L[k * n + i] * x[k * st];
+    x[i * st] = t / L[i * n + i];
+  }
+}
+
+/* G + eps I with eps = 1e-6 trace(G) / n, then its Cholesky factor. */
+static int ridge_factor(double* g, int n) {
+  double tr = 0.0;
+  for (int i = 0; i < n; ++i) tr += g[i * n + i];
+  const double eps = 1e-6 * tr / (double)n;
+  for (int i = 0; i < n; ++i) g[i * n + i] += eps;
+  return cholesky(g, n);
+}
+
+int orc_decompose_block(const float* A, int64_t m, int64_t n, int64_t k, int b, float tau, int iters,
+                        uint64_t seed, int8_t* B, int8_t* C, double* D, double* trace, double* energy,
+                        int64_t* retries) {
+  if (b < 1) return -1;
+  double* R = (double*)malloc(sizeof(double) * (size_t)(m * n));
+  double* U = (double*)malloc(sizeof(double) * (size_t)(m * b));    /* m x b */
+  double* V = (double*)malloc(sizeof(double) * (size_t)(n * b));    /* n x b */
+  double* Tv = (double*)malloc(sizeof(double) * (size_t)(b * n));   /* b x n: V target, row per component */
+  double* Tu = (double*)malloc(sizeof(double) * (size_t)(b * m));   /* b x m: U target */
+  double* Q = (double*)malloc(sizeof(double) * (size_t)(m * b));    /* R V */
+  double* G = (double*)malloc(sizeof(double) * (size_t)(b * b));
+  double* G2 = (double*)malloc(sizeof(double) * (size_t)(b * b));
+  double* rhs = (double*)malloc(sizeof(double) * (size_t)b);
+  int8_t* t8 = (int8_t*)malloc((size_t)(m > n ? m : n));
+  double* col = (double*)malloc(sizeof(double) * (size_t)(m > n ? m : n));
+  if (!R || !U || !V || !Tv || !Tu || !Q || !G || !G2 || !rhs || !t8 || !col) {
+    free(R); free(U); free(V); free(Tv); free(Tu); free(Q); free(G); free(G2); free(rhs); free(t8); free(col);
+    return -1;
+  }
+  double norm_a2 = 0.0;
+  for (int64_t p = 0; p < m * n; ++p) {
+    R[p] = (double)A[p];
+    norm_a2 += R[p] * R[p];
+  }
+  double r2 = norm_a2;
+  int64_t nretry = 0;
+  const int64_t nblocks = (k + b - 1) / b;
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    const int64_t c0 = blk * b;
+    const int bb = (int)(k - c0 < b ? k - c0 : b);
+    for (int j = 0; j < bb; ++j) {
+      orc_start_vector(seed, c0 + j, m, col);
+      for (int64_t r = 0; r < m; ++r) U[r * bb + j] = col[r];
+    }
+    for (int it = 0; it < iters; ++it) {
+      /* G = U^T U, the V target rows Tv = (G + eps I)^-1 U^T R */
+      for (int i = 0; i < bb; ++i)
+        for (int j = 0; j < bb; ++j) {
+          double s = 0.0;
+          for (int64_t r = 0; r < m; ++r) s += U[r * bb + i] * U[r * bb + j];
+          G[i * bb + j] = s;
+        }
+      for (int i = 0; i < bb; ++i)
+        for (int64_t c = 0; c < n; ++c) Tv[i * n + c] = 0.0;
+      for (int64_t r = 0; r < m; ++r)
+        for (int i = 0; i < bb; ++i) {
+          const double ur = U[r * bb + i];
+          if (ur != 0.0)
+            for (int64_t c = 0; c < n; ++c) Tv[i * n + c] += ur * R[r * n + c];
+        }
+      if (!ridge_factor(G, bb)) goto fail;
+      for (int64_t c = 0; c < n; ++c) cholesky_solve(G, bb, Tv + c, n);
+      for (int i = 0; i < bb; ++i) {
+        orc_ternarize(Tv + (int64_t)i * n, n, tau, t8);
+        for (int64_t c = 0; c < n; ++c) V[c * bb + i] = (double)t8[c];
+      }
+      /* Q = R V, G = V^T V, the U target rows Tu = (G + eps I)^-1 Q^T */
+      for (int64_t r = 0; r < m; ++r)
+        for (int j = 0; j < bb; ++j) {
+          double s = 0.0;
+          for (int64_t c = 0; c < n; ++c) s += R[r * n + c] * V[c * bb + j];
+          Q[r * bb + j] = s;
+        }
+      for (int i = 0; i < bb; ++i)
+        for (int j = 0; j < bb; ++j) {
+          double s = 0.0;
+          for (int64_t c = 0; c < n; ++c) s += V[c * bb + i] * V[c * bb + j];
+          G[i * bb + j] = s;
+        }
+      for (int i = 0; i < bb; ++i)
+        for (int64_t r = 0; r < m; ++r) Tu[i * m + r] = Q[r * bb + i];
+      if (!ridge_factor(G, bb)) goto fail;
+      for (int64_t r = 0; r < m; ++r) cholesky_solve(G, bb, Tu + r, m);
+      for (int i = 0; i < bb; ++i) {
+        orc_ternarize(Tu + (int64_t)i * m, m, tau, t8);
+        for (int64_t r = 0; r < m; ++r) U[r * bb + i] = (double)t8[r];
+      }
+    }
+    /* the joint scales: [(U^T U) o (V^T V)] d = diag(U^T R V), read off Q */
+    for (int j = 0; j < bb; ++j) {
+      double s = 0.0;
+      for (int64_t r = 0; r < m; ++r) s += U[r * bb + j] * Q[r * bb + j];
+      rhs[j] = s;
+    }
+    for (int i = 0; i < bb; ++i)
+      for (int j = 0; j < bb; ++j) {
+        double gu = 0.0, gv = 0.0;
+        for (int64_t r = 0; r < m; ++r) gu += U[r * bb + i] * U[r * bb + j];
+        for (int64_t c = 0; c < n; ++c) gv += V[c * bb + i] * V[c * bb + j];
+        G[i * bb + j] = gu * gv;
+      }
+    memcpy(G2, G, sizeof(double) * (size_t)(bb * bb));
+    if (!cholesky(G2, bb)) {
+      ++nretry;
+      memcpy(G2, G, sizeof(double) * (size_t)(bb * bb));
+      if (!ridge_factor(G2, bb)) goto fail;
+    }
+    for (int j = 0; j < bb; ++j) col[j] = rhs[j];
+    cholesky_solve(G2, bb, col, 1);
+    r2 = 0.0;
+    for (int64_t r = 0; r < m; ++r)
+      for (int64_t c = 0; c < n; ++c) {
+        double s = 0.0;
+        for (int j = 0; j < bb; ++j) s += U[r * bb + j] * col[j] * V[c * bb + j];
+        R[r * n + c] -= s;
+        r2 += R[r * n + c] * R[r * n + c];
+      }
+    for (int j = 0; j < bb; ++j) {
+      for (int64_t r = 0; r < m; ++r) B[(c0 + j) * m + r] = (int8_t)U[r * bb + j];
+      for (int64_t c = 0; c < n; ++c) C[(c0 + j) * n + c] = (int8_t)V[c * bb + j];
+      D[c0 + j] = col[j];
+    }
+    if (trace) trace[blk] = r2;
+  }
+  *energy = norm_a2 > 0.0 ? 1.0 - r2 / norm_a2 : 1.0;
+  if (retries) *retries = nretry;
+  free(R); free(U); free(V); free(Tv); free(Tu); free(Q); free(G); free(G2); free(rhs); free(t8); free(col);
+  return 0;
+fail:
+  free(R); free(U); free(V); free(Tv); free(Tu); free(Q); free(G); free(G2); free(rhs); free(t8); free(col);
+  return -2;
 }

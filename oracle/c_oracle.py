@@ -2,7 +2,8 @@
 
 Test infrastructure: only tests, the smoke check and the benchmark's CPU
 baseline may use this module.  The C library implements T_tau (§2.2, with the
-fixed-point mean reading) and the greedy sequential decomposition (§2.3) of
+fixed-point mean reading), the greedy sequential decomposition (§2.3) and
+the plain batched block ALS (§2.4) of
 "ExTernD: Expanded-Rank Ternary Decomposition Ternary LLM PTQ with Accuracy
 Approaching Any Quantization Level" in plain loops; it shares no code with
 the GPU library or with the numpy oracle.  build() in __graft_entry__.py
@@ -18,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "c", "externd_oracle.c")
 LIB = os.path.join(HERE, "c", "liboracle_c.so")
 
-__all__ = ["build_c", "splitmix64_mix", "start_vector", "threshold", "ternarize", "decompose_seq"]
+__all__ = ["build_c", "splitmix64_mix", "start_vector", "threshold", "ternarize", "decompose_seq",
+           "decompose_block"]
 
 
 def build_c():
@@ -51,6 +53,9 @@ def _load():
         lib.orc_ternarize.argtypes = [p, i64, f32, p]
         lib.orc_decompose_seq.restype = ctypes.c_int
         lib.orc_decompose_seq.argtypes = [p, i64, i64, i64, f32, ctypes.c_int, u64, p, p, p, p, p]
+        lib.orc_decompose_block.restype = ctypes.c_int
+        lib.orc_decompose_block.argtypes = [p, i64, i64, i64, ctypes.c_int, f32, ctypes.c_int, u64, p, p, p, p,
+                                            p, p]
         _lib = lib
     return _lib
 
@@ -100,3 +105,23 @@ def decompose_seq(A, k, tau, iters=15, seed=0):
     if rc != 0:
         raise MemoryError("C oracle: out of memory")
     return Bt.T.copy(), C, D, trace, E.value
+
+
+def decompose_block(A, k, b, tau, iters=15, seed=0):
+    """Block ALS with exactly width b (the last block takes the rest).
+    Returns (B m x k, C k x n, D, trace per block, E, ridge retries)."""
+    A32 = np.ascontiguousarray(A, dtype=np.float32)
+    m, n = A32.shape
+    Bt = np.zeros((k, m), dtype=np.int8)
+    C = np.zeros((k, n), dtype=np.int8)
+    D = np.zeros(k, dtype=np.float64)
+    trace = np.zeros((k + b - 1) // b, dtype=np.float64)
+    E = ctypes.c_double(0.0)
+    retries = ctypes.c_int64(0)
+    rc = _load().orc_decompose_block(_ptr(A32), m, n, k, b, float(tau), iters, seed, _ptr(Bt), _ptr(C), _ptr(D),
+                                     _ptr(trace), ctypes.byref(E), ctypes.byref(retries))
+    if rc == -1:
+        raise MemoryError("C oracle: out of memory")
+    if rc != 0:
+        raise ArithmeticError("C oracle: a ridge-regularised Gram is not positive definite")
+    return Bt.T.copy(), C, D, trace, E.value, retries.value

@@ -144,3 +144,43 @@ def test_agrees_with_the_numpy_oracle():
     np.testing.assert_allclose(D, ref.D, rtol=1e-12, atol=0)
     np.testing.assert_allclose(trace, ref.trace, rtol=1e-10)
     assert abs(E - ref.E) < 1e-12
+
+
+def test_block_width_one_equals_sequential():
+    # With b = 1 the decorrelated targets are positive multiples of R^T u
+    # and R v, T_tau is scale invariant and the joint solve is the single
+    # scale: the block iteration reproduces the sequential one (§2.3, §2.4).
+    A = synthetic.gaussian(40, 28, 4)
+    Bs, Cs, Ds, ts, Es = coracle.decompose_seq(A, 28, 0.7, seed=5)
+    Bb, Cb, Db, tb, Eb, retries = coracle.decompose_block(A, 28, 1, 0.7, seed=5)
+    assert np.array_equal(Bb, Bs) and np.array_equal(Cb, Cs)
+    np.testing.assert_allclose(Db, Ds, rtol=1e-10)
+    np.testing.assert_allclose(tb, ts, rtol=1e-9)
+    assert retries == 0
+
+
+def test_block_energy_and_residual_bookkeeping():
+    # E = 1 - ||A - B diag(D) C||^2 / ||A||^2 (§2.1) recomputed from the C
+    # oracle's own factors, a residual that never grows block to block, and
+    # ternary factors with a trailing partial block (k = 150, b = 8).
+    A = synthetic.gaussian(96, 80, 6)
+    B, C, D, trace, E, retries = coracle.decompose_block(A, 150, 8, 0.7, seed=0)
+    assert trace.size == 19 and set(np.unique(B)).issubset({-1, 0, 1}) and set(np.unique(C)).issubset({-1, 0, 1})
+    A64 = A.astype(np.float64)
+    a2 = float(np.sum(A64 ** 2))
+    resid = A64 - (B.astype(np.float64) * D) @ C.astype(np.float64)
+    assert abs((1.0 - float(np.sum(resid ** 2)) / a2) - E) < 1e-12
+    prev = np.concatenate([[a2], trace[:-1]])
+    assert np.all(trace <= prev * (1 + 1e-14))
+
+
+def test_block_agrees_with_the_numpy_oracle():
+    A = synthetic.gaussian(96, 80, 6)
+    B, C, D, trace, E, retries = coracle.decompose_block(A, 160, 8, 0.7, seed=0)
+    ref = oracle.decompose_block(A, 2.0, 0.7, block=8, seed=0)
+    assert ref.extra["b"] == 8 and ref.B.shape[1] == 160
+    assert np.array_equal(B, ref.B) and np.array_equal(C, ref.C)
+    np.testing.assert_allclose(D, ref.D, rtol=1e-9)
+    np.testing.assert_allclose(trace, ref.trace, rtol=1e-9)
+    assert abs(E - ref.E) < 1e-12
+    assert retries == ref.extra["ridge_retries"]
