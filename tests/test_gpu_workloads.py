@@ -107,3 +107,29 @@ def test_lowrank4096_mu_tau_sweep(lib):
         zf_by_tau[tau] = oracle.zero_fraction(B, C)
     taus = sorted(zf_by_tau)
     assert all(zf_by_tau[t1] < zf_by_tau[t2] for t1, t2 in zip(taus, taus[1:])), zf_by_tau
+
+
+@pytest.mark.parametrize("block", [0, 16])
+def test_gauss256_against_the_c_oracle(lib, block):
+    # The 256 x 256 Gaussian workload in both modes against the plain C fp64
+    # oracle run on the same seeded input: energy within 2e-3, and the GPU's
+    # energy within 1e-5 of the one recomputed from its own factors.
+    import oracle.c_oracle as coracle
+    if not os.path.exists(coracle.LIB):
+        coracle.build_c()
+    c = synthetic.WORKLOADS["gauss256"]
+    A = synthetic.workload_matrix("gauss256")
+    k = lib.rank(256, 256, c["mu"])
+    res = lib.decompose(torch.from_numpy(A).cuda(), c["mu"], c["tau"], c["iters"], block, c["seed"],
+                        stats=True)
+    torch.cuda.synchronize()
+    if block:
+        b = lib.block_width(256, 256, block)
+        *_, E_ref, _ = coracle.decompose_block(A, k, b, c["tau"], c["iters"], c["seed"])
+    else:
+        *_, E_ref = coracle.decompose_seq(A, k, c["tau"], c["iters"], c["seed"])
+    E = float(res.energy.item())
+    print(f"  gauss256 block={block}: E gpu {E:.6f} C oracle {E_ref:.6f}", flush=True)
+    assert abs(E - E_ref) <= 2e-3
+    B, C, D = _factors(res)
+    assert abs(E - oracle.energy_from_factors(A, B, C, D)) <= 1e-5
