@@ -328,11 +328,15 @@ def test_streaming_beyond_resident_limit(lib):
 
 
 @pytest.mark.parametrize("m,n,comp", [(37, 52, 3), (2, 128, 1), (700, 452, 9), (5000, 300, 4),
-                                      (1100, 5000, 2), (4096, 4096, 1)])
+                                      (1100, 5000, 2), (4096, 4096, 1), (2000, 8000, 2),
+                                      (10240, 10240, 1)])
 def test_capture_parity_streaming_persistent(lib, m, n, comp):
     # The persistent streaming kernel (R in device memory, one cooperative
     # launch) on every kind of shape it covers: ragged slabs, workgroups with
-    # no rows or no columns, and each of its instantiations.
+    # no rows or no columns, each of its (KR, KC) tilings (5,5), (5,10),
+    # (10,5), (8,8), (5,20) through the 9728 x 2560 tests, (20,5) and (20,20),
+    # and its largest shape, 10240 x 10240 (40 rows per workgroup, column
+    # blocks of 64 words; R is 419 MB, past the 256 MB last-level cache).
     A = synthetic.gaussian(m, n, 12)
     mu = (comp + 3.25) / min(m, n)
     res = lib.decompose(_dev(A), mu, 1.0, 6, 0, 3, mode=lib.MODE_PERSISTENT, capture=comp, stats=True)
