@@ -296,17 +296,22 @@ def measure_streaming(trw, Ad, c, k=256):
     return out
 
 
-def measure_streaming_large(trw, k=64, name="mlp9728"):
+def measure_streaming_large(trw, k=64, name="mlp9728", shape=None):
     """The sequential decomposition on a shape past the resident limit
-    (9728 x 2560, the LLM-shaped MLP workload, mu for its first k components,
-    tau 0.7), in the persistent streaming mode and in the streaming kernel
-    chain: event time, components/s, the algorithmic bytes rate (the
-    roofline's byte model) and its fraction of the HBM peak."""
+    (9728 x 2560, the LLM-shaped MLP workload, or with `shape` an LLM-shaped
+    matrix of that size, e.g. 10240 x 10240, whose 419 MB exceed the 256 MB
+    last-level cache; mu for its first k components, tau 0.7), in the
+    persistent streaming mode and in the streaming kernel chain: event time,
+    components/s, the algorithmic bytes rate (the roofline's byte model) and
+    its fraction of the HBM peak."""
     import torch
     import synthetic
-    A = torch.from_numpy(synthetic.workload_matrix(name)).cuda()
-    m, n = A.shape
     c = synthetic.WORKLOADS[name]
+    if shape is None:
+        A = torch.from_numpy(synthetic.workload_matrix(name)).cuda()
+    else:
+        A = torch.from_numpy(synthetic.llm_like(shape[0], shape[1], c["seed"])).cuda()
+    m, n = A.shape
     mu = (k + 0.25) / min(m, n)
     out = {"workload": f"{m}x{n} LLM-shaped, first {k} components, tau 0.7, sequential mode"}
     for label, mode in (("persistent", trw.MODE_PERSISTENT), ("streaming", trw.MODE_STREAMING)):
@@ -664,6 +669,8 @@ def main():
         if args.workload != "mlp9728":
             print("[bench] streaming 9728x2560", file=sys.stderr, flush=True)
             streaming["large"] = measure_streaming_large(trw)
+        print("[bench] streaming 10240x10240", file=sys.stderr, flush=True)
+        streaming["past_cache"] = measure_streaming_large(trw, shape=(10240, 10240))
     sweeps = None
     if "block" in per_mode and args.sweeps > 0:
         print("[bench] sweeps", file=sys.stderr, flush=True)
